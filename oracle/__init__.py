@@ -1,0 +1,41 @@
+"""CPU oracle for position-agnostic (deferred-RoPE) paged attention.
+
+TEST INFRASTRUCTURE ONLY.  This package is the slow, plain reference that the
+HIP library is checked against.  Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import it; the product path
+(``position_agnostic_kv_amd``) never does, and the two share no code.
+
+Everything here is numpy in float64 and follows the definitions on the pages
+step by step, without blocking, fusion or reordering:
+
+* [LA]  gist.science, "Resumo Técnico: LazyAttention" (summary of the
+  LazyAttention paper): sections "Declaração do Problema", "Metodologia",
+  "Implementação Técnica" (Prefilling, Decoding), "Equivalência Matemática".
+* [KVF] ai-engineering.academy, "KV Cache, Flash Attention & Otimização de
+  Inferência": sections "Flash Attention" (standard attention, running
+  softmax), "PagedAttention", "Construa" (Passo 1 KVCache, Passo 2 tiled
+  softmax).
+* [WHY] lynx-cortex, "00 — Por qué existe un KV Cache": sections
+  "Lo que hace el decoding autorregresivo", "El remedio", "El precio".
+
+Every function is pinned by a ``-m "not gpu"`` test in ``tests/`` against
+something other than itself (closed forms, a complex-number formulation of
+the rotation, brute force, torch's CPU scaled_dot_product_attention, values
+the pages print).  No function here is "parity unpinned".
+"""
+
+from .lazy_oracle import (  # noqa: F401
+    BLOCK_TOKENS,
+    append,
+    cache_bytes,
+    decode,
+    decode_one,
+    materialize_sequence,
+    prefill,
+    prefill_rows,
+    rope,
+    rope_frequencies,
+    softmax,
+    tiled_softmax_dot,
+    unpack_block_word,
+)

@@ -1,0 +1,460 @@
+"""Seeded synthetic inputs for the deferred-RoPE paged attention workloads.
+
+Shared by the tests, ``bench.py`` and ``__graft_entry__.smoke()``: the only
+code that both the CPU oracle and the HIP path are fed from.  It holds none of
+the attention arithmetic -- it draws random values, builds documents, packs
+block-table words, assigns pool slots, and converts between float32 and
+bfloat16 bit patterns.
+
+Workload shapes (documents of 256..2048 tokens, 8B / 70B head geometry,
+Zipf-skewed document reuse, a ~1 GB KV budget) stand in for the RAG
+benchmarks of the LazyAttention summary's "Resultados Experimentais", whose
+datasets and model weights are not available; all values are synthetic.
+
+Layout conventions (the same ones the library documents):
+  * K/V pool: [num_blocks][num_kv_heads][16][head_dim], content-only keys.
+  * Table word: block id in bits 0..15, position offset in bits 16..31.
+  * Every block of a document carries the document's start position as its
+    offset; a prompt's (or a new token's) blocks carry the prompt's first
+    position.  Only a sequence's last block may be partly filled.
+"""
+
+from dataclasses import dataclass, field
+from typing import List
+
+import numpy as np
+
+BLOCK = 16
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+# ----------------------------------------------------------------- bit helpers
+def f32_to_bf16_bits(x):
+    """Round float32 values to bfloat16 (round to nearest even); uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b):
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def pack_words(block_ids, offsets):
+    """Pack (block id, offset) pairs into uint32 table words (16 | 16 bits)."""
+    ids = np.asarray(block_ids, dtype=np.int64)
+    offs = np.asarray(offsets, dtype=np.int64)
+    if ids.size and (ids.min() < 0 or ids.max() > 0xFFFF):
+        raise ValueError("block id out of the 16-bit range")
+    if offs.size and (offs.min() < 0 or offs.max() > 0xFFFF):
+        raise ValueError("offset out of the 16-bit range")
+    return (ids | (offs << 16)).astype(np.uint32)
+
+
+# ------------------------------------------------------------------- layouts
+@dataclass
+class Layout:
+    """Block placement of a batch of sequences over one shared pool.
+
+    table[b] lists the sequence's blocks in logical order; tail_* describe the
+    region written by the step's append (a new decode token or a prompt).
+    """
+    num_blocks: int
+    table: np.ndarray            # uint32 [B, max_blocks]
+    cached_lens: np.ndarray      # int32 [B] tokens already in the cache
+    tail_lens: np.ndarray        # int32 [B] tokens the step appends
+    tail_pos: np.ndarray         # int32 [B] position of the first appended token
+    slot_mapping: np.ndarray     # int32 [sum(tail_lens)] pool slot of each appended token
+    doc_spans: List[list] = field(default_factory=list)  # per seq: (doc, length, offset)
+    unique_doc_tokens: int = 0   # tokens physically stored for documents
+
+    @property
+    def total_lens(self):
+        return (self.cached_lens + self.tail_lens).astype(np.int32)
+
+    @property
+    def batch(self):
+        return int(self.table.shape[0])
+
+
+def build_layout(rng, seq_docs, doc_lens, tail_lens, offsets=None, tail_pos=None,
+                 spare_blocks=0, shuffle=True):
+    """Place documents and appended tails into a shuffled block pool.
+
+    seq_docs[b]  : list of document indices making up sequence b (in order).
+    doc_lens[d]  : length of document d; every document except a sequence's
+                   last item must be a whole number of blocks.
+    tail_lens[b] : tokens the step appends after the documents.
+    offsets[b]   : optional explicit offset of each document of sequence b;
+                   default is contiguous placement (prefix sums).
+    tail_pos[b]  : position of the first appended token (default: right after
+                   the documents).
+    A document used by several sequences is stored once (zero-copy reuse).
+    """
+    bsz = len(seq_docs)
+    doc_blocks = {}
+    n_blocks = 0
+    for docs in seq_docs:
+        for d in docs:
+            if d not in doc_blocks:
+                nb = -(-int(doc_lens[d]) // BLOCK)
+                doc_blocks[d] = (n_blocks, nb)
+                n_blocks += nb
+    unique_tokens = sum(int(doc_lens[d]) for d in doc_blocks)
+    tail_first = []
+    for b in range(bsz):
+        tail_first.append(n_blocks)
+        n_blocks += -(-int(tail_lens[b]) // BLOCK)
+    n_blocks += spare_blocks
+    if n_blocks > 0x10000:
+        raise ValueError("pool needs more than 65536 blocks")
+    perm = rng.permutation(n_blocks) if shuffle else np.arange(n_blocks)
+
+    rows, cached, tpos, spans, slots = [], [], [], [], []
+    for b, docs in enumerate(seq_docs):
+        words = []
+        pos = 0
+        span = []
+        for i, d in enumerate(docs):
+            ln = int(doc_lens[d])
+            if ln % BLOCK and (i != len(docs) - 1 or tail_lens[b]):
+                raise ValueError("only a sequence's last item may end mid-block")
+            off = pos if offsets is None else int(offsets[b][i])
+            first, nb = doc_blocks[d]
+            words.extend(pack_words(perm[first:first + nb], [off] * nb).tolist())
+            span.append((d, ln, off))
+            pos += ln
+        cached.append(pos)
+        tp = pos if tail_pos is None else int(tail_pos[b])
+        tpos.append(tp)
+        nt = int(tail_lens[b])
+        nbt = -(-nt // BLOCK)
+        ids = perm[tail_first[b]:tail_first[b] + nbt]
+        words.extend(pack_words(ids, [tp] * nbt).tolist())
+        for t in range(nt):
+            slots.append(int(ids[t // BLOCK]) * BLOCK + t % BLOCK)
+        rows.append(words)
+        spans.append(span)
+    width = max(1, max(len(r) for r in rows))
+    table = np.zeros((bsz, width), dtype=np.uint32)
+    for b, r in enumerate(rows):
+        table[b, :len(r)] = r
+    return Layout(num_blocks=n_blocks, table=table,
+                  cached_lens=np.array(cached, dtype=np.int32),
+                  tail_lens=np.array(tail_lens, dtype=np.int32),
+                  tail_pos=np.array(tpos, dtype=np.int32),
+                  slot_mapping=np.array(slots, dtype=np.int32),
+                  doc_spans=spans, unique_doc_tokens=unique_tokens)
+
+
+def _docs_filling(rng, total, lo_blocks, hi_blocks):
+    """Document lengths (multiples of 16, uniform in blocks) summing to total."""
+    lens = []
+    left = total
+    while left > 0:
+        ln = BLOCK * int(rng.integers(lo_blocks, hi_blocks + 1))
+        ln = min(ln, left)
+        lens.append(ln)
+        left -= ln
+    return lens
+
+
+def _split_into(rng, total_blocks, parts):
+    """Cut total_blocks into `parts` non-empty block counts at random points."""
+    cuts = np.sort(rng.choice(np.arange(1, total_blocks), size=parts - 1, replace=False))
+    edges = np.concatenate([[0], cuts, [total_blocks]])
+    return (np.diff(edges) * BLOCK).tolist()
+
+
+# -------------------------------------------------------------------- values
+@dataclass
+class Case:
+    """One workload: geometry, layout and (once materialised) its values."""
+    name: str
+    kind: str                    # "decode" | "prefill"
+    dtype: str                   # F32 | BF16
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    rope_theta: float
+    layout: Layout
+    q_std: float = 1.0
+    kv_std: float = 0.5
+    seed: int = 0
+    # values: numpy arrays (float32, or uint16 bf16 bits) or torch tensors
+    q: object = None             # decode [B, Hq, D]; prefill [Tq, Hq, D]
+    k_pool: object = None        # [NB, Hkv, 16, D]
+    v_pool: object = None
+    k_new: object = None         # [T_new, Hkv, D]
+    v_new: object = None
+
+    @property
+    def scale(self):
+        return 1.0 / float(np.sqrt(self.head_dim))
+
+    @property
+    def batch(self):
+        return self.layout.batch
+
+    @property
+    def q_pos(self):
+        """Decode: position of the new query token."""
+        return self.layout.tail_pos.astype(np.int32)
+
+    @property
+    def seq_lens(self):
+        """Tokens attended by the step (cached + appended)."""
+        return self.layout.total_lens
+
+    @property
+    def cu_q_lens(self):
+        return np.concatenate([[0], np.cumsum(self.layout.tail_lens)]).astype(np.int32)
+
+    @property
+    def max_q_len(self):
+        return int(self.layout.tail_lens.max()) if self.batch else 0
+
+    def kv_bytes_read(self):
+        """Logical K+V bytes a decode pass reads (every attended token once)."""
+        esz = 4 if self.dtype == F32 else 2
+        return int(self.seq_lens.sum()) * self.num_kv_heads * self.head_dim * 2 * esz
+
+    def attention_flops(self):
+        """4*D FLOPs per visible (query, key) pair per query head (QK^T and PV)."""
+        if self.kind == "decode":
+            pairs = int(self.seq_lens.sum())
+        else:
+            pairs = 0
+            for c, p in zip(self.layout.cached_lens.tolist(), self.layout.tail_lens.tolist()):
+                pairs += p * c + p * (p + 1) // 2
+        return 4 * self.head_dim * pairs * self.num_q_heads
+
+
+def _shape_of(case):
+    lay = case.layout
+    nq = lay.batch if case.kind == "decode" else int(lay.tail_lens.sum())
+    nnew = int(lay.tail_lens.sum())
+    return ((nq, case.num_q_heads, case.head_dim),
+            (lay.num_blocks, case.num_kv_heads, BLOCK, case.head_dim),
+            (nnew, case.num_kv_heads, case.head_dim))
+
+
+def materialize_numpy(case):
+    """Draw the case's values on the host with numpy (seeded)."""
+    rng = np.random.default_rng(case.seed + 1000)
+    qs, ps, ns = _shape_of(case)
+
+    def draw(shape, std):
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        return x if case.dtype == F32 else f32_to_bf16_bits(x)
+
+    case.q = draw(qs, case.q_std)
+    case.k_pool = draw(ps, case.kv_std)
+    case.v_pool = draw(ps, case.kv_std)
+    case.k_new = draw(ns, case.kv_std)
+    case.v_new = draw(ns, case.kv_std)
+    return case
+
+
+def materialize_torch(case, device):
+    """Draw the case's values directly in device memory with torch (seeded).
+
+    Used for the full-size workloads, whose pools are gigabytes.
+    """
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(case.seed + 2000)
+    qs, ps, ns = _shape_of(case)
+    tdt = torch.float32 if case.dtype == F32 else torch.bfloat16
+
+    def draw(shape, std):
+        x = torch.empty(shape, dtype=torch.float32, device=device)
+        x.normal_(0.0, std, generator=gen)
+        return x if tdt == torch.float32 else x.to(tdt)
+
+    case.q = draw(qs, case.q_std)
+    case.k_pool = draw(ps, case.kv_std)
+    case.v_pool = draw(ps, case.kv_std)
+    case.k_new = draw(ns, case.kv_std)
+    case.v_new = draw(ns, case.kv_std)
+    return case
+
+
+def to_float(arr, dtype):
+    """Host float32 view of a case value (bf16 bits widened exactly)."""
+    try:
+        import torch
+        if isinstance(arr, torch.Tensor):
+            t = arr.detach()
+            if t.dtype == torch.bfloat16:
+                return bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16))
+            return t.float().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.asarray(arr)
+    return bf16_bits_to_f32(a) if dtype == BF16 else a.astype(np.float32)
+
+
+# ------------------------------------------------------------ the workloads
+def tiny_decode(seed=1, layer=0, swap_docs=False):
+    """Tiny fp32 decode step, one layer of the 4-layer / 4-head / d_h=16 model.
+
+    Two 16-token documents stored position-free and placed at positions 0 and
+    16 (swapped order with swap_docs); 32 cached tokens; the new query at
+    position 32 appends its own K/V and attends 33 tokens.  theta = 1e4,
+    q, K, V ~ N(0, 1).  Each layer is an independent draw.
+    """
+    rng = np.random.default_rng(seed * 100 + layer)
+    order = [1, 0] if swap_docs else [0, 1]
+    lay = build_layout(rng, [order], [16, 16], [1], offsets=[[0, 16]])
+    case = Case("tiny_fp32_decode", "decode", F32, 4, 4, 16, 1.0e4, lay,
+                q_std=1.0, kv_std=1.0, seed=seed * 100 + layer)
+    return case
+
+
+def decode_case(seed, batch, num_q_heads, num_kv_heads, head_dim, ctx, doc_blocks=(16, 128),
+                dtype=BF16, theta=5.0e5, offsets="contiguous", new_token=True, name="decode",
+                kv_std=0.5):
+    """Decode batch whose sequences are cached documents filling ctx tokens each.
+
+    ctx may be an int or a per-sequence list; documents have lengths
+    16 * U{doc_blocks}; only the last document of a sequence is truncated to
+    hit ctx exactly (ctx not a multiple of 16 gives a ragged last block when
+    new_token is False).  offsets="random" places documents at arbitrary,
+    non-contiguous positions instead of prefix sums.
+    """
+    rng = np.random.default_rng(seed)
+    ctxs = [ctx] * batch if np.isscalar(ctx) else list(ctx)
+    seq_docs, doc_lens, offs = [], [], []
+    for b in range(batch):
+        c = int(ctxs[b])
+        if new_token and c % BLOCK:
+            raise ValueError("with a new token the cached context must fill whole blocks")
+        lens = _docs_filling(rng, c, *doc_blocks) if c else []
+        ids = list(range(len(doc_lens), len(doc_lens) + len(lens)))
+        doc_lens.extend(lens)
+        seq_docs.append(ids)
+        if offsets == "random":
+            offs.append([int(x) for x in rng.integers(0, 60000 - 2048, size=len(lens))])
+    tails = [1 if new_token else 0] * batch
+    tail_pos = None
+    if offsets == "random":
+        tail_pos = [int(x) for x in rng.integers(0, 60000, size=batch)]
+    lay = build_layout(rng, seq_docs, doc_lens, tails,
+                       offsets=offs if offsets == "random" else None, tail_pos=tail_pos)
+    return Case(name, "decode", dtype, num_q_heads, num_kv_heads, head_dim, theta, lay,
+                kv_std=kv_std, seed=seed)
+
+
+def llama8b_decode(seed=2, batch=64, ctx=8192):
+    """Llama-3.1-8B-shaped single-layer decode, bf16: 32 q / 8 KV heads, d_h=128.
+
+    64 sequences of 8192 cached tokens built from documents of 256..2048
+    tokens in 16-token blocks shuffled in a pool; the new token (position
+    8192) is appended and attends 8193 tokens.  K, V ~ N(0,1)*0.5,
+    theta = 5e5.
+    """
+    return decode_case(seed, batch, 32, 8, 128, ctx, (16, 128), name="llama8b_decode")
+
+
+def llama70b_decode(seed=4, batch=16, ctx=32768, docs=(16, 64)):
+    """Llama-3.1-70B-shaped single-layer decode, bf16: 64 q / 8 KV heads (GQA 8).
+
+    16 sequences of 32768 cached tokens cut at block granularity into
+    U{16..64} documents each; the new token at position 32768 is appended.
+    """
+    rng = np.random.default_rng(seed)
+    seq_docs, doc_lens = [], []
+    for _ in range(batch):
+        parts = int(rng.integers(docs[0], docs[1] + 1))
+        lens = _split_into(rng, ctx // BLOCK, parts)
+        seq_docs.append(list(range(len(doc_lens), len(doc_lens) + len(lens))))
+        doc_lens.extend(lens)
+    lay = build_layout(rng, seq_docs, doc_lens, [1] * batch)
+    return Case("llama70b_decode", "decode", BF16, 64, 8, 128, 5.0e5, lay, seed=seed)
+
+
+def zipf_decode(seed=5, batch=128, catalogue=1000, zipf_s=1.2, docs_per_seq=(4, 8),
+                doc_blocks=(16, 128)):
+    """Zipf document-reuse decode mix, bf16, 8B shape.
+
+    A catalogue of 1000 documents (16 * U{16..128} tokens); each of the 128
+    sequences draws U{4..8} distinct documents with p(rank i) ~ i^-1.2 and
+    places them contiguously in random order.  A document drawn by several
+    sequences is stored once and its blocks are shared zero-copy.
+    """
+    rng = np.random.default_rng(seed)
+    doc_lens = [BLOCK * int(x) for x in rng.integers(doc_blocks[0], doc_blocks[1] + 1, size=catalogue)]
+    p = np.arange(1, catalogue + 1, dtype=np.float64) ** (-zipf_s)
+    p /= p.sum()
+    seq_docs = []
+    for _ in range(batch):
+        k = int(rng.integers(docs_per_seq[0], docs_per_seq[1] + 1))
+        seq_docs.append([int(d) for d in rng.choice(catalogue, size=k, replace=False, p=p)])
+    lay = build_layout(rng, seq_docs, doc_lens, [1] * batch)
+    return Case("zipf_reuse_decode", "decode", BF16, 32, 8, 128, 5.0e5, lay, seed=seed)
+
+
+def prefill_case(seed, batch, num_q_heads, num_kv_heads, head_dim, cached, prompt,
+                 doc_blocks=(16, 128), dtype=BF16, theta=5.0e5, offsets="contiguous",
+                 name="prefill"):
+    """Prefill batch: cached documents then a prompt that is appended and attends.
+
+    cached / prompt may be ints or per-sequence lists.  The prompt's blocks
+    carry the prompt's first position as offset (contiguous after the
+    documents unless offsets="random").
+    """
+    rng = np.random.default_rng(seed)
+    cs = [cached] * batch if np.isscalar(cached) else list(cached)
+    ps = [prompt] * batch if np.isscalar(prompt) else list(prompt)
+    seq_docs, doc_lens, offs, tpos = [], [], [], []
+    for b in range(batch):
+        if cs[b] % BLOCK:
+            raise ValueError("cached documents must fill whole blocks")
+        lens = _docs_filling(rng, int(cs[b]), *doc_blocks) if cs[b] else []
+        seq_docs.append(list(range(len(doc_lens), len(doc_lens) + len(lens))))
+        doc_lens.extend(lens)
+        if offsets == "random":
+            offs.append([int(x) for x in rng.integers(0, 30000, size=len(lens))])
+            tpos.append(int(rng.integers(0, 30000)))
+    lay = build_layout(rng, seq_docs, doc_lens, ps,
+                       offsets=offs if offsets == "random" else None,
+                       tail_pos=tpos if offsets == "random" else None)
+    return Case(name, "prefill", dtype, num_q_heads, num_kv_heads, head_dim, theta, lay, seed=seed)
+
+
+def llama8b_prefill(seed=3, batch=4, cached=6144, prompt=2048):
+    """Llama-3.1-8B-shaped single-layer prefill, bf16: 32 q / 8 KV heads, d_h=128.
+
+    4 sequences; 6144 cached document tokens (documents of 256..2048 tokens)
+    followed by a 2048-token prompt at position 6144 that is appended and
+    attends causally (query tiles of 128).  theta = 5e5.
+    """
+    return prefill_case(seed, batch, 32, 8, 128, cached, prompt, name="llama8b_prefill")
+
+
+WORKLOADS = {
+    "tiny_fp32_decode": tiny_decode,
+    "llama8b_decode": llama8b_decode,
+    "llama8b_prefill": llama8b_prefill,
+    "llama70b_decode": llama70b_decode,
+    "zipf_reuse_decode": zipf_decode,
+}
+
+
+def make(name, **kw) -> Case:
+    return WORKLOADS[name](**kw)
+
+
+__all__ = [
+    "BLOCK", "F32", "BF16", "Case", "Layout", "build_layout", "pack_words",
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "to_float", "materialize_numpy",
+    "materialize_torch", "decode_case", "prefill_case", "tiny_decode",
+    "llama8b_decode", "llama8b_prefill", "llama70b_decode", "zipf_decode", "make",
+    "WORKLOADS",
+]
