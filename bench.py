@@ -1,0 +1,283 @@
+"""Benchmark of the deferred-RoPE paged attention hot path on one MI355X.
+
+One step = one pass over the whole path on synthetic, HBM-resident inputs:
+  decode pass : kvcache_append of the 64 new tokens, then lazyattn_decode over
+                the Llama-3.1-8B-shaped batch (64 x 8193 tokens, 32 q / 8 KV
+                heads, d_h 128, bf16, documents of 256..2048 tokens);
+  prefill pass: kvcache_append of the 4 x 2048 prompt tokens, then
+                lazyattn_prefill against 6144 cached document tokens each.
+Prints one JSON line.  `value` is the decode pass's KV throughput (logical K+V
+bytes of the attended tokens / decode-pass time); the prefill attention
+TFLOP/s rides along.  Kernel durations come from HIP events recorded on the
+stream the library launches on (torch's current stream).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "decode KV GB/s (% HBM peak) + prefill attn TFLOP/s, 8B-shape lazy-RoPE"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_SOURCES = ["position_agnostic_kv_amd/csrc/decode.hip", "position_agnostic_kv_amd/csrc/common.h"]
+PREFILL_SOURCES = ["position_agnostic_kv_amd/csrc/prefill.hip", "position_agnostic_kv_amd/csrc/common.h"]
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name, sources):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None
+    if it is missing or the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{name}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash(sources):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def decode_algorithmic_bytes(case):
+    """K+V of every attended token once, plus q in, out, table words and lengths."""
+    esz = 2
+    d, hq, hkv = case.head_dim, case.num_q_heads, case.num_kv_heads
+    tokens = int(case.seq_lens.sum())
+    kv = tokens * hkv * d * 2 * esz
+    qo = case.batch * hq * d * esz * 2
+    table = int(sum(-(-int(n) // 16) for n in case.seq_lens)) * 4 + case.batch * 8
+    return kv, kv + qo + table
+
+
+def cpu_baseline_decode(case, dc, seconds):
+    """The oracle, single-threaded, on whole (sequence, KV head) groups of the
+    same workload until `seconds` of CPU work; scaled to GB/s of K+V."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    import workloads as W
+    import torch
+    lay = case.layout
+    q = W.to_float(case.q, case.dtype)
+    g = case.num_q_heads // case.num_kv_heads
+    done_bytes, groups, t_used = 0, 0, 0.0
+    with threadpool_limits(1):
+        for b in range(case.batch):
+            nb = -(-int(case.seq_lens[b]) // 16)
+            ids = (lay.table[b, :nb] & 0xFFFF).astype(np.int64)
+            sel = torch.from_numpy(ids).to(dc.k_pool.device)
+            kp = W.to_float(dc.k_pool.index_select(0, sel), case.dtype)
+            vp = W.to_float(dc.v_pool.index_select(0, sel), case.dtype)
+            row = ((lay.table[b, :nb] & 0xFFFF0000) | np.arange(nb, dtype=np.uint32)).astype(np.uint32)
+            for kvh in range(case.num_kv_heads):
+                t0 = time.perf_counter()
+                k_hat, v_hat = oracle.materialize_sequence(kp, vp, row, int(case.seq_lens[b]), kvh,
+                                                           case.rope_theta)
+                qr = oracle.rope(q[b, kvh * g:(kvh + 1) * g], int(case.q_pos[b]), case.rope_theta)
+                p = oracle.softmax(case.scale * (qr @ k_hat.T))
+                _ = p @ v_hat
+                t_used += time.perf_counter() - t0
+                done_bytes += int(case.seq_lens[b]) * case.head_dim * 2 * 2
+                groups += 1
+                if t_used >= seconds:
+                    break
+            if t_used >= seconds:
+                break
+    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{groups} (sequence, KV head) groups of llama8b_decode "
+                      f"({groups * g} query heads x 8193 tokens), {t_used:.1f} s, float64 numpy, 1 thread"}
+
+
+def cpu_baseline_prefill(case, dc, seconds):
+    """The oracle on prompt rows of one (sequence, head) of the prefill workload."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    import workloads as W
+    import torch
+    lay = case.layout
+    b, h = 0, 0
+    g = case.num_q_heads // case.num_kv_heads
+    nb = -(-int(case.seq_lens[b]) // 16)
+    ids = (lay.table[b, :nb] & 0xFFFF).astype(np.int64)
+    sel = torch.from_numpy(ids).to(dc.k_pool.device)
+    kp = W.to_float(dc.k_pool.index_select(0, sel), case.dtype)
+    vp = W.to_float(dc.v_pool.index_select(0, sel), case.dtype)
+    row = ((lay.table[b, :nb] & 0xFFFF0000) | np.arange(nb, dtype=np.uint32)).astype(np.uint32)
+    q = W.to_float(case.q, case.dtype)
+    plen = case.max_q_len
+    kv_len = int(case.seq_lens[b])
+    cached = kv_len - plen
+    flops, t_used, rows_done = 0, 0.0, 0
+    with threadpool_limits(1):
+        for r0 in range(0, plen, 128):
+            rows = np.arange(r0, min(plen, r0 + 128))
+            t0 = time.perf_counter()
+            oracle.prefill_rows(q[rows, h], rows, plen, int(lay.tail_pos[b]), kp, vp, row, kv_len,
+                                h // g, case.scale, case.rope_theta)
+            t_used += time.perf_counter() - t0
+            flops += 4 * case.head_dim * int(np.sum(cached + rows + 1))
+            rows_done += len(rows)
+            if t_used >= seconds:
+                break
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows_done} prompt rows of one (sequence, head) of llama8b_prefill, "
+                      f"{t_used:.1f} s, float64 numpy, 1 thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-blocks", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for rocprofv3 counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import position_agnostic_kv_amd as pak
+    import workloads as W
+    from workloads.device import DeviceInputs
+
+    pak.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    dcase = W.llama8b_decode()
+    pcase = W.llama8b_prefill()
+    W.materialize_torch(dcase, dev)
+    W.materialize_torch(pcase, dev)
+    dd = DeviceInputs(dcase, dev)
+    pd = DeviceInputs(pcase, dev)
+    ws_bytes = pak.decode_workspace_size(dcase.batch, dcase.num_q_heads, dcase.num_kv_heads,
+                                         dcase.head_dim, dcase.layout.table.shape[1], args.split_blocks)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    dout = torch.empty_like(dd.q)
+    pout = torch.empty_like(pd.q)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pak.kvcache_append(dd.k_pool, dd.v_pool, dd.k_new, dd.v_new, dd.slots)
+        if ev is not None:
+            ev[1].record()
+        pak.lazyattn_decode(dd.q, dd.q_pos, dd.k_pool, dd.v_pool, dd.table, dd.seq_lens,
+                            scale=dcase.scale, rope_theta=dcase.rope_theta,
+                            split_blocks=args.split_blocks, out=dout, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+        pak.kvcache_append(pd.k_pool, pd.v_pool, pd.k_new, pd.v_new, pd.slots)
+        if ev is not None:
+            ev[3].record()
+        pak.lazyattn_prefill(pd.q, pd.cu, pd.q_pos_start, pd.k_pool, pd.v_pool, pd.table, pd.seq_lens,
+                             pcase.max_q_len, scale=pcase.scale, rope_theta=pcase.rope_theta, out=pout)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def mean_ms(i, j):
+        return float(np.mean([e[i].elapsed_time(e[j]) for e in events]))
+
+    decode_pass_ms = mean_ms(0, 2)
+    decode_kernel_ms = mean_ms(1, 2)
+    prefill_kernel_ms = mean_ms(3, 4)
+    prefill_pass_ms = mean_ms(2, 4)
+    step_ms = mean_ms(0, 4)
+
+    kv_bytes, dec_alg_bytes = decode_algorithmic_bytes(dcase)
+    value = kv_bytes / (decode_pass_ms * 1e-3) / 1e9
+    dec_achieved = dec_alg_bytes / (decode_kernel_ms * 1e-3) / 1e9
+    flops = pcase.attention_flops()
+    pf_tflops = flops / (prefill_kernel_ms * 1e-3) / 1e12
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama8b_decode + llama8b_prefill",
+            "decode": {"batch": dcase.batch, "tokens_per_seq": int(dcase.seq_lens[0]), "q_heads": 32,
+                       "kv_heads": 8, "head_dim": 128, "kv_bytes": kv_bytes, "docs_tokens": "256..2048"},
+            "prefill": {"batch": pcase.batch, "cached_tokens": 6144, "prompt_tokens": 2048, "q_heads": 32,
+                        "kv_heads": 8, "head_dim": 128, "attention_flops": flops, "q_tile": 128},
+        },
+        "decode_pass_ms": round(decode_pass_ms, 4),
+        "decode_kernel_ms": round(decode_kernel_ms, 4),
+        "prefill_pass_ms": round(prefill_pass_ms, 4),
+        "prefill_kernel_ms": round(prefill_kernel_ms, 4),
+        "prefill_tflops": round(pf_tflops, 2),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {
+            "kernel": "lazyattn::decode_kernel<bf16,128,4>",
+            "bound": "hbm",
+            "achieved": round(dec_achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(dec_achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic("decode_llama8b", DECODE_SOURCES),
+            "algorithmic_bytes": dec_alg_bytes,
+        },
+        "roofline_prefill": {
+            "kernel": "lazyattn::prefill_kernel<128>",
+            "bound": "mfma",
+            "achieved": round(pf_tflops, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(pf_tflops / BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic("prefill_llama8b", PREFILL_SOURCES),
+            "algorithmic_flops": flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(dcase, dd, args.cpu_seconds)
+        res["cpu_baseline_prefill"] = cpu_baseline_prefill(pcase, pd, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

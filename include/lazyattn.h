@@ -1,0 +1,159 @@
+/*
+ * lazyattn.h -- position-agnostic paged KV attention (deferred RoPE) on gfx950.
+ *
+ * The cache stores keys and values by content only; the rotary position of a
+ * cached document is applied inside the attention kernel, so one physical copy
+ * of a document serves any position without re-encoding (LazyAttention summary
+ * on gist.science, sections "Metodologia" and "Equivalência Matemática").
+ *
+ * Data layout (all device memory, row-major, owned by the caller):
+ *   K/V pool   [num_blocks][num_kv_heads][16][head_dim]   element type `dtype`
+ *   table word uint32: bits 0..15 = physical block id (< num_blocks <= 65536),
+ *              bits 16..31 = the block's position offset (unsigned).
+ *   block_table [batch][max_blocks_per_seq] table words; logical token j of a
+ *              sequence lives in block word[j / 16], slot j % 16.
+ *
+ * Position convention.  A stored key carries the rotation of its place within
+ * its own frame (a document encoded from position 0, or a prompt encoded from
+ * its first position); the block's offset is where that frame starts in the
+ * sequence.  The key a placed token really has is therefore
+ * rot(stored, offset), and a query at absolute position n scores it as
+ * rot(q, n - offset) . stored.  RoPE is the rotate-half form: pairs
+ * (i, i + D/2) turned by the angle p * theta^(-2i/D).  Values never rotate.
+ *
+ * Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is
+ * the null stream), allocate nothing, keep no device state and are
+ * re-entrant.  Argument errors are reported by a negative status before any
+ * launch.  Device-side preconditions (block ids < num_blocks, offsets and
+ * positions < 65536, only a sequence's last block partly filled) are checked
+ * by the kernels where cheap: a sequence whose length is negative or exceeds
+ * 16 * max_blocks_per_seq, or whose table holds a block id >= num_blocks,
+ * gets NaN output instead of touching memory outside the pool.
+ */
+#ifndef LAZYATTN_H
+#define LAZYATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LAZYATTN_BLOCK_TOKENS 16
+#define LAZYATTN_MAX_BLOCKS 65536
+#define LAZYATTN_MAX_POSITION 65535
+
+/* Element type of q, K/V pools, new rows and outputs. */
+enum { LAZYATTN_F32 = 0, LAZYATTN_BF16 = 1 };
+
+/* Status codes. */
+enum {
+  LAZYATTN_OK = 0,
+  LAZYATTN_ERR_NULL = -1,        /* a required pointer is NULL */
+  LAZYATTN_ERR_DTYPE = -2,       /* unknown dtype, or dtype not offered by this call */
+  LAZYATTN_ERR_SHAPE = -3,       /* bad size: head_dim, head counts, num_blocks, ... */
+  LAZYATTN_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+  LAZYATTN_ERR_LAUNCH = -5       /* the HIP launch failed (hipGetLastError) */
+};
+
+/* Text for a status code (static storage). */
+const char *lazyattn_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int lazyattn_version(void);
+
+/*
+ * kvcache_append -- write new content-only K/V rows into pool slots.
+ *
+ * Appending the new rows of K and V to the cache before attending is the
+ * cache step of lynx-cortex "00 — Por qué existe un KV Cache", section
+ * "El remedio"; the per-layer, per-head append of ai-engineering.academy
+ * "KV Cache, Flash Attention & Otimização de Inferência", "Construa" Passo 1.
+ *
+ *   k_pool, v_pool  [num_blocks][num_kv_heads][16][head_dim]   (written)
+ *   k_new, v_new    [num_tokens][num_kv_heads][head_dim]       (read)
+ *   slot_mapping    int32 [num_tokens]: pool slot = block_id * 16 + slot;
+ *                   a slot < 0 or >= 16 * num_blocks is skipped (padding).
+ * Rows are copied bit-exactly, unrotated.  head_dim in {16, 32, 64, 128, 256}.
+ * num_tokens == 0 is a no-op.
+ */
+int kvcache_append(void *k_pool, void *v_pool, int dtype, int num_blocks, int num_kv_heads,
+                   int head_dim, const void *k_new, const void *v_new,
+                   const int32_t *slot_mapping, int num_tokens, void *stream);
+
+/*
+ * Bytes of workspace lazyattn_decode needs for these sizes (split_blocks as
+ * passed to lazyattn_decode; 0 = automatic).  The workspace holds the per-split
+ * partial results (max, sum, unnormalised output) and one arrival counter per
+ * (sequence, KV head).  It must be zero-filled before its first use; every
+ * call leaves the counters at zero again, so a workspace may be reused by
+ * later calls on the same stream without clearing.  Calls that share one
+ * workspace must not overlap.
+ */
+size_t lazyattn_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                      int max_blocks_per_seq, int split_blocks);
+
+/*
+ * lazyattn_decode -- one new query token per sequence against its paged,
+ * position-free cache (LazyAttention summary, "Implementação Técnica",
+ * Decoding: the query is rotated inside the kernel only when the offset
+ * changes, and only K and V are read).
+ *
+ *   out         [batch][num_q_heads][head_dim]  dtype      (written)
+ *   q           [batch][num_q_heads][head_dim]  dtype, raw (unrotated) query
+ *   q_pos       int32 [batch]: absolute position n of each query
+ *   k_pool, v_pool, block_table, max_blocks_per_seq: see the layout above
+ *   seq_lens    int32 [batch]: tokens of the table the query attends (>= 0)
+ *   num_q_heads a multiple of num_kv_heads; query head h reads KV head
+ *               h / (num_q_heads / num_kv_heads); the group size is 1, 2, 4 or 8.
+ *   head_dim    f32: 16, 64 or 128; bf16: 64 or 128.
+ *   scale       softmax scale (usually 1/sqrt(head_dim))
+ *   rope_theta  RoPE base (> 1)
+ *   split_blocks blocks per split-K partition (0 = automatic; else 4..1024)
+ *   workspace   see lazyattn_decode_workspace_size
+ *
+ * out[b][h] = sum_j softmax_j(scale * rot(q, n) . rot(k_j, off_j)) v_j over the
+ * seq_lens[b] tokens, computed with fp32 accumulation; a sequence with
+ * seq_lens[b] == 0 gets zeros.  batch == 0 is a no-op.
+ */
+int lazyattn_decode(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                    const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                    const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                    int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
+                    int split_blocks, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * lazyattn_prefill -- a prompt's queries against cached documents plus the
+ * prompt itself, causal within the prompt (LazyAttention summary,
+ * "Implementação Técnica", Prefilling: query tiles of M = 128 rows, one
+ * relative rotation per tile and document instead of two).
+ *
+ *   out         [total_q][num_q_heads][head_dim]  bf16            (written)
+ *   q           [total_q][num_q_heads][head_dim]  bf16, raw, packed by cu_q_lens
+ *   cu_q_lens   int32 [batch + 1]: prompt b is rows cu_q_lens[b] .. cu_q_lens[b+1]-1
+ *   total_q     rows of q and out; a prompt whose rows fall outside [0, total_q)
+ *               (or with cu_q_lens decreasing) is left unwritten
+ *   q_pos_start int32 [batch]: position of prompt b's first token
+ *   kv_lens     int32 [batch]: tokens in the table INCLUDING the prompt, whose
+ *               K/V must already be appended as the table's last P_b tokens
+ *   max_q_len   >= every prompt length (sizes the launch grid)
+ *   num_q_heads a multiple of num_kv_heads (group size 1..64)
+ *   head_dim    64 or 128; dtype must be LAZYATTN_BF16.
+ *
+ * Prompt row r of sequence b sits at logical index kv_lens[b] - P_b + r and
+ * position q_pos_start[b] + r, and sees the table tokens with logical index
+ * <= its own (masking uses table order, never positions).  bf16 MFMA with
+ * fp32 accumulation; P is rounded to bf16 for the P.V product.
+ */
+int lazyattn_prefill(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                     const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                     const uint32_t *block_table, int max_blocks_per_seq, const int32_t *kv_lens,
+                     int batch, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                     int num_blocks, int dtype, float scale, float rope_theta, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAZYATTN_H */

@@ -186,11 +186,13 @@ def append(k_pool, v_pool, k_new, v_new, slot_mapping):
     [KVF] "Construa", Passo 1 (append per layer/head) and [WHY] "El remedio"
     (add the new row to the cache).  Token t of k_new/v_new [T, Hkv, D] goes
     to block slot_mapping[t] // 16, slot slot_mapping[t] % 16, every head.
-    Slots < 0 are padding and are skipped.  The copy is exact.
+    Slots < 0 are padding and slots past the pool do not exist; both are
+    skipped.  The copy is exact.
     """
     k_out, v_out = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+    capacity = k_out.shape[0] * BLOCK_TOKENS
     for t, slot in enumerate(np.asarray(slot_mapping).tolist()):
-        if slot < 0:
+        if slot < 0 or slot >= capacity:
             continue
         k_out[slot // BLOCK_TOKENS, :, slot % BLOCK_TOKENS, :] = k_new[t]
         v_out[slot // BLOCK_TOKENS, :, slot % BLOCK_TOKENS, :] = v_new[t]

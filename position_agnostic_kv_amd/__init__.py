@@ -1,0 +1,209 @@
+"""Position-agnostic paged KV attention (deferred RoPE) for MI355X / gfx950.
+
+A thin ctypes binding over ``liblazyattn.so`` (C ABI in ``include/lazyattn.h``):
+argument marshalling only.  PyTorch supplies device memory and the current
+stream; every step of the attention runs in the library's HIP kernels.  If the
+library has not been built, every entry point raises -- there is no fallback.
+
+Entry points (same names as the C ABI):
+  kvcache_append(k_pool, v_pool, k_new, v_new, slot_mapping)
+  lazyattn_decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, ...)
+  lazyattn_prefill(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len, ...)
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "LazyAttnError", "lib_path", "load_library", "version", "kvcache_append",
+    "decode_workspace_size", "lazyattn_decode", "lazyattn_prefill", "BLOCK_TOKENS",
+]
+
+BLOCK_TOKENS = 16
+_F32, _BF16 = 0, 1
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblazyattn.so")
+_lib = None
+
+_vp, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+_SIGNATURES = {
+    "lazyattn_status_string": (ctypes.c_char_p, [_i32]),
+    "lazyattn_version": (_i32, []),
+    "kvcache_append": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp]),
+    "lazyattn_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "lazyattn_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                               _i32, _f32, _f32, _i32, _vp, _sz, _vp]),
+    "lazyattn_prefill": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                                _i32, _i32, _i32, _i32, _f32, _f32, _vp]),
+}
+
+
+class LazyAttnError(RuntimeError):
+    pass
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load liblazyattn.so (raises if it is missing: there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise LazyAttnError(
+                f"{_LIB_PATH} is not built; run `python -m position_agnostic_kv_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def version():
+    return load_library().lazyattn_version()
+
+
+def _check(status, what):
+    if status != 0:
+        msg = load_library().lazyattn_status_string(status).decode()
+        raise LazyAttnError(f"{what} failed: {msg} (status {status})")
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return _F32
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    raise LazyAttnError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(*tensors):
+    dev = tensors[0].device
+    for t in tensors:
+        if t.device.type != "cuda":
+            raise LazyAttnError("all tensors must be on the GPU")
+        if t.device != dev:
+            raise LazyAttnError("all tensors must be on the same GPU")
+        if not t.is_contiguous():
+            raise LazyAttnError("all tensors must be contiguous")
+    return dev
+
+
+def _int32(t, name):
+    if t.dtype not in (torch.int32, torch.uint32):
+        raise LazyAttnError(f"{name} must be int32 (uint32 bit patterns for the block table)")
+    return t
+
+
+def _stream_ptr(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def kvcache_append(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
+    """Write rows k_new/v_new [T, Hkv, D] into pool slots (block*16 + slot); < 0 skipped."""
+    dev = _dev(k_pool, v_pool, k_new, v_new, slot_mapping)
+    _int32(slot_mapping, "slot_mapping")
+    nb, hkv, bt, d = k_pool.shape
+    if bt != BLOCK_TOKENS or v_pool.shape != k_pool.shape:
+        raise LazyAttnError("pools must be [num_blocks, num_kv_heads, 16, head_dim]")
+    if k_new.shape != v_new.shape or k_new.shape[1:] != (hkv, d) or k_new.dtype != k_pool.dtype:
+        raise LazyAttnError("k_new/v_new must be [T, num_kv_heads, head_dim] of the pool dtype")
+    if slot_mapping.numel() != k_new.shape[0]:
+        raise LazyAttnError("slot_mapping must have one entry per new row")
+    lib = load_library()
+    _check(lib.kvcache_append(_ptr(k_pool), _ptr(v_pool), _dtype_code(k_pool), nb, hkv, d,
+                              _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), k_new.shape[0],
+                              _stream_ptr(stream, dev)), "kvcache_append")
+
+
+def decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                          split_blocks=0):
+    return int(load_library().lazyattn_decode_workspace_size(
+        batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, split_blocks))
+
+
+def lazyattn_decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, *, scale=None,
+                    rope_theta=10000.0, split_blocks=0, out=None, workspace=None, stream=None):
+    """Decode attention; q [B, Hq, D] raw queries at positions q_pos [B].
+
+    block_table [B, max_blocks] int32/uint32 words (block id | offset << 16);
+    seq_lens [B] tokens attended.  ``workspace`` (uint8, zero-filled once) is
+    allocated zeroed when not given.  Returns out [B, Hq, D] in q's dtype.
+    """
+    dev = _dev(q, q_pos, k_pool, v_pool, block_table, seq_lens)
+    _int32(q_pos, "q_pos")
+    _int32(block_table, "block_table")
+    _int32(seq_lens, "seq_lens")
+    b, hq, d = q.shape
+    nb, hkv, bt, dk = k_pool.shape
+    if bt != BLOCK_TOKENS or dk != d or v_pool.shape != k_pool.shape:
+        raise LazyAttnError("pools must be [num_blocks, num_kv_heads, 16, head_dim]")
+    if q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
+        raise LazyAttnError("q and pools must share a dtype")
+    if block_table.dim() != 2 or block_table.shape[0] != b or q_pos.numel() != b or seq_lens.numel() != b:
+        raise LazyAttnError("block_table [B, max_blocks], q_pos [B], seq_lens [B]")
+    max_blocks = block_table.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, q)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise LazyAttnError("out must match q")
+    need = decode_workspace_size(b, hq, hkv, d, max_blocks, split_blocks) if b else 0
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _dev(workspace, q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load_library()
+    _check(lib.lazyattn_decode(_ptr(out), _ptr(q), _ptr(q_pos), _ptr(k_pool), _ptr(v_pool),
+                               _ptr(block_table), max_blocks, _ptr(seq_lens), b, hq, hkv, d, nb,
+                               _dtype_code(q), scale, float(rope_theta), int(split_blocks),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream_ptr(stream, dev)), "lazyattn_decode")
+    return out
+
+
+def lazyattn_prefill(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len,
+                     *, scale=None, rope_theta=10000.0, out=None, stream=None):
+    """Prefill attention; q [Tq, Hq, D] bf16 packed by cu_q_lens [B+1].
+
+    The prompts' K/V must already be appended as each table's last tokens;
+    kv_lens [B] counts them.  Returns out [Tq, Hq, D] bf16.
+    """
+    dev = _dev(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens)
+    for t, n in ((cu_q_lens, "cu_q_lens"), (q_pos_start, "q_pos_start"), (kv_lens, "kv_lens"),
+                 (block_table, "block_table")):
+        _int32(t, n)
+    tq, hq, d = q.shape
+    nb, hkv, bt, dk = k_pool.shape
+    b = kv_lens.numel()
+    if bt != BLOCK_TOKENS or dk != d or v_pool.shape != k_pool.shape:
+        raise LazyAttnError("pools must be [num_blocks, num_kv_heads, 16, head_dim]")
+    if q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
+        raise LazyAttnError("q and pools must share a dtype")
+    if cu_q_lens.numel() != b + 1 or q_pos_start.numel() != b or block_table.dim() != 2 \
+            or block_table.shape[0] != b:
+        raise LazyAttnError("cu_q_lens [B+1], q_pos_start [B], block_table [B, max_blocks], kv_lens [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, q)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise LazyAttnError("out must match q")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load_library()
+    _check(lib.lazyattn_prefill(_ptr(out), _ptr(q), tq, _ptr(cu_q_lens), _ptr(q_pos_start), _ptr(k_pool),
+                                _ptr(v_pool), _ptr(block_table), block_table.shape[1], _ptr(kv_lens),
+                                b, int(max_q_len), hq, hkv, d, nb, _dtype_code(q), scale,
+                                float(rope_theta), _stream_ptr(stream, dev)), "lazyattn_prefill")
+    return out

@@ -1,0 +1,148 @@
+// C ABI of the lazyattn library: argument checks, then launches on the caller's
+// stream.  Nothing here allocates or synchronises.
+#include "lazyattn.h"
+
+#include <math.h>
+
+#include "launch.h"
+
+using namespace lazyattn;
+
+namespace {
+
+bool valid_dtype(int dtype) { return dtype == LAZYATTN_F32 || dtype == LAZYATTN_BF16; }
+int elem_bytes(int dtype) { return dtype == LAZYATTN_F32 ? 4 : 2; }
+bool pow2_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? LAZYATTN_OK : LAZYATTN_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *lazyattn_status_string(int status) {
+  switch (status) {
+    case LAZYATTN_OK: return "ok";
+    case LAZYATTN_ERR_NULL: return "a required pointer is NULL";
+    case LAZYATTN_ERR_DTYPE: return "unsupported dtype for this call";
+    case LAZYATTN_ERR_SHAPE: return "unsupported or inconsistent size argument";
+    case LAZYATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case LAZYATTN_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int lazyattn_version(void) { return 100; }
+
+int kvcache_append(void *k_pool, void *v_pool, int dtype, int num_blocks, int num_kv_heads,
+                   int head_dim, const void *k_new, const void *v_new,
+                   const int32_t *slot_mapping, int num_tokens, void *stream) {
+  if (!valid_dtype(dtype)) return LAZYATTN_ERR_DTYPE;
+  if (num_tokens < 0 || num_blocks < 1 || num_blocks > LAZYATTN_MAX_BLOCKS || num_kv_heads < 1 ||
+      num_kv_heads > 1024)
+    return LAZYATTN_ERR_SHAPE;
+  if (!(head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256))
+    return LAZYATTN_ERR_SHAPE;
+  if (num_tokens == 0) return LAZYATTN_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return LAZYATTN_ERR_NULL;
+  return from_hip(launch_append(k_pool, v_pool, elem_bytes(dtype), num_blocks, num_kv_heads,
+                                head_dim, k_new, v_new, slot_mapping, num_tokens,
+                                (hipStream_t)stream));
+}
+
+size_t lazyattn_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                      int max_blocks_per_seq, int split_blocks) {
+  if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || head_dim <= 0 ||
+      max_blocks_per_seq <= 0 || split_blocks < 0 || num_q_heads % num_kv_heads)
+    return 0;
+  return decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                               split_blocks);
+}
+
+int lazyattn_decode(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                    const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                    const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                    int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
+                    int split_blocks, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!valid_dtype(dtype)) return LAZYATTN_ERR_DTYPE;
+  if (batch < 0 || batch > 65535 || num_kv_heads < 1 || num_kv_heads > 65535 || num_q_heads < 1 ||
+      num_q_heads % num_kv_heads || !pow2_group(num_q_heads / num_kv_heads))
+    return LAZYATTN_ERR_SHAPE;
+  const bool bf16 = dtype == LAZYATTN_BF16;
+  if (bf16 ? !(head_dim == 64 || head_dim == 128)
+           : !(head_dim == 16 || head_dim == 64 || head_dim == 128))
+    return LAZYATTN_ERR_SHAPE;
+  if (num_blocks < 1 || num_blocks > LAZYATTN_MAX_BLOCKS || max_blocks_per_seq < 1 ||
+      max_blocks_per_seq > LAZYATTN_MAX_POSITION / LAZYATTN_BLOCK_TOKENS + 1)
+    return LAZYATTN_ERR_SHAPE;
+  if (split_blocks != 0 && (split_blocks < 4 || split_blocks > 1024)) return LAZYATTN_ERR_SHAPE;
+  if (!(rope_theta > 1.0f) || !isfinite(rope_theta) || !isfinite(scale)) return LAZYATTN_ERR_SHAPE;
+  if (batch == 0) return LAZYATTN_OK;
+  if (!out || !q || !q_pos || !k_pool || !v_pool || !block_table || !seq_lens)
+    return LAZYATTN_ERR_NULL;
+  const size_t need = decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
+                                            max_blocks_per_seq, split_blocks);
+  if (need && (!workspace || workspace_bytes < need)) return LAZYATTN_ERR_WORKSPACE;
+
+  DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.q_pos = q_pos;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.table = block_table;
+  a.seq_lens = seq_lens;
+  a.workspace = need ? workspace : nullptr;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.split_blocks = decode_split_blocks(batch, num_kv_heads, max_blocks_per_seq, split_blocks);
+  a.scale = scale;
+  a.rope_theta = rope_theta;
+  return from_hip(launch_decode(a, bf16, (hipStream_t)stream));
+}
+
+int lazyattn_prefill(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                     const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                     const uint32_t *block_table, int max_blocks_per_seq, const int32_t *kv_lens,
+                     int batch, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                     int num_blocks, int dtype, float scale, float rope_theta, void *stream) {
+  if (dtype != LAZYATTN_BF16) return LAZYATTN_ERR_DTYPE;
+  if (batch < 0 || batch > 65535 || max_q_len < 0 || max_q_len > LAZYATTN_MAX_POSITION + 1 || total_q < 0 ||
+      num_kv_heads < 1 || num_kv_heads > 65535 || num_q_heads < 1 || num_q_heads % num_kv_heads ||
+      num_q_heads / num_kv_heads > 64)
+    return LAZYATTN_ERR_SHAPE;
+  if (!(head_dim == 64 || head_dim == 128)) return LAZYATTN_ERR_SHAPE;
+  if (num_blocks < 1 || num_blocks > LAZYATTN_MAX_BLOCKS || max_blocks_per_seq < 1 ||
+      max_blocks_per_seq > LAZYATTN_MAX_POSITION / LAZYATTN_BLOCK_TOKENS + 1)
+    return LAZYATTN_ERR_SHAPE;
+  if (!(rope_theta > 1.0f) || !isfinite(rope_theta) || !isfinite(scale)) return LAZYATTN_ERR_SHAPE;
+  if (batch == 0 || max_q_len == 0 || total_q == 0) return LAZYATTN_OK;
+  if (!out || !q || !cu_q_lens || !q_pos_start || !k_pool || !v_pool || !block_table || !kv_lens)
+    return LAZYATTN_ERR_NULL;
+  PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.total_q = total_q;
+  a.cu_q_lens = cu_q_lens;
+  a.q_pos_start = q_pos_start;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.table = block_table;
+  a.kv_lens = kv_lens;
+  a.batch = batch;
+  a.max_q_len = max_q_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.scale = scale;
+  a.rope_theta = rope_theta;
+  return from_hip(launch_prefill(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

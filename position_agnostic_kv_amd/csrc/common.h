@@ -1,0 +1,92 @@
+// Device helpers shared by the lazyattn kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lazyattn {
+
+constexpr int kBlockTokens = 16;
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// bfloat16 storage is handled as raw 16-bit patterns.
+struct bf16 {
+  uint16_t bits;
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Widen the low / high bfloat16 halves of a dword (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round two floats to bfloat16 (nearest even, the hardware conversion) and pack lo | hi << 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Table word: block id in bits 0..15, position offset in bits 16..31.
+__device__ __forceinline__ uint32_t word_block(uint32_t w) { return w & 0xffffu; }
+__device__ __forceinline__ int word_offset(uint32_t w) { return (int)(w >> 16); }
+
+// RoPE frequency theta^(-2i/D) in double precision.
+__device__ __forceinline__ double rope_inv_freq(int i, int head_dim, float theta) {
+  return pow((double)theta, -2.0 * (double)i / (double)head_dim);
+}
+
+// cos/sin of delta * inv_freq, with the angle formed and reduced in double
+// precision (|delta| reaches 65535, where a float angle would be off by ~4e-3 rad).
+__device__ __forceinline__ void rope_cos_sin(int delta, double inv_freq, float &c, float &s) {
+  double sd, cd;
+  sincos((double)delta * inv_freq, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+// Cheaper variant for small angles (|delta * inv_freq| < ~200 rad): the angle is
+// formed and reduced to [-pi, pi] in double, then evaluated in float.
+__device__ __forceinline__ void rope_cos_sin_small(int delta, double inv_freq, float &c, float &s) {
+  const double a = (double)delta * inv_freq;
+  const double k = rint(a * 0.15915494309189535);        // 1 / (2 pi)
+  double r = fma(-k, 6.283185307179586232, a);            // 2 pi, high part
+  r = fma(-k, 2.4492935982947064e-16, r);                 // 2 pi, low part
+  sincosf((float)r, &s, &c);
+}
+
+// ------------------------------------------------------------ cross-lane sums
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppRowMirror = 0x140;     // lane i <-> 15-i within 16
+
+// Sum over aligned groups of N consecutive lanes (N a power of two, <= 64).
+// Every lane of a group gets the bit-identical total (each step pairs lanes
+// symmetrically and float addition is commutative).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp_f32<kDppQuadXor1>(x);
+  if constexpr (N >= 4) x += dpp_f32<kDppQuadXor2>(x);
+  if constexpr (N >= 8) x += dpp_f32<kDppRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp_f32<kDppRowMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Wave-uniform "any lane true".
+__device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
+
+}  // namespace lazyattn

@@ -1,0 +1,468 @@
+// lazyattn_decode: one query token per sequence against a paged, position-free
+// KV cache, split-K over 16-token blocks (flash-decoding).
+//
+// Method (LazyAttention summary on gist.science, "Implementação Técnica",
+// Decoding): the cached keys carry no placement, so the rotation for a
+// document's offset is applied to the *query*, and only when the offset
+// changes (a new document); the kernel reads K and V exactly once and nothing
+// else per block except the packed (block id, offset) word.  The scores
+// rot(q, n - off) . k equal rot(q, n) . rot(k, off) ("Equivalência
+// Matemática"), i.e. attention against the eager position-adjusted copy.
+// Softmax is the running (max, sum) form of ai-engineering.academy
+// "Flash Attention" (the numerical trick), kept per lane stream and merged at
+// the end of each split, then across splits.
+//
+// gfx950 mapping (wave64):
+//   * A K (or V) block of one KV head is 16 rows x D contiguous elements.  A
+//     lane loads 16-byte chunks; LPT = D / (16 B / elem) lanes cover one row,
+//     so one dwordx4 load instruction reads 64 * 16 B = 1 KiB of the block
+//     contiguously, and NI instructions cover the block.
+//   * Each lane holds the rotated query slice for its chunk's dims for all G
+//     query heads of the KV head (grouped-query attention); partial dot products
+//     are summed over the LPT lanes of a row with DPP (quad perms and row
+//     mirrors; no LDS traffic).
+//   * A lane keeps its own running max/sum per head over the rows it sees, so a
+//     block needs no cross-lane max; the rows are merged once per split.  The
+//     max is only raised when a block exceeds it by more than 2^8 (values stay
+//     bounded by 256), which skips almost every rescale of the accumulators.
+//   * The next block's K/V loads are issued before the current block is
+//     computed (one block per wave in flight beyond the one being consumed).
+//   * Splits write (max, sum, unnormalised output) to the workspace; the last
+//     split to arrive for a (sequence, KV head) merges them (log-sum-exp) and
+//     writes the output, then re-arms its counter.  One launch per call.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace lazyattn {
+
+constexpr int kDecodeWaves = 4;
+constexpr float kRescaleSlack = 8.0f;  // in log2 units
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int kPerChunk = 4;
+  static __device__ __forceinline__ float load(const float *p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float *p, size_t i, float x) { p[i] = x; }
+  static __device__ __forceinline__ void unpack(const uint4 &c, float *f) {
+    f[0] = __uint_as_float(c.x);
+    f[1] = __uint_as_float(c.y);
+    f[2] = __uint_as_float(c.z);
+    f[3] = __uint_as_float(c.w);
+  }
+};
+template <>
+struct Elem<bf16> {
+  static constexpr int kPerChunk = 8;
+  static __device__ __forceinline__ float load(const bf16 *p, size_t i) {
+    return __uint_as_float((uint32_t)p[i].bits << 16);
+  }
+  static __device__ __forceinline__ void store(bf16 *p, size_t i, float x) {
+    p[i].bits = to_bf16_bits(x);
+  }
+  static __device__ __forceinline__ void unpack(const uint4 &c, float *f) {
+    f[0] = bf16_lo(c.x);
+    f[1] = bf16_hi(c.x);
+    f[2] = bf16_lo(c.y);
+    f[3] = bf16_hi(c.y);
+    f[4] = bf16_lo(c.z);
+    f[5] = bf16_hi(c.z);
+    f[6] = bf16_lo(c.w);
+    f[7] = bf16_hi(c.w);
+  }
+};
+
+struct DecodeKernelArgs {
+  void *out;
+  const void *q;
+  const int32_t *q_pos;
+  const uint4 *k_pool;
+  const uint4 *v_pool;
+  const uint32_t *table;
+  const int32_t *seq_lens;
+  float *ws_o;       // [B][Hkv][S][G][D]
+  float2 *ws_ml;     // [B][Hkv][S][G] (max, sum)
+  uint32_t *ws_cnt;  // [B][Hkv]
+  int max_blocks, num_kv_heads, num_blocks, split_blocks, max_splits;
+  float scale_log2, rope_theta;
+};
+
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(kDecodeWaves * kWave)
+decode_kernel(const DecodeKernelArgs a) {
+  using E = Elem<T>;
+  constexpr int EPL = E::kPerChunk;        // elements per 16-byte chunk
+  constexpr int LPT = D / EPL;             // lanes per token row
+  constexpr int TPI = kWave / LPT;         // token rows per load instruction
+  constexpr int NI = kBlockTokens / TPI;   // load instructions per block
+  constexpr int HALF = D / 2;
+  constexpr int NT = kDecodeWaves * kWave;
+  static_assert(LPT >= 4 && LPT <= kWave && TPI <= kBlockTokens, "unsupported head geometry");
+
+  __shared__ float s_q[G][D];
+  __shared__ float s_m[kDecodeWaves][G];
+  __shared__ float s_l[kDecodeWaves][G];
+  __shared__ float s_o[kDecodeWaves][G][D];
+  __shared__ int s_bad;
+  __shared__ int s_last;
+
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int hkv = a.num_kv_heads;
+  const int hq = hkv * G;
+
+  const int seq_len = a.seq_lens[b];
+  const bool bad_len = seq_len < 0 || seq_len > a.max_blocks * kBlockTokens;
+  const int nblk = bad_len ? 0 : (seq_len + kBlockTokens - 1) / kBlockTokens;
+  const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
+  T *out = (T *)a.out + ((size_t)b * hq + (size_t)g * G) * D;
+
+  if (nsplit == 0) {  // empty sequence -> zeros; invalid length -> NaN
+    if (split == 0)
+      for (int i = tid; i < G * D; i += NT) E::store(out, i, bad_len ? __builtin_nanf("") : 0.f);
+    return;
+  }
+  if (split >= nsplit) return;
+
+  const T *qg = (const T *)a.q + ((size_t)b * hq + (size_t)g * G) * D;
+  for (int i = tid; i < G * D; i += NT) s_q[i / D][i % D] = E::load(qg, i);
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+
+  const int n_pos = a.q_pos[b];
+  const int c = lane % LPT;
+  const int r = lane / LPT;
+  const int d0 = c * EPL;
+  const bool upper = d0 >= HALF;
+  const int pd0 = upper ? d0 - HALF : d0 + HALF;
+  const double inv_freq = lane < HALF ? rope_inv_freq(lane, D, a.rope_theta) : 0.0;
+
+  float qr[G][EPL];
+  float acc[G][EPL];
+  float m[G], l[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  const int blk0 = split * a.split_blocks;
+  const int blk1 = min(nblk, blk0 + a.split_blocks);
+  const uint32_t *trow = a.table + (size_t)b * a.max_blocks;
+  constexpr size_t kChunksPerHeadBlock = (size_t)kBlockTokens * LPT;
+  bool bad = false;
+  int cur_off = -1;
+
+  auto issue = [&](int bk, uint32_t &w, uint4 (&kk)[NI], uint4 (&vv)[NI]) {
+    w = trow[bk];
+    uint32_t id = word_block(w);
+    if (id >= (uint32_t)a.num_blocks) {  // table points outside the pool
+      bad = true;
+      id = 0;
+    }
+    const size_t base = ((size_t)id * hkv + g) * kChunksPerHeadBlock + lane;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kk[i] = a.k_pool[base + (size_t)i * kWave];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) vv[i] = a.v_pool[base + (size_t)i * kWave];
+  };
+
+  // q' = rot(q, n - off) * scale * log2(e), for this lane's dims and all G heads.
+  auto rotate = [&](int delta) {
+    float cs = 0.f, sn = 0.f;
+    if (lane < HALF) rope_cos_sin(delta, inv_freq, cs, sn);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int fi = (d0 + e) % HALF;
+      const float ce = __shfl(cs, fi);
+      const float se = __shfl(sn, fi);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float x = s_q[h][d0 + e];
+        const float y = s_q[h][pd0 + e];
+        const float rot = upper ? fmaf(x, ce, y * se) : fmaf(x, ce, -(y * se));
+        qr[h][e] = rot * a.scale_log2;
+      }
+    }
+  };
+
+  int blk = blk0 + wave;
+  uint32_t wcur = 0;
+  uint4 kc[NI], vc[NI];
+  if (blk < blk1) issue(blk, wcur, kc, vc);
+  while (blk < blk1) {
+    const int nb = blk + kDecodeWaves;
+    uint32_t wn = 0;
+    uint4 kn[NI], vn[NI];
+    if (nb < blk1) issue(nb, wn, kn, vn);
+
+    const int off = word_offset(wcur);
+    if (off != cur_off) {
+      rotate(n_pos - off);
+      cur_off = off;
+    }
+
+    // scores (log2 units) of this lane's NI rows for every head
+    float s[NI][G];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float kf[EPL];
+      E::unpack(kc[i], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) t = fmaf(qr[h][e], kf[e], t);
+        s[i][h] = group_sum<LPT>(t);
+      }
+    }
+    const int nvalid = seq_len - blk * kBlockTokens;
+    if (nvalid < kBlockTokens) {  // last, partly filled block
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        if (i * TPI + r >= nvalid) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) s[i][h] = -INFINITY;
+          vc[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    }
+
+    float bm[G];
+    bool need = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      bm[h] = s[0][h];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) bm[h] = fmaxf(bm[h], s[i][h]);
+      need |= bm[h] > m[h] + kRescaleSlack;
+    }
+    if (wave_any(need)) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mn = fmaxf(m[h], bm[h]);
+        const float alpha = mn == -INFINITY ? 1.f : exp2f(m[h] - mn);
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+        m[h] = mn;
+      }
+    }
+
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float vf[EPL];
+      E::unpack(vc[i], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float ms = m[h] == -INFINITY ? 0.f : m[h];
+        const float p = exp2f(s[i][h] - ms);
+        l[h] += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+      }
+    }
+
+    wcur = wn;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      kc[i] = kn[i];
+      vc[i] = vn[i];
+    }
+    blk = nb;
+  }
+
+  // merge the TPI row streams of this wave (lanes with equal c)
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mx = m[h];
+#pragma unroll
+    for (int x = LPT; x < kWave; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
+    const float f = mx == -INFINITY ? 0.f : exp2f(m[h] - mx);
+    float lw = l[h] * f;
+#pragma unroll
+    for (int x = LPT; x < kWave; x <<= 1) lw += __shfl_xor(lw, x);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float v = acc[h][e] * f;
+#pragma unroll
+      for (int x = LPT; x < kWave; x <<= 1) v += __shfl_xor(v, x);
+      acc[h][e] = v;
+    }
+    m[h] = mx;
+    l[h] = lw;
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_o[wave][h][d0 + e] = acc[h][e];
+      if (c == 0) {
+        s_m[wave][h] = m[h];
+        s_l[wave][h] = l[h];
+      }
+    }
+  }
+  if (bad) s_bad = 1;
+  __syncthreads();
+
+  // merge the waves
+  const bool single = nsplit == 1;
+  const bool flagged = s_bad != 0;
+  const size_t part = ((size_t)b * hkv + g) * a.max_splits;
+  for (int i = tid; i < G * D; i += NT) {
+    const int h = i / D, d = i % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
+    float o = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float f = s_m[w][h] == -INFINITY ? 0.f : exp2f(s_m[w][h] - mx);
+      o = fmaf(s_o[w][h][d], f, o);
+      lsum = fmaf(s_l[w][h], f, lsum);
+    }
+    if (flagged) {
+      o = __builtin_nanf("");
+      lsum = __builtin_nanf("");
+    }
+    if (single) {
+      E::store(out, i, o / lsum);
+    } else {
+      a.ws_o[(part + split) * G * D + i] = o;
+      if (d == 0) a.ws_ml[(part + split) * G + h] = make_float2(mx, lsum);
+    }
+  }
+  if (single) return;
+
+  // the last split to arrive merges all partial results
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&a.ws_cnt[(size_t)b * hkv + g], 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (uint32_t)(nsplit - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const float *po = a.ws_o + part * G * D;
+  const float2 *pml = a.ws_ml + part * G;
+  for (int i = tid; i < G * D; i += NT) {
+    const int h = i / D;
+    float mx = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, pml[sp * G + h].x);
+    float o = 0.f, lsum = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float2 ml = pml[sp * G + h];
+      const float f = exp2f(ml.x - mx);
+      o = fmaf(po[(size_t)sp * G * D + i], f, o);
+      lsum = fmaf(ml.y, f, lsum);
+    }
+    E::store(out, i, o / lsum);
+  }
+  if (tid == 0)
+    __hip_atomic_store(&a.ws_cnt[(size_t)b * hkv + g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------- host side
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int decode_split_blocks(int batch, int num_kv_heads, int max_blocks_per_seq, int requested) {
+  if (requested > 0) return requested;
+  // Aim at roughly 4096 workgroups for a full batch (16 per CU on 256 CUs), with
+  // splits of 16..256 blocks, a multiple of the wave count.
+  const long long work = (long long)batch * num_kv_heads * max_blocks_per_seq;
+  long long sb = (work + 4095) / 4096;
+  if (sb < 16) sb = 16;
+  if (sb > 256) sb = 256;
+  sb = (sb + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
+  return (int)sb;
+}
+
+static void workspace_layout(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                             int max_blocks, int split_blocks, size_t *off_ml, size_t *off_o,
+                             size_t *total) {
+  const size_t units = (size_t)batch * num_kv_heads;
+  const size_t splits = (size_t)((max_blocks + split_blocks - 1) / split_blocks);
+  const size_t group = (size_t)(num_q_heads / num_kv_heads);
+  *off_ml = align_up(units * sizeof(uint32_t), 256);
+  *off_o = align_up(*off_ml + units * splits * group * sizeof(float2), 256);
+  *total = *off_o + units * splits * group * head_dim * sizeof(float);
+}
+
+size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                             int max_blocks_per_seq, int split_blocks) {
+  const int sb = decode_split_blocks(batch, num_kv_heads, max_blocks_per_seq, split_blocks);
+  if ((max_blocks_per_seq + sb - 1) / sb <= 1) return 0;  // one split: no partials
+  size_t a, b, t;
+  workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sb, &a, &b, &t);
+  return t;
+}
+
+template <typename T, int D, int G>
+static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
+  DecodeKernelArgs k;
+  k.out = a.out;
+  k.q = a.q;
+  k.q_pos = a.q_pos;
+  k.k_pool = (const uint4 *)a.k_pool;
+  k.v_pool = (const uint4 *)a.v_pool;
+  k.table = a.table;
+  k.seq_lens = a.seq_lens;
+  k.max_blocks = a.max_blocks;
+  k.num_kv_heads = a.num_kv_heads;
+  k.num_blocks = a.num_blocks;
+  k.split_blocks = a.split_blocks;
+  k.max_splits = (a.max_blocks + a.split_blocks - 1) / a.split_blocks;
+  k.scale_log2 = a.scale * kLog2e;
+  k.rope_theta = a.rope_theta;
+  size_t off_ml, off_o, total;
+  workspace_layout(a.batch, a.num_q_heads, a.num_kv_heads, a.head_dim, a.max_blocks,
+                   a.split_blocks, &off_ml, &off_o, &total);
+  char *ws = (char *)a.workspace;
+  k.ws_cnt = (uint32_t *)ws;
+  k.ws_ml = ws ? (float2 *)(ws + off_ml) : nullptr;
+  k.ws_o = ws ? (float *)(ws + off_o) : nullptr;
+  const dim3 grid((unsigned)k.max_splits, (unsigned)a.num_kv_heads, (unsigned)a.batch);
+  hipLaunchKernelGGL((decode_kernel<T, D, G>), grid, dim3(kDecodeWaves * kWave), 0, stream, k);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t dispatch_group(const DecodeArgs &a, hipStream_t s) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_decode_t<T, D, 1>(a, s);
+    case 2: return launch_decode_t<T, D, 2>(a, s);
+    case 4: return launch_decode_t<T, D, 4>(a, s);
+    case 8: return launch_decode_t<T, D, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode(const DecodeArgs &a, bool is_bf16, hipStream_t s) {
+  if (is_bf16) {
+    switch (a.head_dim) {
+      case 64: return dispatch_group<bf16, 64>(a, s);
+      case 128: return dispatch_group<bf16, 128>(a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (a.head_dim) {
+    case 16: return dispatch_group<float, 16>(a, s);
+    case 64: return dispatch_group<float, 64>(a, s);
+    case 128: return dispatch_group<float, 128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace lazyattn

@@ -1,0 +1,48 @@
+// Internal launchers behind the C ABI (argument checks happen in abi.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lazyattn {
+
+hipError_t launch_append(void *k_pool, void *v_pool, int elem_bytes, int num_blocks,
+                         int num_kv_heads, int head_dim, const void *k_new, const void *v_new,
+                         const int32_t *slot_mapping, int num_tokens, hipStream_t stream);
+
+// Blocks per split-K partition for a decode launch (requested == 0: automatic).
+int decode_split_blocks(int batch, int num_kv_heads, int max_blocks_per_seq, int requested);
+size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                             int max_blocks_per_seq, int split_blocks);
+
+struct DecodeArgs {
+  void *out;
+  const void *q;
+  const int32_t *q_pos;
+  const void *k_pool;
+  const void *v_pool;
+  const uint32_t *table;
+  const int32_t *seq_lens;
+  void *workspace;
+  int batch, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks;
+  int split_blocks;  // resolved (> 0)
+  float scale, rope_theta;
+};
+hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t stream);
+
+struct PrefillArgs {
+  void *out;
+  const void *q;
+  const int32_t *cu_q_lens;
+  const int32_t *q_pos_start;
+  const void *k_pool;
+  const void *v_pool;
+  const uint32_t *table;
+  const int32_t *kv_lens;
+  int total_q, batch, max_q_len, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks;
+  float scale, rope_theta;
+};
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+}  // namespace lazyattn

@@ -278,15 +278,15 @@ def check_append(O):
     k_before, v_before = k_pool.copy(), v_pool.copy()
     k_new = rng.standard_normal((5, 2, 8)).astype(np.float32)
     v_new = rng.standard_normal((5, 2, 8)).astype(np.float32)
-    slots = np.array([0, 17, -1, 63, 35])
+    slots = np.array([0, 17, -1, 63, 64 + 7])  # -1: padding; 71: past the 4-block pool
     k2, v2 = O.append(k_pool, v_pool, k_new, v_new, slots)
     for t, s in enumerate(slots):
-        if s >= 0:
+        if 0 <= s < 64:
             assert np.array_equal(k2[s // 16, :, s % 16], k_new[t]), "append K"
             assert np.array_equal(v2[s // 16, :, s % 16], v_new[t]), "append V"
     touched = np.zeros((4, 16), dtype=bool)
     for s in slots:
-        if s >= 0:
+        if 0 <= s < 64:
             touched[s // 16, s % 16] = True
     for blk in range(4):
         for sl in range(16):

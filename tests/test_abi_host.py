@@ -1,0 +1,110 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/lazyattn.h declares, and rejects bad arguments with the
+documented status codes before any launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lazyattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import position_agnostic_kv_amd as pak
+    if not os.path.exists(pak.lib_path()):
+        from position_agnostic_kv_amd import build
+        build.build()
+    return pak.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("kvcache_append", "lazyattn_decode", "lazyattn_prefill"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} is declared in lazyattn.h but not exported"
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.lazyattn_status_string(code)
+    assert lib.lazyattn_version() >= 100
+
+
+NULL = ctypes.c_void_p(0)
+P = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def decode(lib, **kw):
+    a = dict(out=P, q=P, q_pos=P, k=P, v=P, table=P, max_blocks=4, seq_lens=P, batch=2, hq=8, hkv=2,
+             d=128, nb=16, dtype=1, scale=0.088, theta=1e4, split=0, ws=P, ws_bytes=1 << 30, stream=NULL)
+    a.update(kw)
+    return lib.lazyattn_decode(a["out"], a["q"], a["q_pos"], a["k"], a["v"], a["table"], a["max_blocks"],
+                               a["seq_lens"], a["batch"], a["hq"], a["hkv"], a["d"], a["nb"], a["dtype"],
+                               a["scale"], a["theta"], a["split"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_decode_argument_errors(lib):
+    assert decode(lib, dtype=7) == -2
+    assert decode(lib, hq=6, hkv=4) == -3          # not a multiple
+    assert decode(lib, hq=24, hkv=2) == -3         # group 12 not offered
+    assert decode(lib, d=96) == -3
+    assert decode(lib, d=16) == -3                 # bf16 needs 64/128
+    assert decode(lib, nb=65537) == -3
+    assert decode(lib, split=2) == -3
+    assert decode(lib, theta=1.0) == -3
+    assert decode(lib, q=NULL) == -1
+    assert decode(lib, batch=0, q=NULL) == 0       # empty batch: no-op before pointer checks
+    assert decode(lib, ws=NULL, max_blocks=4000) == -4
+    assert decode(lib, ws_bytes=16, max_blocks=4000) == -4
+
+
+def test_workspace_size(lib):
+    ws = lib.lazyattn_decode_workspace_size
+    assert ws(1, 4, 4, 16, 3, 0) == 0                   # one split: no partials
+    small = ws(64, 32, 8, 128, 513, 64)
+    big = ws(64, 32, 8, 128, 513, 16)
+    splits = -(-513 // 64)
+    assert small >= 64 * 8 * splits * 4 * (128 * 4 + 8) + 64 * 8 * 4
+    assert big > small
+    assert ws(0, 4, 4, 16, 3, 0) == 0
+
+
+def test_prefill_and_append_argument_errors(lib):
+    f = lib.lazyattn_prefill
+    ok = [P, P, 4096, P, P, P, P, P, 8, P, 2, 128, 32, 8, 128, 64, 1, 0.088, 5e5, NULL]
+    bad_dtype = list(ok)
+    bad_dtype[16] = 0
+    assert f(*bad_dtype) == -2                      # fp32 prefill not offered
+    bad_d = list(ok)
+    bad_d[14] = 256
+    assert f(*bad_d) == -3
+    bad_tq = list(ok)
+    bad_tq[2] = -1
+    assert f(*bad_tq) == -3
+    null_q = list(ok)
+    null_q[1] = NULL
+    assert f(*null_q) == -1
+    empty = list(ok)
+    empty[10] = 0
+    empty[1] = NULL
+    assert f(*empty) == 0
+    a = lib.kvcache_append
+    assert a(P, P, 3, 16, 8, 128, P, P, P, 4, NULL) == -2
+    assert a(P, P, 1, 16, 8, 100, P, P, P, 4, NULL) == -3
+    assert a(P, P, 1, 16, 8, 128, P, P, NULL, 4, NULL) == -1
+    assert a(NULL, NULL, 1, 16, 8, 128, NULL, NULL, NULL, 0, NULL) == 0

@@ -1,0 +1,303 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Small cases compare every output element; the full-size workloads (run in the
+launch configuration bench.py times) compare sampled (sequence, head) rows,
+which the oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_helpers import (DeviceCase, assert_parity, host_pools_after_append, oracle_decode,
+                               oracle_prefill, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode_case(case, split_blocks=0, label=None):
+    label = label or case.name
+    say(f"[decode] {label} B={case.batch} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
+        f"D={case.head_dim} {case.dtype} split={split_blocks}")
+    W.materialize_numpy(case)
+    dc = DeviceCase(case)
+    dc.append()
+    out = dc.decode(split_blocks=split_blocks)
+    torch.cuda.synchronize()
+    got = W.to_float(out, case.dtype)
+    want = oracle_decode(case)
+    assert_parity(got, want, case.dtype, label)
+    return dc, out
+
+
+# ------------------------------------------------------------------ append
+@pytest.mark.parametrize("dtype,d", [(W.F32, 16), (W.BF16, 128), (W.BF16, 64), (W.F32, 128)])
+def test_append_bit_exact(dtype, d):
+    say(f"[append] {dtype} D={d}")
+    rng = np.random.default_rng(7)
+    case = W.Case("append", "decode", dtype, 4, 2, d, 1e4,
+                  W.build_layout(rng, [[0], [1]], [32, 48], [20, 5]), seed=7)
+    W.materialize_numpy(case)
+    dc = DeviceCase(case)
+    # a padding slot (-1) and a slot past the pool are skipped
+    slots = case.layout.slot_mapping.copy()
+    slots[3] = -1
+    slots[7] = case.layout.num_blocks * 16 + 5
+    dc.slots = torch.from_numpy(slots).to("cuda:0")
+    case.layout.slot_mapping = slots
+    dc.append()
+    torch.cuda.synchronize()
+    kw, vw = host_pools_after_append(case)
+    kg = W.to_float(dc.k_pool, dtype)
+    vg = W.to_float(dc.v_pool, dtype)
+    assert np.array_equal(kg.view(np.uint32), kw.astype(np.float32).view(np.uint32))
+    assert np.array_equal(vg.view(np.uint32), vw.astype(np.float32).view(np.uint32))
+
+
+# -------------------------------------------------------------- decode small
+@pytest.mark.parametrize("layer", range(4))
+@pytest.mark.parametrize("swap", [False, True])
+def test_decode_tiny_fp32(layer, swap):
+    """Tiny fp32 decode step: 4 layers x 4 heads, d_h=16, two 16-token docs at 0 and 16."""
+    run_decode_case(W.tiny_decode(layer=layer, swap_docs=swap), label=f"tiny L{layer} swap={swap}")
+
+
+DECODE_SMALL = [
+    # dtype, D, Hq, Hkv, ctx list, doc_blocks, offsets, split
+    (W.BF16, 128, 8, 2, [640, 1024, 208], (2, 20), "contiguous", 4),
+    (W.BF16, 128, 8, 2, [640, 1024, 208], (2, 20), "contiguous", 0),
+    (W.BF16, 128, 32, 8, [512, 96], (4, 12), "random", 8),
+    (W.BF16, 128, 8, 8, [400, 16, 1008], (1, 30), "contiguous", 4),
+    (W.BF16, 128, 16, 2, [784, 320], (3, 9), "random", 4),
+    (W.BF16, 64, 8, 4, [672, 48], (2, 10), "contiguous", 4),
+    (W.BF16, 64, 16, 2, [320], (2, 10), "random", 0),
+    (W.F32, 16, 4, 4, [32, 96, 400], (1, 4), "contiguous", 4),
+    (W.F32, 64, 8, 2, [512, 80], (2, 8), "random", 4),
+    (W.F32, 128, 8, 1, [384, 208], (2, 8), "contiguous", 4),
+    (W.F32, 128, 8, 4, [256], (2, 8), "random", 0),
+]
+
+
+@pytest.mark.parametrize("dtype,d,hq,hkv,ctx,docs,offs,split", DECODE_SMALL)
+def test_decode_small(dtype, d, hq, hkv, ctx, docs, offs, split):
+    case = W.decode_case(11 + d + hq, len(ctx), hq, hkv, d, ctx, docs, dtype=dtype, offsets=offs)
+    run_decode_case(case, split, label=f"{dtype} D{d} G{hq // hkv} {offs} split{split}")
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_decode_ragged_no_append_poisoned_slots(dtype):
+    """Lengths not a multiple of 16 and NaN in the unused slots of last blocks."""
+    case = W.decode_case(31, 3, 8, 2, 128, [1000, 17, 333], (2, 12), dtype=dtype, new_token=False)
+    W.materialize_numpy(case)
+    lay = case.layout
+    nan_bits = np.uint16(0x7fc0) if dtype == W.BF16 else np.float32(np.nan)
+    for b in range(case.batch):
+        n = int(lay.cached_lens[b])
+        if n % 16:
+            blk = int(lay.table[b, n // 16]) & 0xFFFF
+            case.k_pool[blk, :, n % 16:, :] = nan_bits
+            case.v_pool[blk, :, n % 16:, :] = nan_bits
+    dc = DeviceCase(case)
+    out = dc.decode(split_blocks=4)
+    torch.cuda.synchronize()
+    kp, vp = W.to_float(case.k_pool, dtype), W.to_float(case.v_pool, dtype)
+    want = oracle.decode(W.to_float(case.q, dtype), case.q_pos, kp, vp, lay.table, case.seq_lens,
+                         case.scale, case.rope_theta)
+    assert_parity(W.to_float(out, dtype), want, dtype, f"ragged+poison {dtype}")
+
+
+def test_decode_split_and_shuffle_invariance():
+    case = W.decode_case(41, 2, 16, 4, 128, [1504, 800], (3, 20))
+    W.materialize_numpy(case)
+    dc = DeviceCase(case)
+    dc.append()
+    want = oracle_decode(case)
+    outs = {}
+    for split in (4, 8, 16, 64, 128):
+        outs[split] = W.to_float(dc.decode(split_blocks=split), case.dtype)
+        assert_parity(outs[split], want, case.dtype, f"split {split}")
+    # physical placement must not matter: permute the pool and remap the table
+    nb = case.layout.num_blocks
+    perm = np.random.default_rng(5).permutation(nb)
+    inv = np.argsort(perm)
+    kp2 = dc.k_pool[torch.from_numpy(perm).cuda()].contiguous()
+    vp2 = dc.v_pool[torch.from_numpy(perm).cuda()].contiguous()
+    tab = case.layout.table.copy()
+    ids = tab & 0xFFFF
+    tab = (tab & 0xFFFF0000) | inv[ids].astype(np.uint32)
+    dc2 = DeviceCase(case)
+    dc2.k_pool, dc2.v_pool = kp2, vp2
+    dc2.table = torch.from_numpy(tab.view(np.int32)).cuda()
+    out2 = W.to_float(dc2.decode(split_blocks=8), case.dtype)
+    torch.cuda.synchronize()
+    assert np.array_equal(out2, outs[8]), "block shuffle changed the result"
+
+
+def test_decode_workspace_reuse_and_degenerate_lengths():
+    case = W.decode_case(51, 4, 8, 2, 128, [800, 800, 800, 800], (2, 20), dtype=W.F32)
+    W.materialize_numpy(case)
+    dc = DeviceCase(case)
+    dc.append()
+    import position_agnostic_kv_amd as pak
+    need = pak.decode_workspace_size(4, 8, 2, 128, case.layout.table.shape[1], 4)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    a = dc.decode(split_blocks=4, workspace=ws).clone()
+    b = dc.decode(split_blocks=4, workspace=ws).clone()
+    assert torch.equal(a, b), "a reused workspace changed the result"
+    lens = torch.tensor([1, 0, -3, 801], dtype=torch.int32, device="cuda:0")
+    out = dc.decode(split_blocks=4, workspace=ws, seq_lens=lens)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    vp = W.to_float(case.v_pool, case.dtype)
+    first = int(case.layout.table[0, 0]) & 0xFFFF
+    for h in range(8):
+        assert np.array_equal(o[0, h], vp[first, h // 4, 0]), "single token must return its value exactly"
+    assert np.all(o[1] == 0), "empty sequence must give zeros"
+    assert np.all(np.isnan(o[2])), "negative length must give NaN"
+    # a table entry pointing past the pool poisons only its own sequence
+    tab = dc.table.clone()
+    tab[3, 2] = (tab[3, 2] & ~0xFFFF) | 0xFFF0
+    out = pak.lazyattn_decode(dc.q, dc.q_pos, dc.k_pool, dc.v_pool, tab, dc.seq_lens,
+                              scale=case.scale, rope_theta=case.rope_theta, split_blocks=4, workspace=ws)
+    o2 = out.cpu().numpy()
+    assert np.all(np.isnan(o2[3])) and np.all(np.isfinite(o2[:3]))
+    c = dc.decode(split_blocks=4, workspace=ws)
+    assert torch.equal(c, a), "workspace counters were not re-armed after a poisoned call"
+
+
+# ------------------------------------------------------------- prefill small
+PREFILL_SMALL = [
+    # D, Hq, Hkv, cached, prompt, docs, offsets
+    (128, 8, 2, [224, 640], [300, 129], (2, 20), "contiguous"),
+    (128, 32, 8, [512], [256], (4, 12), "contiguous"),
+    (128, 4, 4, [0, 96], [77, 200], (1, 4), "random"),
+    (128, 16, 2, [1056], [64], (3, 40), "random"),
+    (64, 8, 4, [320, 48], [150, 31], (2, 10), "contiguous"),
+    (64, 8, 1, [160], [260], (2, 5), "random"),
+]
+
+
+@pytest.mark.parametrize("d,hq,hkv,cached,prompt,docs,offs", PREFILL_SMALL)
+def test_prefill_small(d, hq, hkv, cached, prompt, docs, offs):
+    case = W.prefill_case(61 + d + hq, len(prompt), hq, hkv, d, cached, prompt, docs, offsets=offs)
+    say(f"[prefill] D{d} Hq{hq} Hkv{hkv} cached={cached} prompt={prompt} {offs}")
+    W.materialize_numpy(case)
+    dc = DeviceCase(case)
+    dc.append()
+    out = dc.prefill()
+    torch.cuda.synchronize()
+    want = oracle_prefill(case)
+    assert_parity(W.to_float(out, case.dtype), want, case.dtype, f"prefill D{d} G{hq // hkv} {offs}")
+
+
+def test_incremental_decode_matches_prefill_rows():
+    """Decoding row t after the prompt is appended equals prefill row t."""
+    case = W.prefill_case(71, 1, 8, 2, 128, [400 - 400 % 16], [150], (2, 10))
+    W.materialize_numpy(case)
+    dc = DeviceCase(case)
+    dc.append()
+    pre = W.to_float(dc.prefill(), case.dtype)
+    p = 150
+    c0 = int(case.layout.cached_lens[0])
+    rows = [0, 1, 63, 64, 127, 128, 149]
+    qd = dc.q[rows].contiguous()
+    tab = dc.table.repeat(len(rows), 1).contiguous()
+    lens = torch.tensor([c0 + r + 1 for r in rows], dtype=torch.int32, device="cuda:0")
+    qpos = torch.tensor([int(case.layout.tail_pos[0]) + r for r in rows], dtype=torch.int32, device="cuda:0")
+    import position_agnostic_kv_amd as pak
+    dec = pak.lazyattn_decode(qd, qpos, dc.k_pool, dc.v_pool, tab, lens, scale=case.scale,
+                              rope_theta=case.rope_theta)
+    dec = W.to_float(dec, case.dtype)
+    assert_parity(dec, pre[rows], W.BF16, "decode rows vs prefill rows")
+    assert p == case.max_q_len
+
+
+# ------------------------------------------------------- full-size workloads
+def _gather(dc, case, seqs):
+    """Host copies of the blocks the sampled sequences use, ids remapped."""
+    lay = case.layout
+    ids = []
+    for b in seqs:
+        nb = -(-int(case.seq_lens[b]) // 16)
+        ids.extend((lay.table[b, :nb] & 0xFFFF).tolist())
+    uniq = np.unique(np.array(ids, dtype=np.int64))
+    remap = {int(x): i for i, x in enumerate(uniq)}
+    sel = torch.from_numpy(uniq).to("cuda:0")
+    kp = W.to_float(dc.k_pool.index_select(0, sel), case.dtype)
+    vp = W.to_float(dc.v_pool.index_select(0, sel), case.dtype)
+    tab = np.zeros((len(seqs), lay.table.shape[1]), dtype=np.uint32)
+    for i, b in enumerate(seqs):
+        nb = -(-int(case.seq_lens[b]) // 16)
+        for j in range(nb):
+            w = int(lay.table[b, j])
+            tab[i, j] = (w & 0xFFFF0000) | remap[w & 0xFFFF]
+    return kp, vp, tab
+
+
+@pytest.mark.parametrize("name", ["llama8b_decode", "llama70b_decode", "zipf_reuse_decode"])
+def test_full_size_decode_sampled(name):
+    case = W.make(name)
+    say(f"[full decode] {name} B={case.batch} NB={case.layout.num_blocks}")
+    W.materialize_torch(case, "cuda:0")
+    dc = DeviceCase(case)
+    dc.append()
+    out = dc.decode()  # automatic split, as bench.py runs it
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(3)
+    seqs = sorted(rng.choice(case.batch, size=min(4, case.batch), replace=False).tolist())
+    kp, vp, tab = _gather(dc, case, seqs)   # pools after the device append
+    q = W.to_float(case.q, case.dtype)
+    got = W.to_float(out, case.dtype)
+    g = case.num_q_heads // case.num_kv_heads
+    rows_got, rows_want = [], []
+    for i, b in enumerate(seqs):
+        for h in rng.choice(case.num_q_heads, size=3, replace=False).tolist():
+            want = oracle.decode_one(q[b, h], int(case.q_pos[b]), kp, vp, tab[i], int(case.seq_lens[b]),
+                                     h // g, case.scale, case.rope_theta)
+            rows_got.append(got[b, h])
+            rows_want.append(want)
+    assert_parity(np.stack(rows_got), np.stack(rows_want), case.dtype, f"{name} sampled")
+
+
+def test_full_size_append_bit_exact_sampled():
+    case = W.make("llama8b_prefill")
+    W.materialize_torch(case, "cuda:0")
+    dc = DeviceCase(case)
+    dc.append()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    for t in rng.choice(len(case.layout.slot_mapping), size=64, replace=False).tolist():
+        s = int(case.layout.slot_mapping[t])
+        assert torch.equal(dc.k_pool[s // 16, :, s % 16], dc.k_new[t])
+        assert torch.equal(dc.v_pool[s // 16, :, s % 16], dc.v_new[t])
+
+
+def test_full_size_prefill_sampled():
+    case = W.make("llama8b_prefill")
+    say(f"[full prefill] B={case.batch} prompt={case.max_q_len}")
+    W.materialize_torch(case, "cuda:0")
+    dc = DeviceCase(case)
+    dc.append()
+    out = dc.prefill()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(4)
+    seqs = [0, 3]
+    kp, vp, tab = _gather(dc, case, seqs)
+    q = W.to_float(case.q, case.dtype)
+    got = W.to_float(out, case.dtype)
+    g = case.num_q_heads // case.num_kv_heads
+    rows = np.array([0, 1, 2, 127, 128, 129, 1023, 1024, 2046, 2047])
+    gots, wants = [], []
+    for i, b in enumerate(seqs):
+        q0 = int(case.cu_q_lens[b])
+        for h in rng.choice(case.num_q_heads, size=3, replace=False).tolist():
+            want = oracle.prefill_rows(q[q0 + rows, h], rows, case.max_q_len, int(case.layout.tail_pos[b]),
+                                       kp, vp, tab[i], int(case.seq_lens[b]), h // g, case.scale,
+                                       case.rope_theta)
+            gots.append(got[q0 + rows, h])
+            wants.append(want)
+    assert_parity(np.concatenate(gots), np.concatenate(wants), case.dtype, "llama8b_prefill sampled")
