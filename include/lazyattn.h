@@ -85,11 +85,10 @@ int kvcache_append(void *k_pool, void *v_pool, int dtype, int num_blocks, int nu
 /*
  * Bytes of workspace lazyattn_decode needs for these sizes (split_blocks as
  * passed to lazyattn_decode; 0 = automatic).  The workspace holds the per-split
- * partial results (max, sum, unnormalised output) and one arrival counter per
- * (sequence, KV head).  It must be zero-filled before its first use; every
- * call leaves the counters at zero again, so a workspace may be reused by
- * later calls on the same stream without clearing.  Calls that share one
- * workspace must not overlap.
+ * partial results (max, sum, unnormalised output) of sequences split over
+ * several workgroups; it needs no initialisation.  0 means the call uses none
+ * (every sequence fits one split) and workspace may be NULL.  Calls that share
+ * one workspace must not overlap.
  */
 size_t lazyattn_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                       int max_blocks_per_seq, int split_blocks);
@@ -110,7 +109,9 @@ size_t lazyattn_decode_workspace_size(int batch, int num_q_heads, int num_kv_hea
  *   head_dim    f32: 16, 64 or 128; bf16: 64 or 128.
  *   scale       softmax scale (usually 1/sqrt(head_dim))
  *   rope_theta  RoPE base (> 1)
- *   split_blocks blocks per split-K partition (0 = automatic; else 4..1024)
+ *   split_blocks blocks per split-K partition (0 = automatic; else 4..1024).
+ *               A sequence longer than one partition is split over several
+ *               workgroups whose partial results a second kernel merges.
  *   workspace   see lazyattn_decode_workspace_size
  *
  * out[b][h] = sum_j softmax_j(scale * rot(q, n) . rot(k_j, off_j)) v_j over the

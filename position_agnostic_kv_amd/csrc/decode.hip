@@ -4,8 +4,8 @@
 // Method (LazyAttention summary on gist.science, "Implementação Técnica",
 // Decoding): the cached keys carry no placement, so the rotation for a
 // document's offset is applied to the *query*, and only when the offset
-// changes (a new document); the kernel reads K and V exactly once and nothing
-// else per block except the packed (block id, offset) word.  The scores
+// changes (a new document); the kernel reads K and V exactly once and, per
+// block, only the packed (block id, offset) word besides.  The scores
 // rot(q, n - off) . k equal rot(q, n) . rot(k, off) ("Equivalência
 // Matemática"), i.e. attention against the eager position-adjusted copy.
 // Softmax is the running (max, sum) form of ai-engineering.academy
@@ -18,18 +18,23 @@
 //     so one dwordx4 load instruction reads 64 * 16 B = 1 KiB of the block
 //     contiguously, and NI instructions cover the block.
 //   * Each lane holds the rotated query slice for its chunk's dims for all G
-//     query heads of the KV head (grouped-query attention); partial dot products
-//     are summed over the LPT lanes of a row with DPP (quad perms and row
-//     mirrors; no LDS traffic).
+//     query heads of the KV head (grouped-query attention).  For bf16 the
+//     slice is kept as packed bf16 pairs and both products use
+//     v_dot2_f32_bf16 (two multiply-adds per instruction, fp32 accumulate):
+//     Q.K pairs along the head dimension, P.V pairs two token rows (P rounded
+//     to bf16, as the MFMA prefill does).  Partial dot products are summed
+//     over the LPT lanes of a row with DPP (quad perms, row mirrors).
 //   * A lane keeps its own running max/sum per head over the rows it sees, so a
 //     block needs no cross-lane max; the rows are merged once per split.  The
 //     max is only raised when a block exceeds it by more than 2^8 (values stay
 //     bounded by 256), which skips almost every rescale of the accumulators.
 //   * The next block's K/V loads are issued before the current block is
-//     computed (one block per wave in flight beyond the one being consumed).
-//   * Splits write (max, sum, unnormalised output) to the workspace; the last
-//     split to arrive for a (sequence, KV head) merges them (log-sum-exp) and
-//     writes the output, then re-arms its counter.  One launch per call.
+//     computed.
+//   * A sequence split over several workgroups writes per-split (max, sum,
+//     unnormalised output) to the workspace and a second, small kernel merges
+//     them (log-sum-exp).  The kernel boundary orders the two; no device-scope
+//     fence is used (on gfx950 one costs an L2 write-back).  A sequence with one
+//     split writes its output directly.
 #include <math.h>
 
 #include "common.h"
@@ -47,12 +52,6 @@ struct Elem<float> {
   static constexpr int kPerChunk = 4;
   static __device__ __forceinline__ float load(const float *p, size_t i) { return p[i]; }
   static __device__ __forceinline__ void store(float *p, size_t i, float x) { p[i] = x; }
-  static __device__ __forceinline__ void unpack(const uint4 &c, float *f) {
-    f[0] = __uint_as_float(c.x);
-    f[1] = __uint_as_float(c.y);
-    f[2] = __uint_as_float(c.z);
-    f[3] = __uint_as_float(c.w);
-  }
 };
 template <>
 struct Elem<bf16> {
@@ -63,17 +62,19 @@ struct Elem<bf16> {
   static __device__ __forceinline__ void store(bf16 *p, size_t i, float x) {
     p[i].bits = to_bf16_bits(x);
   }
-  static __device__ __forceinline__ void unpack(const uint4 &c, float *f) {
-    f[0] = bf16_lo(c.x);
-    f[1] = bf16_hi(c.x);
-    f[2] = bf16_lo(c.y);
-    f[3] = bf16_hi(c.y);
-    f[4] = bf16_lo(c.z);
-    f[5] = bf16_hi(c.z);
-    f[6] = bf16_lo(c.w);
-    f[7] = bf16_hi(c.w);
-  }
 };
+
+__device__ __forceinline__ uint32_t dw(const uint4 &v, int w) {
+  return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 struct DecodeKernelArgs {
   void *out;
@@ -83,17 +84,17 @@ struct DecodeKernelArgs {
   const uint4 *v_pool;
   const uint32_t *table;
   const int32_t *seq_lens;
-  float *ws_o;       // [B][Hkv][S][G][D]
-  float2 *ws_ml;     // [B][Hkv][S][G] (max, sum)
-  uint32_t *ws_cnt;  // [B][Hkv]
+  float *ws_o;    // [B][Hkv][S][G][D]
+  float2 *ws_ml;  // [B][Hkv][S][G] (max, sum)
   int max_blocks, num_kv_heads, num_blocks, split_blocks, max_splits;
   float scale_log2, rope_theta;
 };
 
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(kDecodeWaves * kWave)
-decode_kernel(const DecodeKernelArgs a) {
+decode_split_kernel(const DecodeKernelArgs a) {
   using E = Elem<T>;
+  constexpr bool kBf16 = sizeof(T) == 2;
   constexpr int EPL = E::kPerChunk;        // elements per 16-byte chunk
   constexpr int LPT = D / EPL;             // lanes per token row
   constexpr int TPI = kWave / LPT;         // token rows per load instruction
@@ -101,13 +102,13 @@ decode_kernel(const DecodeKernelArgs a) {
   constexpr int HALF = D / 2;
   constexpr int NT = kDecodeWaves * kWave;
   static_assert(LPT >= 4 && LPT <= kWave && TPI <= kBlockTokens, "unsupported head geometry");
+  static_assert(!kBf16 || NI % 2 == 0, "bf16 P.V pairs token rows");
 
   __shared__ float s_q[G][D];
   __shared__ float s_m[kDecodeWaves][G];
   __shared__ float s_l[kDecodeWaves][G];
   __shared__ float s_o[kDecodeWaves][G][D];
   __shared__ int s_bad;
-  __shared__ int s_last;
 
   const int split = blockIdx.x;
   const int g = blockIdx.y;
@@ -144,7 +145,9 @@ decode_kernel(const DecodeKernelArgs a) {
   const int pd0 = upper ? d0 - HALF : d0 + HALF;
   const double inv_freq = lane < HALF ? rope_inv_freq(lane, D, a.rope_theta) : 0.0;
 
-  float qr[G][EPL];
+  // rotated, pre-scaled query slice: packed bf16 pairs (bf16) or floats (f32)
+  uint32_t qp[G][EPL / 2];
+  float qf[G][kBf16 ? 1 : EPL];
   float acc[G][EPL];
   float m[G], l[G];
 #pragma unroll
@@ -180,6 +183,7 @@ decode_kernel(const DecodeKernelArgs a) {
   auto rotate = [&](int delta) {
     float cs = 0.f, sn = 0.f;
     if (lane < HALF) rope_cos_sin(delta, inv_freq, cs, sn);
+    float rot[G][EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const int fi = (d0 + e) % HALF;
@@ -189,8 +193,17 @@ decode_kernel(const DecodeKernelArgs a) {
       for (int h = 0; h < G; ++h) {
         const float x = s_q[h][d0 + e];
         const float y = s_q[h][pd0 + e];
-        const float rot = upper ? fmaf(x, ce, y * se) : fmaf(x, ce, -(y * se));
-        qr[h][e] = rot * a.scale_log2;
+        rot[h][e] = (upper ? fmaf(x, ce, y * se) : fmaf(x, ce, -(y * se))) * a.scale_log2;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if constexpr (kBf16) {
+#pragma unroll
+        for (int w = 0; w < EPL / 2; ++w) qp[h][w] = pack_bf16x2(rot[h][2 * w], rot[h][2 * w + 1]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qf[h][e] = rot[h][e];
       }
     }
   };
@@ -215,13 +228,16 @@ decode_kernel(const DecodeKernelArgs a) {
     float s[NI][G];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      float kf[EPL];
-      E::unpack(kc[i], kf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float t = 0.f;
+        if constexpr (kBf16) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) t = fmaf(qr[h][e], kf[e], t);
+          for (int w = 0; w < EPL / 2; ++w) t = dot2_bf16(qp[h][w], dw(kc[i], w), t);
+        } else {
+#pragma unroll
+          for (int w = 0; w < EPL; ++w) t = fmaf(qf[h][w], __uint_as_float(dw(kc[i], w)), t);
+        }
         s[i][h] = group_sum<LPT>(t);
       }
     }
@@ -250,7 +266,7 @@ decode_kernel(const DecodeKernelArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float mn = fmaxf(m[h], bm[h]);
-        const float alpha = mn == -INFINITY ? 1.f : exp2f(m[h] - mn);
+        const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[h] - mn);
         l[h] *= alpha;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
@@ -258,18 +274,42 @@ decode_kernel(const DecodeKernelArgs a) {
       }
     }
 
+    float p[NI][G];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float vf[EPL];
-      E::unpack(vc[i], vf);
+    for (int h = 0; h < G; ++h) {
+      const float ms = m[h] == -INFINITY ? 0.f : m[h];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float ms = m[h] == -INFINITY ? 0.f : m[h];
-        const float p = exp2f(s[i][h] - ms);
-        l[h] += p;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+      for (int i = 0; i < NI; ++i) {
+        p[i][h] = fast_exp2(s[i][h] - ms);
+        l[h] += p[i][h];
       }
+    }
+    if constexpr (kBf16) {
+#pragma unroll
+      for (int i = 0; i < NI; i += 2) {
+        uint32_t pp[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) pp[h] = pack_bf16x2(p[i][h], p[i + 1][h]);
+#pragma unroll
+        for (int w = 0; w < EPL / 2; ++w) {
+          const uint32_t v0 = dw(vc[i], w), v1 = dw(vc[i + 1], w);
+          const uint32_t lo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);  // dim 2w of rows i, i+1
+          const uint32_t hi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);  // dim 2w+1
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            acc[h][2 * w] = dot2_bf16(pp[h], lo, acc[h][2 * w]);
+            acc[h][2 * w + 1] = dot2_bf16(pp[h], hi, acc[h][2 * w + 1]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e)
+            acc[h][e] = fmaf(p[i][h], __uint_as_float(dw(vc[i], e)), acc[h][e]);
     }
 
     wcur = wn;
@@ -287,7 +327,7 @@ decode_kernel(const DecodeKernelArgs a) {
     float mx = m[h];
 #pragma unroll
     for (int x = LPT; x < kWave; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
-    const float f = mx == -INFINITY ? 0.f : exp2f(m[h] - mx);
+    const float f = mx == -INFINITY ? 0.f : fast_exp2(m[h] - mx);
     float lw = l[h] * f;
 #pragma unroll
     for (int x = LPT; x < kWave; x <<= 1) lw += __shfl_xor(lw, x);
@@ -315,10 +355,10 @@ decode_kernel(const DecodeKernelArgs a) {
   if (bad) s_bad = 1;
   __syncthreads();
 
-  // merge the waves
+  // merge the waves; one split -> final output, else a partial for the combine kernel
   const bool single = nsplit == 1;
   const bool flagged = s_bad != 0;
-  const size_t part = ((size_t)b * hkv + g) * a.max_splits;
+  const size_t part = ((size_t)b * hkv + g) * a.max_splits + split;
   for (int i = tid; i < G * D; i += NT) {
     const int h = i / D, d = i % D;
     float mx = -INFINITY;
@@ -327,7 +367,7 @@ decode_kernel(const DecodeKernelArgs a) {
     float o = 0.f, lsum = 0.f;
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w) {
-      const float f = s_m[w][h] == -INFINITY ? 0.f : exp2f(s_m[w][h] - mx);
+      const float f = s_m[w][h] == -INFINITY ? 0.f : fast_exp2(s_m[w][h] - mx);
       o = fmaf(s_o[w][h][d], f, o);
       lsum = fmaf(s_l[w][h], f, lsum);
     }
@@ -338,40 +378,42 @@ decode_kernel(const DecodeKernelArgs a) {
     if (single) {
       E::store(out, i, o / lsum);
     } else {
-      a.ws_o[(part + split) * G * D + i] = o;
-      if (d == 0) a.ws_ml[(part + split) * G + h] = make_float2(mx, lsum);
+      a.ws_o[part * G * D + i] = o;
+      if (d == 0) a.ws_ml[part * G + h] = make_float2(mx, lsum);
     }
   }
-  if (single) return;
+}
 
-  // the last split to arrive merges all partial results
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&a.ws_cnt[(size_t)b * hkv + g], 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == (uint32_t)(nsplit - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+// Merge the per-split partials of one (sequence, KV head): log-sum-exp weights.
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256)
+decode_combine_kernel(const DecodeKernelArgs a) {
+  using E = Elem<T>;
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  const int hkv = a.num_kv_heads;
+  const int seq_len = a.seq_lens[b];
+  if (seq_len < 0 || seq_len > a.max_blocks * kBlockTokens) return;  // written by the split kernel
+  const int nblk = (seq_len + kBlockTokens - 1) / kBlockTokens;
+  const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
+  if (nsplit <= 1) return;
+  T *out = (T *)a.out + ((size_t)b * hkv * G + (size_t)g * G) * D;
+  const size_t part = ((size_t)b * hkv + g) * a.max_splits;
   const float *po = a.ws_o + part * G * D;
   const float2 *pml = a.ws_ml + part * G;
-  for (int i = tid; i < G * D; i += NT) {
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
     const int h = i / D;
     float mx = -INFINITY;
     for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, pml[sp * G + h].x);
     float o = 0.f, lsum = 0.f;
     for (int sp = 0; sp < nsplit; ++sp) {
       const float2 ml = pml[sp * G + h];
-      const float f = exp2f(ml.x - mx);
+      const float f = fast_exp2(ml.x - mx);
       o = fmaf(po[(size_t)sp * G * D + i], f, o);
       lsum = fmaf(ml.y, f, lsum);
     }
     E::store(out, i, o / lsum);
   }
-  if (tid == 0)
-    __hip_atomic_store(&a.ws_cnt[(size_t)b * hkv + g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------- host side
@@ -379,24 +421,22 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int decode_split_blocks(int batch, int num_kv_heads, int max_blocks_per_seq, int requested) {
   if (requested > 0) return requested;
-  // Aim at roughly 4096 workgroups for a full batch (16 per CU on 256 CUs), with
-  // splits of 16..256 blocks, a multiple of the wave count.
-  const long long work = (long long)batch * num_kv_heads * max_blocks_per_seq;
-  long long sb = (work + 4095) / 4096;
-  if (sb < 16) sb = 16;
-  if (sb > 256) sb = 256;
+  // Enough (sequence, KV head) units to fill the chip at two workgroups per CU:
+  // one split each.  Otherwise cut sequences so ~1024 workgroups run.
+  const long long units = (long long)batch * num_kv_heads;
+  if (units >= 512) return max_blocks_per_seq;
+  long long sb = (units * max_blocks_per_seq + 1023) / 1024;
+  if (sb < 32) sb = 32;
   sb = (sb + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
   return (int)sb;
 }
 
 static void workspace_layout(int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                             int max_blocks, int split_blocks, size_t *off_ml, size_t *off_o,
-                             size_t *total) {
+                             int max_blocks, int split_blocks, size_t *off_o, size_t *total) {
   const size_t units = (size_t)batch * num_kv_heads;
   const size_t splits = (size_t)((max_blocks + split_blocks - 1) / split_blocks);
   const size_t group = (size_t)(num_q_heads / num_kv_heads);
-  *off_ml = align_up(units * sizeof(uint32_t), 256);
-  *off_o = align_up(*off_ml + units * splits * group * sizeof(float2), 256);
+  *off_o = align_up(units * splits * group * sizeof(float2), 256);
   *total = *off_o + units * splits * group * head_dim * sizeof(float);
 }
 
@@ -404,8 +444,8 @@ size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int h
                              int max_blocks_per_seq, int split_blocks) {
   const int sb = decode_split_blocks(batch, num_kv_heads, max_blocks_per_seq, split_blocks);
   if ((max_blocks_per_seq + sb - 1) / sb <= 1) return 0;  // one split: no partials
-  size_t a, b, t;
-  workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sb, &a, &b, &t);
+  size_t off_o, t;
+  workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sb, &off_o, &t);
   return t;
 }
 
@@ -426,15 +466,18 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   k.max_splits = (a.max_blocks + a.split_blocks - 1) / a.split_blocks;
   k.scale_log2 = a.scale * kLog2e;
   k.rope_theta = a.rope_theta;
-  size_t off_ml, off_o, total;
+  size_t off_o, total;
   workspace_layout(a.batch, a.num_q_heads, a.num_kv_heads, a.head_dim, a.max_blocks,
-                   a.split_blocks, &off_ml, &off_o, &total);
+                   a.split_blocks, &off_o, &total);
   char *ws = (char *)a.workspace;
-  k.ws_cnt = (uint32_t *)ws;
-  k.ws_ml = ws ? (float2 *)(ws + off_ml) : nullptr;
+  k.ws_ml = ws ? (float2 *)ws : nullptr;
   k.ws_o = ws ? (float *)(ws + off_o) : nullptr;
   const dim3 grid((unsigned)k.max_splits, (unsigned)a.num_kv_heads, (unsigned)a.batch);
-  hipLaunchKernelGGL((decode_kernel<T, D, G>), grid, dim3(kDecodeWaves * kWave), 0, stream, k);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, G>), grid, dim3(kDecodeWaves * kWave), 0, stream, k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || k.max_splits <= 1) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D, G>), dim3((unsigned)a.num_kv_heads, (unsigned)a.batch),
+                     dim3(256), 0, stream, k);
   return hipGetLastError();
 }
 
