@@ -253,7 +253,7 @@ def main():
         "prefill_tflops": round(pf_tflops, 2),
         "wall_s_timed": round(wall, 3),
         "roofline": {
-            "kernel": "lazyattn::decode_kernel<bf16,128,4>",
+            "kernel": "lazyattn::decode_split_kernel<bf16, 128, 4>",
             "bound": "hbm",
             "achieved": round(dec_achieved, 1),
             "peak": HBM_PEAK_GBPS,
