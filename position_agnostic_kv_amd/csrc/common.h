@@ -33,6 +33,11 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
+// Dword w (a compile-time constant after unrolling) of a 16-byte chunk.
+__device__ __forceinline__ uint32_t dw4(const uint4 &v, int w) {
+  return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+}
+
 // Table word: block id in bits 0..15, position offset in bits 16..31.
 __device__ __forceinline__ uint32_t word_block(uint32_t w) { return w & 0xffffu; }
 __device__ __forceinline__ int word_offset(uint32_t w) { return (int)(w >> 16); }

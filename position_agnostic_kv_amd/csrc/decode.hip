@@ -64,10 +64,6 @@ struct Elem<bf16> {
   }
 };
 
-__device__ __forceinline__ uint32_t dw(const uint4 &v, int w) {
-  return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
-}
-
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -233,10 +229,10 @@ decode_split_kernel(const DecodeKernelArgs a) {
         float t = 0.f;
         if constexpr (kBf16) {
 #pragma unroll
-          for (int w = 0; w < EPL / 2; ++w) t = dot2_bf16(qp[h][w], dw(kc[i], w), t);
+          for (int w = 0; w < EPL / 2; ++w) t = dot2_bf16(qp[h][w], dw4(kc[i], w), t);
         } else {
 #pragma unroll
-          for (int w = 0; w < EPL; ++w) t = fmaf(qf[h][w], __uint_as_float(dw(kc[i], w)), t);
+          for (int w = 0; w < EPL; ++w) t = fmaf(qf[h][w], __uint_as_float(dw4(kc[i], w)), t);
         }
         s[i][h] = group_sum<LPT>(t);
       }
@@ -292,7 +288,7 @@ decode_split_kernel(const DecodeKernelArgs a) {
         for (int h = 0; h < G; ++h) pp[h] = pack_bf16x2(p[i][h], p[i + 1][h]);
 #pragma unroll
         for (int w = 0; w < EPL / 2; ++w) {
-          const uint32_t v0 = dw(vc[i], w), v1 = dw(vc[i + 1], w);
+          const uint32_t v0 = dw4(vc[i], w), v1 = dw4(vc[i + 1], w);
           const uint32_t lo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);  // dim 2w of rows i, i+1
           const uint32_t hi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);  // dim 2w+1
 #pragma unroll
@@ -309,7 +305,7 @@ decode_split_kernel(const DecodeKernelArgs a) {
         for (int h = 0; h < G; ++h)
 #pragma unroll
           for (int e = 0; e < EPL; ++e)
-            acc[h][e] = fmaf(p[i][h], __uint_as_float(dw(vc[i], e)), acc[h][e]);
+            acc[h][e] = fmaf(p[i][h], __uint_as_float(dw4(vc[i], e)), acc[h][e]);
     }
 
     wcur = wn;

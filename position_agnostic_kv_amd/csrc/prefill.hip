@@ -37,7 +37,7 @@
 namespace lazyattn {
 
 constexpr int kPfWaves = 4;
-constexpr int kPfM = 128;         // query rows per workgroup
+constexpr int kPfRows = 128;      // query rows per workgroup (M)
 constexpr int kPfTileBlocks = 4;  // K/V tile: up to 4 blocks = 64 keys
 constexpr int kPfN = kPfTileBlocks * kBlockTokens;
 constexpr float kPfSlack = 8.0f;
@@ -52,88 +52,144 @@ struct PrefillKernelArgs {
   const uint16_t *v_pool;
   const uint32_t *table;
   const int32_t *kv_lens;
-  int total_q, batch, num_q_heads, num_kv_heads, num_blocks, max_blocks, q_tiles, num_units;
+  int total_q, batch, num_q_heads, num_kv_heads, num_blocks, max_blocks;
+  int head_groups;  // workgroups per KV head (G / HP)
+  int tok_tiles;    // token tiles per sequence
+  int num_units;    // batch * num_kv_heads * head_groups
   float scale_log2, rope_theta;
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-template <int D>
+// A K/V tile: a run of up to 4 table blocks, starting at block j, sharing one offset.
+struct Tile {
+  int j, cnt, off;
+  uint32_t wt[kPfTileBlocks];
+};
+
+__device__ __forceinline__ Tile make_tile(const uint32_t *trow, int j, int nblk) {
+  Tile t;
+  t.j = j;
+#pragma unroll
+  for (int u = 0; u < kPfTileBlocks; ++u) t.wt[u] = (j + u < nblk) ? trow[j + u] : 0u;
+  t.off = word_offset(t.wt[0]);
+  t.cnt = 1;
+#pragma unroll
+  for (int u = 1; u < kPfTileBlocks; ++u)
+    if (t.cnt == u && j + u < nblk && word_offset(t.wt[u]) == t.off) t.cnt = u + 1;
+  return t;
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, output
+// lane i gets element (i % 4) of the 8-byte rows read by source lanes
+// i / 4 + 4k, k = 0..3.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t *)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// HP query heads of one KV head share a workgroup: rows = HP heads x (128 / HP)
+// tokens; wave w owns 32 consecutive rows (one head).
+//
+// K/V tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
+// registers), row-major as in the pool, with the 16-byte chunk index of each
+// row XOR-swizzled by the row so that both operand reads are free of bank
+// conflicts: K rows feed the A operand of S^T = K Q^T with ds_read_b128, V
+// rows feed the A operand of O^T = V^T P^T through two transposing reads.
+// Two buffers: the next tile streams in while the current one is computed.
+template <int D, int HP>
 __global__ void __launch_bounds__(kPfWaves * kWave)
 prefill_kernel(const PrefillKernelArgs a) {
   constexpr int KC = D / 32;          // 32-dim k-chunks of the QK product
   constexpr int DT = D / 16;          // 16-dim m-tiles of O^T
   constexpr int HALF = D / 2;
-  constexpr int KSTR = D + 8;         // sK row stride (bf16)
-  constexpr int VSTR = kPfN + 4;      // sVt row stride (bf16)
-  constexpr int CPR = D / 8;          // 16-byte chunks per key row
-  constexpr int NT = kPfWaves * kWave;
+  constexpr int CPR = D / 8;          // 16-byte chunks per key row (the swizzle period)
+  constexpr int RPI = kWave / CPR;    // rows per 1 KiB load instruction
+  constexpr int IPB = kBlockTokens / RPI;  // load instructions per block (K or V)
+  constexpr int ROWB = D * 2;         // bytes per row
+  constexpr int TILEB = kPfN * ROWB;  // bytes per K (or V) tile
+  constexpr int TOK = kPfRows / HP;   // tokens per workgroup
+  constexpr int WPH = kPfWaves / HP;  // waves per head
   static_assert(D == 64 || D == 128, "head_dim must be 64 or 128");
+  static_assert(HP == 1 || HP == 2 || HP == 4, "1, 2 or 4 heads per workgroup");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kPfN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * VSTR];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILEB / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILEB / 2];
   __shared__ double s_invf[HALF];
+  __shared__ float s_qf[kPfWaves][2 * KC * 8][kWave];  // q_rho per wave, lane-minor
+  __shared__ float s_rot[kPfWaves][2][HALF];          // cos, sin of the current run
   __shared__ int s_bad;
 
-  // ---- work item: heavy-first units of (q tile, sequence, KV head), the G
-  // query heads of a unit consecutive on one XCD
-  const int G = a.num_q_heads / a.num_kv_heads;
+  // ---- work item: the token tiles of one (sequence, KV head, head group) run
+  // consecutively on one XCD (their K/V tiles share its L2), heaviest first
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
-  const int unit = (slot / G) * kXcds + xcd;
+  const int unit = (slot / a.tok_tiles) * kXcds + xcd;
   if (unit >= a.num_units) return;
-  const int hi = slot % G;
-  const int g = unit % a.num_kv_heads;
-  const int rest = unit / a.num_kv_heads;
-  const int b = rest % a.batch;
-  const int qt = a.q_tiles - 1 - rest / a.batch;
-  const int hq = g * G + hi;
+  const int tt = a.tok_tiles - 1 - slot % a.tok_tiles;
+  const int hgrp = unit % a.head_groups;
+  const int g = (unit / a.head_groups) % a.num_kv_heads;
+  const int b = unit / (a.head_groups * a.num_kv_heads);
+  const int G = a.num_q_heads / a.num_kv_heads;
 
   const int q0 = a.cu_q_lens[b];
   const int plen = a.cu_q_lens[b + 1] - q0;
   if (q0 < 0 || plen < 0 || q0 + plen > a.total_q) return;  // rows outside q/out: not written
-  if (qt * kPfM >= plen) return;
+  if (tt * TOK >= plen) return;
   const int kv_len = a.kv_lens[b];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int l16 = lane & 15;
   const int lg = lane >> 4;
+  const int hq = g * G + hgrp * HP + wave / WPH;   // this wave's query head
+  const int tw0 = (wave % WPH) * 32;               // this wave's first token in the tile
 
-  const int rows_valid = min(kPfM, plen - qt * kPfM);
+  const int tok_valid = min(TOK, plen - tt * TOK);
   uint16_t *out = a.out;
   if (plen > kv_len || kv_len > a.max_blocks * kBlockTokens) {  // inconsistent lengths: NaN
-    for (int i = tid; i < rows_valid * D; i += NT) {
-      const int rr = i / D, d = i % D;
-      out[((size_t)(q0 + qt * kPfM + rr) * a.num_q_heads + hq) * D + d] = 0x7fc0;
+    for (int i = lane; i < 32 * D; i += kWave) {
+      const int tk = tw0 + i / D;
+      if (tk < tok_valid)
+        out[((size_t)(q0 + tt * TOK + tk) * a.num_q_heads + hq) * D + i % D] = 0x7fc0;
     }
     return;
   }
 
+  // zero both V buffers once: rows a tile does not load must hold finite values
+  for (int i = tid; i < TILEB / 4; i += kPfWaves * kWave) {
+    ((uint32_t *)sV[0])[i] = 0u;
+    ((uint32_t *)sV[1])[i] = 0u;
+  }
   if (tid < HALF) s_invf[tid] = rope_inv_freq(tid, D, a.rope_theta);
   if (tid == 0) s_bad = 0;
   __syncthreads();
 
-  // ---- query tile: this lane holds rows (nt*16 + l16) of the wave's 32 and the
-  // dims kc*32 + lg*8 + e; q_rho = rot(q, rho), rho = row index inside the tile.
-  float qf[2][KC][8];
+  // ---- query rows: this lane holds tokens tw0 + nt*16 + l16 and the dims
+  // kc*32 + lg*8 + e; q_rho = rot(q, rho), rho = token index inside the tile,
+  // is parked in LDS (it is read again only when a new document starts).
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    const int rho = wave * 32 + nt * 16 + l16;
-    const int row = qt * kPfM + rho;
+    float qf[KC][8];
+    const int rho = tw0 + nt * 16 + l16;
+    const int row = tt * TOK + rho;
     const bool ok = row < plen;
     const uint4 *src = (const uint4 *)(a.q + ((size_t)(q0 + (ok ? row : 0)) * a.num_q_heads + hq) * D);
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       const uint4 v = ok ? src[kc * 4 + lg] : make_uint4(0u, 0u, 0u, 0u);
-      qf[nt][kc][0] = bf16_lo(v.x);
-      qf[nt][kc][1] = bf16_hi(v.x);
-      qf[nt][kc][2] = bf16_lo(v.y);
-      qf[nt][kc][3] = bf16_hi(v.y);
-      qf[nt][kc][4] = bf16_lo(v.z);
-      qf[nt][kc][5] = bf16_hi(v.z);
-      qf[nt][kc][6] = bf16_lo(v.w);
-      qf[nt][kc][7] = bf16_hi(v.w);
+      qf[kc][0] = bf16_lo(v.x);
+      qf[kc][1] = bf16_hi(v.x);
+      qf[kc][2] = bf16_lo(v.y);
+      qf[kc][3] = bf16_hi(v.y);
+      qf[kc][4] = bf16_lo(v.z);
+      qf[kc][5] = bf16_hi(v.z);
+      qf[kc][6] = bf16_lo(v.w);
+      qf[kc][7] = bf16_hi(v.w);
     }
 #pragma unroll
     for (int kc = 0; kc < KC / 2; ++kc) {
@@ -141,20 +197,59 @@ prefill_kernel(const PrefillKernelArgs a) {
       for (int e = 0; e < 8; ++e) {
         float c, s;
         rope_cos_sin_small(rho, s_invf[kc * 32 + lg * 8 + e], c, s);
-        const float x = qf[nt][kc][e], y = qf[nt][kc + KC / 2][e];
-        qf[nt][kc][e] = fmaf(x, c, -(y * s));
-        qf[nt][kc + KC / 2][e] = fmaf(y, c, x * s);
+        const float x = qf[kc][e], y = qf[kc + KC / 2][e];
+        s_qf[wave][(nt * KC + kc) * 8 + e][lane] = fmaf(x, c, -(y * s));
+        s_qf[wave][(nt * KC + kc + KC / 2) * 8 + e][lane] = fmaf(y, c, x * s);
       }
     }
   }
 
-  const int n0 = a.q_pos_start[b] + qt * kPfM;   // position of tile row 0
-  const int t_lo = kv_len - plen + qt * kPfM;    // logical index of tile row 0
-  const int t_hi = t_lo + rows_valid - 1;
-  const int t_wave = t_lo + wave * 32;           // this wave's first row
+  const int n0 = a.q_pos_start[b] + tt * TOK;    // position of tile token 0
+  const int t_lo = kv_len - plen + tt * TOK;     // logical index of tile token 0
+  const int t_hi = t_lo + tok_valid - 1;
+  const int t_wave = t_lo + tw0;                 // this wave's first token
   const int nblk_vis = t_hi / kBlockTokens + 1;
   const uint32_t *trow = a.table + (size_t)b * a.max_blocks;
   const int hkv = a.num_kv_heads;
+
+  // ---- staging: wave w streams block w of the tile (K then V) into LDS.
+  // Lane L of load instruction i fills LDS row r = i*RPI + L/CPR of the block,
+  // chunk slot L % CPR, with global chunk (L % CPR) ^ (r % CPR).
+  const int ld_row = lane / CPR;
+  const int ld_chunk = (lane % CPR);
+  auto issue_tile = [&](const Tile &t, int buf) {
+    if (wave >= t.cnt) return;
+    uint32_t w = t.wt[0];
+#pragma unroll
+    for (int u = 1; u < kPfTileBlocks; ++u)
+      if (wave == u) w = t.wt[u];
+    uint32_t id = word_block(w);
+    if (id >= (uint32_t)a.num_blocks) {
+      s_bad = 1;
+      id = 0;
+    }
+    const uint16_t *kg = a.k_pool + ((size_t)id * hkv + g) * kBlockTokens * D;
+    const uint16_t *vg = a.v_pool + ((size_t)id * hkv + g) * kBlockTokens * D;
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      const int r = i * RPI + ld_row;
+      const int src = r * D + ((ld_chunk ^ (r % CPR)) * 8);
+      const int dst = (wave * kBlockTokens + i * RPI) * D;  // wave-uniform row base
+      __builtin_amdgcn_global_load_lds((const void *)(kg + src), (lds_ptr_t)(&sK[buf][dst]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(vg + src), (lds_ptr_t)(&sV[buf][dst]), 16, 0, 0);
+    }
+  };
+  // after the wave's own loads landed: zero V rows of its block past kv_len
+  auto fix_tail = [&](const Tile &t, int buf) {
+    if (wave >= t.cnt) return;
+    const int key0 = (t.j + wave) * kBlockTokens;
+    const int valid = kv_len - key0;
+    if (valid >= kBlockTokens) return;
+    for (int i = lane; i < kBlockTokens * CPR; i += kWave) {
+      const int r = i / CPR;
+      if (r >= valid) *(uint4 *)(&sV[buf][(wave * kBlockTokens + r) * D + (i % CPR) * 8]) = make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
 
   bf16x8_t bq[2][KC];
   f32x4_t O[DT][2];
@@ -166,80 +261,54 @@ prefill_kernel(const PrefillKernelArgs a) {
   float lsum[2] = {0.f, 0.f};
   int cur_off = -1;
 
-  for (int j = 0; j < nblk_vis;) {
-    // ---- tile = run of up to 4 blocks sharing one offset
-    uint32_t wt[kPfTileBlocks];
-#pragma unroll
-    for (int u = 0; u < kPfTileBlocks; ++u) wt[u] = (j + u < nblk_vis) ? trow[j + u] : 0u;
-    const int off = word_offset(wt[0]);
-    int cnt = 1;
-#pragma unroll
-    for (int u = 1; u < kPfTileBlocks; ++u)
-      if (cnt == u && j + u < nblk_vis && word_offset(wt[u]) == off) cnt = u + 1;
-
-    // ---- stage K (row-major) and V (transposed) into LDS; invalid keys -> 0
+  Tile cur = make_tile(trow, 0, nblk_vis);
+  issue_tile(cur, 0);
+  int buf = 0;
+  for (;;) {
+    // this tile's loads (the only ones in flight) have landed; patch its tail
+    __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) and lgkmcnt(0) on gfx9
+    fix_tail(cur, buf);
     __syncthreads();
-    for (int p = tid; p < 16 * CPR; p += NT) {
-      const int kg = p & 15;        // keys 4kg .. 4kg+3 (all in block kg/4)
-      const int cc = p >> 4;        // dims cc*8 .. cc*8+7
-      const int bt = kg >> 2;
-      uint32_t w = wt[0];
-#pragma unroll
-      for (int u = 1; u < kPfTileBlocks; ++u)
-        if (bt == u) w = wt[u];
-      uint32_t id = word_block(w);
-      const bool blk_ok = bt < cnt;
-      if (blk_ok && id >= (uint32_t)a.num_blocks) {
-        s_bad = 1;
-        id = 0;
-      }
-      const int kbase = (j + bt) * kBlockTokens + (kg & 3) * 4;
-      uint4 kv[4], vv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = blk_ok && kbase + i < kv_len;
-        const size_t idx = (((size_t)id * hkv + g) * kBlockTokens + (kg & 3) * 4 + i) * D + cc * 8;
-        kv[i] = ok ? *(const uint4 *)(a.k_pool + idx) : make_uint4(0u, 0u, 0u, 0u);
-        vv[i] = ok ? *(const uint4 *)(a.v_pool + idx) : make_uint4(0u, 0u, 0u, 0u);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *(uint4 *)(sK + (kg * 4 + i) * KSTR + cc * 8) = kv[i];
-      const uint32_t *v32[4] = {&vv[0].x, &vv[1].x, &vv[2].x, &vv[3].x};
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {  // dims cc*8 + 2*e2 (+1)
-        const uint32_t x0 = v32[0][e2], x1 = v32[1][e2], x2 = v32[2][e2], x3 = v32[3][e2];
-        const uint2 lo = make_uint2((x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16));
-        const uint2 hi2 = make_uint2((x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u));
-        *(uint2 *)(sVt + (cc * 8 + 2 * e2) * VSTR + kg * 4) = lo;
-        *(uint2 *)(sVt + (cc * 8 + 2 * e2 + 1) * VSTR + kg * 4) = hi2;
-      }
+
+    const int jn = cur.j + cur.cnt;
+    const bool more = jn < nblk_vis;
+    Tile nxt;
+    if (more) {
+      nxt = make_tile(trow, jn, nblk_vis);
+      issue_tile(nxt, buf ^ 1);  // streams in while this tile is computed
     }
-    __syncthreads();
 
-    // ---- re-rotate the query tile when the offset changes (a new document)
-    if (off != cur_off) {
-      cur_off = off;
-      float cs = 0.f, sn = 0.f;
-      if (lane < HALF) rope_cos_sin(n0 - off, s_invf[lane], cs, sn);
+    // ---- re-rotate the query rows when the offset changes (a new document)
+    if (cur.off != cur_off) {
+      cur_off = cur.off;
+      if (lane < HALF) {
+        float cs, sn;
+        rope_cos_sin(n0 - cur.off, s_invf[lane], cs, sn);
+        s_rot[wave][0][lane] = cs;
+        s_rot[wave][1][lane] = sn;
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the table is visible to the wave
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int kc = 0; kc < KC / 2; ++kc) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int fi = kc * 32 + lg * 8 + e;
-          const float c = __shfl(cs, fi), s = __shfl(sn, fi);
+          const float c = s_rot[wave][0][fi], s = s_rot[wave][1][fi];
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
-            const float x = qf[nt][kc][e], y = qf[nt][kc + KC / 2][e];
-            const float lo = fmaf(x, c, -(y * s)) * a.scale_log2;
-            const float up = fmaf(y, c, x * s) * a.scale_log2;
-            bq[nt][kc][e] = (__bf16)lo;
-            bq[nt][kc + KC / 2][e] = (__bf16)up;
+            const float x = s_qf[wave][(nt * KC + kc) * 8 + e][lane];
+            const float y = s_qf[wave][(nt * KC + kc + KC / 2) * 8 + e][lane];
+            bq[nt][kc][e] = (__bf16)(fmaf(x, c, -(y * s)) * a.scale_log2);
+            bq[nt][kc + KC / 2][e] = (__bf16)(fmaf(y, c, x * s) * a.scale_log2);
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
 
-    // ---- S^T = K Q^T  (per lane: keys mt*16 + lg*4 + i, query nt*16 + l16)
+    // ---- S^T = K Q^T  (per lane: keys mt*16 + lg*4 + i, token nt*16 + l16)
+    const uint16_t *kb = sK[buf];
     f32x4_t S[kPfTileBlocks][2];
 #pragma unroll
     for (int mt = 0; mt < kPfTileBlocks; ++mt) {
@@ -247,16 +316,17 @@ prefill_kernel(const PrefillKernelArgs a) {
       S[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const bf16x8_t ka = as_bf16x8(*(const uint4 *)(sK + (mt * 16 + l16) * KSTR + kc * 32 + lg * 8));
+        const int row = mt * 16 + l16;
+        const int chunk = (kc * 4 + lg) ^ (row % CPR);
+        const bf16x8_t ka = as_bf16x8(*(const uint4 *)(kb + row * D + chunk * 8));
         S[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bq[0][kc], S[mt][0], 0, 0, 0);
         S[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bq[1][kc], S[mt][1], 0, 0, 0);
       }
     }
 
-    // ---- mask: keys past the tile's run, past kv_len, or after the query
-    const int key0 = j * kBlockTokens;
-    const bool need_mask = cnt < kPfTileBlocks || key0 + kPfN > kv_len || key0 + kPfN - 1 > t_wave;
-    if (need_mask) {
+    // ---- mask: keys past the tile's run, past kv_len, or after the query token
+    const int key0 = cur.j * kBlockTokens;
+    if (cur.cnt < kPfTileBlocks || key0 + kPfN > kv_len || key0 + kPfN - 1 > t_wave) {
 #pragma unroll
       for (int mt = 0; mt < kPfTileBlocks; ++mt)
 #pragma unroll
@@ -265,7 +335,7 @@ prefill_kernel(const PrefillKernelArgs a) {
           for (int i = 0; i < 4; ++i) {
             const int kidx = key0 + mt * 16 + lg * 4 + i;
             const int tq = t_wave + nt * 16 + l16;
-            if (mt >= cnt || kidx >= kv_len || kidx > tq) S[mt][nt][i] = -INFINITY;
+            if (mt >= cur.cnt || kidx >= kv_len || kidx > tq) S[mt][nt][i] = -INFINITY;
           }
     }
 
@@ -274,11 +344,11 @@ prefill_kernel(const PrefillKernelArgs a) {
     bool need = false;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float x = S[0][nt][0];
+      float x = fmaxf(S[0][nt][0], S[0][nt][1]);
 #pragma unroll
       for (int mt = 0; mt < kPfTileBlocks; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x = fmaxf(x, S[mt][nt][i]);
+        for (int i = (mt == 0 ? 2 : 0); i < 4; i += 2) x = fmaxf(x, fmaxf(S[mt][nt][i], S[mt][nt][i + 1]));
       x = fmaxf(x, __shfl_xor(x, 16));
       x = fmaxf(x, __shfl_xor(x, 32));
       bm[nt] = x;
@@ -288,7 +358,7 @@ prefill_kernel(const PrefillKernelArgs a) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const float mn = fmaxf(m[nt], bm[nt]);
-        const float alpha = mn == -INFINITY ? 1.f : exp2f(m[nt] - mn);
+        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[nt] - mn);
         lsum[nt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) O[dt][nt] *= alpha;
@@ -303,30 +373,42 @@ prefill_kernel(const PrefillKernelArgs a) {
       for (int mt = 0; mt < kPfTileBlocks; ++mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(S[mt][nt][i] - ms);
+          const float p = __builtin_amdgcn_exp2f(S[mt][nt][i] - ms);
           lsum[nt] += p;
           bp[mt >> 1][nt][(mt & 1) * 4 + i] = (__bf16)p;
         }
       }
     }
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T: A operand rows = dims, k-slots = keys
+    // 32ks + lg*4 + 0..3 and 32ks + 16 + lg*4 + 0..3, read transposed.
+    const uint16_t *vb = sV[buf];
+    const int trow_k = lg * 4 + (l16 >> 2);  // source key row inside a 16-key group
+    const int tdim = (l16 & 3) * 4;          // source dims (4) inside a 16-dim tile
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
+      const int chunk = (dt * 16 + tdim) / 8;
+      const int half = ((dt * 16 + tdim) % 8) * 2;  // bytes
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const uint16_t *vrow = sVt + (dt * 16 + l16) * VSTR + ks * 32 + lg * 4;
-        const uint2 lo = *(const uint2 *)vrow;
-        const uint2 up = *(const uint2 *)(vrow + 16);
+        const int r0 = ks * 32 + trow_k, r1 = r0 + 16;
+        const uint2 lo = lds_read_tr16((const uint16_t *)((const char *)vb + r0 * ROWB +
+                                                         ((chunk ^ (r0 % CPR)) * 16) + half));
+        const uint2 up = lds_read_tr16((const uint16_t *)((const char *)vb + r1 * ROWB +
+                                                         ((chunk ^ (r1 % CPR)) * 16) + half));
         const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, up.x, up.y));
         O[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[ks][0], O[dt][0], 0, 0, 0);
         O[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[ks][1], O[dt][1], 0, 0, 0);
       }
     }
-    j += cnt;
+
+    if (!more) break;
+    buf ^= 1;
+    cur = nxt;
   }
 
-  // ---- normalise and write: lane holds O^T[dt*16 + lg*4 + i][nt*16 + l16]
+  // ---- normalise and write: lane holds O^T[dt*16 + lg*4 + i][token nt*16 + l16]
+  __syncthreads();  // s_bad is final
   const bool flagged = s_bad != 0;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -334,9 +416,9 @@ prefill_kernel(const PrefillKernelArgs a) {
     tot += __shfl_xor(tot, 16);
     tot += __shfl_xor(tot, 32);
     const float inv = flagged ? __builtin_nanf("") : 1.f / tot;
-    const int row = qt * kPfM + wave * 32 + nt * 16 + l16;
-    if (row < plen) {
-      uint16_t *dst = out + ((size_t)(q0 + row) * a.num_q_heads + hq) * D + lg * 4;
+    const int tk = tw0 + nt * 16 + l16;
+    if (tk < tok_valid) {
+      uint16_t *dst = out + ((size_t)(q0 + tt * TOK + tk) * a.num_q_heads + hq) * D + lg * 4;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const uint2 pk = make_uint2(pack_bf16x2(O[dt][nt][0] * inv, O[dt][nt][1] * inv),
@@ -347,7 +429,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   }
 }
 
-template <int D>
+template <int D, int HP>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   PrefillKernelArgs k;
   k.out = (uint16_t *)a.out;
@@ -364,23 +446,31 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   k.num_kv_heads = a.num_kv_heads;
   k.num_blocks = a.num_blocks;
   k.max_blocks = a.max_blocks;
-  k.q_tiles = (a.max_q_len + kPfM - 1) / kPfM;
-  k.num_units = k.q_tiles * a.batch * a.num_kv_heads;
+  k.head_groups = a.num_q_heads / a.num_kv_heads / HP;
+  constexpr int tok = kPfRows / HP;
+  k.tok_tiles = (a.max_q_len + tok - 1) / tok;
+  k.num_units = a.batch * a.num_kv_heads * k.head_groups;
   k.scale_log2 = a.scale * kLog2e;
   k.rope_theta = a.rope_theta;
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const long long slots = (long long)(k.num_units + kXcds - 1) / kXcds * group;
-  const long long grid = slots * kXcds;
+  const long long grid = (long long)(k.num_units + kXcds - 1) / kXcds * kXcds * k.tok_tiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D>), dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream, k);
+  hipLaunchKernelGGL((prefill_kernel<D, HP>), dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream, k);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_prefill_d(const PrefillArgs &a, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  if (group % 4 == 0) return launch_prefill_t<D, 4>(a, stream);
+  if (group % 2 == 0) return launch_prefill_t<D, 2>(a, stream);
+  return launch_prefill_t<D, 1>(a, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   switch (a.head_dim) {
-    case 64: return launch_prefill_t<64>(a, stream);
-    case 128: return launch_prefill_t<128>(a, stream);
+    case 64: return launch_prefill_d<64>(a, stream);
+    case 128: return launch_prefill_d<128>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
