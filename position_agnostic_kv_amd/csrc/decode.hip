@@ -111,7 +111,7 @@ decode_split_kernel(const DecodeKernelArgs a) {
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: SGPR
   const int hkv = a.num_kv_heads;
   const int hq = hkv * G;
 

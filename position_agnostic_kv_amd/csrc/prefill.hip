@@ -102,7 +102,7 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
 // rows feed the A operand of O^T = V^T P^T through two transposing reads.
 // Two buffers: the next tile streams in while the current one is computed.
 template <int D, int HP>
-__global__ void __launch_bounds__(kPfWaves * kWave)
+__global__ void __launch_bounds__(kPfWaves * kWave, 2)
 prefill_kernel(const PrefillKernelArgs a) {
   constexpr int KC = D / 32;          // 32-dim k-chunks of the QK product
   constexpr int DT = D / 16;          // 16-dim m-tiles of O^T
@@ -119,9 +119,8 @@ prefill_kernel(const PrefillKernelArgs a) {
 
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILEB / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILEB / 2];
-  __shared__ double s_invf[HALF];
-  __shared__ float s_qf[kPfWaves][2 * KC * 8][kWave];  // q_rho per wave, lane-minor
-  __shared__ float s_rot[kPfWaves][2][HALF];          // cos, sin of the current run
+  __shared__ float s_turn[HALF];                // theta_i / (2 pi): turns per position
+  __shared__ float s_frac[kPfWaves][HALF];       // frac((n0 - off) * turn_i) of the current run
   __shared__ int s_bad;
 
   // ---- work item: the token tiles of one (sequence, KV head, head group) run
@@ -143,7 +142,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   const int kv_len = a.kv_lens[b];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: SGPR
   const int l16 = lane & 15;
   const int lg = lane >> 4;
   const int hq = g * G + hgrp * HP + wave / WPH;   // this wave's query head
@@ -165,43 +164,22 @@ prefill_kernel(const PrefillKernelArgs a) {
     ((uint32_t *)sV[0])[i] = 0u;
     ((uint32_t *)sV[1])[i] = 0u;
   }
-  if (tid < HALF) s_invf[tid] = rope_inv_freq(tid, D, a.rope_theta);
+  double turn_d = 0.0;  // this lane's frequency in turns per position (lanes < HALF), double
+  if (lane < HALF) turn_d = rope_inv_freq(lane, D, a.rope_theta) * 0.15915494309189535;
+  if (tid < HALF) s_turn[tid] = (float)turn_d;
   if (tid == 0) s_bad = 0;
   __syncthreads();
 
   // ---- query rows: this lane holds tokens tw0 + nt*16 + l16 and the dims
-  // kc*32 + lg*8 + e; q_rho = rot(q, rho), rho = token index inside the tile,
-  // is parked in LDS (it is read again only when a new document starts).
+  // kc*32 + lg*8 + e.  The raw (bf16, exact) rows are re-read from memory and
+  // rotated afresh whenever a new document starts.
+  const uint4 *qsrc[2];
+  bool qok[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    float qf[KC][8];
-    const int rho = tw0 + nt * 16 + l16;
-    const int row = tt * TOK + rho;
-    const bool ok = row < plen;
-    const uint4 *src = (const uint4 *)(a.q + ((size_t)(q0 + (ok ? row : 0)) * a.num_q_heads + hq) * D);
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const uint4 v = ok ? src[kc * 4 + lg] : make_uint4(0u, 0u, 0u, 0u);
-      qf[kc][0] = bf16_lo(v.x);
-      qf[kc][1] = bf16_hi(v.x);
-      qf[kc][2] = bf16_lo(v.y);
-      qf[kc][3] = bf16_hi(v.y);
-      qf[kc][4] = bf16_lo(v.z);
-      qf[kc][5] = bf16_hi(v.z);
-      qf[kc][6] = bf16_lo(v.w);
-      qf[kc][7] = bf16_hi(v.w);
-    }
-#pragma unroll
-    for (int kc = 0; kc < KC / 2; ++kc) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float c, s;
-        rope_cos_sin_small(rho, s_invf[kc * 32 + lg * 8 + e], c, s);
-        const float x = qf[kc][e], y = qf[kc + KC / 2][e];
-        s_qf[wave][(nt * KC + kc) * 8 + e][lane] = fmaf(x, c, -(y * s));
-        s_qf[wave][(nt * KC + kc + KC / 2) * 8 + e][lane] = fmaf(y, c, x * s);
-      }
-    }
+    const int row = tt * TOK + tw0 + nt * 16 + l16;
+    qok[nt] = row < plen;
+    qsrc[nt] = (const uint4 *)(a.q + ((size_t)(q0 + (qok[nt] ? row : 0)) * a.num_q_heads + hq) * D);
   }
 
   const int n0 = a.q_pos_start[b] + tt * TOK;    // position of tile token 0
@@ -278,31 +256,37 @@ prefill_kernel(const PrefillKernelArgs a) {
       issue_tile(nxt, buf ^ 1);  // streams in while this tile is computed
     }
 
-    // ---- re-rotate the query rows when the offset changes (a new document)
+    // ---- re-rotate the query rows when the offset changes (a new document):
+    // q' = rot(q, rho + n0 - off), rho = token index inside the tile.  The angle
+    // in turns is rho * turn_i + frac((n0 - off) * turn_i); the large part is
+    // reduced in double, the rest (< TOK turns) evaluated with v_sin/v_cos.
     if (cur.off != cur_off) {
       cur_off = cur.off;
       if (lane < HALF) {
-        float cs, sn;
-        rope_cos_sin(n0 - cur.off, s_invf[lane], cs, sn);
-        s_rot[wave][0][lane] = cs;
-        s_rot[wave][1][lane] = sn;
+        const double t = (double)(n0 - cur.off) * turn_d;
+        s_frac[wave][lane] = (float)(t - rint(t));
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the table is visible to the wave
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int kc = 0; kc < KC / 2; ++kc) {
+      for (int nt = 0; nt < 2; ++nt) {
+        const float rho = (float)(tw0 + nt * 16 + l16);
+        uint4 qraw[KC];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int fi = kc * 32 + lg * 8 + e;
-          const float c = s_rot[wave][0][fi], s = s_rot[wave][1][fi];
+        for (int kc = 0; kc < KC; ++kc) qraw[kc] = qok[nt] ? qsrc[nt][kc * 4 + lg] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const float x = s_qf[wave][(nt * KC + kc) * 8 + e][lane];
-            const float y = s_qf[wave][(nt * KC + kc + KC / 2) * 8 + e][lane];
+        for (int kc = 0; kc < KC / 2; ++kc) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int fi = kc * 32 + lg * 8 + e;
+            const float turns = fmaf(rho, s_turn[fi], s_frac[wave][fi]);
+            const float c = __builtin_amdgcn_cosf(turns), s = __builtin_amdgcn_sinf(turns);
+            const uint32_t wx = dw4(qraw[kc], e >> 1), wy = dw4(qraw[kc + KC / 2], e >> 1);
+            const float x = (e & 1) ? bf16_hi(wx) : bf16_lo(wx);
+            const float y = (e & 1) ? bf16_hi(wy) : bf16_lo(wy);
             bq[nt][kc][e] = (__bf16)(fmaf(x, c, -(y * s)) * a.scale_log2);
             bq[nt][kc + KC / 2][e] = (__bf16)(fmaf(y, c, x * s) * a.scale_log2);
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
