@@ -81,6 +81,17 @@ __device__ __forceinline__ Tile make_tile(const uint32_t *trow, int j, int nblk)
 }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// LDS chunk swizzle of a K/V tile row (16-byte chunks, CPR per row): slot =
+// chunk ^ swz(row).  For 16 chunks per row a bit rotation of the row keeps both
+// readers conflict-free: the 16 rows of a K operand read (one chunk column)
+// land in 16 distinct bank groups, and the 8 rows x 2 chunks that a half-wave
+// of the transposing V read touches land in 16 distinct groups too.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (r >> 1) & (CPR - 1);
+}
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, output
@@ -192,9 +203,14 @@ prefill_kernel(const PrefillKernelArgs a) {
 
   // ---- staging: wave w streams block w of the tile (K then V) into LDS.
   // Lane L of load instruction i fills LDS row r = i*RPI + L/CPR of the block,
-  // chunk slot L % CPR, with global chunk (L % CPR) ^ (r % CPR).
-  const int ld_row = lane / CPR;
-  const int ld_chunk = (lane % CPR);
+  // chunk slot L % CPR, with global chunk (L % CPR) ^ swz(r).  The per-lane
+  // source offsets do not depend on the tile.
+  uint32_t ld_off[IPB];
+#pragma unroll
+  for (int i = 0; i < IPB; ++i) {
+    const int r = i * RPI + lane / CPR;
+    ld_off[i] = (uint32_t)(r * ROWB + (((lane % CPR) ^ swz<CPR>(r)) * 16));
+  }
   auto issue_tile = [&](const Tile &t, int buf) {
     if (wave >= t.cnt) return;
     uint32_t w = t.wt[0];
@@ -206,15 +222,13 @@ prefill_kernel(const PrefillKernelArgs a) {
       s_bad = 1;
       id = 0;
     }
-    const uint16_t *kg = a.k_pool + ((size_t)id * hkv + g) * kBlockTokens * D;
-    const uint16_t *vg = a.v_pool + ((size_t)id * hkv + g) * kBlockTokens * D;
+    const char *kg = (const char *)(a.k_pool + ((size_t)id * hkv + g) * kBlockTokens * D);
+    const char *vg = (const char *)(a.v_pool + ((size_t)id * hkv + g) * kBlockTokens * D);
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
-      const int r = i * RPI + ld_row;
-      const int src = r * D + ((ld_chunk ^ (r % CPR)) * 8);
       const int dst = (wave * kBlockTokens + i * RPI) * D;  // wave-uniform row base
-      __builtin_amdgcn_global_load_lds((const void *)(kg + src), (lds_ptr_t)(&sK[buf][dst]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(vg + src), (lds_ptr_t)(&sV[buf][dst]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(kg + ld_off[i]), (lds_ptr_t)(&sK[buf][dst]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(vg + ld_off[i]), (lds_ptr_t)(&sV[buf][dst]), 16, 0, 0);
     }
   };
   // after the wave's own loads landed: zero V rows of its block past kv_len
@@ -228,6 +242,22 @@ prefill_kernel(const PrefillKernelArgs a) {
       if (r >= valid) *(uint4 *)(&sV[buf][(wave * kBlockTokens + r) * D + (i % CPR) * 8]) = make_uint4(0u, 0u, 0u, 0u);
     }
   };
+
+  // per-lane LDS read offsets (bytes), independent of the tile and the buffer:
+  // K operand rows mt*16 + l16, chunk kc*4 + lg; V^T operand source rows
+  // lg*4 + l16/4 (+16, +32ks), dims dt*16 + 4*(l16 % 4)
+  uint32_t k_off[KC], v_off[DT];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) k_off[kc] = (uint32_t)(l16 * ROWB + (((kc * 4 + lg) ^ swz<CPR>(l16)) * 16));
+  {
+    const int vr = lg * 4 + (l16 >> 2);
+    const int tdim = (l16 & 3) * 4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int chunk = (dt * 16 + tdim) / 8;
+      v_off[dt] = (uint32_t)(vr * ROWB + ((chunk ^ swz<CPR>(vr)) * 16) + ((dt * 16 + tdim) % 8) * 2);
+    }
+  }
 
   bf16x8_t bq[2][KC];
   f32x4_t O[DT][2];
@@ -291,18 +321,21 @@ prefill_kernel(const PrefillKernelArgs a) {
       }
     }
 
-    // ---- S^T = K Q^T  (per lane: keys mt*16 + lg*4 + i, token nt*16 + l16)
-    const uint16_t *kb = sK[buf];
+    // ---- S'^T = K Q^T - ms  (per lane: keys mt*16 + lg*4 + i, token nt*16 + l16).
+    // The running max (ms, 0 before the first tile) seeds the accumulators, so
+    // the matrix core returns scores already shifted for exp2.
+    const char *kb = (const char *)sK[buf];
+    float ms[2];
     f32x4_t S[kPfTileBlocks][2];
 #pragma unroll
+    for (int nt = 0; nt < 2; ++nt) ms[nt] = m[nt] == -INFINITY ? 0.f : m[nt];
+#pragma unroll
     for (int mt = 0; mt < kPfTileBlocks; ++mt) {
-      S[mt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      S[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      S[mt][0] = f32x4_t{-ms[0], -ms[0], -ms[0], -ms[0]};
+      S[mt][1] = f32x4_t{-ms[1], -ms[1], -ms[1], -ms[1]};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const int row = mt * 16 + l16;
-        const int chunk = (kc * 4 + lg) ^ (row % CPR);
-        const bf16x8_t ka = as_bf16x8(*(const uint4 *)(kb + row * D + chunk * 8));
+        const bf16x8_t ka = as_bf16x8(*(const uint4 *)(kb + mt * 16 * ROWB + k_off[kc]));
         S[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bq[0][kc], S[mt][0], 0, 0, 0);
         S[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bq[1][kc], S[mt][1], 0, 0, 0);
       }
@@ -323,63 +356,63 @@ prefill_kernel(const PrefillKernelArgs a) {
           }
     }
 
-    // ---- online softmax per query column
+    // ---- online softmax per query column (on S' = S - ms)
     float bm[2];
     bool need = false;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float x = fmaxf(S[0][nt][0], S[0][nt][1]);
-#pragma unroll
-      for (int mt = 0; mt < kPfTileBlocks; ++mt)
-#pragma unroll
-        for (int i = (mt == 0 ? 2 : 0); i < 4; i += 2) x = fmaxf(x, fmaxf(S[mt][nt][i], S[mt][nt][i + 1]));
-      x = fmaxf(x, __shfl_xor(x, 16));
-      x = fmaxf(x, __shfl_xor(x, 32));
-      bm[nt] = x;
-      need |= x > m[nt] + kPfSlack;
+      float x = fmaxf(S[0][nt][0], fmaxf(S[0][nt][1], S[0][nt][2]));
+      x = fmaxf(x, fmaxf(S[0][nt][3], S[1][nt][0]));
+      x = fmaxf(x, fmaxf(S[1][nt][1], S[1][nt][2]));
+      x = fmaxf(x, fmaxf(S[1][nt][3], S[2][nt][0]));
+      x = fmaxf(x, fmaxf(S[2][nt][1], S[2][nt][2]));
+      x = fmaxf(x, fmaxf(S[2][nt][3], S[3][nt][0]));
+      x = fmaxf(x, fmaxf(S[3][nt][1], S[3][nt][2]));
+      x = col_max4(fmaxf(x, S[3][nt][3]));
+      bm[nt] = x;  // tile max - ms
+      need |= m[nt] == -INFINITY ? x > -INFINITY : x > kPfSlack;
     }
-    if (wave_any(need)) {
+    if (wave_any(need)) {  // raise the running max: rescale O and l, shift S'
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const float mn = fmaxf(m[nt], bm[nt]);
+        const float mn = fmaxf(m[nt], ms[nt] + bm[nt]);
         const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[nt] - mn);
+        const float shift = mn == -INFINITY ? 0.f : mn - ms[nt];
         lsum[nt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) O[dt][nt] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < kPfTileBlocks; ++mt) S[mt][nt] -= shift;
         m[nt] = mn;
       }
     }
     bf16x8_t bp[2][2];  // [ks][nt]: keys 32ks + {lg*4 + 0..3, 16 + lg*4 + 0..3}
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const float ms = m[nt] == -INFINITY ? 0.f : m[nt];
 #pragma unroll
-      for (int mt = 0; mt < kPfTileBlocks; ++mt) {
+      for (int mt = 0; mt < kPfTileBlocks; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(S[mt][nt][i] - ms);
-          lsum[nt] += p;
-          bp[mt >> 1][nt][(mt & 1) * 4 + i] = (__bf16)p;
-        }
+        for (int i = 0; i < 4; ++i) bp[mt >> 1][nt][(mt & 1) * 4 + i] = (__bf16)__builtin_amdgcn_exp2f(S[mt][nt][i]);
+      // row sums from the rounded weights P.V uses: dot2 against (1, 1)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 pw = __builtin_bit_cast(uint4, bp[ks][nt]);
+        lsum[nt] = dot2_bf16(pw.x, 0x3f803f80u, lsum[nt]);
+        lsum[nt] = dot2_bf16(pw.y, 0x3f803f80u, lsum[nt]);
+        lsum[nt] = dot2_bf16(pw.z, 0x3f803f80u, lsum[nt]);
+        lsum[nt] = dot2_bf16(pw.w, 0x3f803f80u, lsum[nt]);
       }
     }
 
     // ---- O^T += V^T P^T: A operand rows = dims, k-slots = keys
     // 32ks + lg*4 + 0..3 and 32ks + 16 + lg*4 + 0..3, read transposed.
-    const uint16_t *vb = sV[buf];
-    const int trow_k = lg * 4 + (l16 >> 2);  // source key row inside a 16-key group
-    const int tdim = (l16 & 3) * 4;          // source dims (4) inside a 16-dim tile
+    const char *vb = (const char *)sV[buf];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const int chunk = (dt * 16 + tdim) / 8;
-      const int half = ((dt * 16 + tdim) % 8) * 2;  // bytes
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int r0 = ks * 32 + trow_k, r1 = r0 + 16;
-        const uint2 lo = lds_read_tr16((const uint16_t *)((const char *)vb + r0 * ROWB +
-                                                         ((chunk ^ (r0 % CPR)) * 16) + half));
-        const uint2 up = lds_read_tr16((const uint16_t *)((const char *)vb + r1 * ROWB +
-                                                         ((chunk ^ (r1 % CPR)) * 16) + half));
+        const uint2 lo = lds_read_tr16((const uint16_t *)(vb + ks * 32 * ROWB + v_off[dt]));
+        const uint2 up = lds_read_tr16((const uint16_t *)(vb + (ks * 32 + 16) * ROWB + v_off[dt]));
         const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, up.x, up.y));
         O[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[ks][0], O[dt][0], 0, 0, 0);
         O[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[ks][1], O[dt][1], 0, 0, 0);
@@ -396,9 +429,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   const bool flagged = s_bad != 0;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    float tot = lsum[nt];
-    tot += __shfl_xor(tot, 16);
-    tot += __shfl_xor(tot, 32);
+    const float tot = col_sum4(lsum[nt]);
     const float inv = flagged ? __builtin_nanf("") : 1.f / tot;
     const int tk = tw0 + nt * 16 + l16;
     if (tk < tok_valid) {
