@@ -263,7 +263,7 @@ def main():
             "algorithmic_bytes": dec_alg_bytes,
         },
         "roofline_prefill": {
-            "kernel": "lazyattn::prefill_kernel<128>",
+            "kernel": "lazyattn::prefill_kernel<128, 4>",
             "bound": "mfma",
             "achieved": round(pf_tflops, 2),
             "peak": BF16_PEAK_TFLOPS,
