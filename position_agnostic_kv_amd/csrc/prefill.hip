@@ -31,6 +31,8 @@
 //   sharing a KV head run on the same XCD (shared L2 for their K/V tiles).
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -40,7 +42,6 @@ constexpr int kPfWaves = 4;
 constexpr int kPfRows = 128;      // query rows per workgroup (M)
 constexpr int kPfTileBlocks = 4;  // K/V tile: up to 4 blocks = 64 keys
 constexpr int kPfN = kPfTileBlocks * kBlockTokens;
-constexpr float kPfSlack = 8.0f;
 constexpr int kXcds = 8;
 
 struct PrefillKernelArgs {
@@ -60,25 +61,6 @@ struct PrefillKernelArgs {
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// A K/V tile: a run of up to 4 table blocks, starting at block j, sharing one offset.
-struct Tile {
-  int j, cnt, off;
-  uint32_t wt[kPfTileBlocks];
-};
-
-__device__ __forceinline__ Tile make_tile(const uint32_t *trow, int j, int nblk) {
-  Tile t;
-  t.j = j;
-#pragma unroll
-  for (int u = 0; u < kPfTileBlocks; ++u) t.wt[u] = (j + u < nblk) ? trow[j + u] : 0u;
-  t.off = word_offset(t.wt[0]);
-  t.cnt = 1;
-#pragma unroll
-  for (int u = 1; u < kPfTileBlocks; ++u)
-    if (t.cnt == u && j + u < nblk && word_offset(t.wt[u]) == t.off) t.cnt = u + 1;
-  return t;
-}
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
@@ -204,42 +186,54 @@ prefill_kernel(const PrefillKernelArgs a) {
   // ---- staging: wave w streams block w of the tile (K then V) into LDS.
   // Lane L of load instruction i fills LDS row r = i*RPI + L/CPR of the block,
   // chunk slot L % CPR, with global chunk (L % CPR) ^ swz(r).  The per-lane
-  // source offsets do not depend on the tile.
+  // source offsets do not depend on the tile; the block base is wave-uniform.
   uint32_t ld_off[IPB];
 #pragma unroll
   for (int i = 0; i < IPB; ++i) {
     const int r = i * RPI + lane / CPR;
     ld_off[i] = (uint32_t)(r * ROWB + (((lane % CPR) ^ swz<CPR>(r)) * 16));
   }
-  auto issue_tile = [&](const Tile &t, int buf) {
-    if (wave >= t.cnt) return;
-    uint32_t w = t.wt[0];
-#pragma unroll
-    for (int u = 1; u < kPfTileBlocks; ++u)
-      if (wave == u) w = t.wt[u];
-    uint32_t id = word_block(w);
+
+  // Table words travel one tile ahead: lanes 0..3 of a VGPR hold the words of
+  // blocks jw .. jw+3 (0 past the visible blocks).  A tile's start, length and
+  // offset are wave-uniform (scalar registers).
+  auto load_words = [&](int jw) -> uint32_t {
+    return (lane < kPfTileBlocks && jw + lane < nblk_vis) ? trow[jw + lane] : 0u;
+  };
+  // blocks jw.. that share block jw's offset (1..4), and that offset
+  auto tile_of = [&](uint32_t wv, int jw, int &cnt, int &off) {
+    const uint32_t w0 = __builtin_amdgcn_readfirstlane(wv);
+    off = word_offset(w0);
+    const uint64_t same =
+        __ballot(lane < kPfTileBlocks && jw + lane < nblk_vis && (wv >> 16) == (w0 >> 16));
+    cnt = __builtin_ctzll(~same);
+  };
+  auto issue_tile = [&](uint32_t wv, int cnt, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    if (wave >= cnt) return;
+    uint32_t id = word_block((uint32_t)__builtin_amdgcn_readlane((int)wv, wave));
     if (id >= (uint32_t)a.num_blocks) {
       s_bad = 1;
       id = 0;
     }
-    const char *kg = (const char *)(a.k_pool + ((size_t)id * hkv + g) * kBlockTokens * D);
-    const char *vg = (const char *)(a.v_pool + ((size_t)id * hkv + g) * kBlockTokens * D);
+    const char *kg = (const char *)a.k_pool + ((size_t)id * hkv + g) * (kBlockTokens * ROWB);
+    const char *vg = (const char *)a.v_pool + ((size_t)id * hkv + g) * (kBlockTokens * ROWB);
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
       const int dst = (wave * kBlockTokens + i * RPI) * D;  // wave-uniform row base
-      __builtin_amdgcn_global_load_lds((const void *)(kg + ld_off[i]), (lds_ptr_t)(&sK[buf][dst]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(vg + ld_off[i]), (lds_ptr_t)(&sV[buf][dst]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(kg + ld_off[i]), (lds_ptr_t)(&sK[BUF][dst]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(vg + ld_off[i]), (lds_ptr_t)(&sV[BUF][dst]), 16, 0, 0);
     }
   };
   // after the wave's own loads landed: zero V rows of its block past kv_len
-  auto fix_tail = [&](const Tile &t, int buf) {
-    if (wave >= t.cnt) return;
-    const int key0 = (t.j + wave) * kBlockTokens;
-    const int valid = kv_len - key0;
+  auto fix_tail = [&](int j, int cnt, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    if (wave >= cnt) return;
+    const int valid = kv_len - (j + wave) * kBlockTokens;
     if (valid >= kBlockTokens) return;
     for (int i = lane; i < kBlockTokens * CPR; i += kWave) {
       const int r = i / CPR;
-      if (r >= valid) *(uint4 *)(&sV[buf][(wave * kBlockTokens + r) * D + (i % CPR) * 8]) = make_uint4(0u, 0u, 0u, 0u);
+      if (r >= valid) *(uint4 *)(&sV[BUF][(wave * kBlockTokens + r) * D + (i % CPR) * 8]) = make_uint4(0u, 0u, 0u, 0u);
     }
   };
 
@@ -259,51 +253,77 @@ prefill_kernel(const PrefillKernelArgs a) {
     }
   }
 
+  // ---- softmax bookkeeping.  Weights are p = 2^(s - r) with a per-row
+  // reference r (0 to start), not the running maximum: the common factor 2^-r
+  // cancels in O / l.  r moves only when a row's sum would leave
+  // [2^-64, 2^64] -- checked per lane against the upper bound every tile, and
+  // per row against the lower bound until every row holds a sum -- so no
+  // per-tile maximum is needed.
   bf16x8_t bq[2][KC];
   f32x4_t O[DT][2];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) O[dt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY};
+  float ref[2] = {0.f, 0.f};
   float lsum[2] = {0.f, 0.f};
+  bool ref_nz = false;    // wave-uniform: some row's reference is not 0
+  bool settled = false;   // wave-uniform: every row's sum is >= 2^-64
   int cur_off = -1;
+  constexpr float kHi = 0x1p64f, kLo = 0x1p-64f;
 
-  Tile cur = make_tile(trow, 0, nblk_vis);
-  issue_tile(cur, 0);
-  int buf = 0;
-  for (;;) {
-    // this tile's loads (the only ones in flight) have landed; patch its tail
-    __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) and lgkmcnt(0) on gfx9
-    fix_tail(cur, buf);
+  // tile state (wave-uniform): current tile (cj, ccnt, coff); the next tile
+  // starts at block nj and its words nw are in flight
+  int cj = 0, ccnt, coff;
+  {
+    const uint32_t w = load_words(0);
+    tile_of(w, 0, ccnt, coff);
+    issue_tile(w, ccnt, std::integral_constant<int, 0>{});
+  }
+  int nj = ccnt;
+  uint32_t nw = nj < nblk_vis ? load_words(nj) : 0u;
+
+  // One tile on LDS buffer BUF; returns false after the last tile.
+  auto step = [&](auto bufc) -> bool {
+    constexpr int BUF = decltype(bufc)::value;
+    __builtin_amdgcn_s_waitcnt(0);   // this tile's loads and the next words have landed
+    fix_tail(cj, ccnt, bufc);
     __syncthreads();
 
-    const int jn = cur.j + cur.cnt;
-    const bool more = jn < nblk_vis;
-    Tile nxt;
-    if (more) {
-      nxt = make_tile(trow, jn, nblk_vis);
-      issue_tile(nxt, buf ^ 1);  // streams in while this tile is computed
+    // a new document: fetch the raw query rows before the next tile's loads
+    const bool rotate = coff != cur_off;
+    uint4 qraw[2][KC];
+    if (rotate) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) qraw[nt][kc] = qok[nt] ? qsrc[nt][kc * 4 + lg] : make_uint4(0u, 0u, 0u, 0u);
     }
 
-    // ---- re-rotate the query rows when the offset changes (a new document):
-    // q' = rot(q, rho + n0 - off), rho = token index inside the tile.  The angle
-    // in turns is rho * turn_i + frac((n0 - off) * turn_i); the large part is
-    // reduced in double, the rest (< TOK turns) evaluated with v_sin/v_cos.
-    if (cur.off != cur_off) {
-      cur_off = cur.off;
+    const bool more = nj < nblk_vis;
+    int ncnt = 0, noff = 0, nnj = 0;
+    uint32_t nnw = 0u;
+    if (more) {
+      tile_of(nw, nj, ncnt, noff);
+      issue_tile(nw, ncnt, std::integral_constant<int, BUF ^ 1>{});  // streams in during this tile
+      nnj = nj + ncnt;
+      nnw = nnj < nblk_vis ? load_words(nnj) : 0u;
+    }
+
+    // ---- re-rotate the query rows: q' = rot(q, rho + n0 - off), rho = token
+    // index inside the tile.  The angle in turns is rho * turn_i +
+    // frac((n0 - off) * turn_i); the large part is reduced in double, the rest
+    // (< TOK turns) evaluated with v_sin/v_cos.
+    if (rotate) {
+      cur_off = coff;
       if (lane < HALF) {
-        const double t = (double)(n0 - cur.off) * turn_d;
+        const double t = (double)(n0 - coff) * turn_d;
         s_frac[wave][lane] = (float)(t - rint(t));
       }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the table is visible to the wave
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const float rho = (float)(tw0 + nt * 16 + l16);
-        uint4 qraw[KC];
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) qraw[kc] = qok[nt] ? qsrc[nt][kc * 4 + lg] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
         for (int kc = 0; kc < KC / 2; ++kc) {
 #pragma unroll
@@ -311,7 +331,7 @@ prefill_kernel(const PrefillKernelArgs a) {
             const int fi = kc * 32 + lg * 8 + e;
             const float turns = fmaf(rho, s_turn[fi], s_frac[wave][fi]);
             const float c = __builtin_amdgcn_cosf(turns), s = __builtin_amdgcn_sinf(turns);
-            const uint32_t wx = dw4(qraw[kc], e >> 1), wy = dw4(qraw[kc + KC / 2], e >> 1);
+            const uint32_t wx = dw4(qraw[nt][kc], e >> 1), wy = dw4(qraw[nt][kc + KC / 2], e >> 1);
             const float x = (e & 1) ? bf16_hi(wx) : bf16_lo(wx);
             const float y = (e & 1) ? bf16_hi(wy) : bf16_lo(wy);
             bq[nt][kc][e] = (__bf16)(fmaf(x, c, -(y * s)) * a.scale_log2);
@@ -321,18 +341,21 @@ prefill_kernel(const PrefillKernelArgs a) {
       }
     }
 
-    // ---- S'^T = K Q^T - ms  (per lane: keys mt*16 + lg*4 + i, token nt*16 + l16).
-    // The running max (ms, 0 before the first tile) seeds the accumulators, so
-    // the matrix core returns scores already shifted for exp2.
-    const char *kb = (const char *)sK[buf];
-    float ms[2];
+    // ---- S'^T = K Q^T - r  (per lane: keys mt*16 + lg*4 + i, token nt*16 + l16)
+    const char *kb = (const char *)sK[BUF];
     f32x4_t S[kPfTileBlocks][2];
+    if (ref_nz) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) ms[nt] = m[nt] == -INFINITY ? 0.f : m[nt];
+      for (int mt = 0; mt < kPfTileBlocks; ++mt) {
+        S[mt][0] = f32x4_t{-ref[0], -ref[0], -ref[0], -ref[0]};
+        S[mt][1] = f32x4_t{-ref[1], -ref[1], -ref[1], -ref[1]};
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < kPfTileBlocks; ++mt) S[mt][0] = S[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int mt = 0; mt < kPfTileBlocks; ++mt) {
-      S[mt][0] = f32x4_t{-ms[0], -ms[0], -ms[0], -ms[0]};
-      S[mt][1] = f32x4_t{-ms[1], -ms[1], -ms[1], -ms[1]};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         const bf16x8_t ka = as_bf16x8(*(const uint4 *)(kb + mt * 16 * ROWB + k_off[kc]));
@@ -341,72 +364,88 @@ prefill_kernel(const PrefillKernelArgs a) {
       }
     }
 
-    // ---- mask: keys past the tile's run, past kv_len, or after the query token
-    const int key0 = cur.j * kBlockTokens;
-    if (cur.cnt < kPfTileBlocks || key0 + kPfN > kv_len || key0 + kPfN - 1 > t_wave) {
-#pragma unroll
-      for (int mt = 0; mt < kPfTileBlocks; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kidx = key0 + mt * 16 + lg * 4 + i;
-            const int tq = t_wave + nt * 16 + l16;
-            if (mt >= cur.cnt || kidx >= kv_len || kidx > tq) S[mt][nt][i] = -INFINITY;
-          }
-    }
-
-    // ---- online softmax per query column (on S' = S - ms)
-    float bm[2];
-    bool need = false;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float x = fmaxf(S[0][nt][0], fmaxf(S[0][nt][1], S[0][nt][2]));
-      x = fmaxf(x, fmaxf(S[0][nt][3], S[1][nt][0]));
-      x = fmaxf(x, fmaxf(S[1][nt][1], S[1][nt][2]));
-      x = fmaxf(x, fmaxf(S[1][nt][3], S[2][nt][0]));
-      x = fmaxf(x, fmaxf(S[2][nt][1], S[2][nt][2]));
-      x = fmaxf(x, fmaxf(S[2][nt][3], S[3][nt][0]));
-      x = fmaxf(x, fmaxf(S[3][nt][1], S[3][nt][2]));
-      x = col_max4(fmaxf(x, S[3][nt][3]));
-      bm[nt] = x;  // tile max - ms
-      need |= m[nt] == -INFINITY ? x > -INFINITY : x > kPfSlack;
-    }
-    if (wave_any(need)) {  // raise the running max: rescale O and l, shift S'
+    // ---- mask: keys past the tile's run, past kv_len, or after the query token.
+    // Per lane and query column, keys mt*16 + lg*4 + i of the tile stay when
+    // mt*16 + i <= lim.
+    const int key0 = cj * kBlockTokens;
+    if (ccnt < kPfTileBlocks || key0 + kPfN > kv_len || key0 + kPfN - 1 > t_wave) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const float mn = fmaxf(m[nt], ms[nt] + bm[nt]);
-        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[nt] - mn);
-        const float shift = mn == -INFINITY ? 0.f : mn - ms[nt];
-        lsum[nt] *= alpha;
+        const int last = min(min(kv_len - 1, t_wave + nt * 16 + l16), key0 + ccnt * kBlockTokens - 1);
+        const int lim = last - key0 - lg * 4;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) O[dt][nt] *= alpha;
+        for (int mt = 0; mt < kPfTileBlocks; ++mt)
 #pragma unroll
-        for (int mt = 0; mt < kPfTileBlocks; ++mt) S[mt][nt] -= shift;
-        m[nt] = mn;
+          for (int i = 0; i < 4; ++i)
+            if (mt * 16 + i > lim) S[mt][nt][i] = -INFINITY;
       }
     }
+
+    // ---- weights p = 2^S' (bf16, as P.V uses them) and the lane's row sums
     bf16x8_t bp[2][2];  // [ks][nt]: keys 32ks + {lg*4 + 0..3, 16 + lg*4 + 0..3}
+    float ln[2];
+    auto weights = [&]() {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
-      for (int mt = 0; mt < kPfTileBlocks; ++mt)
+        for (int mt = 0; mt < kPfTileBlocks; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bp[mt >> 1][nt][(mt & 1) * 4 + i] = (__bf16)__builtin_amdgcn_exp2f(S[mt][nt][i]);
-      // row sums from the rounded weights P.V uses: dot2 against (1, 1)
+          for (int i = 0; i < 4; ++i) bp[mt >> 1][nt][(mt & 1) * 4 + i] = (__bf16)__builtin_amdgcn_exp2f(S[mt][nt][i]);
+        float l = lsum[nt];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint4 pw = __builtin_bit_cast(uint4, bp[ks][nt]);
-        lsum[nt] = dot2_bf16(pw.x, 0x3f803f80u, lsum[nt]);
-        lsum[nt] = dot2_bf16(pw.y, 0x3f803f80u, lsum[nt]);
-        lsum[nt] = dot2_bf16(pw.z, 0x3f803f80u, lsum[nt]);
-        lsum[nt] = dot2_bf16(pw.w, 0x3f803f80u, lsum[nt]);
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint4 pw = __builtin_bit_cast(uint4, bp[ks][nt]);
+          l = dot2_bf16(pw.x, 0x3f803f80u, l);
+          l = dot2_bf16(pw.y, 0x3f803f80u, l);
+          l = dot2_bf16(pw.z, 0x3f803f80u, l);
+          l = dot2_bf16(pw.w, 0x3f803f80u, l);
+        }
+        ln[nt] = l;
       }
+    };
+    weights();
+    bool bad = !(ln[0] <= kHi) || !(ln[1] <= kHi);   // NaN counts as bad
+    if (!settled) bad |= !(col_sum4(ln[0]) >= kLo) || !(col_sum4(ln[1]) >= kLo);
+    if (wave_any(bad)) {
+      // Rare: move the reference of every row whose sum left the range to
+      // max(tile maximum, log2 of the sum so far), rescale what the row holds,
+      // and recompute its weights.  Afterwards such a row's sum is in [1, 65].
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float x = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < kPfTileBlocks; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x = fmaxf(x, S[mt][nt][i]);
+        const float tmax = col_max4(x);
+        const float t_old = col_sum4(lsum[nt]);
+        const float t_new = col_sum4(ln[nt]);
+        float sh = 0.f;
+        if (!(t_new >= kLo && t_new <= kHi)) {
+          sh = fmaxf(tmax, t_old > 0.f ? __builtin_amdgcn_logf(t_old) : -INFINITY);
+          if (!(sh > -INFINITY && sh < INFINITY)) sh = 0.f;
+        }
+        // alpha = 2^-sh = half^2, applied in two steps: with a sum so far,
+        // sh >= log2(sum) >= -149 keeps half <= 2^74.5; without one, the row
+        // holds only zeros and alpha is irrelevant (0 avoids 0 * inf)
+        const float half = t_old > 0.f ? __builtin_amdgcn_exp2f(-0.5f * sh) : 0.f;
+        ref[nt] += sh;
+        lsum[nt] = lsum[nt] * half * half;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) O[dt][nt] = O[dt][nt] * half * half;
+#pragma unroll
+        for (int mt = 0; mt < kPfTileBlocks; ++mt) S[mt][nt] -= sh;
+      }
+      weights();
+      ref_nz = wave_any(ref[0] != 0.f || ref[1] != 0.f);
     }
+    settled = true;
+    lsum[0] = ln[0];
+    lsum[1] = ln[1];
 
     // ---- O^T += V^T P^T: A operand rows = dims, k-slots = keys
     // 32ks + lg*4 + 0..3 and 32ks + 16 + lg*4 + 0..3, read transposed.
-    const char *vb = (const char *)sV[buf];
+    const char *vb = (const char *)sV[BUF];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -419,9 +458,17 @@ prefill_kernel(const PrefillKernelArgs a) {
       }
     }
 
-    if (!more) break;
-    buf ^= 1;
-    cur = nxt;
+    if (!more) return false;
+    cj = nj;
+    ccnt = ncnt;
+    coff = noff;
+    nj = nnj;
+    nw = nnw;
+    return true;
+  };
+  for (;;) {
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if (!step(std::integral_constant<int, 1>{})) break;
   }
 
   // ---- normalise and write: lane holds O^T[dt*16 + lg*4 + i][token nt*16 + l16]

@@ -192,6 +192,42 @@ def test_prefill_small(d, hq, hkv, cached, prompt, docs, offs):
     assert_parity(W.to_float(out, case.dtype), want, case.dtype, f"prefill D{d} G{hq // hkv} {offs}")
 
 
+# Scores with a large common part per query row (up to ~2^300 before
+# normalisation): the kernels must leave exp's range safely -- overflow on the
+# first tile, underflow on the first tile, and a jump mid-row when the prompt's
+# keys arrive -- and still agree with the oracle.
+SHIFT_CASES = [
+    # kind, D, k_x of cached keys, k_x of appended keys
+    ("prefill", 128, 4.0, 4.0),
+    ("prefill", 128, 0.0, 4.0),
+    ("prefill", 128, -4.0, 4.0),
+    ("prefill", 64, 4.0, -4.0),
+    ("decode", 128, -4.0, 4.0),
+    ("decode", 128, 4.0, -4.0),
+]
+
+
+@pytest.mark.parametrize("kind,d,kc,kn", SHIFT_CASES)
+def test_large_score_shift(kind, d, kc, kn):
+    if kind == "prefill":
+        case = W.prefill_case(81 + d, 2, 8, 2, d, [512, 240], [300, 129], (2, 10), theta=1e30)
+    else:
+        case = W.decode_case(82 + d, 6, 8, 2, d, [512, 800, 16, 1024, 304, 96], (2, 10), theta=1e30)
+    W.materialize_numpy(case)
+    W.add_score_shift(case, 600.0, kc, kn, seed=d)
+    qx = W.to_float(case.q, case.dtype)[..., d // 2 - 1]
+    span = float(np.abs(qx).max()) * max(abs(kc), abs(kn)) * case.scale / np.log(2.0)
+    assert span > 200.0  # log2 units: far past fp32's exp range
+    say(f"[shift] {kind} D{d} k_cached={kc} k_new={kn} span 2^{span:.0f}")
+    dc = DeviceCase(case)
+    dc.append()
+    want = oracle_prefill(case) if kind == "prefill" else oracle_decode(case)
+    for split in ([0] if kind == "prefill" else [0, 4]):
+        out = dc.prefill() if kind == "prefill" else dc.decode(split_blocks=split)
+        torch.cuda.synchronize()
+        assert_parity(W.to_float(out, case.dtype), want, case.dtype, f"shift {kind} D{d} split {split}")
+
+
 def test_incremental_decode_matches_prefill_rows():
     """Decoding row t after the prompt is appended equals prefill row t."""
     case = W.prefill_case(71, 1, 8, 2, 128, [400 - 400 % 16], [150], (2, 10))

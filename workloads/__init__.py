@@ -261,6 +261,41 @@ def materialize_numpy(case):
     return case
 
 
+def add_score_shift(case, q_amp, k_cached, k_new, seed=0):
+    """Give every score of a query row a large common part (host arrays).
+
+    The last rotary pair (dims D/2-1 and D-1, the lowest frequency) is
+    overwritten: q gets x = U(-q_amp, q_amp), y = 0; cached keys x = k_cached
+    and appended keys x = k_new, y = 0.  With rope_theta ~ 1e30 that pair turns
+    by a negligible angle, so q.k gains q_x * k_x, equal for all keys of a
+    kind: scores far outside exp's range while the softmax itself stays as
+    well-conditioned as without the shift.  Call after materialize_numpy.
+    """
+    rng = np.random.default_rng(seed + 3000)
+    d = case.head_dim
+    xi, yi = d // 2 - 1, d - 1
+
+    def edit(arr, fn):
+        x = to_float(arr, case.dtype).copy()
+        fn(x)
+        return x if case.dtype == F32 else f32_to_bf16_bits(x)
+
+    def q_fn(x):
+        x[..., xi] = rng.uniform(-q_amp, q_amp, size=x.shape[:-1]).astype(np.float32)
+        x[..., yi] = 0.0
+
+    def k_fn(val):
+        def fn(x):
+            x[..., xi] = np.float32(val)
+            x[..., yi] = 0.0
+        return fn
+
+    case.q = edit(case.q, q_fn)
+    case.k_pool = edit(case.k_pool, k_fn(k_cached))
+    case.k_new = edit(case.k_new, k_fn(k_new))
+    return case
+
+
 def materialize_torch(case, device):
     """Draw the case's values directly in device memory with torch (seeded).
 
@@ -454,7 +489,7 @@ def make(name, **kw) -> Case:
 __all__ = [
     "BLOCK", "F32", "BF16", "Case", "Layout", "build_layout", "pack_words",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "to_float", "materialize_numpy",
-    "materialize_torch", "decode_case", "prefill_case", "tiny_decode",
+    "materialize_torch", "add_score_shift", "decode_case", "prefill_case", "tiny_decode",
     "llama8b_decode", "llama8b_prefill", "llama70b_decode", "zipf_decode", "make",
     "WORKLOADS",
 ]
