@@ -76,6 +76,23 @@ __device__ __forceinline__ int swz(int r) {
 }
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4, scalar base + per-lane 32-bit offset): lane L's
+// bytes land at LDS address lds + 16 * L.  Issued as inline assembly so the
+// compiler does not order every later LDS read behind it (it cannot tell the
+// buffers apart); the kernel waits for these loads itself (s_waitcnt and a
+// barrier at each tile start).  M0 holds the LDS address; one wait state
+// separates its write from the load.
+__device__ __forceinline__ void lds_dma16(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(lds)
+      : "memory", "m0");
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, output
 // lane i gets element (i % 4) of the 8-byte rows read by source lanes
 // i / 4 + 4k, k = 0..3.
@@ -221,8 +238,8 @@ prefill_kernel(const PrefillKernelArgs a) {
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
       const int dst = (wave * kBlockTokens + i * RPI) * D;  // wave-uniform row base
-      __builtin_amdgcn_global_load_lds((const void *)(kg + ld_off[i]), (lds_ptr_t)(&sK[BUF][dst]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(vg + ld_off[i]), (lds_ptr_t)(&sV[BUF][dst]), 16, 0, 0);
+      lds_dma16(kg, ld_off[i], (uint32_t)(uintptr_t)(lds_ptr_t)(&sK[BUF][dst]));
+      lds_dma16(vg, ld_off[i], (uint32_t)(uintptr_t)(lds_ptr_t)(&sV[BUF][dst]));
     }
   };
   // after the wave's own loads landed: zero V rows of its block past kv_len
@@ -282,6 +299,17 @@ prefill_kernel(const PrefillKernelArgs a) {
   }
   int nj = ccnt;
   uint32_t nw = nj < nblk_vis ? load_words(nj) : 0u;
+  // raw (bf16) query rows for the next rotation, fetched one tile ahead (when
+  // the next tile starts a new document) so that a rotation never waits on a
+  // load; the registers stay live across the loop
+  uint4 qraw[2][KC];
+  auto load_q = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) qraw[nt][kc] = qok[nt] ? qsrc[nt][kc * 4 + lg] : make_uint4(0u, 0u, 0u, 0u);
+  };
+  load_q();
 
   // One tile on LDS buffer BUF; returns false after the last tile.
   auto step = [&](auto bufc) -> bool {
@@ -289,16 +317,6 @@ prefill_kernel(const PrefillKernelArgs a) {
     __builtin_amdgcn_s_waitcnt(0);   // this tile's loads and the next words have landed
     fix_tail(cj, ccnt, bufc);
     __syncthreads();
-
-    // a new document: fetch the raw query rows before the next tile's loads
-    const bool rotate = coff != cur_off;
-    uint4 qraw[2][KC];
-    if (rotate) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) qraw[nt][kc] = qok[nt] ? qsrc[nt][kc * 4 + lg] : make_uint4(0u, 0u, 0u, 0u);
-    }
 
     const bool more = nj < nblk_vis;
     int ncnt = 0, noff = 0, nnj = 0;
@@ -314,7 +332,7 @@ prefill_kernel(const PrefillKernelArgs a) {
     // index inside the tile.  The angle in turns is rho * turn_i +
     // frac((n0 - off) * turn_i); the large part is reduced in double, the rest
     // (< TOK turns) evaluated with v_sin/v_cos.
-    if (rotate) {
+    if (coff != cur_off) {
       cur_off = coff;
       if (lane < HALF) {
         const double t = (double)(n0 - coff) * turn_d;
@@ -340,6 +358,8 @@ prefill_kernel(const PrefillKernelArgs a) {
         }
       }
     }
+
+    if (more && noff != coff) load_q();   // the next tile starts a new document
 
     // ---- S'^T = K Q^T - r  (per lane: keys mt*16 + lg*4 + i, token nt*16 + l16)
     const char *kb = (const char *)sK[BUF];
