@@ -62,6 +62,14 @@ def decode_algorithmic_bytes(case):
     return kv, kv + qo + table
 
 
+def host_threads():
+    """Host cores this process may run on (the oracle's BLAS thread count)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline_decode(case, dc, seconds):
     """The oracle, single-threaded, on whole (sequence, KV head) groups of the
     same workload until `seconds` of CPU work; scaled to GB/s of K+V."""
@@ -73,7 +81,8 @@ def cpu_baseline_decode(case, dc, seconds):
     q = W.to_float(case.q, case.dtype)
     g = case.num_q_heads // case.num_kv_heads
     done_bytes, groups, t_used = 0, 0, 0.0
-    with threadpool_limits(1):
+    nthr = host_threads()
+    with threadpool_limits(nthr):
         for b in range(case.batch):
             nb = -(-int(case.seq_lens[b]) // 16)
             ids = (lay.table[b, :nb] & 0xFFFF).astype(np.int64)
@@ -95,45 +104,126 @@ def cpu_baseline_decode(case, dc, seconds):
                     break
             if t_used >= seconds:
                 break
-    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": nthr, "kind": "oracle",
             "sample": f"{groups} (sequence, KV head) groups of llama8b_decode "
-                      f"({groups * g} query heads x 8193 tokens), {t_used:.1f} s, float64 numpy, 1 thread"}
+                      f"({groups * g} query heads x 8193 tokens), {t_used:.1f} s, float64 numpy, "
+                      f"{nthr} BLAS threads"}
 
 
 def cpu_baseline_prefill(case, dc, seconds):
-    """The oracle on prompt rows of one (sequence, head) of the prefill workload."""
+    """The oracle on the prompt rows of (sequence, head) pairs of the prefill
+    workload, head by head, until `seconds` of CPU work."""
     from threadpoolctl import threadpool_limits
     import oracle
     import workloads as W
     import torch
     lay = case.layout
-    b, h = 0, 0
     g = case.num_q_heads // case.num_kv_heads
-    nb = -(-int(case.seq_lens[b]) // 16)
-    ids = (lay.table[b, :nb] & 0xFFFF).astype(np.int64)
-    sel = torch.from_numpy(ids).to(dc.k_pool.device)
-    kp = W.to_float(dc.k_pool.index_select(0, sel), case.dtype)
-    vp = W.to_float(dc.v_pool.index_select(0, sel), case.dtype)
-    row = ((lay.table[b, :nb] & 0xFFFF0000) | np.arange(nb, dtype=np.uint32)).astype(np.uint32)
     q = W.to_float(case.q, case.dtype)
     plen = case.max_q_len
-    kv_len = int(case.seq_lens[b])
-    cached = kv_len - plen
-    flops, t_used, rows_done = 0, 0.0, 0
-    with threadpool_limits(1):
-        for r0 in range(0, plen, 128):
-            rows = np.arange(r0, min(plen, r0 + 128))
-            t0 = time.perf_counter()
-            oracle.prefill_rows(q[rows, h], rows, plen, int(lay.tail_pos[b]), kp, vp, row, kv_len,
-                                h // g, case.scale, case.rope_theta)
-            t_used += time.perf_counter() - t0
-            flops += 4 * case.head_dim * int(np.sum(cached + rows + 1))
-            rows_done += len(rows)
+    flops, t_used, rows_done, heads = 0, 0.0, 0, 0
+    nthr = host_threads()
+    with threadpool_limits(nthr):
+        for b in range(case.batch):
+            nb = -(-int(case.seq_lens[b]) // 16)
+            ids = (lay.table[b, :nb] & 0xFFFF).astype(np.int64)
+            sel = torch.from_numpy(ids).to(dc.k_pool.device)
+            kp = W.to_float(dc.k_pool.index_select(0, sel), case.dtype)
+            vp = W.to_float(dc.v_pool.index_select(0, sel), case.dtype)
+            row = ((lay.table[b, :nb] & 0xFFFF0000) | np.arange(nb, dtype=np.uint32)).astype(np.uint32)
+            kv_len = int(case.seq_lens[b])
+            cached = kv_len - plen
+            q0 = int(case.cu_q_lens[b])
+            for h in range(case.num_q_heads):
+                for r0 in range(0, plen, 128):
+                    rows = np.arange(r0, min(plen, r0 + 128))
+                    t0 = time.perf_counter()
+                    oracle.prefill_rows(q[q0 + rows, h], rows, plen, int(lay.tail_pos[b]), kp, vp, row,
+                                        kv_len, h // g, case.scale, case.rope_theta)
+                    t_used += time.perf_counter() - t0
+                    flops += 4 * case.head_dim * int(np.sum(cached + rows + 1))
+                    rows_done += len(rows)
+                heads += 1
+                if t_used >= seconds:
+                    break
             if t_used >= seconds:
                 break
-    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows_done} prompt rows of one (sequence, head) of llama8b_prefill, "
-                      f"{t_used:.1f} s, float64 numpy, 1 thread"}
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": nthr, "kind": "oracle",
+            "sample": f"{rows_done} prompt rows ({heads} (sequence, head) pairs) of llama8b_prefill, "
+                      f"{t_used:.1f} s, float64 numpy, {nthr} BLAS threads"}
+
+
+def overhead_main(args):
+    """Cost of laziness: the lazy kernels against the non-lazy baseline
+    (lazyattn_*_eager: keys taken as already rotated to absolute positions,
+    offsets ignored, the query rotated once) on identical inputs.  Launches
+    alternate lazy / eager so clock drift hits both alike; medians of
+    `args.steps` launches each.  Also a documents-per-sequence sweep of the 8B
+    decode shape (1, 16, 64 documents per 8192-token sequence).  One JSON line."""
+    import torch
+    import position_agnostic_kv_amd as pak
+    import workloads as W
+    from workloads.device import DeviceInputs
+
+    pak.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def ab(run_lazy, run_eager):
+        for _ in range(args.warmup):
+            run_lazy()
+            run_eager()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for e in ev:
+            e[0].record()
+            run_lazy()
+            e[1].record()
+            run_eager()
+            e[2].record()
+        torch.cuda.synchronize()
+        lazy = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+        eager = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+        return {"lazy_ms": round(lazy, 4), "eager_ms": round(eager, 4),
+                "overhead_pct": round(100.0 * (lazy - eager) / eager, 3)}
+
+    def decode_ab(case):
+        W.materialize_torch(case, dev)
+        d = DeviceInputs(case, dev)
+        pak.kvcache_append(d.k_pool, d.v_pool, d.k_new, d.v_new, d.slots)
+        out = torch.empty_like(d.q)
+        kw = dict(scale=case.scale, rope_theta=case.rope_theta, out=out)
+        r = ab(lambda: pak.lazyattn_decode(d.q, d.q_pos, d.k_pool, d.v_pool, d.table, d.seq_lens, **kw),
+               lambda: pak.lazyattn_decode_eager(d.q, d.q_pos, d.k_pool, d.v_pool, d.table, d.seq_lens, **kw))
+        docs = [len(x) for x in case.layout.doc_spans]
+        r["docs_per_seq"] = round(float(np.mean(docs)), 2)
+        r["offset_changes_per_seq"] = round(float(np.mean(docs)) + 1, 2)  # + the new token's block
+        del d, out
+        case.q = case.k_pool = case.v_pool = case.k_new = case.v_new = None
+        torch.cuda.empty_cache()
+        return r
+
+    res = {"metric": "lazy vs eager (non-lazy baseline) kernel time, same inputs", "unit": "ms",
+           "steps": args.steps, "warmup": args.warmup, "data": "synthetic"}
+    res["decode_llama8b"] = decode_ab(W.llama8b_decode())
+    pcase = W.llama8b_prefill()
+    W.materialize_torch(pcase, dev)
+    pd = DeviceInputs(pcase, dev)
+    pak.kvcache_append(pd.k_pool, pd.v_pool, pd.k_new, pd.v_new, pd.slots)
+    pout = torch.empty_like(pd.q)
+    pkw = dict(scale=pcase.scale, rope_theta=pcase.rope_theta, out=pout)
+    res["prefill_llama8b"] = ab(
+        lambda: pak.lazyattn_prefill(pd.q, pd.cu, pd.q_pos_start, pd.k_pool, pd.v_pool, pd.table,
+                                     pd.seq_lens, pcase.max_q_len, **pkw),
+        lambda: pak.lazyattn_prefill_eager(pd.q, pd.cu, pd.q_pos_start, pd.k_pool, pd.v_pool, pd.table,
+                                           pd.seq_lens, pcase.max_q_len, **pkw))
+    del pd, pout
+    torch.cuda.empty_cache()
+    sweep = {}
+    for label, blocks in (("1_doc", (512, 512)), ("16_docs", (32, 32)), ("64_docs", (8, 8))):
+        sweep[label] = decode_ab(W.decode_case(2, 64, 32, 8, 128, 8192, blocks, name=f"sweep_{label}"))
+    res["decode_docs_sweep"] = sweep
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -144,6 +234,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-blocks", type=int, default=0)
+    ap.add_argument("--overhead", action="store_true",
+                    help="time the lazy kernels against the non-lazy baseline instead (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for rocprofv3 counter scaling)")
     args = ap.parse_args()
@@ -152,6 +244,9 @@ def main():
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    if args.overhead:
+        overhead_main(args)
+        return
 
     import torch
     import position_agnostic_kv_amd as pak
@@ -214,6 +309,26 @@ def main():
     def mean_ms(i, j):
         return float(np.mean([e[i].elapsed_time(e[j]) for e in events]))
 
+    def pct_ms(i, j):
+        x = np.array([e[i].elapsed_time(e[j]) for e in events])
+        return {"p10": round(float(np.percentile(x, 10)), 4), "p50": round(float(np.median(x)), 4),
+                "p90": round(float(np.percentile(x, 90)), 4)}
+
+    # measured copy roof (outside the timed region): a plain 2 GiB device copy
+    # (torch's copy kernel), bytes read + written per second
+    csrc = torch.empty(1 << 30, dtype=torch.int16, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+    cev[0].record()
+    for i in range(10):
+        cdst.copy_(csrc)
+        cev[i + 1].record()
+    torch.cuda.synchronize()
+    copy_ms = float(np.median([cev[i].elapsed_time(cev[i + 1]) for i in range(10)]))
+    copy_gbps = 2 * csrc.numel() * 2 / (copy_ms * 1e-3) / 1e9
+    del csrc, cdst
+
     decode_pass_ms = mean_ms(0, 2)
     decode_kernel_ms = mean_ms(1, 2)
     prefill_kernel_ms = mean_ms(3, 4)
@@ -251,6 +366,11 @@ def main():
         "prefill_pass_ms": round(prefill_pass_ms, 4),
         "prefill_kernel_ms": round(prefill_kernel_ms, 4),
         "prefill_tflops": round(pf_tflops, 2),
+        "decode_kernel_ms_pct": pct_ms(1, 2),
+        "prefill_kernel_ms_pct": pct_ms(3, 4),
+        "copy_roof": {"gbps": round(copy_gbps, 1), "bytes_moved": 2 * (1 << 31),
+                      "note": "2 GiB device-to-device copy (read + write), median of 10"},
+        "decode_frac_of_copy_roof": round(dec_achieved / copy_gbps, 4),
         "wall_s_timed": round(wall, 3),
         "roofline": {
             "kernel": "lazyattn::decode_split_kernel<bf16, 128, 4>",

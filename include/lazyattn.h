@@ -153,6 +153,31 @@ int lazyattn_prefill(void *out, const void *q, int total_q, const int32_t *cu_q_
                      int batch, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
                      int num_blocks, int dtype, float scale, float rope_theta, void *stream);
 
+/*
+ * lazyattn_decode_eager, lazyattn_prefill_eager -- the non-lazy baseline that
+ * the method's overhead is measured against (LazyAttention summary,
+ * "Declaração do Problema": conventional caches hold keys already rotated to
+ * their place in the sequence, and reuse at a new place means re-encoding or
+ * re-rotating them).  Same arguments, layout, ownership and error codes as
+ * lazyattn_decode / lazyattn_prefill, with one difference in meaning: the
+ * pool's keys are taken as already rotated to their absolute positions, the
+ * offset half of every table word is ignored, and each query is rotated once
+ * by its own position.  Equivalently: the lazy call on a table whose offsets
+ * are all 0.
+ */
+int lazyattn_decode_eager(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                          const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                          const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                          int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
+                          int split_blocks, void *workspace, size_t workspace_bytes, void *stream);
+
+int lazyattn_prefill_eager(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                           const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                           const uint32_t *block_table, int max_blocks_per_seq,
+                           const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads,
+                           int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
+                           float rope_theta, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

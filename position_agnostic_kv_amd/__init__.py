@@ -9,6 +9,8 @@ Entry points (same names as the C ABI):
   kvcache_append(k_pool, v_pool, k_new, v_new, slot_mapping)
   lazyattn_decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, ...)
   lazyattn_prefill(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len, ...)
+  lazyattn_decode_eager / lazyattn_prefill_eager: the non-lazy baseline (keys
+  already rotated to absolute positions, table offsets ignored)
 """
 
 import ctypes
@@ -19,7 +21,8 @@ import torch
 
 __all__ = [
     "LazyAttnError", "lib_path", "load_library", "version", "kvcache_append",
-    "decode_workspace_size", "lazyattn_decode", "lazyattn_prefill", "BLOCK_TOKENS",
+    "decode_workspace_size", "lazyattn_decode", "lazyattn_prefill", "lazyattn_decode_eager",
+    "lazyattn_prefill_eager", "BLOCK_TOKENS",
 ]
 
 BLOCK_TOKENS = 16
@@ -38,6 +41,8 @@ _SIGNATURES = {
     "lazyattn_prefill": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _i32, _f32, _f32, _vp]),
 }
+_SIGNATURES["lazyattn_decode_eager"] = _SIGNATURES["lazyattn_decode"]
+_SIGNATURES["lazyattn_prefill_eager"] = _SIGNATURES["lazyattn_prefill"]
 
 
 class LazyAttnError(RuntimeError):
@@ -139,6 +144,20 @@ def lazyattn_decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, *, scale=No
     seq_lens [B] tokens attended.  ``workspace`` (uint8, zero-filled once) is
     allocated zeroed when not given.  Returns out [B, Hq, D] in q's dtype.
     """
+    return _decode("lazyattn_decode", q, q_pos, k_pool, v_pool, block_table, seq_lens, scale,
+                   rope_theta, split_blocks, out, workspace, stream)
+
+
+def lazyattn_decode_eager(q, q_pos, k_pool, v_pool, block_table, seq_lens, *, scale=None,
+                          rope_theta=10000.0, split_blocks=0, out=None, workspace=None, stream=None):
+    """Non-lazy baseline of lazyattn_decode: the pool holds keys already rotated
+    to their absolute positions, table offsets are ignored, q is rotated once."""
+    return _decode("lazyattn_decode_eager", q, q_pos, k_pool, v_pool, block_table, seq_lens, scale,
+                   rope_theta, split_blocks, out, workspace, stream)
+
+
+def _decode(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, rope_theta, split_blocks,
+            out, workspace, stream):
     dev = _dev(q, q_pos, k_pool, v_pool, block_table, seq_lens)
     _int32(q_pos, "q_pos")
     _int32(block_table, "block_table")
@@ -165,11 +184,11 @@ def lazyattn_decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, *, scale=No
         _dev(workspace, q)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     lib = load_library()
-    _check(lib.lazyattn_decode(_ptr(out), _ptr(q), _ptr(q_pos), _ptr(k_pool), _ptr(v_pool),
-                               _ptr(block_table), max_blocks, _ptr(seq_lens), b, hq, hkv, d, nb,
-                               _dtype_code(q), scale, float(rope_theta), int(split_blocks),
-                               _ptr(workspace), workspace.numel() * workspace.element_size(),
-                               _stream_ptr(stream, dev)), "lazyattn_decode")
+    _check(getattr(lib, fn)(_ptr(out), _ptr(q), _ptr(q_pos), _ptr(k_pool), _ptr(v_pool),
+                            _ptr(block_table), max_blocks, _ptr(seq_lens), b, hq, hkv, d, nb,
+                            _dtype_code(q), scale, float(rope_theta), int(split_blocks),
+                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                            _stream_ptr(stream, dev)), fn)
     return out
 
 
@@ -180,6 +199,20 @@ def lazyattn_prefill(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_
     The prompts' K/V must already be appended as each table's last tokens;
     kv_lens [B] counts them.  Returns out [Tq, Hq, D] bf16.
     """
+    return _prefill("lazyattn_prefill", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                    kv_lens, max_q_len, scale, rope_theta, out, stream)
+
+
+def lazyattn_prefill_eager(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len,
+                           *, scale=None, rope_theta=10000.0, out=None, stream=None):
+    """Non-lazy baseline of lazyattn_prefill: keys already rotated to their
+    absolute positions, table offsets ignored, each query row rotated once."""
+    return _prefill("lazyattn_prefill_eager", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                    kv_lens, max_q_len, scale, rope_theta, out, stream)
+
+
+def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len, scale,
+             rope_theta, out, stream):
     dev = _dev(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens)
     for t, n in ((cu_q_lens, "cu_q_lens"), (q_pos_start, "q_pos_start"), (kv_lens, "kv_lens"),
                  (block_table, "block_table")):
@@ -202,8 +235,8 @@ def lazyattn_prefill(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_
             raise LazyAttnError("out must match q")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     lib = load_library()
-    _check(lib.lazyattn_prefill(_ptr(out), _ptr(q), tq, _ptr(cu_q_lens), _ptr(q_pos_start), _ptr(k_pool),
-                                _ptr(v_pool), _ptr(block_table), block_table.shape[1], _ptr(kv_lens),
-                                b, int(max_q_len), hq, hkv, d, nb, _dtype_code(q), scale,
-                                float(rope_theta), _stream_ptr(stream, dev)), "lazyattn_prefill")
+    _check(getattr(lib, fn)(_ptr(out), _ptr(q), tq, _ptr(cu_q_lens), _ptr(q_pos_start), _ptr(k_pool),
+                            _ptr(v_pool), _ptr(block_table), block_table.shape[1], _ptr(kv_lens),
+                            b, int(max_q_len), hq, hkv, d, nb, _dtype_code(q), scale,
+                            float(rope_theta), _stream_ptr(stream, dev)), fn)
     return out

@@ -59,11 +59,12 @@ size_t lazyattn_decode_workspace_size(int batch, int num_q_heads, int num_kv_hea
                                split_blocks);
 }
 
-int lazyattn_decode(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
-                    const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
-                    const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
-                    int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
-                    int split_blocks, void *workspace, size_t workspace_bytes, void *stream) {
+static int decode_common(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                         const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                         const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                         int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
+                         int split_blocks, void *workspace, size_t workspace_bytes, void *stream,
+                         bool eager) {
   if (!valid_dtype(dtype)) return LAZYATTN_ERR_DTYPE;
   if (batch < 0 || batch > 65535 || num_kv_heads < 1 || num_kv_heads > 65535 || num_q_heads < 1 ||
       num_q_heads % num_kv_heads || !pow2_group(num_q_heads / num_kv_heads))
@@ -102,14 +103,36 @@ int lazyattn_decode(void *out, const void *q, const int32_t *q_pos, const void *
   a.split_blocks = decode_split_blocks(batch, num_kv_heads, max_blocks_per_seq, split_blocks);
   a.scale = scale;
   a.rope_theta = rope_theta;
+  a.eager = eager;
   return from_hip(launch_decode(a, bf16, (hipStream_t)stream));
 }
 
-int lazyattn_prefill(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
-                     const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
-                     const uint32_t *block_table, int max_blocks_per_seq, const int32_t *kv_lens,
-                     int batch, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
-                     int num_blocks, int dtype, float scale, float rope_theta, void *stream) {
+int lazyattn_decode(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                    const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                    const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                    int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
+                    int split_blocks, void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens,
+                       batch, num_q_heads, num_kv_heads, head_dim, num_blocks, dtype, scale,
+                       rope_theta, split_blocks, workspace, workspace_bytes, stream, false);
+}
+
+int lazyattn_decode_eager(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                          const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                          const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                          int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
+                          int split_blocks, void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens,
+                       batch, num_q_heads, num_kv_heads, head_dim, num_blocks, dtype, scale,
+                       rope_theta, split_blocks, workspace, workspace_bytes, stream, true);
+}
+
+static int prefill_common(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                          const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                          const uint32_t *block_table, int max_blocks_per_seq, const int32_t *kv_lens,
+                          int batch, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                          int num_blocks, int dtype, float scale, float rope_theta, void *stream,
+                          bool eager) {
   if (dtype != LAZYATTN_BF16) return LAZYATTN_ERR_DTYPE;
   if (batch < 0 || batch > 65535 || max_q_len < 0 || max_q_len > LAZYATTN_MAX_POSITION + 1 || total_q < 0 ||
       num_kv_heads < 1 || num_kv_heads > 65535 || num_q_heads < 1 || num_q_heads % num_kv_heads ||
@@ -142,7 +165,29 @@ int lazyattn_prefill(void *out, const void *q, int total_q, const int32_t *cu_q_
   a.max_blocks = max_blocks_per_seq;
   a.scale = scale;
   a.rope_theta = rope_theta;
+  a.eager = eager;
   return from_hip(launch_prefill(a, (hipStream_t)stream));
+}
+
+int lazyattn_prefill(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                     const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                     const uint32_t *block_table, int max_blocks_per_seq, const int32_t *kv_lens,
+                     int batch, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
+                     int num_blocks, int dtype, float scale, float rope_theta, void *stream) {
+  return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                        max_blocks_per_seq, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
+                        head_dim, num_blocks, dtype, scale, rope_theta, stream, false);
+}
+
+int lazyattn_prefill_eager(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                           const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                           const uint32_t *block_table, int max_blocks_per_seq,
+                           const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads,
+                           int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
+                           float rope_theta, void *stream) {
+  return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                        max_blocks_per_seq, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
+                        head_dim, num_blocks, dtype, scale, rope_theta, stream, true);
 }
 
 }  // extern "C"

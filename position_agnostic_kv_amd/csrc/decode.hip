@@ -80,7 +80,11 @@ struct DecodeKernelArgs {
   float scale_log2, rope_theta;
 };
 
-template <typename T, int D, int G>
+// EAGER: the non-lazy baseline the method is measured against.  The pool then
+// holds keys already rotated to their absolute positions (the eager,
+// position-adjusted copy), table offsets are ignored, and the query is rotated
+// once by its own position.
+template <typename T, int D, int G, bool EAGER>
 __global__ void __launch_bounds__(kDecodeWaves * kWave)
 decode_split_kernel(const DecodeKernelArgs a) {
   using E = Elem<T>;
@@ -202,16 +206,19 @@ decode_split_kernel(const DecodeKernelArgs a) {
   uint32_t wcur = 0;
   uint4 kc[NI], vc[NI];
   if (blk < blk1) issue(blk, wcur, kc, vc);
+  if constexpr (EAGER) rotate(n_pos);
   while (blk < blk1) {
     const int nb = blk + kDecodeWaves;
     uint32_t wn = 0;
     uint4 kn[NI], vn[NI];
     if (nb < blk1) issue(nb, wn, kn, vn);
 
-    const int off = word_offset(wcur);
-    if (off != cur_off) {
-      rotate(n_pos - off);
-      cur_off = off;
+    if constexpr (!EAGER) {
+      const int off = word_offset(wcur);
+      if (off != cur_off) {
+        rotate(n_pos - off);
+        cur_off = off;
+      }
     }
 
     // scores (log2 units) of this lane's NI rows for every head
@@ -439,7 +446,7 @@ size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int h
   return t;
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool EAGER>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   DecodeKernelArgs k;
   k.out = a.out;
@@ -463,7 +470,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   k.ws_ml = ws ? (float2 *)ws : nullptr;
   k.ws_o = ws ? (float *)(ws + off_o) : nullptr;
   const dim3 grid((unsigned)k.max_splits, (unsigned)a.num_kv_heads, (unsigned)a.batch);
-  hipLaunchKernelGGL((decode_split_kernel<T, D, G>), grid, dim3(kDecodeWaves * kWave), 0, stream, k);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, G, EAGER>), grid, dim3(kDecodeWaves * kWave), 0, stream, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k.max_splits <= 1) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D, G>), dim3((unsigned)a.num_kv_heads, (unsigned)a.batch),
@@ -471,15 +478,20 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D>
-static hipError_t dispatch_group(const DecodeArgs &a, hipStream_t s) {
+template <typename T, int D, bool EAGER>
+static hipError_t dispatch_group_e(const DecodeArgs &a, hipStream_t s) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_decode_t<T, D, 1>(a, s);
-    case 2: return launch_decode_t<T, D, 2>(a, s);
-    case 4: return launch_decode_t<T, D, 4>(a, s);
-    case 8: return launch_decode_t<T, D, 8>(a, s);
+    case 1: return launch_decode_t<T, D, 1, EAGER>(a, s);
+    case 2: return launch_decode_t<T, D, 2, EAGER>(a, s);
+    case 4: return launch_decode_t<T, D, 4, EAGER>(a, s);
+    case 8: return launch_decode_t<T, D, 8, EAGER>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <typename T, int D>
+static hipError_t dispatch_group(const DecodeArgs &a, hipStream_t s) {
+  return a.eager ? dispatch_group_e<T, D, true>(a, s) : dispatch_group_e<T, D, false>(a, s);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, bool is_bf16, hipStream_t s) {

@@ -28,6 +28,7 @@ struct DecodeArgs {
   int batch, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks;
   int split_blocks;  // resolved (> 0)
   float scale, rope_theta;
+  bool eager;        // non-lazy baseline: keys pre-rotated, offsets ignored
 };
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t stream);
 
@@ -42,6 +43,7 @@ struct PrefillArgs {
   const int32_t *kv_lens;
   int total_q, batch, max_q_len, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks;
   float scale, rope_theta;
+  bool eager;        // non-lazy baseline: keys pre-rotated, offsets ignored
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 

@@ -111,7 +111,12 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
 // conflicts: K rows feed the A operand of S^T = K Q^T with ds_read_b128, V
 // rows feed the A operand of O^T = V^T P^T through two transposing reads.
 // Two buffers: the next tile streams in while the current one is computed.
-template <int D, int HP>
+//
+// EAGER: the non-lazy baseline the method is measured against.  The pool then
+// holds keys already rotated to their absolute positions and table offsets are
+// ignored: every run has offset 0 (runs are cut only at 4 blocks), so the query
+// rows are rotated once, by their own positions, on the first tile.
+template <int D, int HP, bool EAGER>
 __global__ void __launch_bounds__(kPfWaves * kWave, 2)
 prefill_kernel(const PrefillKernelArgs a) {
   constexpr int KC = D / 32;          // 32-dim k-chunks of the QK product
@@ -220,9 +225,9 @@ prefill_kernel(const PrefillKernelArgs a) {
   // blocks jw.. that share block jw's offset (1..4), and that offset
   auto tile_of = [&](uint32_t wv, int jw, int &cnt, int &off) {
     const uint32_t w0 = __builtin_amdgcn_readfirstlane(wv);
-    off = word_offset(w0);
+    off = EAGER ? 0 : word_offset(w0);
     const uint64_t same =
-        __ballot(lane < kPfTileBlocks && jw + lane < nblk_vis && (wv >> 16) == (w0 >> 16));
+        __ballot(lane < kPfTileBlocks && jw + lane < nblk_vis && (EAGER || (wv >> 16) == (w0 >> 16)));
     cnt = __builtin_ctzll(~same);
   };
   auto issue_tile = [&](uint32_t wv, int cnt, auto bufc) {
@@ -374,15 +379,21 @@ prefill_kernel(const PrefillKernelArgs a) {
 #pragma unroll
       for (int mt = 0; mt < kPfTileBlocks; ++mt) S[mt][0] = S[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    // per 32-key half; a run of at most 2 blocks (the end of a document)
+    // skips the second half's products (its scores are masked below)
+    auto qk_half = [&](int h) {
 #pragma unroll
-    for (int mt = 0; mt < kPfTileBlocks; ++mt) {
+      for (int mt = 2 * h; mt < 2 * h + 2; ++mt) {
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const bf16x8_t ka = as_bf16x8(*(const uint4 *)(kb + mt * 16 * ROWB + k_off[kc]));
-        S[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bq[0][kc], S[mt][0], 0, 0, 0);
-        S[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bq[1][kc], S[mt][1], 0, 0, 0);
+        for (int kc = 0; kc < KC; ++kc) {
+          const bf16x8_t ka = as_bf16x8(*(const uint4 *)(kb + mt * 16 * ROWB + k_off[kc]));
+          S[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bq[0][kc], S[mt][0], 0, 0, 0);
+          S[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bq[1][kc], S[mt][1], 0, 0, 0);
+        }
       }
-    }
+    };
+    qk_half(0);
+    if (ccnt > kPfTileBlocks / 2) qk_half(1);
 
     // ---- mask: keys past the tile's run, past kv_len, or after the query token.
     // Per lane and query column, keys mt*16 + lg*4 + i of the tile stay when
@@ -466,17 +477,18 @@ prefill_kernel(const PrefillKernelArgs a) {
     // ---- O^T += V^T P^T: A operand rows = dims, k-slots = keys
     // 32ks + lg*4 + 0..3 and 32ks + 16 + lg*4 + 0..3, read transposed.
     const char *vb = (const char *)sV[BUF];
+    auto pv_half = [&](int ks) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int dt = 0; dt < DT; ++dt) {
         const uint2 lo = lds_read_tr16((const uint16_t *)(vb + ks * 32 * ROWB + v_off[dt]));
         const uint2 up = lds_read_tr16((const uint16_t *)(vb + (ks * 32 + 16) * ROWB + v_off[dt]));
         const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, up.x, up.y));
         O[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[ks][0], O[dt][0], 0, 0, 0);
         O[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[ks][1], O[dt][1], 0, 0, 0);
       }
-    }
+    };
+    pv_half(0);
+    if (ccnt > kPfTileBlocks / 2) pv_half(1);   // a short run has no keys there
 
     if (!more) return false;
     cj = nj;
@@ -511,7 +523,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   }
 }
 
-template <int D, int HP>
+template <int D, int HP, bool EAGER>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   PrefillKernelArgs k;
   k.out = (uint16_t *)a.out;
@@ -537,16 +549,21 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   const long long grid = (long long)(k.num_units + kXcds - 1) / kXcds * kXcds * k.tok_tiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D, HP>), dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream, k);
+  hipLaunchKernelGGL((prefill_kernel<D, HP, EAGER>), dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream, k);
   return hipGetLastError();
+}
+
+template <int D, bool EAGER>
+static hipError_t launch_prefill_e(const PrefillArgs &a, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  if (group % 4 == 0) return launch_prefill_t<D, 4, EAGER>(a, stream);
+  if (group % 2 == 0) return launch_prefill_t<D, 2, EAGER>(a, stream);
+  return launch_prefill_t<D, 1, EAGER>(a, stream);
 }
 
 template <int D>
 static hipError_t launch_prefill_d(const PrefillArgs &a, hipStream_t stream) {
-  const int group = a.num_q_heads / a.num_kv_heads;
-  if (group % 4 == 0) return launch_prefill_t<D, 4>(a, stream);
-  if (group % 2 == 0) return launch_prefill_t<D, 2>(a, stream);
-  return launch_prefill_t<D, 1>(a, stream);
+  return a.eager ? launch_prefill_e<D, true>(a, stream) : launch_prefill_e<D, false>(a, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {

@@ -53,9 +53,22 @@ def decode(lib, **kw):
     a = dict(out=P, q=P, q_pos=P, k=P, v=P, table=P, max_blocks=4, seq_lens=P, batch=2, hq=8, hkv=2,
              d=128, nb=16, dtype=1, scale=0.088, theta=1e4, split=0, ws=P, ws_bytes=1 << 30, stream=NULL)
     a.update(kw)
-    return lib.lazyattn_decode(a["out"], a["q"], a["q_pos"], a["k"], a["v"], a["table"], a["max_blocks"],
-                               a["seq_lens"], a["batch"], a["hq"], a["hkv"], a["d"], a["nb"], a["dtype"],
-                               a["scale"], a["theta"], a["split"], a["ws"], a["ws_bytes"], a["stream"])
+    fn = lib.lazyattn_decode_eager if a.pop("eager", False) else lib.lazyattn_decode
+    return fn(a["out"], a["q"], a["q_pos"], a["k"], a["v"], a["table"], a["max_blocks"],
+              a["seq_lens"], a["batch"], a["hq"], a["hkv"], a["d"], a["nb"], a["dtype"],
+              a["scale"], a["theta"], a["split"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_eager_baseline_checks_arguments_alike(lib):
+    for kw in ({"dtype": 7}, {"hq": 6, "hkv": 4}, {"d": 96}, {"split": 2}, {"q": NULL},
+               {"batch": 0, "q": NULL}, {"ws": NULL, "max_blocks": 4000}):
+        assert decode(lib, eager=True, **kw) == decode(lib, **kw)
+    f, g = lib.lazyattn_prefill, lib.lazyattn_prefill_eager
+    ok = [P, P, 4096, P, P, P, P, P, 8, P, 2, 128, 32, 8, 128, 64, 1, 0.088, 5e5, NULL]
+    for idx, val in ((16, 0), (14, 256), (2, -1), (1, NULL)):
+        bad = list(ok)
+        bad[idx] = val
+        assert g(*bad) == f(*bad) != 0
 
 
 def test_decode_argument_errors(lib):
