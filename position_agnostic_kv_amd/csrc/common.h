@@ -40,6 +40,14 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// max of four scores that are never NaN (v_max3_f32 + v_max_f32), without the
+// canonicalising moves that fmaxf's NaN rules add.
+__device__ __forceinline__ float max4_nn(float a, float b, float c, float d) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3\n\tv_max_f32 %0, %0, %4" : "=&v"(r) : "v"(a), "v"(b), "v"(c), "v"(d));
+  return r;
+}
+
 // Dword w (a compile-time constant after unrolling) of a 16-byte chunk.
 __device__ __forceinline__ uint32_t dw4(const uint4 &v, int w) {
   return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
@@ -96,6 +104,37 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 32) x += __shfl_xor(x, 16);
   if constexpr (N >= 64) x += __shfl_xor(x, 32);
   return x;
+}
+
+// group_sum over the n values x[0..n): each DPP step is applied to all values
+// before the next step, so a value is never read by DPP right after the
+// instruction that wrote it (no wait states between dependent DPP adds).
+template <int N, int n>
+__device__ __forceinline__ void group_sum_all(float *x) {
+  if constexpr (N >= 2) {
+#pragma unroll
+    for (int j = 0; j < n; ++j) x[j] += dpp_f32<kDppQuadXor1>(x[j]);
+  }
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int j = 0; j < n; ++j) x[j] += dpp_f32<kDppQuadXor2>(x[j]);
+  }
+  if constexpr (N >= 8) {
+#pragma unroll
+    for (int j = 0; j < n; ++j) x[j] += dpp_f32<kDppRowHalfMirror>(x[j]);
+  }
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int j = 0; j < n; ++j) x[j] += dpp_f32<kDppRowMirror>(x[j]);
+  }
+  if constexpr (N >= 32) {
+#pragma unroll
+    for (int j = 0; j < n; ++j) x[j] += __shfl_xor(x[j], 16);
+  }
+  if constexpr (N >= 64) {
+#pragma unroll
+    for (int j = 0; j < n; ++j) x[j] += __shfl_xor(x[j], 32);
+  }
 }
 
 // Reduce over lanes l, l^16, l^32, l^48 (the four lane groups holding one

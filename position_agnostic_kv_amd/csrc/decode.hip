@@ -43,7 +43,9 @@
 namespace lazyattn {
 
 constexpr int kDecodeWaves = 4;
+constexpr int kXcds = 8;
 constexpr float kRescaleSlack = 8.0f;  // in log2 units
+constexpr float kMaxFloor = -0x1p127f;  // below any finite score that does not overflow
 
 template <typename T>
 struct Elem;
@@ -76,7 +78,11 @@ struct DecodeKernelArgs {
   const int32_t *seq_lens;
   float *ws_o;    // [B][Hkv][S][G][D]
   float2 *ws_ml;  // [B][Hkv][S][G] (max, sum)
-  int max_blocks, num_kv_heads, num_blocks, split_blocks, max_splits;
+  int max_blocks;
+  int num_kv_heads;  // work heads: KV heads x head split (each takes G query heads)
+  int kv_shift;      // log2 of the head split
+  int num_units;     // splits x KV heads x batch
+  int num_blocks, split_blocks, max_splits;
   float scale_log2, rope_theta;
 };
 
@@ -104,13 +110,23 @@ decode_split_kernel(const DecodeKernelArgs a) {
   __shared__ float s_o[kDecodeWaves][G][D];
   __shared__ int s_bad;
 
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  // Work item -> (split, KV head, sequence).  A KV head whose query heads are
+  // split over 2^kv_shift workgroups gives them consecutive slots on one XCD
+  // (workgroups go round-robin over the XCDs), so they run side by side and
+  // the twin reads of each K/V block are served by that XCD's L2.
+  const int hkv = a.num_kv_heads;
+  const int slot = blockIdx.x / kXcds;
+  const int hsub = slot & ((1 << a.kv_shift) - 1);
+  const int unit = (slot >> a.kv_shift) * kXcds + (int)(blockIdx.x % kXcds);
+  if (unit >= a.num_units) return;
+  const int hkv_pool = hkv >> a.kv_shift;
+  const int split = unit % a.max_splits;
+  const int gp = (unit / a.max_splits) % hkv_pool;    // KV head in the pool
+  const int b = unit / a.max_splits / hkv_pool;
+  const int g = (gp << a.kv_shift) | hsub;            // work head: query heads g*G .. g*G+G-1
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: SGPR
-  const int hkv = a.num_kv_heads;
   const int hq = hkv * G;
 
   const int seq_len = a.seq_lens[b];
@@ -144,9 +160,12 @@ decode_split_kernel(const DecodeKernelArgs a) {
   float qf[G][kBf16 ? 1 : EPL];
   float acc[G][EPL];
   float m[G], l[G];
+  // Running maxima start at a finite floor far below any score: the first
+  // block with a finite score always rescales (alpha = 2^(floor - max) = 0),
+  // masked scores (-inf) give p = 0, and p needs no guard against -inf - -inf.
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
+    m[h] = kMaxFloor;
     l[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
@@ -166,11 +185,14 @@ decode_split_kernel(const DecodeKernelArgs a) {
       bad = true;
       id = 0;
     }
-    const size_t base = ((size_t)id * hkv + g) * kChunksPerHeadBlock + lane;
+    // wave-uniform block base (scalar registers) + a 32-bit lane offset
+    const size_t hb = ((size_t)id * hkv_pool + gp) * kChunksPerHeadBlock;
+    const uint4 *kb = a.k_pool + hb;
+    const uint4 *vb = a.v_pool + hb;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kk[i] = a.k_pool[base + (size_t)i * kWave];
+    for (int i = 0; i < NI; ++i) kk[i] = kb[lane + i * kWave];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vv[i] = a.v_pool[base + (size_t)i * kWave];
+    for (int i = 0; i < NI; ++i) vv[i] = vb[lane + i * kWave];
   };
 
   // q' = rot(q, n - off) * scale * log2(e), for this lane's dims and all G heads.
@@ -202,24 +224,35 @@ decode_split_kernel(const DecodeKernelArgs a) {
     }
   };
 
+  // Two register sets for K/V take turns as "current" and "next" block: the
+  // loop body runs twice per iteration with their roles swapped, so no
+  // registers are copied between blocks.  The second pass of the last
+  // iteration may find no block left (blk >= blk1); it then masks every row
+  // (the partial-block path) and adds nothing.
+  // Loads are issued unconditionally (a conditional load would make the
+  // compiler copy the landed registers, i.e. wait for them, right after
+  // issuing): past the split's last block they re-read that block (an L2 hit)
+  // and the step that takes it masks every row.
   int blk = blk0 + wave;
-  uint32_t wcur = 0;
-  uint4 kc[NI], vc[NI];
-  if (blk < blk1) issue(blk, wcur, kc, vc);
+  const int blast = blk1 - 1;  // >= blk0: a split has at least one block
+  uint32_t wA = 0, wB = 0;
+  uint4 kA[NI], vA[NI], kB[NI], vB[NI];
+  issue(min(blk, blast), wA, kA, vA);
   if constexpr (EAGER) rotate(n_pos);
-  while (blk < blk1) {
-    const int nb = blk + kDecodeWaves;
-    uint32_t wn = 0;
-    uint4 kn[NI], vn[NI];
-    if (nb < blk1) issue(nb, wn, kn, vn);
-
+  auto step = [&](const uint32_t &wcur, uint4 (&kc)[NI], uint4 (&vc)[NI], uint32_t &wn, uint4 (&kn)[NI],
+                  uint4 (&vn)[NI]) {
+    // a new document: re-rotate the query (the lazy rotation).  Done before
+    // the next block's loads are issued, so that the rotation's temporaries
+    // never share registers with loads in flight.
     if constexpr (!EAGER) {
       const int off = word_offset(wcur);
-      if (off != cur_off) {
+      if (off != cur_off && blk < blk1) {
         rotate(n_pos - off);
         cur_off = off;
       }
     }
+    const int nb = blk + kDecodeWaves;
+    issue(min(nb, blast), wn, kn, vn);
 
     // scores (log2 units) of this lane's NI rows for every head
     float s[NI][G];
@@ -227,19 +260,26 @@ decode_split_kernel(const DecodeKernelArgs a) {
     for (int i = 0; i < NI; ++i) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float t = 0.f;
+        float t;
         if constexpr (kBf16) {
+          t = dot2_bf16(qp[h][0], dw4(kc[i], 0), 0.f);
 #pragma unroll
-          for (int w = 0; w < EPL / 2; ++w) t = dot2_bf16(qp[h][w], dw4(kc[i], w), t);
+          for (int w = 1; w < EPL / 2; ++w) t = dot2_bf16(qp[h][w], dw4(kc[i], w), t);
         } else {
+          t = qf[h][0] * __uint_as_float(dw4(kc[i], 0));
 #pragma unroll
-          for (int w = 0; w < EPL; ++w) t = fmaf(qf[h][w], __uint_as_float(dw4(kc[i], w)), t);
+          for (int w = 1; w < EPL; ++w) t = fmaf(qf[h][w], __uint_as_float(dw4(kc[i], w)), t);
         }
-        s[i][h] = group_sum<LPT>(t);
+        s[i][h] = t;
       }
     }
-    const int nvalid = seq_len - blk * kBlockTokens;
-    if (nvalid < kBlockTokens) {  // last, partly filled block
+    // sum the partial products over the LPT lanes of each row, one DPP step at
+    // a time over all NI*G values (independent neighbours: no wait states)
+    group_sum_all<LPT, NI * G>(&s[0][0]);
+    // rows of this block that count: all but the tail of a sequence's last
+    // block, none once the split is exhausted (blk >= blk1: a re-read block)
+    const int nvalid = blk < blk1 ? seq_len - blk * kBlockTokens : 0;
+    if (nvalid < kBlockTokens) {  // partly filled or exhausted
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         if (i * TPI + r >= nvalid) {
@@ -254,16 +294,20 @@ decode_split_kernel(const DecodeKernelArgs a) {
     bool need = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      bm[h] = s[0][h];
+      if constexpr (NI == 4) {
+        bm[h] = max4_nn(s[0][h], s[1][h], s[2][h], s[3][h]);
+      } else {
+        bm[h] = s[0][h];
 #pragma unroll
-      for (int i = 1; i < NI; ++i) bm[h] = fmaxf(bm[h], s[i][h]);
+        for (int i = 1; i < NI; ++i) bm[h] = fmaxf(bm[h], s[i][h]);
+      }
       need |= bm[h] > m[h] + kRescaleSlack;
     }
     if (wave_any(need)) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float mn = fmaxf(m[h], bm[h]);
-        const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m[h] - mn);
+        const float alpha = fast_exp2(m[h] - mn);  // 0 on the first rescale
         l[h] *= alpha;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
@@ -273,20 +317,20 @@ decode_split_kernel(const DecodeKernelArgs a) {
 
     float p[NI][G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float ms = m[h] == -INFINITY ? 0.f : m[h];
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        p[i][h] = fast_exp2(s[i][h] - ms);
-        l[h] += p[i][h];
-      }
-    }
+      for (int i = 0; i < NI; ++i) p[i][h] = fast_exp2(s[i][h] - m[h]);
     if constexpr (kBf16) {
+      // P.V pairs token rows i, i+1; the row sums take the same bf16-rounded
+      // weights that P.V uses
 #pragma unroll
       for (int i = 0; i < NI; i += 2) {
         uint32_t pp[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) pp[h] = pack_bf16x2(p[i][h], p[i + 1][h]);
+        for (int h = 0; h < G; ++h) {
+          pp[h] = pack_bf16x2(p[i][h], p[i + 1][h]);
+          l[h] = dot2_bf16(pp[h], 0x3f803f80u, l[h]);
+        }
 #pragma unroll
         for (int w = 0; w < EPL / 2; ++w) {
           const uint32_t v0 = dw4(vc[i], w), v1 = dw4(vc[i + 1], w);
@@ -303,19 +347,18 @@ decode_split_kernel(const DecodeKernelArgs a) {
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int h = 0; h < G; ++h) {
+          l[h] += p[i][h];
 #pragma unroll
           for (int e = 0; e < EPL; ++e)
             acc[h][e] = fmaf(p[i][h], __uint_as_float(dw4(vc[i], e)), acc[h][e]);
-    }
-
-    wcur = wn;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      kc[i] = kn[i];
-      vc[i] = vn[i];
+        }
     }
     blk = nb;
+  };
+  while (blk < blk1) {
+    step(wA, kA, vA, wB, kB, vB);
+    step(wB, kB, vB, wA, kA, vA);
   }
 
   // merge the TPI row streams of this wave (lanes with equal c)
@@ -416,11 +459,20 @@ decode_combine_kernel(const DecodeKernelArgs a) {
 // ------------------------------------------------------------------- host side
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int decode_split_blocks(int batch, int num_kv_heads, int max_blocks_per_seq, int requested) {
+// Query heads of one KV head per workgroup: G = 8 keeps 8 heads x 8 dims of
+// output accumulators per lane and caps the kernel at one wave per SIMD, too
+// few loads in flight to cover HBM latency; two workgroups of 4 heads each
+// (sharing every K/V block through L2) run at two waves per SIMD.
+int decode_head_split(int num_q_heads, int num_kv_heads) {
+  return num_q_heads / num_kv_heads == 8 ? 2 : 1;
+}
+
+int decode_split_blocks(int batch, int num_q_heads, int num_kv_heads, int max_blocks_per_seq,
+                        int requested) {
   if (requested > 0) return requested;
-  // Enough (sequence, KV head) units to fill the chip at two workgroups per CU:
-  // one split each.  Otherwise cut sequences so ~1024 workgroups run.
-  const long long units = (long long)batch * num_kv_heads;
+  // Enough (sequence, work head) units to fill the chip at two workgroups per
+  // CU: one split each.  Otherwise cut sequences so ~1024 workgroups run.
+  const long long units = (long long)batch * num_kv_heads * decode_head_split(num_q_heads, num_kv_heads);
   if (units >= 512) return max_blocks_per_seq;
   long long sb = (units * max_blocks_per_seq + 1023) / 1024;
   if (sb < 32) sb = 32;
@@ -439,7 +491,7 @@ static void workspace_layout(int batch, int num_q_heads, int num_kv_heads, int h
 
 size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                              int max_blocks_per_seq, int split_blocks) {
-  const int sb = decode_split_blocks(batch, num_kv_heads, max_blocks_per_seq, split_blocks);
+  const int sb = decode_split_blocks(batch, num_q_heads, num_kv_heads, max_blocks_per_seq, split_blocks);
   if ((max_blocks_per_seq + sb - 1) / sb <= 1) return 0;  // one split: no partials
   size_t off_o, t;
   workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sb, &off_o, &t);
@@ -456,31 +508,38 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   k.v_pool = (const uint4 *)a.v_pool;
   k.table = a.table;
   k.seq_lens = a.seq_lens;
+  const int hsplit = a.num_q_heads / a.num_kv_heads / G;  // work heads per KV head
+  const int work_heads = a.num_kv_heads * hsplit;
   k.max_blocks = a.max_blocks;
-  k.num_kv_heads = a.num_kv_heads;
+  k.num_kv_heads = work_heads;
+  k.kv_shift = hsplit == 1 ? 0 : hsplit == 2 ? 1 : hsplit == 4 ? 2 : 3;
   k.num_blocks = a.num_blocks;
   k.split_blocks = a.split_blocks;
   k.max_splits = (a.max_blocks + a.split_blocks - 1) / a.split_blocks;
   k.scale_log2 = a.scale * kLog2e;
   k.rope_theta = a.rope_theta;
+  const long long units = (long long)k.max_splits * a.num_kv_heads * a.batch;
+  const long long grid = (units + kXcds - 1) / kXcds * kXcds * hsplit;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  k.num_units = (int)units;
   size_t off_o, total;
-  workspace_layout(a.batch, a.num_q_heads, a.num_kv_heads, a.head_dim, a.max_blocks,
-                   a.split_blocks, &off_o, &total);
+  workspace_layout(a.batch, a.num_q_heads, work_heads, a.head_dim, a.max_blocks, a.split_blocks,
+                   &off_o, &total);
   char *ws = (char *)a.workspace;
   k.ws_ml = ws ? (float2 *)ws : nullptr;
   k.ws_o = ws ? (float *)(ws + off_o) : nullptr;
-  const dim3 grid((unsigned)k.max_splits, (unsigned)a.num_kv_heads, (unsigned)a.batch);
-  hipLaunchKernelGGL((decode_split_kernel<T, D, G, EAGER>), grid, dim3(kDecodeWaves * kWave), 0, stream, k);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, G, EAGER>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave),
+                     0, stream, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k.max_splits <= 1) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D, G>), dim3((unsigned)a.num_kv_heads, (unsigned)a.batch),
+  hipLaunchKernelGGL((decode_combine_kernel<T, D, G>), dim3((unsigned)work_heads, (unsigned)a.batch),
                      dim3(256), 0, stream, k);
   return hipGetLastError();
 }
 
 template <typename T, int D, bool EAGER>
 static hipError_t dispatch_group_e(const DecodeArgs &a, hipStream_t s) {
-  switch (a.num_q_heads / a.num_kv_heads) {
+  switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads)) {
     case 1: return launch_decode_t<T, D, 1, EAGER>(a, s);
     case 2: return launch_decode_t<T, D, 2, EAGER>(a, s);
     case 4: return launch_decode_t<T, D, 4, EAGER>(a, s);

@@ -11,8 +11,11 @@ hipError_t launch_append(void *k_pool, void *v_pool, int elem_bytes, int num_blo
                          int num_kv_heads, int head_dim, const void *k_new, const void *v_new,
                          const int32_t *slot_mapping, int num_tokens, hipStream_t stream);
 
+// Workgroups that share one KV head's query heads in a decode launch.
+int decode_head_split(int num_q_heads, int num_kv_heads);
 // Blocks per split-K partition for a decode launch (requested == 0: automatic).
-int decode_split_blocks(int batch, int num_kv_heads, int max_blocks_per_seq, int requested);
+int decode_split_blocks(int batch, int num_q_heads, int num_kv_heads, int max_blocks_per_seq,
+                        int requested);
 size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                              int max_blocks_per_seq, int split_blocks);
 
