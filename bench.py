@@ -226,6 +226,81 @@ def overhead_main(args):
     print(json.dumps(res), flush=True)
 
 
+def shapes_main(args):
+    """Kernel time of every decode workload (8B, 70B, Zipf mix) and of the 8B
+    prefill, each on its own HBM-resident inputs: medians and p10/p90 of
+    `args.steps` launches after `args.warmup`.  One JSON line."""
+    import torch
+    import position_agnostic_kv_amd as pak
+    import workloads as W
+    from workloads.device import DeviceInputs
+
+    pak.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for e in ev:
+            e[0].record()
+            fn()
+            e[1].record()
+        torch.cuda.synchronize()
+        x = np.array([e[0].elapsed_time(e[1]) for e in ev])
+        return float(np.median(x)), float(np.percentile(x, 10)), float(np.percentile(x, 90))
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    res = {"metric": "kernel time per workload (decode: K+V GB/s; prefill: attention TFLOP/s)",
+           "steps": args.steps, "warmup": args.warmup, "data": "synthetic", "peak_hbm_gbps": HBM_PEAK_GBPS,
+           "peak_bf16_tflops": BF16_PEAK_TFLOPS}
+    for name in ("llama8b_decode", "llama70b_decode", "zipf_reuse_decode"):
+        case = W.make(name)
+        W.materialize_torch(case, dev)
+        d = DeviceInputs(case, dev)
+        pak.kvcache_append(d.k_pool, d.v_pool, d.k_new, d.v_new, d.slots)
+        out = torch.empty_like(d.q)
+        wsb = pak.decode_workspace_size(case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                                        case.layout.table.shape[1], 0)
+        ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
+        med, p10, p90 = timed(lambda: pak.lazyattn_decode(d.q, d.q_pos, d.k_pool, d.v_pool, d.table, d.seq_lens,
+                                                          scale=case.scale, rope_theta=case.rope_theta,
+                                                          out=out, workspace=ws))
+        kv, alg = decode_algorithmic_bytes(case)
+        phys = int(case.k_pool.numel()) * 2 * 2 if name == "zipf_reuse_decode" else None
+        r = {"ms_p50": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
+             "kv_bytes_logical": kv, "gbps_logical": round(kv / (med * 1e-3) / 1e9, 1),
+             "frac_of_hbm_peak": round(alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+             "batch": case.batch, "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads}
+        if phys is not None:
+            r["pool_bytes_physical"] = phys
+        res[name] = r
+        del d, out, ws
+        case.q = case.k_pool = case.v_pool = case.k_new = case.v_new = None
+        torch.cuda.empty_cache()
+    case = W.llama8b_prefill()
+    W.materialize_torch(case, dev)
+    d = DeviceInputs(case, dev)
+    pak.kvcache_append(d.k_pool, d.v_pool, d.k_new, d.v_new, d.slots)
+    out = torch.empty_like(d.q)
+    med, p10, p90 = timed(lambda: pak.lazyattn_prefill(d.q, d.cu, d.q_pos_start, d.k_pool, d.v_pool, d.table,
+                                                       d.seq_lens, case.max_q_len, scale=case.scale,
+                                                       rope_theta=case.rope_theta, out=out))
+    fl = case.attention_flops()
+    res["llama8b_prefill"] = {"ms_p50": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
+                              "attention_flops": fl, "tflops": round(fl / (med * 1e-3) / 1e12, 1),
+                              "frac_of_bf16_peak": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,6 +311,8 @@ def main():
     ap.add_argument("--split-blocks", type=int, default=0)
     ap.add_argument("--overhead", action="store_true",
                     help="time the lazy kernels against the non-lazy baseline instead (one JSON line)")
+    ap.add_argument("--shapes", action="store_true",
+                    help="time every decode workload and the prefill separately instead (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for rocprofv3 counter scaling)")
     args = ap.parse_args()
@@ -246,6 +323,9 @@ def main():
         sys.exit(2)
     if args.overhead:
         overhead_main(args)
+        return
+    if args.shapes:
+        shapes_main(args)
         return
 
     import torch
@@ -369,11 +449,12 @@ def main():
         "decode_kernel_ms_pct": pct_ms(1, 2),
         "prefill_kernel_ms_pct": pct_ms(3, 4),
         "copy_roof": {"gbps": round(copy_gbps, 1), "bytes_moved": 2 * (1 << 31),
-                      "note": "2 GiB device-to-device copy (read + write), median of 10"},
-        "decode_frac_of_copy_roof": round(dec_achieved / copy_gbps, 4),
+                      "note": "context only: torch's 2 GiB device-to-device copy, bytes read + written "
+                              "per second, median of 10 (a read+write stream, not the read-only "
+                              "pattern of decode)"},
         "wall_s_timed": round(wall, 3),
         "roofline": {
-            "kernel": "lazyattn::decode_split_kernel<bf16, 128, 4>",
+            "kernel": "lazyattn::decode_split_kernel<bf16, 128, 4, false>",
             "bound": "hbm",
             "achieved": round(dec_achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -383,7 +464,7 @@ def main():
             "algorithmic_bytes": dec_alg_bytes,
         },
         "roofline_prefill": {
-            "kernel": "lazyattn::prefill_kernel<128, 4>",
+            "kernel": "lazyattn::prefill_kernel<128, 4, false>",
             "bound": "mfma",
             "achieved": round(pf_tflops, 2),
             "peak": BF16_PEAK_TFLOPS,
