@@ -105,7 +105,9 @@ size_t lazyattn_decode_workspace_size(int batch, int num_q_heads, int num_kv_hea
  *   k_pool, v_pool, block_table, max_blocks_per_seq: see the layout above
  *   seq_lens    int32 [batch]: tokens of the table the query attends (>= 0)
  *   num_q_heads a multiple of num_kv_heads; query head h reads KV head
- *               h / (num_q_heads / num_kv_heads); the group size is 1, 2, 4 or 8.
+ *               h / (num_q_heads / num_kv_heads); the group size is a power
+ *               of two up to 64 (64 covers multi-query attention with
+ *               num_kv_heads = 1 and up to 64 query heads).
  *   head_dim    f32: 16, 64 or 128; bf16: 64 or 128.
  *   scale       softmax scale (usually 1/sqrt(head_dim))
  *   rope_theta  RoPE base (> 1)

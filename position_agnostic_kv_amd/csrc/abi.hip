@@ -12,7 +12,7 @@ namespace {
 
 bool valid_dtype(int dtype) { return dtype == LAZYATTN_F32 || dtype == LAZYATTN_BF16; }
 int elem_bytes(int dtype) { return dtype == LAZYATTN_F32 ? 4 : 2; }
-bool pow2_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+bool pow2_group(int g) { return g >= 1 && g <= 64 && (g & (g - 1)) == 0; }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? LAZYATTN_OK : LAZYATTN_ERR_LAUNCH; }
 

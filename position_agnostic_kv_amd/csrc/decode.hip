@@ -462,9 +462,11 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Query heads of one KV head per workgroup: G = 8 keeps 8 heads x 8 dims of
 // output accumulators per lane and caps the kernel at one wave per SIMD, too
 // few loads in flight to cover HBM latency; two workgroups of 4 heads each
-// (sharing every K/V block through L2) run at two waves per SIMD.
+// (sharing every K/V block through L2) run at two waves per SIMD.  Larger
+// groups (multi-query attention) take G / 4 workgroups of 4 heads.
 int decode_head_split(int num_q_heads, int num_kv_heads) {
-  return num_q_heads / num_kv_heads == 8 ? 2 : 1;
+  const int group = num_q_heads / num_kv_heads;
+  return group >= 8 ? group / 4 : 1;  // MQA-like groups (16..64): 4..16 workgroups of 4 heads
 }
 
 int decode_split_blocks(int batch, int num_q_heads, int num_kv_heads, int max_blocks_per_seq,
@@ -512,7 +514,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   const int work_heads = a.num_kv_heads * hsplit;
   k.max_blocks = a.max_blocks;
   k.num_kv_heads = work_heads;
-  k.kv_shift = hsplit == 1 ? 0 : hsplit == 2 ? 1 : hsplit == 4 ? 2 : 3;
+  k.kv_shift = __builtin_ctz((unsigned)hsplit);  // hsplit is a power of two
   k.num_blocks = a.num_blocks;
   k.split_blocks = a.split_blocks;
   k.max_splits = (a.max_blocks + a.split_blocks - 1) / a.split_blocks;

@@ -75,6 +75,7 @@ def test_decode_argument_errors(lib):
     assert decode(lib, dtype=7) == -2
     assert decode(lib, hq=6, hkv=4) == -3          # not a multiple
     assert decode(lib, hq=24, hkv=2) == -3         # group 12 not offered
+    assert decode(lib, hq=128, hkv=1) == -3        # groups beyond 64 not offered
     assert decode(lib, d=96) == -3
     assert decode(lib, d=16) == -3                 # bf16 needs 64/128
     assert decode(lib, nb=65537) == -3

@@ -77,6 +77,11 @@ DECODE_SMALL = [
     (W.F32, 64, 8, 2, [512, 80], (2, 8), "random", 4),
     (W.F32, 128, 8, 1, [384, 208], (2, 8), "contiguous", 4),
     (W.F32, 128, 8, 4, [256], (2, 8), "random", 0),
+    # multi-query attention (one KV head; G = 16..64 query heads per KV head)
+    (W.BF16, 128, 32, 1, [704, 208], (2, 12), "random", 0),
+    (W.BF16, 128, 64, 1, [512, 48], (2, 12), "contiguous", 8),
+    (W.BF16, 64, 16, 1, [336], (1, 9), "random", 4),
+    (W.F32, 64, 16, 1, [272, 64], (2, 6), "random", 4),
 ]
 
 
@@ -176,6 +181,7 @@ PREFILL_SMALL = [
     (128, 16, 2, [1056], [64], (3, 40), "random"),
     (64, 8, 4, [320, 48], [150, 31], (2, 10), "contiguous"),
     (64, 8, 1, [160], [260], (2, 5), "random"),
+    (128, 32, 1, [416, 96], [200, 70], (2, 9), "random"),   # multi-query attention
 ]
 
 
