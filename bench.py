@@ -301,6 +301,56 @@ def shapes_main(args):
     print(json.dumps(res), flush=True)
 
 
+def cache_sim_main(args):
+    """Hit rates of the host pool manager under a KV budget (CPU only, no GPU).
+
+    A Zipf-skewed RAG trace (the recipe of zipf_reuse_decode: a 1000-document
+    catalogue of 16*U{16..128} tokens, rank-i probability ~ i^-1.2, U{4..8}
+    distinct documents per request in random order, a 64-token prompt) is
+    placed request by request and released, for each cache-key policy.  The
+    budget is 1 GB of KV in two readings: the whole Llama-3.1-8B model
+    (32 layers x 8 KV heads x 128 dims x K,V x bf16 = 128 KiB per token: 512
+    blocks) and one layer of it (4 KiB per token: 16384 blocks).  A request
+    that does not fit counts as all misses.  One JSON line."""
+    from position_agnostic_kv_amd import cache as C
+
+    rng = np.random.default_rng(5)
+    catalogue, zipf_s, prompt = 1000, 1.2, 64
+    lens = 16 * rng.integers(16, 129, size=catalogue)
+    p = 1.0 / np.arange(1, catalogue + 1) ** zipf_s
+    p /= p.sum()
+    trace = []
+    for _ in range(args.cache_requests):
+        k = int(rng.integers(4, 9))
+        ids = rng.choice(catalogue, size=k, replace=False, p=p)
+        trace.append(([int(x) for x in ids], [int(lens[x]) for x in ids]))
+    res = {"metric": "document-token hit rate of the KV pool manager", "unit": "fraction",
+           "requests": len(trace), "data": "synthetic Zipf trace",
+           "trace": "1000 docs of 16*U{16..128} tokens, p(rank i) ~ i^-1.2, U{4..8} docs/request, 64-token prompt"}
+    for label, blocks in (("1GB_whole_8B_model_512_blocks", 512), ("1GB_one_8B_layer_16384_blocks", 16384)):
+        row = {}
+        for mode in ("agnostic", "aware", "prefix"):
+            m = C.CacheManager(blocks, mode)
+            hit = total = unplaced = 0
+            t0 = time.perf_counter()
+            for ids, ls in trace:
+                total += sum(ls)
+                try:
+                    _, miss, rid = m.acquire(ids, ls, prompt)
+                except C.CacheError:
+                    unplaced += 1
+                    continue
+                hit += sum(L for L, x in zip(ls, miss) if not x)
+                m.release(rid)
+            row[mode] = {"hit_rate": round(hit / total, 4), "unplaced_requests": unplaced,
+                         "evicted": m.stats()["evicted"],
+                         "us_per_request": round((time.perf_counter() - t0) / len(trace) * 1e6, 2)}
+        row["agnostic_over_aware"] = round(row["agnostic"]["hit_rate"] / max(row["aware"]["hit_rate"], 1e-9), 2)
+        row["agnostic_over_prefix"] = round(row["agnostic"]["hit_rate"] / max(row["prefix"]["hit_rate"], 1e-9), 2)
+        res[label] = row
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,6 +363,9 @@ def main():
                     help="time the lazy kernels against the non-lazy baseline instead (one JSON line)")
     ap.add_argument("--shapes", action="store_true",
                     help="time every decode workload and the prefill separately instead (one JSON line)")
+    ap.add_argument("--cache-sim", action="store_true",
+                    help="hit rates of the host pool manager on a Zipf trace (CPU only; one JSON line)")
+    ap.add_argument("--cache-requests", type=int, default=5000)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for rocprofv3 counter scaling)")
     args = ap.parse_args()
@@ -326,6 +379,9 @@ def main():
         return
     if args.shapes:
         shapes_main(args)
+        return
+    if args.cache_sim:
+        cache_sim_main(args)
         return
 
     import torch

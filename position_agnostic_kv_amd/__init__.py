@@ -41,6 +41,13 @@ _SIGNATURES = {
     "lazyattn_prefill": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _i32, _f32, _f32, _vp]),
 }
+_SIGNATURES.update({
+    "lazyattn_cache_create": (_vp, [_i32, _i32]),
+    "lazyattn_cache_destroy": (None, [_vp]),
+    "lazyattn_cache_acquire": (_i32, [_vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _vp]),
+    "lazyattn_cache_release": (_i32, [_vp, _i32]),
+    "lazyattn_cache_stats": (_i32, [_vp, _vp, _i32]),
+})
 _SIGNATURES["lazyattn_decode_eager"] = _SIGNATURES["lazyattn_decode"]
 _SIGNATURES["lazyattn_prefill_eager"] = _SIGNATURES["lazyattn_prefill"]
 

@@ -1,7 +1,8 @@
 """Build the lazyattn shared library for gfx950 with hipcc (in-tree).
 
-``python -m position_agnostic_kv_amd.build`` compiles every ``csrc/*.hip`` into
-``_build/`` and links ``position_agnostic_kv_amd/liblazyattn.so``.
+``python -m position_agnostic_kv_amd.build`` compiles every ``csrc/*.hip`` (with
+hipcc) and ``csrc/*.cpp`` (host-only code, with the host compiler) into ``_build/``
+and links ``position_agnostic_kv_amd/liblazyattn.so``.
 """
 
 import concurrent.futures
@@ -35,8 +36,17 @@ def _run(cmd):
     return out
 
 
+HOST_CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def host_sources():
+    """Plain C++ host code (the cache manager), built with the host compiler."""
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".cpp"))
 
 
 def build(verbose=False, jobs=None):
@@ -44,15 +54,18 @@ def build(verbose=False, jobs=None):
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
-    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 8)
+    hsrcs = host_sources()
+    hobjs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".host.o") for s in hsrcs]
+    jobs = jobs or min(len(srcs) + len(hsrcs), os.cpu_count() or 4, 8)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         futs = [ex.submit(_run, [HIPCC, *FLAGS, "-c", s, "-o", o]) for s, o in zip(srcs, objs)]
+        futs += [ex.submit(_run, [HOST_CXX, *HOST_FLAGS, "-c", s, "-o", o]) for s, o in zip(hsrcs, hobjs)]
         for f in futs:
             out = f.result()
             if verbose and out.strip():
                 print(out)
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *hobjs])
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,6 +1,6 @@
 """Host-side checks of the C ABI (no GPU): the library loads, exports every
-function include/lazyattn.h declares, and rejects bad arguments with the
-documented status codes before any launch."""
+function include/*.h declares, and rejects bad arguments with the documented
+status codes before any launch."""
 
 import ctypes
 import os
@@ -9,7 +9,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "lazyattn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -22,21 +23,23 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
     return sorted(set(names))
 
 
 def test_header_declares_the_three_calls():
     names = declared_functions()
-    for n in ("kvcache_append", "lazyattn_decode", "lazyattn_prefill"):
+    for n in ("kvcache_append", "lazyattn_decode", "lazyattn_prefill", "lazyattn_cache_acquire"):
         assert n in names
 
 
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
-        assert hasattr(lib, name), f"{name} is declared in lazyattn.h but not exported"
+        assert hasattr(lib, name), f"{name} is declared in include/ but not exported"
 
 
 def test_status_strings(lib):
