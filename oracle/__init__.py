@@ -18,6 +18,10 @@ step by step, without blocking, fusion or reordering:
 * [WHY] lynx-cortex, "00 — Por qué existe un KV Cache": sections
   "Lo que hace el decoding autorregresivo", "El remedio", "El precio".
 
+Modules: ``lazy_oracle`` (deferred-RoPE attention, append, cache bytes, the
+tiled softmax), ``alibi_oracle`` (the ALiBi variant) and ``cache_policy``
+(a plain model of the host pool manager's block and eviction policy).
+
 Every function is pinned by a ``-m "not gpu"`` test in ``tests/`` against
 something other than itself (closed forms, a complex-number formulation of
 the rotation, brute force, torch's CPU scaled_dot_product_attention, values
@@ -39,3 +43,4 @@ from .lazy_oracle import (  # noqa: F401
     tiled_softmax_dot,
     unpack_block_word,
 )
+from .alibi_oracle import alibi_slopes, decode_alibi, key_positions, prefill_alibi  # noqa: F401
