@@ -283,6 +283,16 @@ def shapes_main(args):
         if phys is not None:
             r["pool_bytes_physical"] = phys
         res[name] = r
+        if name == "llama8b_decode":  # the same inputs read with ALiBi biases instead of RoPE
+            import oracle
+            tab = torch.from_numpy(W.block_frame_table(case.layout).view(np.int32)).to(dev)
+            sl = torch.from_numpy(oracle.alibi_slopes(case.num_q_heads).astype(np.float32)).to(dev)
+            med, p10, p90 = timed(lambda: pak.lazyattn_decode_alibi(d.q, d.q_pos, d.k_pool, d.v_pool, tab,
+                                                                    d.seq_lens, sl, out=out, workspace=ws))
+            res["llama8b_decode_alibi"] = {"ms_p50": round(med, 4), "ms_p10": round(p10, 4),
+                                           "ms_p90": round(p90, 4),
+                                           "gbps_logical": round(kv / (med * 1e-3) / 1e9, 1),
+                                           "frac_of_hbm_peak": round(alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
         del d, out, ws
         case.q = case.k_pool = case.v_pool = case.k_new = case.v_new = None
         torch.cuda.empty_cache()
@@ -298,6 +308,14 @@ def shapes_main(args):
     res["llama8b_prefill"] = {"ms_p50": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
                               "attention_flops": fl, "tflops": round(fl / (med * 1e-3) / 1e12, 1),
                               "frac_of_bf16_peak": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    import oracle
+    tab = torch.from_numpy(W.block_frame_table(case.layout).view(np.int32)).to(dev)
+    sl = torch.from_numpy(oracle.alibi_slopes(case.num_q_heads).astype(np.float32)).to(dev)
+    med, p10, p90 = timed(lambda: pak.lazyattn_prefill_alibi(d.q, d.cu, d.q_pos_start, d.k_pool, d.v_pool, tab,
+                                                             d.seq_lens, case.max_q_len, sl, out=out))
+    res["llama8b_prefill_alibi"] = {"ms_p50": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
+                                    "tflops": round(fl / (med * 1e-3) / 1e12, 1),
+                                    "frac_of_bf16_peak": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
     print(json.dumps(res), flush=True)
 
 

@@ -180,6 +180,34 @@ int lazyattn_prefill_eager(void *out, const void *q, int total_q, const int32_t 
                            int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
                            float rope_theta, void *stream);
 
+/*
+ * lazyattn_decode_alibi, lazyattn_prefill_alibi -- the same attention with
+ * ALiBi linear biases instead of RoPE (the LazyAttention summary on
+ * gist.science, "Principais Contribuições" 4, names ALiBi among the position
+ * schemes deferred lazily).  Nothing rotates: the score of query position n
+ * against a key at position p is scale * q . k + slopes[h] * (p - n) for query
+ * head h.  Keys and values are stored by content only, as for RoPE; since no
+ * position is baked into a stored key, each block's table word carries the
+ * absolute position of the block's first token in its offset half, and the
+ * token in slot s sits at offset + s (a block frame).
+ *   slopes  [num_q_heads] float32, device, read only; e.g. 2^(-8 (h+1) / Hq).
+ * Every other argument, layout, ownership and status code is that of
+ * lazyattn_decode / lazyattn_prefill (rope_theta is not taken); slopes NULL
+ * gives LAZYATTN_ERR_NULL.
+ */
+int lazyattn_decode_alibi(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                          const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                          const int32_t *seq_lens, const float *slopes, int batch, int num_q_heads,
+                          int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
+                          int split_blocks, void *workspace, size_t workspace_bytes, void *stream);
+
+int lazyattn_prefill_alibi(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                           const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                           const uint32_t *block_table, int max_blocks_per_seq, const int32_t *kv_lens,
+                           const float *slopes, int batch, int max_q_len, int num_q_heads,
+                           int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "LazyAttnError", "lib_path", "load_library", "version", "kvcache_append",
     "decode_workspace_size", "lazyattn_decode", "lazyattn_prefill", "lazyattn_decode_eager",
-    "lazyattn_prefill_eager", "BLOCK_TOKENS",
+    "lazyattn_prefill_eager", "lazyattn_decode_alibi", "lazyattn_prefill_alibi", "BLOCK_TOKENS",
 ]
 
 BLOCK_TOKENS = 16
@@ -49,6 +49,10 @@ _SIGNATURES.update({
     "lazyattn_cache_stats": (_i32, [_vp, _vp, _i32]),
 })
 _SIGNATURES["lazyattn_decode_eager"] = _SIGNATURES["lazyattn_decode"]
+_SIGNATURES["lazyattn_decode_alibi"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                                               _i32, _i32, _f32, _i32, _vp, _sz, _vp])
+_SIGNATURES["lazyattn_prefill_alibi"] = (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
+                                                _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp])
 _SIGNATURES["lazyattn_prefill_eager"] = _SIGNATURES["lazyattn_prefill"]
 
 
@@ -163,8 +167,17 @@ def lazyattn_decode_eager(q, q_pos, k_pool, v_pool, block_table, seq_lens, *, sc
                    rope_theta, split_blocks, out, workspace, stream)
 
 
+def lazyattn_decode_alibi(q, q_pos, k_pool, v_pool, block_table, seq_lens, slopes, *, scale=None,
+                          split_blocks=0, out=None, workspace=None, stream=None):
+    """Decode with ALiBi biases instead of RoPE: slopes [Hq] float32 on the
+    device; each table word's offset is the absolute position of its block's
+    first token.  Otherwise as lazyattn_decode."""
+    return _decode("lazyattn_decode_alibi", q, q_pos, k_pool, v_pool, block_table, seq_lens, scale,
+                   None, split_blocks, out, workspace, stream, slopes=slopes)
+
+
 def _decode(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, rope_theta, split_blocks,
-            out, workspace, stream):
+            out, workspace, stream, slopes=None):
     dev = _dev(q, q_pos, k_pool, v_pool, block_table, seq_lens)
     _int32(q_pos, "q_pos")
     _int32(block_table, "block_table")
@@ -191,12 +204,27 @@ def _decode(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, rope_the
         _dev(workspace, q)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     lib = load_library()
+    if slopes is not None:
+        _slopes(slopes, hq, dev)
+        _check(getattr(lib, fn)(_ptr(out), _ptr(q), _ptr(q_pos), _ptr(k_pool), _ptr(v_pool),
+                                _ptr(block_table), max_blocks, _ptr(seq_lens), _ptr(slopes), b, hq, hkv,
+                                d, nb, _dtype_code(q), scale, int(split_blocks), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev)), fn)
+        return out
     _check(getattr(lib, fn)(_ptr(out), _ptr(q), _ptr(q_pos), _ptr(k_pool), _ptr(v_pool),
                             _ptr(block_table), max_blocks, _ptr(seq_lens), b, hq, hkv, d, nb,
                             _dtype_code(q), scale, float(rope_theta), int(split_blocks),
                             _ptr(workspace), workspace.numel() * workspace.element_size(),
                             _stream_ptr(stream, dev)), fn)
     return out
+
+
+def _slopes(slopes, hq, dev):
+    _dev(slopes)
+    if slopes.dtype != torch.float32 or slopes.numel() != hq or not slopes.is_contiguous():
+        raise LazyAttnError("slopes must be a contiguous float32 tensor of num_q_heads entries")
+    if slopes.device != dev:
+        raise LazyAttnError("slopes must be on the inputs' device")
 
 
 def lazyattn_prefill(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len,
@@ -218,8 +246,15 @@ def lazyattn_prefill_eager(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_tabl
                     kv_lens, max_q_len, scale, rope_theta, out, stream)
 
 
+def lazyattn_prefill_alibi(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len,
+                           slopes, *, scale=None, out=None, stream=None):
+    """Prefill with ALiBi biases instead of RoPE (see lazyattn_decode_alibi)."""
+    return _prefill("lazyattn_prefill_alibi", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                    kv_lens, max_q_len, scale, None, out, stream, slopes=slopes)
+
+
 def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len, scale,
-             rope_theta, out, stream):
+             rope_theta, out, stream, slopes=None):
     dev = _dev(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens)
     for t, n in ((cu_q_lens, "cu_q_lens"), (q_pos_start, "q_pos_start"), (kv_lens, "kv_lens"),
                  (block_table, "block_table")):
@@ -242,6 +277,13 @@ def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens
             raise LazyAttnError("out must match q")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     lib = load_library()
+    if slopes is not None:
+        _slopes(slopes, hq, dev)
+        _check(getattr(lib, fn)(_ptr(out), _ptr(q), tq, _ptr(cu_q_lens), _ptr(q_pos_start), _ptr(k_pool),
+                                _ptr(v_pool), _ptr(block_table), block_table.shape[1], _ptr(kv_lens),
+                                _ptr(slopes), b, int(max_q_len), hq, hkv, d, nb, _dtype_code(q), scale,
+                                _stream_ptr(stream, dev)), fn)
+        return out
     _check(getattr(lib, fn)(_ptr(out), _ptr(q), tq, _ptr(cu_q_lens), _ptr(q_pos_start), _ptr(k_pool),
                             _ptr(v_pool), _ptr(block_table), block_table.shape[1], _ptr(kv_lens),
                             b, int(max_q_len), hq, hkv, d, nb, _dtype_code(q), scale,

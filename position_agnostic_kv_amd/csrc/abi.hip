@@ -64,7 +64,7 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
                          const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
                          int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
                          int split_blocks, void *workspace, size_t workspace_bytes, void *stream,
-                         bool eager) {
+                         int mode, const float *slopes) {
   if (!valid_dtype(dtype)) return LAZYATTN_ERR_DTYPE;
   if (batch < 0 || batch > 65535 || num_kv_heads < 1 || num_kv_heads > 65535 || num_q_heads < 1 ||
       num_q_heads % num_kv_heads || !pow2_group(num_q_heads / num_kv_heads))
@@ -81,6 +81,7 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
   if (batch == 0) return LAZYATTN_OK;
   if (!out || !q || !q_pos || !k_pool || !v_pool || !block_table || !seq_lens)
     return LAZYATTN_ERR_NULL;
+  if (mode == kAlibi && !slopes) return LAZYATTN_ERR_NULL;
   const size_t need = decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
                                             max_blocks_per_seq, split_blocks);
   if (need && (!workspace || workspace_bytes < need)) return LAZYATTN_ERR_WORKSPACE;
@@ -103,7 +104,8 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
   a.split_blocks = decode_split_blocks(batch, num_q_heads, num_kv_heads, max_blocks_per_seq, split_blocks);
   a.scale = scale;
   a.rope_theta = rope_theta;
-  a.eager = eager;
+  a.mode = mode;
+  a.slopes = slopes;
   return from_hip(launch_decode(a, bf16, (hipStream_t)stream));
 }
 
@@ -114,7 +116,7 @@ int lazyattn_decode(void *out, const void *q, const int32_t *q_pos, const void *
                     int split_blocks, void *workspace, size_t workspace_bytes, void *stream) {
   return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens,
                        batch, num_q_heads, num_kv_heads, head_dim, num_blocks, dtype, scale,
-                       rope_theta, split_blocks, workspace, workspace_bytes, stream, false);
+                       rope_theta, split_blocks, workspace, workspace_bytes, stream, kRopeLazy, nullptr);
 }
 
 int lazyattn_decode_eager(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
@@ -124,7 +126,18 @@ int lazyattn_decode_eager(void *out, const void *q, const int32_t *q_pos, const 
                           int split_blocks, void *workspace, size_t workspace_bytes, void *stream) {
   return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens,
                        batch, num_q_heads, num_kv_heads, head_dim, num_blocks, dtype, scale,
-                       rope_theta, split_blocks, workspace, workspace_bytes, stream, true);
+                       rope_theta, split_blocks, workspace, workspace_bytes, stream, kRopeEager, nullptr);
+}
+
+int lazyattn_decode_alibi(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                          const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                          const int32_t *seq_lens, const float *slopes, int batch, int num_q_heads,
+                          int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
+                          int split_blocks, void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens,
+                       batch, num_q_heads, num_kv_heads, head_dim, num_blocks, dtype, scale,
+                       10000.0f /* unused */, split_blocks, workspace, workspace_bytes, stream, kAlibi,
+                       slopes);
 }
 
 static int prefill_common(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
@@ -132,7 +145,7 @@ static int prefill_common(void *out, const void *q, int total_q, const int32_t *
                           const uint32_t *block_table, int max_blocks_per_seq, const int32_t *kv_lens,
                           int batch, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
                           int num_blocks, int dtype, float scale, float rope_theta, void *stream,
-                          bool eager) {
+                          int mode, const float *slopes) {
   if (dtype != LAZYATTN_BF16) return LAZYATTN_ERR_DTYPE;
   if (batch < 0 || batch > 65535 || max_q_len < 0 || max_q_len > LAZYATTN_MAX_POSITION + 1 || total_q < 0 ||
       num_kv_heads < 1 || num_kv_heads > 65535 || num_q_heads < 1 || num_q_heads % num_kv_heads ||
@@ -146,6 +159,7 @@ static int prefill_common(void *out, const void *q, int total_q, const int32_t *
   if (batch == 0 || max_q_len == 0 || total_q == 0) return LAZYATTN_OK;
   if (!out || !q || !cu_q_lens || !q_pos_start || !k_pool || !v_pool || !block_table || !kv_lens)
     return LAZYATTN_ERR_NULL;
+  if (mode == kAlibi && !slopes) return LAZYATTN_ERR_NULL;
   PrefillArgs a;
   a.out = out;
   a.q = q;
@@ -165,7 +179,8 @@ static int prefill_common(void *out, const void *q, int total_q, const int32_t *
   a.max_blocks = max_blocks_per_seq;
   a.scale = scale;
   a.rope_theta = rope_theta;
-  a.eager = eager;
+  a.mode = mode;
+  a.slopes = slopes;
   return from_hip(launch_prefill(a, (hipStream_t)stream));
 }
 
@@ -176,7 +191,7 @@ int lazyattn_prefill(void *out, const void *q, int total_q, const int32_t *cu_q_
                      int num_blocks, int dtype, float scale, float rope_theta, void *stream) {
   return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
                         max_blocks_per_seq, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
-                        head_dim, num_blocks, dtype, scale, rope_theta, stream, false);
+                        head_dim, num_blocks, dtype, scale, rope_theta, stream, kRopeLazy, nullptr);
 }
 
 int lazyattn_prefill_eager(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
@@ -187,7 +202,18 @@ int lazyattn_prefill_eager(void *out, const void *q, int total_q, const int32_t 
                            float rope_theta, void *stream) {
   return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
                         max_blocks_per_seq, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
-                        head_dim, num_blocks, dtype, scale, rope_theta, stream, true);
+                        head_dim, num_blocks, dtype, scale, rope_theta, stream, kRopeEager, nullptr);
+}
+
+int lazyattn_prefill_alibi(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                           const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                           const uint32_t *block_table, int max_blocks_per_seq, const int32_t *kv_lens,
+                           const float *slopes, int batch, int max_q_len, int num_q_heads,
+                           int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
+                           void *stream) {
+  return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                        max_blocks_per_seq, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
+                        head_dim, num_blocks, dtype, scale, 10000.0f /* unused */, stream, kAlibi, slopes);
 }
 
 }  // extern "C"

@@ -76,6 +76,7 @@ struct DecodeKernelArgs {
   const uint4 *v_pool;
   const uint32_t *table;
   const int32_t *seq_lens;
+  const float *slopes;  // ALiBi: per query head
   float *ws_o;    // [B][Hkv][S][G][D]
   float2 *ws_ml;  // [B][Hkv][S][G] (max, sum)
   int max_blocks;
@@ -86,15 +87,19 @@ struct DecodeKernelArgs {
   float scale_log2, rope_theta;
 };
 
-// EAGER: the non-lazy baseline the method is measured against.  The pool then
-// holds keys already rotated to their absolute positions (the eager,
+// MODE kRopeEager: the non-lazy baseline the method is measured against.  The
+// pool then holds keys already rotated to their absolute positions (the eager,
 // position-adjusted copy), table offsets are ignored, and the query is rotated
 // once by its own position.
-template <typename T, int D, int G, bool EAGER>
+// MODE kAlibi: no rotation at all; the score of a key at position p (block
+// offset + slot) takes the bias slope_h * (p - n) of query head h.
+template <typename T, int D, int G, int MODE>
 __global__ void __launch_bounds__(kDecodeWaves * kWave)
 decode_split_kernel(const DecodeKernelArgs a) {
   using E = Elem<T>;
   constexpr bool kBf16 = sizeof(T) == 2;
+  constexpr bool EAGER = MODE == kRopeEager;
+  constexpr bool ALIBI = MODE == kAlibi;
   constexpr int EPL = E::kPerChunk;        // elements per 16-byte chunk
   constexpr int LPT = D / EPL;             // lanes per token row
   constexpr int TPI = kWave / LPT;         // token rows per load instruction
@@ -239,12 +244,19 @@ decode_split_kernel(const DecodeKernelArgs a) {
   uint4 kA[NI], vA[NI], kB[NI], vB[NI];
   issue(min(blk, blast), wA, kA, vA);
   if constexpr (EAGER) rotate(n_pos);
+  if constexpr (ALIBI) rotate(0);  // the identity: q * scale * log2(e)
+  // ALiBi: slopes of this workgroup's heads, in log2 units
+  float slope2[ALIBI ? G : 1];
+  if constexpr (ALIBI) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) slope2[h] = a.slopes[g * G + h] * kLog2e;
+  }
   auto step = [&](const uint32_t &wcur, uint4 (&kc)[NI], uint4 (&vc)[NI], uint32_t &wn, uint4 (&kn)[NI],
                   uint4 (&vn)[NI]) {
     // a new document: re-rotate the query (the lazy rotation).  Done before
     // the next block's loads are issued, so that the rotation's temporaries
     // never share registers with loads in flight.
-    if constexpr (!EAGER) {
+    if constexpr (MODE == kRopeLazy) {
       const int off = word_offset(wcur);
       if (off != cur_off && blk < blk1) {
         rotate(n_pos - off);
@@ -276,6 +288,13 @@ decode_split_kernel(const DecodeKernelArgs a) {
     // sum the partial products over the LPT lanes of each row, one DPP step at
     // a time over all NI*G values (independent neighbours: no wait states)
     group_sum_all<LPT, NI * G>(&s[0][0]);
+    if constexpr (ALIBI) {  // key position - query position, per row of this lane
+      const float base = (float)(word_offset(wcur) + r - n_pos);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[i][h] = fmaf(slope2[h], base + (float)(i * TPI), s[i][h]);
+    }
     // rows of this block that count: all but the tail of a sequence's last
     // block, none once the split is exhausted (blk >= blk1: a re-read block)
     const int nvalid = blk < blk1 ? seq_len - blk * kBlockTokens : 0;
@@ -500,7 +519,7 @@ size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int h
   return t;
 }
 
-template <typename T, int D, int G, bool EAGER>
+template <typename T, int D, int G, int MODE>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   DecodeKernelArgs k;
   k.out = a.out;
@@ -510,6 +529,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   k.v_pool = (const uint4 *)a.v_pool;
   k.table = a.table;
   k.seq_lens = a.seq_lens;
+  k.slopes = a.slopes;
   const int hsplit = a.num_q_heads / a.num_kv_heads / G;  // work heads per KV head
   const int work_heads = a.num_kv_heads * hsplit;
   k.max_blocks = a.max_blocks;
@@ -530,7 +550,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   char *ws = (char *)a.workspace;
   k.ws_ml = ws ? (float2 *)ws : nullptr;
   k.ws_o = ws ? (float *)(ws + off_o) : nullptr;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, G, EAGER>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave),
+  hipLaunchKernelGGL((decode_split_kernel<T, D, G, MODE>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave),
                      0, stream, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k.max_splits <= 1) return e;
@@ -539,20 +559,25 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D, bool EAGER>
+template <typename T, int D, int MODE>
 static hipError_t dispatch_group_e(const DecodeArgs &a, hipStream_t s) {
   switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads)) {
-    case 1: return launch_decode_t<T, D, 1, EAGER>(a, s);
-    case 2: return launch_decode_t<T, D, 2, EAGER>(a, s);
-    case 4: return launch_decode_t<T, D, 4, EAGER>(a, s);
-    case 8: return launch_decode_t<T, D, 8, EAGER>(a, s);
+    case 1: return launch_decode_t<T, D, 1, MODE>(a, s);
+    case 2: return launch_decode_t<T, D, 2, MODE>(a, s);
+    case 4: return launch_decode_t<T, D, 4, MODE>(a, s);
+    case 8: return launch_decode_t<T, D, 8, MODE>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T, int D>
 static hipError_t dispatch_group(const DecodeArgs &a, hipStream_t s) {
-  return a.eager ? dispatch_group_e<T, D, true>(a, s) : dispatch_group_e<T, D, false>(a, s);
+  switch (a.mode) {
+    case kRopeLazy: return dispatch_group_e<T, D, kRopeLazy>(a, s);
+    case kRopeEager: return dispatch_group_e<T, D, kRopeEager>(a, s);
+    case kAlibi: return dispatch_group_e<T, D, kAlibi>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_decode(const DecodeArgs &a, bool is_bf16, hipStream_t s) {

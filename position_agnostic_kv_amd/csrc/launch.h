@@ -7,6 +7,13 @@
 
 namespace lazyattn {
 
+// Position scheme of a decode/prefill launch.
+enum PosMode : int {
+  kRopeLazy = 0,   // RoPE, keys in their own frames, offsets applied lazily
+  kRopeEager = 1,  // RoPE, keys already at absolute positions, offsets ignored
+  kAlibi = 2       // ALiBi: no rotation; key position = block offset + slot
+};
+
 hipError_t launch_append(void *k_pool, void *v_pool, int elem_bytes, int num_blocks,
                          int num_kv_heads, int head_dim, const void *k_new, const void *v_new,
                          const int32_t *slot_mapping, int num_tokens, hipStream_t stream);
@@ -31,7 +38,8 @@ struct DecodeArgs {
   int batch, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks;
   int split_blocks;  // resolved (> 0)
   float scale, rope_theta;
-  bool eager;        // non-lazy baseline: keys pre-rotated, offsets ignored
+  const float *slopes;  // ALiBi slopes [num_q_heads] (device), else unused
+  int mode;             // PosMode
 };
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t stream);
 
@@ -46,7 +54,8 @@ struct PrefillArgs {
   const int32_t *kv_lens;
   int total_q, batch, max_q_len, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks;
   float scale, rope_theta;
-  bool eager;        // non-lazy baseline: keys pre-rotated, offsets ignored
+  const float *slopes;  // ALiBi slopes [num_q_heads] (device), else unused
+  int mode;             // PosMode
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 

@@ -53,6 +53,7 @@ struct PrefillKernelArgs {
   const uint16_t *v_pool;
   const uint32_t *table;
   const int32_t *kv_lens;
+  const float *slopes;  // ALiBi: per query head
   int total_q, batch, num_q_heads, num_kv_heads, num_blocks, max_blocks;
   int head_groups;  // workgroups per KV head (G / HP)
   int tok_tiles;    // token tiles per sequence
@@ -112,11 +113,16 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
 // rows feed the A operand of O^T = V^T P^T through two transposing reads.
 // Two buffers: the next tile streams in while the current one is computed.
 //
-// EAGER: the non-lazy baseline the method is measured against.  The pool then
-// holds keys already rotated to their absolute positions and table offsets are
-// ignored: every run has offset 0 (runs are cut only at 4 blocks), so the query
-// rows are rotated once, by their own positions, on the first tile.
-template <int D, int HP, bool EAGER>
+// MODE kRopeEager: the non-lazy baseline the method is measured against.  The
+// pool then holds keys already rotated to their absolute positions and table
+// offsets are ignored: every run has offset 0 (runs are cut only at 4 blocks),
+// so the query rows are rotated once, by their own positions, on the first
+// tile.
+// MODE kAlibi: no rotation; a key at position p (block offset + slot) takes the
+// bias slope_h * (p - n).  Runs are cut only at 4 blocks, and the tiles are
+// walked from the last visible block back to the first, so that each row meets
+// its largest biases first and the reference below rarely has to move.
+template <int D, int HP, int MODE>
 __global__ void __launch_bounds__(kPfWaves * kWave, 2)
 prefill_kernel(const PrefillKernelArgs a) {
   constexpr int KC = D / 32;          // 32-dim k-chunks of the QK product
@@ -131,6 +137,8 @@ prefill_kernel(const PrefillKernelArgs a) {
   constexpr int WPH = kPfWaves / HP;  // waves per head
   static_assert(D == 64 || D == 128, "head_dim must be 64 or 128");
   static_assert(HP == 1 || HP == 2 || HP == 4, "1, 2 or 4 heads per workgroup");
+  constexpr bool ALIBI = MODE == kAlibi;
+  constexpr bool NOCUT = MODE != kRopeLazy;  // runs ignore offsets
 
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILEB / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILEB / 2];
@@ -225,9 +233,9 @@ prefill_kernel(const PrefillKernelArgs a) {
   // blocks jw.. that share block jw's offset (1..4), and that offset
   auto tile_of = [&](uint32_t wv, int jw, int &cnt, int &off) {
     const uint32_t w0 = __builtin_amdgcn_readfirstlane(wv);
-    off = EAGER ? 0 : word_offset(w0);
+    off = NOCUT ? 0 : word_offset(w0);
     const uint64_t same =
-        __ballot(lane < kPfTileBlocks && jw + lane < nblk_vis && (EAGER || (wv >> 16) == (w0 >> 16)));
+        __ballot(lane < kPfTileBlocks && jw + lane < nblk_vis && (NOCUT || (wv >> 16) == (w0 >> 16)));
     cnt = __builtin_ctzll(~same);
   };
   auto issue_tile = [&](uint32_t wv, int cnt, auto bufc) {
@@ -290,20 +298,29 @@ prefill_kernel(const PrefillKernelArgs a) {
   float ref[2] = {0.f, 0.f};
   float lsum[2] = {0.f, 0.f};
   bool ref_nz = false;    // wave-uniform: some row's reference is not 0
-  bool settled = false;   // wave-uniform: every row's sum is >= 2^-64
+  bool settled = false;   // wave-uniform: every row holds a sum (>= 2^-64)
   int cur_off = -1;
   constexpr float kHi = 0x1p64f, kLo = 0x1p-64f;
 
-  // tile state (wave-uniform): current tile (cj, ccnt, coff); the next tile
-  // starts at block nj and its words nw are in flight
-  int cj = 0, ccnt, coff;
-  {
-    const uint32_t w = load_words(0);
-    tile_of(w, 0, ccnt, coff);
-    issue_tile(w, ccnt, std::integral_constant<int, 0>{});
+  // tile state (wave-uniform): current tile (cj, ccnt, coff; its words cw);
+  // the next tile starts at block nj and its words nw are in flight.  ALiBi
+  // walks backwards: tile [cj, cj + ccnt) is followed by [nj, cj).
+  int cj = 0, ccnt, coff = 0;
+  if constexpr (ALIBI) {
+    ccnt = min(kPfTileBlocks, nblk_vis);
+    cj = nblk_vis - ccnt;
   }
-  int nj = ccnt;
-  uint32_t nw = nj < nblk_vis ? load_words(nj) : 0u;
+  uint32_t cw = load_words(cj);
+  if constexpr (!ALIBI) tile_of(cw, 0, ccnt, coff);
+  issue_tile(cw, ccnt, std::integral_constant<int, 0>{});
+  int nj = ALIBI ? cj - min(kPfTileBlocks, cj) : ccnt;
+  uint32_t nw = (ALIBI ? cj > 0 : nj < nblk_vis) ? load_words(nj) : 0u;
+  // ALiBi: this wave's slope in log2 units, and the workgroup's reference
+  // position (its last query token): the bias is taken as slope * (p - nref),
+  // which differs from slope * (p - n) by a constant per query row (softmax
+  // ignores it) and is <= 0 for every key a row sees
+  const float slope2 = ALIBI ? a.slopes[hq] * kLog2e : 0.f;
+  const int nref = n0 + TOK - 1;
   // raw (bf16) query rows for the next rotation, fetched one tile ahead (when
   // the next tile starts a new document) so that a rotation never waits on a
   // load; the registers stay live across the loop
@@ -315,6 +332,17 @@ prefill_kernel(const PrefillKernelArgs a) {
       for (int kc = 0; kc < KC; ++kc) qraw[nt][kc] = qok[nt] ? qsrc[nt][kc * 4 + lg] : make_uint4(0u, 0u, 0u, 0u);
   };
   load_q();
+  if constexpr (ALIBI) {  // no rotation: q * scale * log2(e), once
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t wx = dw4(qraw[nt][kc], e >> 1);
+          bq[nt][kc][e] = (__bf16)(((e & 1) ? bf16_hi(wx) : bf16_lo(wx)) * a.scale_log2);
+        }
+  }
 
   // One tile on LDS buffer BUF; returns false after the last tile.
   auto step = [&](auto bufc) -> bool {
@@ -323,21 +351,26 @@ prefill_kernel(const PrefillKernelArgs a) {
     fix_tail(cj, ccnt, bufc);
     __syncthreads();
 
-    const bool more = nj < nblk_vis;
+    const bool more = ALIBI ? cj > 0 : nj < nblk_vis;
     int ncnt = 0, noff = 0, nnj = 0;
     uint32_t nnw = 0u;
     if (more) {
-      tile_of(nw, nj, ncnt, noff);
+      if constexpr (ALIBI) {
+        ncnt = cj - nj;
+        nnj = nj - min(kPfTileBlocks, nj);
+      } else {
+        tile_of(nw, nj, ncnt, noff);
+        nnj = nj + ncnt;
+      }
       issue_tile(nw, ncnt, std::integral_constant<int, BUF ^ 1>{});  // streams in during this tile
-      nnj = nj + ncnt;
-      nnw = nnj < nblk_vis ? load_words(nnj) : 0u;
+      nnw = (ALIBI ? nj > 0 : nnj < nblk_vis) ? load_words(nnj) : 0u;
     }
 
     // ---- re-rotate the query rows: q' = rot(q, rho + n0 - off), rho = token
     // index inside the tile.  The angle in turns is rho * turn_i +
     // frac((n0 - off) * turn_i); the large part is reduced in double, the rest
     // (< TOK turns) evaluated with v_sin/v_cos.
-    if (coff != cur_off) {
+    if (!ALIBI && coff != cur_off) {
       cur_off = coff;
       if (lane < HALF) {
         const double t = (double)(n0 - coff) * turn_d;
@@ -364,12 +397,25 @@ prefill_kernel(const PrefillKernelArgs a) {
       }
     }
 
-    if (more && noff != coff) load_q();   // the next tile starts a new document
+    if (!NOCUT && more && noff != coff) load_q();   // the next tile starts a new document
 
     // ---- S'^T = K Q^T - r  (per lane: keys mt*16 + lg*4 + i, token nt*16 + l16)
     const char *kb = (const char *)sK[BUF];
     f32x4_t S[kPfTileBlocks][2];
-    if (ref_nz) {
+    if constexpr (ALIBI) {
+      // per-key bias slope * (offset + slot - nref), minus the row reference
+#pragma unroll
+      for (int mt = 0; mt < kPfTileBlocks; ++mt) {
+        const int offm = word_offset((uint32_t)__builtin_amdgcn_readlane((int)cw, mt));
+        const float b0 = slope2 * (float)(offm + lg * 4 - nref);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float bias = fmaf(slope2, (float)i, b0);
+          S[mt][0][i] = bias - ref[0];
+          S[mt][1][i] = bias - ref[1];
+        }
+      }
+    } else if (ref_nz) {
 #pragma unroll
       for (int mt = 0; mt < kPfTileBlocks; ++mt) {
         S[mt][0] = f32x4_t{-ref[0], -ref[0], -ref[0], -ref[0]};
@@ -470,7 +516,11 @@ prefill_kernel(const PrefillKernelArgs a) {
       weights();
       ref_nz = wave_any(ref[0] != 0.f || ref[1] != 0.f);
     }
-    settled = true;
+    // A row's sum is now >= 2^-64 (after a rescale: >= 1) or 0 because no
+    // key of the row has been visible yet (a later tile holds them: the first
+    // tile need not reach every row when the walk starts at the far end).
+    // Stop checking the lower bound once every row of the wave holds a sum.
+    if (!settled) settled = !wave_any(!(col_sum4(ln[0]) > 0.f) || !(col_sum4(ln[1]) > 0.f));
     lsum[0] = ln[0];
     lsum[1] = ln[1];
 
@@ -494,6 +544,7 @@ prefill_kernel(const PrefillKernelArgs a) {
     cj = nj;
     ccnt = ncnt;
     coff = noff;
+    cw = nw;
     nj = nnj;
     nw = nnw;
     return true;
@@ -523,7 +574,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   }
 }
 
-template <int D, int HP, bool EAGER>
+template <int D, int HP, int MODE>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   PrefillKernelArgs k;
   k.out = (uint16_t *)a.out;
@@ -535,6 +586,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   k.v_pool = (const uint16_t *)a.v_pool;
   k.table = a.table;
   k.kv_lens = a.kv_lens;
+  k.slopes = a.slopes;
   k.batch = a.batch;
   k.num_q_heads = a.num_q_heads;
   k.num_kv_heads = a.num_kv_heads;
@@ -549,21 +601,26 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   const long long grid = (long long)(k.num_units + kXcds - 1) / kXcds * kXcds * k.tok_tiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D, HP, EAGER>), dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream, k);
+  hipLaunchKernelGGL((prefill_kernel<D, HP, MODE>), dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream, k);
   return hipGetLastError();
 }
 
-template <int D, bool EAGER>
+template <int D, int MODE>
 static hipError_t launch_prefill_e(const PrefillArgs &a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
-  if (group % 4 == 0) return launch_prefill_t<D, 4, EAGER>(a, stream);
-  if (group % 2 == 0) return launch_prefill_t<D, 2, EAGER>(a, stream);
-  return launch_prefill_t<D, 1, EAGER>(a, stream);
+  if (group % 4 == 0) return launch_prefill_t<D, 4, MODE>(a, stream);
+  if (group % 2 == 0) return launch_prefill_t<D, 2, MODE>(a, stream);
+  return launch_prefill_t<D, 1, MODE>(a, stream);
 }
 
 template <int D>
 static hipError_t launch_prefill_d(const PrefillArgs &a, hipStream_t stream) {
-  return a.eager ? launch_prefill_e<D, true>(a, stream) : launch_prefill_e<D, false>(a, stream);
+  switch (a.mode) {
+    case kRopeLazy: return launch_prefill_e<D, kRopeLazy>(a, stream);
+    case kRopeEager: return launch_prefill_e<D, kRopeEager>(a, stream);
+    case kAlibi: return launch_prefill_e<D, kAlibi>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {

@@ -90,6 +90,19 @@ def test_decode_argument_errors(lib):
     assert decode(lib, ws_bytes=16, max_blocks=4000) == -4
 
 
+def test_alibi_entry_points_check_arguments(lib):
+    fd, fp = lib.lazyattn_decode_alibi, lib.lazyattn_prefill_alibi
+    ok_d = [P, P, P, P, P, P, 4, P, P, 2, 8, 2, 128, 16, 1, 0.088, 0, P, 1 << 30, NULL]
+    assert fd(*[NULL if i == 8 else x for i, x in enumerate(ok_d)]) == -1     # slopes NULL
+    assert fd(*[7 if i == 14 else x for i, x in enumerate(ok_d)]) == -2      # dtype
+    assert fd(*[96 if i == 12 else x for i, x in enumerate(ok_d)]) == -3     # head_dim
+    assert fd(*[0 if i == 9 else (NULL if i == 8 else x) for i, x in enumerate(ok_d)]) == 0  # empty batch
+    ok_p = [P, P, 4096, P, P, P, P, P, 8, P, P, 2, 128, 32, 8, 128, 64, 1, 0.088, NULL]
+    assert fp(*[NULL if i == 10 else x for i, x in enumerate(ok_p)]) == -1
+    assert fp(*[0 if i == 17 else x for i, x in enumerate(ok_p)]) == -2      # fp32 prefill not offered
+    assert fp(*[96 if i == 15 else x for i, x in enumerate(ok_p)]) == -3
+
+
 def test_workspace_size(lib):
     ws = lib.lazyattn_decode_workspace_size
     assert ws(1, 4, 4, 16, 3, 0) == 0                   # one split: no partials

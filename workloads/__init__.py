@@ -150,6 +150,24 @@ def build_layout(rng, seq_docs, doc_lens, tail_lens, offsets=None, tail_pos=None
                   doc_spans=spans, unique_doc_tokens=unique_tokens)
 
 
+def block_frame_table(layout):
+    """The layout's table with every block carrying its own first token's
+    position (frame start + 16 * block index within the frame) instead of the
+    frame start: the rows ALiBi reads, where a key's position is its block's
+    offset plus its slot."""
+    table = layout.table.copy()
+    for b in range(layout.batch):
+        col = 0
+        runs = [(ln, off) for _, ln, off in layout.doc_spans[b]]
+        runs.append((int(layout.tail_lens[b]), int(layout.tail_pos[b])))
+        for ln, off in runs:
+            nb = -(-int(ln) // BLOCK)
+            ids = table[b, col:col + nb] & np.uint32(0xFFFF)
+            table[b, col:col + nb] = pack_words(ids, off + BLOCK * np.arange(nb))
+            col += nb
+    return table
+
+
 def _docs_filling(rng, total, lo_blocks, hi_blocks):
     """Document lengths (multiples of 16, uniform in blocks) summing to total."""
     lens = []
