@@ -201,30 +201,45 @@ decode_split_kernel(const DecodeKernelArgs a) {
   };
 
   // q' = rot(q, n - off) * scale * log2(e), for this lane's dims and all G heads.
+  // Lane i < D/2 evaluates frequency i once; the values are shuffled to the
+  // lanes holding dims i and i + D/2.  bf16: the angle is reduced in double to
+  // a fraction of a turn and evaluated with v_cos/v_sin (which take turns): far
+  // below the bf16 rounding of the result, and light on registers (this runs
+  // inside the block loop).  f32: double-precision cos/sin.
   auto rotate = [&](int delta) {
-    float cs = 0.f, sn = 0.f;
-    if (lane < HALF) rope_cos_sin(delta, inv_freq, cs, sn);
-    float rot[G][EPL];
+    float cs = 1.f, sn = 0.f;
+    if (lane < HALF) {
+      if constexpr (kBf16) {
+        const double t = (double)delta * (inv_freq * 0.15915494309189535);
+        const float f = (float)(t - rint(t));
+        cs = __builtin_amdgcn_cosf(f);
+        sn = __builtin_amdgcn_sinf(f);
+      } else {
+        rope_cos_sin(delta, inv_freq, cs, sn);
+      }
+    }
+    float ce[EPL], se[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const int fi = (d0 + e) % HALF;
-      const float ce = __shfl(cs, fi);
-      const float se = __shfl(sn, fi);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float x = s_q[h][d0 + e];
-        const float y = s_q[h][pd0 + e];
-        rot[h][e] = (upper ? fmaf(x, ce, y * se) : fmaf(x, ce, -(y * se))) * a.scale_log2;
-      }
+      ce[e] = __shfl(cs, fi);
+      se[e] = __shfl(sn, fi);
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      float rot[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float x = s_q[h][d0 + e];
+        const float y = s_q[h][pd0 + e];
+        rot[e] = (upper ? fmaf(x, ce[e], y * se[e]) : fmaf(x, ce[e], -(y * se[e]))) * a.scale_log2;
+      }
       if constexpr (kBf16) {
 #pragma unroll
-        for (int w = 0; w < EPL / 2; ++w) qp[h][w] = pack_bf16x2(rot[h][2 * w], rot[h][2 * w + 1]);
+        for (int w = 0; w < EPL / 2; ++w) qp[h][w] = pack_bf16x2(rot[2 * w], rot[2 * w + 1]);
       } else {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) qf[h][e] = rot[h][e];
+        for (int e = 0; e < EPL; ++e) qf[h][e] = rot[e];
       }
     }
   };
