@@ -42,5 +42,6 @@ from .lazy_oracle import (  # noqa: F401
     softmax,
     tiled_softmax_dot,
     unpack_block_word,
+    valid_slots,
 )
 from .alibi_oracle import alibi_slopes, decode_alibi, key_positions, prefill_alibi  # noqa: F401

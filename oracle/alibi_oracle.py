@@ -22,21 +22,21 @@ but do not define ALiBi.  Readings taken here:
 
 import numpy as np
 
-from .lazy_oracle import BLOCK_TOKENS, _attend, unpack_block_word
+from .lazy_oracle import BLOCK_TOKENS, unpack_block_word, valid_slots
 
 
-def key_positions(table_row, length):
-    """Absolute position of each of the sequence's first `length` tokens:
-    the offset of its block plus its slot."""
-    j = np.arange(int(length))
+def key_positions(table_row, length, block_fill=None):
+    """Absolute position of each token of the sequence's first `length` table
+    slots: the offset of its block plus its slot."""
+    j = valid_slots(table_row, length, block_fill)
     _, offs = unpack_block_word(np.asarray(table_row)[j // BLOCK_TOKENS])
     return offs + j % BLOCK_TOKENS
 
 
-def gather_sequence(k_pool, v_pool, table_row, length, kv_head):
-    """The sequence's stored keys and values in logical order ([length, D],
+def gather_sequence(k_pool, v_pool, table_row, length, kv_head, block_fill=None):
+    """The sequence's stored keys and values in logical order ([tokens, D],
     float64), untouched: ALiBi never rotates them."""
-    j = np.arange(int(length))
+    j = valid_slots(table_row, length, block_fill)
     ids, _ = unpack_block_word(np.asarray(table_row)[j // BLOCK_TOKENS])
     slots = j % BLOCK_TOKENS
     return (np.asarray(k_pool)[ids, kv_head, slots, :].astype(np.float64),
@@ -59,7 +59,7 @@ def _attend_bias(q_rows, k, v, scale, bias, visible):
     return out
 
 
-def decode_alibi(q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, slopes):
+def decode_alibi(q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, slopes, block_fill=None):
     """Decode with ALiBi: q [B, Hq, D]; out [B, Hq, D] float64.  Query head h
     reads KV head h // (Hq / Hkv) and takes bias slopes[h] * (p - q_pos[b])."""
     q = np.asarray(q, dtype=np.float64)
@@ -69,15 +69,17 @@ def decode_alibi(q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, slopes)
     out = np.zeros((bsz, hq, d))
     for b in range(bsz):
         n = int(seq_lens[b])
-        pos = key_positions(block_table[b], n).astype(np.float64)
+        pos = key_positions(block_table[b], n, block_fill).astype(np.float64)
         for h in range(hq):
-            k, v = gather_sequence(k_pool, v_pool, block_table[b], n, h // group)
+            k, v = gather_sequence(k_pool, v_pool, block_table[b], n, h // group, block_fill)
             bias = (slopes[h] * (pos - float(q_pos[b])))[None, :]
-            out[b, h] = _attend_bias(q[b, h][None, :], k, v, scale, bias, np.ones((1, n), bool))[0]
+            out[b, h] = _attend_bias(q[b, h][None, :], k, v, scale, bias,
+                                     np.ones((1, pos.size), bool))[0]
     return out
 
 
-def prefill_alibi(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, scale, slopes):
+def prefill_alibi(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, scale, slopes,
+                  block_fill=None):
     """Prefill with ALiBi: prompt row r of sequence b is logical index
     kv_len - P + r at position q_pos_start + r and sees keys of logical
     index <= its own (causal by table order)."""
@@ -95,10 +97,10 @@ def prefill_alibi(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_len
         rows = np.arange(p)
         t = kv - p + rows
         npos = float(q_pos_start[b]) + rows
-        pos = key_positions(block_table[b], kv).astype(np.float64)
-        vis = np.arange(kv)[None, :] <= t[:, None]
+        pos = key_positions(block_table[b], kv, block_fill).astype(np.float64)
+        vis = valid_slots(block_table[b], kv, block_fill)[None, :] <= t[:, None]
         for h in range(hq):
-            k, v = gather_sequence(k_pool, v_pool, block_table[b], kv, h // group)
+            k, v = gather_sequence(k_pool, v_pool, block_table[b], kv, h // group, block_fill)
             bias = slopes[h] * (pos[None, :] - npos[:, None])
             out[s0:s1, h] = _attend_bias(q[s0:s1, h], k, v, scale, bias, vis)
     return out

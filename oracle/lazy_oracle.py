@@ -68,20 +68,35 @@ def softmax(scores):
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
-def materialize_sequence(k_pool, v_pool, table_row, length, kv_head, theta):
+def valid_slots(table_row, length, block_fill=None):
+    """Table slots j < length that hold a token, in order.
+
+    Slot j is slot j % 16 of block table_row[j // 16].  Without fill counts
+    every slot does; with them (block_fill[block id] = tokens stored in that
+    physical block, the rest of it unused, e.g. the end of a document whose
+    length is not a multiple of 16) only slots below their block's count.
+    """
+    j = np.arange(int(length))
+    if block_fill is None or j.size == 0:
+        return j
+    ids, _ = unpack_block_word(np.asarray(table_row)[j // BLOCK_TOKENS])
+    return j[(j % BLOCK_TOKENS) < np.asarray(block_fill)[ids]]
+
+
+def materialize_sequence(k_pool, v_pool, table_row, length, kv_head, theta, block_fill=None):
     """Eager position-adjusted copy of one sequence's keys and values.
 
     Logical token j of the sequence lives in block table_row[j // 16], slot
-    j % 16.  Its key is the stored key rotated by that block's offset (the
-    copy that position-aware caching would keep, [LA] "Declaração do
-    Problema"); its value is the stored value.  Returns (K_hat, V_hat), each
-    [length, D] float64.
+    j % 16 (slots past a block's fill count hold no token and are skipped).
+    Its key is the stored key rotated by that block's offset (the copy that
+    position-aware caching would keep, [LA] "Declaração do Problema"); its
+    value is the stored value.  Returns (K_hat, V_hat), each [tokens, D]
+    float64.
     """
-    length = int(length)
     d = k_pool.shape[-1]
-    if length == 0:
+    j = valid_slots(table_row, length, block_fill)
+    if j.size == 0:
         return np.zeros((0, d)), np.zeros((0, d))
-    j = np.arange(length)
     ids, offs = unpack_block_word(np.asarray(table_row)[j // BLOCK_TOKENS])
     slots = j % BLOCK_TOKENS
     k_stored = np.asarray(k_pool)[ids, kv_head, slots, :].astype(np.float64)
@@ -109,7 +124,7 @@ def _attend(q_rot, k_hat, v_hat, scale, visible):
     return out
 
 
-def decode_one(q_vec, q_pos, k_pool, v_pool, table_row, seq_len, kv_head, scale, theta):
+def decode_one(q_vec, q_pos, k_pool, v_pool, table_row, seq_len, kv_head, scale, theta, block_fill=None):
     """One decode row: a single query against all seq_len cached tokens.
 
     [WHY] "El remedio": the new query attends a 1 x (t+1) row of the cache,
@@ -117,13 +132,13 @@ def decode_one(q_vec, q_pos, k_pool, v_pool, table_row, seq_len, kv_head, scale,
     each key is the materialised position-adjusted copy ([LA] "Equivalência
     Matemática" states that deferring the rotation gives the same result).
     """
-    k_hat, v_hat = materialize_sequence(k_pool, v_pool, table_row, seq_len, kv_head, theta)
+    k_hat, v_hat = materialize_sequence(k_pool, v_pool, table_row, seq_len, kv_head, theta, block_fill)
     q_rot = rope(np.asarray(q_vec, dtype=np.float64)[None, :], q_pos, theta)
     vis = np.ones((1, k_hat.shape[0]), dtype=bool)
     return _attend(q_rot, k_hat, v_hat, scale, vis)[0]
 
 
-def decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, theta):
+def decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, theta, block_fill=None):
     """Decode for a batch.  q [B, Hq, D] raw; returns out [B, Hq, D] float64.
 
     Query head h reads KV head h // (Hq / Hkv) (grouped-query attention).
@@ -135,7 +150,8 @@ def decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, theta):
     out = np.zeros((bsz, hq, d))
     for b in range(bsz):
         for g in range(hkv):
-            k_hat, v_hat = materialize_sequence(k_pool, v_pool, block_table[b], seq_lens[b], g, theta)
+            k_hat, v_hat = materialize_sequence(k_pool, v_pool, block_table[b], seq_lens[b], g, theta,
+                                                block_fill)
             q_rot = rope(q[b, g * group:(g + 1) * group], q_pos[b], theta)
             vis = np.ones((group, k_hat.shape[0]), dtype=bool)
             out[b, g * group:(g + 1) * group] = _attend(q_rot, k_hat, v_hat, scale, vis)
@@ -143,7 +159,7 @@ def decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, theta):
 
 
 def prefill_rows(q_rows, rows, q_len, q_pos_start, k_pool, v_pool, table_row, kv_len,
-                 kv_head, scale, theta):
+                 kv_head, scale, theta, block_fill=None):
     """Prefill output for selected prompt rows of one sequence and one head.
 
     The prompt's P = q_len tokens are the last P logical tokens of the table
@@ -154,14 +170,14 @@ def prefill_rows(q_rows, rows, q_len, q_pos_start, k_pool, v_pool, table_row, kv
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
     rows = np.asarray(rows, dtype=np.int64)
-    k_hat, v_hat = materialize_sequence(k_pool, v_pool, table_row, kv_len, kv_head, theta)
+    k_hat, v_hat = materialize_sequence(k_pool, v_pool, table_row, kv_len, kv_head, theta, block_fill)
     q_rot = rope(q_rows, q_pos_start + rows, theta)
-    t = kv_len - q_len + rows
-    vis = np.arange(k_hat.shape[0])[None, :] <= t[:, None]
+    t = kv_len - q_len + rows     # the prompt fills the table's last slots
+    vis = valid_slots(table_row, kv_len, block_fill)[None, :] <= t[:, None]
     return _attend(q_rot, k_hat, v_hat, scale, vis)
 
 
-def prefill(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, scale, theta):
+def prefill(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, scale, theta, block_fill=None):
     """Prefill for a batch.  q [Tq, Hq, D] packed by cu_q_lens [B+1]."""
     q = np.asarray(q, dtype=np.float64)
     tq, hq, d = q.shape
@@ -176,7 +192,8 @@ def prefill(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, sca
         rows = np.arange(p)
         for h in range(hq):
             out[s0:s1, h] = prefill_rows(q[s0:s1, h], rows, p, int(q_pos_start[b]), k_pool, v_pool,
-                                         block_table[b], int(kv_lens[b]), h // group, scale, theta)
+                                         block_table[b], int(kv_lens[b]), h // group, scale, theta,
+                                         block_fill)
     return out
 
 

@@ -91,6 +91,25 @@ def _brute_attention(q_vec, q_pos, k_pool, v_pool, words, n_keys, kv_head, scale
     return [sum(e[j] * vals[j][c] for j in range(n_keys)) / tot for c in range(len(q_vec))]
 
 
+def _brute_attention_fill(q_vec, q_pos, k_pool, v_pool, words, n_slots, kv_head, scale, theta, fill,
+                          last_slot=None):
+    """Triple-loop attention over the first n_slots table slots, skipping
+    slots past their block's fill count; with last_slot, only slots <= it."""
+    qr = _brute_rotate(list(q_vec), q_pos, theta)
+    scores, vals = [], []
+    for j in range(n_slots):
+        off, blk = divmod(int(words[j // BLOCK]), 65536)
+        if j % BLOCK >= int(fill[blk]) or (last_slot is not None and j > last_slot):
+            continue
+        kr = _brute_rotate(list(k_pool[blk][kv_head][j % BLOCK]), off, theta)
+        scores.append(scale * sum(a * b for a, b in zip(qr, kr)))
+        vals.append(list(v_pool[blk][kv_head][j % BLOCK]))
+    m = max(scores)
+    e = [math.exp(x - m) for x in scores]
+    tot = sum(e)
+    return [sum(e[i] * vals[i][c] for i in range(len(e))) / tot for c in range(len(q_vec))]
+
+
 # ------------------------------------------------------------------- checks
 def check_rope_frequency_closed_forms(O):
     # theta = 1e4, D = 16: theta^(-2i/16) = 10^(-i/2)
@@ -234,6 +253,46 @@ def check_prefill_bruteforce(O):
                 ref = _brute_attention(q[cu[b] + r, h], qps[b] + r, k_pool, v_pool, table[b], t + 1,
                                        h // 2, 0.4, 1.0e4)
                 _close(out[cu[b] + r, h], ref, 1e-11, f"prefill brute b={b} r={r} h={h}")
+
+
+def check_decode_fill_bruteforce(O):
+    """Blocks partly filled in the middle of a sequence (documents whose
+    length is not a multiple of 16): the unused slots are skipped."""
+    rng = np.random.default_rng(27)
+    hq, hkv, d = 4, 2, 8
+    seqs = [[(16, 0), (16, 0), (16, 37), (16, 900)], [(16, 5), (16, 400)]]
+    k_pool, v_pool, table, lens = _pool_case(rng, 8, hkv, d, seqs)
+    fill = rng.integers(1, 17, size=8)
+    fill[int(table[1, 1]) % 65536] = 16
+    q = rng.standard_normal((2, hq, d))
+    qpos = np.array([2000, 430])
+    out = O.decode(q, qpos, k_pool, v_pool, table, lens, 0.3, 1.0e4, block_fill=fill)
+    for b in range(2):
+        for h in range(hq):
+            ref = _brute_attention_fill(q[b, h], qpos[b], k_pool, v_pool, table[b], lens[b], h // 2, 0.3,
+                                        1.0e4, fill)
+            _close(out[b, h], ref, 1e-11, f"decode fill brute b={b} h={h}")
+
+
+def check_prefill_fill_bruteforce(O):
+    """Prefill after partly filled document blocks: a prompt row sees the
+    document tokens actually stored and the prompt up to itself."""
+    rng = np.random.default_rng(28)
+    hq, hkv, d = 2, 1, 8
+    seqs = [[(16, 0), (16, 0), (16, 21), (16, 55), (3, 55)]]   # docs of 25 and 34 tokens, then a 19-token prompt
+    k_pool, v_pool, table, lens = _pool_case(rng, 6, hkv, d, seqs)
+    fill = np.full(6, 16)
+    fill[int(table[0, 1]) % 65536] = 9
+    fill[int(table[0, 2]) % 65536] = 13
+    p = 19
+    q = rng.standard_normal((p, hq, d))
+    out = O.prefill(q, np.array([0, p]), np.array([55]), k_pool, v_pool, table, lens, 0.4, 1.0e4, block_fill=fill)
+    for r in range(p):
+        t = lens[0] - p + r
+        for h in range(hq):
+            ref = _brute_attention_fill(q[r, h], 55 + r, k_pool, v_pool, table[0], lens[0], 0, 0.4, 1.0e4, fill,
+                                        last_slot=t)
+            _close(out[r, h], ref, 1e-11, f"prefill fill brute r={r} h={h}")
 
 
 def check_incremental_equals_full(O):

@@ -29,8 +29,14 @@ MUTATIONS = {
                        ("out[b, g * group:(g + 1) * group] = _attend", "out[b, g::hkv] = _attend")],
     "decode_query_position": [("q_rot = rope(q[b, g * group:(g + 1) * group], q_pos[b], theta)",
                                "q_rot = rope(q[b, g * group:(g + 1) * group], q_pos[b] + 1, theta)")],
-    "prefill_gqa_map": [("block_table[b], int(kv_lens[b]), h // group, scale, theta)",
-                         "block_table[b], int(kv_lens[b]), h % hkv, scale, theta)")],
+    "prefill_gqa_map": [("block_table[b], int(kv_lens[b]), h // group, scale, theta,",
+                         "block_table[b], int(kv_lens[b]), h % hkv, scale, theta,")],
+    "fill_off_by_one": [("j[(j % BLOCK_TOKENS) < np.asarray(block_fill)[ids]]",
+                         "j[(j % BLOCK_TOKENS) <= np.asarray(block_fill)[ids]]")],
+    "fill_ignored": [("    if block_fill is None or j.size == 0:\n        return j",
+                      "    if True:\n        return j")],
+    "fill_visibility_by_token_count": [("vis = valid_slots(table_row, kv_len, block_fill)[None, :] <= t[:, None]",
+                                        "vis = np.arange(k_hat.shape[0])[None, :] <= t[:, None]")],
     "causal_off_by_one": [("<= t[:, None]", "< t[:, None]")],
     "prefill_query_position": [("q_rot = rope(q_rows, q_pos_start + rows, theta)",
                                 "q_rot = rope(q_rows, q_pos_start + rows + 1, theta)")],
