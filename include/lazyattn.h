@@ -10,8 +10,18 @@
  *   K/V pool   [num_blocks][num_kv_heads][16][head_dim]   element type `dtype`
  *   table word uint32: bits 0..15 = physical block id (< num_blocks <= 65536),
  *              bits 16..31 = the block's position offset (unsigned).
- *   block_table [batch][max_blocks_per_seq] table words; logical token j of a
- *              sequence lives in block word[j / 16], slot j % 16.
+ *   block_table [batch][max_blocks_per_seq] table words; table slot j of a
+ *              sequence is block word[j / 16], slot j % 16.
+ *   block_fill uint8 [num_blocks rounded up to a multiple of 4] or NULL:
+ *              tokens stored in each physical block (0..16; larger values
+ *              count as 16), the rest of the block unused -- the end of a
+ *              document whose length is not a multiple of 16.  NULL means
+ *              every block is full.  Slots past their block's count hold no
+ *              token and are skipped; lengths (seq_lens, kv_lens) still count
+ *              table slots, and a prompt's rows sit in the table's last
+ *              kv_lens - q_len .. kv_lens - 1 slots.  A query that sees no
+ *              token gets zeros.  Read as 32-bit words, hence the rounding.
+ *              Device memory, read only.
  *
  * Position convention.  A stored key carries the rotation of its place within
  * its own frame (a document encoded from position 0, or a prompt encoded from
@@ -25,7 +35,7 @@
  * the null stream), allocate nothing, keep no device state and are
  * re-entrant.  Argument errors are reported by a negative status before any
  * launch.  Device-side preconditions (block ids < num_blocks, offsets and
- * positions < 65536, only a sequence's last block partly filled) are checked
+ * positions < 65536) are checked
  * by the kernels where cheap: a sequence whose length is negative or exceeds
  * 16 * max_blocks_per_seq, or whose table holds a block id >= num_blocks,
  * gets NaN output instead of touching memory outside the pool.
@@ -102,8 +112,8 @@ size_t lazyattn_decode_workspace_size(int batch, int num_q_heads, int num_kv_hea
  *   out         [batch][num_q_heads][head_dim]  dtype      (written)
  *   q           [batch][num_q_heads][head_dim]  dtype, raw (unrotated) query
  *   q_pos       int32 [batch]: absolute position n of each query
- *   k_pool, v_pool, block_table, max_blocks_per_seq: see the layout above
- *   seq_lens    int32 [batch]: tokens of the table the query attends (>= 0)
+ *   k_pool, v_pool, block_table, max_blocks_per_seq, block_fill: see the layout above
+ *   seq_lens    int32 [batch]: table slots the query attends (>= 0)
  *   num_q_heads a multiple of num_kv_heads; query head h reads KV head
  *               h / (num_q_heads / num_kv_heads); the group size is a power
  *               of two up to 64 (64 covers multi-query attention with
@@ -122,7 +132,7 @@ size_t lazyattn_decode_workspace_size(int batch, int num_q_heads, int num_kv_hea
  */
 int lazyattn_decode(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
                     const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
-                    const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                    const uint8_t *block_fill, const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
                     int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
                     int split_blocks, void *workspace, size_t workspace_bytes, void *stream);
 
@@ -138,20 +148,22 @@ int lazyattn_decode(void *out, const void *q, const int32_t *q_pos, const void *
  *   total_q     rows of q and out; a prompt whose rows fall outside [0, total_q)
  *               (or with cu_q_lens decreasing) is left unwritten
  *   q_pos_start int32 [batch]: position of prompt b's first token
- *   kv_lens     int32 [batch]: tokens in the table INCLUDING the prompt, whose
- *               K/V must already be appended as the table's last P_b tokens
+ *   kv_lens     int32 [batch]: table slots INCLUDING the prompt, whose K/V
+ *               must already be appended in the table's last P_b slots (in
+ *               blocks of their own, full except the last)
  *   max_q_len   >= every prompt length (sizes the launch grid)
  *   num_q_heads a multiple of num_kv_heads (group size 1..64)
  *   head_dim    64 or 128; dtype must be LAZYATTN_BF16.
  *
- * Prompt row r of sequence b sits at logical index kv_lens[b] - P_b + r and
- * position q_pos_start[b] + r, and sees the table tokens with logical index
- * <= its own (masking uses table order, never positions).  bf16 MFMA with
+ * Prompt row r of sequence b sits at table slot kv_lens[b] - P_b + r and
+ * position q_pos_start[b] + r, and sees the stored tokens in table slots <=
+ * its own (masking uses table order, never positions).  bf16 MFMA with
  * fp32 accumulation; P is rounded to bf16 for the P.V product.
  */
 int lazyattn_prefill(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
                      const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
-                     const uint32_t *block_table, int max_blocks_per_seq, const int32_t *kv_lens,
+                     const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
+                     const int32_t *kv_lens,
                      int batch, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
                      int num_blocks, int dtype, float scale, float rope_theta, void *stream);
 
@@ -169,13 +181,13 @@ int lazyattn_prefill(void *out, const void *q, int total_q, const int32_t *cu_q_
  */
 int lazyattn_decode_eager(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
                           const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
-                          const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                          const uint8_t *block_fill, const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
                           int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
                           int split_blocks, void *workspace, size_t workspace_bytes, void *stream);
 
 int lazyattn_prefill_eager(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
                            const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
-                           const uint32_t *block_table, int max_blocks_per_seq,
+                           const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
                            const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads,
                            int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
                            float rope_theta, void *stream);
@@ -197,13 +209,14 @@ int lazyattn_prefill_eager(void *out, const void *q, int total_q, const int32_t 
  */
 int lazyattn_decode_alibi(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
                           const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
-                          const int32_t *seq_lens, const float *slopes, int batch, int num_q_heads,
+                          const uint8_t *block_fill, const int32_t *seq_lens, const float *slopes, int batch, int num_q_heads,
                           int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
                           int split_blocks, void *workspace, size_t workspace_bytes, void *stream);
 
 int lazyattn_prefill_alibi(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
                            const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
-                           const uint32_t *block_table, int max_blocks_per_seq, const int32_t *kv_lens,
+                           const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
+                           const int32_t *kv_lens,
                            const float *slopes, int batch, int max_q_len, int num_q_heads,
                            int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
                            void *stream);

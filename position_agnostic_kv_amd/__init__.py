@@ -36,9 +36,9 @@ _SIGNATURES = {
     "lazyattn_version": (_i32, []),
     "kvcache_append": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp]),
     "lazyattn_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
-    "lazyattn_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+    "lazyattn_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                _i32, _f32, _f32, _i32, _vp, _sz, _vp]),
-    "lazyattn_prefill": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+    "lazyattn_prefill": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _i32, _f32, _f32, _vp]),
 }
 _SIGNATURES.update({
@@ -49,10 +49,10 @@ _SIGNATURES.update({
     "lazyattn_cache_stats": (_i32, [_vp, _vp, _i32]),
 })
 _SIGNATURES["lazyattn_decode_eager"] = _SIGNATURES["lazyattn_decode"]
-_SIGNATURES["lazyattn_decode_alibi"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
-                                               _i32, _i32, _f32, _i32, _vp, _sz, _vp])
-_SIGNATURES["lazyattn_prefill_alibi"] = (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
-                                                _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp])
+_SIGNATURES["lazyattn_decode_alibi"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
+                                               _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp])
+_SIGNATURES["lazyattn_prefill_alibi"] = (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+                                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp])
 _SIGNATURES["lazyattn_prefill_eager"] = _SIGNATURES["lazyattn_prefill"]
 
 
@@ -148,36 +148,55 @@ def decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_blocks
 
 
 def lazyattn_decode(q, q_pos, k_pool, v_pool, block_table, seq_lens, *, scale=None,
-                    rope_theta=10000.0, split_blocks=0, out=None, workspace=None, stream=None):
+                    rope_theta=10000.0, split_blocks=0, out=None, workspace=None, stream=None,
+                    block_fill=None):
     """Decode attention; q [B, Hq, D] raw queries at positions q_pos [B].
 
     block_table [B, max_blocks] int32/uint32 words (block id | offset << 16);
-    seq_lens [B] tokens attended.  ``workspace`` (uint8, zero-filled once) is
-    allocated zeroed when not given.  Returns out [B, Hq, D] in q's dtype.
+    seq_lens [B] table slots attended.  ``workspace`` (uint8, zero-filled once)
+    is allocated zeroed when not given.  ``block_fill`` (uint8 [num_blocks],
+    optional): tokens stored in each physical block; None = all full.
+    Returns out [B, Hq, D] in q's dtype.
     """
     return _decode("lazyattn_decode", q, q_pos, k_pool, v_pool, block_table, seq_lens, scale,
-                   rope_theta, split_blocks, out, workspace, stream)
+                   rope_theta, split_blocks, out, workspace, stream, block_fill=block_fill)
 
 
 def lazyattn_decode_eager(q, q_pos, k_pool, v_pool, block_table, seq_lens, *, scale=None,
-                          rope_theta=10000.0, split_blocks=0, out=None, workspace=None, stream=None):
+                          rope_theta=10000.0, split_blocks=0, out=None, workspace=None, stream=None,
+                          block_fill=None):
     """Non-lazy baseline of lazyattn_decode: the pool holds keys already rotated
     to their absolute positions, table offsets are ignored, q is rotated once."""
     return _decode("lazyattn_decode_eager", q, q_pos, k_pool, v_pool, block_table, seq_lens, scale,
-                   rope_theta, split_blocks, out, workspace, stream)
+                   rope_theta, split_blocks, out, workspace, stream, block_fill=block_fill)
 
 
 def lazyattn_decode_alibi(q, q_pos, k_pool, v_pool, block_table, seq_lens, slopes, *, scale=None,
-                          split_blocks=0, out=None, workspace=None, stream=None):
+                          split_blocks=0, out=None, workspace=None, stream=None, block_fill=None):
     """Decode with ALiBi biases instead of RoPE: slopes [Hq] float32 on the
     device; each table word's offset is the absolute position of its block's
     first token.  Otherwise as lazyattn_decode."""
     return _decode("lazyattn_decode_alibi", q, q_pos, k_pool, v_pool, block_table, seq_lens, scale,
-                   None, split_blocks, out, workspace, stream, slopes=slopes)
+                   None, split_blocks, out, workspace, stream, slopes=slopes, block_fill=block_fill)
+
+
+def _fill_arg(block_fill, num_blocks, dev):
+    """The block_fill pointer (NULL for None); the library reads it in 4-byte
+    words, so a tensor shorter than num_blocks rounded up to 4 is padded."""
+    if block_fill is None:
+        return None, ctypes.c_void_p(0)
+    _dev(block_fill)
+    if block_fill.device != dev or block_fill.dtype != torch.uint8 or block_fill.dim() != 1 \
+            or block_fill.numel() < num_blocks:
+        raise LazyAttnError("block_fill must be a uint8 tensor of num_blocks entries on the inputs' device")
+    need = (num_blocks + 3) // 4 * 4
+    if block_fill.numel() < need:
+        block_fill = torch.cat([block_fill, block_fill.new_full((need - block_fill.numel(),), 16)])
+    return block_fill, _ptr(block_fill)
 
 
 def _decode(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, rope_theta, split_blocks,
-            out, workspace, stream, slopes=None):
+            out, workspace, stream, slopes=None, block_fill=None):
     dev = _dev(q, q_pos, k_pool, v_pool, block_table, seq_lens)
     _int32(q_pos, "q_pos")
     _int32(block_table, "block_table")
@@ -203,16 +222,17 @@ def _decode(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, rope_the
     else:
         _dev(workspace, q)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    fill_keep, fill = _fill_arg(block_fill, nb, dev)
     lib = load_library()
     if slopes is not None:
         _slopes(slopes, hq, dev)
         _check(getattr(lib, fn)(_ptr(out), _ptr(q), _ptr(q_pos), _ptr(k_pool), _ptr(v_pool),
-                                _ptr(block_table), max_blocks, _ptr(seq_lens), _ptr(slopes), b, hq, hkv,
+                                _ptr(block_table), max_blocks, fill, _ptr(seq_lens), _ptr(slopes), b, hq, hkv,
                                 d, nb, _dtype_code(q), scale, int(split_blocks), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev)), fn)
         return out
     _check(getattr(lib, fn)(_ptr(out), _ptr(q), _ptr(q_pos), _ptr(k_pool), _ptr(v_pool),
-                            _ptr(block_table), max_blocks, _ptr(seq_lens), b, hq, hkv, d, nb,
+                            _ptr(block_table), max_blocks, fill, _ptr(seq_lens), b, hq, hkv, d, nb,
                             _dtype_code(q), scale, float(rope_theta), int(split_blocks),
                             _ptr(workspace), workspace.numel() * workspace.element_size(),
                             _stream_ptr(stream, dev)), fn)
@@ -228,33 +248,33 @@ def _slopes(slopes, hq, dev):
 
 
 def lazyattn_prefill(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len,
-                     *, scale=None, rope_theta=10000.0, out=None, stream=None):
+                     *, scale=None, rope_theta=10000.0, out=None, stream=None, block_fill=None):
     """Prefill attention; q [Tq, Hq, D] bf16 packed by cu_q_lens [B+1].
 
     The prompts' K/V must already be appended as each table's last tokens;
     kv_lens [B] counts them.  Returns out [Tq, Hq, D] bf16.
     """
     return _prefill("lazyattn_prefill", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
-                    kv_lens, max_q_len, scale, rope_theta, out, stream)
+                    kv_lens, max_q_len, scale, rope_theta, out, stream, block_fill=block_fill)
 
 
 def lazyattn_prefill_eager(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len,
-                           *, scale=None, rope_theta=10000.0, out=None, stream=None):
+                           *, scale=None, rope_theta=10000.0, out=None, stream=None, block_fill=None):
     """Non-lazy baseline of lazyattn_prefill: keys already rotated to their
     absolute positions, table offsets ignored, each query row rotated once."""
     return _prefill("lazyattn_prefill_eager", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
-                    kv_lens, max_q_len, scale, rope_theta, out, stream)
+                    kv_lens, max_q_len, scale, rope_theta, out, stream, block_fill=block_fill)
 
 
 def lazyattn_prefill_alibi(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len,
-                           slopes, *, scale=None, out=None, stream=None):
+                           slopes, *, scale=None, out=None, stream=None, block_fill=None):
     """Prefill with ALiBi biases instead of RoPE (see lazyattn_decode_alibi)."""
     return _prefill("lazyattn_prefill_alibi", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
-                    kv_lens, max_q_len, scale, None, out, stream, slopes=slopes)
+                    kv_lens, max_q_len, scale, None, out, stream, slopes=slopes, block_fill=block_fill)
 
 
 def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len, scale,
-             rope_theta, out, stream, slopes=None):
+             rope_theta, out, stream, slopes=None, block_fill=None):
     dev = _dev(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens)
     for t, n in ((cu_q_lens, "cu_q_lens"), (q_pos_start, "q_pos_start"), (kv_lens, "kv_lens"),
                  (block_table, "block_table")):
@@ -276,16 +296,17 @@ def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens
         if out.shape != q.shape or out.dtype != q.dtype:
             raise LazyAttnError("out must match q")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    fill_keep, fill = _fill_arg(block_fill, nb, dev)
     lib = load_library()
     if slopes is not None:
         _slopes(slopes, hq, dev)
         _check(getattr(lib, fn)(_ptr(out), _ptr(q), tq, _ptr(cu_q_lens), _ptr(q_pos_start), _ptr(k_pool),
-                                _ptr(v_pool), _ptr(block_table), block_table.shape[1], _ptr(kv_lens),
+                                _ptr(v_pool), _ptr(block_table), block_table.shape[1], fill, _ptr(kv_lens),
                                 _ptr(slopes), b, int(max_q_len), hq, hkv, d, nb, _dtype_code(q), scale,
                                 _stream_ptr(stream, dev)), fn)
         return out
     _check(getattr(lib, fn)(_ptr(out), _ptr(q), tq, _ptr(cu_q_lens), _ptr(q_pos_start), _ptr(k_pool),
-                            _ptr(v_pool), _ptr(block_table), block_table.shape[1], _ptr(kv_lens),
+                            _ptr(v_pool), _ptr(block_table), block_table.shape[1], fill, _ptr(kv_lens),
                             b, int(max_q_len), hq, hkv, d, nb, _dtype_code(q), scale,
                             float(rope_theta), _stream_ptr(stream, dev)), fn)
     return out

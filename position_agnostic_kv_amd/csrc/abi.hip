@@ -61,7 +61,7 @@ size_t lazyattn_decode_workspace_size(int batch, int num_q_heads, int num_kv_hea
 
 static int decode_common(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
                          const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
-                         const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                         const uint8_t *block_fill, const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
                          int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
                          int split_blocks, void *workspace, size_t workspace_bytes, void *stream,
                          int mode, const float *slopes) {
@@ -106,35 +106,36 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
   a.rope_theta = rope_theta;
   a.mode = mode;
   a.slopes = slopes;
+  a.block_fill = block_fill;
   return from_hip(launch_decode(a, bf16, (hipStream_t)stream));
 }
 
 int lazyattn_decode(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
                     const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
-                    const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                    const uint8_t *block_fill, const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
                     int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
                     int split_blocks, void *workspace, size_t workspace_bytes, void *stream) {
-  return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens,
+  return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, block_fill, seq_lens,
                        batch, num_q_heads, num_kv_heads, head_dim, num_blocks, dtype, scale,
                        rope_theta, split_blocks, workspace, workspace_bytes, stream, kRopeLazy, nullptr);
 }
 
 int lazyattn_decode_eager(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
                           const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
-                          const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
+                          const uint8_t *block_fill, const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
                           int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
                           int split_blocks, void *workspace, size_t workspace_bytes, void *stream) {
-  return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens,
+  return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, block_fill, seq_lens,
                        batch, num_q_heads, num_kv_heads, head_dim, num_blocks, dtype, scale,
                        rope_theta, split_blocks, workspace, workspace_bytes, stream, kRopeEager, nullptr);
 }
 
 int lazyattn_decode_alibi(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
                           const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
-                          const int32_t *seq_lens, const float *slopes, int batch, int num_q_heads,
+                          const uint8_t *block_fill, const int32_t *seq_lens, const float *slopes, int batch, int num_q_heads,
                           int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
                           int split_blocks, void *workspace, size_t workspace_bytes, void *stream) {
-  return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, seq_lens,
+  return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, block_fill, seq_lens,
                        batch, num_q_heads, num_kv_heads, head_dim, num_blocks, dtype, scale,
                        10000.0f /* unused */, split_blocks, workspace, workspace_bytes, stream, kAlibi,
                        slopes);
@@ -142,7 +143,8 @@ int lazyattn_decode_alibi(void *out, const void *q, const int32_t *q_pos, const 
 
 static int prefill_common(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
                           const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
-                          const uint32_t *block_table, int max_blocks_per_seq, const int32_t *kv_lens,
+                          const uint32_t *block_table, int max_blocks_per_seq,
+                          const uint8_t *block_fill, const int32_t *kv_lens,
                           int batch, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
                           int num_blocks, int dtype, float scale, float rope_theta, void *stream,
                           int mode, const float *slopes) {
@@ -181,38 +183,39 @@ static int prefill_common(void *out, const void *q, int total_q, const int32_t *
   a.rope_theta = rope_theta;
   a.mode = mode;
   a.slopes = slopes;
+  a.block_fill = block_fill;
   return from_hip(launch_prefill(a, (hipStream_t)stream));
 }
 
 int lazyattn_prefill(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
                      const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
-                     const uint32_t *block_table, int max_blocks_per_seq, const int32_t *kv_lens,
+                     const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill, const int32_t *kv_lens,
                      int batch, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
                      int num_blocks, int dtype, float scale, float rope_theta, void *stream) {
   return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
-                        max_blocks_per_seq, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
+                        max_blocks_per_seq, block_fill, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
                         head_dim, num_blocks, dtype, scale, rope_theta, stream, kRopeLazy, nullptr);
 }
 
 int lazyattn_prefill_eager(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
                            const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
-                           const uint32_t *block_table, int max_blocks_per_seq,
+                           const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
                            const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads,
                            int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
                            float rope_theta, void *stream) {
   return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
-                        max_blocks_per_seq, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
+                        max_blocks_per_seq, block_fill, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
                         head_dim, num_blocks, dtype, scale, rope_theta, stream, kRopeEager, nullptr);
 }
 
 int lazyattn_prefill_alibi(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
                            const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
-                           const uint32_t *block_table, int max_blocks_per_seq, const int32_t *kv_lens,
+                           const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill, const int32_t *kv_lens,
                            const float *slopes, int batch, int max_q_len, int num_q_heads,
                            int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
                            void *stream) {
   return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
-                        max_blocks_per_seq, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
+                        max_blocks_per_seq, block_fill, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
                         head_dim, num_blocks, dtype, scale, 10000.0f /* unused */, stream, kAlibi, slopes);
 }
 

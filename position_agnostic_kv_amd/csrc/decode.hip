@@ -77,6 +77,7 @@ struct DecodeKernelArgs {
   const uint32_t *table;
   const int32_t *seq_lens;
   const float *slopes;  // ALiBi: per query head
+  const uint32_t *fill4;  // per-block fill counts, 4 per word (nullptr: all full)
   float *ws_o;    // [B][Hkv][S][G][D]
   float2 *ws_ml;  // [B][Hkv][S][G] (max, sum)
   int max_blocks;
@@ -183,6 +184,9 @@ decode_split_kernel(const DecodeKernelArgs a) {
   bool bad = false;
   int cur_off = -1;
 
+  // Loads block bk's K/V and returns in w its table word with the block id
+  // replaced by the block's fill count (the id is not needed afterwards; the
+  // offset stays in the high half).
   auto issue = [&](int bk, uint32_t &w, uint4 (&kk)[NI], uint4 (&vv)[NI]) {
     w = trow[bk];
     uint32_t id = word_block(w);
@@ -190,6 +194,8 @@ decode_split_kernel(const DecodeKernelArgs a) {
       bad = true;
       id = 0;
     }
+    const uint32_t fill = a.fill4 ? (a.fill4[id >> 2] >> ((id & 3u) * 8u)) & 0xffu : (uint32_t)kBlockTokens;
+    w = (w & 0xffff0000u) | fill;
     // wave-uniform block base (scalar registers) + a 32-bit lane offset
     const size_t hb = ((size_t)id * hkv_pool + gp) * kChunksPerHeadBlock;
     const uint4 *kb = a.k_pool + hb;
@@ -310,9 +316,10 @@ decode_split_kernel(const DecodeKernelArgs a) {
 #pragma unroll
         for (int h = 0; h < G; ++h) s[i][h] = fmaf(slope2[h], base + (float)(i * TPI), s[i][h]);
     }
-    // rows of this block that count: all but the tail of a sequence's last
-    // block, none once the split is exhausted (blk >= blk1: a re-read block)
-    const int nvalid = blk < blk1 ? seq_len - blk * kBlockTokens : 0;
+    // rows of this block that count: its fill count, the sequence's length in
+    // its last block, none once the split is exhausted (blk >= blk1: a
+    // re-read block)
+    const int nvalid = blk < blk1 ? min(seq_len - blk * kBlockTokens, (int)(wcur & 0xffffu)) : 0;
     if (nvalid < kBlockTokens) {  // partly filled or exhausted
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
@@ -450,7 +457,7 @@ decode_split_kernel(const DecodeKernelArgs a) {
       lsum = __builtin_nanf("");
     }
     if (single) {
-      E::store(out, i, o / lsum);
+      E::store(out, i, lsum != 0.f ? o / lsum : 0.f);  // no visible token -> 0 (NaN stays NaN)
     } else {
       a.ws_o[part * G * D + i] = o;
       if (d == 0) a.ws_ml[part * G + h] = make_float2(mx, lsum);
@@ -486,7 +493,7 @@ decode_combine_kernel(const DecodeKernelArgs a) {
       o = fmaf(po[(size_t)sp * G * D + i], f, o);
       lsum = fmaf(ml.y, f, lsum);
     }
-    E::store(out, i, o / lsum);
+    E::store(out, i, lsum != 0.f ? o / lsum : 0.f);
   }
 }
 
@@ -545,6 +552,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   k.table = a.table;
   k.seq_lens = a.seq_lens;
   k.slopes = a.slopes;
+  k.fill4 = (const uint32_t *)a.block_fill;
   const int hsplit = a.num_q_heads / a.num_kv_heads / G;  // work heads per KV head
   const int work_heads = a.num_kv_heads * hsplit;
   k.max_blocks = a.max_blocks;

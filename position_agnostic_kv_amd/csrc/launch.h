@@ -39,6 +39,7 @@ struct DecodeArgs {
   int split_blocks;  // resolved (> 0)
   float scale, rope_theta;
   const float *slopes;  // ALiBi slopes [num_q_heads] (device), else unused
+  const uint8_t *block_fill;  // per-block fill counts, or nullptr (all full)
   int mode;             // PosMode
 };
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t stream);
@@ -55,6 +56,7 @@ struct PrefillArgs {
   int total_q, batch, max_q_len, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks;
   float scale, rope_theta;
   const float *slopes;  // ALiBi slopes [num_q_heads] (device), else unused
+  const uint8_t *block_fill;  // per-block fill counts, or nullptr (all full)
   int mode;             // PosMode
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);

@@ -54,6 +54,7 @@ struct PrefillKernelArgs {
   const uint32_t *table;
   const int32_t *kv_lens;
   const float *slopes;  // ALiBi: per query head
+  const uint32_t *fill4;  // per-block fill counts, 4 per word (nullptr: all full)
   int total_q, batch, num_q_heads, num_kv_heads, num_blocks, max_blocks;
   int head_groups;  // workgroups per KV head (G / HP)
   int tok_tiles;    // token tiles per sequence
@@ -255,11 +256,20 @@ prefill_kernel(const PrefillKernelArgs a) {
       lds_dma16(vg, ld_off[i], (uint32_t)(uintptr_t)(lds_ptr_t)(&sV[BUF][dst]));
     }
   };
+  // per lane: the fill count of the block whose table word the lane holds
+  auto load_fill = [&](uint32_t wv) -> uint32_t {
+    if (!a.fill4) return (uint32_t)kBlockTokens;
+    uint32_t id = word_block(wv);
+    if (id >= (uint32_t)a.num_blocks) id = 0;
+    return (a.fill4[id >> 2] >> ((id & 3u) * 8u)) & 0xffu;
+  };
   // after the wave's own loads landed: zero V rows of its block past kv_len
-  auto fix_tail = [&](int j, int cnt, auto bufc) {
+  // or past the block's fill count (their weights are 0; whatever the pool
+  // holds there must not turn 0 * x into NaN)
+  auto fix_tail = [&](int j, int cnt, uint32_t fv, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
     if (wave >= cnt) return;
-    const int valid = kv_len - (j + wave) * kBlockTokens;
+    const int valid = min(kv_len - (j + wave) * kBlockTokens, __builtin_amdgcn_readlane((int)fv, wave));
     if (valid >= kBlockTokens) return;
     for (int i = lane; i < kBlockTokens * CPR; i += kWave) {
       const int r = i / CPR;
@@ -311,6 +321,7 @@ prefill_kernel(const PrefillKernelArgs a) {
     cj = nblk_vis - ccnt;
   }
   uint32_t cw = load_words(cj);
+  uint32_t cf = load_fill(cw);   // the current tile's fill counts (lanes 0..3)
   if constexpr (!ALIBI) tile_of(cw, 0, ccnt, coff);
   issue_tile(cw, ccnt, std::integral_constant<int, 0>{});
   int nj = ALIBI ? cj - min(kPfTileBlocks, cj) : ccnt;
@@ -348,7 +359,9 @@ prefill_kernel(const PrefillKernelArgs a) {
   auto step = [&](auto bufc) -> bool {
     constexpr int BUF = decltype(bufc)::value;
     __builtin_amdgcn_s_waitcnt(0);   // this tile's loads and the next words have landed
-    fix_tail(cj, ccnt, bufc);
+    fix_tail(cj, ccnt, cf, bufc);
+    // the next tile's fill counts (its words landed above), used when it is current
+    const uint32_t nf = load_fill(nw);
     __syncthreads();
 
     const bool more = ALIBI ? cj > 0 : nj < nblk_vis;
@@ -441,9 +454,10 @@ prefill_kernel(const PrefillKernelArgs a) {
     qk_half(0);
     if (ccnt > kPfTileBlocks / 2) qk_half(1);
 
-    // ---- mask: keys past the tile's run, past kv_len, or after the query token.
-    // Per lane and query column, keys mt*16 + lg*4 + i of the tile stay when
-    // mt*16 + i <= lim.
+    // ---- mask: keys past the tile's run, past kv_len, or after the query token;
+    // and slots past a block's fill count.  Per lane and query column, keys
+    // mt*16 + lg*4 + i of the tile stay when mt*16 + i <= lim and
+    // lg*4 + i < fill(mt).
     const int key0 = cj * kBlockTokens;
     if (ccnt < kPfTileBlocks || key0 + kPfN > kv_len || key0 + kPfN - 1 > t_wave) {
 #pragma unroll
@@ -455,6 +469,15 @@ prefill_kernel(const PrefillKernelArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (mt * 16 + i > lim) S[mt][nt][i] = -INFINITY;
+      }
+    }
+    if (wave_any(lane < ccnt && cf < (uint32_t)kBlockTokens)) {
+#pragma unroll
+      for (int mt = 0; mt < kPfTileBlocks; ++mt) {
+        const int flim = __builtin_amdgcn_readlane((int)cf, mt) - 1 - lg * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i > flim) S[mt][0][i] = S[mt][1][i] = -INFINITY;
       }
     }
 
@@ -545,6 +568,7 @@ prefill_kernel(const PrefillKernelArgs a) {
     ccnt = ncnt;
     coff = noff;
     cw = nw;
+    cf = nf;
     nj = nnj;
     nw = nnw;
     return true;
@@ -560,7 +584,8 @@ prefill_kernel(const PrefillKernelArgs a) {
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const float tot = col_sum4(lsum[nt]);
-    const float inv = flagged ? __builtin_nanf("") : 1.f / tot;
+    // a row with no visible token (fill counts below its own slot) gives 0
+    const float inv = flagged ? __builtin_nanf("") : tot != 0.f ? 1.f / tot : 0.f;
     const int tk = tw0 + nt * 16 + l16;
     if (tk < tok_valid) {
       uint16_t *dst = out + ((size_t)(q0 + tt * TOK + tk) * a.num_q_heads + hq) * D + lg * 4;
@@ -587,6 +612,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   k.table = a.table;
   k.kv_lens = a.kv_lens;
   k.slopes = a.slopes;
+  k.fill4 = (const uint32_t *)a.block_fill;
   k.batch = a.batch;
   k.num_q_heads = a.num_q_heads;
   k.num_kv_heads = a.num_kv_heads;

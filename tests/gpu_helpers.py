@@ -42,13 +42,13 @@ class DeviceCase(DeviceInputs):
                                    self.v_pool, self.table,
                                    self.seq_lens if seq_lens is None else seq_lens,
                                    scale=c.scale, rope_theta=c.rope_theta,
-                                   split_blocks=split_blocks, workspace=workspace)
+                                   split_blocks=split_blocks, workspace=workspace, block_fill=self.fill)
 
     def prefill(self):
         c = self.case
         return pak.lazyattn_prefill(self.q, self.cu, self.q_pos_start, self.k_pool, self.v_pool,
                                     self.table, self.seq_lens, c.max_q_len, scale=c.scale,
-                                    rope_theta=c.rope_theta)
+                                    rope_theta=c.rope_theta, block_fill=self.fill)
 
 
 def host_float(t_or_a, dtype):
@@ -69,7 +69,7 @@ def oracle_decode(case, k_pool=None, v_pool=None):
         k_pool, v_pool = host_pools_after_append(case)
     q = W.to_float(case.q, case.dtype)
     return oracle.decode(q, case.q_pos, k_pool, v_pool, case.layout.table, case.seq_lens,
-                         case.scale, case.rope_theta)
+                         case.scale, case.rope_theta, block_fill=case.block_fill)
 
 
 def oracle_prefill(case, k_pool=None, v_pool=None):
@@ -77,7 +77,7 @@ def oracle_prefill(case, k_pool=None, v_pool=None):
         k_pool, v_pool = host_pools_after_append(case)
     q = W.to_float(case.q, case.dtype)
     return oracle.prefill(q, case.cu_q_lens, case.layout.tail_pos, k_pool, v_pool, case.layout.table,
-                          case.seq_lens, case.scale, case.rope_theta)
+                          case.seq_lens, case.scale, case.rope_theta, block_fill=case.block_fill)
 
 
 def errors(got, want):

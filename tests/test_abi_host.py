@@ -53,11 +53,11 @@ P = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails valida
 
 
 def decode(lib, **kw):
-    a = dict(out=P, q=P, q_pos=P, k=P, v=P, table=P, max_blocks=4, seq_lens=P, batch=2, hq=8, hkv=2,
+    a = dict(out=P, q=P, q_pos=P, k=P, v=P, table=P, max_blocks=4, fill=NULL, seq_lens=P, batch=2, hq=8, hkv=2,
              d=128, nb=16, dtype=1, scale=0.088, theta=1e4, split=0, ws=P, ws_bytes=1 << 30, stream=NULL)
     a.update(kw)
     fn = lib.lazyattn_decode_eager if a.pop("eager", False) else lib.lazyattn_decode
-    return fn(a["out"], a["q"], a["q_pos"], a["k"], a["v"], a["table"], a["max_blocks"],
+    return fn(a["out"], a["q"], a["q_pos"], a["k"], a["v"], a["table"], a["max_blocks"], a["fill"],
               a["seq_lens"], a["batch"], a["hq"], a["hkv"], a["d"], a["nb"], a["dtype"],
               a["scale"], a["theta"], a["split"], a["ws"], a["ws_bytes"], a["stream"])
 
@@ -67,8 +67,8 @@ def test_eager_baseline_checks_arguments_alike(lib):
                {"batch": 0, "q": NULL}, {"ws": NULL, "max_blocks": 4000}):
         assert decode(lib, eager=True, **kw) == decode(lib, **kw)
     f, g = lib.lazyattn_prefill, lib.lazyattn_prefill_eager
-    ok = [P, P, 4096, P, P, P, P, P, 8, P, 2, 128, 32, 8, 128, 64, 1, 0.088, 5e5, NULL]
-    for idx, val in ((16, 0), (14, 256), (2, -1), (1, NULL)):
+    ok = [P, P, 4096, P, P, P, P, P, 8, NULL, P, 2, 128, 32, 8, 128, 64, 1, 0.088, 5e5, NULL]
+    for idx, val in ((17, 0), (15, 256), (2, -1), (1, NULL)):
         bad = list(ok)
         bad[idx] = val
         assert g(*bad) == f(*bad) != 0
@@ -92,15 +92,15 @@ def test_decode_argument_errors(lib):
 
 def test_alibi_entry_points_check_arguments(lib):
     fd, fp = lib.lazyattn_decode_alibi, lib.lazyattn_prefill_alibi
-    ok_d = [P, P, P, P, P, P, 4, P, P, 2, 8, 2, 128, 16, 1, 0.088, 0, P, 1 << 30, NULL]
-    assert fd(*[NULL if i == 8 else x for i, x in enumerate(ok_d)]) == -1     # slopes NULL
-    assert fd(*[7 if i == 14 else x for i, x in enumerate(ok_d)]) == -2      # dtype
-    assert fd(*[96 if i == 12 else x for i, x in enumerate(ok_d)]) == -3     # head_dim
-    assert fd(*[0 if i == 9 else (NULL if i == 8 else x) for i, x in enumerate(ok_d)]) == 0  # empty batch
-    ok_p = [P, P, 4096, P, P, P, P, P, 8, P, P, 2, 128, 32, 8, 128, 64, 1, 0.088, NULL]
-    assert fp(*[NULL if i == 10 else x for i, x in enumerate(ok_p)]) == -1
-    assert fp(*[0 if i == 17 else x for i, x in enumerate(ok_p)]) == -2      # fp32 prefill not offered
-    assert fp(*[96 if i == 15 else x for i, x in enumerate(ok_p)]) == -3
+    ok_d = [P, P, P, P, P, P, 4, NULL, P, P, 2, 8, 2, 128, 16, 1, 0.088, 0, P, 1 << 30, NULL]
+    assert fd(*[NULL if i == 9 else x for i, x in enumerate(ok_d)]) == -1     # slopes NULL
+    assert fd(*[7 if i == 15 else x for i, x in enumerate(ok_d)]) == -2      # dtype
+    assert fd(*[96 if i == 13 else x for i, x in enumerate(ok_d)]) == -3     # head_dim
+    assert fd(*[0 if i == 10 else (NULL if i == 9 else x) for i, x in enumerate(ok_d)]) == 0  # empty batch
+    ok_p = [P, P, 4096, P, P, P, P, P, 8, NULL, P, P, 2, 128, 32, 8, 128, 64, 1, 0.088, NULL]
+    assert fp(*[NULL if i == 11 else x for i, x in enumerate(ok_p)]) == -1
+    assert fp(*[0 if i == 18 else x for i, x in enumerate(ok_p)]) == -2      # fp32 prefill not offered
+    assert fp(*[96 if i == 16 else x for i, x in enumerate(ok_p)]) == -3
 
 
 def test_workspace_size(lib):
@@ -116,12 +116,12 @@ def test_workspace_size(lib):
 
 def test_prefill_and_append_argument_errors(lib):
     f = lib.lazyattn_prefill
-    ok = [P, P, 4096, P, P, P, P, P, 8, P, 2, 128, 32, 8, 128, 64, 1, 0.088, 5e5, NULL]
+    ok = [P, P, 4096, P, P, P, P, P, 8, NULL, P, 2, 128, 32, 8, 128, 64, 1, 0.088, 5e5, NULL]
     bad_dtype = list(ok)
-    bad_dtype[16] = 0
+    bad_dtype[17] = 0
     assert f(*bad_dtype) == -2                      # fp32 prefill not offered
     bad_d = list(ok)
-    bad_d[14] = 256
+    bad_d[15] = 256
     assert f(*bad_d) == -3
     bad_tq = list(ok)
     bad_tq[2] = -1
@@ -130,7 +130,7 @@ def test_prefill_and_append_argument_errors(lib):
     null_q[1] = NULL
     assert f(*null_q) == -1
     empty = list(ok)
-    empty[10] = 0
+    empty[11] = 0
     empty[1] = NULL
     assert f(*empty) == 0
     a = lib.kvcache_append

@@ -16,7 +16,10 @@ Layout conventions (the same ones the library documents):
   * Table word: block id in bits 0..15, position offset in bits 16..31.
   * Every block of a document carries the document's start position as its
     offset; a prompt's (or a new token's) blocks carry the prompt's first
-    position.  Only a sequence's last block may be partly filled.
+    position.  Only a sequence's last block may be partly filled, except in
+    ragged layouts, where every document's last block may be: there a
+    per-block fill count (uint8 per physical block) says how many of its 16
+    slots hold tokens, and lengths count table slots.
 """
 
 from dataclasses import dataclass, field
@@ -70,6 +73,8 @@ class Layout:
     slot_mapping: np.ndarray     # int32 [sum(tail_lens)] pool slot of each appended token
     doc_spans: List[list] = field(default_factory=list)  # per seq: (doc, length, offset)
     unique_doc_tokens: int = 0   # tokens physically stored for documents
+    block_fill: np.ndarray = None  # ragged layouts: uint8 [num_blocks] tokens per block
+    slot_lens: np.ndarray = None   # ragged layouts: int32 [B] table slots up to the last token
 
     @property
     def total_lens(self):
@@ -81,7 +86,7 @@ class Layout:
 
 
 def build_layout(rng, seq_docs, doc_lens, tail_lens, offsets=None, tail_pos=None,
-                 spare_blocks=0, shuffle=True):
+                 spare_blocks=0, shuffle=True, ragged=False):
     """Place documents and appended tails into a shuffled block pool.
 
     seq_docs[b]  : list of document indices making up sequence b (in order).
@@ -93,6 +98,8 @@ def build_layout(rng, seq_docs, doc_lens, tail_lens, offsets=None, tail_pos=None
     tail_pos[b]  : position of the first appended token (default: right after
                    the documents).
     A document used by several sequences is stored once (zero-copy reuse).
+    ragged=True lets any document end mid-block and records block_fill (the
+    tokens of each physical block, 16 for spare blocks) and slot_lens.
     """
     bsz = len(seq_docs)
     doc_blocks = {}
@@ -112,15 +119,20 @@ def build_layout(rng, seq_docs, doc_lens, tail_lens, offsets=None, tail_pos=None
     if n_blocks > 0x10000:
         raise ValueError("pool needs more than 65536 blocks")
     perm = rng.permutation(n_blocks) if shuffle else np.arange(n_blocks)
+    fill = None
+    if ragged:
+        fill = np.full(n_blocks, BLOCK, dtype=np.uint8)
+        for d, (first, nb) in doc_blocks.items():
+            fill[perm[first + nb - 1]] = int(doc_lens[d]) - BLOCK * (nb - 1)
 
-    rows, cached, tpos, spans, slots = [], [], [], [], []
+    rows, cached, tpos, spans, slots, slot_lens = [], [], [], [], [], []
     for b, docs in enumerate(seq_docs):
         words = []
         pos = 0
         span = []
         for i, d in enumerate(docs):
             ln = int(doc_lens[d])
-            if ln % BLOCK and (i != len(docs) - 1 or tail_lens[b]):
+            if ln % BLOCK and not ragged and (i != len(docs) - 1 or tail_lens[b]):
                 raise ValueError("only a sequence's last item may end mid-block")
             off = pos if offsets is None else int(offsets[b][i])
             first, nb = doc_blocks[d]
@@ -136,6 +148,10 @@ def build_layout(rng, seq_docs, doc_lens, tail_lens, offsets=None, tail_pos=None
         words.extend(pack_words(ids, [tp] * nbt).tolist())
         for t in range(nt):
             slots.append(int(ids[t // BLOCK]) * BLOCK + t % BLOCK)
+        if ragged:
+            for i in range(nbt):
+                fill[ids[i]] = min(BLOCK, nt - BLOCK * i)
+        slot_lens.append(BLOCK * (len(words) - nbt) + nt)
         rows.append(words)
         spans.append(span)
     width = max(1, max(len(r) for r in rows))
@@ -147,7 +163,8 @@ def build_layout(rng, seq_docs, doc_lens, tail_lens, offsets=None, tail_pos=None
                   tail_lens=np.array(tail_lens, dtype=np.int32),
                   tail_pos=np.array(tpos, dtype=np.int32),
                   slot_mapping=np.array(slots, dtype=np.int32),
-                  doc_spans=spans, unique_doc_tokens=unique_tokens)
+                  doc_spans=spans, unique_doc_tokens=unique_tokens, block_fill=fill,
+                  slot_lens=np.array(slot_lens, dtype=np.int32) if ragged else None)
 
 
 def block_frame_table(layout):
@@ -224,8 +241,14 @@ class Case:
 
     @property
     def seq_lens(self):
-        """Tokens attended by the step (cached + appended)."""
-        return self.layout.total_lens
+        """Lengths the library takes: tokens attended by the step (cached +
+        appended), counted in table slots for ragged layouts."""
+        lay = self.layout
+        return lay.total_lens if lay.slot_lens is None else lay.slot_lens
+
+    @property
+    def block_fill(self):
+        return self.layout.block_fill
 
     @property
     def cu_q_lens(self):
@@ -238,7 +261,7 @@ class Case:
     def kv_bytes_read(self):
         """Logical K+V bytes a decode pass reads (every attended token once)."""
         esz = 4 if self.dtype == F32 else 2
-        return int(self.seq_lens.sum()) * self.num_kv_heads * self.head_dim * 2 * esz
+        return int(self.layout.total_lens.sum()) * self.num_kv_heads * self.head_dim * 2 * esz
 
     def attention_flops(self):
         """4*D FLOPs per visible (query, key) pair per query head (QK^T and PV)."""
@@ -481,6 +504,38 @@ def prefill_case(seed, batch, num_q_heads, num_kv_heads, head_dim, cached, promp
     return Case(name, "prefill", dtype, num_q_heads, num_kv_heads, head_dim, theta, lay, seed=seed)
 
 
+def ragged_case(seed, kind, batch, num_q_heads, num_kv_heads, head_dim, docs_per_seq=(2, 5),
+                doc_len=(1, 700), prompt=(1, 300), catalogue=None, dtype=BF16, theta=5.0e5,
+                offsets="contiguous", name="ragged"):
+    """Documents of any token count (their last blocks partly filled).
+
+    A catalogue of documents (default: enough that few are shared) with
+    lengths U{doc_len}, whose first entries are forced to the edge lengths 1,
+    15, 16, 17, 31 and 33; each sequence draws U{docs_per_seq} distinct ones.
+    Decode appends one new token per sequence; prefill a prompt of U{prompt}
+    tokens.  Layout is ragged: block_fill and table-slot lengths are set.
+    """
+    rng = np.random.default_rng(seed)
+    ncat = catalogue or batch * docs_per_seq[1]
+    lens = [int(x) for x in rng.integers(doc_len[0], doc_len[1] + 1, size=ncat)]
+    edge = [1, 15, 16, 17, 31, 33]
+    lens[:min(len(edge), ncat)] = edge[:ncat]
+    seq_docs, offs, tpos = [], [], []
+    for _ in range(batch):
+        k = int(rng.integers(docs_per_seq[0], docs_per_seq[1] + 1))
+        seq_docs.append([int(d) for d in rng.choice(ncat, size=min(k, ncat), replace=False)])
+        if offsets == "random":
+            offs.append([int(x) for x in rng.integers(0, 30000, size=len(seq_docs[-1]))])
+            tpos.append(int(rng.integers(0, 30000)))
+    if kind == "decode":
+        tails = [1] * batch
+    else:
+        tails = [int(x) for x in rng.integers(prompt[0], prompt[1] + 1, size=batch)]
+    lay = build_layout(rng, seq_docs, lens, tails, offsets=offs if offsets == "random" else None,
+                       tail_pos=tpos if offsets == "random" else None, ragged=True)
+    return Case(name, kind, dtype, num_q_heads, num_kv_heads, head_dim, theta, lay, seed=seed)
+
+
 def llama8b_prefill(seed=3, batch=4, cached=6144, prompt=2048):
     """Llama-3.1-8B-shaped single-layer prefill, bf16: 32 q / 8 KV heads, d_h=128.
 
@@ -508,6 +563,6 @@ __all__ = [
     "BLOCK", "F32", "BF16", "Case", "Layout", "build_layout", "pack_words",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "to_float", "materialize_numpy",
     "materialize_torch", "add_score_shift", "decode_case", "prefill_case", "tiny_decode",
-    "llama8b_decode", "llama8b_prefill", "llama70b_decode", "zipf_decode", "make",
+    "llama8b_decode", "llama8b_prefill", "llama70b_decode", "zipf_decode", "ragged_case", "make",
     "WORKLOADS",
 ]

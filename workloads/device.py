@@ -41,3 +41,4 @@ class DeviceInputs:
         self.q_pos = int32_to_device(case.q_pos, device)
         self.cu = int32_to_device(case.cu_q_lens, device)
         self.q_pos_start = int32_to_device(lay.tail_pos, device)
+        self.fill = None if lay.block_fill is None else torch.from_numpy(lay.block_fill).to(device)
