@@ -52,13 +52,15 @@ def measured_traffic(name, sources):
 
 
 def decode_algorithmic_bytes(case):
-    """K+V of every attended token once, plus q in, out, table words and lengths."""
+    """K+V of every attended token once, plus q in, out, table words and
+    lengths (and one fill count per block when documents end mid-block)."""
     esz = 2
     d, hq, hkv = case.head_dim, case.num_q_heads, case.num_kv_heads
-    tokens = int(case.seq_lens.sum())
+    tokens = int(case.layout.total_lens.sum())
     kv = tokens * hkv * d * 2 * esz
     qo = case.batch * hq * d * esz * 2
-    table = int(sum(-(-int(n) // 16) for n in case.seq_lens)) * 4 + case.batch * 8
+    nblk = int(sum(-(-int(n) // 16) for n in case.seq_lens))
+    table = nblk * (4 if case.block_fill is None else 5) + case.batch * 8
     return kv, kv + qo + table
 
 
@@ -227,8 +229,10 @@ def overhead_main(args):
 
 
 def shapes_main(args):
-    """Kernel time of every decode workload (8B, 70B, Zipf mix) and of the 8B
-    prefill, each on its own HBM-resident inputs: medians and p10/p90 of
+    """Kernel time of every decode workload (8B, 70B, Zipf mix, 8B with
+    documents of any token count, 8B with ALiBi) and of the 8B prefill (RoPE,
+    ALiBi, documents of any token count), each on its own HBM-resident
+    inputs: medians and p10/p90 of
     `args.steps` launches after `args.warmup`.  One JSON line."""
     import torch
     import position_agnostic_kv_amd as pak
@@ -262,7 +266,7 @@ def shapes_main(args):
     res = {"metric": "kernel time per workload (decode: K+V GB/s; prefill: attention TFLOP/s)",
            "steps": args.steps, "warmup": args.warmup, "data": "synthetic", "peak_hbm_gbps": HBM_PEAK_GBPS,
            "peak_bf16_tflops": BF16_PEAK_TFLOPS}
-    for name in ("llama8b_decode", "llama70b_decode", "zipf_reuse_decode"):
+    for name in ("llama8b_decode", "llama70b_decode", "zipf_reuse_decode", "llama8b_decode_ragged"):
         case = W.make(name)
         W.materialize_torch(case, dev)
         d = DeviceInputs(case, dev)
@@ -273,7 +277,7 @@ def shapes_main(args):
         ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
         med, p10, p90 = timed(lambda: pak.lazyattn_decode(d.q, d.q_pos, d.k_pool, d.v_pool, d.table, d.seq_lens,
                                                           scale=case.scale, rope_theta=case.rope_theta,
-                                                          out=out, workspace=ws))
+                                                          out=out, workspace=ws, block_fill=d.fill))
         kv, alg = decode_algorithmic_bytes(case)
         phys = int(case.k_pool.numel()) * 2 * 2 if name == "zipf_reuse_decode" else None
         r = {"ms_p50": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
@@ -282,6 +286,8 @@ def shapes_main(args):
              "batch": case.batch, "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads}
         if phys is not None:
             r["pool_bytes_physical"] = phys
+        if d.fill is not None:
+            r["table_slots_per_token"] = round(float(case.seq_lens.sum() / case.layout.total_lens.sum()), 4)
         res[name] = r
         if name == "llama8b_decode":  # the same inputs read with ALiBi biases instead of RoPE
             import oracle
@@ -316,6 +322,25 @@ def shapes_main(args):
     res["llama8b_prefill_alibi"] = {"ms_p50": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
                                     "tflops": round(fl / (med * 1e-3) / 1e12, 1),
                                     "frac_of_bf16_peak": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del d, out
+    case.q = case.k_pool = case.v_pool = case.k_new = case.v_new = None
+    torch.cuda.empty_cache()
+    # documents of any token count: tiles are cut at document starts, so the
+    # partly filled last blocks cost MFMA work on masked slots
+    case = W.make("llama8b_prefill_ragged")
+    W.materialize_torch(case, dev)
+    d = DeviceInputs(case, dev)
+    pak.kvcache_append(d.k_pool, d.v_pool, d.k_new, d.v_new, d.slots)
+    out = torch.empty_like(d.q)
+    med, p10, p90 = timed(lambda: pak.lazyattn_prefill(d.q, d.cu, d.q_pos_start, d.k_pool, d.v_pool, d.table,
+                                                       d.seq_lens, case.max_q_len, scale=case.scale,
+                                                       rope_theta=case.rope_theta, out=out, block_fill=d.fill))
+    fl = case.attention_flops()
+    res["llama8b_prefill_ragged"] = {"ms_p50": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
+                                     "attention_flops": fl, "tflops": round(fl / (med * 1e-3) / 1e12, 1),
+                                     "frac_of_bf16_peak": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                     "table_slots_per_token": round(float(case.seq_lens.sum()
+                                                                          / case.layout.total_lens.sum()), 4)}
     print(json.dumps(res), flush=True)
 
 
@@ -528,7 +553,7 @@ def main():
                               "pattern of decode)"},
         "wall_s_timed": round(wall, 3),
         "roofline": {
-            "kernel": "lazyattn::decode_split_kernel<bf16, 128, 4, false>",
+            "kernel": "lazyattn::decode_split_kernel<lazyattn::bf16, 128, 4, 0>",
             "bound": "hbm",
             "achieved": round(dec_achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -538,7 +563,7 @@ def main():
             "algorithmic_bytes": dec_alg_bytes,
         },
         "roofline_prefill": {
-            "kernel": "lazyattn::prefill_kernel<128, 4, false>",
+            "kernel": "lazyattn::prefill_kernel<128, 4, 0>",
             "bound": "mfma",
             "achieved": round(pf_tflops, 2),
             "peak": BF16_PEAK_TFLOPS,

@@ -536,6 +536,43 @@ def ragged_case(seed, kind, batch, num_q_heads, num_kv_heads, head_dim, docs_per
     return Case(name, kind, dtype, num_q_heads, num_kv_heads, head_dim, theta, lay, seed=seed)
 
 
+def _ragged_docs(rng, total, lo, hi):
+    """Document lengths U{lo..hi} tokens (any count, not whole blocks) summing to total."""
+    lens = []
+    left = total
+    while left > 0:
+        ln = min(int(rng.integers(lo, hi + 1)), left)
+        lens.append(ln)
+        left -= ln
+    return lens
+
+
+def llama8b_decode_ragged(seed=6, batch=64, ctx=8192):
+    """The 8B decode shape with documents of U{256..2048} tokens, any count:
+    every document's last block is partly filled (on average 7.5 unused
+    slots per document), lengths are table slots."""
+    rng = np.random.default_rng(seed)
+    seq_docs, doc_lens = [], []
+    for _ in range(batch):
+        lens = _ragged_docs(rng, ctx, 256, 2048)
+        seq_docs.append(list(range(len(doc_lens), len(doc_lens) + len(lens))))
+        doc_lens.extend(lens)
+    lay = build_layout(rng, seq_docs, doc_lens, [1] * batch, ragged=True)
+    return Case("llama8b_decode_ragged", "decode", BF16, 32, 8, 128, 5.0e5, lay, seed=seed)
+
+
+def llama8b_prefill_ragged(seed=7, batch=4, cached=6144, prompt=2048):
+    """The 8B prefill shape with cached documents of U{256..2048} tokens, any count."""
+    rng = np.random.default_rng(seed)
+    seq_docs, doc_lens = [], []
+    for _ in range(batch):
+        lens = _ragged_docs(rng, cached, 256, 2048)
+        seq_docs.append(list(range(len(doc_lens), len(doc_lens) + len(lens))))
+        doc_lens.extend(lens)
+    lay = build_layout(rng, seq_docs, doc_lens, [prompt] * batch, ragged=True)
+    return Case("llama8b_prefill_ragged", "prefill", BF16, 32, 8, 128, 5.0e5, lay, seed=seed)
+
+
 def llama8b_prefill(seed=3, batch=4, cached=6144, prompt=2048):
     """Llama-3.1-8B-shaped single-layer prefill, bf16: 32 q / 8 KV heads, d_h=128.
 
@@ -552,6 +589,8 @@ WORKLOADS = {
     "llama8b_prefill": llama8b_prefill,
     "llama70b_decode": llama70b_decode,
     "zipf_reuse_decode": zipf_decode,
+    "llama8b_decode_ragged": llama8b_decode_ragged,
+    "llama8b_prefill_ragged": llama8b_prefill_ragged,
 }
 
 
@@ -563,6 +602,7 @@ __all__ = [
     "BLOCK", "F32", "BF16", "Case", "Layout", "build_layout", "pack_words",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "to_float", "materialize_numpy",
     "materialize_torch", "add_score_shift", "decode_case", "prefill_case", "tiny_decode",
-    "llama8b_decode", "llama8b_prefill", "llama70b_decode", "zipf_decode", "ragged_case", "make",
+    "llama8b_decode", "llama8b_prefill", "llama70b_decode", "zipf_decode", "ragged_case",
+    "llama8b_decode_ragged", "llama8b_prefill_ragged", "make",
     "WORKLOADS",
 ]
