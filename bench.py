@@ -228,6 +228,35 @@ def overhead_main(args):
     print(json.dumps(res), flush=True)
 
 
+def fp8_decode_algorithmic_bytes(case):
+    """decode_algorithmic_bytes with one byte per K/V element."""
+    kv, total = decode_algorithmic_bytes(case)
+    return kv // 2, total - kv // 2
+
+
+def fp8_decode_shape(case, d, out, ws, timed):
+    """Time lazyattn_decode_fp8 on the case's layout with an 8-bit pool of
+    random E4M3 codes (k_scale 0.25, v_scale 0.125); the step's new rows are
+    quantised in by kvcache_append_fp8 first."""
+    import torch
+    import position_agnostic_kv_amd as pak
+    import workloads as W
+    shape = tuple(d.k_pool.shape)
+    k8 = W.e4m3_codes_torch(shape, d.k_pool.device, case.seed + 5000)
+    v8 = W.e4m3_codes_torch(shape, d.k_pool.device, case.seed + 6000)
+    pak.kvcache_append_fp8(k8, v8, d.k_new, d.v_new, d.slots, 0.25, 0.125)
+    med, p10, p90 = timed(lambda: pak.lazyattn_decode_fp8(d.q, d.q_pos, k8, v8, d.table, d.seq_lens, 0.25, 0.125,
+                                                          scale=case.scale, rope_theta=case.rope_theta,
+                                                          out=out, workspace=ws))
+    kv, alg = fp8_decode_algorithmic_bytes(case)
+    del k8, v8
+    torch.cuda.empty_cache()
+    return {"ms_p50": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
+            "kv_bytes_logical": kv, "gbps_logical": round(kv / (med * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "tokens_per_s": round(float(case.layout.total_lens.sum()) / (med * 1e-3), 0)}
+
+
 def shapes_main(args):
     """Kernel time of every decode workload (8B, 70B, Zipf mix, 8B with
     documents of any token count, 8B with ALiBi) and of the 8B prefill (RoPE,
@@ -289,6 +318,8 @@ def shapes_main(args):
         if d.fill is not None:
             r["table_slots_per_token"] = round(float(case.seq_lens.sum() / case.layout.total_lens.sum()), 4)
         res[name] = r
+        if name in ("llama8b_decode", "llama70b_decode"):  # the same geometry over an 8-bit (E4M3) pool
+            res[name + "_fp8"] = fp8_decode_shape(case, d, out, ws, timed)
         if name == "llama8b_decode":  # the same inputs read with ALiBi biases instead of RoPE
             import oracle
             tab = torch.from_numpy(W.block_frame_table(case.layout).view(np.int32)).to(dev)

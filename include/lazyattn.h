@@ -221,6 +221,43 @@ int lazyattn_prefill_alibi(void *out, const void *q, int total_q, const int32_t 
                            int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
                            void *stream);
 
+/*
+ * 8-bit KV pools.  The pages name a one-byte KV cache without defining it
+ * (ai-engineering.academy "KV Cache, Flash Attention & Otimização de
+ * Inferência", section "Use-o": serving with an fp8 KV-cache dtype;
+ * lynx-cortex "00 — Por qué existe un KV Cache", "El precio": one byte per
+ * element).  Here a pool element is an OCP FP8 E4M3 code (1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits, subnormals, no infinities, S.1111.111 =
+ * NaN, largest magnitude 448) with one float scale per tensor: the value a
+ * code stands for is decode(code) * scale.  Layout as above with one byte per
+ * element: [num_blocks][num_kv_heads][16][head_dim] uint8.
+ *
+ * kvcache_append_fp8 -- kvcache_append into 8-bit pools.  k_new/v_new are
+ * `dtype` rows (LAZYATTN_F32 or LAZYATTN_BF16).  Each element is stored as the
+ * E4M3 code nearest to the float32 quotient x / scale (correctly rounded
+ * division), ties to an even mantissa, magnitudes above 448 saturating to
+ * +-448, NaN as 0x7F.  k_scale, v_scale must be finite and > 0
+ * (LAZYATTN_ERR_SHAPE otherwise).  Other arguments as kvcache_append.
+ */
+int kvcache_append_fp8(void *k_pool, void *v_pool, int dtype, int num_blocks, int num_kv_heads,
+                       int head_dim, const void *k_new, const void *v_new, const int32_t *slot_mapping,
+                       int num_tokens, float k_scale, float v_scale, void *stream);
+
+/*
+ * lazyattn_decode_fp8 -- lazyattn_decode (lazy RoPE) against 8-bit pools:
+ * keys are decode(code) * k_scale, values decode(code) * v_scale.  q and out
+ * are bf16; head_dim must be 128.  Reads one byte per K/V element, half of the
+ * bf16 pool's traffic.  The workspace is sized by
+ * lazyattn_decode_workspace_size with the same arguments.  Other arguments
+ * and errors as lazyattn_decode.
+ */
+int lazyattn_decode_fp8(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                        const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                        const uint8_t *block_fill, const int32_t *seq_lens, int batch, int num_q_heads,
+                        int num_kv_heads, int head_dim, int num_blocks, float scale, float rope_theta,
+                        float k_scale, float v_scale, int split_blocks, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

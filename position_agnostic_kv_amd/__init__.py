@@ -22,7 +22,8 @@ import torch
 __all__ = [
     "LazyAttnError", "lib_path", "load_library", "version", "kvcache_append",
     "decode_workspace_size", "lazyattn_decode", "lazyattn_prefill", "lazyattn_decode_eager",
-    "lazyattn_prefill_eager", "lazyattn_decode_alibi", "lazyattn_prefill_alibi", "BLOCK_TOKENS",
+    "lazyattn_prefill_eager", "lazyattn_decode_alibi", "lazyattn_prefill_alibi", "kvcache_append_fp8",
+    "lazyattn_decode_fp8", "BLOCK_TOKENS",
 ]
 
 BLOCK_TOKENS = 16
@@ -54,6 +55,9 @@ _SIGNATURES["lazyattn_decode_alibi"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i3
 _SIGNATURES["lazyattn_prefill_alibi"] = (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
                                                 _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp])
 _SIGNATURES["lazyattn_prefill_eager"] = _SIGNATURES["lazyattn_prefill"]
+_SIGNATURES["kvcache_append_fp8"] = (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _f32, _f32, _vp])
+_SIGNATURES["lazyattn_decode_fp8"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                                             _i32, _f32, _f32, _f32, _f32, _i32, _vp, _sz, _vp])
 
 
 class LazyAttnError(RuntimeError):
@@ -141,6 +145,42 @@ def kvcache_append(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
                               _stream_ptr(stream, dev)), "kvcache_append")
 
 
+_POOL8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def kvcache_append_fp8(k_pool, v_pool, k_new, v_new, slot_mapping, k_scale, v_scale, stream=None):
+    """Quantise rows k_new/v_new [T, Hkv, D] (bf16 or f32) into an 8-bit pool
+    (uint8 or float8_e4m3fn [NB, Hkv, 16, D] of E4M3 codes): code = nearest E4M3
+    of the float32 x / scale, saturating at 448.  Slots < 0 are skipped."""
+    dev = _dev(k_pool, v_pool, k_new, v_new, slot_mapping)
+    _int32(slot_mapping, "slot_mapping")
+    nb, hkv, bt, d = k_pool.shape
+    if bt != BLOCK_TOKENS or v_pool.shape != k_pool.shape:
+        raise LazyAttnError("pools must be [num_blocks, num_kv_heads, 16, head_dim]")
+    if k_pool.dtype not in _POOL8 or v_pool.dtype != k_pool.dtype:
+        raise LazyAttnError("8-bit pools must be uint8 or float8_e4m3fn")
+    if k_new.shape != v_new.shape or k_new.shape[1:] != (hkv, d) or k_new.dtype != v_new.dtype:
+        raise LazyAttnError("k_new/v_new must be [T, num_kv_heads, head_dim] of one dtype")
+    if slot_mapping.numel() != k_new.shape[0]:
+        raise LazyAttnError("slot_mapping must have one entry per new row")
+    lib = load_library()
+    _check(lib.kvcache_append_fp8(_ptr(k_pool), _ptr(v_pool), _dtype_code(k_new), nb, hkv, d,
+                                  _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), k_new.shape[0],
+                                  float(k_scale), float(v_scale), _stream_ptr(stream, dev)),
+           "kvcache_append_fp8")
+
+
+def lazyattn_decode_fp8(q, q_pos, k_pool, v_pool, block_table, seq_lens, k_scale, v_scale, *, scale=None,
+                        rope_theta=10000.0, split_blocks=0, out=None, workspace=None, stream=None,
+                        block_fill=None):
+    """lazyattn_decode over an 8-bit pool of E4M3 codes (uint8 or
+    float8_e4m3fn): keys are decode(code) * k_scale, values decode(code) *
+    v_scale.  q and out are bf16; head_dim 128."""
+    return _decode("lazyattn_decode_fp8", q, q_pos, k_pool, v_pool, block_table, seq_lens, scale,
+                   rope_theta, split_blocks, out, workspace, stream, block_fill=block_fill,
+                   kv_scales=(float(k_scale), float(v_scale)))
+
+
 def decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
                           split_blocks=0):
     return int(load_library().lazyattn_decode_workspace_size(
@@ -196,7 +236,7 @@ def _fill_arg(block_fill, num_blocks, dev):
 
 
 def _decode(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, rope_theta, split_blocks,
-            out, workspace, stream, slopes=None, block_fill=None):
+            out, workspace, stream, slopes=None, block_fill=None, kv_scales=None):
     dev = _dev(q, q_pos, k_pool, v_pool, block_table, seq_lens)
     _int32(q_pos, "q_pos")
     _int32(block_table, "block_table")
@@ -205,7 +245,10 @@ def _decode(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, rope_the
     nb, hkv, bt, dk = k_pool.shape
     if bt != BLOCK_TOKENS or dk != d or v_pool.shape != k_pool.shape:
         raise LazyAttnError("pools must be [num_blocks, num_kv_heads, 16, head_dim]")
-    if q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
+    if kv_scales is not None:
+        if q.dtype != torch.bfloat16 or k_pool.dtype not in _POOL8 or v_pool.dtype != k_pool.dtype:
+            raise LazyAttnError("8-bit pools (uint8 or float8_e4m3fn) take bf16 queries")
+    elif q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
         raise LazyAttnError("q and pools must share a dtype")
     if block_table.dim() != 2 or block_table.shape[0] != b or q_pos.numel() != b or seq_lens.numel() != b:
         raise LazyAttnError("block_table [B, max_blocks], q_pos [B], seq_lens [B]")
@@ -230,6 +273,13 @@ def _decode(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, rope_the
                                 _ptr(block_table), max_blocks, fill, _ptr(seq_lens), _ptr(slopes), b, hq, hkv,
                                 d, nb, _dtype_code(q), scale, int(split_blocks), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev)), fn)
+        return out
+    if kv_scales is not None:
+        _check(getattr(lib, fn)(_ptr(out), _ptr(q), _ptr(q_pos), _ptr(k_pool), _ptr(v_pool),
+                                _ptr(block_table), max_blocks, fill, _ptr(seq_lens), b, hq, hkv, d, nb,
+                                scale, float(rope_theta), kv_scales[0], kv_scales[1], int(split_blocks),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream_ptr(stream, dev)), fn)
         return out
     _check(getattr(lib, fn)(_ptr(out), _ptr(q), _ptr(q_pos), _ptr(k_pool), _ptr(v_pool),
                             _ptr(block_table), max_blocks, fill, _ptr(seq_lens), b, hq, hkv, d, nb,

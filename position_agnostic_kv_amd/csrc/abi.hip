@@ -13,6 +13,7 @@ namespace {
 bool valid_dtype(int dtype) { return dtype == LAZYATTN_F32 || dtype == LAZYATTN_BF16; }
 int elem_bytes(int dtype) { return dtype == LAZYATTN_F32 ? 4 : 2; }
 bool pow2_group(int g) { return g >= 1 && g <= 64 && (g & (g - 1)) == 0; }
+bool valid_kv_scale(float s) { return s > 0.f && isfinite(s); }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? LAZYATTN_OK : LAZYATTN_ERR_LAUNCH; }
 
@@ -50,6 +51,23 @@ int kvcache_append(void *k_pool, void *v_pool, int dtype, int num_blocks, int nu
                                 (hipStream_t)stream));
 }
 
+int kvcache_append_fp8(void *k_pool, void *v_pool, int dtype, int num_blocks, int num_kv_heads,
+                       int head_dim, const void *k_new, const void *v_new, const int32_t *slot_mapping,
+                       int num_tokens, float k_scale, float v_scale, void *stream) {
+  if (!valid_dtype(dtype)) return LAZYATTN_ERR_DTYPE;
+  if (num_tokens < 0 || num_blocks < 1 || num_blocks > LAZYATTN_MAX_BLOCKS || num_kv_heads < 1 ||
+      num_kv_heads > 1024)
+    return LAZYATTN_ERR_SHAPE;
+  if (!(head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256))
+    return LAZYATTN_ERR_SHAPE;
+  if (!valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)) return LAZYATTN_ERR_SHAPE;
+  if (num_tokens == 0) return LAZYATTN_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return LAZYATTN_ERR_NULL;
+  return from_hip(launch_append_fp8(k_pool, v_pool, dtype == LAZYATTN_BF16, num_blocks, num_kv_heads,
+                                    head_dim, k_new, v_new, slot_mapping, num_tokens, k_scale, v_scale,
+                                    (hipStream_t)stream));
+}
+
 size_t lazyattn_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                       int max_blocks_per_seq, int split_blocks) {
   if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || head_dim <= 0 ||
@@ -64,7 +82,8 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
                          const uint8_t *block_fill, const int32_t *seq_lens, int batch, int num_q_heads, int num_kv_heads,
                          int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
                          int split_blocks, void *workspace, size_t workspace_bytes, void *stream,
-                         int mode, const float *slopes) {
+                         int mode, const float *slopes, bool pool8 = false, float k_scale = 1.f,
+                         float v_scale = 1.f) {
   if (!valid_dtype(dtype)) return LAZYATTN_ERR_DTYPE;
   if (batch < 0 || batch > 65535 || num_kv_heads < 1 || num_kv_heads > 65535 || num_q_heads < 1 ||
       num_q_heads % num_kv_heads || !pow2_group(num_q_heads / num_kv_heads))
@@ -78,6 +97,8 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
     return LAZYATTN_ERR_SHAPE;
   if (split_blocks != 0 && (split_blocks < 4 || split_blocks > 1024)) return LAZYATTN_ERR_SHAPE;
   if (!(rope_theta > 1.0f) || !isfinite(rope_theta) || !isfinite(scale)) return LAZYATTN_ERR_SHAPE;
+  if (pool8 && (head_dim != 128 || !valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
+    return LAZYATTN_ERR_SHAPE;
   if (batch == 0) return LAZYATTN_OK;
   if (!out || !q || !q_pos || !k_pool || !v_pool || !block_table || !seq_lens)
     return LAZYATTN_ERR_NULL;
@@ -107,7 +128,22 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
   a.mode = mode;
   a.slopes = slopes;
   a.block_fill = block_fill;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  if (pool8) return from_hip(launch_decode_fp8(a, (hipStream_t)stream));
   return from_hip(launch_decode(a, bf16, (hipStream_t)stream));
+}
+
+int lazyattn_decode_fp8(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                        const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                        const uint8_t *block_fill, const int32_t *seq_lens, int batch, int num_q_heads,
+                        int num_kv_heads, int head_dim, int num_blocks, float scale, float rope_theta,
+                        float k_scale, float v_scale, int split_blocks, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+  return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, block_fill, seq_lens,
+                       batch, num_q_heads, num_kv_heads, head_dim, num_blocks, LAZYATTN_BF16, scale,
+                       rope_theta, split_blocks, workspace, workspace_bytes, stream, kRopeLazy, nullptr,
+                       true, k_scale, v_scale);
 }
 
 int lazyattn_decode(void *out, const void *q, const int32_t *q_pos, const void *k_pool,

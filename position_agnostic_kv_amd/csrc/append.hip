@@ -41,4 +41,94 @@ hipError_t launch_append(void *k_pool, void *v_pool, int elem_bytes, int num_blo
   return hipGetLastError();
 }
 
+// ---- 8-bit pools: quantise on the way in -------------------------------------
+// A pool of OCP E4M3 codes with one scale per tensor: the stored code is the
+// float32 quotient x / scale rounded to the nearest E4M3 value (ties to an even
+// mantissa), magnitudes above 448 saturating, NaN stored as 0x7F.  The rounding
+// works on the quotient's bits: a normal E4M3 value keeps the float's top three
+// mantissa bits with the exponent rebiased from 127 to 7; below 2^-6 the codes
+// are the multiples of 2^-9.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t mag = u & 0x7fffffffu;
+  if (mag > 0x7f800000u) return 0x7fu;           // NaN
+  if (mag > 0x43e00000u) return sign | 0x7eu;    // beyond 448, infinity included
+  uint32_t code;
+  if (mag >= 0x3c800000u) {                      // >= 2^-6
+    // round away the low 20 mantissa bits, ties to even; a carry moves the
+    // exponent up, which is the next E4M3 binade's first code
+    const uint32_t r = (mag + 0x7ffffu + ((mag >> 20) & 1u)) >> 20;
+    code = r - (120u << 3);                      // exponent bias 127 -> 7
+  } else {
+    code = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);  // 0..8, ties to even
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ void load8(const uint16_t *p, float (&x)[8]) {
+  const uint4 c = *(const uint4 *)p;
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
+  const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ uint2 quant8(const float (&x)[8], float scale) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i >> 2] |= f32_to_e4m3(__fdiv_rn(x[i], scale)) << (8 * (i & 3));
+  return make_uint2(w[0], w[1]);
+}
+
+// One thread quantises 8 elements of K and the same 8 of V (8 bytes out each).
+template <typename TI>
+__global__ void __launch_bounds__(256)
+append_fp8_kernel(uint2 *__restrict__ k_pool, uint2 *__restrict__ v_pool, const TI *__restrict__ k_new,
+                  const TI *__restrict__ v_new, const int32_t *__restrict__ slot_mapping, int num_tokens,
+                  int num_kv_heads, int groups_per_row, long long num_slots, float k_scale, float v_scale) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)num_tokens * num_kv_heads * groups_per_row;
+  if (idx >= total) return;
+  const int grp = (int)(idx % groups_per_row);
+  const long long row = idx / groups_per_row;      // token * heads + head
+  const int head = (int)(row % num_kv_heads);
+  const int tok = (int)(row / num_kv_heads);
+  const long long slot = slot_mapping[tok];
+  if (slot < 0 || slot >= num_slots) return;        // padding / out of the pool
+  const long long blk = slot / kBlockTokens;
+  const long long in_blk = slot % kBlockTokens;
+  const long long dst = ((blk * num_kv_heads + head) * kBlockTokens + in_blk) * groups_per_row + grp;
+  float x[8];
+  load8(k_new + idx * 8, x);
+  k_pool[dst] = quant8(x, k_scale);
+  load8(v_new + idx * 8, x);
+  v_pool[dst] = quant8(x, v_scale);
+}
+
+hipError_t launch_append_fp8(void *k_pool, void *v_pool, bool bf16_rows, int num_blocks,
+                             int num_kv_heads, int head_dim, const void *k_new, const void *v_new,
+                             const int32_t *slot_mapping, int num_tokens, float k_scale, float v_scale,
+                             hipStream_t stream) {
+  const int gpr = head_dim / 8;
+  const long long total = (long long)num_tokens * num_kv_heads * gpr;
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  const long long slots = (long long)num_blocks * kBlockTokens;
+  if (bf16_rows)
+    hipLaunchKernelGGL(append_fp8_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, (uint2 *)k_pool,
+                       (uint2 *)v_pool, (const uint16_t *)k_new, (const uint16_t *)v_new, slot_mapping,
+                       num_tokens, num_kv_heads, gpr, slots, k_scale, v_scale);
+  else
+    hipLaunchKernelGGL(append_fp8_kernel<float>, dim3(grid), dim3(256), 0, stream, (uint2 *)k_pool,
+                       (uint2 *)v_pool, (const float *)k_new, (const float *)v_new, slot_mapping,
+                       num_tokens, num_kv_heads, gpr, slots, k_scale, v_scale);
+  return hipGetLastError();
+}
+
 }  // namespace lazyattn

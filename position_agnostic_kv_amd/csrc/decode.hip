@@ -30,6 +30,12 @@
 //     bounded by 256), which skips almost every rescale of the accumulators.
 //   * The next block's K/V loads are issued before the current block is
 //     computed.
+//   * 8-bit pools (F8): K and V are OCP E4M3 codes with one scale per tensor
+//     (the pages' one-byte KV cache).  A 16-byte chunk then holds 16 dims, so
+//     8 lanes cover a row and a load instruction reads 8 rows; the codes are
+//     widened to bf16 pairs with v_cvt_scalef32_pk_bf16_fp8 (exact: every E4M3
+//     value is a bf16 value) and the products are the bf16 ones.  The K scale
+//     is folded into the rotated query, the V scale into the output.
 //   * A sequence split over several workgroups writes per-split (max, sum,
 //     unnormalised output) to the workspace and a second, small kernel merges
 //     them (log-sum-exp).  The kernel boundary orders the two; no device-scope
@@ -86,7 +92,14 @@ struct DecodeKernelArgs {
   int num_units;     // splits x KV heads x batch
   int num_blocks, split_blocks, max_splits;
   float scale_log2, rope_theta;
+  float out_scale;   // V scale of an 8-bit pool (1 otherwise)
 };
+
+// Two E4M3 codes (bytes 0-1, or 2-3 with HI) of a word -> a packed bf16 pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
 
 // MODE kRopeEager: the non-lazy baseline the method is measured against.  The
 // pool then holds keys already rotated to their absolute positions (the eager,
@@ -94,14 +107,16 @@ struct DecodeKernelArgs {
 // once by its own position.
 // MODE kAlibi: no rotation at all; the score of a key at position p (block
 // offset + slot) takes the bias slope_h * (p - n) of query head h.
-template <typename T, int D, int G, int MODE>
+// F8: the pools hold E4M3 codes (T, the q/out type, is then bf16).
+template <typename T, int D, int G, int MODE, bool F8 = false>
 __global__ void __launch_bounds__(kDecodeWaves * kWave)
 decode_split_kernel(const DecodeKernelArgs a) {
   using E = Elem<T>;
   constexpr bool kBf16 = sizeof(T) == 2;
   constexpr bool EAGER = MODE == kRopeEager;
   constexpr bool ALIBI = MODE == kAlibi;
-  constexpr int EPL = E::kPerChunk;        // elements per 16-byte chunk
+  static_assert(!F8 || kBf16, "8-bit pools take bf16 queries");
+  constexpr int EPL = F8 ? 16 : E::kPerChunk;  // pool elements per 16-byte chunk
   constexpr int LPT = D / EPL;             // lanes per token row
   constexpr int TPI = kWave / LPT;         // token rows per load instruction
   constexpr int NI = kBlockTokens / TPI;   // load instructions per block
@@ -294,7 +309,15 @@ decode_split_kernel(const DecodeKernelArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float t;
-        if constexpr (kBf16) {
+        if constexpr (F8) {  // word j = dims 4j..4j+3: pairs 2j (bytes 0-1) and 2j+1 (bytes 2-3)
+          t = dot2_bf16(qp[h][0], e4m3x2_to_bf16x2<false>(dw4(kc[i], 0)), 0.f);
+          t = dot2_bf16(qp[h][1], e4m3x2_to_bf16x2<true>(dw4(kc[i], 0)), t);
+#pragma unroll
+          for (int j = 1; j < EPL / 4; ++j) {
+            t = dot2_bf16(qp[h][2 * j], e4m3x2_to_bf16x2<false>(dw4(kc[i], j)), t);
+            t = dot2_bf16(qp[h][2 * j + 1], e4m3x2_to_bf16x2<true>(dw4(kc[i], j)), t);
+          }
+        } else if constexpr (kBf16) {
           t = dot2_bf16(qp[h][0], dw4(kc[i], 0), 0.f);
 #pragma unroll
           for (int w = 1; w < EPL / 2; ++w) t = dot2_bf16(qp[h][w], dw4(kc[i], w), t);
@@ -372,15 +395,32 @@ decode_split_kernel(const DecodeKernelArgs a) {
           pp[h] = pack_bf16x2(p[i][h], p[i + 1][h]);
           l[h] = dot2_bf16(pp[h], 0x3f803f80u, l[h]);
         }
+        if constexpr (F8) {
+          // word j holds dims 4j..4j+3 of a row; interleave the two rows'
+          // bytes, then widen: (row i, row i+1) pairs of one dim each
 #pragma unroll
-        for (int w = 0; w < EPL / 2; ++w) {
-          const uint32_t v0 = dw4(vc[i], w), v1 = dw4(vc[i + 1], w);
-          const uint32_t lo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);  // dim 2w of rows i, i+1
-          const uint32_t hi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);  // dim 2w+1
+          for (int j = 0; j < EPL / 4; ++j) {
+            const uint32_t v0 = dw4(vc[i], j), v1 = dw4(vc[i + 1], j);
+            const uint32_t x01 = __builtin_amdgcn_perm(v1, v0, 0x05010400u);  // dims 4j, 4j+1
+            const uint32_t x23 = __builtin_amdgcn_perm(v1, v0, 0x07030602u);  // dims 4j+2, 4j+3
+            const uint32_t pr[4] = {e4m3x2_to_bf16x2<false>(x01), e4m3x2_to_bf16x2<true>(x01),
+                                    e4m3x2_to_bf16x2<false>(x23), e4m3x2_to_bf16x2<true>(x23)};
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            acc[h][2 * w] = dot2_bf16(pp[h], lo, acc[h][2 * w]);
-            acc[h][2 * w + 1] = dot2_bf16(pp[h], hi, acc[h][2 * w + 1]);
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+              for (int k = 0; k < 4; ++k) acc[h][4 * j + k] = dot2_bf16(pp[h], pr[k], acc[h][4 * j + k]);
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < EPL / 2; ++w) {
+            const uint32_t v0 = dw4(vc[i], w), v1 = dw4(vc[i + 1], w);
+            const uint32_t lo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);  // dim 2w of rows i, i+1
+            const uint32_t hi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);  // dim 2w+1
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              acc[h][2 * w] = dot2_bf16(pp[h], lo, acc[h][2 * w]);
+              acc[h][2 * w + 1] = dot2_bf16(pp[h], hi, acc[h][2 * w + 1]);
+            }
           }
         }
       }
@@ -457,7 +497,7 @@ decode_split_kernel(const DecodeKernelArgs a) {
       lsum = __builtin_nanf("");
     }
     if (single) {
-      E::store(out, i, lsum != 0.f ? o / lsum : 0.f);  // no visible token -> 0 (NaN stays NaN)
+      E::store(out, i, lsum != 0.f ? o / lsum * a.out_scale : 0.f);  // no visible token -> 0 (NaN stays NaN)
     } else {
       a.ws_o[part * G * D + i] = o;
       if (d == 0) a.ws_ml[part * G + h] = make_float2(mx, lsum);
@@ -493,7 +533,7 @@ decode_combine_kernel(const DecodeKernelArgs a) {
       o = fmaf(po[(size_t)sp * G * D + i], f, o);
       lsum = fmaf(ml.y, f, lsum);
     }
-    E::store(out, i, lsum != 0.f ? o / lsum : 0.f);
+    E::store(out, i, lsum != 0.f ? o / lsum * a.out_scale : 0.f);
   }
 }
 
@@ -541,7 +581,7 @@ size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int h
   return t;
 }
 
-template <typename T, int D, int G, int MODE>
+template <typename T, int D, int G, int MODE, bool F8 = false>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   DecodeKernelArgs k;
   k.out = a.out;
@@ -561,7 +601,8 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   k.num_blocks = a.num_blocks;
   k.split_blocks = a.split_blocks;
   k.max_splits = (a.max_blocks + a.split_blocks - 1) / a.split_blocks;
-  k.scale_log2 = a.scale * kLog2e;
+  k.scale_log2 = a.scale * kLog2e * (F8 ? a.k_scale : 1.f);
+  k.out_scale = F8 ? a.v_scale : 1.f;
   k.rope_theta = a.rope_theta;
   const long long units = (long long)k.max_splits * a.num_kv_heads * a.batch;
   const long long grid = (units + kXcds - 1) / kXcds * kXcds * hsplit;
@@ -573,7 +614,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   char *ws = (char *)a.workspace;
   k.ws_ml = ws ? (float2 *)ws : nullptr;
   k.ws_o = ws ? (float *)(ws + off_o) : nullptr;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, G, MODE>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave),
+  hipLaunchKernelGGL((decode_split_kernel<T, D, G, MODE, F8>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave),
                      0, stream, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k.max_splits <= 1) return e;
@@ -599,6 +640,17 @@ static hipError_t dispatch_group(const DecodeArgs &a, hipStream_t s) {
     case kRopeLazy: return dispatch_group_e<T, D, kRopeLazy>(a, s);
     case kRopeEager: return dispatch_group_e<T, D, kRopeEager>(a, s);
     case kAlibi: return dispatch_group_e<T, D, kAlibi>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// bf16 queries against an 8-bit (E4M3) pool, lazy RoPE, head_dim 128.
+hipError_t launch_decode_fp8(const DecodeArgs &a, hipStream_t s) {
+  if (a.head_dim != 128 || a.mode != kRopeLazy) return hipErrorInvalidValue;
+  switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads)) {
+    case 1: return launch_decode_t<bf16, 128, 1, kRopeLazy, true>(a, s);
+    case 2: return launch_decode_t<bf16, 128, 2, kRopeLazy, true>(a, s);
+    case 4: return launch_decode_t<bf16, 128, 4, kRopeLazy, true>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -17,6 +17,10 @@ enum PosMode : int {
 hipError_t launch_append(void *k_pool, void *v_pool, int elem_bytes, int num_blocks,
                          int num_kv_heads, int head_dim, const void *k_new, const void *v_new,
                          const int32_t *slot_mapping, int num_tokens, hipStream_t stream);
+hipError_t launch_append_fp8(void *k_pool, void *v_pool, bool bf16_rows, int num_blocks,
+                             int num_kv_heads, int head_dim, const void *k_new, const void *v_new,
+                             const int32_t *slot_mapping, int num_tokens, float k_scale, float v_scale,
+                             hipStream_t stream);
 
 // Workgroups that share one KV head's query heads in a decode launch.
 int decode_head_split(int num_q_heads, int num_kv_heads);
@@ -41,8 +45,10 @@ struct DecodeArgs {
   const float *slopes;  // ALiBi slopes [num_q_heads] (device), else unused
   const uint8_t *block_fill;  // per-block fill counts, or nullptr (all full)
   int mode;             // PosMode
+  float k_scale = 1.f, v_scale = 1.f;  // 8-bit pools: value = code * scale
 };
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeArgs &a, hipStream_t stream);
 
 struct PrefillArgs {
   void *out;

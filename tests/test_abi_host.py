@@ -138,3 +138,40 @@ def test_prefill_and_append_argument_errors(lib):
     assert a(P, P, 1, 16, 8, 100, P, P, P, 4, NULL) == -3
     assert a(P, P, 1, 16, 8, 128, P, P, NULL, 4, NULL) == -1
     assert a(NULL, NULL, 1, 16, 8, 128, NULL, NULL, NULL, 0, NULL) == 0
+
+
+def test_fp8_entry_points_check_arguments(lib):
+    a = lib.kvcache_append_fp8
+    ok = [P, P, 1, 16, 8, 128, P, P, P, 4, 0.5, 0.5, NULL]
+
+    def with_(args, **kw):
+        idx = {"dtype": 2, "d": 5, "k_new": 6, "tokens": 9, "ks": 10, "vs": 11}
+        out = list(args)
+        for k, v in kw.items():
+            out[idx[k]] = v
+        return out
+    assert a(*with_(ok, dtype=7)) == -2
+    assert a(*with_(ok, d=100)) == -3
+    assert a(*with_(ok, ks=0.0)) == -3
+    assert a(*with_(ok, vs=float("nan"))) == -3
+    assert a(*with_(ok, vs=float("inf"))) == -3
+    assert a(*with_(ok, k_new=NULL)) == -1
+    assert a(*with_(ok, tokens=0, k_new=NULL)) == 0
+    d = lib.lazyattn_decode_fp8
+    ok_d = [P, P, P, P, P, P, 4, NULL, P, 2, 8, 2, 128, 16, 0.088, 1e4, 0.5, 0.5, 0, P, 1 << 30, NULL]
+
+    def dwith(**kw):
+        idx = {"q": 1, "max_blocks": 6, "batch": 9, "hq": 10, "hkv": 11, "d": 12, "ks": 16, "vs": 17,
+               "split": 18, "ws": 19}
+        out = list(ok_d)
+        for k, v in kw.items():
+            out[idx[k]] = v
+        return d(*out)
+    assert dwith(d=64) == -3                        # 8-bit pools: head_dim 128 only
+    assert dwith(ks=-1.0) == -3
+    assert dwith(vs=0.0) == -3
+    assert dwith(hq=6, hkv=4) == -3
+    assert dwith(split=2) == -3
+    assert dwith(q=NULL) == -1
+    assert dwith(batch=0, q=NULL) == 0
+    assert dwith(ws=NULL, max_blocks=4000) == -4

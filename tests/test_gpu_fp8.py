@@ -1,0 +1,134 @@
+"""GPU parity of the 8-bit KV pool (kvcache_append_fp8, lazyattn_decode_fp8)
+against the E4M3 oracle.  Pools hold random E4M3 byte patterns (every
+exponent from subnormal to 2^2, both signs); the step's new rows are bf16 or
+f32 values that the append quantises, bit for bit as the oracle does,
+including saturation, subnormals, signed zero, infinities and NaN.  Decode
+covers GQA 4, GQA 8 (two workgroups per KV head), a 32-query-head group,
+split-K, random offsets and documents of any length (fill counts)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import position_agnostic_kv_amd as pak
+import workloads as W
+from tests.gpu_helpers import DEV, DeviceCase, assert_parity, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+@pytest.mark.parametrize("rows_dtype", [W.BF16, W.F32])
+@pytest.mark.parametrize("ks,vs", [(1.0, 1.0), (0.05, 0.37), (3.0, 1.0e-3)])
+def test_append_fp8_bit_exact(rows_dtype, ks, vs):
+    rng = np.random.default_rng(11)
+    nb, hkv, d, t = 8, 4, 128, 70
+    x = rng.standard_normal((2, t, hkv, d)).astype(np.float32) * np.float32(4.0)
+    flat = x.reshape(-1)
+    pick = rng.permutation(flat.size)
+    flat[pick[:40]] = 1e5                              # saturates
+    flat[pick[40:80]] = -3e4
+    flat[pick[80:120]] = rng.standard_normal(40) * 1e-4  # subnormal codes and zeros
+    flat[pick[120:130]] = -0.0
+    flat[pick[130:135]] = np.inf
+    flat[pick[135:140]] = np.nan
+    if rows_dtype == W.BF16:
+        bits = W.f32_to_bf16_bits(x)
+        x = W.bf16_bits_to_f32(bits)
+        kd = torch.from_numpy(bits[0].view(np.int16)).to(DEV).view(torch.bfloat16)
+        vd = torch.from_numpy(bits[1].view(np.int16)).to(DEV).view(torch.bfloat16)
+    else:
+        kd, vd = torch.from_numpy(x[0]).to(DEV), torch.from_numpy(x[1]).to(DEV)
+    slots = rng.permutation(nb * 16)[:t].astype(np.int32)
+    slots[:5] = -1                                     # padding rows
+    slots[5] = nb * 16 + 3                             # past the pool: skipped
+    say(f"[fp8 append] rows {rows_dtype} k_scale {ks} v_scale {vs}")
+    kp = torch.full((nb, hkv, 16, d), 0x5A, dtype=torch.uint8, device=DEV)
+    vp = torch.full_like(kp, 0x5A)
+    pak.kvcache_append_fp8(kp, vp, kd, vd, _u8(slots), ks, vs)
+    torch.cuda.synchronize()
+    init = np.full((nb, hkv, 16, d), 0x5A, dtype=np.uint8)
+    wk, wv = oracle.append_fp8(init, init, x[0], x[1], slots, np.float32(ks), np.float32(vs))
+    gk, gv = kp.cpu().numpy(), vp.cpu().numpy()
+    bad = int((gk != wk).sum() + (gv != wv).sum())
+    say(f"  mismatching bytes: {bad}")
+    assert bad == 0
+
+
+def _fp8_case(case, seed):
+    rng = np.random.default_rng(seed)
+    shape = (case.layout.num_blocks, case.num_kv_heads, 16, case.head_dim)
+    return W.e4m3_codes(rng, shape), W.e4m3_codes(rng, shape)
+
+
+def _run(case, seed, ks, vs, split=0):
+    W.materialize_numpy(case)
+    kc, vc = _fp8_case(case, seed)
+    dc = DeviceCase(case)
+    k8, v8 = _u8(kc), _u8(vc)
+    if dc.k_new.shape[0]:
+        pak.kvcache_append_fp8(k8, v8, dc.k_new, dc.v_new, dc.slots, ks, vs)
+    out = pak.lazyattn_decode_fp8(dc.q, dc.q_pos, k8, v8, dc.table, dc.seq_lens, ks, vs, scale=case.scale,
+                                  rope_theta=case.rope_theta, split_blocks=split, block_fill=dc.fill)
+    torch.cuda.synchronize()
+    kn, vn = W.to_float(case.k_new, case.dtype), W.to_float(case.v_new, case.dtype)
+    kc2, vc2 = oracle.append_fp8(kc, vc, kn, vn, case.layout.slot_mapping, np.float32(ks), np.float32(vs))
+    assert np.array_equal(k8.cpu().numpy(), kc2) and np.array_equal(v8.cpu().numpy(), vc2), "append bytes"
+    want = oracle.decode_fp8(W.to_float(case.q, case.dtype), case.q_pos, kc2, vc2, case.layout.table,
+                             case.seq_lens, case.scale, case.rope_theta, np.float32(ks), np.float32(vs),
+                             block_fill=case.block_fill)
+    return W.to_float(out, case.dtype), want
+
+
+DECODE = [
+    # Hq, Hkv, ctx, doc blocks, offsets, split, k_scale, v_scale
+    (32, 8, [512, 1024, 96], (2, 10), "contiguous", 0, 0.25, 0.125),
+    (64, 8, [2048, 64], (4, 16), "contiguous", 8, 0.25, 0.5),
+    (32, 1, [400, 96], (2, 9), "contiguous", 0, 0.2, 0.1),
+    (16, 8, [320, 16, 784], (1, 6), "random", 4, 0.3, 0.07),
+    (8, 8, [1056, 48], (3, 40), "contiguous", 5, 0.25, 1.0),
+]
+
+
+@pytest.mark.parametrize("hq,hkv,ctx,docs,offs,split,ks,vs", DECODE)
+def test_decode_fp8(hq, hkv, ctx, docs, offs, split, ks, vs):
+    case = W.decode_case(201 + hq + hkv, len(ctx), hq, hkv, 128, ctx, docs, offsets=offs)
+    say(f"[fp8 decode] Hq{hq} Hkv{hkv} ctx={ctx} {offs} split={split} k_scale {ks} v_scale {vs}")
+    got, want = _run(case, 7 + hq, ks, vs, split)
+    assert_parity(got, want, W.BF16, f"fp8 decode G{hq // hkv}")
+
+
+def test_decode_fp8_ragged_documents():
+    case = W.ragged_case(221, "decode", 4, 32, 8, 128, (2, 6), (1, 700))
+    say("[fp8 decode] ragged documents, fill counts")
+    got, want = _run(case, 9, 0.25, 0.125, 4)
+    assert_parity(got, want, W.BF16, "fp8 decode ragged")
+
+
+def test_single_token_reads_every_code_exactly():
+    """A sequence of one token gives out = v_scale * decode(v code) exactly (the
+    softmax of one key is 1); v_scale a power of two keeps the product exact,
+    so all 256 codes (NaN patterns included) must come out bit for bit."""
+    hkv, hq, d = 2, 8, 128
+    nb = 4
+    vc = np.zeros((nb, hkv, 16, d), dtype=np.uint8)
+    vc[1, 0, 0] = np.arange(128, dtype=np.uint8)
+    vc[1, 1, 0] = np.arange(128, 256, dtype=np.uint8)
+    rng = np.random.default_rng(2)
+    kc = W.e4m3_codes(rng, (nb, hkv, 16, d))
+    q = torch.from_numpy(W.f32_to_bf16_bits(rng.standard_normal((1, hq, d)).astype(np.float32)).view(np.int16))
+    q = q.to(DEV).view(torch.bfloat16)
+    table = _u8(np.array([[1 | (7 << 16)]], dtype=np.uint32).view(np.int32))
+    out = pak.lazyattn_decode_fp8(q, _u8(np.array([7], np.int32)), _u8(kc), _u8(vc), table,
+                                  _u8(np.array([1], np.int32)), 0.25, 0.5)
+    torch.cuda.synchronize()
+    got = W.to_float(out, W.BF16)[0]                       # [Hq, D]
+    ref = oracle.e4m3_decode(np.arange(256, dtype=np.uint8)) * 0.5
+    for h in range(hq):
+        want = ref[:128] if h < hq // hkv else ref[128:]
+        same = (got[h] == want) | (np.isnan(got[h]) & np.isnan(want))
+        assert same.all(), f"head {h}: {np.flatnonzero(~same)[:8]}"

@@ -57,6 +57,31 @@ def pack_words(block_ids, offsets):
     return (ids | (offs << 16)).astype(np.uint32)
 
 
+def e4m3_codes(rng, shape, exp_lo=3, exp_hi=9, subnormal_frac=0.05):
+    """Random contents of an 8-bit (E4M3) pool: byte patterns with a uniform
+    sign, exponent field U{exp_lo..exp_hi} (magnitudes 2^-4 .. 7.5), mantissa
+    U{0..7}, and a fraction of subnormal patterns (exponent field 0).  Never
+    the NaN pattern.  Input data only: no value is quantised here."""
+    n = int(np.prod(shape))
+    sign = rng.integers(0, 2, size=n, dtype=np.uint8) << np.uint8(7)
+    exp = rng.integers(exp_lo, exp_hi + 1, size=n).astype(np.uint8)
+    exp[rng.random(n) < subnormal_frac] = 0
+    man = rng.integers(0, 8, size=n, dtype=np.uint8)
+    return (sign | (exp << np.uint8(3)) | man).reshape(shape)
+
+
+def e4m3_codes_torch(shape, device, seed, exp_lo=3, exp_hi=9):
+    """e4m3_codes drawn on the GPU with torch's seeded generator (full-size
+    pools), without subnormal patterns."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    sign = torch.randint(0, 2, shape, dtype=torch.uint8, device=device, generator=gen) << 7
+    exp = torch.randint(exp_lo, exp_hi + 1, shape, dtype=torch.uint8, device=device, generator=gen)
+    man = torch.randint(0, 8, shape, dtype=torch.uint8, device=device, generator=gen)
+    return sign | (exp << 3) | man
+
+
 # ------------------------------------------------------------------- layouts
 @dataclass
 class Layout:
@@ -603,6 +628,6 @@ __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "to_float", "materialize_numpy",
     "materialize_torch", "add_score_shift", "decode_case", "prefill_case", "tiny_decode",
     "llama8b_decode", "llama8b_prefill", "llama70b_decode", "zipf_decode", "ragged_case",
-    "llama8b_decode_ragged", "llama8b_prefill_ragged", "make",
+    "llama8b_decode_ragged", "llama8b_prefill_ragged", "e4m3_codes", "e4m3_codes_torch", "make",
     "WORKLOADS",
 ]
