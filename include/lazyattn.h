@@ -229,15 +229,21 @@ int lazyattn_prefill_alibi(void *out, const void *q, int total_q, const int32_t 
  * element).  Here a pool element is an OCP FP8 E4M3 code (1 sign, 4 exponent
  * bits with bias 7, 3 mantissa bits, subnormals, no infinities, S.1111.111 =
  * NaN, largest magnitude 448) with one float scale per tensor: the value a
- * code stands for is decode(code) * scale.  Layout as above with one byte per
- * element: [num_blocks][num_kv_heads][16][head_dim] uint8.
+ * code stands for is decode(code) * scale.  head_dim is 128.  Each
+ * (block, KV head) record is 2048 bytes at [num_blocks][num_kv_heads] as in the
+ * bf16 pool, with its codes in the lane order of the matrix-core decode: for
+ * half i < 2, lane l = 16 g + t < 64 and x < 16, byte 1024 i + 16 l + x holds
+ *   K: token t, dim 32 g + 16 i + x
+ *   V: token 4 g + x % 4, dim 16 (4 i + x / 4) + t
+ * so that every wave load reads 1 KiB contiguously and feeds the matrix cores
+ * without exchanging data between lanes.  kvcache_append_fp8 writes this order.
  *
  * kvcache_append_fp8 -- kvcache_append into 8-bit pools.  k_new/v_new are
  * `dtype` rows (LAZYATTN_F32 or LAZYATTN_BF16).  Each element is stored as the
  * E4M3 code nearest to the float32 quotient x / scale (correctly rounded
  * division), ties to an even mantissa, magnitudes above 448 saturating to
- * +-448, NaN as 0x7F.  k_scale, v_scale must be finite and > 0
- * (LAZYATTN_ERR_SHAPE otherwise).  Other arguments as kvcache_append.
+ * +-448, NaN as 0x7F.  k_scale, v_scale must be finite and > 0, head_dim
+ * 128 (LAZYATTN_ERR_SHAPE otherwise).  Other arguments as kvcache_append.
  */
 int kvcache_append_fp8(void *k_pool, void *v_pool, int dtype, int num_blocks, int num_kv_heads,
                        int head_dim, const void *k_new, const void *v_new, const int32_t *slot_mapping,
@@ -246,7 +252,8 @@ int kvcache_append_fp8(void *k_pool, void *v_pool, int dtype, int num_blocks, in
 /*
  * lazyattn_decode_fp8 -- lazyattn_decode (lazy RoPE) against 8-bit pools:
  * keys are decode(code) * k_scale, values decode(code) * v_scale.  q and out
- * are bf16; head_dim must be 128.  Reads one byte per K/V element, half of the
+ * are bf16; head_dim must be 128; any power-of-two group up to 64 (up to 16
+ * query heads per workgroup).  Reads one byte per K/V element, half of the
  * bf16 pool's traffic.  The workspace is sized by
  * lazyattn_decode_workspace_size with the same arguments.  Other arguments
  * and errors as lazyattn_decode.

@@ -58,8 +58,7 @@ int kvcache_append_fp8(void *k_pool, void *v_pool, int dtype, int num_blocks, in
   if (num_tokens < 0 || num_blocks < 1 || num_blocks > LAZYATTN_MAX_BLOCKS || num_kv_heads < 1 ||
       num_kv_heads > 1024)
     return LAZYATTN_ERR_SHAPE;
-  if (!(head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256))
-    return LAZYATTN_ERR_SHAPE;
+  if (head_dim != 128) return LAZYATTN_ERR_SHAPE;  // the 8-bit pool layout is defined for 128 dims
   if (!valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)) return LAZYATTN_ERR_SHAPE;
   if (num_tokens == 0) return LAZYATTN_OK;
   if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return LAZYATTN_ERR_NULL;
@@ -122,7 +121,7 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
   a.head_dim = head_dim;
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
-  a.split_blocks = decode_split_blocks(batch, num_q_heads, num_kv_heads, max_blocks_per_seq, split_blocks);
+  a.split_blocks = decode_split_blocks(batch, num_q_heads, num_kv_heads, max_blocks_per_seq, split_blocks, pool8);
   a.scale = scale;
   a.rope_theta = rope_theta;
   a.mode = mode;

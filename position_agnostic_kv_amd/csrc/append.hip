@@ -87,47 +87,60 @@ __device__ __forceinline__ uint2 quant8(const float (&x)[8], float scale) {
   return make_uint2(w[0], w[1]);
 }
 
-// One thread quantises 8 elements of K and the same 8 of V (8 bytes out each).
+// One thread quantises 8 consecutive dims of one K row and of one V row.  The
+// 8-bit pool keeps each (block, KV head) of 16 x 128 codes in the lane order of
+// the matrix-core decode: byte 1024 i + 16 l + x (half i, lane l = 16 g + t,
+// x < 16) holds K[token t][dim 32 g + 16 i + x] and
+// V[token 4 g + x % 4][dim 16 (4 i + x / 4) + t].  The K codes of 8 dims are 8
+// adjacent bytes; the V codes of 8 dims go to 8 lanes' bytes.
 template <typename TI>
 __global__ void __launch_bounds__(256)
-append_fp8_kernel(uint2 *__restrict__ k_pool, uint2 *__restrict__ v_pool, const TI *__restrict__ k_new,
+append_fp8_kernel(uint8_t *__restrict__ k_pool, uint8_t *__restrict__ v_pool, const TI *__restrict__ k_new,
                   const TI *__restrict__ v_new, const int32_t *__restrict__ slot_mapping, int num_tokens,
-                  int num_kv_heads, int groups_per_row, long long num_slots, float k_scale, float v_scale) {
+                  int num_kv_heads, long long num_slots, float k_scale, float v_scale) {
+  constexpr int kGroups = 16;  // 128 dims / 8
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)num_tokens * num_kv_heads * groups_per_row;
+  const long long total = (long long)num_tokens * num_kv_heads * kGroups;
   if (idx >= total) return;
-  const int grp = (int)(idx % groups_per_row);
-  const long long row = idx / groups_per_row;      // token * heads + head
+  const int grp = (int)(idx % kGroups);
+  const long long row = idx / kGroups;      // token * heads + head
   const int head = (int)(row % num_kv_heads);
   const int tok = (int)(row / num_kv_heads);
   const long long slot = slot_mapping[tok];
-  if (slot < 0 || slot >= num_slots) return;        // padding / out of the pool
+  if (slot < 0 || slot >= num_slots) return;  // padding / out of the pool
   const long long blk = slot / kBlockTokens;
-  const long long in_blk = slot % kBlockTokens;
-  const long long dst = ((blk * num_kv_heads + head) * kBlockTokens + in_blk) * groups_per_row + grp;
+  const int t = (int)(slot % kBlockTokens);
+  uint8_t *kb = k_pool + (blk * num_kv_heads + head) * 2048;
+  uint8_t *vb = v_pool + (blk * num_kv_heads + head) * 2048;
+  const int d0 = grp * 8;
   float x[8];
   load8(k_new + idx * 8, x);
-  k_pool[dst] = quant8(x, k_scale);
+  *(uint2 *)(kb + ((d0 >> 4) & 1) * 1024 + (16 * (d0 >> 5) + t) * 16 + (d0 & 15)) = quant8(x, k_scale);
   load8(v_new + idx * 8, x);
-  v_pool[dst] = quant8(x, v_scale);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int d = d0 + e, c = d >> 4;
+    vb[(c >> 2) * 1024 + (16 * (t >> 2) + (d & 15)) * 16 + (c & 3) * 4 + (t & 3)] =
+        (uint8_t)f32_to_e4m3(__fdiv_rn(x[e], v_scale));
+  }
 }
 
 hipError_t launch_append_fp8(void *k_pool, void *v_pool, bool bf16_rows, int num_blocks,
                              int num_kv_heads, int head_dim, const void *k_new, const void *v_new,
                              const int32_t *slot_mapping, int num_tokens, float k_scale, float v_scale,
                              hipStream_t stream) {
-  const int gpr = head_dim / 8;
-  const long long total = (long long)num_tokens * num_kv_heads * gpr;
+  if (head_dim != 128) return hipErrorInvalidValue;  // the lane-order layout is defined for 128 dims
+  const long long total = (long long)num_tokens * num_kv_heads * 16;
   const unsigned grid = (unsigned)((total + 255) / 256);
   const long long slots = (long long)num_blocks * kBlockTokens;
   if (bf16_rows)
-    hipLaunchKernelGGL(append_fp8_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, (uint2 *)k_pool,
-                       (uint2 *)v_pool, (const uint16_t *)k_new, (const uint16_t *)v_new, slot_mapping,
-                       num_tokens, num_kv_heads, gpr, slots, k_scale, v_scale);
+    hipLaunchKernelGGL(append_fp8_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, (uint8_t *)k_pool,
+                       (uint8_t *)v_pool, (const uint16_t *)k_new, (const uint16_t *)v_new, slot_mapping,
+                       num_tokens, num_kv_heads, slots, k_scale, v_scale);
   else
-    hipLaunchKernelGGL(append_fp8_kernel<float>, dim3(grid), dim3(256), 0, stream, (uint2 *)k_pool,
-                       (uint2 *)v_pool, (const float *)k_new, (const float *)v_new, slot_mapping,
-                       num_tokens, num_kv_heads, gpr, slots, k_scale, v_scale);
+    hipLaunchKernelGGL(append_fp8_kernel<float>, dim3(grid), dim3(256), 0, stream, (uint8_t *)k_pool,
+                       (uint8_t *)v_pool, (const float *)k_new, (const float *)v_new, slot_mapping,
+                       num_tokens, num_kv_heads, slots, k_scale, v_scale);
   return hipGetLastError();
 }
 

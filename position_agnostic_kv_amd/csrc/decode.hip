@@ -505,6 +505,272 @@ decode_split_kernel(const DecodeKernelArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 8-bit pools on the matrix cores.  With one byte per element the VALU form
+// above runs out of issue slots before HBM does (its dot products, row sums and
+// conversions cost ~240 VALU instructions per block and wave, and the block
+// arrives in half the time), so here the two contractions of a block go to
+// MFMA: S = K.q'^T as 4 x v_mfma_f32_16x16x32_bf16 (16 tokens x up to 16 query
+// heads, k = 32 dims each) and O += P.V as 8 x v_mfma_f32_16x16x16_bf16
+// (16 heads x 16 dims, k = 16 tokens each).  The VALU keeps the code widening
+// (exact), the exponentials and the running maximum.
+//
+// Lane l = 16 g + t (t = l % 16, g = l / 16):
+//   * QK: A = K rows: token t, dims 32 g + 8 c .. + 8 of chunk c; B = q' with
+//     the same dims for query head t (zero for t >= G).  Output S[token][head]:
+//     lane l holds tokens 4g .. 4g+3 of head t.
+//   * PV: A = P (rows = heads, k = tokens): exactly the lane's 4 weights of head
+//     t at tokens 4g .. 4g+3, so P never moves between lanes.  B = V: tokens
+//     4g .. 4g+3 of dim 16 c + t.  Output O[head 4g+j][dim 16 c + t].
+//   * The 8-bit pool stores each (block, KV head) in that lane order, so that
+//     every load instruction reads 1 KiB contiguously: byte
+//     1024 i + 16 l + x holds K[t][32 g + 16 i + x] and
+//     V[4 g + x % 4][16 (4 i + x / 4) + t].
+//   * The four lane groups of a head share one running maximum (two permlane
+//     swaps per block), since P.V sums their tokens in one accumulator.
+constexpr int kMma8WorkgroupsPerCu = 2;  // occupancy the register allocation is held to
+
+template <int G, int MODE>
+__global__ void __launch_bounds__(kDecodeWaves * kWave, kMma8WorkgroupsPerCu)
+decode_mma8_kernel(const DecodeKernelArgs a) {
+  using E = Elem<bf16>;
+  constexpr int D = 128;
+  constexpr int NT = kDecodeWaves * kWave;
+  static_assert(G >= 1 && G <= 16, "one workgroup takes up to 16 query heads");
+  static_assert(MODE == kRopeLazy, "8-bit pools: lazy RoPE");
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+  __shared__ float s_q[G][D];
+  __shared__ float s_m[kDecodeWaves][G];
+  __shared__ float s_l[kDecodeWaves][G];
+  __shared__ float s_o[kDecodeWaves][G][D];
+  __shared__ int s_bad;
+
+  const int hkv = a.num_kv_heads;
+  const int slot = blockIdx.x / kXcds;
+  const int hsub = slot & ((1 << a.kv_shift) - 1);
+  const int unit = (slot >> a.kv_shift) * kXcds + (int)(blockIdx.x % kXcds);
+  if (unit >= a.num_units) return;
+  const int hkv_pool = hkv >> a.kv_shift;
+  const int split = unit % a.max_splits;
+  const int gp = (unit / a.max_splits) % hkv_pool;
+  const int b = unit / a.max_splits / hkv_pool;
+  const int g = (gp << a.kv_shift) | hsub;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int hq = hkv * G;
+
+  const int seq_len = a.seq_lens[b];
+  const bool bad_len = seq_len < 0 || seq_len > a.max_blocks * kBlockTokens;
+  const int nblk = bad_len ? 0 : (seq_len + kBlockTokens - 1) / kBlockTokens;
+  const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
+  bf16 *out = (bf16 *)a.out + ((size_t)b * hq + (size_t)g * G) * D;
+  if (nsplit == 0) {
+    if (split == 0)
+      for (int i = tid; i < G * D; i += NT) E::store(out, i, bad_len ? __builtin_nanf("") : 0.f);
+    return;
+  }
+  if (split >= nsplit) return;
+
+  const bf16 *qg = (const bf16 *)a.q + ((size_t)b * hq + (size_t)g * G) * D;
+  for (int i = tid; i < G * D; i += NT) s_q[i / D][i % D] = E::load(qg, i);
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+
+  const int n_pos = a.q_pos[b];
+  const int t16 = lane & 15;  // token row of K, head column of S / P, dim of O
+  const int g4 = lane >> 4;   // lane group
+  const bool live = t16 < G;
+  const double inv_freq = rope_inv_freq(lane, D, a.rope_theta);  // lane i: frequency i (64 of them)
+
+  bf16x8_t qb[4];
+  f32x4_t O[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) qb[c] = bf16x8_t{};
+  float m = kMaxFloor, lsum = 0.f;
+
+  const int blk0 = split * a.split_blocks;
+  const int blk1 = min(nblk, blk0 + a.split_blocks);
+  const uint32_t *trow = a.table + (size_t)b * a.max_blocks;
+  bool bad = false;
+  int cur_off = -1;
+
+  // K and V of block bk (this lane's 32 bytes of each); w returns with the
+  // block id replaced by the block's fill count
+  auto issue = [&](int bk, uint32_t &w, uint4 (&kk)[2], uint4 (&vv)[2]) {
+    w = trow[bk];
+    uint32_t id = word_block(w);
+    if (id >= (uint32_t)a.num_blocks) {
+      bad = true;
+      id = 0;
+    }
+    const uint32_t fill = a.fill4 ? (a.fill4[id >> 2] >> ((id & 3u) * 8u)) & 0xffu : (uint32_t)kBlockTokens;
+    w = (w & 0xffff0000u) | fill;
+    const size_t hb = ((size_t)id * hkv_pool + gp) * 128;  // 2 KiB = 128 chunks per (block, KV head)
+    kk[0] = a.k_pool[hb + lane];
+    kk[1] = a.k_pool[hb + 64 + lane];
+    vv[0] = a.v_pool[hb + lane];
+    vv[1] = a.v_pool[hb + 64 + lane];
+  };
+
+  // q' = rot(q, n - off) * scale * log2(e) * k_scale for head t16, dims
+  // 32 g4 .. 32 g4 + 31 (frequency d % 64, the pair of dim d is d ^ 64)
+  auto rotate = [&](int delta) {
+    const double tt = (double)delta * (inv_freq * 0.15915494309189535);
+    const float f = (float)(tt - rint(tt));
+    const float cs = __builtin_amdgcn_cosf(f), sn = __builtin_amdgcn_sinf(f);
+    const int hh = live ? t16 : 0;
+    const int d0 = 32 * g4;
+    const bool upper = d0 >= 64;
+    float r[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int fi = (d0 + k) & 63;
+      const float c = __shfl(cs, fi), sv = __shfl(sn, fi);
+      const float x = s_q[hh][d0 + k], y = s_q[hh][(d0 + k) ^ 64];
+      const float v = (upper ? fmaf(x, c, y * sv) : fmaf(x, c, -(y * sv))) * a.scale_log2;
+      r[k] = live ? v : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w4[k] = pack_bf16x2(r[8 * c + 2 * k], r[8 * c + 2 * k + 1]);
+      qb[c] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+    }
+  };
+
+  // two register sets take turns as current and next block, as in the kernel
+  // above (no copies; loads past the split's end re-read its last block and
+  // are masked).  Loading further ahead was measured and gains nothing.
+  int blk = blk0 + wave;
+  const int blast = blk1 - 1;
+  uint32_t wA = 0, wB = 0;
+  uint4 kA[2], vA[2], kB[2], vB[2];
+  issue(min(blk, blast), wA, kA, vA);
+  auto step = [&](const uint32_t &wcur, uint4 (&kc)[2], uint4 (&vc)[2], uint32_t &wn, uint4 (&kn)[2],
+                  uint4 (&vn)[2]) {
+    const int off = word_offset(wcur);
+    if (off != cur_off && blk < blk1) {
+      rotate(n_pos - off);
+      cur_off = off;
+    }
+    issue(min(blk + kDecodeWaves, blast), wn, kn, vn);
+
+    // S[token 4 g4 + j][head t16], log2 units
+    f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t w0 = dw4(kc[c >> 1], 2 * (c & 1)), w1 = dw4(kc[c >> 1], 2 * (c & 1) + 1);
+      const uint4 ka = make_uint4(e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
+                                  e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1));
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qb[c], S, 0, 0, 0);
+    }
+    float sv[4] = {S[0], S[1], S[2], S[3]};
+    const int nvalid = blk < blk1 ? min(seq_len - blk * kBlockTokens, (int)(wcur & 0xffffu)) : 0;
+    if (nvalid < kBlockTokens) {  // partly filled or exhausted: mask tokens, zero their V bytes
+      const int nv = nvalid - 4 * g4;  // valid tokens among this lane's 4
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j >= nv) sv[j] = -INFINITY;
+      const uint32_t keep = nv >= 4 ? 0xffffffffu : nv <= 0 ? 0u : (0xffffffffu >> (8 * (4 - nv)));
+      vc[0] = make_uint4(vc[0].x & keep, vc[0].y & keep, vc[0].z & keep, vc[0].w & keep);
+      vc[1] = make_uint4(vc[1].x & keep, vc[1].y & keep, vc[1].z & keep, vc[1].w & keep);
+    }
+    // block maximum of head t16 over the four lane groups
+    float bm = max4_nn(sv[0], sv[1], sv[2], sv[3]);
+    {
+      const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+      bm = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+      const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+      bm = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+    }
+    if (wave_any(live && bm > m + kRescaleSlack)) {
+      const float mn = fmaxf(m, bm);
+      const float alpha = fast_exp2(m - mn);  // 0 on the first rescale
+      lsum *= alpha;
+      m = mn;
+      // O rows are heads 4 g4 + j: their factors live in lanes 4 g4 + j
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float aj = __shfl(alpha, 4 * g4 + j);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) O[c][j] *= aj;
+      }
+    }
+    const float p0 = fast_exp2(sv[0] - m), p1 = fast_exp2(sv[1] - m);
+    const float p2 = fast_exp2(sv[2] - m), p3 = fast_exp2(sv[3] - m);
+    const uint32_t pa0 = pack_bf16x2(p0, p1), pa1 = pack_bf16x2(p2, p3);
+    lsum = dot2_bf16(pa0, 0x3f803f80u, lsum);  // the bf16 weights P.V uses
+    lsum = dot2_bf16(pa1, 0x3f803f80u, lsum);
+    const s16x4_t pa = __builtin_bit_cast(s16x4_t, make_uint2(pa0, pa1));
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t vw = dw4(vc[c >> 2], c & 3);
+      const s16x4_t vb =
+          __builtin_bit_cast(s16x4_t, make_uint2(e4m3x2_to_bf16x2<false>(vw), e4m3x2_to_bf16x2<true>(vw)));
+      O[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[c], 0, 0, 0);
+    }
+    blk += kDecodeWaves;
+  };
+  while (blk < blk1) {
+    step(wA, kA, vA, wB, kB, vB);
+    step(wB, kB, vB, wA, kA, vA);
+  }
+
+  // this wave's (max, sum, output) per head; sums over the four lane groups
+  {
+    const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+    lsum = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
+    const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+    lsum = __uint_as_float(x16[0]) + __uint_as_float(x16[1]);
+  }
+  if (live && g4 == 0) {
+    s_m[wave][t16] = m;
+    s_l[wave][t16] = lsum;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = 4 * g4 + j;
+    if (h < G) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s_o[wave][h][16 * c + t16] = O[c][j];
+    }
+  }
+  if (bad) s_bad = 1;
+  __syncthreads();
+
+  const bool single = nsplit == 1;
+  const bool flagged = s_bad != 0;
+  const size_t part = ((size_t)b * hkv + g) * a.max_splits + split;
+  for (int i = tid; i < G * D; i += NT) {
+    const int h = i / D, d = i % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
+    float o = 0.f, ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float f = s_m[w][h] == -INFINITY ? 0.f : fast_exp2(s_m[w][h] - mx);
+      o = fmaf(s_o[w][h][d], f, o);
+      ls = fmaf(s_l[w][h], f, ls);
+    }
+    if (flagged) {
+      o = __builtin_nanf("");
+      ls = __builtin_nanf("");
+    }
+    if (single) {
+      E::store(out, i, ls != 0.f ? o / ls * a.out_scale : 0.f);
+    } else {
+      a.ws_o[part * G * D + i] = o;
+      if (d == 0) a.ws_ml[part * G + h] = make_float2(mx, ls);
+    }
+  }
+}
+
 // Merge the per-split partials of one (sequence, KV head): log-sum-exp weights.
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256)
@@ -545,19 +811,25 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // few loads in flight to cover HBM latency; two workgroups of 4 heads each
 // (sharing every K/V block through L2) run at two waves per SIMD.  Larger
 // groups (multi-query attention) take G / 4 workgroups of 4 heads.
-int decode_head_split(int num_q_heads, int num_kv_heads) {
+// The matrix-core kernel of 8-bit pools takes up to 16 query heads (one MFMA
+// column each) per workgroup.
+int decode_head_split(int num_q_heads, int num_kv_heads, bool mma) {
   const int group = num_q_heads / num_kv_heads;
+  if (mma) return group > 16 ? group / 16 : 1;
   return group >= 8 ? group / 4 : 1;  // MQA-like groups (16..64): 4..16 workgroups of 4 heads
 }
 
 int decode_split_blocks(int batch, int num_q_heads, int num_kv_heads, int max_blocks_per_seq,
-                        int requested) {
+                        int requested, bool mma) {
   if (requested > 0) return requested;
   // Enough (sequence, work head) units to fill the chip at two workgroups per
-  // CU: one split each.  Otherwise cut sequences so ~1024 workgroups run.
-  const long long units = (long long)batch * num_kv_heads * decode_head_split(num_q_heads, num_kv_heads);
+  // CU: one split each.  Otherwise cut sequences so ~1024 workgroups run (the
+  // matrix-core kernel: ~512, one round of resident workgroups; a second,
+  // partial round cost it 9 % on the 70B shape).
+  const long long units = (long long)batch * num_kv_heads * decode_head_split(num_q_heads, num_kv_heads, mma);
   if (units >= 512) return max_blocks_per_seq;
-  long long sb = (units * max_blocks_per_seq + 1023) / 1024;
+  const long long target = mma ? 512 : 1024;
+  long long sb = (units * max_blocks_per_seq + target - 1) / target;
   if (sb < 32) sb = 32;
   sb = (sb + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
   return (int)sb;
@@ -572,16 +844,22 @@ static void workspace_layout(int batch, int num_q_heads, int num_kv_heads, int h
   *total = *off_o + units * splits * group * head_dim * sizeof(float);
 }
 
+// The partials' size depends only on the number of splits (units x heads per
+// unit is the query head count); it covers both kernels' split choice.
 size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                              int max_blocks_per_seq, int split_blocks) {
-  const int sb = decode_split_blocks(batch, num_q_heads, num_kv_heads, max_blocks_per_seq, split_blocks);
-  if ((max_blocks_per_seq + sb - 1) / sb <= 1) return 0;  // one split: no partials
-  size_t off_o, t;
-  workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sb, &off_o, &t);
-  return t;
+  size_t need = 0;
+  for (const bool mma : {false, true}) {
+    const int sb = decode_split_blocks(batch, num_q_heads, num_kv_heads, max_blocks_per_seq, split_blocks, mma);
+    if ((max_blocks_per_seq + sb - 1) / sb <= 1) continue;  // one split: no partials
+    size_t off_o, t;
+    workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sb, &off_o, &t);
+    need = t > need ? t : need;
+  }
+  return need;
 }
 
-template <typename T, int D, int G, int MODE, bool F8 = false>
+template <typename T, int D, int G, int MODE, bool F8 = false, bool MMA = false>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   DecodeKernelArgs k;
   k.out = a.out;
@@ -614,8 +892,12 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   char *ws = (char *)a.workspace;
   k.ws_ml = ws ? (float2 *)ws : nullptr;
   k.ws_o = ws ? (float *)(ws + off_o) : nullptr;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, G, MODE, F8>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave),
-                     0, stream, k);
+  if constexpr (MMA)
+    hipLaunchKernelGGL((decode_mma8_kernel<G, MODE>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave), 0, stream,
+                       k);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<T, D, G, MODE, F8>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave),
+                       0, stream, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k.max_splits <= 1) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D, G>), dim3((unsigned)work_heads, (unsigned)a.batch),
@@ -625,7 +907,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
 
 template <typename T, int D, int MODE>
 static hipError_t dispatch_group_e(const DecodeArgs &a, hipStream_t s) {
-  switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads)) {
+  switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads, false)) {
     case 1: return launch_decode_t<T, D, 1, MODE>(a, s);
     case 2: return launch_decode_t<T, D, 2, MODE>(a, s);
     case 4: return launch_decode_t<T, D, 4, MODE>(a, s);
@@ -644,13 +926,16 @@ static hipError_t dispatch_group(const DecodeArgs &a, hipStream_t s) {
   }
 }
 
-// bf16 queries against an 8-bit (E4M3) pool, lazy RoPE, head_dim 128.
+// bf16 queries against an 8-bit (E4M3) pool, lazy RoPE, head_dim 128, on the
+// matrix cores (the pool in the lane order decode_mma8_kernel reads).
 hipError_t launch_decode_fp8(const DecodeArgs &a, hipStream_t s) {
   if (a.head_dim != 128 || a.mode != kRopeLazy) return hipErrorInvalidValue;
-  switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads)) {
-    case 1: return launch_decode_t<bf16, 128, 1, kRopeLazy, true>(a, s);
-    case 2: return launch_decode_t<bf16, 128, 2, kRopeLazy, true>(a, s);
-    case 4: return launch_decode_t<bf16, 128, 4, kRopeLazy, true>(a, s);
+  switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads, true)) {
+    case 1: return launch_decode_t<bf16, 128, 1, kRopeLazy, true, true>(a, s);
+    case 2: return launch_decode_t<bf16, 128, 2, kRopeLazy, true, true>(a, s);
+    case 4: return launch_decode_t<bf16, 128, 4, kRopeLazy, true, true>(a, s);
+    case 8: return launch_decode_t<bf16, 128, 8, kRopeLazy, true, true>(a, s);
+    case 16: return launch_decode_t<bf16, 128, 16, kRopeLazy, true, true>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

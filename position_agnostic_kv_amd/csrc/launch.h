@@ -22,11 +22,12 @@ hipError_t launch_append_fp8(void *k_pool, void *v_pool, bool bf16_rows, int num
                              const int32_t *slot_mapping, int num_tokens, float k_scale, float v_scale,
                              hipStream_t stream);
 
-// Workgroups that share one KV head's query heads in a decode launch.
-int decode_head_split(int num_q_heads, int num_kv_heads);
+// Workgroups that share one KV head's query heads in a decode launch (mma:
+// the matrix-core kernel of 8-bit pools).
+int decode_head_split(int num_q_heads, int num_kv_heads, bool mma);
 // Blocks per split-K partition for a decode launch (requested == 0: automatic).
 int decode_split_blocks(int batch, int num_q_heads, int num_kv_heads, int max_blocks_per_seq,
-                        int requested);
+                        int requested, bool mma);
 size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                              int max_blocks_per_seq, int split_blocks);
 

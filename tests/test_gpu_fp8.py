@@ -2,7 +2,9 @@
 against the E4M3 oracle.  Pools hold random E4M3 byte patterns (every
 exponent from subnormal to 2^2, both signs); the step's new rows are bf16 or
 f32 values that the append quantises, bit for bit as the oracle does,
-including saturation, subnormals, signed zero, infinities and NaN.  Decode
+including saturation, subnormals, signed zero, infinities and NaN.  The
+device pools hold the codes in the library's lane order; the tests move host
+codes into it and back with the index permutation the header documents.  Decode
 covers GQA 4, GQA 8 (two workgroups per KV head), a 32-query-head group,
 split-K, random offsets and documents of any length (fill counts)."""
 
@@ -47,13 +49,14 @@ def test_append_fp8_bit_exact(rows_dtype, ks, vs):
     slots[:5] = -1                                     # padding rows
     slots[5] = nb * 16 + 3                             # past the pool: skipped
     say(f"[fp8 append] rows {rows_dtype} k_scale {ks} v_scale {vs}")
-    kp = torch.full((nb, hkv, 16, d), 0x5A, dtype=torch.uint8, device=DEV)
-    vp = torch.full_like(kp, 0x5A)
+    init_k = np.random.default_rng(5).integers(0, 256, (nb, hkv, 16, d)).astype(np.uint8)
+    init_v = np.random.default_rng(6).integers(0, 256, (nb, hkv, 16, d)).astype(np.uint8)
+    dk, dv = W.fp8_pools_to_device_order(init_k, init_v)
+    kp, vp = _u8(dk), _u8(dv)
     pak.kvcache_append_fp8(kp, vp, kd, vd, _u8(slots), ks, vs)
     torch.cuda.synchronize()
-    init = np.full((nb, hkv, 16, d), 0x5A, dtype=np.uint8)
-    wk, wv = oracle.append_fp8(init, init, x[0], x[1], slots, np.float32(ks), np.float32(vs))
-    gk, gv = kp.cpu().numpy(), vp.cpu().numpy()
+    wk, wv = oracle.append_fp8(init_k, init_v, x[0], x[1], slots, np.float32(ks), np.float32(vs))
+    gk, gv = W.fp8_pools_from_device_order(kp.cpu().numpy(), vp.cpu().numpy())
     bad = int((gk != wk).sum() + (gv != wv).sum())
     say(f"  mismatching bytes: {bad}")
     assert bad == 0
@@ -69,7 +72,7 @@ def _run(case, seed, ks, vs, split=0):
     W.materialize_numpy(case)
     kc, vc = _fp8_case(case, seed)
     dc = DeviceCase(case)
-    k8, v8 = _u8(kc), _u8(vc)
+    k8, v8 = (_u8(x) for x in W.fp8_pools_to_device_order(kc, vc))
     if dc.k_new.shape[0]:
         pak.kvcache_append_fp8(k8, v8, dc.k_new, dc.v_new, dc.slots, ks, vs)
     out = pak.lazyattn_decode_fp8(dc.q, dc.q_pos, k8, v8, dc.table, dc.seq_lens, ks, vs, scale=case.scale,
@@ -77,7 +80,8 @@ def _run(case, seed, ks, vs, split=0):
     torch.cuda.synchronize()
     kn, vn = W.to_float(case.k_new, case.dtype), W.to_float(case.v_new, case.dtype)
     kc2, vc2 = oracle.append_fp8(kc, vc, kn, vn, case.layout.slot_mapping, np.float32(ks), np.float32(vs))
-    assert np.array_equal(k8.cpu().numpy(), kc2) and np.array_equal(v8.cpu().numpy(), vc2), "append bytes"
+    gk, gv = W.fp8_pools_from_device_order(k8.cpu().numpy(), v8.cpu().numpy())
+    assert np.array_equal(gk, kc2) and np.array_equal(gv, vc2), "append bytes"
     want = oracle.decode_fp8(W.to_float(case.q, case.dtype), case.q_pos, kc2, vc2, case.layout.table,
                              case.seq_lens, case.scale, case.rope_theta, np.float32(ks), np.float32(vs),
                              block_fill=case.block_fill)
@@ -88,7 +92,10 @@ DECODE = [
     # Hq, Hkv, ctx, doc blocks, offsets, split, k_scale, v_scale
     (32, 8, [512, 1024, 96], (2, 10), "contiguous", 0, 0.25, 0.125),
     (64, 8, [2048, 64], (4, 16), "contiguous", 8, 0.25, 0.5),
+    (64, 8, [1024, 16, 336], (2, 12), "random", 0, 0.25, 0.5),
     (32, 1, [400, 96], (2, 9), "contiguous", 0, 0.2, 0.1),
+    (64, 1, [272, 48], (2, 9), "contiguous", 4, 0.2, 0.1),
+    (16, 1, [208, 512], (1, 8), "random", 0, 0.2, 0.1),
     (16, 8, [320, 16, 784], (1, 6), "random", 4, 0.3, 0.07),
     (8, 8, [1056, 48], (3, 40), "contiguous", 5, 0.25, 1.0),
 ]
@@ -123,7 +130,8 @@ def test_single_token_reads_every_code_exactly():
     q = torch.from_numpy(W.f32_to_bf16_bits(rng.standard_normal((1, hq, d)).astype(np.float32)).view(np.int16))
     q = q.to(DEV).view(torch.bfloat16)
     table = _u8(np.array([[1 | (7 << 16)]], dtype=np.uint32).view(np.int32))
-    out = pak.lazyattn_decode_fp8(q, _u8(np.array([7], np.int32)), _u8(kc), _u8(vc), table,
+    kd, vd = W.fp8_pools_to_device_order(kc, vc)
+    out = pak.lazyattn_decode_fp8(q, _u8(np.array([7], np.int32)), _u8(kd), _u8(vd), table,
                                   _u8(np.array([1], np.int32)), 0.25, 0.5)
     torch.cuda.synchronize()
     got = W.to_float(out, W.BF16)[0]                       # [Hq, D]

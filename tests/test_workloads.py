@@ -63,3 +63,19 @@ def test_block_frame_table_on_ragged_layout():
         # positions of the valid slots run off, off+1, ... within each document
         pos = oracle.key_positions(t[b], case.seq_lens[b], lay.block_fill)
         assert pos.size == lay.total_lens[b]
+
+
+def test_fp8_lane_order_is_a_permutation_and_round_trips():
+    from workloads import _fp8_lane_order
+    ks, vs = _fp8_lane_order()
+    assert sorted(ks.tolist()) == list(range(2048)) and sorted(vs.tolist()) == list(range(2048))
+    rng = np.random.default_rng(1)
+    k = rng.integers(0, 256, size=(3, 2, 16, 128)).astype(np.uint8)
+    v = rng.integers(0, 256, size=(3, 2, 16, 128)).astype(np.uint8)
+    kd, vd = W.fp8_pools_to_device_order(k, v)
+    k2, v2 = W.fp8_pools_from_device_order(kd, vd)
+    assert np.array_equal(k, k2) and np.array_equal(v, v2)
+    # spot checks of the documented order: byte 1024 i + 16 l + x
+    i, lane, x = 1, 37, 11            # g = 2, t = 5
+    assert kd[0, 0].reshape(-1)[1024 * i + 16 * lane + x] == k[0, 0, 5, 32 * 2 + 16 * i + x]
+    assert vd[0, 0].reshape(-1)[1024 * i + 16 * lane + x] == v[0, 0, 4 * 2 + x % 4, 16 * (4 * i + x // 4) + 5]

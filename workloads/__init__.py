@@ -82,6 +82,39 @@ def e4m3_codes_torch(shape, device, seed, exp_lo=3, exp_hi=9):
     return sign | (exp << 3) | man
 
 
+def _fp8_lane_order():
+    """For byte b of an 8-bit pool's (block, KV head) record (2048 bytes, the
+    lane order the library documents), the logical index token * 128 + dim of
+    the K code and of the V code stored there."""
+    b = np.arange(2048)
+    i, lane, x = b // 1024, (b % 1024) // 16, b % 16
+    g, t = lane // 16, lane % 16
+    k_src = t * 128 + 32 * g + 16 * i + x
+    v_src = (4 * g + x % 4) * 128 + 16 * (4 * i + x // 4) + t
+    return k_src, v_src
+
+
+def fp8_pools_to_device_order(k_codes, v_codes):
+    """Logical [NB, Hkv, 16, 128] E4M3 codes -> the library's byte order (same
+    shape, bytes permuted within each (block, KV head))."""
+    ks, vs = _fp8_lane_order()
+    shp = k_codes.shape
+    k = np.ascontiguousarray(k_codes).reshape(shp[0], shp[1], 2048)[..., ks].reshape(shp)
+    v = np.ascontiguousarray(v_codes).reshape(shp[0], shp[1], 2048)[..., vs].reshape(shp)
+    return k, v
+
+
+def fp8_pools_from_device_order(k_dev, v_dev):
+    """Inverse of fp8_pools_to_device_order."""
+    ks, vs = _fp8_lane_order()
+    shp = k_dev.shape
+    k = np.empty((shp[0], shp[1], 2048), dtype=k_dev.dtype)
+    v = np.empty_like(k)
+    k[..., ks] = np.ascontiguousarray(k_dev).reshape(shp[0], shp[1], 2048)
+    v[..., vs] = np.ascontiguousarray(v_dev).reshape(shp[0], shp[1], 2048)
+    return k.reshape(shp), v.reshape(shp)
+
+
 # ------------------------------------------------------------------- layouts
 @dataclass
 class Layout:
@@ -628,6 +661,7 @@ __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "to_float", "materialize_numpy",
     "materialize_torch", "add_score_shift", "decode_case", "prefill_case", "tiny_decode",
     "llama8b_decode", "llama8b_prefill", "llama70b_decode", "zipf_decode", "ragged_case",
-    "llama8b_decode_ragged", "llama8b_prefill_ragged", "e4m3_codes", "e4m3_codes_torch", "make",
+    "llama8b_decode_ragged", "llama8b_prefill_ragged", "e4m3_codes", "e4m3_codes_torch",
+    "fp8_pools_to_device_order", "fp8_pools_from_device_order", "make",
     "WORKLOADS",
 ]
