@@ -140,3 +140,63 @@ def test_single_token_reads_every_code_exactly():
         want = ref[:128] if h < hq // hkv else ref[128:]
         same = (got[h] == want) | (np.isnan(got[h]) & np.isnan(want))
         assert same.all(), f"head {h}: {np.flatnonzero(~same)[:8]}"
+
+
+@pytest.mark.parametrize("name", ["llama8b_decode", "llama70b_decode"])
+def test_full_size_decode_fp8_sampled(name):
+    """The bench's 8-bit shapes at full size, in its launch configuration
+    (automatic split), against the oracle on sampled (sequence, head) rows.
+    Pools: random E4M3 bytes drawn on the GPU; the oracle reads the sampled
+    sequences' blocks as generated and appends the new rows itself."""
+    ks, vs = 0.25, 0.125
+    case = W.make(name)
+    say(f"[full fp8 decode] {name} B={case.batch} NB={case.layout.num_blocks}")
+    W.materialize_torch(case, DEV)
+    dc = DeviceCase(case)
+    shape = tuple(dc.k_pool.shape)
+    dc.k_pool = dc.v_pool = None
+    case.k_pool = case.v_pool = None
+    torch.cuda.empty_cache()
+    k8 = W.e4m3_codes_torch(shape, DEV, case.seed + 5000)
+    v8 = W.e4m3_codes_torch(shape, DEV, case.seed + 6000)
+    lay = case.layout
+    rng = np.random.default_rng(5)
+    seqs = sorted(rng.choice(case.batch, size=min(4, case.batch), replace=False).tolist())
+    ids = []
+    for b in seqs:
+        ids.extend((lay.table[b, :-(-int(case.seq_lens[b]) // 16)] & 0xFFFF).tolist())
+    uniq = np.unique(np.array(ids, dtype=np.int64))
+    remap = {int(x): i for i, x in enumerate(uniq)}
+    sel = torch.from_numpy(uniq).to(DEV)
+    kc, vc = W.fp8_pools_from_device_order(k8.index_select(0, sel).cpu().numpy(),
+                                           v8.index_select(0, sel).cpu().numpy())
+    rows, slots = [], []
+    for t, sl in enumerate(lay.slot_mapping.tolist()):
+        if sl >= 0 and sl // 16 in remap:
+            rows.append(t)
+            slots.append(remap[sl // 16] * 16 + sl % 16)
+    r = torch.tensor(rows, device=DEV)
+    kc, vc = oracle.append_fp8(kc, vc, W.to_float(dc.k_new.index_select(0, r), W.BF16),
+                               W.to_float(dc.v_new.index_select(0, r), W.BF16), np.array(slots),
+                               np.float32(ks), np.float32(vs))
+    kf, vf = oracle.dequantize(kc, np.float32(ks)), oracle.dequantize(vc, np.float32(vs))
+    tab = np.zeros((len(seqs), lay.table.shape[1]), dtype=np.uint32)
+    for i, b in enumerate(seqs):
+        for j in range(-(-int(case.seq_lens[b]) // 16)):
+            w = int(lay.table[b, j])
+            tab[i, j] = (w & 0xFFFF0000) | remap[w & 0xFFFF]
+    pak.kvcache_append_fp8(k8, v8, dc.k_new, dc.v_new, dc.slots, ks, vs)
+    out = pak.lazyattn_decode_fp8(dc.q, dc.q_pos, k8, v8, dc.table, dc.seq_lens, ks, vs, scale=case.scale,
+                                  rope_theta=case.rope_theta)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    q = W.to_float(case.q, W.BF16)
+    got = W.to_float(out, W.BF16)
+    g = case.num_q_heads // case.num_kv_heads
+    rows_got, rows_want = [], []
+    for i, b in enumerate(seqs):
+        for h in rng.choice(case.num_q_heads, size=3, replace=False).tolist():
+            rows_want.append(oracle.decode_one(q[b, h], int(case.q_pos[b]), kf, vf, tab[i], int(case.seq_lens[b]),
+                                               h // g, case.scale, case.rope_theta))
+            rows_got.append(got[b, h])
+    assert_parity(np.stack(rows_got), np.stack(rows_want), W.BF16, f"{name} fp8 sampled")

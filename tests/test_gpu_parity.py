@@ -258,7 +258,10 @@ def test_incremental_decode_matches_prefill_rows():
 
 # ------------------------------------------------------- full-size workloads
 def _gather(dc, case, seqs):
-    """Host copies of the blocks the sampled sequences use, ids remapped."""
+    """Oracle pools for the sampled sequences: host copies of the blocks they
+    use, taken from the generated pools BEFORE the library's append, ids
+    remapped, then the step's new rows that land there written by the
+    oracle's own append.  Returns (k, v, remapped table rows)."""
     lay = case.layout
     ids = []
     for b in seqs:
@@ -269,6 +272,15 @@ def _gather(dc, case, seqs):
     sel = torch.from_numpy(uniq).to("cuda:0")
     kp = W.to_float(dc.k_pool.index_select(0, sel), case.dtype)
     vp = W.to_float(dc.v_pool.index_select(0, sel), case.dtype)
+    rows, slots = [], []
+    for t, sl in enumerate(lay.slot_mapping.tolist()):
+        if sl >= 0 and sl // 16 in remap:
+            rows.append(t)
+            slots.append(remap[sl // 16] * 16 + sl % 16)
+    if rows:
+        r = torch.tensor(rows, device="cuda:0")
+        kp, vp = oracle.append(kp, vp, W.to_float(dc.k_new.index_select(0, r), case.dtype),
+                               W.to_float(dc.v_new.index_select(0, r), case.dtype), np.array(slots))
     tab = np.zeros((len(seqs), lay.table.shape[1]), dtype=np.uint32)
     for i, b in enumerate(seqs):
         nb = -(-int(case.seq_lens[b]) // 16)
@@ -284,13 +296,13 @@ def test_full_size_decode_sampled(name):
     say(f"[full decode] {name} B={case.batch} NB={case.layout.num_blocks}")
     W.materialize_torch(case, "cuda:0")
     dc = DeviceCase(case)
+    rng = np.random.default_rng(3)
+    seqs = sorted(rng.choice(case.batch, size=min(4, case.batch), replace=False).tolist())
+    kp, vp, tab = _gather(dc, case, seqs)   # generated pools + the oracle's append
     dc.append()
     out = dc.decode()  # automatic split, as bench.py runs it
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
-    rng = np.random.default_rng(3)
-    seqs = sorted(rng.choice(case.batch, size=min(4, case.batch), replace=False).tolist())
-    kp, vp, tab = _gather(dc, case, seqs)   # pools after the device append
     q = W.to_float(case.q, case.dtype)
     got = W.to_float(out, case.dtype)
     g = case.num_q_heads // case.num_kv_heads
@@ -322,13 +334,13 @@ def test_full_size_prefill_sampled():
     say(f"[full prefill] B={case.batch} prompt={case.max_q_len}")
     W.materialize_torch(case, "cuda:0")
     dc = DeviceCase(case)
+    rng = np.random.default_rng(4)
+    seqs = [0, 3]
+    kp, vp, tab = _gather(dc, case, seqs)   # generated pools + the oracle's append
     dc.append()
     out = dc.prefill()
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
-    rng = np.random.default_rng(4)
-    seqs = [0, 3]
-    kp, vp, tab = _gather(dc, case, seqs)
     q = W.to_float(case.q, case.dtype)
     got = W.to_float(out, case.dtype)
     g = case.num_q_heads // case.num_kv_heads
