@@ -41,11 +41,20 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // max of four scores that are never NaN (v_max3_f32 + v_max_f32), without the
-// canonicalising moves that fmaxf's NaN rules add.
+// canonicalising moves that fmaxf's NaN rules add.  Inline assembly: the
+// compiler pads no hazard wait states in front of it, so its inputs must come
+// from ordinary VALU instructions (which the hardware interlocks), never
+// straight from a matrix-core (MFMA) result -- use max4_mfma for those.
 __device__ __forceinline__ float max4_nn(float a, float b, float c, float d) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3\n\tv_max_f32 %0, %0, %4" : "=&v"(r) : "v"(a), "v"(b), "v"(c), "v"(d));
   return r;
+}
+
+// max of four MFMA results: plain builtins, so that the compiler inserts the
+// wait states a VALU read of a matrix-core result needs on gfx950.
+__device__ __forceinline__ float max4_mfma(float a, float b, float c, float d) {
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
 // Dword w (a compile-time constant after unrolling) of a 16-byte chunk.
@@ -150,6 +159,60 @@ __device__ __forceinline__ float col_sum4(float x) {
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// ------------------------------------------ LDS staging of K/V tiles (DMA)
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// LDS chunk swizzle of a K/V tile row (16-byte chunks, CPR per row): slot =
+// chunk ^ swz(row).  For 16 chunks per row a bit rotation of the row keeps both
+// readers conflict-free: the 16 rows of a K operand read (one chunk column)
+// land in 16 distinct bank groups, and the 8 rows x 2 chunks that a half-wave
+// of the transposing V read touches land in 16 distinct groups too.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (r >> 1) & (CPR - 1);
+}
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4, scalar base + per-lane 32-bit offset): lane L's
+// bytes land at LDS address lds + 16 * L.  Issued as inline assembly so the
+// compiler does not order every later LDS read behind it (it cannot tell the
+// buffers apart); the kernel waits for these loads itself (s_waitcnt and a
+// barrier at each tile start).  M0 holds the LDS address; one wait state
+// separates its write from the load.
+__device__ __forceinline__ void lds_dma16(const void *base, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(lds)
+      : "memory", "m0");
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, output
+// lane i gets element (i % 4) of the 8-byte rows read by source lanes
+// i / 4 + 4k, k = 0..3.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t *)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Read-only kernel inputs seen through the constant address space: uniform
+// loads from it are always scalar (s_load, counted by lgkmcnt), even next to
+// inline assembly that clobbers memory, so they never wait on, or make the
+// compiler wait for, vector loads in flight.
+template <typename T>
+using const_as_ptr = const __attribute__((address_space(4))) T *;
+template <typename T>
+__device__ __forceinline__ const_as_ptr<T> as_const_as(const T *p) {
+  return (const_as_ptr<T>)(uintptr_t)p;
 }
 
 // Wave-uniform "any lane true".

@@ -681,7 +681,7 @@ decode_mma8_kernel(const DecodeKernelArgs a) {
       vc[1] = make_uint4(vc[1].x & keep, vc[1].y & keep, vc[1].z & keep, vc[1].w & keep);
     }
     // block maximum of head t16 over the four lane groups
-    float bm = max4_nn(sv[0], sv[1], sv[2], sv[3]);
+    float bm = max4_mfma(sv[0], sv[1], sv[2], sv[3]);
     {
       const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
       bm = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
@@ -771,6 +771,317 @@ decode_mma8_kernel(const DecodeKernelArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 pools on the matrix cores.  For a large query group the VALU form runs
+// out of issue slots before HBM does (its Q.K and P.V dot products grow with
+// G), so here, as for 8-bit pools, both contractions of a block go to MFMA:
+// S = K.q'^T as 4 x v_mfma_f32_16x16x32_bf16 (16 tokens x up to 16 query heads)
+// and O^T += V^T.P^T as 8 x v_mfma_f32_16x16x16_bf16 (16 dims x 16 heads,
+// k = the block's 16 tokens).  The pool keeps its plain [block][head][16][D]
+// layout; each wave streams its blocks straight into a two-slot LDS ring
+// (global_load_lds_dwordx4, 1 KiB contiguous per instruction, chunks swizzled
+// as in the prefill) and reads them back in operand order: K rows with
+// ds_read_b128, V transposed with ds_read_b64_tr_b16.
+//
+// Lane l = 16 g + t (t = l % 16, g = l / 16):
+//   * QK: A = K[token t][dims 32c + 8g .. + 8], B = q'[head t][same dims].
+//     Output: lane l holds the scores of head t at tokens 4g .. 4g+3.
+//   * PV: A = V^T[dim 16c + t][tokens 4g .. 4g+3] (one transposing read),
+//     B = the lane's own four weights (head t, tokens 4g .. 4g+3), so P never
+//     moves.  Output: lane l holds O^T[dims 16c + 4g .. + 4][head t], so a
+//     head's rescale factor is the lane's own.
+//   * The four lane groups of a head share one running maximum (two permlane
+//     swaps per block), since P.V sums their tokens into one accumulator.
+//   * A slot is refilled with the block two steps ahead as soon as its
+//     contents are in registers, so about two blocks per wave stay in flight.
+constexpr int kMmaSlots = 2;           // LDS ring slots per wave (K and V of one block each)
+constexpr int kMma16WorkgroupsPerCu = 2;
+
+template <int G, int MODE>
+__global__ void __launch_bounds__(kDecodeWaves * kWave, kMma16WorkgroupsPerCu)
+decode_mma16_kernel(const DecodeKernelArgs a) {
+  using E = Elem<bf16>;
+  constexpr int D = 128;
+  constexpr int CPR = D / 8;               // 16-byte chunks per row
+  constexpr int RPI = kWave / CPR;         // rows per DMA instruction
+  constexpr int IPB = kBlockTokens / RPI;  // DMA instructions per block (K or V)
+  constexpr int ROWB = D * 2;
+  constexpr int BLKB = kBlockTokens * ROWB;  // 4 KiB: one block of one KV head
+  constexpr int NT = kDecodeWaves * kWave;
+  constexpr bool EAGER = MODE == kRopeEager;
+  constexpr bool ALIBI = MODE == kAlibi;
+  static_assert(G >= 1 && G <= 16, "one workgroup takes up to 16 query heads");
+  static_assert(G * D * sizeof(float) <= kMmaSlots * 2 * BLKB, "a wave's partial output fits its ring");
+
+  // per wave: kMmaSlots x (K tile, V tile); after the loop a wave's ring holds
+  // its partial output [G][D] for the merge
+  __shared__ __attribute__((aligned(1024))) char s_ring[kDecodeWaves][kMmaSlots][2][BLKB];
+  __shared__ float s_m[kDecodeWaves][G];
+  __shared__ float s_l[kDecodeWaves][G];
+  __shared__ int s_bad[kDecodeWaves];  // per wave: a table word pointed outside the pool
+
+  const int hkv = a.num_kv_heads;
+  const int slot = blockIdx.x / kXcds;
+  const int hsub = slot & ((1 << a.kv_shift) - 1);
+  const int unit = (slot >> a.kv_shift) * kXcds + (int)(blockIdx.x % kXcds);
+  if (unit >= a.num_units) return;
+  const int hkv_pool = hkv >> a.kv_shift;
+  const int split = unit % a.max_splits;
+  const int gp = (unit / a.max_splits) % hkv_pool;
+  const int b = unit / a.max_splits / hkv_pool;
+  const int g = (gp << a.kv_shift) | hsub;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int hq = hkv * G;
+
+  const int seq_len = a.seq_lens[b];
+  const bool bad_len = seq_len < 0 || seq_len > a.max_blocks * kBlockTokens;
+  const int nblk = bad_len ? 0 : (seq_len + kBlockTokens - 1) / kBlockTokens;
+  const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
+  bf16 *out = (bf16 *)a.out + ((size_t)b * hq + (size_t)g * G) * D;
+  if (nsplit == 0) {
+    if (split == 0)
+      for (int i = tid; i < G * D; i += NT) E::store(out, i, bad_len ? __builtin_nanf("") : 0.f);
+    return;
+  }
+  if (split >= nsplit) return;
+
+  const int n_pos = a.q_pos[b];
+  const int t16 = lane & 15;  // K token row / query head column / V^T dim row
+  const int g4 = lane >> 4;   // lane group
+  const bool live = t16 < G;
+
+  // raw (bf16) query of head t16, dims 32c + 8 g4 .. + 8 (chunk 4c + g4)
+  uint4 qraw[4];
+  {
+    const uint4 *qh = (const uint4 *)((const bf16 *)a.q + ((size_t)b * hq + (size_t)g * G + (live ? t16 : 0)) * D);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qraw[c] = live ? qh[4 * c + g4] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const double inv_freq = rope_inv_freq(lane, D, a.rope_theta);  // lane i: frequency i (D/2 = 64 of them)
+
+  // q' = rot(q, delta) * scale * log2(e) in bf16, for head t16.  The lane's
+  // dims d (c = 0, 1) and d + 64 (c + 2) form rotate-half pairs, so the
+  // rotation is lane-local; cos/sin of frequency i come from lane i (angle
+  // reduced in double to a fraction of a turn, then v_cos/v_sin).
+  bf16x8_t qb[4];
+  auto rotate = [&](int delta) {
+    const double tt = (double)delta * (inv_freq * 0.15915494309189535);
+    const float f = (float)(tt - rint(tt));
+    const float cs = __builtin_amdgcn_cosf(f), sn = __builtin_amdgcn_sinf(f);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float r[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const int e = 2 * k + e2;
+          const int fi = 32 * c + 8 * g4 + e;
+          const float cv = __shfl(cs, fi), sv = __shfl(sn, fi);
+          const uint32_t wx = dw4(qraw[c], k), wy = dw4(qraw[c + 2], k);
+          const float x = e2 ? bf16_hi(wx) : bf16_lo(wx);
+          const float y = e2 ? bf16_hi(wy) : bf16_lo(wy);
+          r[e2] = fmaf(x, cv, -(y * sv)) * a.scale_log2;
+          r[2 + e2] = fmaf(y, cv, x * sv) * a.scale_log2;
+        }
+        lo[k] = pack_bf16x2(r[0], r[1]);
+        hi[k] = pack_bf16x2(r[2], r[3]);
+      }
+      qb[c] = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+      qb[c + 2] = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+    }
+  };
+  if constexpr (EAGER) rotate(n_pos);
+  if constexpr (ALIBI) rotate(0);  // the identity: q * scale * log2(e)
+  const float slope2 = ALIBI && live ? a.slopes[g * G + t16] * kLog2e : 0.f;
+
+  // DMA source offsets (tile-independent): lane L of instruction i fills row
+  // i * RPI + L / CPR, chunk slot L % CPR, from global chunk (L % CPR) ^ swz(row)
+  uint32_t ld_off[IPB];
+#pragma unroll
+  for (int i = 0; i < IPB; ++i) {
+    const int r = i * RPI + lane / CPR;
+    ld_off[i] = (uint32_t)(r * ROWB + (((lane % CPR) ^ swz<CPR>(r)) * 16));
+  }
+  // operand read offsets: K row t16, chunk 4c + g4; V^T source row 4 g4 + t16 / 4, dims 16c + 4 (t16 % 4)
+  uint32_t k_off[4], v_off[8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) k_off[c] = (uint32_t)(t16 * ROWB + (((4 * c + g4) ^ swz<CPR>(t16)) * 16));
+  {
+    const int vr = 4 * g4 + (t16 >> 2);
+    const int tdim = (t16 & 3) * 4;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int dim = 16 * c + tdim;
+      v_off[c] = (uint32_t)(vr * ROWB + (((dim / 8) ^ swz<CPR>(vr)) * 16) + (dim % 8) * 2);
+    }
+  }
+  char *ring = &s_ring[wave][0][0][0];
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr_t)ring;
+
+  const int blk0 = split * a.split_blocks;
+  const int blk1 = min(nblk, blk0 + a.split_blocks);
+  // table words and fill counts as scalar loads (see as_const_as)
+  const auto trow = as_const_as(a.table + (size_t)b * a.max_blocks);
+  const auto fill4 = a.fill4 ? as_const_as(a.fill4) : nullptr;
+  bool bad = false;
+
+  // K and V of the block whose table word is w into ring slot SL; returns the
+  // block's (offset << 16 | fill count)
+  auto issue = [&](uint32_t w, auto slc) -> uint32_t {
+    constexpr int SL = decltype(slc)::value;
+    uint32_t id = word_block(w);
+    if (id >= (uint32_t)a.num_blocks) {
+      bad = true;
+      id = 0;
+    }
+    const char *kg = (const char *)a.k_pool + ((size_t)id * hkv_pool + gp) * BLKB;
+    const char *vg = (const char *)a.v_pool + ((size_t)id * hkv_pool + gp) * BLKB;
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      lds_dma16(kg, ld_off[i], ring_lds + (SL * 2) * BLKB + i * 1024);
+      lds_dma16(vg, ld_off[i], ring_lds + (SL * 2 + 1) * BLKB + i * 1024);
+    }
+    const uint32_t fill = fill4 ? (fill4[id >> 2] >> ((id & 3u) * 8u)) & 0xffu : (uint32_t)kBlockTokens;
+    return (w & 0xffff0000u) | fill;
+  };
+
+  f32x4_t O[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kMaxFloor, lsum = 0.f;
+  int cur_off = -1;
+
+  // this wave takes blocks blk0 + wave, + 4, ...; slots alternate
+  int blk = blk0 + wave;
+  uint32_t meta0 = 0, meta1 = 0;
+  if (blk < blk1) meta0 = issue(trow[blk], std::integral_constant<int, 0>{});
+  if (blk + kDecodeWaves < blk1) meta1 = issue(trow[blk + kDecodeWaves], std::integral_constant<int, 1>{});
+  // table word of the block two steps ahead, loaded one step before its DMA
+  uint32_t wpre = blk + 2 * kDecodeWaves < blk1 ? trow[blk + 2 * kDecodeWaves] : 0u;
+
+  auto step = [&](uint32_t &meta, auto slc) {
+    constexpr int SL = decltype(slc)::value;
+    // this block's loads have landed (the next block's may still be in flight)
+    if (blk + kDecodeWaves < blk1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * IPB) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const char *kb = ring + (SL * 2) * BLKB;
+    const char *vb = ring + (SL * 2 + 1) * BLKB;
+    uint4 ka[4];
+    uint2 va[8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ka[c] = *(const uint4 *)(kb + k_off[c]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) va[c] = lds_read_tr16((const uint16_t *)(vb + v_off[c]));
+    const uint32_t mcur = meta;
+    // refill the slot with the block two steps ahead once the reads are done
+    const int bfar = blk + 2 * kDecodeWaves;
+    if (bfar < blk1) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      meta = issue(wpre, slc);
+      wpre = bfar + kDecodeWaves < blk1 ? trow[bfar + kDecodeWaves] : 0u;
+    }
+
+    if constexpr (MODE == kRopeLazy) {
+      const int off = word_offset(mcur);
+      if (off != cur_off) {
+        rotate(n_pos - off);
+        cur_off = off;
+      }
+    }
+    // S[token 4 g4 + j][head t16], log2 units
+    f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[c]), qb[c], S, 0, 0, 0);
+    float sv[4] = {S[0], S[1], S[2], S[3]};
+    if constexpr (ALIBI) {  // key position (block offset + slot) - query position
+      const float base = (float)(word_offset(mcur) + 4 * g4 - n_pos);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sv[j] = fmaf(slope2, base + (float)j, sv[j]);
+    }
+    const int nvalid = min(seq_len - blk * kBlockTokens, (int)(mcur & 0xffffu));
+    if (nvalid < kBlockTokens) {  // partly filled: mask tokens, zero their V values
+      const int nv = nvalid - 4 * g4;  // valid tokens among this lane's 4
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j >= nv) sv[j] = -INFINITY;
+      const uint32_t kx = nv >= 2 ? 0xffffffffu : nv == 1 ? 0xffffu : 0u;
+      const uint32_t ky = nv >= 4 ? 0xffffffffu : nv == 3 ? 0xffffu : 0u;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) va[c] = make_uint2(va[c].x & kx, va[c].y & ky);
+    }
+    // block maximum of head t16 over the four lane groups
+    const float bm = col_max4(max4_mfma(sv[0], sv[1], sv[2], sv[3]));
+    if (wave_any(live && bm > m + kRescaleSlack)) {
+      const float mn = fmaxf(m, bm);
+      const float alpha = fast_exp2(m - mn);  // 0 on the first rescale
+      lsum *= alpha;
+      m = mn;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) O[c] *= alpha;
+    }
+    const uint32_t pa0 = pack_bf16x2(fast_exp2(sv[0] - m), fast_exp2(sv[1] - m));
+    const uint32_t pa1 = pack_bf16x2(fast_exp2(sv[2] - m), fast_exp2(sv[3] - m));
+    lsum = dot2_bf16(pa0, 0x3f803f80u, lsum);  // the bf16 weights P.V uses
+    lsum = dot2_bf16(pa1, 0x3f803f80u, lsum);
+    const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(pa0, pa1));
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      O[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, va[c]), pb, O[c], 0, 0, 0);
+    blk += kDecodeWaves;
+  };
+  while (blk < blk1) {
+    step(meta0, std::integral_constant<int, 0>{});
+    if (blk >= blk1) break;
+    step(meta1, std::integral_constant<int, 1>{});
+  }
+
+  // this wave's (max, sum, output): sums over the four lane groups; the
+  // output goes to the wave's own ring (its loads have all landed)
+  lsum = col_sum4(lsum);
+  if (live && g4 == 0) {
+    s_m[wave][t16] = m;
+    s_l[wave][t16] = lsum;
+  }
+  if (live) {
+    float *so = (float *)ring + t16 * D + 4 * g4;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) *(f32x4_t *)(so + 16 * c) = O[c];
+  }
+  if (lane == 0) s_bad[wave] = bad;
+  __syncthreads();
+
+  const bool single = nsplit == 1;
+  const bool flagged = (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) != 0;
+  const size_t part = ((size_t)b * hkv + g) * a.max_splits + split;
+  for (int i = tid; i < G * D; i += NT) {
+    const int h = i / D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
+    float o = 0.f, ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float f = s_m[w][h] == -INFINITY ? 0.f : fast_exp2(s_m[w][h] - mx);
+      o = fmaf(((const float *)&s_ring[w][0][0][0])[i], f, o);
+      ls = fmaf(s_l[w][h], f, ls);
+    }
+    if (flagged) {
+      o = __builtin_nanf("");
+      ls = __builtin_nanf("");
+    }
+    if (single) {
+      E::store(out, i, ls != 0.f ? o / ls : 0.f);
+    } else {
+      a.ws_o[part * G * D + i] = o;
+      if (i % D == 0) a.ws_ml[part * G + h] = make_float2(mx, ls);
+    }
+  }
+}
+
 // Merge the per-split partials of one (sequence, KV head): log-sum-exp weights.
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256)
@@ -813,6 +1124,14 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // groups (multi-query attention) take G / 4 workgroups of 4 heads.
 // The matrix-core kernel of 8-bit pools takes up to 16 query heads (one MFMA
 // column each) per workgroup.
+// Query groups that the matrix-core kernel of bf16 pools takes (head_dim 128).
+constexpr int kMma16MinGroup = 8;
+
+bool decode_uses_mma(bool pool8, bool bf16, int head_dim, int num_q_heads, int num_kv_heads) {
+  if (pool8) return true;
+  return bf16 && head_dim == 128 && num_q_heads / num_kv_heads >= kMma16MinGroup;
+}
+
 int decode_head_split(int num_q_heads, int num_kv_heads, bool mma) {
   const int group = num_q_heads / num_kv_heads;
   if (mma) return group > 16 ? group / 16 : 1;
@@ -859,7 +1178,10 @@ size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int h
   return need;
 }
 
-template <typename T, int D, int G, int MODE, bool F8 = false, bool MMA = false>
+// IMPL: kValu (decode_split_kernel), kMma8 (8-bit pools), kMma16 (bf16 pools, matrix cores)
+enum DecodeImpl { kValu = 0, kMma8 = 1, kMma16 = 2 };
+
+template <typename T, int D, int G, int MODE, bool F8 = false, int IMPL = kValu>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   DecodeKernelArgs k;
   k.out = a.out;
@@ -892,8 +1214,11 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   char *ws = (char *)a.workspace;
   k.ws_ml = ws ? (float2 *)ws : nullptr;
   k.ws_o = ws ? (float *)(ws + off_o) : nullptr;
-  if constexpr (MMA)
+  if constexpr (IMPL == kMma8)
     hipLaunchKernelGGL((decode_mma8_kernel<G, MODE>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave), 0, stream,
+                       k);
+  else if constexpr (IMPL == kMma16)
+    hipLaunchKernelGGL((decode_mma16_kernel<G, MODE>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave), 0, stream,
                        k);
   else
     hipLaunchKernelGGL((decode_split_kernel<T, D, G, MODE, F8>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave),
@@ -905,8 +1230,20 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int MODE>
+static hipError_t dispatch_mma16(const DecodeArgs &a, hipStream_t s) {
+  switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads, true)) {
+    case 8: return launch_decode_t<bf16, 128, 8, MODE, false, kMma16>(a, s);
+    case 16: return launch_decode_t<bf16, 128, 16, MODE, false, kMma16>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, int D, int MODE>
 static hipError_t dispatch_group_e(const DecodeArgs &a, hipStream_t s) {
+  if constexpr (sizeof(T) == 2 && D == 128) {
+    if (decode_uses_mma(false, true, D, a.num_q_heads, a.num_kv_heads)) return dispatch_mma16<MODE>(a, s);
+  }
   switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads, false)) {
     case 1: return launch_decode_t<T, D, 1, MODE>(a, s);
     case 2: return launch_decode_t<T, D, 2, MODE>(a, s);
@@ -931,11 +1268,11 @@ static hipError_t dispatch_group(const DecodeArgs &a, hipStream_t s) {
 hipError_t launch_decode_fp8(const DecodeArgs &a, hipStream_t s) {
   if (a.head_dim != 128 || a.mode != kRopeLazy) return hipErrorInvalidValue;
   switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads, true)) {
-    case 1: return launch_decode_t<bf16, 128, 1, kRopeLazy, true, true>(a, s);
-    case 2: return launch_decode_t<bf16, 128, 2, kRopeLazy, true, true>(a, s);
-    case 4: return launch_decode_t<bf16, 128, 4, kRopeLazy, true, true>(a, s);
-    case 8: return launch_decode_t<bf16, 128, 8, kRopeLazy, true, true>(a, s);
-    case 16: return launch_decode_t<bf16, 128, 16, kRopeLazy, true, true>(a, s);
+    case 1: return launch_decode_t<bf16, 128, 1, kRopeLazy, true, kMma8>(a, s);
+    case 2: return launch_decode_t<bf16, 128, 2, kRopeLazy, true, kMma8>(a, s);
+    case 4: return launch_decode_t<bf16, 128, 4, kRopeLazy, true, kMma8>(a, s);
+    case 8: return launch_decode_t<bf16, 128, 8, kRopeLazy, true, kMma8>(a, s);
+    case 16: return launch_decode_t<bf16, 128, 16, kRopeLazy, true, kMma8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -22,8 +22,11 @@ hipError_t launch_append_fp8(void *k_pool, void *v_pool, bool bf16_rows, int num
                              const int32_t *slot_mapping, int num_tokens, float k_scale, float v_scale,
                              hipStream_t stream);
 
+// Whether a decode launch runs on a matrix-core kernel (every 8-bit pool;
+// bf16 pools with head_dim 128 and large query groups).
+bool decode_uses_mma(bool pool8, bool bf16, int head_dim, int num_q_heads, int num_kv_heads);
 // Workgroups that share one KV head's query heads in a decode launch (mma:
-// the matrix-core kernel of 8-bit pools).
+// a matrix-core kernel).
 int decode_head_split(int num_q_heads, int num_kv_heads, bool mma);
 // Blocks per split-K partition for a decode launch (requested == 0: automatic).
 int decode_split_blocks(int batch, int num_q_heads, int num_kv_heads, int max_blocks_per_seq,

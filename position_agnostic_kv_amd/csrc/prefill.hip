@@ -62,48 +62,6 @@ struct PrefillKernelArgs {
   float scale_log2, rope_theta;
 };
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-
-// LDS chunk swizzle of a K/V tile row (16-byte chunks, CPR per row): slot =
-// chunk ^ swz(row).  For 16 chunks per row a bit rotation of the row keeps both
-// readers conflict-free: the 16 rows of a K operand read (one chunk column)
-// land in 16 distinct bank groups, and the 8 rows x 2 chunks that a half-wave
-// of the transposing V read touches land in 16 distinct groups too.
-template <int CPR>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (CPR == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
-  else return (r >> 1) & (CPR - 1);
-}
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
-
-// 16 bytes per lane from global memory straight into LDS
-// (global_load_lds_dwordx4, scalar base + per-lane 32-bit offset): lane L's
-// bytes land at LDS address lds + 16 * L.  Issued as inline assembly so the
-// compiler does not order every later LDS read behind it (it cannot tell the
-// buffers apart); the kernel waits for these loads itself (s_waitcnt and a
-// barrier at each tile start).  M0 holds the LDS address; one wait state
-// separates its write from the load.
-__device__ __forceinline__ void lds_dma16(const void *base, uint32_t voff, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(base), "s"(lds)
-      : "memory", "m0");
-}
-
-// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, output
-// lane i gets element (i % 4) of the 8-byte rows read by source lanes
-// i / 4 + 4k, k = 0..3.
-__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p) {
-  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4_t *)(p));
-  return __builtin_bit_cast(uint2, v);
-}
-
 // HP query heads of one KV head share a workgroup: rows = HP heads x (128 / HP)
 // tokens; wave w owns 32 consecutive rows (one head).
 //
