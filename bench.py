@@ -584,7 +584,7 @@ def main():
                               "pattern of decode)"},
         "wall_s_timed": round(wall, 3),
         "roofline": {
-            "kernel": "lazyattn::decode_split_kernel<lazyattn::bf16, 128, 4, 0, false>",
+            "kernel": "lazyattn::decode_mma16_kernel<4, 0>",
             "bound": "hbm",
             "achieved": round(dec_achieved, 1),
             "peak": HBM_PEAK_GBPS,
