@@ -375,6 +375,194 @@ def shapes_main(args):
     print(json.dumps(res), flush=True)
 
 
+# --shapes launches each kernel on these workloads, in this order, warmup +
+# steps times each (other kernels in between); the profile summary splits a
+# kernel's dispatches into consecutive runs accordingly.  Value: (profile
+# file stem, kernel source files, algorithmic bytes of one launch).
+SHAPES_DISPATCH_ORDER = {
+    "lazyattn::decode_mma16_kernel<4, 0>": ["llama8b_decode", "zipf_reuse_decode", "llama8b_decode_ragged"],
+    "lazyattn::decode_mma16_kernel<4, 2>": ["llama8b_decode_alibi"],
+    "lazyattn::decode_mma16_kernel<8, 0>": ["llama70b_decode"],
+    "lazyattn::decode_mma8_kernel<4, 0>": ["llama8b_decode_fp8"],
+    "lazyattn::decode_mma8_kernel<8, 0>": ["llama70b_decode_fp8"],
+    "lazyattn::prefill_kernel<128, 4, 0>": ["llama8b_prefill", "llama8b_prefill_ragged"],
+    "lazyattn::prefill_kernel<128, 4, 2>": ["llama8b_prefill_alibi"],
+}
+PROFILE_STEMS = {
+    "llama8b_decode": "decode_llama8b", "zipf_reuse_decode": "decode_zipf",
+    "llama8b_decode_ragged": "decode_llama8b_ragged", "llama8b_decode_alibi": "decode_llama8b_alibi",
+    "llama70b_decode": "decode_llama70b", "llama8b_decode_fp8": "decode_llama8b_fp8",
+    "llama70b_decode_fp8": "decode_llama70b_fp8", "llama8b_prefill": "prefill_llama8b",
+    "llama8b_prefill_ragged": "prefill_llama8b_ragged", "llama8b_prefill_alibi": "prefill_llama8b_alibi",
+}
+
+
+def _profile_workload_bytes(name):
+    """(description, algorithmic bytes of one launch) of a --shapes workload."""
+    import workloads as W
+    base = name.replace("_fp8", "").replace("_alibi", "")
+    case = W.make(base)
+    if case.kind == "decode":
+        kv, total = decode_algorithmic_bytes(case)
+        if name.endswith("_fp8"):
+            kv, total = fp8_decode_algorithmic_bytes(case)
+        desc = (f"{name}: {case.batch} seqs, {int(case.layout.total_lens.sum())} tokens attended, "
+                f"{case.num_q_heads} q / {case.num_kv_heads} KV heads, d_h {case.head_dim}, "
+                f"{'E4M3 pool, bf16 q' if name.endswith('_fp8') else 'bf16'}; algorithmic = K+V once + q, out, "
+                f"table words")
+        return desc, total
+    toks = int(case.layout.total_lens.sum())
+    rows = int(case.cu_q_lens[-1])
+    total = toks * case.num_kv_heads * case.head_dim * 2 * 2 + 2 * rows * case.num_q_heads * case.head_dim * 2
+    desc = (f"{name}: {case.batch} seqs, {toks} K/V tokens ({rows} prompt rows), {case.num_q_heads} q / "
+            f"{case.num_kv_heads} KV heads, d_h {case.head_dim}, bf16; algorithmic = K+V once + q + out")
+    return desc, total
+
+
+def _rocpd_rows(root, query):
+    """Rows of a query over every rocprofv3 result database (rocpd SQLite) under root."""
+    import sqlite3
+    rows = []
+    for dirpath, _, files in os.walk(root):
+        for fn in sorted(files):
+            if fn.endswith("_results.db"):
+                con = sqlite3.connect(os.path.join(dirpath, fn))
+                rows.extend(con.execute(query).fetchall())
+                con.close()
+    if not rows:
+        raise SystemExit(f"no rocprofv3 results under {root}")
+    return rows
+
+
+def _kernel_key(name):
+    name = name.replace("(anonymous namespace)::", "").split("(")[0].strip()
+    return name[5:] if name.startswith("void ") else name
+
+
+def pmc_summary_main(args):
+    """Write profiles/*_pmc.json and profiles/decode_shapes_kernel_trace.md
+    from the rocprofv3 result databases of three runs of `bench.py --shapes --steps S
+    --warmup W --copy-calibration` (FETCH_SIZE, WRITE_SIZE, kernel trace).
+    Counters are per dispatch; each is scaled by what it reads for the
+    calibration dispatches at the start of the run (a 1 GiB fill for
+    WRITE_SIZE, a 1 GiB device copy for FETCH_SIZE)."""
+    fetch_dir, write_dir, trace_dir = args.pmc_summary
+    per_run = args.steps + args.warmup
+    known = 1 << 30
+
+    def counters(root, counter):
+        vals = {}
+        for disp, kname, cname, value in _rocpd_rows(
+                root, "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+            if cname != counter:
+                continue
+            prev = vals.get(int(disp), (_kernel_key(kname), 0.0))
+            vals[int(disp)] = (prev[0], prev[1] + float(value))
+        return [vals[k] for k in sorted(vals)]
+
+    fetch = counters(fetch_dir, "FETCH_SIZE")
+    write = counters(write_dir, "WRITE_SIZE")
+    first_copy = next(v for n, v in fetch if "copyBuffer" in n or "copy" in n.lower())
+    first_fill = next(v for n, v in write if "Fill" in n)
+    fetch_scale = known / (first_copy * 1024)
+    write_scale = known / (first_fill * 1024)
+
+    durs = {}
+    for name, start, end in sorted(_rocpd_rows(trace_dir, "select name, start, end from kernels"),
+                                   key=lambda r: int(r[1])):
+        durs.setdefault(_kernel_key(name), []).append((int(end) - int(start)) / 1000.0)
+
+    def runs(seq, kernel):
+        vals = [v for n, v in seq if n == kernel]
+        return [vals[i * per_run:(i + 1) * per_run] for i in range(len(vals) // per_run)]
+
+    cmd_base = f"python -u bench.py --shapes --steps {args.steps} --warmup {args.warmup} --copy-calibration"
+    cal = {"known_bytes": known, "copy_fetch_kib": round(first_copy, 3), "fetch_scale": round(fetch_scale, 5),
+           "fill_write_kib": round(first_fill, 3), "write_scale": round(write_scale, 5),
+           "note": "1 GiB device copy read back by FETCH_SIZE; 1 GiB fill by WRITE_SIZE"}
+    for kernel, names in SHAPES_DISPATCH_ORDER.items():
+        fr, wr = runs(fetch, kernel), runs(write, kernel)
+        tr = [durs.get(kernel, [])[i * per_run:(i + 1) * per_run] for i in range(len(names))]
+        if len(fr) != len(names) or len(wr) != len(names):
+            print(f"skip {kernel}: {len(fr)}/{len(wr)} runs for {len(names)} workloads", file=sys.stderr)
+            continue
+        for name, f_run, w_run, t_run in zip(names, fr, wr, tr):
+            desc, alg = _profile_workload_bytes(name)
+            f_kib = float(np.mean(f_run[args.warmup:]))
+            w_kib = float(np.mean(w_run[args.warmup:]))
+            traffic = int(round(f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale))
+            src = PREFILL_SOURCES if "prefill" in kernel else DECODE_SOURCES
+            rec = {"kernel": kernel.replace("lazyattn::", ""), "workload": desc, "source_files": src,
+                   "source_hash": source_hash(src), "fetch_kib_per_dispatch": round(f_kib, 3),
+                   "write_kib_per_dispatch": round(w_kib, 3), "dispatches": len(f_run) - args.warmup,
+                   "copy_calibration": cal, "traffic_bytes_per_launch": traffic, "algorithmic_bytes": alg,
+                   "traffic_over_algorithmic": round(traffic / alg, 4),
+                   "trace_avg_duration_us": round(float(np.mean(t_run[args.warmup:])), 1) if t_run else None,
+                   "commands": [f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run -- {cmd_base}",
+                                f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run -- {cmd_base}",
+                                f"rocprofv3 --kernel-trace --stats -d {trace_dir} -o run -- {cmd_base}",
+                                f"python bench.py --pmc-summary {fetch_dir} {write_dir} {trace_dir} "
+                                f"--steps {args.steps} --warmup {args.warmup}"]}
+            path = os.path.join(PROFILES, f"{PROFILE_STEMS[name]}_pmc.json")
+            with open(path, "w") as f:
+                json.dump(rec, f, indent=1)
+                f.write("\n")
+            print(f"{path}: traffic/algorithmic {rec['traffic_over_algorithmic']}, "
+                  f"{rec['trace_avg_duration_us']} us")
+
+    # kernel-trace summary: every kernel, then the per-workload runs
+    lines = ["# rocprofv3 kernel trace: bench.py --shapes (every decode workload, the 8-bit pool, ALiBi; "
+             "8B prefill, ALiBi and ragged prefill)", "",
+             "Command (GPU box, from the repository root):", "",
+             f"    rocprofv3 --kernel-trace --stats -d {trace_dir} -o run -- {cmd_base}", "",
+             f"Summarised by `python bench.py --pmc-summary {fetch_dir} {write_dir} {trace_dir} "
+             f"--steps {args.steps} --warmup {args.warmup}`.  Torch's fill, copy and random kernels are input "
+             "generation or the counter calibration, outside the timed work.", "",
+             "kernel | calls | avg us | total us | %", "---|---|---|---|---"]
+    tot = sum(sum(v) for v in durs.values())
+    for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{k[:90]} | {len(v)} | {np.mean(v):.1f} | {sum(v):.1f} | {100 * sum(v) / tot:.1f}")
+    lines += ["", f"Per workload ({args.warmup} warm-up + {args.steps} timed dispatches each; the timed ones):", "",
+              "kernel | workload | median us | min us | max us", "---|---|---|---|---"]
+    for kernel, names in SHAPES_DISPATCH_ORDER.items():
+        v = durs.get(kernel, [])
+        for i, name in enumerate(names):
+            run = v[i * per_run:(i + 1) * per_run][args.warmup:]
+            if run:
+                lines.append(f"{kernel.replace('lazyattn::', '')} | {name} | {np.median(run):.1f} | "
+                             f"{min(run):.1f} | {max(run):.1f}")
+    with open(os.path.join(PROFILES, "decode_shapes_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote profiles/decode_shapes_kernel_trace.md")
+
+
+def trace_summary_main(args):
+    """Write profiles/decode_prefill_llama8b_kernel_trace.md from the rocprofv3
+    kernel trace of the default bench step (`bench.py --steps S --warmup W
+    --no-cpu-baseline`): per-kernel calls and durations."""
+    trace_dir = args.trace_summary
+    durs = {}
+    for name, start, end in _rocpd_rows(trace_dir, "select name, start, end from kernels"):
+        durs.setdefault(_kernel_key(name), []).append((int(end) - int(start)) / 1000.0)
+    cmd = (f"rocprofv3 --kernel-trace --stats -d {trace_dir} -o run -- python -u bench.py --steps {args.steps} "
+           f"--warmup {args.warmup} --no-cpu-baseline")
+    lines = ["# rocprofv3 kernel trace: bench.py step (8B decode + 8B prefill)", "",
+             "Command (GPU box, from the repository root):", "", f"    {cmd}", "",
+             f"Summarised by `python bench.py --trace-summary {trace_dir} --steps {args.steps} --warmup "
+             f"{args.warmup}`.  Each step is kvcache_append + lazyattn_decode, then kvcache_append + "
+             "lazyattn_prefill; the calls include the warm-up steps.  Torch's fill, copy and random kernels "
+             "are input generation or the copy roof, outside the timed step.", "",
+             "kernel | calls | avg us | median us | total us | %", "---|---|---|---|---|---"]
+    tot = sum(sum(v) for v in durs.values())
+    for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{k[:90]} | {len(v)} | {np.mean(v):.1f} | {np.median(v):.1f} | {sum(v):.1f} | "
+                     f"{100 * sum(v) / tot:.1f}")
+    path = os.path.join(PROFILES, "decode_prefill_llama8b_kernel_trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {path}")
+
+
 def cache_sim_main(args):
     """Hit rates of the host pool manager under a KV budget (CPU only, no GPU).
 
@@ -442,8 +630,18 @@ def main():
     ap.add_argument("--cache-requests", type=int, default=5000)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for rocprofv3 counter scaling)")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
+                    help="summarise rocprofv3 output of --shapes runs into profiles/ (no GPU)")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="summarise the rocprofv3 kernel trace of a default bench run into profiles/ (no GPU)")
     args = ap.parse_args()
 
+    if args.trace_summary:
+        trace_summary_main(args)
+        return
+    if args.pmc_summary:
+        pmc_summary_main(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
