@@ -536,6 +536,79 @@ def pmc_summary_main(args):
     print("wrote profiles/decode_shapes_kernel_trace.md")
 
 
+ACTIVITY_COUNTERS = ["GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                     "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_LDS_IDX_ACTIVE",
+                     "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CU_CYCLES"]
+MI355X_XCDS, MI355X_CUS, MI355X_SIMDS = 8, 256, 1024
+
+
+def activity_summary_main(args):
+    """Write profiles/decode_prefill_shapes_activity.md from one rocprofv3 run
+    of `bench.py --shapes` with ACTIVITY_COUNTERS: per kernel and workload the
+    clock, MFMA utilisation (rocprofv3's MfmaUtil: MFMA-busy cycles over GPU
+    cycles x SIMDs), the bf16 MFMA FLOPs the counters saw against the
+    algorithmic ones, VALU busy, MFMA/VALU co-issue and LDS utilisation.  The
+    per-dispatch GRBM_GUI_ACTIVE is summed over the 8 XCDs, so it is divided
+    by 8 to get GPU cycles."""
+    root = args.activity_summary
+    per_run = args.steps + args.warmup
+    vals, names, durs = {}, {}, {}
+    for disp, kname, cname, value, start, end in _rocpd_rows(
+            root, "select dispatch_id, kernel_name, counter_name, value, start, end from counters_collection"):
+        d = int(disp)
+        vals.setdefault(d, {})
+        vals[d][cname] = vals[d].get(cname, 0.0) + float(value)
+        names[d] = _kernel_key(kname)
+        durs[d] = (int(end) - int(start)) * 1e-9
+    order = sorted(vals)
+    cmd = (f"rocprofv3 --pmc {' '.join(ACTIVITY_COUNTERS)} -d {root} -o run -- python -u bench.py --shapes "
+           f"--steps {args.steps} --warmup {args.warmup}")
+    lines = ["# rocprofv3 activity counters: bench.py --shapes", "", "Command (GPU box, from the repository root):",
+             "", f"    {cmd}", "", f"Summarised by `python bench.py --activity-summary {root} --steps {args.steps} "
+             f"--warmup {args.warmup}` (means over the {args.steps} timed dispatches of each workload; the "
+             "dispatches run serialised under counter collection).", "",
+             "* clock = GRBM_GUI_ACTIVE / 8 XCDs / dispatch time;",
+             "* MFMA util = SQ_VALU_MFMA_BUSY_CYCLES / (GPU cycles x 1024 SIMDs), rocprofv3's MfmaUtil;",
+             "* MFMA TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / dispatch time; counted/alg = those FLOPs over the "
+             "algorithmic ones (masked keys inside computed tiles count as work done);",
+             "* VALU busy = SQ_ACTIVE_INST_VALU (quad-cycles) / (GPU cycles x 256 CUs), rocprofv3's VALUBusy; "
+             "co-issue = SQ_VALU_MFMA_COEXEC_CYCLES / (GPU cycles x 1024 SIMDs);",
+             "* LDS util = SQ_LDS_IDX_ACTIVE / (GPU cycles x 256 CUs), rocprofv3's LdsUtil; conflicts = "
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
+             "kernel | workload | us | clock GHz | MFMA util | MFMA TFLOP/s | counted/alg | VALU busy | co-issue "
+             "| LDS util | LDS conflict cycles",
+             "---|---|---|---|---|---|---|---|---|---|---"]
+    for kernel, wl in SHAPES_DISPATCH_ORDER.items():
+        ds = [d for d in order if names[d] == kernel]
+        for i, name in enumerate(wl):
+            run = ds[i * per_run:(i + 1) * per_run][args.warmup:]
+            if not run:
+                continue
+
+            def mean(c):
+                return float(np.mean([vals[d].get(c, 0.0) for d in run]))
+            t = float(np.mean([durs[d] for d in run]))
+            cyc = mean("GRBM_GUI_ACTIVE") / MI355X_XCDS
+            flops = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512
+            alg = None
+            if "prefill" in kernel:
+                import workloads as W
+                alg = W.make(name.replace("_alibi", "")).attention_flops()
+            lds = mean("SQ_LDS_IDX_ACTIVE")
+            lines.append(
+                f"{kernel.replace('lazyattn::', '')} | {name} | {t * 1e6:.1f} | {cyc / t / 1e9:.3f} | "
+                f"{100 * mean('SQ_VALU_MFMA_BUSY_CYCLES') / (cyc * MI355X_SIMDS):.1f} % | {flops / t / 1e12:.1f} | "
+                f"{'' if alg is None else f'{flops / alg:.3f}'} | "
+                f"{100 * mean('SQ_ACTIVE_INST_VALU') / (cyc * MI355X_CUS):.1f} % | "
+                f"{100 * mean('SQ_VALU_MFMA_COEXEC_CYCLES') / (cyc * MI355X_SIMDS):.1f} % | "
+                f"{100 * lds / (cyc * MI355X_CUS):.1f} % | "
+                f"{100 * mean('SQ_LDS_BANK_CONFLICT') / lds if lds else 0:.1f} %")
+    path = os.path.join(PROFILES, "decode_prefill_shapes_activity.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {path}")
+
+
 def trace_summary_main(args):
     """Write profiles/decode_prefill_llama8b_kernel_trace.md from the rocprofv3
     kernel trace of the default bench step (`bench.py --steps S --warmup W
@@ -634,8 +707,13 @@ def main():
                     help="summarise rocprofv3 output of --shapes runs into profiles/ (no GPU)")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR",
                     help="summarise the rocprofv3 kernel trace of a default bench run into profiles/ (no GPU)")
+    ap.add_argument("--activity-summary", metavar="PMC_DIR",
+                    help="summarise a rocprofv3 --pmc run of --shapes with the activity counters (no GPU)")
     args = ap.parse_args()
 
+    if args.activity_summary:
+        activity_summary_main(args)
+        return
     if args.trace_summary:
         trace_summary_main(args)
         return
