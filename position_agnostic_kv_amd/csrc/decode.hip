@@ -12,7 +12,17 @@
 // "Flash Attention" (the numerical trick), kept per lane stream and merged at
 // the end of each split, then across splits.
 //
-// gfx950 mapping (wave64):
+// Two kernels.  bf16 pools with head_dim 128 (and 8-bit pools) run on the
+// matrix cores (decode_mma16_kernel, decode_mma8_kernel, described where they
+// are defined); fp32 pools and head_dim 64 run on the VALU
+// (decode_split_kernel).  Both walk a sequence's 16-token blocks split-K
+// (flash-decoding); a sequence split over several workgroups writes per-split
+// (max, sum, unnormalised output) to the workspace and a second, small kernel
+// merges them (log-sum-exp).  The kernel boundary orders the two; no
+// device-scope fence is used (on gfx950 one costs an L2 write-back).  A
+// sequence with one split writes its output directly.
+//
+// VALU kernel, gfx950 mapping (wave64):
 //   * A K (or V) block of one KV head is 16 rows x D contiguous elements.  A
 //     lane loads 16-byte chunks; LPT = D / (16 B / elem) lanes cover one row,
 //     so one dwordx4 load instruction reads 64 * 16 B = 1 KiB of the block
@@ -30,17 +40,6 @@
 //     bounded by 256), which skips almost every rescale of the accumulators.
 //   * The next block's K/V loads are issued before the current block is
 //     computed.
-//   * 8-bit pools (F8): K and V are OCP E4M3 codes with one scale per tensor
-//     (the pages' one-byte KV cache).  A 16-byte chunk then holds 16 dims, so
-//     8 lanes cover a row and a load instruction reads 8 rows; the codes are
-//     widened to bf16 pairs with v_cvt_scalef32_pk_bf16_fp8 (exact: every E4M3
-//     value is a bf16 value) and the products are the bf16 ones.  The K scale
-//     is folded into the rotated query, the V scale into the output.
-//   * A sequence split over several workgroups writes per-split (max, sum,
-//     unnormalised output) to the workspace and a second, small kernel merges
-//     them (log-sum-exp).  The kernel boundary orders the two; no device-scope
-//     fence is used (on gfx950 one costs an L2 write-back).  A sequence with one
-//     split writes its output directly.
 #include <math.h>
 
 #include "common.h"
@@ -107,16 +106,14 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
 // once by its own position.
 // MODE kAlibi: no rotation at all; the score of a key at position p (block
 // offset + slot) takes the bias slope_h * (p - n) of query head h.
-// F8: the pools hold E4M3 codes (T, the q/out type, is then bf16).
-template <typename T, int D, int G, int MODE, bool F8 = false>
+template <typename T, int D, int G, int MODE>
 __global__ void __launch_bounds__(kDecodeWaves * kWave)
 decode_split_kernel(const DecodeKernelArgs a) {
   using E = Elem<T>;
   constexpr bool kBf16 = sizeof(T) == 2;
   constexpr bool EAGER = MODE == kRopeEager;
   constexpr bool ALIBI = MODE == kAlibi;
-  static_assert(!F8 || kBf16, "8-bit pools take bf16 queries");
-  constexpr int EPL = F8 ? 16 : E::kPerChunk;  // pool elements per 16-byte chunk
+  constexpr int EPL = E::kPerChunk;  // pool elements per 16-byte chunk
   constexpr int LPT = D / EPL;             // lanes per token row
   constexpr int TPI = kWave / LPT;         // token rows per load instruction
   constexpr int NI = kBlockTokens / TPI;   // load instructions per block
@@ -309,15 +306,7 @@ decode_split_kernel(const DecodeKernelArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float t;
-        if constexpr (F8) {  // word j = dims 4j..4j+3: pairs 2j (bytes 0-1) and 2j+1 (bytes 2-3)
-          t = dot2_bf16(qp[h][0], e4m3x2_to_bf16x2<false>(dw4(kc[i], 0)), 0.f);
-          t = dot2_bf16(qp[h][1], e4m3x2_to_bf16x2<true>(dw4(kc[i], 0)), t);
-#pragma unroll
-          for (int j = 1; j < EPL / 4; ++j) {
-            t = dot2_bf16(qp[h][2 * j], e4m3x2_to_bf16x2<false>(dw4(kc[i], j)), t);
-            t = dot2_bf16(qp[h][2 * j + 1], e4m3x2_to_bf16x2<true>(dw4(kc[i], j)), t);
-          }
-        } else if constexpr (kBf16) {
+        if constexpr (kBf16) {
           t = dot2_bf16(qp[h][0], dw4(kc[i], 0), 0.f);
 #pragma unroll
           for (int w = 1; w < EPL / 2; ++w) t = dot2_bf16(qp[h][w], dw4(kc[i], w), t);
@@ -395,22 +384,6 @@ decode_split_kernel(const DecodeKernelArgs a) {
           pp[h] = pack_bf16x2(p[i][h], p[i + 1][h]);
           l[h] = dot2_bf16(pp[h], 0x3f803f80u, l[h]);
         }
-        if constexpr (F8) {
-          // word j holds dims 4j..4j+3 of a row; interleave the two rows'
-          // bytes, then widen: (row i, row i+1) pairs of one dim each
-#pragma unroll
-          for (int j = 0; j < EPL / 4; ++j) {
-            const uint32_t v0 = dw4(vc[i], j), v1 = dw4(vc[i + 1], j);
-            const uint32_t x01 = __builtin_amdgcn_perm(v1, v0, 0x05010400u);  // dims 4j, 4j+1
-            const uint32_t x23 = __builtin_amdgcn_perm(v1, v0, 0x07030602u);  // dims 4j+2, 4j+3
-            const uint32_t pr[4] = {e4m3x2_to_bf16x2<false>(x01), e4m3x2_to_bf16x2<true>(x01),
-                                    e4m3x2_to_bf16x2<false>(x23), e4m3x2_to_bf16x2<true>(x23)};
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-              for (int k = 0; k < 4; ++k) acc[h][4 * j + k] = dot2_bf16(pp[h], pr[k], acc[h][4 * j + k]);
-          }
-        } else {
 #pragma unroll
           for (int w = 0; w < EPL / 2; ++w) {
             const uint32_t v0 = dw4(vc[i], w), v1 = dw4(vc[i + 1], w);
@@ -422,7 +395,6 @@ decode_split_kernel(const DecodeKernelArgs a) {
               acc[h][2 * w + 1] = dot2_bf16(pp[h], hi, acc[h][2 * w + 1]);
             }
           }
-        }
       }
     } else {
 #pragma unroll
@@ -931,9 +903,12 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
   const auto fill4 = a.fill4 ? as_const_as(a.fill4) : nullptr;
   bool bad = false;
 
-  // K and V of the block whose table word is w into ring slot SL; returns the
-  // block's (offset << 16 | fill count)
-  auto issue = [&](uint32_t w, auto slc) -> uint32_t {
+  // K and V of the block whose table word is w into ring slot SL.  Returns the
+  // block's offset << 16 | the bit position of its fill count in fw, the
+  // 32-bit word of the fill array that holds it (all ones without an array).
+  // The count is extracted when the block is computed, two steps later, so
+  // its scalar load is never waited for here.
+  auto issue = [&](uint32_t w, uint32_t &fw, auto slc) -> uint32_t {
     constexpr int SL = decltype(slc)::value;
     uint32_t id = word_block(w);
     if (id >= (uint32_t)a.num_blocks) {
@@ -947,8 +922,8 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
       lds_dma16(kg, ld_off[i], ring_lds + (SL * 2) * BLKB + i * 1024);
       lds_dma16(vg, ld_off[i], ring_lds + (SL * 2 + 1) * BLKB + i * 1024);
     }
-    const uint32_t fill = fill4 ? (fill4[id >> 2] >> ((id & 3u) * 8u)) & 0xffu : (uint32_t)kBlockTokens;
-    return (w & 0xffff0000u) | fill;
+    fw = fill4 ? fill4[id >> 2] : 0xffffffffu;
+    return (w & 0xffff0000u) | ((id & 3u) * 8u);
   };
 
   f32x4_t O[8];
@@ -959,13 +934,13 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
 
   // this wave takes blocks blk0 + wave, + 4, ...; slots alternate
   int blk = blk0 + wave;
-  uint32_t meta0 = 0, meta1 = 0;
-  if (blk < blk1) meta0 = issue(trow[blk], std::integral_constant<int, 0>{});
-  if (blk + kDecodeWaves < blk1) meta1 = issue(trow[blk + kDecodeWaves], std::integral_constant<int, 1>{});
+  uint32_t meta0 = 0, meta1 = 0, fw0 = 0, fw1 = 0;
+  if (blk < blk1) meta0 = issue(trow[blk], fw0, std::integral_constant<int, 0>{});
+  if (blk + kDecodeWaves < blk1) meta1 = issue(trow[blk + kDecodeWaves], fw1, std::integral_constant<int, 1>{});
   // table word of the block two steps ahead, loaded one step before its DMA
   uint32_t wpre = blk + 2 * kDecodeWaves < blk1 ? trow[blk + 2 * kDecodeWaves] : 0u;
 
-  auto step = [&](uint32_t &meta, auto slc) {
+  auto step = [&](uint32_t &meta, uint32_t &fw, auto slc) {
     constexpr int SL = decltype(slc)::value;
     // this block's loads have landed (the next block's may still be in flight)
     if (blk + kDecodeWaves < blk1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * IPB) : "memory");
@@ -979,11 +954,12 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) va[c] = lds_read_tr16((const uint16_t *)(vb + v_off[c]));
     const uint32_t mcur = meta;
+    const uint32_t fcur = (fw >> (mcur & 31u)) & 0xffu;  // fill count (255: no array)
     // refill the slot with the block two steps ahead once the reads are done
     const int bfar = blk + 2 * kDecodeWaves;
     if (bfar < blk1) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      meta = issue(wpre, slc);
+      meta = issue(wpre, fw, slc);
       wpre = bfar + kDecodeWaves < blk1 ? trow[bfar + kDecodeWaves] : 0u;
     }
 
@@ -1004,7 +980,7 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) sv[j] = fmaf(slope2, base + (float)j, sv[j]);
     }
-    const int nvalid = min(seq_len - blk * kBlockTokens, (int)(mcur & 0xffffu));
+    const int nvalid = min(seq_len - blk * kBlockTokens, (int)fcur);
     if (nvalid < kBlockTokens) {  // partly filled: mask tokens, zero their V values
       const int nv = nvalid - 4 * g4;  // valid tokens among this lane's 4
 #pragma unroll
@@ -1036,9 +1012,9 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
     blk += kDecodeWaves;
   };
   while (blk < blk1) {
-    step(meta0, std::integral_constant<int, 0>{});
+    step(meta0, fw0, std::integral_constant<int, 0>{});
     if (blk >= blk1) break;
-    step(meta1, std::integral_constant<int, 1>{});
+    step(meta1, fw1, std::integral_constant<int, 1>{});
   }
 
   // this wave's (max, sum, output): sums over the four lane groups; the
@@ -1225,7 +1201,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_mma16_kernel<G, MODE>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave), 0, stream,
                        k);
   else
-    hipLaunchKernelGGL((decode_split_kernel<T, D, G, MODE, F8>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave),
+    hipLaunchKernelGGL((decode_split_kernel<T, D, G, MODE>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave),
                        0, stream, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k.max_splits <= 1) return e;
