@@ -1061,35 +1061,36 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
 }
 
 // Merge the per-split partials of one (sequence, KV head): log-sum-exp weights.
+// One workgroup per (sequence, query head), one thread per output element, so
+// that every partial is read by a single round of independent loads.
 template <typename T, int D, int G>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(D)
 decode_combine_kernel(const DecodeKernelArgs a) {
   using E = Elem<T>;
-  const int g = blockIdx.x;
+  const int h = blockIdx.x % G;
+  const int g = blockIdx.x / G;
   const int b = blockIdx.y;
+  const int d = threadIdx.x;
   const int hkv = a.num_kv_heads;
   const int seq_len = a.seq_lens[b];
   if (seq_len < 0 || seq_len > a.max_blocks * kBlockTokens) return;  // written by the split kernel
   const int nblk = (seq_len + kBlockTokens - 1) / kBlockTokens;
   const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
   if (nsplit <= 1) return;
-  T *out = (T *)a.out + ((size_t)b * hkv * G + (size_t)g * G) * D;
   const size_t part = ((size_t)b * hkv + g) * a.max_splits;
-  const float *po = a.ws_o + part * G * D;
-  const float2 *pml = a.ws_ml + part * G;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int h = i / D;
-    float mx = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, pml[sp * G + h].x);
-    float o = 0.f, lsum = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float2 ml = pml[sp * G + h];
-      const float f = fast_exp2(ml.x - mx);
-      o = fmaf(po[(size_t)sp * G * D + i], f, o);
-      lsum = fmaf(ml.y, f, lsum);
-    }
-    E::store(out, i, lsum != 0.f ? o / lsum * a.out_scale : 0.f);
+  const float *po = a.ws_o + (part * G + h) * D + d;
+  const float2 *pml = a.ws_ml + part * G + h;
+  float mx = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, pml[sp * G].x);
+  float o = 0.f, lsum = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float2 ml = pml[sp * G];
+    const float f = fast_exp2(ml.x - mx);
+    o = fmaf(po[(size_t)sp * G * D], f, o);
+    lsum = fmaf(ml.y, f, lsum);
   }
+  T *out = (T *)a.out + (((size_t)b * hkv + g) * G + h) * D;
+  E::store(out, d, lsum != 0.f ? o / lsum * a.out_scale : 0.f);
 }
 
 // ------------------------------------------------------------------- host side
@@ -1205,8 +1206,8 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
                        0, stream, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k.max_splits <= 1) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D, G>), dim3((unsigned)work_heads, (unsigned)a.batch),
-                     dim3(256), 0, stream, k);
+  hipLaunchKernelGGL((decode_combine_kernel<T, D, G>), dim3((unsigned)(work_heads * G), (unsigned)a.batch),
+                     dim3(D), 0, stream, k);
   return hipGetLastError();
 }
 
