@@ -257,6 +257,28 @@ def fp8_decode_shape(case, d, out, ws, timed):
             "tokens_per_s": round(float(case.layout.total_lens.sum()) / (med * 1e-3), 0)}
 
 
+def fp8_prefill_shape(case, d, out, timed):
+    """Time lazyattn_prefill_fp8 on the case's layout with an 8-bit pool of
+    random E4M3 codes (k_scale 0.25, v_scale 0.125); the prompts' rows are
+    quantised in by kvcache_append_fp8 first."""
+    import torch
+    import position_agnostic_kv_amd as pak
+    import workloads as W
+    shape = tuple(d.k_pool.shape)
+    k8 = W.e4m3_codes_torch(shape, d.k_pool.device, case.seed + 5000)
+    v8 = W.e4m3_codes_torch(shape, d.k_pool.device, case.seed + 6000)
+    pak.kvcache_append_fp8(k8, v8, d.k_new, d.v_new, d.slots, 0.25, 0.125)
+    med, p10, p90 = timed(lambda: pak.lazyattn_prefill_fp8(d.q, d.cu, d.q_pos_start, k8, v8, d.table, d.seq_lens,
+                                                           case.max_q_len, 0.25, 0.125, scale=case.scale,
+                                                           rope_theta=case.rope_theta, out=out))
+    del k8, v8
+    torch.cuda.empty_cache()
+    fl = case.attention_flops()
+    return {"ms_p50": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
+            "tflops": round(fl / (med * 1e-3) / 1e12, 1),
+            "frac_of_bf16_peak": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
 def shapes_main(args):
     """Kernel time of every decode workload (8B, 70B, Zipf mix, 8B with
     documents of any token count, 8B with ALiBi) and of the 8B prefill (RoPE,
@@ -345,6 +367,7 @@ def shapes_main(args):
     res["llama8b_prefill"] = {"ms_p50": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
                               "attention_flops": fl, "tflops": round(fl / (med * 1e-3) / 1e12, 1),
                               "frac_of_bf16_peak": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    res["llama8b_prefill_fp8"] = fp8_prefill_shape(case, d, out, timed)  # the same shape over an 8-bit pool
     import oracle
     tab = torch.from_numpy(W.block_frame_table(case.layout).view(np.int32)).to(dev)
     sl = torch.from_numpy(oracle.alibi_slopes(case.num_q_heads).astype(np.float32)).to(dev)
@@ -385,8 +408,9 @@ SHAPES_DISPATCH_ORDER = {
     "lazyattn::decode_mma16_kernel<8, 0>": ["llama70b_decode"],
     "lazyattn::decode_mma8_kernel<4, 0>": ["llama8b_decode_fp8"],
     "lazyattn::decode_mma8_kernel<8, 0>": ["llama70b_decode_fp8"],
-    "lazyattn::prefill_kernel<128, 4, 0>": ["llama8b_prefill", "llama8b_prefill_ragged"],
-    "lazyattn::prefill_kernel<128, 4, 2>": ["llama8b_prefill_alibi"],
+    "lazyattn::prefill_kernel<128, 4, 0, false>": ["llama8b_prefill", "llama8b_prefill_ragged"],
+    "lazyattn::prefill_kernel<128, 4, 0, true>": ["llama8b_prefill_fp8"],
+    "lazyattn::prefill_kernel<128, 4, 2, false>": ["llama8b_prefill_alibi"],
 }
 PROFILE_STEMS = {
     "llama8b_decode": "decode_llama8b", "zipf_reuse_decode": "decode_zipf",
@@ -394,6 +418,7 @@ PROFILE_STEMS = {
     "llama70b_decode": "decode_llama70b", "llama8b_decode_fp8": "decode_llama8b_fp8",
     "llama70b_decode_fp8": "decode_llama70b_fp8", "llama8b_prefill": "prefill_llama8b",
     "llama8b_prefill_ragged": "prefill_llama8b_ragged", "llama8b_prefill_alibi": "prefill_llama8b_alibi",
+    "llama8b_prefill_fp8": "prefill_llama8b_fp8",
 }
 
 
@@ -413,9 +438,11 @@ def _profile_workload_bytes(name):
         return desc, total
     toks = int(case.layout.total_lens.sum())
     rows = int(case.cu_q_lens[-1])
-    total = toks * case.num_kv_heads * case.head_dim * 2 * 2 + 2 * rows * case.num_q_heads * case.head_dim * 2
+    kv_esz = 1 if name.endswith("_fp8") else 2
+    total = toks * case.num_kv_heads * case.head_dim * 2 * kv_esz + 2 * rows * case.num_q_heads * case.head_dim * 2
     desc = (f"{name}: {case.batch} seqs, {toks} K/V tokens ({rows} prompt rows), {case.num_q_heads} q / "
-            f"{case.num_kv_heads} KV heads, d_h {case.head_dim}, bf16; algorithmic = K+V once + q + out")
+            f"{case.num_kv_heads} KV heads, d_h {case.head_dim}, "
+            f"{'E4M3 pool, bf16 q' if kv_esz == 1 else 'bf16'}; algorithmic = K+V once + q + out")
     return desc, total
 
 
@@ -593,7 +620,7 @@ def activity_summary_main(args):
             alg = None
             if "prefill" in kernel:
                 import workloads as W
-                alg = W.make(name.replace("_alibi", "")).attention_flops()
+                alg = W.make(name.replace("_alibi", "").replace("_fp8", "")).attention_flops()
             lds = mean("SQ_LDS_IDX_ACTIVE")
             lines.append(
                 f"{kernel.replace('lazyattn::', '')} | {name} | {t * 1e6:.1f} | {cyc / t / 1e9:.3f} | "
@@ -870,7 +897,7 @@ def main():
             "algorithmic_bytes": dec_alg_bytes,
         },
         "roofline_prefill": {
-            "kernel": "lazyattn::prefill_kernel<128, 4, 0>",
+            "kernel": "lazyattn::prefill_kernel<128, 4, 0, false>",
             "bound": "mfma",
             "achieved": round(pf_tflops, 2),
             "peak": BF16_PEAK_TFLOPS,

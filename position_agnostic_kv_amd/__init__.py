@@ -23,7 +23,7 @@ __all__ = [
     "LazyAttnError", "lib_path", "load_library", "version", "kvcache_append",
     "decode_workspace_size", "lazyattn_decode", "lazyattn_prefill", "lazyattn_decode_eager",
     "lazyattn_prefill_eager", "lazyattn_decode_alibi", "lazyattn_prefill_alibi", "kvcache_append_fp8",
-    "lazyattn_decode_fp8", "BLOCK_TOKENS",
+    "lazyattn_decode_fp8", "lazyattn_prefill_fp8", "BLOCK_TOKENS",
 ]
 
 BLOCK_TOKENS = 16
@@ -58,6 +58,8 @@ _SIGNATURES["lazyattn_prefill_eager"] = _SIGNATURES["lazyattn_prefill"]
 _SIGNATURES["kvcache_append_fp8"] = (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _f32, _f32, _vp])
 _SIGNATURES["lazyattn_decode_fp8"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                              _i32, _f32, _f32, _f32, _f32, _i32, _vp, _sz, _vp])
+_SIGNATURES["lazyattn_prefill_fp8"] = (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
+                                              _i32, _i32, _i32, _i32, _f32, _f32, _f32, _f32, _vp])
 
 
 class LazyAttnError(RuntimeError):
@@ -323,8 +325,19 @@ def lazyattn_prefill_alibi(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_tabl
                     kv_lens, max_q_len, scale, None, out, stream, slopes=slopes, block_fill=block_fill)
 
 
+def lazyattn_prefill_fp8(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len,
+                         k_scale, v_scale, *, scale=None, rope_theta=10000.0, out=None, stream=None,
+                         block_fill=None):
+    """lazyattn_prefill over an 8-bit pool of E4M3 codes (uint8 or
+    float8_e4m3fn) written by kvcache_append_fp8: keys are decode(code) *
+    k_scale, values decode(code) * v_scale.  q and out are bf16; head_dim 128."""
+    return _prefill("lazyattn_prefill_fp8", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                    kv_lens, max_q_len, scale, rope_theta, out, stream, block_fill=block_fill,
+                    kv_scales=(float(k_scale), float(v_scale)))
+
+
 def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len, scale,
-             rope_theta, out, stream, slopes=None, block_fill=None):
+             rope_theta, out, stream, slopes=None, block_fill=None, kv_scales=None):
     dev = _dev(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens)
     for t, n in ((cu_q_lens, "cu_q_lens"), (q_pos_start, "q_pos_start"), (kv_lens, "kv_lens"),
                  (block_table, "block_table")):
@@ -334,7 +347,10 @@ def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens
     b = kv_lens.numel()
     if bt != BLOCK_TOKENS or dk != d or v_pool.shape != k_pool.shape:
         raise LazyAttnError("pools must be [num_blocks, num_kv_heads, 16, head_dim]")
-    if q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
+    if kv_scales is not None:
+        if q.dtype != torch.bfloat16 or k_pool.dtype not in _POOL8 or v_pool.dtype != k_pool.dtype:
+            raise LazyAttnError("8-bit pools (uint8 or float8_e4m3fn) take bf16 queries")
+    elif q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
         raise LazyAttnError("q and pools must share a dtype")
     if cu_q_lens.numel() != b + 1 or q_pos_start.numel() != b or block_table.dim() != 2 \
             or block_table.shape[0] != b:
@@ -354,6 +370,12 @@ def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens
                                 _ptr(v_pool), _ptr(block_table), block_table.shape[1], fill, _ptr(kv_lens),
                                 _ptr(slopes), b, int(max_q_len), hq, hkv, d, nb, _dtype_code(q), scale,
                                 _stream_ptr(stream, dev)), fn)
+        return out
+    if kv_scales is not None:
+        _check(getattr(lib, fn)(_ptr(out), _ptr(q), tq, _ptr(cu_q_lens), _ptr(q_pos_start), _ptr(k_pool),
+                                _ptr(v_pool), _ptr(block_table), block_table.shape[1], fill, _ptr(kv_lens),
+                                b, int(max_q_len), hq, hkv, d, nb, scale, float(rope_theta), kv_scales[0],
+                                kv_scales[1], _stream_ptr(stream, dev)), fn)
         return out
     _check(getattr(lib, fn)(_ptr(out), _ptr(q), tq, _ptr(cu_q_lens), _ptr(q_pos_start), _ptr(k_pool),
                             _ptr(v_pool), _ptr(block_table), block_table.shape[1], fill, _ptr(kv_lens),

@@ -183,8 +183,11 @@ static int prefill_common(void *out, const void *q, int total_q, const int32_t *
                           const uint8_t *block_fill, const int32_t *kv_lens,
                           int batch, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
                           int num_blocks, int dtype, float scale, float rope_theta, void *stream,
-                          int mode, const float *slopes) {
+                          int mode, const float *slopes, bool pool8 = false, float k_scale = 1.f,
+                          float v_scale = 1.f) {
   if (dtype != LAZYATTN_BF16) return LAZYATTN_ERR_DTYPE;
+  if (pool8 && (head_dim != 128 || !valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
+    return LAZYATTN_ERR_SHAPE;
   if (batch < 0 || batch > 65535 || max_q_len < 0 || max_q_len > LAZYATTN_MAX_POSITION + 1 || total_q < 0 ||
       num_kv_heads < 1 || num_kv_heads > 65535 || num_q_heads < 1 || num_q_heads % num_kv_heads ||
       num_q_heads / num_kv_heads > 64)
@@ -220,6 +223,9 @@ static int prefill_common(void *out, const void *q, int total_q, const int32_t *
   a.mode = mode;
   a.slopes = slopes;
   a.block_fill = block_fill;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  if (pool8) return from_hip(launch_prefill_fp8(a, (hipStream_t)stream));
   return from_hip(launch_prefill(a, (hipStream_t)stream));
 }
 
@@ -253,6 +259,18 @@ int lazyattn_prefill_alibi(void *out, const void *q, int total_q, const int32_t 
   return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
                         max_blocks_per_seq, block_fill, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
                         head_dim, num_blocks, dtype, scale, 10000.0f /* unused */, stream, kAlibi, slopes);
+}
+
+int lazyattn_prefill_fp8(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                         const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                         const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
+                         const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads, int num_kv_heads,
+                         int head_dim, int num_blocks, float scale, float rope_theta, float k_scale,
+                         float v_scale, void *stream) {
+  return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                        max_blocks_per_seq, block_fill, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
+                        head_dim, num_blocks, LAZYATTN_BF16, scale, rope_theta, stream, kRopeLazy, nullptr,
+                        true, k_scale, v_scale);
 }
 
 }  // extern "C"

@@ -57,6 +57,14 @@ __device__ __forceinline__ float max4_mfma(float a, float b, float c, float d) {
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
+// Two OCP E4M3 codes (bytes 0-1, or 2-3 with HI) of a word -> a packed bf16
+// pair (v_cvt_scalef32_pk_bf16_fp8 with scale 1: exact, every E4M3 value is
+// a bf16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 // Dword w (a compile-time constant after unrolling) of a 16-byte chunk.
 __device__ __forceinline__ uint32_t dw4(const uint4 &v, int w) {
   return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;

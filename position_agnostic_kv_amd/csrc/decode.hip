@@ -94,12 +94,6 @@ struct DecodeKernelArgs {
   float out_scale;   // V scale of an 8-bit pool (1 otherwise)
 };
 
-// Two E4M3 codes (bytes 0-1, or 2-3 with HI) of a word -> a packed bf16 pair.
-template <bool HI>
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
-}
-
 // MODE kRopeEager: the non-lazy baseline the method is measured against.  The
 // pool then holds keys already rotated to their absolute positions (the eager,
 // position-adjusted copy), table offsets are ignored, and the query is rotated

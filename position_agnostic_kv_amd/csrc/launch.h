@@ -68,7 +68,9 @@ struct PrefillArgs {
   const float *slopes;  // ALiBi slopes [num_q_heads] (device), else unused
   const uint8_t *block_fill;  // per-block fill counts, or nullptr (all full)
   int mode;             // PosMode
+  float k_scale = 1.f, v_scale = 1.f;  // 8-bit pools: value = code * scale
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_prefill_fp8(const PrefillArgs &a, hipStream_t stream);
 
 }  // namespace lazyattn

@@ -60,6 +60,7 @@ struct PrefillKernelArgs {
   int tok_tiles;    // token tiles per sequence
   int num_units;    // batch * num_kv_heads * head_groups
   float scale_log2, rope_theta;
+  float out_scale;  // V scale of an 8-bit pool (1 otherwise)
 };
 
 // HP query heads of one KV head share a workgroup: rows = HP heads x (128 / HP)
@@ -81,7 +82,19 @@ struct PrefillKernelArgs {
 // bias slope_h * (p - n).  Runs are cut only at 4 blocks, and the tiles are
 // walked from the last visible block back to the first, so that each row meets
 // its largest biases first and the reference below rarely has to move.
-template <int D, int HP, int MODE>
+//
+// F8: the pools hold 8-bit (E4M3) codes in the lane order of the matrix-core
+// decode (per (block, KV head) 2 KiB: byte 1024 i + 16 l + x, l = 16 g + t,
+// holds K[t][32 g + 16 i + x] and V[4 g + x % 4][16 (4 i + x / 4) + t]).
+// Wave w DMAs the 2 KiB of K codes and the 2 KiB of V codes of its block of
+// the next tile (1 KiB contiguous per instruction) into the upper halves of
+// its own 4 KiB regions of the next tile's K and V buffers.  At the start of
+// the next step it reads them into registers, widens them exactly to bf16 and
+// writes the block in place, in the same swizzled row-major layout the bf16
+// pool's DMA produces; everything after that is the bf16 kernel.  (Holding the
+// codes in registers across a step would spill.)  The K scale is folded into the rotated query, the
+// V scale into the final normalisation.
+template <int D, int HP, int MODE, bool F8 = false>
 __global__ void __launch_bounds__(kPfWaves * kWave, 2)
 prefill_kernel(const PrefillKernelArgs a) {
   constexpr int KC = D / 32;          // 32-dim k-chunks of the QK product
@@ -96,6 +109,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   constexpr int WPH = kPfWaves / HP;  // waves per head
   static_assert(D == 64 || D == 128, "head_dim must be 64 or 128");
   static_assert(HP == 1 || HP == 2 || HP == 4, "1, 2 or 4 heads per workgroup");
+  static_assert(!F8 || (D == 128 && MODE == kRopeLazy), "8-bit pools: head_dim 128, lazy RoPE");
   constexpr bool ALIBI = MODE == kAlibi;
   constexpr bool NOCUT = MODE != kRopeLazy;  // runs ignore offsets
 
@@ -205,6 +219,18 @@ prefill_kernel(const PrefillKernelArgs a) {
       s_bad = 1;
       id = 0;
     }
+    if constexpr (F8) {  // the block's codes, into the upper half of its region
+      const uint8_t *kr = (const uint8_t *)a.k_pool + ((size_t)id * hkv + g) * 2048;
+      const uint8_t *vr = (const uint8_t *)a.v_pool + ((size_t)id * hkv + g) * 2048;
+      const int half = (wave * kBlockTokens + kBlockTokens / 2) * D;  // element offset
+      const uint32_t kd = (uint32_t)(uintptr_t)(lds_ptr_t)(&sK[BUF][half]);
+      const uint32_t vd = (uint32_t)(uintptr_t)(lds_ptr_t)(&sV[BUF][half]);
+      lds_dma16(kr, (uint32_t)(16 * lane), kd);
+      lds_dma16(kr, (uint32_t)(1024 + 16 * lane), kd + 1024);
+      lds_dma16(vr, (uint32_t)(16 * lane), vd);
+      lds_dma16(vr, (uint32_t)(1024 + 16 * lane), vd + 1024);
+      return;
+    }
     const char *kg = (const char *)a.k_pool + ((size_t)id * hkv + g) * (kBlockTokens * ROWB);
     const char *vg = (const char *)a.v_pool + ((size_t)id * hkv + g) * (kBlockTokens * ROWB);
 #pragma unroll
@@ -212,6 +238,62 @@ prefill_kernel(const PrefillKernelArgs a) {
       const int dst = (wave * kBlockTokens + i * RPI) * D;  // wave-uniform row base
       lds_dma16(kg, ld_off[i], (uint32_t)(uintptr_t)(lds_ptr_t)(&sK[BUF][dst]));
       lds_dma16(vg, ld_off[i], (uint32_t)(uintptr_t)(lds_ptr_t)(&sV[BUF][dst]));
+    }
+  };
+  // F8, after the codes landed: widen this wave's block and write it into
+  // buffer BUF as the bf16 DMA would have (rows wave*16 + token, 16-byte
+  // chunks swizzled by the row within the block)
+  auto widen_tile = [&](int cnt, auto bufc) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
+    if constexpr (F8) {
+      if (wave >= cnt) return;
+      char *kb = (char *)sK[BUF] + wave * kBlockTokens * ROWB;
+      char *vb = (char *)sV[BUF] + wave * kBlockTokens * ROWB;
+      // every code of the block into registers before the block is rewritten
+      uint4 kraw[2], vraw[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        kraw[i] = *(const uint4 *)(kb + kBlockTokens / 2 * ROWB + 1024 * i + 16 * lane);
+        vraw[i] = *(const uint4 *)(vb + kBlockTokens / 2 * ROWB + 1024 * i + 16 * lane);
+      }
+      // The swizzle swz(r) = ((r & 7) << 1) | ((r >> 3) & 1) written out so that
+      // every store is a per-lane base plus a compile-time offset.
+      // K: code x of chunk i is K[l16][32 lg + 16 i + x]: 16-byte chunk
+      // c = 4 lg + 2 i + u (u = x / 8) of row l16, stored at chunk
+      // c ^ swz(l16) = (u ^ s0) + 2 (i ^ s1) + 4 (lg ^ s23).
+      const int s0 = (l16 >> 3) & 1, s1 = l16 & 1, s23 = (l16 >> 1) & 3;
+      char *krow = kb + l16 * ROWB + 64 * (lg ^ s23);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        uint32_t w[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          w[2 * d] = e4m3x2_to_bf16x2<false>(dw4(kraw[i], d));
+          w[2 * d + 1] = e4m3x2_to_bf16x2<true>(dw4(kraw[i], d));
+        }
+        char *ki = krow + 32 * (i ^ s1);
+        *(uint4 *)(ki + 16 * s0) = make_uint4(w[0], w[1], w[2], w[3]);
+        *(uint4 *)(ki + 16 * (1 ^ s0)) = make_uint4(w[4], w[5], w[6], w[7]);
+      }
+      // V: byte 4 j + k of chunk i is V[4 lg + k][16 (4 i + j) + l16]: row
+      // r = 4 lg + k, 16-byte chunk 8 i + 2 j + (l16 >> 3), element l16 & 7;
+      // with a = lg & 1, b = lg >> 1 the stored chunk is
+      // (h ^ b) + 2 (j ^ k) + 8 (i ^ a), h = l16 >> 3.
+      char *vlane = vb + 4 * lg * ROWB + 16 * ((l16 >> 3) ^ (lg >> 1)) + 2 * (l16 & 7);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        char *vi = vlane + 128 * (i ^ (lg & 1));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = e4m3x2_to_bf16x2<false>(dw4(vraw[i], j));  // k = 0, 1
+          const uint32_t hi = e4m3x2_to_bf16x2<true>(dw4(vraw[i], j));   // k = 2, 3
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t pr = k < 2 ? lo : hi;
+            *(uint16_t *)(vi + k * ROWB + 32 * (j ^ k)) = (uint16_t)((k & 1) ? (pr >> 16) : (pr & 0xffffu));
+          }
+        }
+      }
     }
   };
   // per lane: the fill count of the block whose table word the lane holds
@@ -317,6 +399,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   auto step = [&](auto bufc) -> bool {
     constexpr int BUF = decltype(bufc)::value;
     __builtin_amdgcn_s_waitcnt(0);   // this tile's loads and the next words have landed
+    widen_tile(ccnt, bufc);
     fix_tail(cj, ccnt, cf, bufc);
     // the next tile's fill counts (its words landed above), used when it is current
     const uint32_t nf = load_fill(nw);
@@ -543,7 +626,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   for (int nt = 0; nt < 2; ++nt) {
     const float tot = col_sum4(lsum[nt]);
     // a row with no visible token (fill counts below its own slot) gives 0
-    const float inv = flagged ? __builtin_nanf("") : tot != 0.f ? 1.f / tot : 0.f;
+    const float inv = flagged ? __builtin_nanf("") : tot != 0.f ? a.out_scale / tot : 0.f;
     const int tk = tw0 + nt * 16 + l16;
     if (tk < tok_valid) {
       uint16_t *dst = out + ((size_t)(q0 + tt * TOK + tk) * a.num_q_heads + hq) * D + lg * 4;
@@ -557,7 +640,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   }
 }
 
-template <int D, int HP, int MODE>
+template <int D, int HP, int MODE, bool F8 = false>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   PrefillKernelArgs k;
   k.out = (uint16_t *)a.out;
@@ -580,12 +663,14 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   constexpr int tok = kPfRows / HP;
   k.tok_tiles = (a.max_q_len + tok - 1) / tok;
   k.num_units = a.batch * a.num_kv_heads * k.head_groups;
-  k.scale_log2 = a.scale * kLog2e;
+  k.scale_log2 = a.scale * kLog2e * (F8 ? a.k_scale : 1.f);
+  k.out_scale = F8 ? a.v_scale : 1.f;
   k.rope_theta = a.rope_theta;
   const long long grid = (long long)(k.num_units + kXcds - 1) / kXcds * kXcds * k.tok_tiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D, HP, MODE>), dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream, k);
+  hipLaunchKernelGGL((prefill_kernel<D, HP, MODE, F8>), dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream,
+                     k);
   return hipGetLastError();
 }
 
@@ -605,6 +690,16 @@ static hipError_t launch_prefill_d(const PrefillArgs &a, hipStream_t stream) {
     case kAlibi: return launch_prefill_e<D, kAlibi>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// bf16 queries against 8-bit (E4M3) pools in the decode's lane order, lazy
+// RoPE, head_dim 128.
+hipError_t launch_prefill_fp8(const PrefillArgs &a, hipStream_t stream) {
+  if (a.head_dim != 128 || a.mode != kRopeLazy) return hipErrorInvalidValue;
+  const int group = a.num_q_heads / a.num_kv_heads;
+  if (group % 4 == 0) return launch_prefill_t<128, 4, kRopeLazy, true>(a, stream);
+  if (group % 2 == 0) return launch_prefill_t<128, 2, kRopeLazy, true>(a, stream);
+  return launch_prefill_t<128, 1, kRopeLazy, true>(a, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {

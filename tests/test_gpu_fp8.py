@@ -1,12 +1,15 @@
-"""GPU parity of the 8-bit KV pool (kvcache_append_fp8, lazyattn_decode_fp8)
-against the E4M3 oracle.  Pools hold random E4M3 byte patterns (every
+"""GPU parity of the 8-bit KV pool (kvcache_append_fp8, lazyattn_decode_fp8,
+lazyattn_prefill_fp8) against the E4M3 oracle.  Pools hold random E4M3 byte patterns (every
 exponent from subnormal to 2^2, both signs); the step's new rows are bf16 or
 f32 values that the append quantises, bit for bit as the oracle does,
 including saturation, subnormals, signed zero, infinities and NaN.  The
 device pools hold the codes in the library's lane order; the tests move host
 codes into it and back with the index permutation the header documents.  Decode
 covers GQA 4, GQA 8 (two workgroups per KV head), a 32-query-head group,
-split-K, random offsets and documents of any length (fill counts)."""
+split-K, random offsets and documents of any length (fill counts); prefill
+covers GQA 1 to 8, multi-query, random offsets, a prompt with no cached
+document, documents of any length, and bit-equality with the bf16 prefill on
+the dequantised pool."""
 
 import numpy as np
 import pytest
@@ -200,3 +203,87 @@ def test_full_size_decode_fp8_sampled(name):
                                                h // g, case.scale, case.rope_theta))
             rows_got.append(got[b, h])
     assert_parity(np.stack(rows_got), np.stack(rows_want), W.BF16, f"{name} fp8 sampled")
+
+
+# ---------------------------------------------------------------- prefill
+def _run_prefill(case, seed, ks, vs):
+    """Append the prompts' rows into an 8-bit pool of random codes, prefill,
+    and return (got, want) with the oracle on the same codes (the append
+    bytes checked exactly on the way)."""
+    W.materialize_numpy(case)
+    kc, vc = _fp8_case(case, seed)
+    dc = DeviceCase(case)
+    k8, v8 = (_u8(x) for x in W.fp8_pools_to_device_order(kc, vc))
+    pak.kvcache_append_fp8(k8, v8, dc.k_new, dc.v_new, dc.slots, ks, vs)
+    out = pak.lazyattn_prefill_fp8(dc.q, dc.cu, dc.q_pos_start, k8, v8, dc.table, dc.seq_lens, case.max_q_len,
+                                   ks, vs, scale=case.scale, rope_theta=case.rope_theta, block_fill=dc.fill)
+    torch.cuda.synchronize()
+    kn, vn = W.to_float(case.k_new, case.dtype), W.to_float(case.v_new, case.dtype)
+    kc2, vc2 = oracle.append_fp8(kc, vc, kn, vn, case.layout.slot_mapping, np.float32(ks), np.float32(vs))
+    gk, gv = W.fp8_pools_from_device_order(k8.cpu().numpy(), v8.cpu().numpy())
+    assert np.array_equal(gk, kc2) and np.array_equal(gv, vc2), "append bytes"
+    want = oracle.prefill_fp8(W.to_float(case.q, case.dtype), case.cu_q_lens, case.layout.tail_pos, kc2, vc2,
+                              case.layout.table, case.seq_lens, case.scale, case.rope_theta, np.float32(ks),
+                              np.float32(vs), block_fill=case.block_fill)
+    return W.to_float(out, case.dtype), want
+
+
+PREFILL = [
+    # Hq, Hkv, cached per sequence, prompt per sequence, doc blocks, offsets, k_scale, v_scale
+    (32, 8, [512, 96], [256, 77], (2, 12), "contiguous", 0.25, 0.125),
+    (64, 8, [1056], [130], (3, 40), "random", 0.25, 0.5),
+    (16, 8, [224, 640], [300, 129], (2, 20), "contiguous", 0.3, 0.07),
+    (8, 8, [320, 48], [150, 31], (2, 10), "random", 0.2, 1.0),
+    (32, 1, [416, 96], [200, 70], (2, 9), "random", 0.2, 0.1),
+    (32, 8, [0, 96], [77, 200], (1, 4), "contiguous", 0.5, 0.25),
+]
+
+
+@pytest.mark.parametrize("hq,hkv,cached,prompt,docs,offs,ks,vs", PREFILL)
+def test_prefill_fp8(hq, hkv, cached, prompt, docs, offs, ks, vs):
+    case = W.prefill_case(241 + hq + hkv, len(prompt), hq, hkv, 128, cached, prompt, docs, offsets=offs)
+    say(f"[fp8 prefill] Hq{hq} Hkv{hkv} cached={cached} prompt={prompt} {offs} k_scale {ks} v_scale {vs}")
+    got, want = _run_prefill(case, 17 + hq, ks, vs)
+    assert_parity(got, want, W.BF16, f"fp8 prefill G{hq // hkv}")
+
+
+def test_prefill_fp8_ragged_documents():
+    case = W.ragged_case(251, "prefill", 3, 32, 8, 128, (2, 5), (1, 600), prompt=(1, 300))
+    say("[fp8 prefill] ragged documents, fill counts")
+    got, want = _run_prefill(case, 19, 0.25, 0.125)
+    assert_parity(got, want, W.BF16, "fp8 prefill ragged")
+
+
+@pytest.mark.parametrize("kind", ["documents", "ragged"])
+def test_prefill_fp8_equals_bf16_prefill_on_dequantised_pool(kind):
+    """Every E4M3 value times a power-of-two scale is a bf16 value, and a
+    power-of-two K scale folded into the rotated query rounds exactly as the
+    unscaled query does, so the 8-bit prefill must equal the bf16 prefill on
+    the dequantised pool bit for bit: this checks the codes' byte order, the
+    swizzle and the widening element by element."""
+    ks, vs = 0.25, 0.5
+    if kind == "ragged":
+        case = W.ragged_case(261, "prefill", 2, 32, 8, 128, (2, 4), (1, 500), prompt=(1, 200))
+    else:
+        case = W.prefill_case(263, 2, 64, 8, 128, [704, 160], [190, 64], (2, 16), offsets="random")
+    say(f"[fp8 prefill == bf16 prefill] {kind}")
+    W.materialize_numpy(case)
+    kc, vc = _fp8_case(case, 23)
+    dc = DeviceCase(case)
+    k8, v8 = (_u8(x) for x in W.fp8_pools_to_device_order(kc, vc))
+    pak.kvcache_append_fp8(k8, v8, dc.k_new, dc.v_new, dc.slots, ks, vs)
+    out8 = pak.lazyattn_prefill_fp8(dc.q, dc.cu, dc.q_pos_start, k8, v8, dc.table, dc.seq_lens, case.max_q_len,
+                                    ks, vs, scale=case.scale, rope_theta=case.rope_theta, block_fill=dc.fill)
+    torch.cuda.synchronize()
+    kc2, vc2 = W.fp8_pools_from_device_order(k8.cpu().numpy(), v8.cpu().numpy())
+
+    def bf16_pool(codes, sc):
+        x = oracle.dequantize(codes, np.float32(sc)).astype(np.float32)
+        bits = W.f32_to_bf16_bits(x)
+        assert np.array_equal(W.bf16_bits_to_f32(bits), x), "dequantised codes are bf16 values"
+        return torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    out16 = pak.lazyattn_prefill(dc.q, dc.cu, dc.q_pos_start, bf16_pool(kc2, ks), bf16_pool(vc2, vs), dc.table,
+                                 dc.seq_lens, case.max_q_len, scale=case.scale, rope_theta=case.rope_theta,
+                                 block_fill=dc.fill)
+    torch.cuda.synchronize()
+    assert torch.equal(out8.view(torch.int16), out16.view(torch.int16))
