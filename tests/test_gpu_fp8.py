@@ -287,3 +287,64 @@ def test_prefill_fp8_equals_bf16_prefill_on_dequantised_pool(kind):
                                  block_fill=dc.fill)
     torch.cuda.synchronize()
     assert torch.equal(out8.view(torch.int16), out16.view(torch.int16))
+
+
+def test_full_size_prefill_fp8_sampled():
+    """The 8B prefill shape over an 8-bit pool at full size, as bench.py
+    --shapes runs it, against the oracle on sampled prompt rows of two
+    sequences.  Pools: random E4M3 bytes drawn on the GPU; the oracle reads
+    the sampled sequences' blocks as generated and appends the prompts itself."""
+    ks, vs = 0.25, 0.125
+    case = W.make("llama8b_prefill")
+    say(f"[full fp8 prefill] B={case.batch} prompt={case.max_q_len} NB={case.layout.num_blocks}")
+    W.materialize_torch(case, DEV)
+    dc = DeviceCase(case)
+    shape = tuple(dc.k_pool.shape)
+    dc.k_pool = dc.v_pool = None
+    case.k_pool = case.v_pool = None
+    torch.cuda.empty_cache()
+    k8 = W.e4m3_codes_torch(shape, DEV, case.seed + 5000)
+    v8 = W.e4m3_codes_torch(shape, DEV, case.seed + 6000)
+    lay = case.layout
+    seqs = [0, 3]
+    ids = []
+    for b in seqs:
+        ids.extend((lay.table[b, :-(-int(case.seq_lens[b]) // 16)] & 0xFFFF).tolist())
+    uniq = np.unique(np.array(ids, dtype=np.int64))
+    remap = {int(x): i for i, x in enumerate(uniq)}
+    sel = torch.from_numpy(uniq).to(DEV)
+    kc, vc = W.fp8_pools_from_device_order(k8.index_select(0, sel).cpu().numpy(),
+                                           v8.index_select(0, sel).cpu().numpy())
+    rows, slots = [], []
+    for t, sl in enumerate(lay.slot_mapping.tolist()):
+        if sl >= 0 and sl // 16 in remap:
+            rows.append(t)
+            slots.append(remap[sl // 16] * 16 + sl % 16)
+    r = torch.tensor(rows, device=DEV)
+    kc, vc = oracle.append_fp8(kc, vc, W.to_float(dc.k_new.index_select(0, r), W.BF16),
+                               W.to_float(dc.v_new.index_select(0, r), W.BF16), np.array(slots),
+                               np.float32(ks), np.float32(vs))
+    kf, vf = oracle.dequantize(kc, np.float32(ks)), oracle.dequantize(vc, np.float32(vs))
+    tab = np.zeros((len(seqs), lay.table.shape[1]), dtype=np.uint32)
+    for i, b in enumerate(seqs):
+        for j in range(-(-int(case.seq_lens[b]) // 16)):
+            w = int(lay.table[b, j])
+            tab[i, j] = (w & 0xFFFF0000) | remap[w & 0xFFFF]
+    pak.kvcache_append_fp8(k8, v8, dc.k_new, dc.v_new, dc.slots, ks, vs)
+    out = pak.lazyattn_prefill_fp8(dc.q, dc.cu, dc.q_pos_start, k8, v8, dc.table, dc.seq_lens, case.max_q_len,
+                                   ks, vs, scale=case.scale, rope_theta=case.rope_theta)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    q = W.to_float(case.q, W.BF16)
+    got = W.to_float(out, W.BF16)
+    g = case.num_q_heads // case.num_kv_heads
+    rng = np.random.default_rng(6)
+    qrows = np.array([0, 1, 2, 127, 128, 129, 1023, 1024, 2046, 2047])
+    gots, wants = [], []
+    for i, b in enumerate(seqs):
+        q0 = int(case.cu_q_lens[b])
+        for h in rng.choice(case.num_q_heads, size=3, replace=False).tolist():
+            wants.append(oracle.prefill_rows(q[q0 + qrows, h], qrows, case.max_q_len, int(lay.tail_pos[b]), kf, vf,
+                                             tab[i], int(case.seq_lens[b]), h // g, case.scale, case.rope_theta))
+            gots.append(got[q0 + qrows, h])
+    assert_parity(np.concatenate(gots), np.concatenate(wants), W.BF16, "llama8b_prefill fp8 sampled")
