@@ -1,0 +1,78 @@
+"""The C-ABI calls are stream-ordered and allocate nothing, so a whole step
+(append + decode with split-K partials, append + prefill, and the 8-bit
+pool's append + decode) can be captured in a HIP graph and replayed.  Every
+replay, with eager work on the same stream between replays, must give the
+eager results bit for bit (the kernels are deterministic).  Outputs and the
+decode workspace are allocated before capture; nothing inside the graph
+clears memory with a memset."""
+
+import numpy as np
+import pytest
+import torch
+
+import position_agnostic_kv_amd as pak
+import workloads as W
+from tests.gpu_helpers import DEV, DeviceCase, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return t.view(torch.int16).clone()
+
+
+def test_graph_replays_equal_eager():
+    dcase = W.decode_case(401, 3, 32, 8, 128, [1024, 512, 208], (2, 12), offsets="random")
+    pcase = W.prefill_case(403, 2, 32, 8, 128, [512, 96], [256, 77], (2, 12))
+    for c in (dcase, pcase):
+        W.materialize_numpy(c)
+    dd, pd = DeviceCase(dcase), DeviceCase(pcase)
+    split = 4   # several splits: the combine kernel reads the workspace partials
+    need = pak.decode_workspace_size(dcase.batch, dcase.num_q_heads, dcase.num_kv_heads, dcase.head_dim,
+                                     dcase.layout.table.shape[1], split)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=DEV)
+    dout, pout = torch.empty_like(dd.q), torch.empty_like(pd.q)
+    shape = tuple(dd.k_pool.shape)
+    k8 = W.e4m3_codes_torch(shape, DEV, 11)
+    v8 = W.e4m3_codes_torch(shape, DEV, 12)
+    out8 = torch.empty_like(dd.q)
+
+    def step():
+        pak.kvcache_append(dd.k_pool, dd.v_pool, dd.k_new, dd.v_new, dd.slots)
+        pak.lazyattn_decode(dd.q, dd.q_pos, dd.k_pool, dd.v_pool, dd.table, dd.seq_lens, scale=dcase.scale,
+                            rope_theta=dcase.rope_theta, split_blocks=split, out=dout, workspace=ws)
+        pak.kvcache_append(pd.k_pool, pd.v_pool, pd.k_new, pd.v_new, pd.slots)
+        pak.lazyattn_prefill(pd.q, pd.cu, pd.q_pos_start, pd.k_pool, pd.v_pool, pd.table, pd.seq_lens,
+                             pcase.max_q_len, scale=pcase.scale, rope_theta=pcase.rope_theta, out=pout)
+        pak.kvcache_append_fp8(k8, v8, dd.k_new, dd.v_new, dd.slots, 0.25, 0.125)
+        pak.lazyattn_decode_fp8(dd.q, dd.q_pos, k8, v8, dd.table, dd.seq_lens, 0.25, 0.125, scale=dcase.scale,
+                                rope_theta=dcase.rope_theta, split_blocks=split, out=out8, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    want = [_bits(dout), _bits(pout), _bits(out8)]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up on the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        for t in (dout, pout, out8):
+            t.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [_bits(dout), _bits(pout), _bits(out8)]
+        say(f"[graph] replay {r}")
+        for name, g, w in zip(("decode", "prefill", "decode fp8"), got, want):
+            assert torch.equal(g, w), f"replay {r}: {name} differs from the eager step"
+        # eager work between replays, on the same buffers
+        step()
+        torch.cuda.synchronize()
+        assert all(torch.equal(_bits(t), w) for t, w in zip((dout, pout, out8), want))
+    assert np.isfinite(W.to_float(dout, W.BF16)).all()
