@@ -278,19 +278,28 @@ prefill_kernel(const PrefillKernelArgs a) {
       // V: byte 4 j + k of chunk i is V[4 lg + k][16 (4 i + j) + l16]: row
       // r = 4 lg + k, 16-byte chunk 8 i + 2 j + (l16 >> 3), element l16 & 7;
       // with a = lg & 1, b = lg >> 1 the stored chunk is
-      // (h ^ b) + 2 (j ^ k) + 8 (i ^ a), h = l16 >> 3.
-      char *vlane = vb + 4 * lg * ROWB + 16 * ((l16 >> 3) ^ (lg >> 1)) + 2 * (l16 & 7);
+      // (h ^ b) + 2 (j ^ k) + 8 (i ^ a), h = l16 >> 3.  Lanes 2m and 2m + 1
+      // hold dims 2m and 2m + 1 of the same rows, so after one swap between
+      // them the even lane writes rows k = 0, 1 and the odd lane rows k = 2, 3
+      // as 4-byte words of both dims (p = lane parity, k = kk + 2 p).
+      const int p = l16 & 1;
+      char *vlane = vb + (4 * lg + 2 * p) * ROWB + 16 * ((l16 >> 3) ^ (lg >> 1)) + 2 * (l16 & 6);
+      const uint32_t sel0 = p ? 0x01000504u : 0x05040100u;  // row kk = 0: (dim 2m, dim 2m + 1)
+      const uint32_t sel1 = p ? 0x03020706u : 0x07060302u;  // row kk = 1
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        char *vi = vlane + 128 * (i ^ (lg & 1));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = e4m3x2_to_bf16x2<false>(dw4(vraw[i], j));  // k = 0, 1
-          const uint32_t hi = e4m3x2_to_bf16x2<true>(dw4(vraw[i], j));   // k = 2, 3
+          // keep: this lane's codes of rows 2 p, 2 p + 1; send: the other two
+          const uint32_t rot = __builtin_amdgcn_alignbit(dw4(vraw[i], j), dw4(vraw[i], j), 16 * p);
+          const uint32_t keep = e4m3x2_to_bf16x2<false>(rot);
+          const uint32_t send = e4m3x2_to_bf16x2<true>(rot);
+          const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, kDppQuadXor1, 0xf, 0xf, false);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t pr = k < 2 ? lo : hi;
-            *(uint16_t *)(vi + k * ROWB + 32 * (j ^ k)) = (uint16_t)((k & 1) ? (pr >> 16) : (pr & 0xffffu));
+          for (int kk = 0; kk < 2; ++kk) {
+            const int t = j ^ kk;   // chunk term 32 (t ^ 2 p) = 32 (t & 1) + 64 ((t >> 1) ^ p)
+            char *vi = vlane + 128 * (i ^ (lg & 1)) + 64 * ((t >> 1) ^ p);
+            *(uint32_t *)(vi + kk * ROWB + 32 * (t & 1)) = __builtin_amdgcn_perm(other, keep, kk ? sel1 : sel0);
           }
         }
       }
