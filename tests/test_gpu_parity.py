@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import oracle
+import position_agnostic_kv_amd as pak
 import workloads as W
 from tests.gpu_helpers import (DeviceCase, assert_parity, host_pools_after_append, oracle_decode,
                                oracle_prefill, say)
@@ -257,12 +258,15 @@ def test_incremental_decode_matches_prefill_rows():
 
 
 # ------------------------------------------------------- full-size workloads
-def _gather(dc, case, seqs):
+def _gather(dc, case, seqs, table=None):
     """Oracle pools for the sampled sequences: host copies of the blocks they
     use, taken from the generated pools BEFORE the library's append, ids
     remapped, then the step's new rows that land there written by the
-    oracle's own append.  Returns (k, v, remapped table rows)."""
+    oracle's own append.  `table`: the table rows the kernel reads (the
+    layout's by default).  Returns (k, v, remapped table rows, the blocks'
+    fill counts under the new ids or None)."""
     lay = case.layout
+    src = lay.table if table is None else table
     ids = []
     for b in seqs:
         nb = -(-int(case.seq_lens[b]) // 16)
@@ -285,12 +289,13 @@ def _gather(dc, case, seqs):
     for i, b in enumerate(seqs):
         nb = -(-int(case.seq_lens[b]) // 16)
         for j in range(nb):
-            w = int(lay.table[b, j])
+            w = int(src[b, j])
             tab[i, j] = (w & 0xFFFF0000) | remap[w & 0xFFFF]
-    return kp, vp, tab
+    fill = None if case.block_fill is None else np.asarray(case.block_fill)[uniq]
+    return kp, vp, tab, fill
 
 
-@pytest.mark.parametrize("name", ["llama8b_decode", "llama70b_decode", "zipf_reuse_decode"])
+@pytest.mark.parametrize("name", ["llama8b_decode", "llama70b_decode", "zipf_reuse_decode", "llama8b_decode_ragged"])
 def test_full_size_decode_sampled(name):
     case = W.make(name)
     say(f"[full decode] {name} B={case.batch} NB={case.layout.num_blocks}")
@@ -298,7 +303,7 @@ def test_full_size_decode_sampled(name):
     dc = DeviceCase(case)
     rng = np.random.default_rng(3)
     seqs = sorted(rng.choice(case.batch, size=min(4, case.batch), replace=False).tolist())
-    kp, vp, tab = _gather(dc, case, seqs)   # generated pools + the oracle's append
+    kp, vp, tab, fill = _gather(dc, case, seqs)   # generated pools + the oracle's append
     dc.append()
     out = dc.decode()  # automatic split, as bench.py runs it
     torch.cuda.synchronize()
@@ -310,7 +315,7 @@ def test_full_size_decode_sampled(name):
     for i, b in enumerate(seqs):
         for h in rng.choice(case.num_q_heads, size=3, replace=False).tolist():
             want = oracle.decode_one(q[b, h], int(case.q_pos[b]), kp, vp, tab[i], int(case.seq_lens[b]),
-                                     h // g, case.scale, case.rope_theta)
+                                     h // g, case.scale, case.rope_theta, block_fill=fill)
             rows_got.append(got[b, h])
             rows_want.append(want)
     assert_parity(np.stack(rows_got), np.stack(rows_want), case.dtype, f"{name} sampled")
@@ -329,14 +334,15 @@ def test_full_size_append_bit_exact_sampled():
         assert torch.equal(dc.v_pool[s // 16, :, s % 16], dc.v_new[t])
 
 
-def test_full_size_prefill_sampled():
-    case = W.make("llama8b_prefill")
-    say(f"[full prefill] B={case.batch} prompt={case.max_q_len}")
+@pytest.mark.parametrize("name", ["llama8b_prefill", "llama8b_prefill_ragged"])
+def test_full_size_prefill_sampled(name):
+    case = W.make(name)
+    say(f"[full prefill] {name} B={case.batch} prompt={case.max_q_len}")
     W.materialize_torch(case, "cuda:0")
     dc = DeviceCase(case)
     rng = np.random.default_rng(4)
     seqs = [0, 3]
-    kp, vp, tab = _gather(dc, case, seqs)   # generated pools + the oracle's append
+    kp, vp, tab, fill = _gather(dc, case, seqs)   # generated pools + the oracle's append
     dc.append()
     out = dc.prefill()
     torch.cuda.synchronize()
@@ -351,7 +357,31 @@ def test_full_size_prefill_sampled():
         for h in rng.choice(case.num_q_heads, size=3, replace=False).tolist():
             want = oracle.prefill_rows(q[q0 + rows, h], rows, case.max_q_len, int(case.layout.tail_pos[b]),
                                        kp, vp, tab[i], int(case.seq_lens[b]), h // g, case.scale,
-                                       case.rope_theta)
+                                       case.rope_theta, block_fill=fill)
             gots.append(got[q0 + rows, h])
             wants.append(want)
-    assert_parity(np.concatenate(gots), np.concatenate(wants), case.dtype, "llama8b_prefill sampled")
+    assert_parity(np.concatenate(gots), np.concatenate(wants), case.dtype, f"{name} sampled")
+
+
+def test_full_size_decode_alibi_sampled():
+    """The 8B decode inputs read with ALiBi biases (block-frame table words),
+    as bench.py --shapes times them, on 4 sampled sequences (all heads)."""
+    case = W.make("llama8b_decode")
+    say(f"[full decode alibi] B={case.batch}")
+    W.materialize_torch(case, "cuda:0")
+    dc = DeviceCase(case)
+    frame = W.block_frame_table(case.layout)
+    rng = np.random.default_rng(5)
+    seqs = sorted(rng.choice(case.batch, size=4, replace=False).tolist())
+    kp, vp, tab, fill = _gather(dc, case, seqs, table=frame)
+    dc.append()
+    slopes = oracle.alibi_slopes(case.num_q_heads)
+    out = pak.lazyattn_decode_alibi(dc.q, dc.q_pos, dc.k_pool, dc.v_pool,
+                                    torch.from_numpy(frame.view(np.int32)).to("cuda:0"), dc.seq_lens,
+                                    torch.from_numpy(slopes.astype(np.float32)).to("cuda:0"))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    q = W.to_float(case.q, case.dtype)[seqs]
+    want = oracle.decode_alibi(q, case.q_pos[seqs], kp, vp, tab, case.seq_lens[seqs], case.scale,
+                               slopes.astype(np.float32), block_fill=fill)
+    assert_parity(W.to_float(out, case.dtype)[seqs], want, case.dtype, "llama8b_decode alibi sampled")
