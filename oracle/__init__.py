@@ -41,6 +41,7 @@ from .lazy_oracle import (  # noqa: F401
     rope,
     rope_frequencies,
     softmax,
+    relative_rotation_overhead,
     tiled_softmax_dot,
     unpack_block_word,
     valid_slots,

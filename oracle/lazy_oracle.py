@@ -221,6 +221,17 @@ def cache_bytes(layers, heads, head_dim, seq_len, batch, elem_bytes):
     return 2 * layers * heads * head_dim * seq_len * batch * elem_bytes
 
 
+def relative_rotation_overhead(m_rows, n_keys, head_dim):
+    """Extra FLOPs of rotating one staged key tile once by the relative offset,
+    as a fraction of the tile's attention FLOPs ([LA] "Implementação Técnica",
+    Prefilling).  Each of the tile's N x D key elements takes 3 FLOPs in the
+    rotate-half form (x cos - y sin: two products and a sum); Q K^T and P V
+    take 2 * M * N * D FLOPs each for a query tile of M rows."""
+    rotate = 3 * n_keys * head_dim
+    attend = 2 * (2 * m_rows * n_keys * head_dim)
+    return rotate / attend
+
+
 def tiled_softmax_dot(q, keys, values, tile):
     """softmax(q . K^T) V computed tile by tile with a running (max, sum).
 

@@ -362,4 +362,16 @@ def check_cache_bytes_golden(O):
         assert got == c["bytes"], f"{c['name']}: {got} != {c['bytes']}"
 
 
+def check_rotation_overhead_golden(O):
+    """The pages' printed overhead of one relative rotation per tile, and its
+    independence of the key tile's size and the head dimension."""
+    with open(os.path.join(GOLDEN, "rotation_overhead.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        pct = 100.0 * O.relative_rotation_overhead(c["M"], c["N"], c["D"])
+        assert round(pct, c["printed_digits"]) == c["percent"], f"{c['name']}: {pct}"
+        for n, d in ((16, 64), (256, 128), (64, 16)):
+            assert O.relative_rotation_overhead(c["M"], n, d) == O.relative_rotation_overhead(c["M"], c["N"], c["D"])
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

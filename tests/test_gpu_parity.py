@@ -141,6 +141,65 @@ def test_decode_split_and_shuffle_invariance():
     assert np.array_equal(out2, outs[8]), "block shuffle changed the result"
 
 
+def _one_hot_case():
+    """Decode case in which query head kvh * G + 1 of each sequence has
+    scale * |q|^2 ~ 600 and its exact rotation rot(q, n - off1) is stored as
+    slot 5 of the first block (offset off1) and, again, as slot 5 of the first
+    block of another document (offset off2).  Returns (case, picks) with picks
+    (b, h, kv head, block 1, block 2, table column of block 1, of block 2)."""
+    case = W.decode_case(61, 2, 8, 2, 128, [640, 512], (4, 10), new_token=False, kv_std=0.05)
+    W.materialize_numpy(case)
+    lay = case.layout
+    g = case.num_q_heads // case.num_kv_heads
+    picks = []
+    for b in range(case.batch):
+        nb = -(-int(case.seq_lens[b]) // 16)
+        offs = (lay.table[b, :nb] >> 16).astype(np.int64)
+        c1, c2 = 0, int(np.nonzero(offs != offs[0])[0][0])
+        id1, id2 = int(lay.table[b, c1]) & 0xFFFF, int(lay.table[b, c2]) & 0xFFFF
+        for kvh in range(case.num_kv_heads):
+            h = kvh * g + 1
+            qf = W.to_float(case.q[b, h], case.dtype).astype(np.float64)
+            qf *= np.sqrt(600.0 / case.scale) / np.linalg.norm(qf)
+            case.q[b, h] = W.f32_to_bf16_bits(qf.astype(np.float32))
+            qb = W.to_float(case.q[b, h], case.dtype).astype(np.float64)
+            key = oracle.rope(qb[None, :], int(case.q_pos[b]) - int(offs[c1]), case.rope_theta)[0]
+            for blk in (id1, id2):
+                case.k_pool[blk, kvh, 5] = W.f32_to_bf16_bits(key.astype(np.float32))
+            picks.append((b, h, kvh, id1, id2, c1, c2))
+    return case, picks
+
+
+def test_decode_one_hot_dominant_key():
+    """Under the right offsets the matched key's weight is 1 and every other
+    weight underflows to 0, so the output is that token's V bit for bit.  On
+    the oracle, exchanging the two blocks' offsets hands the win to the other
+    copy: the case tells a right offset from a wrong one."""
+    case, picks = _one_hot_case()
+    lay = case.layout
+    say("[one-hot] dominant key under its own offset")
+    kp, vp = W.to_float(case.k_pool, case.dtype), W.to_float(case.v_pool, case.dtype)
+    q = W.to_float(case.q, case.dtype)
+    want = oracle.decode(q, case.q_pos, kp, vp, lay.table, case.seq_lens, case.scale, case.rope_theta)
+    wrong_tab = lay.table.copy()
+    for b, c1, c2 in sorted({(p[0], p[5], p[6]) for p in picks}):   # once per sequence
+        w1, w2 = int(wrong_tab[b, c1]), int(wrong_tab[b, c2])
+        wrong_tab[b, c1] = (w2 & 0xFFFF0000) | (w1 & 0xFFFF)
+        wrong_tab[b, c2] = (w1 & 0xFFFF0000) | (w2 & 0xFFFF)
+    wrong = oracle.decode(q, case.q_pos, kp, vp, wrong_tab, case.seq_lens, case.scale, case.rope_theta)
+    for b, h, kvh, id1, id2, c1, c2 in picks:
+        assert np.abs(want[b, h] - vp[id1, kvh, 5]).max() < 1e-9, "the matched key dominates"
+        assert np.abs(wrong[b, h] - vp[id2, kvh, 5]).max() < 1e-9, "a wrong offset selects the other copy"
+        assert np.abs(vp[id1, kvh, 5] - vp[id2, kvh, 5]).max() > 1e-3
+    dc = DeviceCase(case)
+    for split in (0, 4):
+        out = dc.decode(split_blocks=split)
+        torch.cuda.synchronize()
+        bits = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        for b, h, kvh, id1, id2, c1, c2 in picks:
+            assert np.array_equal(bits[b, h], case.v_pool[id1, kvh, 5]), f"split {split}: seq {b} head {h}"
+
+
 def test_decode_workspace_reuse_and_degenerate_lengths():
     case = W.decode_case(51, 4, 8, 2, 128, [800, 800, 800, 800], (2, 20), dtype=W.F32)
     W.materialize_numpy(case)

@@ -44,6 +44,9 @@ MUTATIONS = {
     "append_wrong_source": [("k_out[slot // BLOCK_TOKENS, :, slot % BLOCK_TOKENS, :] = k_new[t]",
                              "k_out[slot // BLOCK_TOKENS, :, slot % BLOCK_TOKENS, :] = v_new[t]")],
     "cache_bytes_no_kv_factor": [("return 2 * layers * heads", "return layers * heads")],
+    "rotation_two_flops": [("rotate = 3 * n_keys * head_dim", "rotate = 2 * n_keys * head_dim")],
+    "rotation_counts_one_product": [("attend = 2 * (2 * m_rows * n_keys * head_dim)",
+                                     "attend = 2 * m_rows * n_keys * head_dim")],
 }
 
 
