@@ -13,13 +13,13 @@ step by step, without blocking, fusion or reordering:
   "Implementação Técnica" (Prefilling, Decoding), "Equivalência Matemática".
 * [KVF] ai-engineering.academy, "KV Cache, Flash Attention & Otimização de
   Inferência": sections "Flash Attention" (standard attention, running
-  softmax), "PagedAttention", "Construa" (Passo 1 KVCache, Passo 2 tiled
+  softmax), "PagedAttention", "Construa" (Passo 1 KVCache, Passo 2 tile-by-tile
   softmax).
 * [WHY] lynx-cortex, "00 — Por qué existe un KV Cache": sections
   "Lo que hace el decoding autorregresivo", "El remedio", "El precio".
 
 Modules: ``lazy_oracle`` (deferred-RoPE attention, append, cache bytes, the
-tiled softmax), ``alibi_oracle`` (the ALiBi variant), ``quant_oracle`` (a KV
+tile-by-tile softmax), ``alibi_oracle`` (the ALiBi variant), ``quant_oracle`` (a KV
 pool of 8-bit E4M3 floats with one scale per tensor) and ``cache_policy``
 (a plain model of the host pool manager's block and eviction policy).
 
@@ -42,7 +42,8 @@ from .lazy_oracle import (  # noqa: F401
     rope_frequencies,
     softmax,
     relative_rotation_overhead,
-    tiled_softmax_dot,
+    blockwise_softmax_dot,
+    merge_tile_partials,
     unpack_block_word,
     valid_slots,
 )

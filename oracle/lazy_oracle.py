@@ -232,27 +232,47 @@ def relative_rotation_overhead(m_rows, n_keys, head_dim):
     return rotate / attend
 
 
-def tiled_softmax_dot(q, keys, values, tile):
-    """softmax(q . K^T) V computed tile by tile with a running (max, sum).
+def _tile_partial(q, keys, values):
+    """Softmax statistics of one key tile on its own: (m, l, u) with
+    m = max_j s_j, l = sum_j exp(s_j - m), u = sum_j exp(s_j - m) v_j, where
+    s_j = q . k_j.  An empty tile has m = -inf, l = 0, u = 0."""
+    if keys.shape[0] == 0:
+        return -np.inf, 0.0, np.zeros(values.shape[1])
+    scores = keys @ q
+    m = float(np.max(scores))
+    w = np.exp(scores - m)
+    return m, float(np.sum(w)), w @ values
 
-    [KVF] "Construa", Passo 2 and "Flash Attention" (the numerical trick):
-    keep the running max m and running sum s; for each tile of keys, raise m
-    to the tile's max, shrink the old sum and output by exp(m_old - m_new),
-    then add the tile's exponentials.  No scale is applied here, as on the
-    page; callers pre-scale q.
+
+def merge_tile_partials(partials):
+    """Log-sum-exp merge of per-tile (m, l, u) statistics.
+
+    With M = max over tiles of m_t, every tile's terms are brought to the
+    common reference by the factor exp(m_t - M):
+      softmax(s) . V = sum_t exp(m_t - M) u_t / sum_t exp(m_t - M) l_t.
+    Tiles with m_t = -inf (no keys) carry weight 0.
+    """
+    big = max(m for m, _, _ in partials)
+    num = np.zeros_like(partials[0][2])
+    den = 0.0
+    for m, l, u in partials:
+        f = 0.0 if m == -np.inf else float(np.exp(m - big))
+        num = num + f * u
+        den = den + f * l
+    return num / den
+
+
+def blockwise_softmax_dot(q, keys, values, tile):
+    """softmax(q . K^T) V from independent key tiles ([KVF] "Construa",
+    Passo 2, and "Flash Attention": the result of a softmax over all keys can
+    be assembled from tiles seen one at a time).
+
+    Each tile of ``tile`` keys is reduced to (max, sum, unnormalised output)
+    by itself; the partials are then combined by one log-sum-exp merge.  No
+    scale is applied, as on the page; callers pre-scale q.
     """
     q = np.asarray(q, dtype=np.float64)
     keys = np.asarray(keys, dtype=np.float64)
     values = np.asarray(values, dtype=np.float64)
-    m = -np.inf
-    s = 0.0
-    acc = np.zeros(values.shape[1])
-    for start in range(0, keys.shape[0], tile):
-        scores = keys[start:start + tile] @ q
-        m_new = max(m, float(np.max(scores)))
-        shrink = np.exp(m - m_new) if m != -np.inf else 0.0
-        e = np.exp(scores - m_new)
-        s = s * shrink + float(np.sum(e))
-        acc = acc * shrink + e @ values[start:start + tile]
-        m = m_new
-    return acc / s
+    starts = range(0, keys.shape[0], tile)
+    return merge_tile_partials([_tile_partial(q, keys[a:a + tile], values[a:a + tile]) for a in starts])

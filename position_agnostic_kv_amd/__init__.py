@@ -126,6 +126,25 @@ def _stream_ptr(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _hold_temporaries(stream, device, *temps):
+    """Make temporaries safe for a launch on a stream other than torch's current one.
+
+    The binding allocates (and fills) its temporaries -- output, workspace,
+    padded fill counts -- on the current stream.  When the launch goes to
+    another stream, that stream first waits for the current one (so the fills
+    are complete and the memory's previous users are done), and each
+    temporary is recorded as used by it, so that the caching allocator does
+    not hand its memory to new work before the launch has finished."""
+    temps = [t for t in temps if t is not None]
+    if stream is None or not temps:
+        return
+    if stream.cuda_stream == torch.cuda.current_stream(device).cuda_stream:
+        return
+    stream.wait_stream(torch.cuda.current_stream(device))
+    for t in temps:
+        t.record_stream(stream)
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
@@ -255,19 +274,23 @@ def _decode(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, rope_the
     if block_table.dim() != 2 or block_table.shape[0] != b or q_pos.numel() != b or seq_lens.numel() != b:
         raise LazyAttnError("block_table [B, max_blocks], q_pos [B], seq_lens [B]")
     max_blocks = block_table.shape[1]
-    if out is None:
+    new_out = out is None
+    if new_out:
         out = torch.empty_like(q)
     else:
         _dev(out, q)
         if out.shape != q.shape or out.dtype != q.dtype:
             raise LazyAttnError("out must match q")
     need = decode_workspace_size(b, hq, hkv, d, max_blocks, split_blocks) if b else 0
-    if workspace is None:
+    new_ws = workspace is None
+    if new_ws:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _dev(workspace, q)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     fill_keep, fill = _fill_arg(block_fill, nb, dev)
+    _hold_temporaries(stream, dev, out if new_out else None, workspace if new_ws else None,
+                      fill_keep if fill_keep is not block_fill else None)
     lib = load_library()
     if slopes is not None:
         _slopes(slopes, hq, dev)
@@ -355,7 +378,8 @@ def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens
     if cu_q_lens.numel() != b + 1 or q_pos_start.numel() != b or block_table.dim() != 2 \
             or block_table.shape[0] != b:
         raise LazyAttnError("cu_q_lens [B+1], q_pos_start [B], block_table [B, max_blocks], kv_lens [B]")
-    if out is None:
+    new_out = out is None
+    if new_out:
         out = torch.empty_like(q)
     else:
         _dev(out, q)
@@ -363,6 +387,8 @@ def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens
             raise LazyAttnError("out must match q")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     fill_keep, fill = _fill_arg(block_fill, nb, dev)
+    _hold_temporaries(stream, dev, out if new_out else None,
+                      fill_keep if fill_keep is not block_fill else None)
     lib = load_library()
     if slopes is not None:
         _slopes(slopes, hq, dev)

@@ -29,6 +29,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// x, y as bf16 pairs hi + lo: hi = bf16(x), lo = bf16(x - hi) (x - hi is
+// exact in float).  hi + lo is within 2^-17 relative of x, against 2^-9 for
+// hi alone, so a product against hi and lo on the matrix cores carries the
+// float operand almost exactly.
+__device__ __forceinline__ void split_bf16x2(float x, float y, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16x2(x, y);
+  lo = pack_bf16x2(x - bf16_lo(hi), y - bf16_hi(hi));
+}
+
 __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
@@ -86,16 +95,6 @@ __device__ __forceinline__ void rope_cos_sin(int delta, double inv_freq, float &
   sincos((double)delta * inv_freq, &sd, &cd);
   c = (float)cd;
   s = (float)sd;
-}
-
-// Cheaper variant for small angles (|delta * inv_freq| < ~200 rad): the angle is
-// formed and reduced to [-pi, pi] in double, then evaluated in float.
-__device__ __forceinline__ void rope_cos_sin_small(int delta, double inv_freq, float &c, float &s) {
-  const double a = (double)delta * inv_freq;
-  const double k = rint(a * 0.15915494309189535);        // 1 / (2 pi)
-  double r = fma(-k, 6.283185307179586232, a);            // 2 pi, high part
-  r = fma(-k, 2.4492935982947064e-16, r);                 // 2 pi, low part
-  sincosf((float)r, &s, &c);
 }
 
 // ------------------------------------------------------------ cross-lane sums

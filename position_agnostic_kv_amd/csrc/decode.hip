@@ -167,8 +167,9 @@ decode_split_kernel(const DecodeKernelArgs a) {
   const int pd0 = upper ? d0 - HALF : d0 + HALF;
   const double inv_freq = lane < HALF ? rope_inv_freq(lane, D, a.rope_theta) : 0.0;
 
-  // rotated, pre-scaled query slice: packed bf16 pairs (bf16) or floats (f32)
-  uint32_t qp[G][EPL / 2];
+  // rotated, pre-scaled query slice: packed bf16 pairs as hi + lo parts (bf16;
+  // see split_bf16x2), or floats (f32)
+  uint32_t qp[G][EPL / 2], ql[G][kBf16 ? EPL / 2 : 1];
   float qf[G][kBf16 ? 1 : EPL];
   float acc[G][EPL];
   float m[G], l[G];
@@ -215,9 +216,9 @@ decode_split_kernel(const DecodeKernelArgs a) {
   // q' = rot(q, n - off) * scale * log2(e), for this lane's dims and all G heads.
   // Lane i < D/2 evaluates frequency i once; the values are shuffled to the
   // lanes holding dims i and i + D/2.  bf16: the angle is reduced in double to
-  // a fraction of a turn and evaluated with v_cos/v_sin (which take turns): far
-  // below the bf16 rounding of the result, and light on registers (this runs
-  // inside the block loop).  f32: double-precision cos/sin.
+  // a fraction of a turn and evaluated with v_cos/v_sin (which take turns), light
+  // on registers (this runs inside the block loop).  f32: double-precision
+  // cos/sin.
   auto rotate = [&](int delta) {
     float cs = 1.f, sn = 0.f;
     if (lane < HALF) {
@@ -248,7 +249,7 @@ decode_split_kernel(const DecodeKernelArgs a) {
       }
       if constexpr (kBf16) {
 #pragma unroll
-        for (int w = 0; w < EPL / 2; ++w) qp[h][w] = pack_bf16x2(rot[2 * w], rot[2 * w + 1]);
+        for (int w = 0; w < EPL / 2; ++w) split_bf16x2(rot[2 * w], rot[2 * w + 1], qp[h][w], ql[h][w]);
       } else {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) qf[h][e] = rot[e];
@@ -304,6 +305,8 @@ decode_split_kernel(const DecodeKernelArgs a) {
           t = dot2_bf16(qp[h][0], dw4(kc[i], 0), 0.f);
 #pragma unroll
           for (int w = 1; w < EPL / 2; ++w) t = dot2_bf16(qp[h][w], dw4(kc[i], w), t);
+#pragma unroll
+          for (int w = 0; w < EPL / 2; ++w) t = dot2_bf16(ql[h][w], dw4(kc[i], w), t);
         } else {
           t = qf[h][0] * __uint_as_float(dw4(kc[i], 0));
 #pragma unroll
@@ -550,12 +553,12 @@ decode_mma8_kernel(const DecodeKernelArgs a) {
   const bool live = t16 < G;
   const double inv_freq = rope_inv_freq(lane, D, a.rope_theta);  // lane i: frequency i (64 of them)
 
-  bf16x8_t qb[4];
+  bf16x8_t qh[4], ql[4];  // q' as bf16 hi + lo parts (see split_bf16x2)
   f32x4_t O[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < 4; ++c) qb[c] = bf16x8_t{};
+  for (int c = 0; c < 4; ++c) qh[c] = ql[c] = bf16x8_t{};
   float m = kMaxFloor, lsum = 0.f;
 
   const int blk0 = split * a.split_blocks;
@@ -583,7 +586,8 @@ decode_mma8_kernel(const DecodeKernelArgs a) {
   };
 
   // q' = rot(q, n - off) * scale * log2(e) * k_scale for head t16, dims
-  // 32 g4 .. 32 g4 + 31 (frequency d % 64, the pair of dim d is d ^ 64)
+  // 32 g4 .. 32 g4 + 31 (frequency d % 64, the pair of dim d is d ^ 64), as
+  // bf16 hi + lo parts: S takes one product against each
   auto rotate = [&](int delta) {
     const double tt = (double)delta * (inv_freq * 0.15915494309189535);
     const float f = (float)(tt - rint(tt));
@@ -602,10 +606,11 @@ decode_mma8_kernel(const DecodeKernelArgs a) {
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      uint32_t w4[4];
+      uint32_t wh[4], wl[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) w4[k] = pack_bf16x2(r[8 * c + 2 * k], r[8 * c + 2 * k + 1]);
-      qb[c] = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+      for (int k = 0; k < 4; ++k) split_bf16x2(r[8 * c + 2 * k], r[8 * c + 2 * k + 1], wh[k], wl[k]);
+      qh[c] = __builtin_bit_cast(bf16x8_t, make_uint4(wh[0], wh[1], wh[2], wh[3]));
+      ql[c] = __builtin_bit_cast(bf16x8_t, make_uint4(wl[0], wl[1], wl[2], wl[3]));
     }
   };
 
@@ -626,16 +631,17 @@ decode_mma8_kernel(const DecodeKernelArgs a) {
     }
     issue(min(blk + kDecodeWaves, blast), wn, kn, vn);
 
-    // S[token 4 g4 + j][head t16], log2 units
-    f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+    // S[token 4 g4 + j][head t16], log2 units: K q_h^T + K q_l^T
+    f32x4_t S = {0.f, 0.f, 0.f, 0.f}, Sl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t w0 = dw4(kc[c >> 1], 2 * (c & 1)), w1 = dw4(kc[c >> 1], 2 * (c & 1) + 1);
       const uint4 ka = make_uint4(e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
                                   e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1));
-      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qb[c], S, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qh[c], S, 0, 0, 0);
+      Sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), ql[c], Sl, 0, 0, 0);
     }
-    float sv[4] = {S[0], S[1], S[2], S[3]};
+    float sv[4] = {S[0] + Sl[0], S[1] + Sl[1], S[2] + Sl[2], S[3] + Sl[3]};
     const int nvalid = blk < blk1 ? min(seq_len - blk * kBlockTokens, (int)(wcur & 0xffffu)) : 0;
     if (nvalid < kBlockTokens) {  // partly filled or exhausted: mask tokens, zero their V bytes
       const int nv = nvalid - 4 * g4;  // valid tokens among this lane's 4
@@ -829,18 +835,20 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
   }
   const double inv_freq = rope_inv_freq(lane, D, a.rope_theta);  // lane i: frequency i (D/2 = 64 of them)
 
-  // q' = rot(q, delta) * scale * log2(e) in bf16, for head t16.  The lane's
-  // dims d (c = 0, 1) and d + 64 (c + 2) form rotate-half pairs, so the
-  // rotation is lane-local; cos/sin of frequency i come from lane i (angle
-  // reduced in double to a fraction of a turn, then v_cos/v_sin).
-  bf16x8_t qb[4];
+  // q' = rot(q, delta) * scale * log2(e) for head t16, as two bf16 parts
+  // (qh + ql, see split_bf16x2): S takes one product against each, so q' is
+  // not rounded to bf16 (that rounding alone limits wide score spreads).
+  // The lane's dims d (c = 0, 1) and d + 64 (c + 2) form rotate-half pairs,
+  // so the rotation is lane-local; cos/sin of frequency i come from lane i
+  // (angle reduced in double to a fraction of a turn, then v_cos/v_sin).
+  bf16x8_t qh[4], ql[4];
   auto rotate = [&](int delta) {
     const double tt = (double)delta * (inv_freq * 0.15915494309189535);
     const float f = (float)(tt - rint(tt));
     const float cs = __builtin_amdgcn_cosf(f), sn = __builtin_amdgcn_sinf(f);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      uint32_t lo[4], hi[4];
+      uint32_t xh[4], xl[4], yh[4], yl[4];  // dims d (x) and d + 64 (y): hi and lo parts
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         float r[4];
@@ -855,11 +863,13 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
           r[e2] = fmaf(x, cv, -(y * sv)) * a.scale_log2;
           r[2 + e2] = fmaf(y, cv, x * sv) * a.scale_log2;
         }
-        lo[k] = pack_bf16x2(r[0], r[1]);
-        hi[k] = pack_bf16x2(r[2], r[3]);
+        split_bf16x2(r[0], r[1], xh[k], xl[k]);
+        split_bf16x2(r[2], r[3], yh[k], yl[k]);
       }
-      qb[c] = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-      qb[c + 2] = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+      qh[c] = as_bf16x8(make_uint4(xh[0], xh[1], xh[2], xh[3]));
+      ql[c] = as_bf16x8(make_uint4(xl[0], xl[1], xl[2], xl[3]));
+      qh[c + 2] = as_bf16x8(make_uint4(yh[0], yh[1], yh[2], yh[3]));
+      ql[c + 2] = as_bf16x8(make_uint4(yl[0], yl[1], yl[2], yl[3]));
     }
   };
   if constexpr (EAGER) rotate(n_pos);
@@ -964,11 +974,14 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
         cur_off = off;
       }
     }
-    // S[token 4 g4 + j][head t16], log2 units
-    f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+    // S[token 4 g4 + j][head t16], log2 units: K q_h^T + K q_l^T
+    f32x4_t S = {0.f, 0.f, 0.f, 0.f}, Sl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[c]), qb[c], S, 0, 0, 0);
-    float sv[4] = {S[0], S[1], S[2], S[3]};
+    for (int c = 0; c < 4; ++c) {
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[c]), qh[c], S, 0, 0, 0);
+      Sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[c]), ql[c], Sl, 0, 0, 0);
+    }
+    float sv[4] = {S[0] + Sl[0], S[1] + Sl[1], S[2] + Sl[2], S[3] + Sl[3]};
     if constexpr (ALIBI) {  // key position (block offset + slot) - query position
       const float base = (float)(word_offset(mcur) + 4 * g4 - n_pos);
 #pragma unroll

@@ -158,19 +158,19 @@ def check_softmax(O):
     _close(O.softmax(np.array([1.0, 0.0])), [math.e / (1 + math.e), 1 / (1 + math.e)], 1e-16, "2-way")
 
 
-def check_tiled_softmax(O):
+def check_blockwise_softmax(O):
     import scipy.special
     with open(os.path.join(GOLDEN, "tiled_softmax_example.json")) as f:
         g = json.load(f)
     e = math.e
     want = [(e + 3 + 5 * e * e) / (e + 1 + e * e), (2 * e + 4 - e * e) / (e + 1 + e * e)]
     for tile in (1, 2, 4):
-        _close(O.tiled_softmax_dot(g["q"], g["K"], g["V"], tile), want, 1e-14, f"worked example tile={tile}")
+        _close(O.blockwise_softmax_dot(g["q"], g["K"], g["V"], tile), want, 1e-14, f"worked example tile={tile}")
     rng = np.random.default_rng(15)
     q, k, v = rng.standard_normal(16), rng.standard_normal((53, 16)), rng.standard_normal((53, 16))
     one_shot = scipy.special.softmax(k @ q) @ v
     for tile in (1, 3, 4, 16, 53, 60):
-        _close(O.tiled_softmax_dot(q, k, v, tile), one_shot, 1e-13, f"tiled == one-shot tile={tile}")
+        _close(O.blockwise_softmax_dot(q, k, v, tile), one_shot, 1e-13, f"tiled == one-shot tile={tile}")
 
 
 def check_decode_vs_torch_sdpa(O):

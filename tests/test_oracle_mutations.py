@@ -40,7 +40,9 @@ MUTATIONS = {
     "causal_off_by_one": [("<= t[:, None]", "< t[:, None]")],
     "prefill_query_position": [("q_rot = rope(q_rows, q_pos_start + rows, theta)",
                                 "q_rot = rope(q_rows, q_pos_start + rows + 1, theta)")],
-    "tiled_no_rescale": [("acc = acc * shrink + e @ values", "acc = acc + e @ values")],
+    "merge_no_rescale": [("num = num + f * u", "num = num + u")],
+    "merge_sum_unscaled": [("den = den + f * l", "den = den + l")],
+    "tile_partial_max_not_subtracted": [("w = np.exp(scores - m)", "w = np.exp(scores)")],
     "append_wrong_source": [("k_out[slot // BLOCK_TOKENS, :, slot % BLOCK_TOKENS, :] = k_new[t]",
                              "k_out[slot // BLOCK_TOKENS, :, slot % BLOCK_TOKENS, :] = v_new[t]")],
     "cache_bytes_no_kv_factor": [("return 2 * layers * heads", "return layers * heads")],

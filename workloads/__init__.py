@@ -395,6 +395,34 @@ def add_score_shift(case, q_amp, k_cached, k_new, seed=0):
     return case
 
 
+def set_score_spread(case, sigma, v_abs=2.0, seed=0):
+    """Scores that spread widely across keys (host arrays).
+
+    Keys (cached and appended) are redrawn as N(0, sigma^2) per element and
+    values as U(-v_abs, v_abs); with q ~ N(0, 1) and the scale 1/sqrt(D), a
+    query's scores then have standard deviation sigma (natural-log units)
+    across keys.  Bounded values keep the output's own bf16 rounding small
+    next to errors in the scores.  Call after materialize_numpy.
+    """
+    rng = np.random.default_rng(seed + 4000)
+
+    def draw(arr, fn):
+        x = fn(np.shape(arr)).astype(np.float32)
+        return x if case.dtype == F32 else f32_to_bf16_bits(x)
+
+    def k_fn(shape):
+        return rng.standard_normal(shape) * sigma
+
+    def v_fn(shape):
+        return rng.uniform(-v_abs, v_abs, size=shape)
+
+    case.k_pool = draw(case.k_pool, k_fn)
+    case.k_new = draw(case.k_new, k_fn)
+    case.v_pool = draw(case.v_pool, v_fn)
+    case.v_new = draw(case.v_new, v_fn)
+    return case
+
+
 def materialize_torch(case, device):
     """Draw the case's values directly in device memory with torch (seeded).
 
