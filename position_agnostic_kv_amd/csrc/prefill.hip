@@ -3,15 +3,19 @@
 //
 // Method (LazyAttention summary on gist.science, "Implementação Técnica",
 // Prefilling): instead of rotating cached keys twice (back to position 0, then
-// to the target), one relative rotation per tile is applied.  Here the rotation
-// goes on the query tile: a K/V tile is a run of up to four blocks that share
-// one offset, and the query tile is re-rotated by (tile start position - offset)
-// only when that offset changes, i.e. once per document.  Since
+// to the target), one relative rotation per tile is applied.  Since
 // rot(q, n) . rot(k, off) = rot(q, n - off) . k ("Equivalência Matemática"),
 // the scores equal those against the eager position-adjusted keys.  On gfx950
-// the VALU is the scarce unit next to the matrix cores, and this costs
-// 3*M*D FLOPs per document instead of 3*N*D per tile (rotating each staged
-// key tile), with K never re-rounded.
+// the VALU is the scarce unit next to the matrix cores, so the rotation is
+// split between the two operands by cost:
+//   * the query tile is rotated to one offset per K/V tile, and re-rotated
+//     only when that offset changes, i.e. about once per document (3*M*D
+//     FLOPs per document instead of 3*N*D per tile);
+//   * a K/V tile is always four whole blocks, whether or not it straddles a
+//     document boundary; a block whose offset differs from the query's is
+//     rotated once in LDS by the difference (the pages' relative rotation of
+//     a staged tile), by the wave that loaded it.  Tiles are therefore never
+//     cut short at a document's end.
 //
 // Structure (FlashAttention tiling, ai-engineering.academy "Flash
 // Attention"): the query tile stays in registers, K/V tiles are staged through
@@ -75,11 +79,10 @@ struct PrefillKernelArgs {
 //
 // MODE kRopeEager: the non-lazy baseline the method is measured against.  The
 // pool then holds keys already rotated to their absolute positions and table
-// offsets are ignored: every run has offset 0 (runs are cut only at 4 blocks),
-// so the query rows are rotated once, by their own positions, on the first
-// tile.
+// offsets are ignored, so the query rows are rotated once, by their own
+// positions, before the first tile.
 // MODE kAlibi: no rotation; a key at position p (block offset + slot) takes the
-// bias slope_h * (p - n).  Runs are cut only at 4 blocks, and the tiles are
+// bias slope_h * (p - n).  The tiles are
 // walked from the last visible block back to the first, so that each row meets
 // its largest biases first and the reference below rarely has to move.
 //
@@ -111,12 +114,13 @@ prefill_kernel(const PrefillKernelArgs a) {
   static_assert(HP == 1 || HP == 2 || HP == 4, "1, 2 or 4 heads per workgroup");
   static_assert(!F8 || (D == 128 && MODE == kRopeLazy), "8-bit pools: head_dim 128, lazy RoPE");
   constexpr bool ALIBI = MODE == kAlibi;
-  constexpr bool NOCUT = MODE != kRopeLazy;  // runs ignore offsets
+  constexpr bool LAZY = MODE == kRopeLazy;  // table offsets rotate queries and keys
 
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILEB / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILEB / 2];
   __shared__ float s_turn[HALF];                // theta_i / (2 pi): turns per position
-  __shared__ float s_frac[kPfWaves][HALF];       // frac((n0 - off) * turn_i) of the current run
+  __shared__ float s_frac[kPfWaves][HALF];       // frac((n0 - off) * turn_i) of the query offset
+  __shared__ __attribute__((aligned(16))) float2 s_kcs[kPfWaves][HALF];  // (cos, sin) of a key block's relative rotation
   __shared__ int s_bad;
 
   // ---- work item: the token tiles of one (sequence, KV head, head group) run
@@ -203,13 +207,14 @@ prefill_kernel(const PrefillKernelArgs a) {
   auto load_words = [&](int jw) -> uint32_t {
     return (lane < kPfTileBlocks && jw + lane < nblk_vis) ? trow[jw + lane] : 0u;
   };
-  // blocks jw.. that share block jw's offset (1..4), and that offset
+  // the tile starting at block jw: its block count (1..4, never cut at a
+  // document boundary) and the offset the query rows are rotated to for it,
+  // that of its third block (or last, if shorter): a tile that straddles a
+  // boundary takes the offset most of its blocks share, and its other
+  // blocks' keys are rotated by the difference (rotate_keys)
   auto tile_of = [&](uint32_t wv, int jw, int &cnt, int &off) {
-    const uint32_t w0 = __builtin_amdgcn_readfirstlane(wv);
-    off = NOCUT ? 0 : word_offset(w0);
-    const uint64_t same =
-        __ballot(lane < kPfTileBlocks && jw + lane < nblk_vis && (NOCUT || (wv >> 16) == (w0 >> 16)));
-    cnt = __builtin_ctzll(~same);
+    cnt = min(kPfTileBlocks, nblk_vis - jw);
+    off = !LAZY ? 0 : word_offset((uint32_t)__builtin_amdgcn_readlane((int)wv, min(2, cnt - 1)));
   };
   auto issue_tile = [&](uint32_t wv, int cnt, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
@@ -302,6 +307,54 @@ prefill_kernel(const PrefillKernelArgs a) {
             *(uint32_t *)(vi + kk * ROWB + 32 * (t & 1)) = __builtin_amdgcn_perm(other, keep, kk ? sel1 : sel0);
           }
         }
+      }
+    }
+  };
+  // [LA] "Implementação Técnica", Prefilling: one relative rotation of a
+  // staged key block.  After this wave's block of the tile has landed (and,
+  // for 8-bit pools, been widened), if its offset differs from the offset
+  // qoff the query rows are rotated to for this tile, its 16 keys are
+  // rotated in place by (offset - qoff), so that rot(q, n - qoff) .
+  // rot(k, offset - qoff) = rot(q, n - offset) . k ("Equivalência
+  // Matemática").  Lane i < D/2 evaluates frequency i (angle reduced in
+  // double to a fraction of a turn); lane l then takes row l / 4 and the
+  // rotate-half chunk pairs (c, c + CPR/2), c = (l % 4) * PPL + t, whose
+  // 16-byte slots are swizzled alike (slot ^ CPR/2).  The rotated key is
+  // rounded to bf16.  Only blocks at a document boundary take this path.
+  auto rotate_keys = [&](int cnt, int qoff, uint32_t wv, auto bufc) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr int PPL = CPR / 8;  // chunk pairs per lane
+    if constexpr (LAZY) {
+      if (wave >= cnt) return;
+      const int delta = word_offset((uint32_t)__builtin_amdgcn_readlane((int)wv, wave)) - qoff;
+      if (delta == 0) return;
+      if (lane < HALF) {
+        const double t = (double)delta * turn_d;
+        const float f = (float)(t - rint(t));
+        s_kcs[wave][lane] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+      }
+      __builtin_amdgcn_wave_barrier();
+      char *kb = (char *)sK[BUF] + wave * kBlockTokens * ROWB;
+      const int r = lane >> 2;
+      const int sw = swz<CPR>(r);
+#pragma unroll
+      for (int t = 0; t < PPL; ++t) {
+        const int cp = (lane & 3) * PPL + t;
+        uint4 *px = (uint4 *)(kb + r * ROWB + ((cp ^ sw) * 16));
+        uint4 *py = (uint4 *)(kb + r * ROWB + (((cp + CPR / 2) ^ sw) * 16));
+        const uint4 x = *px, y = *py;
+        const float4 *cs = (const float4 *)&s_kcs[wave][8 * cp];
+        uint32_t xo[4], yo[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float4 c2 = cs[k];  // (cos, sin) of frequencies 8 cp + 2k, 8 cp + 2k + 1
+          const uint32_t wx = dw4(x, k), wy = dw4(y, k);
+          const float x0 = bf16_lo(wx), x1 = bf16_hi(wx), y0 = bf16_lo(wy), y1 = bf16_hi(wy);
+          xo[k] = pack_bf16x2(fmaf(x0, c2.x, -(y0 * c2.y)), fmaf(x1, c2.z, -(y1 * c2.w)));
+          yo[k] = pack_bf16x2(fmaf(y0, c2.x, x0 * c2.y), fmaf(y1, c2.z, x1 * c2.w));
+        }
+        *px = make_uint4(xo[0], xo[1], xo[2], xo[3]);
+        *py = make_uint4(yo[0], yo[1], yo[2], yo[3]);
       }
     }
   };
@@ -404,11 +457,44 @@ prefill_kernel(const PrefillKernelArgs a) {
         }
   }
 
+  // q' = rot(q, rho + n0 - off) * scale * log2(e), rho = token index inside
+  // the tile.  The angle in turns is rho * turn_i + frac((n0 - off) *
+  // turn_i); the large part is reduced in double, the rest (< TOK turns)
+  // evaluated with v_sin/v_cos.
+  auto rotate_q = [&](int off) __attribute__((always_inline)) {
+    if (lane < HALF) {
+      const double t = (double)(n0 - off) * turn_d;
+      s_frac[wave][lane] = (float)(t - rint(t));
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float rho = (float)(tw0 + nt * 16 + l16);
+#pragma unroll
+      for (int kc = 0; kc < KC / 2; ++kc) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int fi = kc * 32 + lg * 8 + e;
+          const float turns = fmaf(rho, s_turn[fi], s_frac[wave][fi]);
+          const float c = __builtin_amdgcn_cosf(turns), s = __builtin_amdgcn_sinf(turns);
+          const uint32_t wx = dw4(qraw[nt][kc], e >> 1), wy = dw4(qraw[nt][kc + KC / 2], e >> 1);
+          const float x = (e & 1) ? bf16_hi(wx) : bf16_lo(wx);
+          const float y = (e & 1) ? bf16_hi(wy) : bf16_lo(wy);
+          bq[nt][kc][e] = (__bf16)(fmaf(x, c, -(y * s)) * a.scale_log2);
+          bq[nt][kc + KC / 2][e] = (__bf16)(fmaf(y, c, x * s) * a.scale_log2);
+        }
+      }
+    }
+  };
+  // the non-lazy baseline rotates the rows once, by their own positions
+  if constexpr (MODE == kRopeEager) rotate_q(0);
+
   // One tile on LDS buffer BUF; returns false after the last tile.
   auto step = [&](auto bufc) -> bool {
     constexpr int BUF = decltype(bufc)::value;
     __builtin_amdgcn_s_waitcnt(0);   // this tile's loads and the next words have landed
     widen_tile(ccnt, bufc);
+    rotate_keys(ccnt, coff, cw, bufc);
     fix_tail(cj, ccnt, cf, bufc);
     // the next tile's fill counts (its words landed above), used when it is current
     const uint32_t nf = load_fill(nw);
@@ -429,38 +515,13 @@ prefill_kernel(const PrefillKernelArgs a) {
       nnw = (ALIBI ? nj > 0 : nnj < nblk_vis) ? load_words(nnj) : 0u;
     }
 
-    // ---- re-rotate the query rows: q' = rot(q, rho + n0 - off), rho = token
-    // index inside the tile.  The angle in turns is rho * turn_i +
-    // frac((n0 - off) * turn_i); the large part is reduced in double, the rest
-    // (< TOK turns) evaluated with v_sin/v_cos.
-    if (!ALIBI && coff != cur_off) {
+    // ---- a new document: re-rotate the query rows (lazy RoPE)
+    if (LAZY && coff != cur_off) {
       cur_off = coff;
-      if (lane < HALF) {
-        const double t = (double)(n0 - coff) * turn_d;
-        s_frac[wave][lane] = (float)(t - rint(t));
-      }
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float rho = (float)(tw0 + nt * 16 + l16);
-#pragma unroll
-        for (int kc = 0; kc < KC / 2; ++kc) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int fi = kc * 32 + lg * 8 + e;
-            const float turns = fmaf(rho, s_turn[fi], s_frac[wave][fi]);
-            const float c = __builtin_amdgcn_cosf(turns), s = __builtin_amdgcn_sinf(turns);
-            const uint32_t wx = dw4(qraw[nt][kc], e >> 1), wy = dw4(qraw[nt][kc + KC / 2], e >> 1);
-            const float x = (e & 1) ? bf16_hi(wx) : bf16_lo(wx);
-            const float y = (e & 1) ? bf16_hi(wy) : bf16_lo(wy);
-            bq[nt][kc][e] = (__bf16)(fmaf(x, c, -(y * s)) * a.scale_log2);
-            bq[nt][kc + KC / 2][e] = (__bf16)(fmaf(y, c, x * s) * a.scale_log2);
-          }
-        }
-      }
+      rotate_q(coff);
     }
 
-    if (!NOCUT && more && noff != coff) load_q();   // the next tile starts a new document
+    if (LAZY && more && noff != coff) load_q();   // the next tile takes another query offset
 
     // ---- S'^T = K Q^T - r  (per lane: keys mt*16 + lg*4 + i, token nt*16 + l16)
     const char *kb = (const char *)sK[BUF];
@@ -488,7 +549,7 @@ prefill_kernel(const PrefillKernelArgs a) {
 #pragma unroll
       for (int mt = 0; mt < kPfTileBlocks; ++mt) S[mt][0] = S[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    // per 32-key half; a run of at most 2 blocks (the end of a document)
+    // per 32-key half; a tile of at most 2 blocks (the end of the table)
     // skips the second half's products (its scores are masked below)
     auto qk_half = [&](int h) {
 #pragma unroll
@@ -504,7 +565,7 @@ prefill_kernel(const PrefillKernelArgs a) {
     qk_half(0);
     if (ccnt > kPfTileBlocks / 2) qk_half(1);
 
-    // ---- mask: keys past the tile's run, past kv_len, or after the query token;
+    // ---- mask: keys past the tile's blocks, past kv_len, or after the query token;
     // and slots past a block's fill count.  Per lane and query column, keys
     // mt*16 + lg*4 + i of the tile stay when mt*16 + i <= lim and
     // lg*4 + i < fill(mt).
@@ -611,7 +672,7 @@ prefill_kernel(const PrefillKernelArgs a) {
       }
     };
     pv_half(0);
-    if (ccnt > kPfTileBlocks / 2) pv_half(1);   // a short run has no keys there
+    if (ccnt > kPfTileBlocks / 2) pv_half(1);   // a short tile has no keys there
 
     if (!more) return false;
     cj = nj;
