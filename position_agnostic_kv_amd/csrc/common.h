@@ -174,13 +174,17 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // LDS chunk swizzle of a K/V tile row (16-byte chunks, CPR per row): slot =
-// chunk ^ swz(row).  For 16 chunks per row a bit rotation of the row keeps both
-// readers conflict-free: the 16 rows of a K operand read (one chunk column)
-// land in 16 distinct bank groups, and the 8 rows x 2 chunks that a half-wave
-// of the transposing V read touches land in 16 distinct groups too.
+// chunk ^ swz(row).  Measured on gfx950 (rocprofv3 SQ_LDS_BANK_CONFLICT over
+// single-pattern kernels): LDS banks repeat every 256 bytes, and
+// ds_read_b128 serves a wave in four groups of 16 lanes, each the four lane
+// quads of one half-wave whose quad index has one bit parity (lanes 0-3,
+// 12-15, 20-27 form one group).  For 16 chunks per row, swz(r) = 2 (r mod 8)
+// gives every such group 16 distinct bank slots in the K operand read (row
+// l16, chunk 4 kc + lg) and keeps the transposing V read (ds_read_b64_tr_b16,
+// two rows x two chunks per lane quad) free of conflicts as well.
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (CPR == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+  if constexpr (CPR == 16) return (r & 7) << 1;
   else return (r >> 1) & (CPR - 1);
 }
 typedef __attribute__((address_space(3))) void *lds_ptr_t;

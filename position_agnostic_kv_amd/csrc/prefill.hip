@@ -254,41 +254,47 @@ prefill_kernel(const PrefillKernelArgs a) {
       if (wave >= cnt) return;
       char *kb = (char *)sK[BUF] + wave * kBlockTokens * ROWB;
       char *vb = (char *)sV[BUF] + wave * kBlockTokens * ROWB;
-      // every code of the block into registers before the block is rewritten
+      // every code of a region into registers before the region is rewritten
+      // (K first, then V: the K stores never touch the V codes)
       uint4 kraw[2], vraw[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        kraw[i] = *(const uint4 *)(kb + kBlockTokens / 2 * ROWB + 1024 * i + 16 * lane);
-        vraw[i] = *(const uint4 *)(vb + kBlockTokens / 2 * ROWB + 1024 * i + 16 * lane);
-      }
-      // The swizzle swz(r) = ((r & 7) << 1) | ((r >> 3) & 1) written out so that
-      // every store is a per-lane base plus a compile-time offset.
+      for (int i = 0; i < 2; ++i) kraw[i] = *(const uint4 *)(kb + kBlockTokens / 2 * ROWB + 1024 * i + 16 * lane);
+      // The swizzle swz(r) = 2 (r mod 8) written out so that every store is a
+      // per-lane base plus a compile-time offset.
       // K: code x of chunk i is K[l16][32 lg + 16 i + x]: 16-byte chunk
       // c = 4 lg + 2 i + u (u = x / 8) of row l16, stored at chunk
-      // c ^ swz(l16) = (u ^ s0) + 2 (i ^ s1) + 4 (lg ^ s23).
-      const int s0 = (l16 >> 3) & 1, s1 = l16 & 1, s23 = (l16 >> 1) & 3;
+      // c ^ swz(l16) = u + 2 (i ^ s1) + 4 (lg ^ s23).  ds_write_b128 serves
+      // eight consecutive lanes at a time, with banks repeating every 128
+      // bytes (measured): lanes l16 and l16 + 4 would meet in one bank with
+      // the same u, so lanes with bit 2 of l16 set store their u = 1 half
+      // first.
+      const int s1 = l16 & 1, s2 = (l16 >> 2) & 1, s23 = (l16 >> 1) & 3;
       char *krow = kb + l16 * ROWB + 64 * (lg ^ s23);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
+        // the half stored first: codes 8 s2 .. 8 s2 + 7 of the chunk
+        const uint4 kr = s2 ? make_uint4(kraw[i].z, kraw[i].w, kraw[i].x, kraw[i].y) : kraw[i];
         uint32_t w[8];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          w[2 * d] = e4m3x2_to_bf16x2<false>(dw4(kraw[i], d));
-          w[2 * d + 1] = e4m3x2_to_bf16x2<true>(dw4(kraw[i], d));
+          w[2 * d] = e4m3x2_to_bf16x2<false>(dw4(kr, d));
+          w[2 * d + 1] = e4m3x2_to_bf16x2<true>(dw4(kr, d));
         }
         char *ki = krow + 32 * (i ^ s1);
-        *(uint4 *)(ki + 16 * s0) = make_uint4(w[0], w[1], w[2], w[3]);
-        *(uint4 *)(ki + 16 * (1 ^ s0)) = make_uint4(w[4], w[5], w[6], w[7]);
+        *(uint4 *)(ki + 16 * s2) = make_uint4(w[0], w[1], w[2], w[3]);
+        *(uint4 *)(ki + 16 * (1 ^ s2)) = make_uint4(w[4], w[5], w[6], w[7]);
       }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) vraw[i] = *(const uint4 *)(vb + kBlockTokens / 2 * ROWB + 1024 * i + 16 * lane);
       // V: byte 4 j + k of chunk i is V[4 lg + k][16 (4 i + j) + l16]: row
       // r = 4 lg + k, 16-byte chunk 8 i + 2 j + (l16 >> 3), element l16 & 7;
-      // with a = lg & 1, b = lg >> 1 the stored chunk is
-      // (h ^ b) + 2 (j ^ k) + 8 (i ^ a), h = l16 >> 3.  Lanes 2m and 2m + 1
+      // with a = lg & 1 the stored chunk is h + 2 (j ^ k) + 8 (i ^ a),
+      // h = l16 >> 3.  Lanes 2m and 2m + 1
       // hold dims 2m and 2m + 1 of the same rows, so after one swap between
       // them the even lane writes rows k = 0, 1 and the odd lane rows k = 2, 3
       // as 4-byte words of both dims (p = lane parity, k = kk + 2 p).
       const int p = l16 & 1;
-      char *vlane = vb + (4 * lg + 2 * p) * ROWB + 16 * ((l16 >> 3) ^ (lg >> 1)) + 2 * (l16 & 6);
+      char *vlane = vb + (4 * lg + 2 * p) * ROWB + 16 * (l16 >> 3) + 2 * (l16 & 6);
       const uint32_t sel0 = p ? 0x01000504u : 0x05040100u;  // row kk = 0: (dim 2m, dim 2m + 1)
       const uint32_t sel1 = p ? 0x03020706u : 0x07060302u;  // row kk = 1
 #pragma unroll
@@ -317,10 +323,11 @@ prefill_kernel(const PrefillKernelArgs a) {
   // rotated in place by (offset - qoff), so that rot(q, n - qoff) .
   // rot(k, offset - qoff) = rot(q, n - offset) . k ("Equivalência
   // Matemática").  Lane i < D/2 evaluates frequency i (angle reduced in
-  // double to a fraction of a turn); lane l then takes row l / 4 and the
-  // rotate-half chunk pairs (c, c + CPR/2), c = (l % 4) * PPL + t, whose
-  // 16-byte slots are swizzled alike (slot ^ CPR/2).  The rotated key is
-  // rounded to bf16.  Only blocks at a document boundary take this path.
+  // double to a fraction of a turn); lane (l16, lg) then takes row l16 and
+  // the rotate-half chunk pairs (c, c + CPR/2), c = 4 t + lg, whose 16-byte
+  // slots are swizzled alike (slot ^ CPR/2): the same lane-to-address map as
+  // the K operand read, free of bank conflicts.  The rotated key is rounded
+  // to bf16.  Only blocks at a document boundary take this path.
   auto rotate_keys = [&](int cnt, int qoff, uint32_t wv, auto bufc) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr int PPL = CPR / 8;  // chunk pairs per lane
@@ -335,11 +342,11 @@ prefill_kernel(const PrefillKernelArgs a) {
       }
       __builtin_amdgcn_wave_barrier();
       char *kb = (char *)sK[BUF] + wave * kBlockTokens * ROWB;
-      const int r = lane >> 2;
+      const int r = l16;
       const int sw = swz<CPR>(r);
 #pragma unroll
       for (int t = 0; t < PPL; ++t) {
-        const int cp = (lane & 3) * PPL + t;
+        const int cp = 4 * t + lg;
         uint4 *px = (uint4 *)(kb + r * ROWB + ((cp ^ sw) * 16));
         uint4 *py = (uint4 *)(kb + r * ROWB + (((cp + CPR / 2) ^ sw) * 16));
         const uint4 x = *px, y = *py;
