@@ -53,6 +53,8 @@ extern "C" {
 #define LAZYATTN_BLOCK_TOKENS 16
 #define LAZYATTN_MAX_BLOCKS 65536
 #define LAZYATTN_MAX_POSITION 65535
+/* fixed device scratch of lazyattn_decode_noalloc, per GPU: 8 MiB */
+#define LAZYATTN_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 /* Element type of q, K/V pools, new rows and outputs. */
 enum { LAZYATTN_F32 = 0, LAZYATTN_BF16 = 1 };
@@ -64,7 +66,8 @@ enum {
   LAZYATTN_ERR_DTYPE = -2,       /* unknown dtype, or dtype not offered by this call */
   LAZYATTN_ERR_SHAPE = -3,       /* bad size: head_dim, head counts, num_blocks, ... */
   LAZYATTN_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
-  LAZYATTN_ERR_LAUNCH = -5       /* the HIP launch failed (hipGetLastError) */
+  LAZYATTN_ERR_LAUNCH = -5,      /* the HIP launch failed (hipGetLastError) */
+  LAZYATTN_ERR_SCRATCH = -6      /* lazyattn_decode_noalloc: partials exceed its fixed scratch */
 };
 
 /* Text for a status code (static storage). */
@@ -166,6 +169,31 @@ int lazyattn_prefill(void *out, const void *q, int total_q, const int32_t *cu_q_
                      const int32_t *kv_lens,
                      int batch, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
                      int num_blocks, int dtype, float scale, float rope_theta, void *stream);
+
+/*
+ * lazyattn_decode_noalloc -- lazyattn_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, layout, results and
+ * error codes as lazyattn_decode, without the workspace: the split-K
+ * partials live in a fixed array of LAZYATTN_NOALLOC_SCRATCH_BYTES in device
+ * memory that the library holds on each GPU it runs on until the process
+ * ends.  The call itself allocates nothing (no hipMalloc/hipFree).
+ *
+ *   Sizes whose partials need more than LAZYATTN_NOALLOC_SCRATCH_BYTES
+ *   (lazyattn_decode_workspace_size with the same arguments) are rejected
+ *   with LAZYATTN_ERR_SCRATCH before any launch; so is a device whose
+ *   scratch address cannot be obtained.  The current HIP device must be the
+ *   one the pointers and the stream belong to.
+ *   All calls on one GPU share that GPU's scratch, which keeps the last
+ *   call's partials (every partial is written before it is read, so nothing
+ *   needs clearing): calls that overlap on one GPU (other streams, other
+ *   threads) race and must be serialised by the caller.
+ */
+int lazyattn_decode_noalloc(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                            const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                            const uint8_t *block_fill, const int32_t *seq_lens, int batch, int num_q_heads,
+                            int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
+                            float rope_theta, int split_blocks, void *stream);
 
 /*
  * lazyattn_decode_eager, lazyattn_prefill_eager -- the non-lazy baseline that

@@ -23,7 +23,7 @@ __all__ = [
     "LazyAttnError", "lib_path", "load_library", "version", "kvcache_append",
     "decode_workspace_size", "lazyattn_decode", "lazyattn_prefill", "lazyattn_decode_eager",
     "lazyattn_prefill_eager", "lazyattn_decode_alibi", "lazyattn_prefill_alibi", "kvcache_append_fp8",
-    "lazyattn_decode_fp8", "lazyattn_prefill_fp8", "BLOCK_TOKENS",
+    "lazyattn_decode_fp8", "lazyattn_prefill_fp8", "lazyattn_decode_noalloc", "BLOCK_TOKENS",
 ]
 
 BLOCK_TOKENS = 16
@@ -50,6 +50,8 @@ _SIGNATURES.update({
     "lazyattn_cache_stats": (_i32, [_vp, _vp, _i32]),
 })
 _SIGNATURES["lazyattn_decode_eager"] = _SIGNATURES["lazyattn_decode"]
+_SIGNATURES["lazyattn_decode_noalloc"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                                                 _i32, _i32, _f32, _f32, _i32, _vp])
 _SIGNATURES["lazyattn_decode_alibi"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
                                                _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp])
 _SIGNATURES["lazyattn_prefill_alibi"] = (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
@@ -239,6 +241,42 @@ def lazyattn_decode_alibi(q, q_pos, k_pool, v_pool, block_table, seq_lens, slope
     first token.  Otherwise as lazyattn_decode."""
     return _decode("lazyattn_decode_alibi", q, q_pos, k_pool, v_pool, block_table, seq_lens, scale,
                    None, split_blocks, out, workspace, stream, slopes=slopes, block_fill=block_fill)
+
+
+def lazyattn_decode_noalloc(q, q_pos, k_pool, v_pool, block_table, seq_lens, *, out, scale=None,
+                            rope_theta=10000.0, split_blocks=0, stream=None, block_fill=None):
+    """lazyattn_decode for callers that cannot allocate: the split-K partials
+    live in the library's fixed per-GPU scratch (8 MiB; larger needs raise),
+    and this wrapper allocates nothing either, so ``out`` must be given and
+    ``block_fill`` (if any) must already hold a multiple of 4 entries.  Calls
+    that overlap on one GPU race on the shared scratch."""
+    dev = _dev(q, q_pos, k_pool, v_pool, block_table, seq_lens, out)
+    for t, n in ((q_pos, "q_pos"), (block_table, "block_table"), (seq_lens, "seq_lens")):
+        _int32(t, n)
+    b, hq, d = q.shape
+    nb, hkv, bt, dk = k_pool.shape
+    if bt != BLOCK_TOKENS or dk != d or v_pool.shape != k_pool.shape:
+        raise LazyAttnError("pools must be [num_blocks, num_kv_heads, 16, head_dim]")
+    if q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
+        raise LazyAttnError("q and pools must share a dtype")
+    if block_table.dim() != 2 or block_table.shape[0] != b or q_pos.numel() != b or seq_lens.numel() != b:
+        raise LazyAttnError("block_table [B, max_blocks], q_pos [B], seq_lens [B]")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise LazyAttnError("out must match q")
+    fill = ctypes.c_void_p(0)
+    if block_fill is not None:
+        _dev(block_fill)
+        if block_fill.device != dev or block_fill.dtype != torch.uint8 or block_fill.dim() != 1 \
+                or block_fill.numel() < (nb + 3) // 4 * 4:
+            raise LazyAttnError("block_fill must be uint8 with num_blocks rounded up to 4 entries "
+                                "(no padding copy is made here)")
+        fill = _ptr(block_fill)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(load_library().lazyattn_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(q_pos), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), block_table.shape[1], fill,
+        _ptr(seq_lens), b, hq, hkv, d, nb, _dtype_code(q), scale, float(rope_theta), int(split_blocks),
+        _stream_ptr(stream, dev)), "lazyattn_decode_noalloc")
+    return out
 
 
 def _fill_arg(block_fill, num_blocks, dev):

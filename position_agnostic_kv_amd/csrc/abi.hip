@@ -4,11 +4,37 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "launch.h"
 
 using namespace lazyattn;
 
 namespace {
+
+// Split-K partials of lazyattn_decode_noalloc: a fixed array in device memory
+// (one copy per GPU the library runs on, held until the process ends).  Host
+// code never passes the array's name to a kernel: its device address on the
+// current GPU comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)LAZYATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices];
+
+// The scratch address on the current device, or nullptr if it cannot be had.
+void *scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_ptr[dev] = ptr;
+  }
+  return scratch_ptr[dev];
+}
 
 bool valid_dtype(int dtype) { return dtype == LAZYATTN_F32 || dtype == LAZYATTN_BF16; }
 int elem_bytes(int dtype) { return dtype == LAZYATTN_F32 ? 4 : 2; }
@@ -29,6 +55,8 @@ const char *lazyattn_status_string(int status) {
     case LAZYATTN_ERR_SHAPE: return "unsupported or inconsistent size argument";
     case LAZYATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case LAZYATTN_ERR_LAUNCH: return "kernel launch failed";
+    case LAZYATTN_ERR_SCRATCH:
+      return "split-K partials exceed the fixed scratch of lazyattn_decode_noalloc (or its address is unavailable)";
     default: return "unknown status";
   }
 }
@@ -132,6 +160,28 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
   a.v_scale = v_scale;
   if (pool8) return from_hip(launch_decode_fp8(a, (hipStream_t)stream));
   return from_hip(launch_decode(a, bf16, (hipStream_t)stream));
+}
+
+int lazyattn_decode_noalloc(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                            const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                            const uint8_t *block_fill, const int32_t *seq_lens, int batch, int num_q_heads,
+                            int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
+                            float rope_theta, int split_blocks, void *stream) {
+  // the partials this call needs (0: every sequence fits one split)
+  const size_t need = (batch > 0 && num_kv_heads > 0 && num_q_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+                       head_dim > 0 && max_blocks_per_seq > 0 && split_blocks >= 0)
+                          ? decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                                  split_blocks)
+                          : 0;
+  if (need > kScratchBytes) return LAZYATTN_ERR_SCRATCH;
+  void *ws = nullptr;
+  if (need) {
+    ws = scratch_for_current_device();
+    if (!ws) return LAZYATTN_ERR_SCRATCH;
+  }
+  return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, block_fill, seq_lens,
+                       batch, num_q_heads, num_kv_heads, head_dim, num_blocks, dtype, scale, rope_theta,
+                       split_blocks, ws, kScratchBytes, stream, kRopeLazy, nullptr);
 }
 
 int lazyattn_decode_fp8(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
