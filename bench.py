@@ -8,7 +8,10 @@ One step = one pass over the whole path on synthetic, HBM-resident inputs:
                 lazyattn_prefill against 6144 cached document tokens each.
 Prints one JSON line.  `value` is the decode pass's KV throughput (logical K+V
 bytes of the attended tokens / decode-pass time); the prefill attention
-TFLOP/s rides along.  Kernel durations come from HIP events recorded on the
+TFLOP/s rides along.  After the timed steps, the metric's other two decode
+workloads (Llama-3.1-70B-shaped decode, and the Zipf-skewed document-reuse
+mix) are each timed the same way as a decode pass of their own, with their
+own roofline and oracle baseline (keys "llama70b_decode", "zipf_reuse_decode").  Kernel durations come from HIP events recorded on the
 stream the library launches on (torch's current stream).
 """
 
@@ -107,9 +110,9 @@ def cpu_baseline_decode(case, dc, seconds):
             if t_used >= seconds:
                 break
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": nthr, "kind": "oracle",
-            "sample": f"{groups} (sequence, KV head) groups of llama8b_decode "
-                      f"({groups * g} query heads x 8193 tokens), {t_used:.1f} s, float64 numpy, "
-                      f"{nthr} BLAS threads"}
+            "sample": f"{groups} (sequence, KV head) groups of {case.name} "
+                      f"({groups * g} query heads, {done_bytes // (case.head_dim * 4)} tokens x KV heads), "
+                      f"{t_used:.1f} s, float64 numpy, {nthr} BLAS threads"}
 
 
 def cpu_baseline_prefill(case, dc, seconds):
@@ -713,6 +716,79 @@ def cache_sim_main(args):
     print(json.dumps(res), flush=True)
 
 
+def decode_workload_line(name, args, dev):
+    """The default step's decode pass (kvcache_append of the new tokens, then
+    lazyattn_decode) on another decode workload of the same metric, timed the
+    same way (W warm-up passes, then K timed ones, HIP events on the launch
+    stream): its own K+V rate, kernel-time percentiles, roofline and oracle
+    baseline.  Inputs are dropped afterwards."""
+    import torch
+    import position_agnostic_kv_amd as pak
+    import workloads as W
+    from workloads.device import DeviceInputs
+
+    case = W.make(name)
+    W.materialize_torch(case, dev)
+    d = DeviceInputs(case, dev)
+    wsb = pak.decode_workspace_size(case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                                    case.layout.table.shape[1], args.split_blocks)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(d.q)
+
+    def one(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pak.kvcache_append(d.k_pool, d.v_pool, d.k_new, d.v_new, d.slots)
+        if ev is not None:
+            ev[1].record()
+        pak.lazyattn_decode(d.q, d.q_pos, d.k_pool, d.v_pool, d.table, d.seq_lens, scale=case.scale,
+                            rope_theta=case.rope_theta, split_blocks=args.split_blocks, out=out, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        one()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        one(events[k])
+    torch.cuda.synchronize()
+    pass_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in events]))
+    kx = np.array([e[1].elapsed_time(e[2]) for e in events])
+    kernel_ms = float(np.mean(kx))
+    kv, alg = decode_algorithmic_bytes(case)
+    g = case.num_q_heads // case.num_kv_heads
+    kname = f"lazyattn::decode_mma16_kernel<{min(g, 16)}, 0>"
+    stem = {"llama70b_decode": "decode_llama70b", "zipf_reuse_decode": "decode_zipf"}[name]
+    rec = {
+        "value": round(kv / (pass_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "config": {"batch": case.batch, "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "tokens_attended": int(case.layout.total_lens.sum()),
+                   "kv_bytes": kv},
+        "decode_pass_ms": round(pass_ms, 4), "decode_kernel_ms": round(kernel_ms, 4),
+        "decode_kernel_ms_pct": {"p10": round(float(np.percentile(kx, 10)), 4),
+                                 "p50": round(float(np.median(kx)), 4),
+                                 "p90": round(float(np.percentile(kx, 90)), 4)},
+        "roofline": {"kernel": kname, "bound": "hbm", "achieved": round(alg / (kernel_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(alg / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(stem, DECODE_SOURCES), "algorithmic_bytes": alg},
+    }
+    if name == "zipf_reuse_decode":
+        phys = int(d.k_pool.numel()) * 2 * 2
+        rec["roofline"]["note"] = ("algorithmic bytes count every attended token once per sequence; documents "
+                                   "shared between sequences are read again and served by L2/MALL, so the "
+                                   "logical rate may exceed the HBM peak")
+        rec["pool_bytes_physical"] = phys
+        rec["physical_pool_gbps"] = round(phys / (kernel_ms * 1e-3) / 1e9, 1)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_decode(case, d, args.cpu_seconds)
+    del d, out, ws
+    case.q = case.k_pool = case.v_pool = case.k_new = case.v_new = None
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -910,6 +986,13 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(dcase, dd, args.cpu_seconds)
         res["cpu_baseline_prefill"] = cpu_baseline_prefill(pcase, pd, args.cpu_seconds)
+    # the metric's other decode workloads, each timed as its own pass after the steps above
+    del dd, pd, ws, dout, pout
+    dcase.q = dcase.k_pool = dcase.v_pool = dcase.k_new = dcase.v_new = None
+    pcase.q = pcase.k_pool = pcase.v_pool = pcase.k_new = pcase.v_new = None
+    torch.cuda.empty_cache()
+    for name in ("llama70b_decode", "zipf_reuse_decode"):
+        res[name] = decode_workload_line(name, args, dev)
     print(json.dumps(res), flush=True)
 
 
