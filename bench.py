@@ -284,7 +284,8 @@ def fp8_prefill_shape(case, d, out, timed):
 
 def shapes_main(args):
     """Kernel time of every decode workload (8B, 70B, Zipf mix, 8B with
-    documents of any token count, 8B with ALiBi) and of the 8B prefill (RoPE,
+    documents of any token count, 8B with ALiBi, and GQA 4 against
+    multi-query groups of 32 and 64 at equal K/V bytes) and of the 8B prefill (RoPE,
     ALiBi, documents of any token count), each on its own HBM-resident
     inputs: medians and p10/p90 of
     `args.steps` launches after `args.warmup`.  One JSON line."""
@@ -320,7 +321,8 @@ def shapes_main(args):
     res = {"metric": "kernel time per workload (decode: K+V GB/s; prefill: attention TFLOP/s)",
            "steps": args.steps, "warmup": args.warmup, "data": "synthetic", "peak_hbm_gbps": HBM_PEAK_GBPS,
            "peak_bf16_tflops": BF16_PEAK_TFLOPS}
-    for name in ("llama8b_decode", "llama70b_decode", "zipf_reuse_decode", "llama8b_decode_ragged"):
+    for name in ("llama8b_decode", "llama70b_decode", "zipf_reuse_decode", "llama8b_decode_ragged",
+                 "decode_g4_equal_bytes", "decode_g32_equal_bytes", "decode_g64_equal_bytes"):
         case = W.make(name)
         W.materialize_torch(case, dev)
         d = DeviceInputs(case, dev)
@@ -406,7 +408,10 @@ def shapes_main(args):
 # kernel's dispatches into consecutive runs accordingly.  Value: (profile
 # file stem, kernel source files, algorithmic bytes of one launch).
 SHAPES_DISPATCH_ORDER = {
-    "lazyattn::decode_mma16_kernel<4, 0>": ["llama8b_decode", "zipf_reuse_decode", "llama8b_decode_ragged"],
+    "lazyattn::decode_mma16_kernel<4, 0>": ["llama8b_decode", "zipf_reuse_decode", "llama8b_decode_ragged",
+                                            "decode_g4_equal_bytes"],
+    "lazyattn::decode_mma16_wide_kernel<2, 0>": ["decode_g32_equal_bytes"],
+    "lazyattn::decode_mma16_wide_kernel<4, 0>": ["decode_g64_equal_bytes"],
     "lazyattn::decode_mma16_kernel<4, 2>": ["llama8b_decode_alibi"],
     "lazyattn::decode_mma16_kernel<8, 0>": ["llama70b_decode"],
     "lazyattn::decode_mma8_kernel<4, 0>": ["llama8b_decode_fp8"],
@@ -421,7 +426,8 @@ PROFILE_STEMS = {
     "llama70b_decode": "decode_llama70b", "llama8b_decode_fp8": "decode_llama8b_fp8",
     "llama70b_decode_fp8": "decode_llama70b_fp8", "llama8b_prefill": "prefill_llama8b",
     "llama8b_prefill_ragged": "prefill_llama8b_ragged", "llama8b_prefill_alibi": "prefill_llama8b_alibi",
-    "llama8b_prefill_fp8": "prefill_llama8b_fp8",
+    "llama8b_prefill_fp8": "prefill_llama8b_fp8", "decode_g4_equal_bytes": "decode_g4_equal_bytes",
+    "decode_g32_equal_bytes": "decode_g32_equal_bytes", "decode_g64_equal_bytes": "decode_g64_equal_bytes",
 }
 
 

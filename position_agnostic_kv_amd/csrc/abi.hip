@@ -150,7 +150,7 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
   a.split_blocks = decode_split_blocks(batch, num_q_heads, num_kv_heads, max_blocks_per_seq, split_blocks,
-                                      decode_uses_mma(pool8, bf16, head_dim, num_q_heads, num_kv_heads));
+                                      decode_impl(pool8, bf16, head_dim));
   a.scale = scale;
   a.rope_theta = rope_theta;
   a.mode = mode;

@@ -1067,6 +1067,333 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Query groups of 32 or 64 heads (multi-query attention) on the matrix cores.
+// The kernel above takes up to 16 heads (one MFMA column tile); giving a larger
+// group to G / 16 workgroups would make each of them walk every block again.
+// Here one workgroup takes all G = 16 CT heads of a KV head, so each K/V block
+// is read from memory once.  Its 4 waves form BS = 4 / CT block streams of CT
+// waves: wave w takes column tile w % CT (heads 16 (w % CT) ..) and stream
+// w / CT, and the CT waves of a stream share each block of that stream
+// through LDS.  A stream owns R = 8 / BS ring slots (the workgroup keeps
+// 8 blocks, 64 KiB, in flight, as the kernel above does): the block of step i
+// goes to slot i % R, R - 1 steps ahead.  Each of the stream's waves issues
+// IPW = 8 / CT of the block's 8 DMA instructions (1 KiB each, K then V), and
+// one workgroup barrier per step both publishes the landed block to every
+// reader and frees the slot all waves read one step before.  Streams that run
+// out of blocks re-read their split's last block (never computed on), so
+// every wave has the same number of loads in flight at each wait.  Per wave
+// and block the products, the lazy rotation, the masking and the softmax are
+// those of the kernel above, for the wave's 16 heads; the streams' partial
+// results are merged in LDS at the end.
+template <int CT, int MODE>
+__global__ void __launch_bounds__(kDecodeWaves * kWave, kMma16WorkgroupsPerCu)
+decode_mma16_wide_kernel(const DecodeKernelArgs a) {
+  using E = Elem<bf16>;
+  constexpr int G = 16 * CT;               // query heads of the workgroup
+  constexpr int BS = kDecodeWaves / CT;    // block streams
+  constexpr int R = 8 / BS;                // ring slots per stream
+  constexpr int P = CT == 4 ? 2 : 1;       // blocks of a stream per step
+  constexpr int RS = R / P;                // steps the ring holds
+  constexpr int D = 128;
+  constexpr int CPR = D / 8;               // 16-byte chunks per row
+  constexpr int RPI = kWave / CPR;         // rows per DMA instruction
+  constexpr int IPB = kBlockTokens / RPI;  // DMA instructions per block (K or V)
+  constexpr int IPW = 2 * IPB / CT;        // DMA instructions per wave and block
+  constexpr int ROWB = D * 2;
+  constexpr int BLKB = kBlockTokens * ROWB;  // 4 KiB: one block of one KV head
+  constexpr int NT = kDecodeWaves * kWave;
+  constexpr bool EAGER = MODE == kRopeEager;
+  constexpr bool ALIBI = MODE == kAlibi;
+  static_assert(CT == 2 || CT == 4, "32 or 64 query heads");
+  static_assert(RS >= 2 && RS * P == R, "at least one step of prefetch");
+  static_assert(kDecodeWaves * 16 * D * sizeof(float) <= BS * R * 2 * BLKB, "the partial outputs fit the ring");
+
+  __shared__ __attribute__((aligned(1024))) char s_ring[BS][R][2][BLKB];
+  __shared__ float s_m[kDecodeWaves][16];
+  __shared__ float s_l[kDecodeWaves][16];
+  __shared__ int s_bad[kDecodeWaves];
+
+  const int hkv = a.num_kv_heads;
+  const int unit = (int)blockIdx.x;
+  if (unit >= a.num_units) return;
+  const int split = unit % a.max_splits;
+  const int g = (unit / a.max_splits) % hkv;
+  const int b = unit / a.max_splits / hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int ct = wave % CT;  // column tile: heads 16 ct .. 16 ct + 15 of the group
+  const int st = wave / CT;  // block stream
+  const int hq = hkv * G;
+
+  const int seq_len = a.seq_lens[b];
+  const bool bad_len = seq_len < 0 || seq_len > a.max_blocks * kBlockTokens;
+  const int nblk = bad_len ? 0 : (seq_len + kBlockTokens - 1) / kBlockTokens;
+  const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
+  bf16 *out = (bf16 *)a.out + ((size_t)b * hq + (size_t)g * G) * D;
+  if (nsplit == 0) {
+    if (split == 0)
+      for (int i = tid; i < G * D; i += NT) E::store(out, i, bad_len ? __builtin_nanf("") : 0.f);
+    return;
+  }
+  if (split >= nsplit) return;
+
+  const int n_pos = a.q_pos[b];
+  const int t16 = lane & 15;  // K token row / query head column / V^T dim row
+  const int g4 = lane >> 4;   // lane group
+  const int head = 16 * ct + t16;
+
+  uint4 qraw[4];
+  {
+    const uint4 *qh = (const uint4 *)((const bf16 *)a.q + ((size_t)b * hq + (size_t)g * G + head) * D);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qraw[c] = qh[4 * c + g4];
+  }
+  const double inv_freq = rope_inv_freq(lane, D, a.rope_theta);
+
+  // q' = rot(q, delta) * scale * log2(e) as bf16 hi + lo parts, as above
+  bf16x8_t qh[4], ql[4];
+  auto rotate = [&](int delta) {
+    const double tt = (double)delta * (inv_freq * 0.15915494309189535);
+    const float f = (float)(tt - rint(tt));
+    const float cs = __builtin_amdgcn_cosf(f), sn = __builtin_amdgcn_sinf(f);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t xh[4], xl[4], yh[4], yl[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float r[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const int fi = 32 * c + 8 * g4 + 2 * k + e2;
+          const float cv = __shfl(cs, fi), sv = __shfl(sn, fi);
+          const uint32_t wx = dw4(qraw[c], k), wy = dw4(qraw[c + 2], k);
+          const float x = e2 ? bf16_hi(wx) : bf16_lo(wx);
+          const float y = e2 ? bf16_hi(wy) : bf16_lo(wy);
+          r[e2] = fmaf(x, cv, -(y * sv)) * a.scale_log2;
+          r[2 + e2] = fmaf(y, cv, x * sv) * a.scale_log2;
+        }
+        split_bf16x2(r[0], r[1], xh[k], xl[k]);
+        split_bf16x2(r[2], r[3], yh[k], yl[k]);
+      }
+      qh[c] = as_bf16x8(make_uint4(xh[0], xh[1], xh[2], xh[3]));
+      ql[c] = as_bf16x8(make_uint4(xl[0], xl[1], xl[2], xl[3]));
+      qh[c + 2] = as_bf16x8(make_uint4(yh[0], yh[1], yh[2], yh[3]));
+      ql[c + 2] = as_bf16x8(make_uint4(yl[0], yl[1], yl[2], yl[3]));
+    }
+  };
+  if constexpr (EAGER) rotate(n_pos);
+  if constexpr (ALIBI) rotate(0);
+  const float slope2 = ALIBI ? a.slopes[g * G + head] * kLog2e : 0.f;
+
+  uint32_t ld_off[IPB];
+#pragma unroll
+  for (int i = 0; i < IPB; ++i) {
+    const int r = i * RPI + lane / CPR;
+    ld_off[i] = (uint32_t)(r * ROWB + (((lane % CPR) ^ swz<CPR>(r)) * 16));
+  }
+  uint32_t k_off[4], v_off[8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) k_off[c] = (uint32_t)(t16 * ROWB + (((4 * c + g4) ^ swz<CPR>(t16)) * 16));
+  {
+    const int vr = 4 * g4 + (t16 >> 2);
+    const int tdim = (t16 & 3) * 4;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int dim = 16 * c + tdim;
+      v_off[c] = (uint32_t)(vr * ROWB + (((dim / 8) ^ swz<CPR>(vr)) * 16) + (dim % 8) * 2);
+    }
+  }
+  char *ring = &s_ring[st][0][0][0];
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr_t)ring;
+
+  const int blk0 = split * a.split_blocks;
+  const int blk1 = min(nblk, blk0 + a.split_blocks);
+  const int steps = (blk1 - blk0 + BS * P - 1) / (BS * P);  // the same for every wave
+  const auto trow = as_const_as(a.table + (size_t)b * a.max_blocks);
+  const auto fill4 = a.fill4 ? as_const_as(a.fill4) : nullptr;
+  bool bad = false;
+
+  // this wave's share of the DMA of its stream's k-th block (past the
+  // stream's end: the split's last block again, never computed on) into
+  // slot k % R
+  auto issue = [&](int kk) {
+    const int bk = min(blk0 + st + BS * kk, blk1 - 1);
+    uint32_t id = word_block(trow[bk]);
+    if (id >= (uint32_t)a.num_blocks) {
+      bad = true;
+      id = 0;
+    }
+    const char *kg = (const char *)a.k_pool + ((size_t)id * hkv + g) * BLKB;
+    const char *vg = (const char *)a.v_pool + ((size_t)id * hkv + g) * BLKB;
+    const uint32_t sl = ring_lds + (uint32_t)((kk % R) * 2 * BLKB);
+#pragma unroll
+    for (int j = ct; j < 2 * IPB; j += CT) {
+      if (j < IPB) lds_dma16(kg, ld_off[j], sl + j * 1024);
+      else lds_dma16(vg, ld_off[j - IPB], sl + BLKB + (j - IPB) * 1024);
+    }
+  };
+
+  f32x4_t O[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kMaxFloor, lsum = 0.f;
+  int cur_off = -1;
+
+  // step i: this wave's 16 heads against the stream's blocks P i .. P i + P - 1
+  // (ring slots kk % R).  The blocks' scores share one maximum update and one
+  // set of exponentials; a block past the stream's end takes no part.
+  auto consume = [&](int i) __attribute__((always_inline)) {
+    int bk[P];
+    bool has[P];
+    uint4 ka[P][4];
+    uint2 va[P][8];
+    float sv[P][4];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int kk = i * P + p;
+      bk[p] = blk0 + st + BS * kk;
+      has[p] = bk[p] < blk1;  // wave-uniform
+      if (!has[p]) continue;
+      const char *kb = ring + (kk % R) * 2 * BLKB;
+      const char *vb = kb + BLKB;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ka[p][c] = *(const uint4 *)(kb + k_off[c]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) va[p][c] = lds_read_tr16((const uint16_t *)(vb + v_off[c]));
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if (!has[p]) {
+        sv[p][0] = sv[p][1] = sv[p][2] = sv[p][3] = -INFINITY;
+        continue;
+      }
+      const uint32_t w = trow[bk[p]];
+      if constexpr (MODE == kRopeLazy) {
+        const int off = word_offset(w);
+        if (off != cur_off) {
+          rotate(n_pos - off);
+          cur_off = off;
+        }
+      }
+      f32x4_t S = {0.f, 0.f, 0.f, 0.f}, Sl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[p][c]), qh[c], S, 0, 0, 0);
+        Sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[p][c]), ql[c], Sl, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sv[p][j] = S[j] + Sl[j];
+      if constexpr (ALIBI) {
+        const float base = (float)(word_offset(w) + 4 * g4 - n_pos);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sv[p][j] = fmaf(slope2, base + (float)j, sv[p][j]);
+      }
+      const uint32_t fcur =
+          a.fill4 ? (fill4[min(word_block(w), (uint32_t)a.num_blocks - 1) >> 2] >> ((word_block(w) & 3u) * 8u)) & 0xffu
+                  : 0xffu;
+      const int nvalid = min(seq_len - bk[p] * kBlockTokens, (int)fcur);
+      if (nvalid < kBlockTokens) {
+        const int nv = nvalid - 4 * g4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j >= nv) sv[p][j] = -INFINITY;
+        const uint32_t kx = nv >= 2 ? 0xffffffffu : nv == 1 ? 0xffffu : 0u;
+        const uint32_t ky = nv >= 4 ? 0xffffffffu : nv == 3 ? 0xffffu : 0u;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) va[p][c] = make_uint2(va[p][c].x & kx, va[p][c].y & ky);
+      }
+    }
+    float bm = max4_mfma(sv[0][0], sv[0][1], sv[0][2], sv[0][3]);
+#pragma unroll
+    for (int p = 1; p < P; ++p) bm = fmaxf(bm, max4_mfma(sv[p][0], sv[p][1], sv[p][2], sv[p][3]));
+    bm = col_max4(bm);
+    if (wave_any(bm > m + kRescaleSlack)) {
+      const float mn = fmaxf(m, bm);
+      const float alpha = fast_exp2(m - mn);
+      lsum *= alpha;
+      m = mn;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) O[c] *= alpha;
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if (!has[p]) continue;
+      const uint32_t pa0 = pack_bf16x2(fast_exp2(sv[p][0] - m), fast_exp2(sv[p][1] - m));
+      const uint32_t pa1 = pack_bf16x2(fast_exp2(sv[p][2] - m), fast_exp2(sv[p][3] - m));
+      lsum = dot2_bf16(pa0, 0x3f803f80u, lsum);
+      lsum = dot2_bf16(pa1, 0x3f803f80u, lsum);
+      const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(pa0, pa1));
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        O[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, va[p][c]), pb, O[c], 0, 0, 0);
+    }
+  };
+
+  // step i takes the stream's blocks P i .. P i + P - 1; the ring holds RS
+  // steps, filled RS - 1 steps ahead
+#pragma unroll
+  for (int kk = 0; kk < (RS - 1) * P; ++kk) issue(kk);
+  for (int i = 0; i < steps; ++i) {
+    // this wave's loads of step i have landed (RS - 2 later steps may be in
+    // flight); after the barrier so have the other waves' shares, and every
+    // wave is done with the slots the next DMAs overwrite
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((RS - 2) * P * IPW) : "memory");
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < P; ++p) issue((i + RS - 1) * P + p);
+    consume(i);
+  }
+  // the re-reads past the end must land before the ring is reused for the merge
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // merge the streams: wave w's partial output [16][D] at ring offset w * 8 KiB
+  lsum = col_sum4(lsum);
+  if (g4 == 0) {
+    s_m[wave][t16] = m;
+    s_l[wave][t16] = lsum;
+  }
+  {
+    float *so = (float *)&s_ring[0][0][0][0] + wave * 16 * D + t16 * D + 4 * g4;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) *(f32x4_t *)(so + 16 * c) = O[c];
+  }
+  if (lane == 0) s_bad[wave] = bad;
+  __syncthreads();
+
+  const bool single = nsplit == 1;
+  const bool flagged = (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) != 0;
+  const size_t part = ((size_t)b * hkv + g) * a.max_splits + split;
+  const float *po = (const float *)&s_ring[0][0][0][0];
+  for (int i = tid; i < G * D; i += NT) {
+    const int h = i / D, d = i % D;
+    const int hc = h / 16, hh = h % 16;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int s2 = 0; s2 < BS; ++s2) mx = fmaxf(mx, s_m[s2 * CT + hc][hh]);
+    float o = 0.f, ls = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < BS; ++s2) {
+      const int w2 = s2 * CT + hc;
+      const float f = s_m[w2][hh] == -INFINITY ? 0.f : fast_exp2(s_m[w2][hh] - mx);
+      o = fmaf(po[(w2 * 16 + hh) * D + d], f, o);
+      ls = fmaf(s_l[w2][hh], f, ls);
+    }
+    if (flagged) {
+      o = __builtin_nanf("");
+      ls = __builtin_nanf("");
+    }
+    if (single) {
+      E::store(out, i, ls != 0.f ? o / ls : 0.f);
+    } else {
+      a.ws_o[part * G * D + i] = o;
+      if (d == 0) a.ws_ml[part * G + h] = make_float2(mx, ls);
+    }
+  }
+}
+
 // Merge the per-split partials of one (sequence, KV head): log-sum-exp weights.
 // One workgroup per (sequence, query head), one thread per output element, so
 // that every partial is read by a single round of independent loads.
@@ -1103,40 +1430,44 @@ decode_combine_kernel(const DecodeKernelArgs a) {
 // ------------------------------------------------------------------- host side
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// bf16 pools with head_dim 128 always take the matrix-core kernel: measured
-// against the VALU kernel on 8B-sized contexts it is as fast for query groups
-// of 1 and 2 and faster from 4 on (GQA-8: 4.6 -> 5.5 TB/s).  The VALU kernel
-// serves fp32 and head_dim 64.
-bool decode_uses_mma(bool pool8, bool bf16, int head_dim, int num_q_heads, int num_kv_heads) {
-  (void)num_q_heads;
-  (void)num_kv_heads;
-  return pool8 || (bf16 && head_dim == 128);
+// bf16 pools with head_dim 128 always take the matrix-core kernels: measured
+// against the VALU kernel on 8B-sized contexts they are as fast for query
+// groups of 1 and 2 and faster from 4 on (GQA-8: 4.6 -> 5.5 TB/s).  The VALU
+// kernel serves fp32 and head_dim 64.
+int decode_impl(bool pool8, bool bf16, int head_dim) {
+  if (pool8) return kDecodeMma8;
+  return bf16 && head_dim == 128 ? kDecodeMma16 : kDecodeValu;
 }
 
-// Query heads of one KV head per workgroup.  VALU kernel: G = 8 keeps 8 heads
-// x 8 dims of output accumulators per lane and caps the kernel at one wave per
-// SIMD, too few loads in flight to cover HBM latency; two workgroups of 4
-// heads each (sharing every K/V block through L2) run at two waves per SIMD,
-// and larger groups (multi-query attention) take G / 4 workgroups of 4 heads.
-// The matrix-core kernels take up to 16 query heads (one MFMA column each)
-// per workgroup.
-int decode_head_split(int num_q_heads, int num_kv_heads, bool mma) {
+// Workgroups that share one KV head's query heads.  VALU kernel: G = 8 keeps
+// 8 heads x 8 dims of output accumulators per lane and caps the kernel at one
+// wave per SIMD, too few loads in flight to cover HBM latency; two workgroups
+// of 4 heads each (sharing every K/V block through L2) run at two waves per
+// SIMD, and larger groups (multi-query attention) take G / 4 workgroups of 4
+// heads.  The 8-bit matrix-core kernel takes up to 16 query heads (one MFMA
+// column each) per workgroup; the bf16 one takes every group up to 64 in one
+// workgroup (decode_mma16_wide_kernel above 16).
+int decode_head_split(int num_q_heads, int num_kv_heads, int impl) {
   const int group = num_q_heads / num_kv_heads;
-  if (mma) return group > 16 ? group / 16 : 1;
+  if (impl == kDecodeMma16) return 1;
+  if (impl == kDecodeMma8) return group > 16 ? group / 16 : 1;
   return group >= 8 ? group / 4 : 1;  // MQA-like groups (16..64): 4..16 workgroups of 4 heads
 }
 
 int decode_split_blocks(int batch, int num_q_heads, int num_kv_heads, int max_blocks_per_seq,
-                        int requested, bool mma) {
+                        int requested, int impl) {
   if (requested > 0) return requested;
   // Enough (sequence, work head) units to fill the chip at two workgroups per
   // CU: one split each.  Otherwise cut sequences so ~1024 workgroups run (the
-  // matrix-core kernel: ~512, one round of resident workgroups; a second,
-  // partial round cost it 9 % on the 70B shape).
-  const long long units = (long long)batch * num_kv_heads * decode_head_split(num_q_heads, num_kv_heads, mma);
+  // matrix-core kernels: ~512, one round of resident workgroups; a second,
+  // partial round cost 9 % on the 70B shape).
+  const long long units = (long long)batch * num_kv_heads * decode_head_split(num_q_heads, num_kv_heads, impl);
   if (units >= 512) return max_blocks_per_seq;
-  const long long target = mma ? 512 : 1024;
-  long long sb = (units * max_blocks_per_seq + target - 1) / target;
+  // splits per unit: as many as keep units x splits within the target (the
+  // block count per split is rounded up, which never adds a split)
+  const long long target = impl == kDecodeValu ? 1024 : 512;
+  const long long splits = target / units;
+  long long sb = (max_blocks_per_seq + splits - 1) / splits;
   if (sb < 32) sb = 32;
   sb = (sb + kDecodeWaves - 1) / kDecodeWaves * kDecodeWaves;
   return (int)sb;
@@ -1152,12 +1483,12 @@ static void workspace_layout(int batch, int num_q_heads, int num_kv_heads, int h
 }
 
 // The partials' size depends only on the number of splits (units x heads per
-// unit is the query head count); it covers both kernels' split choice.
+// unit is the query head count); it covers every kernel's split choice.
 size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                              int max_blocks_per_seq, int split_blocks) {
   size_t need = 0;
-  for (const bool mma : {false, true}) {
-    const int sb = decode_split_blocks(batch, num_q_heads, num_kv_heads, max_blocks_per_seq, split_blocks, mma);
+  for (const int impl : {kDecodeValu, kDecodeMma8, kDecodeMma16}) {
+    const int sb = decode_split_blocks(batch, num_q_heads, num_kv_heads, max_blocks_per_seq, split_blocks, impl);
     if ((max_blocks_per_seq + sb - 1) / sb <= 1) continue;  // one split: no partials
     size_t off_o, t;
     workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sb, &off_o, &t);
@@ -1166,8 +1497,9 @@ size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int h
   return need;
 }
 
-// IMPL: kValu (decode_split_kernel), kMma8 (8-bit pools), kMma16 (bf16 pools, matrix cores)
-enum DecodeImpl { kValu = 0, kMma8 = 1, kMma16 = 2 };
+// IMPL: kValu (decode_split_kernel), kMma8 (8-bit pools), kMma16 (bf16 pools,
+// matrix cores, up to 16 heads), kMma16Wide (bf16 pools, 32 or 64 heads)
+enum DecodeImplKernel { kValu = 0, kMma8 = 1, kMma16 = 2, kMma16Wide = 3 };
 
 template <typename T, int D, int G, int MODE, bool F8 = false, int IMPL = kValu>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
@@ -1205,6 +1537,9 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   if constexpr (IMPL == kMma8)
     hipLaunchKernelGGL((decode_mma8_kernel<G, MODE>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave), 0, stream,
                        k);
+  else if constexpr (IMPL == kMma16Wide)
+    hipLaunchKernelGGL((decode_mma16_wide_kernel<G / 16, MODE>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave),
+                       0, stream, k);
   else if constexpr (IMPL == kMma16)
     hipLaunchKernelGGL((decode_mma16_kernel<G, MODE>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave), 0, stream,
                        k);
@@ -1220,12 +1555,14 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
 
 template <int MODE>
 static hipError_t dispatch_mma16(const DecodeArgs &a, hipStream_t s) {
-  switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads, true)) {
+  switch (a.num_q_heads / a.num_kv_heads) {
     case 1: return launch_decode_t<bf16, 128, 1, MODE, false, kMma16>(a, s);
     case 2: return launch_decode_t<bf16, 128, 2, MODE, false, kMma16>(a, s);
     case 4: return launch_decode_t<bf16, 128, 4, MODE, false, kMma16>(a, s);
     case 8: return launch_decode_t<bf16, 128, 8, MODE, false, kMma16>(a, s);
     case 16: return launch_decode_t<bf16, 128, 16, MODE, false, kMma16>(a, s);
+    case 32: return launch_decode_t<bf16, 128, 32, MODE, false, kMma16Wide>(a, s);
+    case 64: return launch_decode_t<bf16, 128, 64, MODE, false, kMma16Wide>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1233,9 +1570,9 @@ static hipError_t dispatch_mma16(const DecodeArgs &a, hipStream_t s) {
 template <typename T, int D, int MODE>
 static hipError_t dispatch_group_e(const DecodeArgs &a, hipStream_t s) {
   if constexpr (sizeof(T) == 2 && D == 128) {
-    if (decode_uses_mma(false, true, D, a.num_q_heads, a.num_kv_heads)) return dispatch_mma16<MODE>(a, s);
+    if (decode_impl(false, true, D) == kDecodeMma16) return dispatch_mma16<MODE>(a, s);
   }
-  switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads, false)) {
+  switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads, kDecodeValu)) {
     case 1: return launch_decode_t<T, D, 1, MODE>(a, s);
     case 2: return launch_decode_t<T, D, 2, MODE>(a, s);
     case 4: return launch_decode_t<T, D, 4, MODE>(a, s);
@@ -1258,7 +1595,7 @@ static hipError_t dispatch_group(const DecodeArgs &a, hipStream_t s) {
 // matrix cores (the pool in the lane order decode_mma8_kernel reads).
 hipError_t launch_decode_fp8(const DecodeArgs &a, hipStream_t s) {
   if (a.head_dim != 128 || a.mode != kRopeLazy) return hipErrorInvalidValue;
-  switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads, true)) {
+  switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads, kDecodeMma8)) {
     case 1: return launch_decode_t<bf16, 128, 1, kRopeLazy, true, kMma8>(a, s);
     case 2: return launch_decode_t<bf16, 128, 2, kRopeLazy, true, kMma8>(a, s);
     case 4: return launch_decode_t<bf16, 128, 4, kRopeLazy, true, kMma8>(a, s);

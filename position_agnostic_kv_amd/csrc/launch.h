@@ -22,15 +22,18 @@ hipError_t launch_append_fp8(void *k_pool, void *v_pool, bool bf16_rows, int num
                              const int32_t *slot_mapping, int num_tokens, float k_scale, float v_scale,
                              hipStream_t stream);
 
-// Whether a decode launch runs on a matrix-core kernel (every 8-bit pool;
-// bf16 pools with head_dim 128 and large query groups).
-bool decode_uses_mma(bool pool8, bool bf16, int head_dim, int num_q_heads, int num_kv_heads);
-// Workgroups that share one KV head's query heads in a decode launch (mma:
-// a matrix-core kernel).
-int decode_head_split(int num_q_heads, int num_kv_heads, bool mma);
+// Which decode kernel family a launch runs on.
+enum DecodeImpl : int {
+  kDecodeValu = 0,   // fp32 pools and head_dim 64: VALU kernel
+  kDecodeMma8 = 1,   // 8-bit pools: matrix cores
+  kDecodeMma16 = 2   // bf16 pools with head_dim 128: matrix cores
+};
+int decode_impl(bool pool8, bool bf16, int head_dim);
+// Workgroups that share one KV head's query heads in a decode launch.
+int decode_head_split(int num_q_heads, int num_kv_heads, int impl);
 // Blocks per split-K partition for a decode launch (requested == 0: automatic).
 int decode_split_blocks(int batch, int num_q_heads, int num_kv_heads, int max_blocks_per_seq,
-                        int requested, bool mma);
+                        int requested, int impl);
 size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                              int max_blocks_per_seq, int split_blocks);
 

@@ -33,6 +33,10 @@ GROUPS = [
     (32, 2, [800, 112], (2, 10), "contiguous", 4),
     (32, 1, [704, 208], (2, 12), "random", 0),
     (64, 1, [480, 32], (2, 6), "contiguous", 6),
+    # multi-query kernel: block streams of unequal length, single-block sequences
+    (32, 4, [1504, 16, 336], (1, 9), "random", 5),
+    (64, 1, [16, 48, 1008], (1, 3), "contiguous", 0),
+    (64, 2, [2048, 272], (2, 30), "random", 7),
 ]
 
 

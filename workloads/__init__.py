@@ -669,6 +669,20 @@ def llama8b_prefill(seed=3, batch=4, cached=6144, prompt=2048):
     return prefill_case(seed, batch, 32, 8, 128, cached, prompt, name="llama8b_prefill")
 
 
+def group_decode_equal_bytes(group, seed=8):
+    """Decode shapes of equal K/V bytes (~0.5 GB) that differ only in how
+    many query heads share a KV head: 15 sequences x 8 KV heads for GQA 4
+    (32 query heads), 120 sequences x 1 KV head for multi-query groups of 32
+    or 64 (a one-head pool holds at most 65536 blocks).  8192 cached tokens
+    per sequence in documents of 16*U{16..128} tokens, plus the new token;
+    bf16, d_h 128, theta 5e5."""
+    if group == 4:
+        batch, hq, hkv = 15, 32, 8
+    else:
+        batch, hq, hkv = 120, group, 1
+    return decode_case(seed, batch, hq, hkv, 128, 8192, (16, 128), name=f"decode_g{group}_equal_bytes")
+
+
 WORKLOADS = {
     "tiny_fp32_decode": tiny_decode,
     "llama8b_decode": llama8b_decode,
@@ -677,6 +691,9 @@ WORKLOADS = {
     "zipf_reuse_decode": zipf_decode,
     "llama8b_decode_ragged": llama8b_decode_ragged,
     "llama8b_prefill_ragged": llama8b_prefill_ragged,
+    "decode_g4_equal_bytes": lambda **kw: group_decode_equal_bytes(4, **kw),
+    "decode_g32_equal_bytes": lambda **kw: group_decode_equal_bytes(32, **kw),
+    "decode_g64_equal_bytes": lambda **kw: group_decode_equal_bytes(64, **kw),
 }
 
 
@@ -689,7 +706,7 @@ __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "to_float", "materialize_numpy",
     "materialize_torch", "add_score_shift", "decode_case", "prefill_case", "tiny_decode",
     "llama8b_decode", "llama8b_prefill", "llama70b_decode", "zipf_decode", "ragged_case",
-    "llama8b_decode_ragged", "llama8b_prefill_ragged", "e4m3_codes", "e4m3_codes_torch",
+    "llama8b_decode_ragged", "llama8b_prefill_ragged", "group_decode_equal_bytes", "e4m3_codes", "e4m3_codes_torch",
     "fp8_pools_to_device_order", "fp8_pools_from_device_order", "make",
     "WORKLOADS",
 ]
