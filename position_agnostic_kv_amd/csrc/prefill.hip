@@ -248,7 +248,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   // F8, after the codes landed: widen this wave's block and write it into
   // buffer BUF as the bf16 DMA would have (rows wave*16 + token, 16-byte
   // chunks swizzled by the row within the block)
-  auto widen_tile = [&](int cnt, auto bufc) __attribute__((always_inline)) {
+  auto widen_tile = [&](int cnt, int vvalid, auto bufc) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
     if constexpr (F8) {
       if (wave >= cnt) return;
@@ -286,32 +286,24 @@ prefill_kernel(const PrefillKernelArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) vraw[i] = *(const uint4 *)(vb + kBlockTokens / 2 * ROWB + 1024 * i + 16 * lane);
-      // V: byte 4 j + k of chunk i is V[4 lg + k][16 (4 i + j) + l16]: row
-      // r = 4 lg + k, 16-byte chunk 8 i + 2 j + (l16 >> 3), element l16 & 7;
-      // with a = lg & 1 the stored chunk is h + 2 (j ^ k) + 8 (i ^ a),
-      // h = l16 >> 3.  Lanes 2m and 2m + 1
-      // hold dims 2m and 2m + 1 of the same rows, so after one swap between
-      // them the even lane writes rows k = 0, 1 and the odd lane rows k = 2, 3
-      // as 4-byte words of both dims (p = lane parity, k = kk + 2 p).
-      const int p = l16 & 1;
-      char *vlane = vb + (4 * lg + 2 * p) * ROWB + 16 * (l16 >> 3) + 2 * (l16 & 6);
-      const uint32_t sel0 = p ? 0x01000504u : 0x05040100u;  // row kk = 0: (dim 2m, dim 2m + 1)
-      const uint32_t sel1 = p ? 0x03020706u : 0x07060302u;  // row kk = 1
+      // V: dword j of chunk i holds V[4 lg + e][16 (4 i + j) + l16], e = byte:
+      // for the 16-dim tile c = 4 i + j, this lane's four tokens 4 lg .. + 3
+      // of dim 16 c + l16 -- exactly its A-operand slice of O^T = V^T P^T for
+      // that tile and block.  So V stays in the pool's lane order: the lane
+      // widens its own codes and stores tile c's four values at
+      // 512 c + 8 lane (contiguous over the wave, free of bank conflicts),
+      // and the products read them back with the same lane map.  Tokens past
+      // the block's valid count are zeroed here (0 x whatever the pool holds
+      // there must not give NaN).
+      const int vlimit = vvalid - 4 * lg;   // this lane's tokens that count
+      const uint32_t keep = vlimit >= 4 ? 0xffffffffu : vlimit <= 0 ? 0u : (0xffffffffu >> (8 * (4 - vlimit)));
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          // keep: this lane's codes of rows 2 p, 2 p + 1; send: the other two
-          const uint32_t rot = __builtin_amdgcn_alignbit(dw4(vraw[i], j), dw4(vraw[i], j), 16 * p);
-          const uint32_t keep = e4m3x2_to_bf16x2<false>(rot);
-          const uint32_t send = e4m3x2_to_bf16x2<true>(rot);
-          const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, kDppQuadXor1, 0xf, 0xf, false);
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const int t = j ^ kk;   // chunk term 32 (t ^ 2 p) = 32 (t & 1) + 64 ((t >> 1) ^ p)
-            char *vi = vlane + 128 * (i ^ (lg & 1)) + 64 * ((t >> 1) ^ p);
-            *(uint32_t *)(vi + kk * ROWB + 32 * (t & 1)) = __builtin_amdgcn_perm(other, keep, kk ? sel1 : sel0);
-          }
+          const uint32_t w = dw4(vraw[i], j) & keep;
+          *(uint2 *)(vb + 512 * (4 * i + j) + 8 * lane) =
+              make_uint2(e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w));
         }
       }
     }
@@ -375,10 +367,15 @@ prefill_kernel(const PrefillKernelArgs a) {
   // after the wave's own loads landed: zero V rows of its block past kv_len
   // or past the block's fill count (their weights are 0; whatever the pool
   // holds there must not turn 0 * x into NaN)
+  // tokens of this wave's block of the tile starting at block j that hold data
+  auto block_valid = [&](int j, uint32_t fv) -> int {
+    return min(kv_len - (j + wave) * kBlockTokens, __builtin_amdgcn_readlane((int)fv, wave));
+  };
   auto fix_tail = [&](int j, int cnt, uint32_t fv, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
+    if constexpr (F8) return;  // the widening zeroes them
     if (wave >= cnt) return;
-    const int valid = min(kv_len - (j + wave) * kBlockTokens, __builtin_amdgcn_readlane((int)fv, wave));
+    const int valid = block_valid(j, fv);
     if (valid >= kBlockTokens) return;
     for (int i = lane; i < kBlockTokens * CPR; i += kWave) {
       const int r = i / CPR;
@@ -429,12 +426,25 @@ prefill_kernel(const PrefillKernelArgs a) {
     ccnt = min(kPfTileBlocks, nblk_vis);
     cj = nblk_vis - ccnt;
   }
+  // After a tile's loads have landed, before the barrier that publishes it:
+  // widen this wave's block (8-bit pools), rotate it if its offset differs
+  // from the query's (lazy RoPE), zero its V rows past the data.  Done at the
+  // end of the step before, behind that step's P.V products on the matrix
+  // cores, instead of at the start of the tile's own step.
+  auto prepare = [&](int j, int cnt, int off, uint32_t wv, uint32_t fv, auto bufc) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the tile have landed
+    widen_tile(cnt, block_valid(j, fv), bufc);
+    rotate_keys(cnt, off, wv, bufc);
+    fix_tail(j, cnt, fv, bufc);
+  };
+
   uint32_t cw = load_words(cj);
   uint32_t cf = load_fill(cw);   // the current tile's fill counts (lanes 0..3)
   if constexpr (!ALIBI) tile_of(cw, 0, ccnt, coff);
   issue_tile(cw, ccnt, std::integral_constant<int, 0>{});
   int nj = ALIBI ? cj - min(kPfTileBlocks, cj) : ccnt;
   uint32_t nw = (ALIBI ? cj > 0 : nj < nblk_vis) ? load_words(nj) : 0u;
+  prepare(cj, ccnt, coff, cw, cf, std::integral_constant<int, 0>{});
   // ALiBi: this wave's slope in log2 units, and the workgroup's reference
   // position (its last query token): the bias is taken as slope * (p - nref),
   // which differs from slope * (p - n) by a constant per query row (softmax
@@ -499,13 +509,10 @@ prefill_kernel(const PrefillKernelArgs a) {
   // One tile on LDS buffer BUF; returns false after the last tile.
   auto step = [&](auto bufc) -> bool {
     constexpr int BUF = decltype(bufc)::value;
-    __builtin_amdgcn_s_waitcnt(0);   // this tile's loads and the next words have landed
-    widen_tile(ccnt, bufc);
-    rotate_keys(ccnt, coff, cw, bufc);
-    fix_tail(cj, ccnt, cf, bufc);
-    // the next tile's fill counts (its words landed above), used when it is current
+    __builtin_amdgcn_s_waitcnt(0);   // the next tile's words (and any raw query rows) have landed
+    // the next tile's fill counts, used when it is prepared and current
     const uint32_t nf = load_fill(nw);
-    __syncthreads();
+    __syncthreads();                 // every wave's block of this tile is prepared
 
     const bool more = ALIBI ? cj > 0 : nj < nblk_vis;
     int ncnt = 0, noff = 0, nnj = 0;
@@ -671,8 +678,14 @@ prefill_kernel(const PrefillKernelArgs a) {
     auto pv_half = [&](int ks) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint2 lo = lds_read_tr16((const uint16_t *)(vb + ks * 32 * ROWB + v_off[dt]));
-        const uint2 up = lds_read_tr16((const uint16_t *)(vb + (ks * 32 + 16) * ROWB + v_off[dt]));
+        uint2 lo, up;
+        if constexpr (F8) {  // blocks 2 ks and 2 ks + 1 in the pool's lane order (see widen_tile)
+          lo = *(const uint2 *)(vb + (2 * ks) * kBlockTokens * ROWB + 512 * dt + 8 * lane);
+          up = *(const uint2 *)(vb + (2 * ks + 1) * kBlockTokens * ROWB + 512 * dt + 8 * lane);
+        } else {
+          lo = lds_read_tr16((const uint16_t *)(vb + ks * 32 * ROWB + v_off[dt]));
+          up = lds_read_tr16((const uint16_t *)(vb + (ks * 32 + 16) * ROWB + v_off[dt]));
+        }
         const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, up.x, up.y));
         O[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[ks][0], O[dt][0], 0, 0, 0);
         O[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[ks][1], O[dt][1], 0, 0, 0);
@@ -682,6 +695,7 @@ prefill_kernel(const PrefillKernelArgs a) {
     if (ccnt > kPfTileBlocks / 2) pv_half(1);   // a short tile has no keys there
 
     if (!more) return false;
+    prepare(nj, ncnt, noff, nw, nf, std::integral_constant<int, BUF ^ 1>{});
     cj = nj;
     ccnt = ncnt;
     coff = noff;

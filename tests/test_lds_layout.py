@@ -4,8 +4,9 @@ The kernels stage each 16-token block of K and V in LDS row-major, 256 bytes
 per row (head_dim 128, bf16), with the 16-byte chunk c of row r stored at
 slot c ^ swz(r), swz(r) = 2 (r mod 8).  This file checks, on the CPU, that
 
-* the 8-bit prefill's widening stores put every element of a block exactly
-  where the bf16 DMA would (so the rest of the kernel is the bf16 one);
+* the 8-bit prefill's K widening stores put every element of a block exactly
+  where the bf16 DMA would, and its V, kept in the pool's lane order, gives
+  each lane of the P.V product its operand slice;
 * the kernels' hot LDS accesses are free of bank conflicts under the rules
   measured on MI355X with single-pattern probe kernels and rocprofv3's
   SQ_LDS_BANK_CONFLICT counter:
@@ -134,21 +135,27 @@ def test_f8_k_widening_stores_are_conflict_free():
         assert conflicts(addrs, write_b128_groups(), 128) == 0
 
 
-def test_f8_v_widening_matches_the_dma_layout():
-    """V: lane (l16, lg) holds V[4 lg + k][16 (4 i + j) + l16]; after the
-    pair swap the lane of parity p writes rows 4 lg + 2 p + kk as 4-byte
-    words of dims (2m, 2m + 1), m = l16 // 2."""
-    covered = set()
+def test_f8_v_lane_order_feeds_the_pv_operand():
+    """8-bit pools: V stays in the pool's byte order.  Lane l of the wave
+    that owns a block reads its 32 codes (bytes 1024 i + 16 l + 4 j + e of
+    the record) and stores the widened values of dword j of chunk i at
+    512 (4 i + j) + 8 l + 2 e.  The P.V product of 16-dim tile dt reads, in
+    lane (l16, lg), the 8 bytes at 512 dt + 8 l of a block and takes them as
+    V[4 lg + e][16 dt + l16], e = 0..3 (its A-operand slice for that block).
+    Checked against the pool byte order the host-side converter uses."""
+    import workloads as W
+    _, v_src = W._fp8_lane_order()   # record byte -> token * 128 + dim
+    stored = {}
+    for lane in range(64):
+        for i, j, e in itertools.product(range(2), range(4), range(4)):
+            byte = 1024 * i + 16 * lane + 4 * j + e
+            stored[512 * (4 * i + j) + 8 * lane + 2 * e] = int(v_src[byte])
+    assert sorted(stored) == list(range(0, 4096, 2))      # the 4 KiB region, once each
     for lane in range(64):
         l16, lg = lane & 15, lane >> 4
-        p = l16 & 1
-        vlane = (4 * lg + 2 * p) * ROWB + 16 * (l16 >> 3) + 2 * (l16 & 6)
-        for i, j, kk in itertools.product(range(2), range(4), range(2)):
-            t = j ^ kk
-            addr = vlane + 128 * (i ^ (lg & 1)) + 64 * ((t >> 1) ^ p) + kk * ROWB + 32 * (t & 1)
-            row = 4 * lg + 2 * p + kk
-            dim = 16 * (4 * i + j) + (l16 & 14)
-            assert addr == dma_addr(row, dim)
-            assert addr + 2 == dma_addr(row, dim + 1)
-            covered.update({(row, dim), (row, dim + 1)})
-    assert len(covered) == 16 * 128
+        for dt, e in itertools.product(range(8), range(4)):
+            assert stored[512 * dt + 8 * lane + 2 * e] == (4 * lg + e) * 128 + 16 * dt + l16
+    # both the widening stores and the operand reads are 512 contiguous bytes per instruction
+    for dt in range(8):
+        addrs = [512 * dt + 8 * lane for lane in range(64)]
+        assert addrs == list(range(512 * dt, 512 * dt + 512, 8))
