@@ -171,7 +171,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   __syncthreads();
 
   // ---- query rows: this lane holds tokens tw0 + nt*16 + l16 and the dims
-  // kc*32 + lg*8 + e.  The raw (bf16, exact) rows are re-read from memory and
+  // kc*32 + lg*8 + e.  The raw (bf16, exact) rows stay in registers and are
   // rotated afresh whenever a new document starts.
   const uint4 *qsrc[2];
   bool qok[2];
@@ -451,17 +451,13 @@ prefill_kernel(const PrefillKernelArgs a) {
   // ignores it) and is <= 0 for every key a row sees
   const float slope2 = ALIBI ? a.slopes[hq] * kLog2e : 0.f;
   const int nref = n0 + TOK - 1;
-  // raw (bf16) query rows for the next rotation, fetched one tile ahead (when
-  // the next tile starts a new document) so that a rotation never waits on a
-  // load; the registers stay live across the loop
+  // raw (bf16) query rows, loaded once and kept packed in registers for the
+  // rotations at document changes
   uint4 qraw[2][KC];
-  auto load_q = [&]() {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+  for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) qraw[nt][kc] = qok[nt] ? qsrc[nt][kc * 4 + lg] : make_uint4(0u, 0u, 0u, 0u);
-  };
-  load_q();
+    for (int kc = 0; kc < KC; ++kc) qraw[nt][kc] = qok[nt] ? qsrc[nt][kc * 4 + lg] : make_uint4(0u, 0u, 0u, 0u);
   if constexpr (ALIBI) {  // no rotation: q * scale * log2(e), once
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
@@ -479,6 +475,13 @@ prefill_kernel(const PrefillKernelArgs a) {
   // turn_i); the large part is reduced in double, the rest (< TOK turns)
   // evaluated with v_sin/v_cos.
   auto rotate_q = [&](int off) __attribute__((always_inline)) {
+    // opaque to the optimiser: otherwise it hoists the bf16 unpacking out of
+    // the tile loop and keeps twice the registers live
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        asm volatile("" : "+v"(qraw[nt][kc].x), "+v"(qraw[nt][kc].y), "+v"(qraw[nt][kc].z), "+v"(qraw[nt][kc].w));
     if (lane < HALF) {
       const double t = (double)(n0 - off) * turn_d;
       s_frac[wave][lane] = (float)(t - rint(t));
@@ -509,7 +512,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   // One tile on LDS buffer BUF; returns false after the last tile.
   auto step = [&](auto bufc) -> bool {
     constexpr int BUF = decltype(bufc)::value;
-    __builtin_amdgcn_s_waitcnt(0);   // the next tile's words (and any raw query rows) have landed
+    __builtin_amdgcn_s_waitcnt(0);   // this tile's K/V and the next tile's words have landed
     // the next tile's fill counts, used when it is prepared and current
     const uint32_t nf = load_fill(nw);
     __syncthreads();                 // every wave's block of this tile is prepared
@@ -534,8 +537,6 @@ prefill_kernel(const PrefillKernelArgs a) {
       cur_off = coff;
       rotate_q(coff);
     }
-
-    if (LAZY && more && noff != coff) load_q();   // the next tile takes another query offset
 
     // ---- S'^T = K Q^T - r  (per lane: keys mt*16 + lg*4 + i, token nt*16 + l16)
     const char *kb = (const char *)sK[BUF];
