@@ -89,14 +89,14 @@ struct PrefillKernelArgs {
 // F8: the pools hold 8-bit (E4M3) codes in the lane order of the matrix-core
 // decode (per (block, KV head) 2 KiB: byte 1024 i + 16 l + x, l = 16 g + t,
 // holds K[t][32 g + 16 i + x] and V[4 g + x % 4][16 (4 i + x / 4) + t]).
-// Wave w DMAs the 2 KiB of K codes and the 2 KiB of V codes of its block of
-// the next tile (1 KiB contiguous per instruction) into the upper halves of
-// its own 4 KiB regions of the next tile's K and V buffers.  At the start of
-// the next step it reads them into registers, widens them exactly to bf16 and
-// writes the block in place, in the same swizzled row-major layout the bf16
-// pool's DMA produces; everything after that is the bf16 kernel.  (Holding the
-// codes in registers across a step would spill.)  The K scale is folded into the rotated query, the
-// V scale into the final normalisation.
+// Wave w loads the 2 KiB of K codes and the 2 KiB of V codes of its block of
+// the next tile into registers (32 bytes of each per lane, 1 KiB contiguous
+// per instruction) while the current tile is computed; at the end of the step
+// it widens them exactly to bf16 and writes the block into the next tile's
+// buffers: K in the same swizzled row-major layout the bf16 pool's DMA
+// produces, V in the pool's lane order, which is the P.V operand's.  The K
+// scale is folded into the rotated query, the V scale into the final
+// normalisation.
 template <int D, int HP, int MODE, bool F8 = false>
 __global__ void __launch_bounds__(kPfWaves * kWave, 2)
 prefill_kernel(const PrefillKernelArgs a) {
@@ -216,6 +216,7 @@ prefill_kernel(const PrefillKernelArgs a) {
     cnt = min(kPfTileBlocks, nblk_vis - jw);
     off = !LAZY ? 0 : word_offset((uint32_t)__builtin_amdgcn_readlane((int)wv, min(2, cnt - 1)));
   };
+  uint4 kcode[2], vcode[2];  // 8-bit pools: this lane's codes of its block of the next tile
   auto issue_tile = [&](uint32_t wv, int cnt, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
     if (wave >= cnt) return;
@@ -224,16 +225,14 @@ prefill_kernel(const PrefillKernelArgs a) {
       s_bad = 1;
       id = 0;
     }
-    if constexpr (F8) {  // the block's codes, into the upper half of its region
-      const uint8_t *kr = (const uint8_t *)a.k_pool + ((size_t)id * hkv + g) * 2048;
-      const uint8_t *vr = (const uint8_t *)a.v_pool + ((size_t)id * hkv + g) * 2048;
-      const int half = (wave * kBlockTokens + kBlockTokens / 2) * D;  // element offset
-      const uint32_t kd = (uint32_t)(uintptr_t)(lds_ptr_t)(&sK[BUF][half]);
-      const uint32_t vd = (uint32_t)(uintptr_t)(lds_ptr_t)(&sV[BUF][half]);
-      lds_dma16(kr, (uint32_t)(16 * lane), kd);
-      lds_dma16(kr, (uint32_t)(1024 + 16 * lane), kd + 1024);
-      lds_dma16(vr, (uint32_t)(16 * lane), vd);
-      lds_dma16(vr, (uint32_t)(1024 + 16 * lane), vd + 1024);
+    if constexpr (F8) {  // the block's codes, into this lane's registers
+      const uint4 *kr = (const uint4 *)((const uint8_t *)a.k_pool + ((size_t)id * hkv + g) * 2048);
+      const uint4 *vr = (const uint4 *)((const uint8_t *)a.v_pool + ((size_t)id * hkv + g) * 2048);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        kcode[i] = kr[64 * i + lane];
+        vcode[i] = vr[64 * i + lane];
+      }
       return;
     }
     const char *kg = (const char *)a.k_pool + ((size_t)id * hkv + g) * (kBlockTokens * ROWB);
@@ -254,11 +253,6 @@ prefill_kernel(const PrefillKernelArgs a) {
       if (wave >= cnt) return;
       char *kb = (char *)sK[BUF] + wave * kBlockTokens * ROWB;
       char *vb = (char *)sV[BUF] + wave * kBlockTokens * ROWB;
-      // every code of a region into registers before the region is rewritten
-      // (K first, then V: the K stores never touch the V codes)
-      uint4 kraw[2], vraw[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) kraw[i] = *(const uint4 *)(kb + kBlockTokens / 2 * ROWB + 1024 * i + 16 * lane);
       // The swizzle swz(r) = 2 (r mod 8) written out so that every store is a
       // per-lane base plus a compile-time offset.
       // K: code x of chunk i is K[l16][32 lg + 16 i + x]: 16-byte chunk
@@ -273,7 +267,7 @@ prefill_kernel(const PrefillKernelArgs a) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         // the half stored first: codes 8 s2 .. 8 s2 + 7 of the chunk
-        const uint4 kr = s2 ? make_uint4(kraw[i].z, kraw[i].w, kraw[i].x, kraw[i].y) : kraw[i];
+        const uint4 kr = s2 ? make_uint4(kcode[i].z, kcode[i].w, kcode[i].x, kcode[i].y) : kcode[i];
         uint32_t w[8];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -284,8 +278,6 @@ prefill_kernel(const PrefillKernelArgs a) {
         *(uint4 *)(ki + 16 * s2) = make_uint4(w[0], w[1], w[2], w[3]);
         *(uint4 *)(ki + 16 * (1 ^ s2)) = make_uint4(w[4], w[5], w[6], w[7]);
       }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) vraw[i] = *(const uint4 *)(vb + kBlockTokens / 2 * ROWB + 1024 * i + 16 * lane);
       // V: dword j of chunk i holds V[4 lg + e][16 (4 i + j) + l16], e = byte:
       // for the 16-dim tile c = 4 i + j, this lane's four tokens 4 lg .. + 3
       // of dim 16 c + l16 -- exactly its A-operand slice of O^T = V^T P^T for
@@ -301,7 +293,7 @@ prefill_kernel(const PrefillKernelArgs a) {
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t w = dw4(vraw[i], j) & keep;
+          const uint32_t w = dw4(vcode[i], j) & keep;
           *(uint2 *)(vb + 512 * (4 * i + j) + 8 * lane) =
               make_uint2(e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w));
         }
