@@ -261,9 +261,9 @@ def fp8_decode_shape(case, d, out, ws, timed):
 
 
 def fp8_prefill_shape(case, d, out, timed):
-    """Time lazyattn_prefill_fp8 on the case's layout with an 8-bit pool of
-    random E4M3 codes (k_scale 0.25, v_scale 0.125); the prompts' rows are
-    quantised in by kvcache_append_fp8 first."""
+    """Time lazyattn_prefill_fp8 (widening pass and prefill) on the case's
+    layout with an 8-bit pool of random E4M3 codes (k_scale 0.25, v_scale
+    0.125); the prompts' rows are quantised in by kvcache_append_fp8 first."""
     import torch
     import position_agnostic_kv_amd as pak
     import workloads as W
@@ -271,10 +271,12 @@ def fp8_prefill_shape(case, d, out, timed):
     k8 = W.e4m3_codes_torch(shape, d.k_pool.device, case.seed + 5000)
     v8 = W.e4m3_codes_torch(shape, d.k_pool.device, case.seed + 6000)
     pak.kvcache_append_fp8(k8, v8, d.k_new, d.v_new, d.slots, 0.25, 0.125)
+    ws = torch.empty(pak.prefill_fp8_workspace_size(case.batch, d.table.shape[1], case.num_kv_heads),
+                     dtype=torch.uint8, device=d.k_pool.device)
     med, p10, p90 = timed(lambda: pak.lazyattn_prefill_fp8(d.q, d.cu, d.q_pos_start, k8, v8, d.table, d.seq_lens,
                                                            case.max_q_len, 0.25, 0.125, scale=case.scale,
-                                                           rope_theta=case.rope_theta, out=out))
-    del k8, v8
+                                                           rope_theta=case.rope_theta, out=out, workspace=ws))
+    del k8, v8, ws
     torch.cuda.empty_cache()
     fl = case.attention_flops()
     return {"ms_p50": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
@@ -416,9 +418,10 @@ SHAPES_DISPATCH_ORDER = {
     "lazyattn::decode_mma16_kernel<8, 0>": ["llama70b_decode"],
     "lazyattn::decode_mma8_kernel<4, 0>": ["llama8b_decode_fp8"],
     "lazyattn::decode_mma8_kernel<8, 0>": ["llama70b_decode_fp8"],
-    "lazyattn::prefill_kernel<128, 4, 0, false>": ["llama8b_prefill", "llama8b_prefill_ragged"],
-    "lazyattn::prefill_kernel<128, 4, 0, true>": ["llama8b_prefill_fp8"],
-    "lazyattn::prefill_kernel<128, 4, 2, false>": ["llama8b_prefill_alibi"],
+    # the 8-bit prefill: the widening pass, then the bf16 kernel on the widened copy
+    "lazyattn::prefill_kernel<128, 4, 0>": ["llama8b_prefill", "llama8b_prefill_fp8", "llama8b_prefill_ragged"],
+    "lazyattn::widen_fp8_kernel": ["llama8b_prefill_fp8_widen"],
+    "lazyattn::prefill_kernel<128, 4, 2>": ["llama8b_prefill_alibi"],
 }
 PROFILE_STEMS = {
     "llama8b_decode": "decode_llama8b", "zipf_reuse_decode": "decode_zipf",
@@ -426,7 +429,8 @@ PROFILE_STEMS = {
     "llama70b_decode": "decode_llama70b", "llama8b_decode_fp8": "decode_llama8b_fp8",
     "llama70b_decode_fp8": "decode_llama70b_fp8", "llama8b_prefill": "prefill_llama8b",
     "llama8b_prefill_ragged": "prefill_llama8b_ragged", "llama8b_prefill_alibi": "prefill_llama8b_alibi",
-    "llama8b_prefill_fp8": "prefill_llama8b_fp8", "decode_g4_equal_bytes": "decode_g4_equal_bytes",
+    "llama8b_prefill_fp8": "prefill_llama8b_fp8", "llama8b_prefill_fp8_widen": "widen_llama8b_fp8",
+    "decode_g4_equal_bytes": "decode_g4_equal_bytes",
     "decode_g32_equal_bytes": "decode_g32_equal_bytes", "decode_g64_equal_bytes": "decode_g64_equal_bytes",
 }
 
@@ -434,6 +438,13 @@ PROFILE_STEMS = {
 def _profile_workload_bytes(name):
     """(description, algorithmic bytes of one launch) of a --shapes workload."""
     import workloads as W
+    if name == "llama8b_prefill_fp8_widen":
+        case = W.make("llama8b_prefill")
+        slots = int(sum(-(-int(n) // W.BLOCK) for n in case.seq_lens)) * case.num_kv_heads
+        total = slots * (2 * 2048 + 2 * 4096)
+        return (f"{name}: the {slots} visible (block, KV head) slots of llama8b_prefill over an E4M3 pool, "
+                f"widened once to bf16; algorithmic = 2 x 2 KiB of codes read + 2 x 4 KiB bf16 written per "
+                f"slot"), total
     base = name.replace("_fp8", "").replace("_alibi", "")
     case = W.make(base)
     if case.kind == "decode":
@@ -447,11 +458,11 @@ def _profile_workload_bytes(name):
         return desc, total
     toks = int(case.layout.total_lens.sum())
     rows = int(case.cu_q_lens[-1])
-    kv_esz = 1 if name.endswith("_fp8") else 2
-    total = toks * case.num_kv_heads * case.head_dim * 2 * kv_esz + 2 * rows * case.num_q_heads * case.head_dim * 2
+    total = toks * case.num_kv_heads * case.head_dim * 2 * 2 + 2 * rows * case.num_q_heads * case.head_dim * 2
     desc = (f"{name}: {case.batch} seqs, {toks} K/V tokens ({rows} prompt rows), {case.num_q_heads} q / "
             f"{case.num_kv_heads} KV heads, d_h {case.head_dim}, "
-            f"{'E4M3 pool, bf16 q' if kv_esz == 1 else 'bf16'}; algorithmic = K+V once + q + out")
+            f"{'bf16 copy widened from an E4M3 pool' if name.endswith('_fp8') else 'bf16'}; "
+            f"algorithmic = K+V once + q + out")
     return desc, total
 
 
@@ -527,7 +538,7 @@ def pmc_summary_main(args):
             f_kib = float(np.mean(f_run[args.warmup:]))
             w_kib = float(np.mean(w_run[args.warmup:]))
             traffic = int(round(f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale))
-            src = PREFILL_SOURCES if "prefill" in kernel else DECODE_SOURCES
+            src = PREFILL_SOURCES if "prefill" in kernel or "widen" in kernel else DECODE_SOURCES
             rec = {"kernel": kernel.replace("lazyattn::", ""), "workload": desc, "source_files": src,
                    "source_hash": source_hash(src), "fetch_kib_per_dispatch": round(f_kib, 3),
                    "write_kib_per_dispatch": round(w_kib, 3), "dispatches": len(f_run) - args.warmup,
@@ -979,7 +990,7 @@ def main():
             "algorithmic_bytes": dec_alg_bytes,
         },
         "roofline_prefill": {
-            "kernel": "lazyattn::prefill_kernel<128, 4, 0, false>",
+            "kernel": "lazyattn::prefill_kernel<128, 4, 0>",
             "bound": "mfma",
             "achieved": round(pf_tflops, 2),
             "peak": BF16_PEAK_TFLOPS,

@@ -294,22 +294,36 @@ int lazyattn_decode_fp8(void *out, const void *q, const int32_t *q_pos, const vo
                         size_t workspace_bytes, void *stream);
 
 /*
+ * lazyattn_prefill_fp8_workspace_size -- bytes of workspace lazyattn_prefill_fp8
+ * needs: a bf16 copy (K and V) of every block slot of the batch,
+ * 2 * batch * max_blocks_per_seq * num_kv_heads * 16 * 128 * 2 bytes.  0 when
+ * head_dim is not 128 or a count is not positive.
+ */
+size_t lazyattn_prefill_fp8_workspace_size(int batch, int max_blocks_per_seq, int num_kv_heads, int head_dim);
+
+/*
  * lazyattn_prefill_fp8 -- lazyattn_prefill (lazy RoPE) against 8-bit pools
  * written by kvcache_append_fp8: keys are decode(code) * k_scale, values
- * decode(code) * v_scale, read one byte per element.  This is the step that
- * reuses cached documents for a new prompt (LazyAttention summary on
- * gist.science, "Implementação Técnica", Prefilling) over the one-byte cache
- * (ai-engineering.academy, "Use-o"; lynx-cortex "00", "El precio").  q and out
- * are bf16 [total_q][num_q_heads][128]; head_dim must be 128; k_scale and
- * v_scale finite and > 0 (LAZYATTN_ERR_SHAPE otherwise).  Other arguments,
- * layouts and errors as lazyattn_prefill.
+ * decode(code) * v_scale.  This is the step that reuses cached documents for
+ * a new prompt (LazyAttention summary on gist.science, "Implementação
+ * Técnica", Prefilling) over the one-byte cache (ai-engineering.academy,
+ * "Use-o"; lynx-cortex "00", "El precio").  A first pass widens each block
+ * the batch can see, once and exactly, into the caller's workspace
+ * (lazyattn_prefill_fp8_workspace_size bytes, device memory the call
+ * overwrites; its previous contents are irrelevant), and the prefill then
+ * reads that bf16 copy: each block is widened once instead of once per query
+ * tile that reads it.  q and out are bf16 [total_q][num_q_heads][128];
+ * head_dim must be 128; k_scale and v_scale finite and > 0
+ * (LAZYATTN_ERR_SHAPE otherwise); a missing or short workspace gives
+ * LAZYATTN_ERR_WORKSPACE before any launch.  Other arguments, layouts and
+ * errors as lazyattn_prefill.
  */
 int lazyattn_prefill_fp8(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
                          const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
                          const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
                          const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads, int num_kv_heads,
                          int head_dim, int num_blocks, float scale, float rope_theta, float k_scale,
-                         float v_scale, void *stream);
+                         float v_scale, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ __all__ = [
     "LazyAttnError", "lib_path", "load_library", "version", "kvcache_append",
     "decode_workspace_size", "lazyattn_decode", "lazyattn_prefill", "lazyattn_decode_eager",
     "lazyattn_prefill_eager", "lazyattn_decode_alibi", "lazyattn_prefill_alibi", "kvcache_append_fp8",
-    "lazyattn_decode_fp8", "lazyattn_prefill_fp8", "lazyattn_decode_noalloc", "BLOCK_TOKENS",
+    "lazyattn_decode_fp8", "lazyattn_prefill_fp8", "prefill_fp8_workspace_size", "lazyattn_decode_noalloc", "BLOCK_TOKENS",
 ]
 
 BLOCK_TOKENS = 16
@@ -61,7 +61,8 @@ _SIGNATURES["kvcache_append_fp8"] = (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _v
 _SIGNATURES["lazyattn_decode_fp8"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                              _i32, _f32, _f32, _f32, _f32, _i32, _vp, _sz, _vp])
 _SIGNATURES["lazyattn_prefill_fp8"] = (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
-                                              _i32, _i32, _i32, _i32, _f32, _f32, _f32, _f32, _vp])
+                                              _i32, _i32, _i32, _i32, _f32, _f32, _f32, _f32, _vp, _sz, _vp])
+_SIGNATURES["lazyattn_prefill_fp8_workspace_size"] = (_sz, [_i32, _i32, _i32, _i32])
 
 
 class LazyAttnError(RuntimeError):
@@ -386,19 +387,26 @@ def lazyattn_prefill_alibi(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_tabl
                     kv_lens, max_q_len, scale, None, out, stream, slopes=slopes, block_fill=block_fill)
 
 
+def prefill_fp8_workspace_size(batch, max_blocks_per_seq, num_kv_heads, head_dim=128):
+    return int(load_library().lazyattn_prefill_fp8_workspace_size(batch, max_blocks_per_seq, num_kv_heads,
+                                                                  head_dim))
+
+
 def lazyattn_prefill_fp8(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len,
-                         k_scale, v_scale, *, scale=None, rope_theta=10000.0, out=None, stream=None,
-                         block_fill=None):
+                         k_scale, v_scale, *, scale=None, rope_theta=10000.0, out=None, workspace=None,
+                         stream=None, block_fill=None):
     """lazyattn_prefill over an 8-bit pool of E4M3 codes (uint8 or
     float8_e4m3fn) written by kvcache_append_fp8: keys are decode(code) *
-    k_scale, values decode(code) * v_scale.  q and out are bf16; head_dim 128."""
+    k_scale, values decode(code) * v_scale.  q and out are bf16; head_dim 128.
+    workspace: device bytes for the widened copy of the visible blocks
+    (prefill_fp8_workspace_size); allocated here when not given."""
     return _prefill("lazyattn_prefill_fp8", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
                     kv_lens, max_q_len, scale, rope_theta, out, stream, block_fill=block_fill,
-                    kv_scales=(float(k_scale), float(v_scale)))
+                    kv_scales=(float(k_scale), float(v_scale)), workspace=workspace)
 
 
 def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len, scale,
-             rope_theta, out, stream, slopes=None, block_fill=None, kv_scales=None):
+             rope_theta, out, stream, slopes=None, block_fill=None, kv_scales=None, workspace=None):
     dev = _dev(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens)
     for t, n in ((cu_q_lens, "cu_q_lens"), (q_pos_start, "q_pos_start"), (kv_lens, "kv_lens"),
                  (block_table, "block_table")):
@@ -425,7 +433,13 @@ def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens
             raise LazyAttnError("out must match q")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     fill_keep, fill = _fill_arg(block_fill, nb, dev)
-    _hold_temporaries(stream, dev, out if new_out else None,
+    new_ws = kv_scales is not None and workspace is None
+    if new_ws:
+        need = prefill_fp8_workspace_size(b, block_table.shape[1], hkv, d) if b else 0
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace is not None:
+        _dev(workspace, q)
+    _hold_temporaries(stream, dev, out if new_out else None, workspace if new_ws else None,
                       fill_keep if fill_keep is not block_fill else None)
     lib = load_library()
     if slopes is not None:
@@ -439,7 +453,8 @@ def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens
         _check(getattr(lib, fn)(_ptr(out), _ptr(q), tq, _ptr(cu_q_lens), _ptr(q_pos_start), _ptr(k_pool),
                                 _ptr(v_pool), _ptr(block_table), block_table.shape[1], fill, _ptr(kv_lens),
                                 b, int(max_q_len), hq, hkv, d, nb, scale, float(rope_theta), kv_scales[0],
-                                kv_scales[1], _stream_ptr(stream, dev)), fn)
+                                kv_scales[1], _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream_ptr(stream, dev)), fn)
         return out
     _check(getattr(lib, fn)(_ptr(out), _ptr(q), tq, _ptr(cu_q_lens), _ptr(q_pos_start), _ptr(k_pool),
                             _ptr(v_pool), _ptr(block_table), block_table.shape[1], fill, _ptr(kv_lens),

@@ -234,7 +234,7 @@ static int prefill_common(void *out, const void *q, int total_q, const int32_t *
                           int batch, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
                           int num_blocks, int dtype, float scale, float rope_theta, void *stream,
                           int mode, const float *slopes, bool pool8 = false, float k_scale = 1.f,
-                          float v_scale = 1.f) {
+                          float v_scale = 1.f, void *workspace = nullptr, size_t workspace_bytes = 0) {
   if (dtype != LAZYATTN_BF16) return LAZYATTN_ERR_DTYPE;
   if (pool8 && (head_dim != 128 || !valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
     return LAZYATTN_ERR_SHAPE;
@@ -251,6 +251,8 @@ static int prefill_common(void *out, const void *q, int total_q, const int32_t *
   if (!out || !q || !cu_q_lens || !q_pos_start || !k_pool || !v_pool || !block_table || !kv_lens)
     return LAZYATTN_ERR_NULL;
   if (mode == kAlibi && !slopes) return LAZYATTN_ERR_NULL;
+  if (pool8 && (!workspace || workspace_bytes < prefill_fp8_workspace_size(batch, max_blocks_per_seq, num_kv_heads)))
+    return LAZYATTN_ERR_WORKSPACE;
   PrefillArgs a;
   a.out = out;
   a.q = q;
@@ -275,7 +277,7 @@ static int prefill_common(void *out, const void *q, int total_q, const int32_t *
   a.block_fill = block_fill;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
-  if (pool8) return from_hip(launch_prefill_fp8(a, (hipStream_t)stream));
+  if (pool8) return from_hip(launch_prefill_fp8(a, workspace, (hipStream_t)stream));
   return from_hip(launch_prefill(a, (hipStream_t)stream));
 }
 
@@ -316,11 +318,16 @@ int lazyattn_prefill_fp8(void *out, const void *q, int total_q, const int32_t *c
                          const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
                          const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads, int num_kv_heads,
                          int head_dim, int num_blocks, float scale, float rope_theta, float k_scale,
-                         float v_scale, void *stream) {
+                         float v_scale, void *workspace, size_t workspace_bytes, void *stream) {
   return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
                         max_blocks_per_seq, block_fill, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
                         head_dim, num_blocks, LAZYATTN_BF16, scale, rope_theta, stream, kRopeLazy, nullptr,
-                        true, k_scale, v_scale);
+                        true, k_scale, v_scale, workspace, workspace_bytes);
+}
+
+size_t lazyattn_prefill_fp8_workspace_size(int batch, int max_blocks_per_seq, int num_kv_heads, int head_dim) {
+  if (head_dim != 128) return 0;
+  return prefill_fp8_workspace_size(batch, max_blocks_per_seq, num_kv_heads);
 }
 
 }  // extern "C"

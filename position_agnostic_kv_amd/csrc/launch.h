@@ -72,8 +72,11 @@ struct PrefillArgs {
   const uint8_t *block_fill;  // per-block fill counts, or nullptr (all full)
   int mode;             // PosMode
   float k_scale = 1.f, v_scale = 1.f;  // 8-bit pools: value = code * scale
+  int staged = 0;       // K/V pools are the widened copy of an 8-bit pool
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
-hipError_t launch_prefill_fp8(const PrefillArgs &a, hipStream_t stream);
+// 8-bit pools: bytes of the bf16 copy of every block slot the batch can see
+size_t prefill_fp8_workspace_size(int batch, int max_blocks, int num_kv_heads);
+hipError_t launch_prefill_fp8(const PrefillArgs &a, void *workspace, hipStream_t stream);
 
 }  // namespace lazyattn

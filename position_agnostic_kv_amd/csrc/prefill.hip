@@ -28,9 +28,11 @@
 //                 and 4 keys per 16-key m-tile, which is exactly a B-operand
 //                 slice of P^T for the next product (the k-slots are permuted
 //                 consistently on both operands), so P never goes through LDS.
-//   O^T = V^T P^T : A = V^T, staged transposed into LDS.
-//   The row max is raised only when a tile exceeds it by more than 2^8, which
-//   skips almost every rescale of the O accumulators.
+//   O^T = V^T P^T : A = V^T, read from the row-major V tile with the
+//                 transposing LDS read (ds_read_b64_tr_b16).
+//   Weights are 2^(s - r) against a per-row reference r that moves only when
+//   a row's running sum leaves [2^-64, 2^64], which skips almost every
+//   rescale of the O accumulators.
 //   Work items are ordered heaviest first and mapped so that the query heads
 //   sharing a KV head run on the same XCD (shared L2 for their K/V tiles).
 #include <math.h>
@@ -65,6 +67,8 @@ struct PrefillKernelArgs {
   int num_units;    // batch * num_kv_heads * head_groups
   float scale_log2, rope_theta;
   float out_scale;  // V scale of an 8-bit pool (1 otherwise)
+  int staged;       // 8-bit pools: K/V come from the widened copy (block j of
+                    // sequence b at index b * max_blocks + j), not the table
 };
 
 // HP query heads of one KV head share a workgroup: rows = HP heads x (128 / HP)
@@ -86,18 +90,13 @@ struct PrefillKernelArgs {
 // walked from the last visible block back to the first, so that each row meets
 // its largest biases first and the reference below rarely has to move.
 //
-// F8: the pools hold 8-bit (E4M3) codes in the lane order of the matrix-core
-// decode (per (block, KV head) 2 KiB: byte 1024 i + 16 l + x, l = 16 g + t,
-// holds K[t][32 g + 16 i + x] and V[4 g + x % 4][16 (4 i + x / 4) + t]).
-// Wave w loads the 2 KiB of K codes and the 2 KiB of V codes of its block of
-// the next tile into registers (32 bytes of each per lane, 1 KiB contiguous
-// per instruction) while the current tile is computed; at the end of the step
-// it widens them exactly to bf16 and writes the block into the next tile's
-// buffers: K in the same swizzled row-major layout the bf16 pool's DMA
-// produces, V in the pool's lane order, which is the P.V operand's.  The K
-// scale is folded into the rotated query, the V scale into the final
-// normalisation.
-template <int D, int HP, int MODE, bool F8 = false>
+// 8-bit pools: a bandwidth-bound pass (widen_fp8_kernel) first widens every
+// visible block of the batch once, exactly, into a bf16 copy laid out like a
+// bf16 pool; this kernel then reads that copy (staged).  Widening inside the
+// kernel would repeat it for every query tile that reads a block (64 times
+// per block for a 2048-token prompt).  The K scale is folded into the
+// rotated query, the V scale into the final normalisation.
+template <int D, int HP, int MODE>
 __global__ void __launch_bounds__(kPfWaves * kWave, 2)
 prefill_kernel(const PrefillKernelArgs a) {
   constexpr int KC = D / 32;          // 32-dim k-chunks of the QK product
@@ -112,7 +111,6 @@ prefill_kernel(const PrefillKernelArgs a) {
   constexpr int WPH = kPfWaves / HP;  // waves per head
   static_assert(D == 64 || D == 128, "head_dim must be 64 or 128");
   static_assert(HP == 1 || HP == 2 || HP == 4, "1, 2 or 4 heads per workgroup");
-  static_assert(!F8 || (D == 128 && MODE == kRopeLazy), "8-bit pools: head_dim 128, lazy RoPE");
   constexpr bool ALIBI = MODE == kAlibi;
   constexpr bool LAZY = MODE == kRopeLazy;  // table offsets rotate queries and keys
 
@@ -216,8 +214,8 @@ prefill_kernel(const PrefillKernelArgs a) {
     cnt = min(kPfTileBlocks, nblk_vis - jw);
     off = !LAZY ? 0 : word_offset((uint32_t)__builtin_amdgcn_readlane((int)wv, min(2, cnt - 1)));
   };
-  uint4 kcode[2], vcode[2];  // 8-bit pools: this lane's codes of its block of the next tile
-  auto issue_tile = [&](uint32_t wv, int cnt, auto bufc) {
+  // the tile [jw, jw + cnt): wave w < cnt streams block jw + w
+  auto issue_tile = [&](uint32_t wv, int jw, int cnt, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
     if (wave >= cnt) return;
     uint32_t id = word_block((uint32_t)__builtin_amdgcn_readlane((int)wv, wave));
@@ -225,18 +223,9 @@ prefill_kernel(const PrefillKernelArgs a) {
       s_bad = 1;
       id = 0;
     }
-    if constexpr (F8) {  // the block's codes, into this lane's registers
-      const uint4 *kr = (const uint4 *)((const uint8_t *)a.k_pool + ((size_t)id * hkv + g) * 2048);
-      const uint4 *vr = (const uint4 *)((const uint8_t *)a.v_pool + ((size_t)id * hkv + g) * 2048);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        kcode[i] = kr[64 * i + lane];
-        vcode[i] = vr[64 * i + lane];
-      }
-      return;
-    }
-    const char *kg = (const char *)a.k_pool + ((size_t)id * hkv + g) * (kBlockTokens * ROWB);
-    const char *vg = (const char *)a.v_pool + ((size_t)id * hkv + g) * (kBlockTokens * ROWB);
+    const size_t src = a.staged ? (size_t)b * a.max_blocks + jw + wave : (size_t)id;
+    const char *kg = (const char *)a.k_pool + (src * hkv + g) * (kBlockTokens * ROWB);
+    const char *vg = (const char *)a.v_pool + (src * hkv + g) * (kBlockTokens * ROWB);
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
       const int dst = (wave * kBlockTokens + i * RPI) * D;  // wave-uniform row base
@@ -244,65 +233,9 @@ prefill_kernel(const PrefillKernelArgs a) {
       lds_dma16(vg, ld_off[i], (uint32_t)(uintptr_t)(lds_ptr_t)(&sV[BUF][dst]));
     }
   };
-  // F8, after the codes landed: widen this wave's block and write it into
-  // buffer BUF as the bf16 DMA would have (rows wave*16 + token, 16-byte
-  // chunks swizzled by the row within the block)
-  auto widen_tile = [&](int cnt, int vvalid, auto bufc) __attribute__((always_inline)) {
-    constexpr int BUF = decltype(bufc)::value;
-    if constexpr (F8) {
-      if (wave >= cnt) return;
-      char *kb = (char *)sK[BUF] + wave * kBlockTokens * ROWB;
-      char *vb = (char *)sV[BUF] + wave * kBlockTokens * ROWB;
-      // The swizzle swz(r) = 2 (r mod 8) written out so that every store is a
-      // per-lane base plus a compile-time offset.
-      // K: code x of chunk i is K[l16][32 lg + 16 i + x]: 16-byte chunk
-      // c = 4 lg + 2 i + u (u = x / 8) of row l16, stored at chunk
-      // c ^ swz(l16) = u + 2 (i ^ s1) + 4 (lg ^ s23).  ds_write_b128 serves
-      // eight consecutive lanes at a time, with banks repeating every 128
-      // bytes (measured): lanes l16 and l16 + 4 would meet in one bank with
-      // the same u, so lanes with bit 2 of l16 set store their u = 1 half
-      // first.
-      const int s1 = l16 & 1, s2 = (l16 >> 2) & 1, s23 = (l16 >> 1) & 3;
-      char *krow = kb + l16 * ROWB + 64 * (lg ^ s23);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        // the half stored first: codes 8 s2 .. 8 s2 + 7 of the chunk
-        const uint4 kr = s2 ? make_uint4(kcode[i].z, kcode[i].w, kcode[i].x, kcode[i].y) : kcode[i];
-        uint32_t w[8];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          w[2 * d] = e4m3x2_to_bf16x2<false>(dw4(kr, d));
-          w[2 * d + 1] = e4m3x2_to_bf16x2<true>(dw4(kr, d));
-        }
-        char *ki = krow + 32 * (i ^ s1);
-        *(uint4 *)(ki + 16 * s2) = make_uint4(w[0], w[1], w[2], w[3]);
-        *(uint4 *)(ki + 16 * (1 ^ s2)) = make_uint4(w[4], w[5], w[6], w[7]);
-      }
-      // V: dword j of chunk i holds V[4 lg + e][16 (4 i + j) + l16], e = byte:
-      // for the 16-dim tile c = 4 i + j, this lane's four tokens 4 lg .. + 3
-      // of dim 16 c + l16 -- exactly its A-operand slice of O^T = V^T P^T for
-      // that tile and block.  So V stays in the pool's lane order: the lane
-      // widens its own codes and stores tile c's four values at
-      // 512 c + 8 lane (contiguous over the wave, free of bank conflicts),
-      // and the products read them back with the same lane map.  Tokens past
-      // the block's valid count are zeroed here (0 x whatever the pool holds
-      // there must not give NaN).
-      const int vlimit = vvalid - 4 * lg;   // this lane's tokens that count
-      const uint32_t keep = vlimit >= 4 ? 0xffffffffu : vlimit <= 0 ? 0u : (0xffffffffu >> (8 * (4 - vlimit)));
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w = dw4(vcode[i], j) & keep;
-          *(uint2 *)(vb + 512 * (4 * i + j) + 8 * lane) =
-              make_uint2(e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w));
-        }
-      }
-    }
-  };
   // [LA] "Implementação Técnica", Prefilling: one relative rotation of a
-  // staged key block.  After this wave's block of the tile has landed (and,
-  // for 8-bit pools, been widened), if its offset differs from the offset
+  // staged key block.  After this wave's block of the tile has landed, if
+  // its offset differs from the offset
   // qoff the query rows are rotated to for this tile, its 16 keys are
   // rotated in place by (offset - qoff), so that rot(q, n - qoff) .
   // rot(k, offset - qoff) = rot(q, n - offset) . k ("Equivalência
@@ -365,7 +298,6 @@ prefill_kernel(const PrefillKernelArgs a) {
   };
   auto fix_tail = [&](int j, int cnt, uint32_t fv, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
-    if constexpr (F8) return;  // the widening zeroes them
     if (wave >= cnt) return;
     const int valid = block_valid(j, fv);
     if (valid >= kBlockTokens) return;
@@ -419,13 +351,12 @@ prefill_kernel(const PrefillKernelArgs a) {
     cj = nblk_vis - ccnt;
   }
   // After a tile's loads have landed, before the barrier that publishes it:
-  // widen this wave's block (8-bit pools), rotate it if its offset differs
-  // from the query's (lazy RoPE), zero its V rows past the data.  Done at the
+  // rotate this wave's block if its offset differs from the query's (lazy
+  // RoPE), zero its V rows past the data.  Done at the
   // end of the step before, behind that step's P.V products on the matrix
   // cores, instead of at the start of the tile's own step.
   auto prepare = [&](int j, int cnt, int off, uint32_t wv, uint32_t fv, auto bufc) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the tile have landed
-    widen_tile(cnt, block_valid(j, fv), bufc);
     rotate_keys(cnt, off, wv, bufc);
     fix_tail(j, cnt, fv, bufc);
   };
@@ -433,7 +364,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   uint32_t cw = load_words(cj);
   uint32_t cf = load_fill(cw);   // the current tile's fill counts (lanes 0..3)
   if constexpr (!ALIBI) tile_of(cw, 0, ccnt, coff);
-  issue_tile(cw, ccnt, std::integral_constant<int, 0>{});
+  issue_tile(cw, cj, ccnt, std::integral_constant<int, 0>{});
   int nj = ALIBI ? cj - min(kPfTileBlocks, cj) : ccnt;
   uint32_t nw = (ALIBI ? cj > 0 : nj < nblk_vis) ? load_words(nj) : 0u;
   prepare(cj, ccnt, coff, cw, cf, std::integral_constant<int, 0>{});
@@ -520,7 +451,7 @@ prefill_kernel(const PrefillKernelArgs a) {
         tile_of(nw, nj, ncnt, noff);
         nnj = nj + ncnt;
       }
-      issue_tile(nw, ncnt, std::integral_constant<int, BUF ^ 1>{});  // streams in during this tile
+      issue_tile(nw, nj, ncnt, std::integral_constant<int, BUF ^ 1>{});  // streams in during this tile
       nnw = (ALIBI ? nj > 0 : nnj < nblk_vis) ? load_words(nnj) : 0u;
     }
 
@@ -671,14 +602,8 @@ prefill_kernel(const PrefillKernelArgs a) {
     auto pv_half = [&](int ks) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        uint2 lo, up;
-        if constexpr (F8) {  // blocks 2 ks and 2 ks + 1 in the pool's lane order (see widen_tile)
-          lo = *(const uint2 *)(vb + (2 * ks) * kBlockTokens * ROWB + 512 * dt + 8 * lane);
-          up = *(const uint2 *)(vb + (2 * ks + 1) * kBlockTokens * ROWB + 512 * dt + 8 * lane);
-        } else {
-          lo = lds_read_tr16((const uint16_t *)(vb + ks * 32 * ROWB + v_off[dt]));
-          up = lds_read_tr16((const uint16_t *)(vb + (ks * 32 + 16) * ROWB + v_off[dt]));
-        }
+        const uint2 lo = lds_read_tr16((const uint16_t *)(vb + ks * 32 * ROWB + v_off[dt]));
+        const uint2 up = lds_read_tr16((const uint16_t *)(vb + (ks * 32 + 16) * ROWB + v_off[dt]));
         const bf16x8_t va = as_bf16x8(make_uint4(lo.x, lo.y, up.x, up.y));
         O[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[ks][0], O[dt][0], 0, 0, 0);
         O[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bp[ks][1], O[dt][1], 0, 0, 0);
@@ -724,7 +649,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   }
 }
 
-template <int D, int HP, int MODE, bool F8 = false>
+template <int D, int HP, int MODE>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   PrefillKernelArgs k;
   k.out = (uint16_t *)a.out;
@@ -747,13 +672,14 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   constexpr int tok = kPfRows / HP;
   k.tok_tiles = (a.max_q_len + tok - 1) / tok;
   k.num_units = a.batch * a.num_kv_heads * k.head_groups;
-  k.scale_log2 = a.scale * kLog2e * (F8 ? a.k_scale : 1.f);
-  k.out_scale = F8 ? a.v_scale : 1.f;
+  k.scale_log2 = a.scale * kLog2e * a.k_scale;
+  k.out_scale = a.v_scale;
+  k.staged = a.staged;
   k.rope_theta = a.rope_theta;
   const long long grid = (long long)(k.num_units + kXcds - 1) / kXcds * kXcds * k.tok_tiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D, HP, MODE, F8>), dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream,
+  hipLaunchKernelGGL((prefill_kernel<D, HP, MODE>), dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream,
                      k);
   return hipGetLastError();
 }
@@ -776,14 +702,116 @@ static hipError_t launch_prefill_d(const PrefillArgs &a, hipStream_t stream) {
   }
 }
 
+// ---- 8-bit pools: widen every visible block once into a bf16 copy
+struct WidenArgs {
+  const uint8_t *k_codes, *v_codes;  // the 8-bit pools, 2 KiB per (block, KV head)
+  const uint32_t *table;
+  const int32_t *kv_lens;
+  uint16_t *k_out, *v_out;           // [batch][max_blocks][num_kv_heads][16][128] bf16
+  int batch, max_blocks, num_kv_heads, num_blocks;
+};
+
+// One wave per (sequence, block slot, KV head), KV head fastest; a slot past
+// the sequence's length, or whose table word names no block, is skipped (the
+// prefill kernel never reads the former and flags the latter).  Codes are
+// stored in the decode's lane order (byte 1024 i + 16 l + x, l = 16 g + t):
+// K[t][32 g + 16 i + x] and V[4 g + x % 4][16 (4 i + x / 4) + t].  K goes
+// straight to its row-major place (32 contiguous bytes per lane and chunk);
+// V is transposed through LDS so that every store is a contiguous 1 KiB.
+// Widening E4M3 to bf16 is exact.
+__global__ void __launch_bounds__(4 * kWave) widen_fp8_kernel(const WidenArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[4][kBlockTokens * 128];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const size_t item = (size_t)blockIdx.x * 4 + wave;
+  const int hkv = a.num_kv_heads;
+  if (item >= (size_t)a.batch * a.max_blocks * hkv) return;
+  const int g = (int)(item % hkv);
+  const size_t slot = item / hkv;
+  const int j = (int)(slot % a.max_blocks);
+  const int b = (int)(slot / a.max_blocks);
+  const int kv_len = a.kv_lens[b];
+  if (kv_len <= 0 || kv_len > a.max_blocks * kBlockTokens || j * kBlockTokens >= kv_len) return;
+  const uint32_t id = word_block(a.table[slot]);
+  if (id >= (uint32_t)a.num_blocks) return;
+  const uint4 *kr = (const uint4 *)(a.k_codes + ((size_t)id * hkv + g) * 2048);
+  const uint4 *vr = (const uint4 *)(a.v_codes + ((size_t)id * hkv + g) * 2048);
+  uint16_t *ko = a.k_out + item * (kBlockTokens * 128);
+  uint4 *vo = (uint4 *)(a.v_out + item * (kBlockTokens * 128));
+  const int t = lane & 15, gq = lane >> 4;
+  uint4 kc[2], vc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    kc[i] = kr[64 * i + lane];
+    vc[i] = vr[64 * i + lane];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    uint32_t w[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      w[2 * d] = e4m3x2_to_bf16x2<false>(dw4(kc[i], d));
+      w[2 * d + 1] = e4m3x2_to_bf16x2<true>(dw4(kc[i], d));
+    }
+    uint4 *dst = (uint4 *)(ko + t * 128 + 32 * gq + 16 * i);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+  uint16_t *sv = s_v[wave];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t c = dw4(vc[i], jj);
+      const uint32_t lo = e4m3x2_to_bf16x2<false>(c), hi = e4m3x2_to_bf16x2<true>(c);
+      const int dim = 16 * (4 * i + jj) + t;
+      sv[(4 * gq + 0) * 128 + dim] = (uint16_t)(lo & 0xffffu);
+      sv[(4 * gq + 1) * 128 + dim] = (uint16_t)(lo >> 16);
+      sv[(4 * gq + 2) * 128 + dim] = (uint16_t)(hi & 0xffffu);
+      sv[(4 * gq + 3) * 128 + dim] = (uint16_t)(hi >> 16);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in order
+#pragma unroll
+  for (int r = 0; r < 4; ++r) vo[64 * r + lane] = ((const uint4 *)sv)[64 * r + lane];
+}
+
+size_t prefill_fp8_workspace_size(int batch, int max_blocks, int num_kv_heads) {
+  if (batch <= 0 || max_blocks <= 0 || num_kv_heads <= 0) return 0;
+  return 2 * (size_t)batch * max_blocks * num_kv_heads * (kBlockTokens * 128 * sizeof(uint16_t));
+}
+
 // bf16 queries against 8-bit (E4M3) pools in the decode's lane order, lazy
-// RoPE, head_dim 128.
-hipError_t launch_prefill_fp8(const PrefillArgs &a, hipStream_t stream) {
-  if (a.head_dim != 128 || a.mode != kRopeLazy) return hipErrorInvalidValue;
+// RoPE, head_dim 128: widen, then the bf16 kernel on the widened copy.
+hipError_t launch_prefill_fp8(const PrefillArgs &a, void *workspace, hipStream_t stream) {
+  if (a.head_dim != 128 || a.mode != kRopeLazy || !workspace) return hipErrorInvalidValue;
+  const size_t half = prefill_fp8_workspace_size(a.batch, a.max_blocks, a.num_kv_heads) / 2;
+  WidenArgs w;
+  w.k_codes = (const uint8_t *)a.k_pool;
+  w.v_codes = (const uint8_t *)a.v_pool;
+  w.table = a.table;
+  w.kv_lens = a.kv_lens;
+  w.k_out = (uint16_t *)workspace;
+  w.v_out = (uint16_t *)((char *)workspace + half);
+  w.batch = a.batch;
+  w.max_blocks = a.max_blocks;
+  w.num_kv_heads = a.num_kv_heads;
+  w.num_blocks = a.num_blocks;
+  const long long items = (long long)a.batch * a.max_blocks * a.num_kv_heads;
+  const long long wgs = (items + 3) / 4;
+  if (wgs <= 0) return hipSuccess;
+  if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(widen_fp8_kernel, dim3((unsigned)wgs), dim3(4 * kWave), 0, stream, w);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  PrefillArgs s = a;
+  s.k_pool = w.k_out;
+  s.v_pool = w.v_out;
+  s.staged = 1;
   const int group = a.num_q_heads / a.num_kv_heads;
-  if (group % 4 == 0) return launch_prefill_t<128, 4, kRopeLazy, true>(a, stream);
-  if (group % 2 == 0) return launch_prefill_t<128, 2, kRopeLazy, true>(a, stream);
-  return launch_prefill_t<128, 1, kRopeLazy, true>(a, stream);
+  if (group % 4 == 0) return launch_prefill_t<128, 4, kRopeLazy>(s, stream);
+  if (group % 2 == 0) return launch_prefill_t<128, 2, kRopeLazy>(s, stream);
+  return launch_prefill_t<128, 1, kRopeLazy>(s, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {

@@ -168,10 +168,11 @@ def test_fp8_entry_points_check_arguments(lib):
             out[idx[k]] = v
         return d(*out)
     p = lib.lazyattn_prefill_fp8
-    ok_p = [P, P, 8, P, P, P, P, P, 4, NULL, P, 1, 8, 8, 2, 128, 16, 0.088, 1e4, 0.5, 0.5, NULL]
+    ok_p = [P, P, 8, P, P, P, P, P, 4, NULL, P, 1, 8, 8, 2, 128, 16, 0.088, 1e4, 0.5, 0.5, P, 1 << 30, NULL]
 
     def pwith(**kw):
-        idx = {"q": 1, "total_q": 2, "batch": 11, "max_q": 12, "hq": 13, "hkv": 14, "d": 15, "ks": 19, "vs": 20}
+        idx = {"q": 1, "total_q": 2, "batch": 11, "max_q": 12, "hq": 13, "hkv": 14, "d": 15, "ks": 19, "vs": 20,
+               "ws": 21, "wsb": 22}
         out = list(ok_p)
         for k, v in kw.items():
             out[idx[k]] = v
@@ -182,6 +183,11 @@ def test_fp8_entry_points_check_arguments(lib):
     assert pwith(hq=6, hkv=4) == -3
     assert pwith(q=NULL) == -1
     assert pwith(batch=0, q=NULL) == 0
+    need = lib.lazyattn_prefill_fp8_workspace_size(1, 4, 2, 128)
+    assert need == 2 * 1 * 4 * 2 * 16 * 128 * 2     # K and V, bf16, every block slot
+    assert lib.lazyattn_prefill_fp8_workspace_size(1, 4, 2, 64) == 0
+    assert pwith(ws=NULL) == -4                     # the widened copy needs a workspace
+    assert pwith(wsb=need - 1) == -4
     assert dwith(d=64) == -3                        # 8-bit pools: head_dim 128 only
     assert dwith(ks=-1.0) == -3
     assert dwith(vs=0.0) == -3

@@ -259,8 +259,8 @@ def test_prefill_fp8_equals_bf16_prefill_on_dequantised_pool(kind):
     """Every E4M3 value times a power-of-two scale is a bf16 value, and a
     power-of-two K scale folded into the rotated query rounds exactly as the
     unscaled query does, so the 8-bit prefill must equal the bf16 prefill on
-    the dequantised pool bit for bit: this checks the codes' byte order, the
-    swizzle and the widening element by element."""
+    the dequantised pool bit for bit: this checks the codes' byte order and
+    the widening pass element by element."""
     ks, vs = 0.25, 0.5
     if kind == "ragged":
         case = W.ragged_case(261, "prefill", 2, 32, 8, 128, (2, 4), (1, 500), prompt=(1, 200))
@@ -287,6 +287,40 @@ def test_prefill_fp8_equals_bf16_prefill_on_dequantised_pool(kind):
                                  block_fill=dc.fill)
     torch.cuda.synchronize()
     assert torch.equal(out8.view(torch.int16), out16.view(torch.int16))
+
+
+def test_prefill_fp8_caller_workspace_contents_are_irrelevant():
+    """The widened copy lives in the caller's workspace: a workspace full of
+    NaN patterns (slots the batch cannot see are never written or read), the
+    same workspace again for a smaller batch, and the binding's own
+    workspace all give the same bits."""
+    ks, vs = 0.25, 0.125
+    case = W.prefill_case(271, 3, 32, 8, 128, [512, 96, 304], [256, 77, 40], (2, 12), offsets="random")
+    say("[fp8 prefill] caller workspace, NaN-filled, reused")
+    W.materialize_numpy(case)
+    kc, vc = _fp8_case(case, 29)
+    dc = DeviceCase(case)
+    k8, v8 = (_u8(x) for x in W.fp8_pools_to_device_order(kc, vc))
+    pak.kvcache_append_fp8(k8, v8, dc.k_new, dc.v_new, dc.slots, ks, vs)
+    need = pak.prefill_fp8_workspace_size(case.batch, dc.table.shape[1], case.num_kv_heads)
+    assert need > 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+
+    def run(workspace, nseq):
+        tq = int(case.cu_q_lens[nseq])
+        return pak.lazyattn_prefill_fp8(dc.q[:tq], dc.cu[:nseq + 1], dc.q_pos_start[:nseq], k8, v8,
+                                        dc.table[:nseq], dc.seq_lens[:nseq], case.max_q_len, ks, vs,
+                                        scale=case.scale, rope_theta=case.rope_theta, block_fill=dc.fill,
+                                        workspace=workspace)
+    own = run(None, case.batch)
+    mine = run(ws, case.batch)
+    again = run(ws, 2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(mine.float()).all()
+    assert torch.equal(own.view(torch.int16), mine.view(torch.int16))
+    assert torch.equal(again.view(torch.int16), own[:again.shape[0]].view(torch.int16))
+    with pytest.raises(pak.LazyAttnError):
+        run(ws[:need - 1], case.batch)
 
 
 def test_full_size_prefill_fp8_sampled():

@@ -4,9 +4,8 @@ The kernels stage each 16-token block of K and V in LDS row-major, 256 bytes
 per row (head_dim 128, bf16), with the 16-byte chunk c of row r stored at
 slot c ^ swz(r), swz(r) = 2 (r mod 8).  This file checks, on the CPU, that
 
-* the 8-bit prefill's K widening stores put every element of a block exactly
-  where the bf16 DMA would, and its V, kept in the pool's lane order, gives
-  each lane of the P.V product its operand slice;
+* the widening pass for 8-bit pools puts every code of a block where the
+  bf16 pool layout holds its element;
 * the kernels' hot LDS accesses are free of bank conflicts under the rules
   measured on MI355X with single-pattern probe kernels and rocprofv3's
   SQ_LDS_BANK_CONFLICT counter:
@@ -15,7 +14,7 @@ slot c ^ swz(r), swz(r) = 2 (r mod 8).  This file checks, on the CPU, that
       quads of one half-wave whose quad index (bits 2..4 of the lane) has the
       same bit parity;
     - ds_write_b128: banks repeat every 128 bytes (8 slots); a wave is served
-      eight consecutive lanes at a time.
+      eight consecutive lanes at a time (no hot store uses it now).
   Two lanes of one group that touch different addresses in one slot
   conflict.  (Reading one address from several lanes does not.)
 
@@ -44,10 +43,6 @@ def read_b128_groups():
         key = (lane >> 5, bin(quad).count("1") & 1)
         groups.setdefault(key, []).append(lane)
     return list(groups.values())
-
-
-def write_b128_groups():
-    return [list(range(i, i + 8)) for i in range(0, 64, 8)]
 
 
 def conflicts(addrs, groups, window):
@@ -103,59 +98,26 @@ def test_k_operand_read_covers_whole_rows():
     assert len(seen) == 256
 
 
-def _f8_k_stores():
-    """(instruction, lane) -> (address, [(row, dim) of the 8 elements])."""
-    out = {}
-    for lane in range(64):
-        l16, lg = lane & 15, lane >> 4
-        s1, s2, s23 = l16 & 1, (l16 >> 2) & 1, (l16 >> 1) & 3
-        krow = l16 * ROWB + 64 * (lg ^ s23)
-        for i in range(2):
-            ki = krow + 32 * (i ^ s1)
-            for n, u in enumerate((s2, 1 ^ s2)):   # first store: half s2
-                elems = [(l16, 32 * lg + 16 * i + 8 * u + e) for e in range(8)]
-                out[(2 * i + n, lane)] = (ki + 16 * u, elems)
-    return out
-
-
-def test_f8_k_widening_matches_the_dma_layout():
-    stores = _f8_k_stores()
-    covered = set()
-    for (_, _), (addr, elems) in stores.items():
-        for e, (row, dim) in enumerate(elems):
-            assert addr + 2 * e == dma_addr(row, dim)
-            covered.add((row, dim))
-    assert len(covered) == 16 * 128
-
-
-def test_f8_k_widening_stores_are_conflict_free():
-    stores = _f8_k_stores()
-    for inst in range(4):
-        addrs = [stores[(inst, lane)][0] for lane in range(64)]
-        assert conflicts(addrs, write_b128_groups(), 128) == 0
-
-
-def test_f8_v_lane_order_feeds_the_pv_operand():
-    """8-bit pools: V stays in the pool's byte order.  Lane l of the wave
-    that owns a block reads its 32 codes (bytes 1024 i + 16 l + 4 j + e of
-    the record) and stores the widened values of dword j of chunk i at
-    512 (4 i + j) + 8 l + 2 e.  The P.V product of 16-dim tile dt reads, in
-    lane (l16, lg), the 8 bytes at 512 dt + 8 l of a block and takes them as
-    V[4 lg + e][16 dt + l16], e = 0..3 (its A-operand slice for that block).
-    Checked against the pool byte order the host-side converter uses."""
+def test_fp8_widening_pass_places_every_code():
+    """The widening pass for 8-bit pools reads a (block, KV head) record in
+    the pool's lane order and writes the bf16 block row-major (token * 128 +
+    dim).  Lane l = 16 g + t, chunk i: K code x goes to row t, dim
+    32 g + 16 i + x; V dword jj, byte e goes (through the wave's LDS
+    transpose) to row 4 g + e, dim 16 (4 i + jj) + t.  Checked against the
+    pool byte order the host-side converter uses: each byte lands exactly
+    where its logical element belongs, and every element is written once."""
     import workloads as W
-    _, v_src = W._fp8_lane_order()   # record byte -> token * 128 + dim
-    stored = {}
+    k_src, v_src = W._fp8_lane_order()   # record byte -> token * 128 + dim
+    k_dst, v_dst = {}, {}
     for lane in range(64):
-        for i, j, e in itertools.product(range(2), range(4), range(4)):
-            byte = 1024 * i + 16 * lane + 4 * j + e
-            stored[512 * (4 * i + j) + 8 * lane + 2 * e] = int(v_src[byte])
-    assert sorted(stored) == list(range(0, 4096, 2))      # the 4 KiB region, once each
-    for lane in range(64):
-        l16, lg = lane & 15, lane >> 4
-        for dt, e in itertools.product(range(8), range(4)):
-            assert stored[512 * dt + 8 * lane + 2 * e] == (4 * lg + e) * 128 + 16 * dt + l16
-    # both the widening stores and the operand reads are 512 contiguous bytes per instruction
-    for dt in range(8):
-        addrs = [512 * dt + 8 * lane for lane in range(64)]
-        assert addrs == list(range(512 * dt, 512 * dt + 512, 8))
+        t, g = lane & 15, lane >> 4
+        for i, x in itertools.product(range(2), range(16)):
+            byte = 1024 * i + 16 * lane + x
+            k_dst[byte] = t * 128 + 32 * g + 16 * i + x
+            jj, e = x // 4, x % 4
+            v_dst[byte] = (4 * g + e) * 128 + 16 * (4 * i + jj) + t
+    for byte in range(2048):
+        assert k_dst[byte] == int(k_src[byte])
+        assert v_dst[byte] == int(v_src[byte])
+    assert sorted(k_dst.values()) == list(range(2048))
+    assert sorted(v_dst.values()) == list(range(2048))
