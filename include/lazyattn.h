@@ -99,9 +99,10 @@ int kvcache_append(void *k_pool, void *v_pool, int dtype, int num_blocks, int nu
  * Bytes of workspace lazyattn_decode needs for these sizes (split_blocks as
  * passed to lazyattn_decode; 0 = automatic).  The workspace holds the per-split
  * partial results (max, sum, unnormalised output) of sequences split over
- * several workgroups; it needs no initialisation.  0 means the call uses none
- * (every sequence fits one split) and workspace may be NULL.  Calls that share
- * one workspace must not overlap.
+ * several workgroups; it needs no initialisation and must be 16-byte aligned
+ * (LAZYATTN_ERR_WORKSPACE otherwise).  0 means the call uses none (every
+ * sequence fits one split) and workspace may be NULL.  Calls that share one
+ * workspace must not overlap.
  */
 size_t lazyattn_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                       int max_blocks_per_seq, int split_blocks);

@@ -132,7 +132,8 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
   if (mode == kAlibi && !slopes) return LAZYATTN_ERR_NULL;
   const size_t need = decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
                                             max_blocks_per_seq, split_blocks);
-  if (need && (!workspace || workspace_bytes < need)) return LAZYATTN_ERR_WORKSPACE;
+  if (need && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u)))
+    return LAZYATTN_ERR_WORKSPACE;
 
   DecodeArgs a;
   a.out = out;

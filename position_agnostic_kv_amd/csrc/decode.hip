@@ -1395,16 +1395,21 @@ decode_mma16_wide_kernel(const DecodeKernelArgs a) {
 }
 
 // Merge the per-split partials of one (sequence, KV head): log-sum-exp weights.
-// One workgroup per (sequence, query head), one thread per output element, so
-// that every partial is read by a single round of independent loads.
+// One workgroup per (sequence, KV head, group of up to 8 query heads); each
+// thread merges 4 consecutive dims of one head with 16-byte loads, so that a
+// 64-head group's partials (16 times those of a 4-head group) are read with
+// few, wide, independent loads.
 template <typename T, int D, int G>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(256)
 decode_combine_kernel(const DecodeKernelArgs a) {
   using E = Elem<T>;
-  const int h = blockIdx.x % G;
-  const int g = blockIdx.x / G;
+  constexpr int GH = G < 8 ? G : 8;  // query heads per workgroup
+  constexpr int TPH = D / 4;         // threads per head
+  const int hg = blockIdx.x % (G / GH);
+  const int g = blockIdx.x / (G / GH);
   const int b = blockIdx.y;
-  const int d = threadIdx.x;
+  const int h = hg * GH + threadIdx.x / TPH;
+  const int d = 4 * (threadIdx.x % TPH);
   const int hkv = a.num_kv_heads;
   const int seq_len = a.seq_lens[b];
   if (seq_len < 0 || seq_len > a.max_blocks * kBlockTokens) return;  // written by the split kernel
@@ -1412,19 +1417,29 @@ decode_combine_kernel(const DecodeKernelArgs a) {
   const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
   if (nsplit <= 1) return;
   const size_t part = ((size_t)b * hkv + g) * a.max_splits;
-  const float *po = a.ws_o + (part * G + h) * D + d;
+  const float4 *po = (const float4 *)(a.ws_o + (part * G + h) * D + d);
   const float2 *pml = a.ws_ml + part * G + h;
   float mx = -INFINITY;
   for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, pml[sp * G].x);
-  float o = 0.f, lsum = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float lsum = 0.f;
+#pragma unroll 4
   for (int sp = 0; sp < nsplit; ++sp) {
     const float2 ml = pml[sp * G];
     const float f = fast_exp2(ml.x - mx);
-    o = fmaf(po[(size_t)sp * G * D], f, o);
+    const float4 v = po[(size_t)sp * (G * D / 4)];
+    o.x = fmaf(v.x, f, o.x);
+    o.y = fmaf(v.y, f, o.y);
+    o.z = fmaf(v.z, f, o.z);
+    o.w = fmaf(v.w, f, o.w);
     lsum = fmaf(ml.y, f, lsum);
   }
-  T *out = (T *)a.out + (((size_t)b * hkv + g) * G + h) * D;
-  E::store(out, d, lsum != 0.f ? o / lsum * a.out_scale : 0.f);
+  T *out = (T *)a.out + (((size_t)b * hkv + g) * G + h) * D + d;
+  const bool any = lsum != 0.f;  // no visible token -> 0 (NaN stays NaN)
+  E::store(out, 0, any ? o.x / lsum * a.out_scale : 0.f);
+  E::store(out, 1, any ? o.y / lsum * a.out_scale : 0.f);
+  E::store(out, 2, any ? o.z / lsum * a.out_scale : 0.f);
+  E::store(out, 3, any ? o.w / lsum * a.out_scale : 0.f);
 }
 
 // ------------------------------------------------------------------- host side
@@ -1548,8 +1563,9 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
                        0, stream, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || k.max_splits <= 1) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D, G>), dim3((unsigned)(work_heads * G), (unsigned)a.batch),
-                     dim3(D), 0, stream, k);
+  constexpr int kGh = G < 8 ? G : 8;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D, G>), dim3((unsigned)(work_heads * (G / kGh)), (unsigned)a.batch),
+                     dim3(kGh * D / 4), 0, stream, k);
   return hipGetLastError();
 }
 

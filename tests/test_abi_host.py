@@ -88,6 +88,7 @@ def test_decode_argument_errors(lib):
     assert decode(lib, batch=0, q=NULL) == 0       # empty batch: no-op before pointer checks
     assert decode(lib, ws=NULL, max_blocks=4000) == -4
     assert decode(lib, ws_bytes=16, max_blocks=4000) == -4
+    assert decode(lib, ws=ctypes.c_void_p(0x1008), max_blocks=4000) == -4   # partials are read 16 bytes at a time
 
 
 def test_alibi_entry_points_check_arguments(lib):
