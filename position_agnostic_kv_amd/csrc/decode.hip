@@ -1472,15 +1472,23 @@ int decode_head_split(int num_q_heads, int num_kv_heads, int impl) {
 int decode_split_blocks(int batch, int num_q_heads, int num_kv_heads, int max_blocks_per_seq,
                         int requested, int impl) {
   if (requested > 0) return requested;
-  // Enough (sequence, work head) units to fill the chip at two workgroups per
-  // CU: one split each.  Otherwise cut sequences so ~1024 workgroups run (the
-  // matrix-core kernels: ~512, one round of resident workgroups; a second,
-  // partial round cost 9 % on the 70B shape).
+  // Workgroups to aim at: one round of resident workgroups, as few as keep
+  // the chip's HBM share busy.  The matrix-core kernels run one workgroup per
+  // CU (256) where a workgroup's work per block is light -- bf16 pools up to
+  // 32 query heads, 8-bit pools up to 4 -- and two per CU (512) otherwise;
+  // the VALU kernel ~1024.  Measured: at ~0.5 GB of K/V and 120 (sequence, KV
+  // head) units, 2 splits instead of 4 took 8-9 % off GQA 4 and a 32-head
+  // group (bf16 and 8-bit), and 2 % off the 70B shape (128 units); the 8-bit
+  // 70B shape and a 64-head group ran 16-25 % slower at one workgroup per CU.
+  // Splits also cost their partials (written, then merged by a second kernel),
+  // and a second, partial round of workgroups cost 9 % on the 70B shape.
   const long long units = (long long)batch * num_kv_heads * decode_head_split(num_q_heads, num_kv_heads, impl);
-  if (units >= 512) return max_blocks_per_seq;
+  const int group = num_q_heads / num_kv_heads;
+  const bool light = (impl == kDecodeMma16 && group <= 32) || (impl == kDecodeMma8 && group <= 4);
+  const long long target = impl == kDecodeValu ? 1024 : light ? 256 : 512;
+  if (units >= target) return max_blocks_per_seq;  // one split each
   // splits per unit: as many as keep units x splits within the target (the
   // block count per split is rounded up, which never adds a split)
-  const long long target = impl == kDecodeValu ? 1024 : 512;
   const long long splits = target / units;
   long long sb = (max_blocks_per_seq + splits - 1) / splits;
   if (sb < 32) sb = 32;
