@@ -509,10 +509,14 @@ decode_mma8_kernel(const DecodeKernelArgs a) {
   static_assert(MODE == kRopeLazy, "8-bit pools: lazy RoPE");
   typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-  __shared__ float s_q[G][D];
+  // rows padded by 16 bytes: the rotation reads 16 heads' rows at once (lane
+  // = head) and the merge writes 4 heads' rows at once (lane group = head);
+  // unpadded, those rows start in the same LDS bank
+  __shared__ float s_q[G][D + 4];
+  __shared__ __attribute__((aligned(16))) float2 s_cs[kDecodeWaves][64];  // a rotation's (cos, sin) per frequency
   __shared__ float s_m[kDecodeWaves][G];
   __shared__ float s_l[kDecodeWaves][G];
-  __shared__ float s_o[kDecodeWaves][G][D];
+  __shared__ float s_o[kDecodeWaves][G][D + 4];
   __shared__ int s_bad;
 
   const int hkv = a.num_kv_heads;
@@ -588,18 +592,22 @@ decode_mma8_kernel(const DecodeKernelArgs a) {
   // q' = rot(q, n - off) * scale * log2(e) * k_scale for head t16, dims
   // 32 g4 .. 32 g4 + 31 (frequency d % 64, the pair of dim d is d ^ 64), as
   // bf16 hi + lo parts: S takes one product against each
+  // lane i evaluates frequency i into the wave's (cos, sin) table; a lane
+  // then reads its 32 frequencies as 16-byte broadcasts
   auto rotate = [&](int delta) {
     const double tt = (double)delta * (inv_freq * 0.15915494309189535);
     const float f = (float)(tt - rint(tt));
-    const float cs = __builtin_amdgcn_cosf(f), sn = __builtin_amdgcn_sinf(f);
+    s_cs[wave][lane] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+    __builtin_amdgcn_wave_barrier();
     const int hh = live ? t16 : 0;
     const int d0 = 32 * g4;
     const bool upper = d0 >= 64;
+    const float4 *cs4 = (const float4 *)&s_cs[wave][d0 & 63];
     float r[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
-      const int fi = (d0 + k) & 63;
-      const float c = __shfl(cs, fi), sv = __shfl(sn, fi);
+      const float4 pr = cs4[k >> 1];  // frequencies d0 + (k & ~1), + 1
+      const float c = (k & 1) ? pr.z : pr.x, sv = (k & 1) ? pr.w : pr.y;
       const float x = s_q[hh][d0 + k], y = s_q[hh][(d0 + k) ^ 64];
       const float v = (upper ? fmaf(x, c, y * sv) : fmaf(x, c, -(y * sv))) * a.scale_log2;
       r[k] = live ? v : 0.f;
@@ -1107,7 +1115,8 @@ decode_mma16_wide_kernel(const DecodeKernelArgs a) {
   constexpr bool ALIBI = MODE == kAlibi;
   static_assert(CT == 2 || CT == 4, "32 or 64 query heads");
   static_assert(RS >= 2 && RS * P == R, "at least one step of prefetch");
-  static_assert(kDecodeWaves * 16 * D * sizeof(float) <= BS * R * 2 * BLKB, "the partial outputs fit the ring");
+  constexpr int OROW = D + 4;  // merge rows padded by 16 bytes (else 16 lanes store into one bank)
+  static_assert(kDecodeWaves * 16 * OROW * sizeof(float) <= BS * R * 2 * BLKB, "the partial outputs fit the ring");
 
   __shared__ __attribute__((aligned(1024))) char s_ring[BS][R][2][BLKB];
   __shared__ float s_m[kDecodeWaves][16];
@@ -1356,7 +1365,7 @@ decode_mma16_wide_kernel(const DecodeKernelArgs a) {
     s_l[wave][t16] = lsum;
   }
   {
-    float *so = (float *)&s_ring[0][0][0][0] + wave * 16 * D + t16 * D + 4 * g4;
+    float *so = (float *)&s_ring[0][0][0][0] + (wave * 16 + t16) * OROW + 4 * g4;
 #pragma unroll
     for (int c = 0; c < 8; ++c) *(f32x4_t *)(so + 16 * c) = O[c];
   }
@@ -1378,7 +1387,7 @@ decode_mma16_wide_kernel(const DecodeKernelArgs a) {
     for (int s2 = 0; s2 < BS; ++s2) {
       const int w2 = s2 * CT + hc;
       const float f = s_m[w2][hh] == -INFINITY ? 0.f : fast_exp2(s_m[w2][hh] - mx);
-      o = fmaf(po[(w2 * 16 + hh) * D + d], f, o);
+      o = fmaf(po[(w2 * 16 + hh) * OROW + d], f, o);
       ls = fmaf(s_l[w2][hh], f, ls);
     }
     if (flagged) {

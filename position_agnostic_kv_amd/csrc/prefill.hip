@@ -720,7 +720,10 @@ struct WidenArgs {
 // V is transposed through LDS so that every store is a contiguous 1 KiB.
 // Widening E4M3 to bf16 is exact.
 __global__ void __launch_bounds__(4 * kWave) widen_fp8_kernel(const WidenArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[4][kBlockTokens * 128];
+  // V rows padded to 272 bytes: the transposing stores write 4 rows at once
+  // (one per lane group), which unpadded start in the same LDS bank
+  constexpr int VROW = 136;
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[4][kBlockTokens * VROW];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const size_t item = (size_t)blockIdx.x * 4 + wave;
@@ -765,15 +768,18 @@ __global__ void __launch_bounds__(4 * kWave) widen_fp8_kernel(const WidenArgs a)
       const uint32_t c = dw4(vc[i], jj);
       const uint32_t lo = e4m3x2_to_bf16x2<false>(c), hi = e4m3x2_to_bf16x2<true>(c);
       const int dim = 16 * (4 * i + jj) + t;
-      sv[(4 * gq + 0) * 128 + dim] = (uint16_t)(lo & 0xffffu);
-      sv[(4 * gq + 1) * 128 + dim] = (uint16_t)(lo >> 16);
-      sv[(4 * gq + 2) * 128 + dim] = (uint16_t)(hi & 0xffffu);
-      sv[(4 * gq + 3) * 128 + dim] = (uint16_t)(hi >> 16);
+      sv[(4 * gq + 0) * VROW + dim] = (uint16_t)(lo & 0xffffu);
+      sv[(4 * gq + 1) * VROW + dim] = (uint16_t)(lo >> 16);
+      sv[(4 * gq + 2) * VROW + dim] = (uint16_t)(hi & 0xffffu);
+      sv[(4 * gq + 3) * VROW + dim] = (uint16_t)(hi >> 16);
     }
   }
   __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in order
 #pragma unroll
-  for (int r = 0; r < 4; ++r) vo[64 * r + lane] = ((const uint4 *)sv)[64 * r + lane];
+  for (int r = 0; r < 4; ++r) {
+    const int q = 64 * r + lane;  // 16-byte chunk q of the block: row q / 16, chunk q % 16
+    vo[q] = *(const uint4 *)(sv + (q / 16) * VROW + (q % 16) * 8);
+  }
 }
 
 size_t prefill_fp8_workspace_size(int batch, int max_blocks, int num_kv_heads) {

@@ -14,7 +14,7 @@ slot c ^ swz(r), swz(r) = 2 (r mod 8).  This file checks, on the CPU, that
       quads of one half-wave whose quad index (bits 2..4 of the lane) has the
       same bit parity;
     - ds_write_b128: banks repeat every 128 bytes (8 slots); a wave is served
-      eight consecutive lanes at a time (no hot store uses it now).
+      eight consecutive lanes at a time.
   Two lanes of one group that touch different addresses in one slot
   conflict.  (Reading one address from several lanes does not.)
 
@@ -121,3 +121,39 @@ def test_fp8_widening_pass_places_every_code():
         assert v_dst[byte] == int(v_src[byte])
     assert sorted(k_dst.values()) == list(range(2048))
     assert sorted(v_dst.values()) == list(range(2048))
+
+
+def _write_b128_groups():
+    return [list(range(i, i + 8)) for i in range(0, 64, 8)]
+
+
+def test_staged_query_rows_are_padded():
+    """8-bit decode: a rotation reads the staged query with lane l = 16 g + t
+    taking head t's dims 32 g + 4 k' .. + 3 (and their rotate-half partners
+    64 apart) with ds_read_b128.  Rows of 128 floats put the 16 heads in one
+    bank; rows of 132 floats (16 bytes of padding) make the reads of groups of
+    up to 8 heads conflict-free and cut a 16-head group's conflicts 7x."""
+    def extra(row, heads):
+        tot = 0
+        for upper, kq in itertools.product((0, 64), range(8)):
+            addrs = []
+            for lane in range(64):
+                t, g = lane & 15, lane >> 4
+                h = t if t < heads else 0          # lanes past the group read row 0 (a broadcast)
+                addrs.append((h * row + ((32 * g + 4 * kq) ^ upper)) * 4)
+            tot += conflicts(addrs, read_b128_groups(), 256)
+        return tot
+    assert extra(132, 4) == 0 and extra(132, 8) == 0
+    assert extra(128, 8) > 0
+    assert extra(132, 16) * 7 == extra(128, 16)
+
+
+def test_wide_merge_stores_are_conflict_free():
+    """Multi-query decode: at the merge, lane (t, g) stores head t's four
+    dims 4 g + 16 c .. + 3 as one ds_write_b128 into rows of 132 floats
+    (unpadded rows of 128 put eight consecutive lanes in one slot)."""
+    for c in range(8):
+        padded = [((lane & 15) * 132 + 4 * (lane >> 4) + 16 * c) * 4 for lane in range(64)]
+        plain = [((lane & 15) * 128 + 4 * (lane >> 4) + 16 * c) * 4 for lane in range(64)]
+        assert conflicts(padded, _write_b128_groups(), 128) == 0
+        assert conflicts(plain, _write_b128_groups(), 128) > 0
