@@ -513,7 +513,10 @@ decode_mma8_kernel(const DecodeKernelArgs a) {
   // = head) and the merge writes 4 heads' rows at once (lane group = head);
   // unpadded, those rows start in the same LDS bank
   __shared__ float s_q[G][D + 4];
-  __shared__ __attribute__((aligned(16))) float2 s_cs[kDecodeWaves][64];  // a rotation's (cos, sin) per frequency
+  // a rotation's (cos, sin) per frequency; frequencies 32..63 sit 16 bytes
+  // further on, so that the two lane groups reading them at once do not
+  // share a bank slot
+  __shared__ __attribute__((aligned(16))) float2 s_cs[kDecodeWaves][64 + 2];
   __shared__ float s_m[kDecodeWaves][G];
   __shared__ float s_l[kDecodeWaves][G];
   __shared__ float s_o[kDecodeWaves][G][D + 4];
@@ -597,12 +600,12 @@ decode_mma8_kernel(const DecodeKernelArgs a) {
   auto rotate = [&](int delta) {
     const double tt = (double)delta * (inv_freq * 0.15915494309189535);
     const float f = (float)(tt - rint(tt));
-    s_cs[wave][lane] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+    s_cs[wave][lane + (lane >= 32 ? 2 : 0)] = make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
     __builtin_amdgcn_wave_barrier();
     const int hh = live ? t16 : 0;
     const int d0 = 32 * g4;
     const bool upper = d0 >= 64;
-    const float4 *cs4 = (const float4 *)&s_cs[wave][d0 & 63];
+    const float4 *cs4 = (const float4 *)&s_cs[wave][(d0 & 63) + ((d0 & 63) >= 32 ? 2 : 0)];
     float r[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k) {

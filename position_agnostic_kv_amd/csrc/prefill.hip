@@ -760,25 +760,39 @@ __global__ void __launch_bounds__(4 * kWave) widen_fp8_kernel(const WidenArgs a)
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
   }
+  // Lanes t and t ^ 1 hold dims 2m and 2m + 1 (m = t / 2) of the same four
+  // rows.  One swap gives each the other's values for two rows, so that each
+  // writes whole 4-byte words (both dims): the even lane rows 4 gq and
+  // 4 gq + 1, the odd lane rows 4 gq + 2 and 4 gq + 3.
   uint16_t *sv = s_v[wave];
+  const bool odd = t & 1;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const uint32_t c = dw4(vc[i], jj);
-      const uint32_t lo = e4m3x2_to_bf16x2<false>(c), hi = e4m3x2_to_bf16x2<true>(c);
-      const int dim = 16 * (4 * i + jj) + t;
-      sv[(4 * gq + 0) * VROW + dim] = (uint16_t)(lo & 0xffffu);
-      sv[(4 * gq + 1) * VROW + dim] = (uint16_t)(lo >> 16);
-      sv[(4 * gq + 2) * VROW + dim] = (uint16_t)(hi & 0xffffu);
-      sv[(4 * gq + 3) * VROW + dim] = (uint16_t)(hi >> 16);
+      const uint32_t lo = e4m3x2_to_bf16x2<false>(c), hi = e4m3x2_to_bf16x2<true>(c);  // rows (0,1), (2,3)
+      const uint32_t give = odd ? lo : hi;
+      const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, kDppQuadXor1, 0xf, 0xf, false);
+      const uint32_t mine = odd ? hi : lo;
+      // word of the first row: (even lane's value, odd lane's value) in dim order
+      const uint32_t w0 = odd ? ((got & 0xffffu) | (mine << 16)) : ((mine & 0xffffu) | (got << 16));
+      const uint32_t w1 = odd ? ((got >> 16) | (mine & 0xffff0000u)) : ((mine >> 16) | (got & 0xffff0000u));
+      const int row = 4 * gq + (odd ? 2 : 0);
+      const int dim = 16 * (4 * i + jj) + (t & ~1);
+      *(uint32_t *)(sv + row * VROW + dim) = w0;
+      *(uint32_t *)(sv + (row + 1) * VROW + dim) = w1;
     }
   }
   __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in order
 #pragma unroll
+  // read back row-major; the 16 lanes of a row take its chunks rotated by
+  // the row, so that with the padded rows every 16-lane group of a 16-byte
+  // read meets 16 different bank slots
   for (int r = 0; r < 4; ++r) {
-    const int q = 64 * r + lane;  // 16-byte chunk q of the block: row q / 16, chunk q % 16
-    vo[q] = *(const uint4 *)(sv + (q / 16) * VROW + (q % 16) * 8);
+    const int row = 4 * r + lane / 16;
+    const int c = (lane - lane / 16) & 15;
+    vo[row * 16 + c] = *(const uint4 *)(sv + row * VROW + c * 8);
   }
 }
 

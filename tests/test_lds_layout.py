@@ -102,25 +102,39 @@ def test_fp8_widening_pass_places_every_code():
     """The widening pass for 8-bit pools reads a (block, KV head) record in
     the pool's lane order and writes the bf16 block row-major (token * 128 +
     dim).  Lane l = 16 g + t, chunk i: K code x goes to row t, dim
-    32 g + 16 i + x; V dword jj, byte e goes (through the wave's LDS
-    transpose) to row 4 g + e, dim 16 (4 i + jj) + t.  Checked against the
-    pool byte order the host-side converter uses: each byte lands exactly
-    where its logical element belongs, and every element is written once."""
+    32 g + 16 i + x.  V: dword jj of chunk i holds, byte e, row 4 g + e of
+    dim 16 (4 i + jj) + t; lanes t and t ^ 1 swap half of their widened
+    values so that the even lane writes rows 4 g, 4 g + 1 and the odd lane
+    rows 4 g + 2, 4 g + 3 as 4-byte words of dims (t & ~1, t | 1).  Checked
+    against the pool byte order the host-side converter uses: each element
+    lands where its logical index belongs, every element written once."""
     import workloads as W
     k_src, v_src = W._fp8_lane_order()   # record byte -> token * 128 + dim
-    k_dst, v_dst = {}, {}
     for lane in range(64):
         t, g = lane & 15, lane >> 4
         for i, x in itertools.product(range(2), range(16)):
-            byte = 1024 * i + 16 * lane + x
-            k_dst[byte] = t * 128 + 32 * g + 16 * i + x
-            jj, e = x // 4, x % 4
-            v_dst[byte] = (4 * g + e) * 128 + 16 * (4 * i + jj) + t
-    for byte in range(2048):
-        assert k_dst[byte] == int(k_src[byte])
-        assert v_dst[byte] == int(v_src[byte])
-    assert sorted(k_dst.values()) == list(range(2048))
-    assert sorted(v_dst.values()) == list(range(2048))
+            assert t * 128 + 32 * g + 16 * i + x == int(k_src[1024 * i + 16 * lane + x])
+    # V: simulate the lanes, the pair swap and the word stores
+    val = {}                              # (lane, i, jj, e) -> logical index the code holds
+    for lane, i, jj, e in itertools.product(range(64), range(2), range(4), range(4)):
+        val[(lane, i, jj, e)] = int(v_src[1024 * i + 16 * lane + 4 * jj + e])
+    lds = {}
+    for lane, i, jj in itertools.product(range(64), range(2), range(4)):
+        t, g = lane & 15, lane >> 4
+        odd = t & 1
+        partner = lane ^ 1
+        mine = [val[(lane, i, jj, e)] for e in ((2, 3) if odd else (0, 1))]
+        got = [val[(partner, i, jj, e)] for e in ((2, 3) if odd else (0, 1))]
+        row = 4 * g + (2 if odd else 0)
+        dim = 16 * (4 * i + jj) + (t & ~1)
+        for r in range(2):
+            lo, hi = (got[r], mine[r]) if odd else (mine[r], got[r])   # (dim, dim + 1)
+            for d, v in ((dim, lo), (dim + 1, hi)):
+                assert (row + r, d) not in lds
+                lds[(row + r, d)] = v
+    assert len(lds) == 2048
+    for (row, d), v in lds.items():
+        assert v == row * 128 + d
 
 
 def _write_b128_groups():
@@ -157,3 +171,38 @@ def test_wide_merge_stores_are_conflict_free():
         plain = [((lane & 15) * 128 + 4 * (lane >> 4) + 16 * c) * 4 for lane in range(64)]
         assert conflicts(padded, _write_b128_groups(), 128) == 0
         assert conflicts(plain, _write_b128_groups(), 128) > 0
+
+
+def test_widening_readback_covers_rows_without_conflicts():
+    """Widening pass: the transposed V block sits in rows of 272 bytes; lane
+    (row offset lane // 16, chunk (lane - lane // 16) mod 16) reads each row
+    back once, in 16-byte reads free of bank conflicts (the plain chunk order
+    meets a conflict in each read with the padded rows)."""
+    for r in range(4):
+        seen, addrs = set(), []
+        for lane in range(64):
+            row = 4 * r + lane // 16
+            c = (lane - lane // 16) % 16
+            seen.add((row, c))
+            addrs.append(row * 272 + c * 16)
+        assert len(seen) == 64
+        assert conflicts(addrs, read_b128_groups(), 256) == 0
+        plain = [(4 * r + lane // 16) * 272 + (lane % 16) * 16 for lane in range(64)]
+        assert conflicts(plain, read_b128_groups(), 256) > 0
+
+
+def test_rotation_table_reads_are_conflict_free():
+    """8-bit decode rotation: lane group g reads (cos, sin) of frequencies
+    (32 g mod 64) + 2 k', + 1 as one 16-byte read; frequencies 32..63 are
+    stored 16 bytes further on, which keeps groups 0 and 1 in different
+    slots (adjacent they would share every slot)."""
+    def extra(pad):
+        tot = 0
+        for kq in range(16):
+            addrs = []
+            for lane in range(64):
+                base = (32 * (lane >> 4)) & 63
+                addrs.append((base + 2 * kq + (pad if base >= 32 else 0)) * 8)
+            tot += conflicts(addrs, read_b128_groups(), 256)
+        return tot
+    assert extra(2) == 0 and extra(0) > 0
