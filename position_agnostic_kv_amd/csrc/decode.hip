@@ -1083,12 +1083,13 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
 // The kernel above takes up to 16 heads (one MFMA column tile); giving a larger
 // group to G / 16 workgroups would make each of them walk every block again.
 // Here one workgroup takes all G = 16 CT heads of a KV head, so each K/V block
-// is read from memory once.  Its 4 waves form BS = 4 / CT block streams of CT
-// waves: wave w takes column tile w % CT (heads 16 (w % CT) ..) and stream
-// w / CT, and the CT waves of a stream share each block of that stream
-// through LDS.  A stream owns R = 8 / BS ring slots (the workgroup keeps
-// 8 blocks, 64 KiB, in flight, as the kernel above does): the block of step i
-// goes to slot i % R, R - 1 steps ahead.  Each of the stream's waves issues
+// is read from memory once.  Its NW waves (4 for 32 heads; 8 for 64, one
+// workgroup per CU, so that each wave takes one block per step) form
+// BS = NW / CT = 2 block streams of CT waves: wave w takes column tile w % CT
+// (heads 16 (w % CT) ..) and stream w / CT, and the CT waves of a stream share
+// each block of that stream through LDS.  A stream owns R = 4 ring slots (the
+// workgroup keeps 8 blocks, 64 KiB, in LDS, as the kernel above does): the
+// block of step i goes to slot i % R, R - 1 steps ahead.  Each of the stream's waves issues
 // IPW = 8 / CT of the block's 8 DMA instructions (1 KiB each, K then V), and
 // one workgroup barrier per step both publishes the landed block to every
 // reader and frees the slot all waves read one step before.  Streams that run
@@ -1097,14 +1098,17 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
 // and block the products, the lazy rotation, the masking and the softmax are
 // those of the kernel above, for the wave's 16 heads; the streams' partial
 // results are merged in LDS at the end.
+constexpr int wide_waves(int ct) { return ct == 4 ? 8 : kDecodeWaves; }
+
 template <int CT, int MODE>
-__global__ void __launch_bounds__(kDecodeWaves * kWave, kMma16WorkgroupsPerCu)
+__global__ void __launch_bounds__(wide_waves(CT) * kWave, CT == 4 ? 1 : kMma16WorkgroupsPerCu)
 decode_mma16_wide_kernel(const DecodeKernelArgs a) {
   using E = Elem<bf16>;
   constexpr int G = 16 * CT;               // query heads of the workgroup
-  constexpr int BS = kDecodeWaves / CT;    // block streams
+  constexpr int NW = wide_waves(CT);       // waves of the workgroup
+  constexpr int BS = NW / CT;              // block streams
   constexpr int R = 8 / BS;                // ring slots per stream
-  constexpr int P = CT == 4 ? 2 : 1;       // blocks of a stream per step
+  constexpr int P = 1;                     // blocks of a stream per step
   constexpr int RS = R / P;                // steps the ring holds
   constexpr int D = 128;
   constexpr int CPR = D / 8;               // 16-byte chunks per row
@@ -1113,18 +1117,19 @@ decode_mma16_wide_kernel(const DecodeKernelArgs a) {
   constexpr int IPW = 2 * IPB / CT;        // DMA instructions per wave and block
   constexpr int ROWB = D * 2;
   constexpr int BLKB = kBlockTokens * ROWB;  // 4 KiB: one block of one KV head
-  constexpr int NT = kDecodeWaves * kWave;
+  constexpr int NT = NW * kWave;
   constexpr bool EAGER = MODE == kRopeEager;
   constexpr bool ALIBI = MODE == kAlibi;
   static_assert(CT == 2 || CT == 4, "32 or 64 query heads");
   static_assert(RS >= 2 && RS * P == R, "at least one step of prefetch");
   constexpr int OROW = D + 4;  // merge rows padded by 16 bytes (else 16 lanes store into one bank)
-  static_assert(kDecodeWaves * 16 * OROW * sizeof(float) <= BS * R * 2 * BLKB, "the partial outputs fit the ring");
-
-  __shared__ __attribute__((aligned(1024))) char s_ring[BS][R][2][BLKB];
-  __shared__ float s_m[kDecodeWaves][16];
-  __shared__ float s_l[kDecodeWaves][16];
-  __shared__ int s_bad[kDecodeWaves];
+  // the ring, and after the loop the waves' partial outputs [NW][16][OROW]
+  constexpr int RINGB = BS * R * 2 * BLKB;
+  constexpr int MERGEB = NW * 16 * OROW * (int)sizeof(float);
+  __shared__ __attribute__((aligned(1024))) char s_ring[RINGB > MERGEB ? RINGB : MERGEB];
+  __shared__ float s_m[NW][16];
+  __shared__ float s_l[NW][16];
+  __shared__ int s_bad[NW];
 
   const int hkv = a.num_kv_heads;
   const int unit = (int)blockIdx.x;
@@ -1217,7 +1222,7 @@ decode_mma16_wide_kernel(const DecodeKernelArgs a) {
       v_off[c] = (uint32_t)(vr * ROWB + (((dim / 8) ^ swz<CPR>(vr)) * 16) + (dim % 8) * 2);
     }
   }
-  char *ring = &s_ring[st][0][0][0];
+  char *ring = s_ring + st * (R * 2 * BLKB);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr_t)ring;
 
   const int blk0 = split * a.split_blocks;
@@ -1368,7 +1373,7 @@ decode_mma16_wide_kernel(const DecodeKernelArgs a) {
     s_l[wave][t16] = lsum;
   }
   {
-    float *so = (float *)&s_ring[0][0][0][0] + (wave * 16 + t16) * OROW + 4 * g4;
+    float *so = (float *)s_ring + (wave * 16 + t16) * OROW + 4 * g4;
 #pragma unroll
     for (int c = 0; c < 8; ++c) *(f32x4_t *)(so + 16 * c) = O[c];
   }
@@ -1376,9 +1381,11 @@ decode_mma16_wide_kernel(const DecodeKernelArgs a) {
   __syncthreads();
 
   const bool single = nsplit == 1;
-  const bool flagged = (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) != 0;
+  bool flagged = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) flagged |= s_bad[w] != 0;
   const size_t part = ((size_t)b * hkv + g) * a.max_splits + split;
-  const float *po = (const float *)&s_ring[0][0][0][0];
+  const float *po = (const float *)s_ring;
   for (int i = tid; i < G * D; i += NT) {
     const int h = i / D, d = i % D;
     const int hc = h / 16, hh = h % 16;
@@ -1486,8 +1493,9 @@ int decode_split_blocks(int batch, int num_q_heads, int num_kv_heads, int max_bl
   if (requested > 0) return requested;
   // Workgroups to aim at: one round of resident workgroups, as few as keep
   // the chip's HBM share busy.  The matrix-core kernels run one workgroup per
-  // CU (256) where a workgroup's work per block is light -- bf16 pools up to
-  // 32 query heads, 8-bit pools up to 4 -- and two per CU (512) otherwise;
+  // CU (256) where a workgroup's work per block is light -- bf16 pools (a
+  // 64-head group runs 8 waves, one workgroup per CU), 8-bit pools up to 4
+  // heads -- and two per CU (512) otherwise;
   // the VALU kernel ~1024.  Measured: at ~0.5 GB of K/V and 120 (sequence, KV
   // head) units, 2 splits instead of 4 took 8-9 % off GQA 4 and a 32-head
   // group (bf16 and 8-bit), and 2 % off the 70B shape (128 units); the 8-bit
@@ -1496,7 +1504,7 @@ int decode_split_blocks(int batch, int num_q_heads, int num_kv_heads, int max_bl
   // and a second, partial round of workgroups cost 9 % on the 70B shape.
   const long long units = (long long)batch * num_kv_heads * decode_head_split(num_q_heads, num_kv_heads, impl);
   const int group = num_q_heads / num_kv_heads;
-  const bool light = (impl == kDecodeMma16 && group <= 32) || (impl == kDecodeMma8 && group <= 4);
+  const bool light = impl == kDecodeMma16 || (impl == kDecodeMma8 && group <= 4);
   const long long target = impl == kDecodeValu ? 1024 : light ? 256 : 512;
   if (units >= target) return max_blocks_per_seq;  // one split each
   // splits per unit: as many as keep units x splits within the target (the
@@ -1573,8 +1581,8 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_mma8_kernel<G, MODE>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave), 0, stream,
                        k);
   else if constexpr (IMPL == kMma16Wide)
-    hipLaunchKernelGGL((decode_mma16_wide_kernel<G / 16, MODE>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave),
-                       0, stream, k);
+    hipLaunchKernelGGL((decode_mma16_wide_kernel<G / 16, MODE>), dim3((unsigned)grid),
+                       dim3(wide_waves(G / 16) * kWave), 0, stream, k);
   else if constexpr (IMPL == kMma16)
     hipLaunchKernelGGL((decode_mma16_kernel<G, MODE>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave), 0, stream,
                        k);
