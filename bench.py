@@ -386,8 +386,8 @@ def shapes_main(args):
     del d, out
     case.q = case.k_pool = case.v_pool = case.k_new = case.v_new = None
     torch.cuda.empty_cache()
-    # documents of any token count: tiles are cut at document starts, so the
-    # partly filled last blocks cost MFMA work on masked slots
+    # documents of any token count: a document's partly filled last block
+    # costs MFMA work on its masked slots
     case = W.make("llama8b_prefill_ragged")
     W.materialize_torch(case, dev)
     d = DeviceInputs(case, dev)

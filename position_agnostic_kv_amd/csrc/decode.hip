@@ -1107,7 +1107,7 @@ decode_mma16_wide_kernel(const DecodeKernelArgs a) {
   constexpr int G = 16 * CT;               // query heads of the workgroup
   constexpr int NW = wide_waves(CT);       // waves of the workgroup
   constexpr int BS = NW / CT;              // block streams
-  constexpr int R = 8 / BS;                // ring slots per stream
+  constexpr int R = 8 / BS;                // ring slots per stream (4)
   constexpr int P = 1;                     // blocks of a stream per step
   constexpr int RS = R / P;                // steps the ring holds
   constexpr int D = 128;

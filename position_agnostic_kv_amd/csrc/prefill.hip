@@ -13,9 +13,9 @@
 //     FLOPs per document instead of 3*N*D per tile);
 //   * a K/V tile is always four whole blocks, whether or not it straddles a
 //     document boundary; a block whose offset differs from the query's is
-//     rotated once in LDS by the difference (the pages' relative rotation of
-//     a staged tile), by the wave that loaded it.  Tiles are therefore never
-//     cut short at a document's end.
+//     rotated once in LDS by the difference (the relative rotation of a
+//     staged key tile, "Implementação Técnica", Prefilling), by the wave that
+//     loaded it.  Tiles are therefore never cut short at a document's end.
 //
 // Structure (FlashAttention tiling, ai-engineering.academy "Flash
 // Attention"): the query tile stays in registers, K/V tiles are staged through
