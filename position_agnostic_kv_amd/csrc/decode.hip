@@ -1492,20 +1492,17 @@ int decode_split_blocks(int batch, int num_q_heads, int num_kv_heads, int max_bl
                         int requested, int impl) {
   if (requested > 0) return requested;
   // Workgroups to aim at: one round of resident workgroups, as few as keep
-  // the chip's HBM share busy.  The matrix-core kernels run one workgroup per
-  // CU (256) where a workgroup's work per block is light -- bf16 pools (a
-  // 64-head group runs 8 waves, one workgroup per CU), 8-bit pools up to 4
-  // heads -- and two per CU (512) otherwise;
-  // the VALU kernel ~1024.  Measured: at ~0.5 GB of K/V and 120 (sequence, KV
-  // head) units, 2 splits instead of 4 took 8-9 % off GQA 4 and a 32-head
-  // group (bf16 and 8-bit), and 2 % off the 70B shape (128 units); the 8-bit
-  // 70B shape and a 64-head group ran 16-25 % slower at one workgroup per CU.
+  // the chip's HBM share busy.  The bf16 matrix-core kernels run one
+  // workgroup per CU (256; a 64-head group runs 8 waves), the 8-bit kernel
+  // two (512), the VALU kernel ~1024.  Measured with launches interleaved: at
+  // ~0.5 GB of K/V and 120 (sequence, KV head) units, 2 splits instead of 4
+  // took 8-9 % off bf16 GQA 4 and a 32-head group, and 2 % off the bf16 70B
+  // shape (128 units); the 8-bit kernel (three workgroups fit a CU) was 34 %
+  // slower at 2 splits than at 4 there, and 3, 5 or 6 were also slower.
   // Splits also cost their partials (written, then merged by a second kernel),
   // and a second, partial round of workgroups cost 9 % on the 70B shape.
   const long long units = (long long)batch * num_kv_heads * decode_head_split(num_q_heads, num_kv_heads, impl);
-  const int group = num_q_heads / num_kv_heads;
-  const bool light = impl == kDecodeMma16 || (impl == kDecodeMma8 && group <= 4);
-  const long long target = impl == kDecodeValu ? 1024 : light ? 256 : 512;
+  const long long target = impl == kDecodeValu ? 1024 : impl == kDecodeMma16 ? 256 : 512;
   if (units >= target) return max_blocks_per_seq;  // one split each
   // splits per unit: as many as keep units x splits within the target (the
   // block count per split is rounded up, which never adds a split)
