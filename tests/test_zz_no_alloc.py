@@ -43,6 +43,15 @@ def test_noalloc_decode_two_calls_second_smaller():
     _check(small, 4)
 
 
+def test_noalloc_decode_multi_query_automatic_splits():
+    """A 64-head group (the 8-wave multi-query kernel) and a 32-head group,
+    splits chosen by the library, partials in the fixed scratch."""
+    wide = W.decode_case(503, 2, 64, 1, 128, [3008, 1200], (2, 16), offsets="random", name="noalloc_g64")
+    mid = W.decode_case(504, 3, 32, 1, 128, [896, 2048, 64], (2, 10), name="noalloc_g32")
+    _check(wide, 0)
+    _check(mid, 0)
+
+
 def test_noalloc_decode_rejects_partials_beyond_the_scratch():
     b, hq, hkv, d, max_blocks = 256, 64, 8, 128, 2048
     need = pak.decode_workspace_size(b, hq, hkv, d, max_blocks, 4)
