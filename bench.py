@@ -11,8 +11,12 @@ bytes of the attended tokens / decode-pass time); the prefill attention
 TFLOP/s rides along.  After the timed steps, the metric's other two decode
 workloads (Llama-3.1-70B-shaped decode, and the Zipf-skewed document-reuse
 mix) are each timed the same way as a decode pass of their own, with their
-own roofline and oracle baseline (keys "llama70b_decode", "zipf_reuse_decode").  Kernel durations come from HIP events recorded on the
-stream the library launches on (torch's current stream).
+own roofline and oracle baseline (keys "llama70b_decode", "zipf_reuse_decode").
+Kernel durations come from HIP events recorded on the stream the library
+launches on (torch's current stream).  Before the W counted warm-up steps,
+untimed steps run until the clock has settled (the prefill kernel's time
+stops changing; "clock_settle" in the record keeps the cold figures;
+--no-settle skips this).
 """
 
 import argparse
@@ -662,16 +666,33 @@ def trace_summary_main(args):
     --no-cpu-baseline`): per-kernel calls and durations."""
     trace_dir = args.trace_summary
     durs = {}
-    for name, start, end in _rocpd_rows(trace_dir, "select name, start, end from kernels"):
-        durs.setdefault(_kernel_key(name), []).append((int(end) - int(start)) / 1000.0)
+    rows = sorted(((_kernel_key(n), int(a), int(b)) for n, a, b in
+                   _rocpd_rows(trace_dir, "select name, start, end from kernels")), key=lambda r: r[1])
+    for key, start, end in rows:
+        durs.setdefault(key, []).append((end - start) / 1000.0)
+    # the timed steps: the last K prefill dispatches, each with the decode dispatch before it
+    pf_key, dec_key = "lazyattn::prefill_kernel<128, 4, 0>", "lazyattn::decode_mma16_kernel<4, 0>"
+    pf_idx = [i for i, r in enumerate(rows) if r[0] == pf_key][-args.steps:]
+    timed_pf = [(rows[i][2] - rows[i][1]) / 1000.0 for i in pf_idx]
+    timed_dec = []
+    for i in pf_idx:
+        j = max(k for k in range(i) if rows[k][0] == dec_key)
+        timed_dec.append((rows[j][2] - rows[j][1]) / 1000.0)
     cmd = (f"rocprofv3 --kernel-trace --stats -d {trace_dir} -o run -- python -u bench.py --steps {args.steps} "
            f"--warmup {args.warmup} --no-cpu-baseline")
     lines = ["# rocprofv3 kernel trace: bench.py step (8B decode + 8B prefill)", "",
              "Command (GPU box, from the repository root):", "", f"    {cmd}", "",
              f"Summarised by `python bench.py --trace-summary {trace_dir} --steps {args.steps} --warmup "
              f"{args.warmup}`.  Each step is kvcache_append + lazyattn_decode, then kvcache_append + "
-             "lazyattn_prefill; the calls include the warm-up steps.  Torch's fill, copy and random kernels "
-             "are input generation or the copy roof, outside the timed step.", "",
+             "lazyattn_prefill.  Torch's fill, copy and random kernels are input generation or the copy roof, "
+             "outside the timed step.", "",
+             f"The {len(pf_idx)} timed steps (the last {len(pf_idx)} dispatches of `{pf_key}`, each with the "
+             f"`{dec_key}` dispatch before it; the bench line's kernel times cover the same dispatches):", "",
+             "kernel | calls | avg us | median us", "---|---|---|---",
+             f"{dec_key} | {len(timed_dec)} | {np.mean(timed_dec):.1f} | {np.median(timed_dec):.1f}",
+             f"{pf_key} | {len(timed_pf)} | {np.mean(timed_pf):.1f} | {np.median(timed_pf):.1f}", "",
+             "Every dispatch of the run (the settling steps, warm-up and timed steps, then the other decode "
+             "workloads' passes):", "",
              "kernel | calls | avg us | median us | total us | %", "---|---|---|---|---|---"]
     tot = sum(sum(v) for v in durs.values())
     for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
@@ -806,6 +827,34 @@ def decode_workload_line(name, args, dev):
     return rec
 
 
+def clock_settle(step, chunk=10, min_steps=40, max_steps=400, tol=0.005):
+    """Untimed steps, before the counted warm-up, until the clock has settled.
+
+    From idle (and again after as little as 0.2 s without work) MI355X takes
+    about 30-40 steps of this workload (40-50 ms) to reach its steady clock: in
+    that stretch the prefill kernel, which is power-limited, runs up to 25 %
+    slower, while the memory-bound decode kernel does not change.  Steps run
+    in chunks of `chunk` until the chunk mean of the prefill kernel's time
+    moves by less than `tol` (at least `min_steps`, at most `max_steps`).
+    Returns the step count and the chunk means, so the cold figures stay in
+    the record."""
+    import torch
+
+    means, done = [], 0
+    while done < max_steps:
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(chunk)]
+        for e in ev:
+            step(e)
+        torch.cuda.synchronize()
+        means.append(float(np.mean([e[3].elapsed_time(e[4]) for e in ev])))
+        done += chunk
+        if done >= min_steps and abs(means[-1] - means[-2]) <= tol * means[-2]:
+            break
+    return {"steps": done, "prefill_kernel_ms_per_10_steps": [round(m, 4) for m in means],
+            "note": "untimed steps before the counted warm-up, run until the prefill kernel's time "
+                    "stops changing (the GPU's clock ramps up from idle); --no-settle skips them"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -814,6 +863,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-blocks", type=int, default=0)
+    ap.add_argument("--no-settle", action="store_true",
+                    help="skip the untimed steps that bring the clock to its steady state before the warm-up")
     ap.add_argument("--overhead", action="store_true",
                     help="time the lazy kernels against the non-lazy baseline instead (one JSON line)")
     ap.add_argument("--shapes", action="store_true",
@@ -901,6 +952,7 @@ def main():
         if ev is not None:
             ev[4].record()
 
+    settle = None if args.no_settle else clock_settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -979,6 +1031,7 @@ def main():
                               "per second, median of 10 (a read+write stream, not the read-only "
                               "pattern of decode)"},
         "wall_s_timed": round(wall, 3),
+        "clock_settle": settle,
         "roofline": {
             "kernel": "lazyattn::decode_mma16_kernel<4, 0>",
             "bound": "hbm",
