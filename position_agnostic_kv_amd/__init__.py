@@ -23,7 +23,8 @@ __all__ = [
     "LazyAttnError", "lib_path", "load_library", "version", "kvcache_append",
     "decode_workspace_size", "lazyattn_decode", "lazyattn_prefill", "lazyattn_decode_eager",
     "lazyattn_prefill_eager", "lazyattn_decode_alibi", "lazyattn_prefill_alibi", "kvcache_append_fp8",
-    "lazyattn_decode_fp8", "lazyattn_prefill_fp8", "prefill_fp8_workspace_size", "lazyattn_decode_noalloc", "BLOCK_TOKENS",
+    "lazyattn_decode_fp8", "lazyattn_prefill_fp8", "prefill_fp8_workspace_size", "lazyattn_decode_noalloc",
+    "DecodePlan", "decode_plan", "decode_planned_workspace_size", "lazyattn_decode_planned", "BLOCK_TOKENS",
 ]
 
 BLOCK_TOKENS = 16
@@ -63,6 +64,11 @@ _SIGNATURES["lazyattn_decode_fp8"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32,
 _SIGNATURES["lazyattn_prefill_fp8"] = (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
                                               _i32, _i32, _i32, _i32, _f32, _f32, _f32, _f32, _vp, _sz, _vp])
 _SIGNATURES["lazyattn_prefill_fp8_workspace_size"] = (_sz, [_i32, _i32, _i32, _i32])
+_SIGNATURES["lazyattn_decode_plan_ints"] = (_sz, [_i32, _i32, _i32])
+_SIGNATURES["lazyattn_decode_plan"] = (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _vp])
+_SIGNATURES["lazyattn_decode_planned_workspace_size"] = (_sz, [_i32, _i32, _i32, _i32, _i32])
+_SIGNATURES["lazyattn_decode_planned"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                                                 _i32, _i32, _f32, _f32, _vp, _i32, _i32, _vp, _sz, _vp])
 
 
 class LazyAttnError(RuntimeError):
@@ -277,6 +283,95 @@ def lazyattn_decode_noalloc(q, q_pos, k_pool, v_pool, block_table, seq_lens, *, 
         _ptr(out), _ptr(q), _ptr(q_pos), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), block_table.shape[1], fill,
         _ptr(seq_lens), b, hq, hkv, d, nb, _dtype_code(q), scale, float(rope_theta), int(split_blocks),
         _stream_ptr(stream, dev)), "lazyattn_decode_noalloc")
+    return out
+
+
+class DecodePlan:
+    """A work plan for lazyattn_decode_planned: ``ints`` (int32, host) as the
+    library's planner wrote it, ``device`` its copy on the GPU, and the item
+    count and largest per-sequence slot count the call needs."""
+
+    def __init__(self, ints, device, num_items, max_items_per_seq, batch, num_kv_heads):
+        self.ints, self.device = ints, device
+        self.num_items, self.max_items_per_seq = num_items, max_items_per_seq
+        self.batch, self.num_kv_heads = batch, num_kv_heads
+
+
+def decode_plan(block_table, seq_lens, num_kv_heads, *, max_item_blocks=0, device=None):
+    """Build a plan for lazyattn_decode_planned with the library's host-side
+    planner (lazyattn_decode_plan) from copies of block_table [B, max_blocks]
+    and seq_lens [B] in host memory; the plan goes to ``device`` (default: the
+    table's device, if a GPU).  Rebuild it when the table, the lengths or the
+    KV head count change."""
+    _int32(block_table, "block_table")
+    _int32(seq_lens, "seq_lens")
+    if block_table.dim() != 2 or seq_lens.numel() != block_table.shape[0]:
+        raise LazyAttnError("block_table [B, max_blocks], seq_lens [B]")
+    b, max_blocks = block_table.shape
+    table = block_table.detach().to("cpu").view(torch.int32).contiguous()
+    lens = seq_lens.detach().to("cpu").view(torch.int32).contiguous()
+    lib = load_library()
+    cap = int(lib.lazyattn_decode_plan_ints(b, max_blocks, num_kv_heads))
+    if cap == 0:
+        raise LazyAttnError("decode_plan: empty batch or bad sizes")
+    buf = torch.empty(cap, dtype=torch.int32)
+    n, m = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib.lazyattn_decode_plan(_ptr(table), _ptr(lens), b, max_blocks, num_kv_heads, int(max_item_blocks),
+                                    _ptr(buf), cap, ctypes.byref(n), ctypes.byref(m)), "lazyattn_decode_plan")
+    ints = buf[:(b + 3) // 4 * 4 + 4 * n.value].clone()
+    if device is None:
+        device = block_table.device if block_table.device.type == "cuda" else None
+    dev_ints = ints.to(device) if device is not None else None
+    return DecodePlan(ints, dev_ints, n.value, m.value, b, num_kv_heads)
+
+
+def decode_planned_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_items_per_seq):
+    return int(load_library().lazyattn_decode_planned_workspace_size(
+        batch, num_q_heads, num_kv_heads, head_dim, max_items_per_seq))
+
+
+def lazyattn_decode_planned(q, q_pos, k_pool, v_pool, block_table, seq_lens, plan, *, scale=None,
+                            rope_theta=10000.0, out=None, workspace=None, stream=None, block_fill=None):
+    """lazyattn_decode with the work of ``plan`` (decode_plan of the same
+    table, lengths and KV head count): sequences that share a cached document
+    read it together.  bf16, head_dim 128, group sizes up to 16."""
+    dev = _dev(q, q_pos, k_pool, v_pool, block_table, seq_lens)
+    for t, nm in ((q_pos, "q_pos"), (block_table, "block_table"), (seq_lens, "seq_lens")):
+        _int32(t, nm)
+    b, hq, d = q.shape
+    nb, hkv, bt, dk = k_pool.shape
+    if bt != BLOCK_TOKENS or dk != d or v_pool.shape != k_pool.shape:
+        raise LazyAttnError("pools must be [num_blocks, num_kv_heads, 16, head_dim]")
+    if q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
+        raise LazyAttnError("q and pools must share a dtype")
+    if block_table.dim() != 2 or block_table.shape[0] != b or q_pos.numel() != b or seq_lens.numel() != b:
+        raise LazyAttnError("block_table [B, max_blocks], q_pos [B], seq_lens [B]")
+    if not isinstance(plan, DecodePlan) or plan.device is None or plan.batch != b or plan.num_kv_heads != hkv:
+        raise LazyAttnError("plan must be decode_plan() of this batch's table and KV heads, on the GPU")
+    _dev(plan.device, q)
+    if out is None:
+        out = torch.empty_like(q)
+        new_out = True
+    else:
+        new_out = False
+        _dev(out, q)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise LazyAttnError("out must match q")
+    need = decode_planned_workspace_size(b, hq, hkv, d, plan.max_items_per_seq) if b else 0
+    new_ws = workspace is None
+    if new_ws:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _dev(workspace, q)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    fill_keep, fill = _fill_arg(block_fill, nb, dev)
+    _hold_temporaries(stream, dev, out if new_out else None, workspace if new_ws else None,
+                      fill_keep if fill_keep is not block_fill else None)
+    _check(load_library().lazyattn_decode_planned(
+        _ptr(out), _ptr(q), _ptr(q_pos), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), block_table.shape[1], fill,
+        _ptr(seq_lens), b, hq, hkv, d, nb, _dtype_code(q), scale, float(rope_theta), _ptr(plan.device),
+        plan.num_items, plan.max_items_per_seq, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_ptr(stream, dev)), "lazyattn_decode_planned")
     return out
 
 

@@ -110,7 +110,8 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
                          int head_dim, int num_blocks, int dtype, float scale, float rope_theta,
                          int split_blocks, void *workspace, size_t workspace_bytes, void *stream,
                          int mode, const float *slopes, bool pool8 = false, float k_scale = 1.f,
-                         float v_scale = 1.f) {
+                         float v_scale = 1.f, const int32_t *plan = nullptr, int plan_items = 0,
+                         int plan_max_items = 0) {
   if (!valid_dtype(dtype)) return LAZYATTN_ERR_DTYPE;
   if (batch < 0 || batch > 65535 || num_kv_heads < 1 || num_kv_heads > 65535 || num_q_heads < 1 ||
       num_q_heads % num_kv_heads || !pow2_group(num_q_heads / num_kv_heads))
@@ -130,8 +131,9 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
   if (!out || !q || !q_pos || !k_pool || !v_pool || !block_table || !seq_lens)
     return LAZYATTN_ERR_NULL;
   if (mode == kAlibi && !slopes) return LAZYATTN_ERR_NULL;
-  const size_t need = decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
-                                            max_blocks_per_seq, split_blocks);
+  const size_t need = plan ? decode_planned_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, plan_max_items)
+                           : decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
+                                                   max_blocks_per_seq, split_blocks);
   if (need && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u)))
     return LAZYATTN_ERR_WORKSPACE;
 
@@ -159,6 +161,9 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
   a.block_fill = block_fill;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.plan = plan;
+  a.plan_items = plan_items;
+  a.plan_max_items = plan_max_items;
   if (pool8) return from_hip(launch_decode_fp8(a, (hipStream_t)stream));
   return from_hip(launch_decode(a, bf16, (hipStream_t)stream));
 }
@@ -205,6 +210,33 @@ int lazyattn_decode(void *out, const void *q, const int32_t *q_pos, const void *
   return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, block_fill, seq_lens,
                        batch, num_q_heads, num_kv_heads, head_dim, num_blocks, dtype, scale,
                        rope_theta, split_blocks, workspace, workspace_bytes, stream, kRopeLazy, nullptr);
+}
+
+size_t lazyattn_decode_planned_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                              int max_items_per_seq) {
+  if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_q_heads % num_kv_heads ||
+      max_items_per_seq <= 0)
+    return 0;
+  return decode_planned_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_items_per_seq);
+}
+
+int lazyattn_decode_planned(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                            const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                            const uint8_t *block_fill, const int32_t *seq_lens, int batch, int num_q_heads,
+                            int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
+                            float rope_theta, const int32_t *plan, int num_items, int max_items_per_seq,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  if (!valid_dtype(dtype)) return LAZYATTN_ERR_DTYPE;
+  if (dtype != LAZYATTN_BF16) return LAZYATTN_ERR_DTYPE;
+  if (head_dim != 128 || num_kv_heads < 1 || num_q_heads < 1 || num_q_heads % num_kv_heads ||
+      num_q_heads / num_kv_heads > 16 || num_items < 1 || max_items_per_seq < 1 || max_items_per_seq > 65535)
+    return LAZYATTN_ERR_SHAPE;
+  if (batch > 0 && !plan) return LAZYATTN_ERR_NULL;
+  if ((uintptr_t)plan & 15u) return LAZYATTN_ERR_SHAPE;
+  return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, block_fill, seq_lens,
+                       batch, num_q_heads, num_kv_heads, head_dim, num_blocks, dtype, scale, rope_theta, 0,
+                       workspace, workspace_bytes, stream, kRopeLazy, nullptr, false, 1.f, 1.f, plan, num_items,
+                       max_items_per_seq);
 }
 
 int lazyattn_decode_eager(void *out, const void *q, const int32_t *q_pos, const void *k_pool,

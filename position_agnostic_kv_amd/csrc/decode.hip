@@ -88,11 +88,67 @@ struct DecodeKernelArgs {
   int max_blocks;
   int num_kv_heads;  // work heads: KV heads x head split (each takes G query heads)
   int kv_shift;      // log2 of the head split
-  int num_units;     // splits x KV heads x batch
+  int num_units;     // splits x KV heads x batch, or the plan's item count
   int num_blocks, split_blocks, max_splits;
   float scale_log2, rope_theta;
   float out_scale;   // V scale of an 8-bit pool (1 otherwise)
+  // A work plan (nullptr: uniform splits of split_blocks blocks).  Item i,
+  // taken by workgroup i: (sequence, work head, slot | first block << 16,
+  // end block); plan_counts[b] = the slots (partials) of sequence b.
+  const int4 *plan_items;
+  const int32_t *plan_counts;
+  int batch;
 };
+
+// The share of the decode a workgroup takes: sequence b, work head g, split
+// `split` of `nsplit`, blocks [blk0, blk1) of the sequence's table (nblk of
+// them in all).  Returns false for a workgroup with nothing to do: past the
+// last unit, or a plan item outside the batch, the heads or the sequence's
+// slot count (a malformed plan is never read past).
+struct DecodeShare {
+  int b, g, split, nsplit, blk0, blk1, nblk, seq_len;
+  bool bad_len;
+};
+__device__ __forceinline__ bool decode_share(const DecodeKernelArgs &a, DecodeShare &w) {
+  const int hkv = a.num_kv_heads;
+  if (a.plan_items) {
+    if ((int)blockIdx.x >= a.num_units) return false;
+    const int4 it = a.plan_items[blockIdx.x];
+    if ((unsigned)it.x >= (unsigned)a.batch || (unsigned)it.y >= (unsigned)hkv) return false;
+    w.b = it.x;
+    w.g = it.y;
+    w.split = it.z & 0xffff;
+    w.nsplit = a.plan_counts[w.b];
+    if (w.nsplit < 1 || w.nsplit > a.max_splits || w.split >= w.nsplit) return false;
+    w.blk0 = (int)((unsigned)it.z >> 16);
+    w.blk1 = it.w;
+  } else {
+    // Work item -> (split, KV head, sequence).  A KV head whose query heads
+    // are split over 2^kv_shift workgroups gives them consecutive slots on
+    // one XCD (workgroups go round-robin over the XCDs), so they run side by
+    // side and the twin reads of each K/V block are served by that XCD's L2.
+    const int slot = blockIdx.x / kXcds;
+    const int hsub = slot & ((1 << a.kv_shift) - 1);
+    const int unit = (slot >> a.kv_shift) * kXcds + (int)(blockIdx.x % kXcds);
+    if (unit >= a.num_units) return false;
+    const int hkv_pool = hkv >> a.kv_shift;
+    w.split = unit % a.max_splits;
+    const int gp = (unit / a.max_splits) % hkv_pool;  // KV head in the pool
+    w.b = unit / a.max_splits / hkv_pool;
+    w.g = (gp << a.kv_shift) | hsub;                  // work head: query heads g*G .. g*G+G-1
+  }
+  w.seq_len = a.seq_lens[w.b];
+  w.bad_len = w.seq_len < 0 || w.seq_len > a.max_blocks * kBlockTokens;
+  w.nblk = w.bad_len ? 0 : (w.seq_len + kBlockTokens - 1) / kBlockTokens;
+  if (!a.plan_items) {
+    w.nsplit = (w.nblk + a.split_blocks - 1) / a.split_blocks;
+    w.blk0 = w.split * a.split_blocks;
+    w.blk1 = w.blk0 + a.split_blocks;
+  }
+  w.blk1 = min(w.blk1, w.nblk);
+  w.blk0 = min(w.blk0, w.blk1);
+  return true;
+}
 
 // MODE kRopeEager: the non-lazy baseline the method is measured against.  The
 // pool then holds keys already rotated to their absolute positions (the eager,
@@ -805,29 +861,21 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
   __shared__ float s_l[kDecodeWaves][G];
   __shared__ int s_bad[kDecodeWaves];  // per wave: a table word pointed outside the pool
 
+  DecodeShare sh;
+  if (!decode_share(a, sh)) return;
   const int hkv = a.num_kv_heads;
-  const int slot = blockIdx.x / kXcds;
-  const int hsub = slot & ((1 << a.kv_shift) - 1);
-  const int unit = (slot >> a.kv_shift) * kXcds + (int)(blockIdx.x % kXcds);
-  if (unit >= a.num_units) return;
   const int hkv_pool = hkv >> a.kv_shift;
-  const int split = unit % a.max_splits;
-  const int gp = (unit / a.max_splits) % hkv_pool;
-  const int b = unit / a.max_splits / hkv_pool;
-  const int g = (gp << a.kv_shift) | hsub;
+  const int b = sh.b, g = sh.g, gp = g >> a.kv_shift, split = sh.split, nsplit = sh.nsplit;
+  const int seq_len = sh.seq_len;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int hq = hkv * G;
 
-  const int seq_len = a.seq_lens[b];
-  const bool bad_len = seq_len < 0 || seq_len > a.max_blocks * kBlockTokens;
-  const int nblk = bad_len ? 0 : (seq_len + kBlockTokens - 1) / kBlockTokens;
-  const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
   bf16 *out = (bf16 *)a.out + ((size_t)b * hq + (size_t)g * G) * D;
-  if (nsplit == 0) {
+  if (sh.nblk == 0) {  // empty sequence -> zeros; invalid length -> NaN
     if (split == 0)
-      for (int i = tid; i < G * D; i += NT) E::store(out, i, bad_len ? __builtin_nanf("") : 0.f);
+      for (int i = tid; i < G * D; i += NT) E::store(out, i, sh.bad_len ? __builtin_nanf("") : 0.f);
     return;
   }
   if (split >= nsplit) return;
@@ -911,8 +959,7 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
   char *ring = &s_ring[wave][0][0][0];
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr_t)ring;
 
-  const int blk0 = split * a.split_blocks;
-  const int blk1 = min(nblk, blk0 + a.split_blocks);
+  const int blk0 = sh.blk0, blk1 = sh.blk1;
   // table words and fill counts as scalar loads (see as_const_as)
   const auto trow = as_const_as(a.table + (size_t)b * a.max_blocks);
   const auto fill4 = a.fill4 ? as_const_as(a.fill4) : nullptr;
@@ -1433,8 +1480,8 @@ decode_combine_kernel(const DecodeKernelArgs a) {
   const int seq_len = a.seq_lens[b];
   if (seq_len < 0 || seq_len > a.max_blocks * kBlockTokens) return;  // written by the split kernel
   const int nblk = (seq_len + kBlockTokens - 1) / kBlockTokens;
-  const int nsplit = (nblk + a.split_blocks - 1) / a.split_blocks;
-  if (nsplit <= 1) return;
+  const int nsplit = a.plan_counts ? a.plan_counts[b] : (nblk + a.split_blocks - 1) / a.split_blocks;
+  if (nblk == 0 || nsplit <= 1 || nsplit > a.max_splits) return;
   const size_t part = ((size_t)b * hkv + g) * a.max_splits;
   const float4 *po = (const float4 *)(a.ws_o + (part * G + h) * D + d);
   const float2 *pml = a.ws_ml + part * G + h;
@@ -1513,10 +1560,11 @@ int decode_split_blocks(int batch, int num_q_heads, int num_kv_heads, int max_bl
   return (int)sb;
 }
 
-static void workspace_layout(int batch, int num_q_heads, int num_kv_heads, int head_dim,
-                             int max_blocks, int split_blocks, size_t *off_o, size_t *total) {
+// Partials of `splits` slots per (sequence, work head): (max, sum) pairs, then
+// the outputs at off_o (256-byte aligned).
+static void workspace_layout(int batch, int num_q_heads, int num_kv_heads, int head_dim, size_t splits,
+                             size_t *off_o, size_t *total) {
   const size_t units = (size_t)batch * num_kv_heads;
-  const size_t splits = (size_t)((max_blocks + split_blocks - 1) / split_blocks);
   const size_t group = (size_t)(num_q_heads / num_kv_heads);
   *off_o = align_up(units * splits * group * sizeof(float2), 256);
   *total = *off_o + units * splits * group * head_dim * sizeof(float);
@@ -1531,11 +1579,22 @@ size_t decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int h
     const int sb = decode_split_blocks(batch, num_q_heads, num_kv_heads, max_blocks_per_seq, split_blocks, impl);
     if ((max_blocks_per_seq + sb - 1) / sb <= 1) continue;  // one split: no partials
     size_t off_o, t;
-    workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, sb, &off_o, &t);
+    workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, (size_t)((max_blocks_per_seq + sb - 1) / sb),
+                     &off_o, &t);
     need = t > need ? t : need;
   }
   return need;
 }
+
+size_t decode_planned_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                     int max_items_per_seq) {
+  if (max_items_per_seq <= 1) return 0;
+  size_t off_o, t;
+  workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, (size_t)max_items_per_seq, &off_o, &t);
+  return t;
+}
+
+size_t decode_plan_items_offset(int batch) { return ((size_t)batch + 3) / 4 * 4; }
 
 // IMPL: kValu (decode_split_kernel), kMma8 (8-bit pools), kMma16 (bf16 pools,
 // matrix cores, up to 16 heads), kMma16Wide (bf16 pools, 32 or 64 heads)
@@ -1543,6 +1602,8 @@ enum DecodeImplKernel { kValu = 0, kMma8 = 1, kMma16 = 2, kMma16Wide = 3 };
 
 template <typename T, int D, int G, int MODE, bool F8 = false, int IMPL = kValu>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
+  // a work plan is read by the bf16 matrix-core kernel for up to 16 heads only
+  if (a.plan && (IMPL != kMma16 || a.plan_items < 1 || a.plan_max_items < 1)) return hipErrorInvalidValue;
   DecodeKernelArgs k;
   k.out = a.out;
   k.q = a.q;
@@ -1560,17 +1621,19 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   k.kv_shift = __builtin_ctz((unsigned)hsplit);  // hsplit is a power of two
   k.num_blocks = a.num_blocks;
   k.split_blocks = a.split_blocks;
-  k.max_splits = (a.max_blocks + a.split_blocks - 1) / a.split_blocks;
+  k.max_splits = a.plan ? a.plan_max_items : (a.max_blocks + a.split_blocks - 1) / a.split_blocks;
+  k.batch = a.batch;
+  k.plan_counts = a.plan;
+  k.plan_items = a.plan ? (const int4 *)(a.plan + decode_plan_items_offset(a.batch)) : nullptr;
   k.scale_log2 = a.scale * kLog2e * (F8 ? a.k_scale : 1.f);
   k.out_scale = F8 ? a.v_scale : 1.f;
   k.rope_theta = a.rope_theta;
-  const long long units = (long long)k.max_splits * a.num_kv_heads * a.batch;
-  const long long grid = (units + kXcds - 1) / kXcds * kXcds * hsplit;
+  const long long units = a.plan ? (long long)a.plan_items : (long long)k.max_splits * a.num_kv_heads * a.batch;
+  const long long grid = a.plan ? units : (units + kXcds - 1) / kXcds * kXcds * hsplit;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   k.num_units = (int)units;
   size_t off_o, total;
-  workspace_layout(a.batch, a.num_q_heads, work_heads, a.head_dim, a.max_blocks, a.split_blocks,
-                   &off_o, &total);
+  workspace_layout(a.batch, a.num_q_heads, work_heads, a.head_dim, (size_t)k.max_splits, &off_o, &total);
   char *ws = (char *)a.workspace;
   k.ws_ml = ws ? (float2 *)ws : nullptr;
   k.ws_o = ws ? (float *)(ws + off_o) : nullptr;

@@ -91,6 +91,38 @@ def test_decode_argument_errors(lib):
     assert decode(lib, ws=ctypes.c_void_p(0x1008), max_blocks=4000) == -4   # partials are read 16 bytes at a time
 
 
+def planned(lib, **kw):
+    a = dict(out=P, q=P, q_pos=P, k=P, v=P, table=P, max_blocks=4, fill=NULL, seq_lens=P, batch=2, hq=8, hkv=2,
+             d=128, nb=16, dtype=1, scale=0.088, theta=1e4, plan=P, items=4, max_items=2, ws=P, ws_bytes=1 << 30,
+             stream=NULL)
+    a.update(kw)
+    return lib.lazyattn_decode_planned(*a.values())
+
+
+def test_planned_decode_argument_errors(lib):
+    """Every argument error returns before any launch (the pointers are never
+    dereferenced)."""
+    assert planned(lib, dtype=0) == -2             # bf16 pools only
+    assert planned(lib, dtype=7) == -2
+    assert planned(lib, d=64) == -3                # head_dim 128 only
+    assert planned(lib, hq=64, hkv=2) == -3        # groups up to 16
+    assert planned(lib, hq=6, hkv=4) == -3
+    assert planned(lib, items=0) == -3
+    assert planned(lib, max_items=0) == -3
+    assert planned(lib, plan=NULL) == -1
+    assert planned(lib, plan=ctypes.c_void_p(0x1008)) == -3   # items are read 16 bytes at a time
+    assert planned(lib, q=NULL) == -1
+    assert planned(lib, nb=65537) == -3
+    assert planned(lib, ws=NULL) == -4
+    assert planned(lib, ws_bytes=16) == -4
+    assert planned(lib, ws=ctypes.c_void_p(0x1008)) == -4
+    assert planned(lib, batch=0, q=NULL) == 0      # empty batch: no-op
+    assert lib.lazyattn_decode_planned_workspace_size(2, 8, 2, 128, 1) == 0
+    # 2 x 2 (sequence, KV head) units, 3 slots, 4 heads: (max, sum) pairs padded to 256 B, then outputs
+    assert lib.lazyattn_decode_planned_workspace_size(2, 8, 2, 128, 3) == 512 + 4 * 3 * 4 * 128 * 4
+    assert lib.lazyattn_decode_planned_workspace_size(2, 8, 2, 128, 0) == 0
+
+
 def test_alibi_entry_points_check_arguments(lib):
     fd, fp = lib.lazyattn_decode_alibi, lib.lazyattn_prefill_alibi
     ok_d = [P, P, P, P, P, P, 4, NULL, P, P, 2, 8, 2, 128, 16, 1, 0.088, 0, P, 1 << 30, NULL]

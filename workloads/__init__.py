@@ -542,7 +542,7 @@ def llama70b_decode(seed=4, batch=16, ctx=32768, docs=(16, 64)):
 
 
 def zipf_decode(seed=5, batch=128, catalogue=1000, zipf_s=1.2, docs_per_seq=(4, 8),
-                doc_blocks=(16, 128)):
+                doc_blocks=(16, 128), num_q_heads=32, num_kv_heads=8):
     """Zipf document-reuse decode mix, bf16, 8B shape.
 
     A catalogue of 1000 documents (16 * U{16..128} tokens); each of the 128
@@ -559,7 +559,7 @@ def zipf_decode(seed=5, batch=128, catalogue=1000, zipf_s=1.2, docs_per_seq=(4, 
         k = int(rng.integers(docs_per_seq[0], docs_per_seq[1] + 1))
         seq_docs.append([int(d) for d in rng.choice(catalogue, size=k, replace=False, p=p)])
     lay = build_layout(rng, seq_docs, doc_lens, [1] * batch)
-    return Case("zipf_reuse_decode", "decode", BF16, 32, 8, 128, 5.0e5, lay, seed=seed)
+    return Case("zipf_reuse_decode", "decode", BF16, num_q_heads, num_kv_heads, 128, 5.0e5, lay, seed=seed)
 
 
 def prefill_case(seed, batch, num_q_heads, num_kv_heads, head_dim, cached, prompt,
