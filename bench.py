@@ -11,7 +11,9 @@ bytes of the attended tokens / decode-pass time); the prefill attention
 TFLOP/s rides along.  After the timed steps, the metric's other two decode
 workloads (Llama-3.1-70B-shaped decode, and the Zipf-skewed document-reuse
 mix) are each timed the same way as a decode pass of their own, with their
-own roofline and oracle baseline (keys "llama70b_decode", "zipf_reuse_decode").
+own roofline and oracle baseline (keys "llama70b_decode", "zipf_reuse_decode";
+the Zipf mix through the planned decode, which runs the readers of each
+shared document together).
 Kernel durations come from HIP events recorded on the stream the library
 launches on (torch's current stream).  Before the W counted warm-up steps,
 untimed steps run until the clock has settled (the prefill kernel's time
@@ -351,6 +353,8 @@ def shapes_main(args):
         if d.fill is not None:
             r["table_slots_per_token"] = round(float(case.seq_lens.sum() / case.layout.total_lens.sum()), 4)
         res[name] = r
+        if name == "zipf_reuse_decode":  # the planned decode: shared documents read together
+            res[name + "_planned"] = planned_decode_shape(case, d, out, timed)
         if name in ("llama8b_decode", "llama70b_decode"):  # the same geometry over an 8-bit (E4M3) pool
             res[name + "_fp8"] = fp8_decode_shape(case, d, out, ws, timed)
         if name == "llama8b_decode":  # the same inputs read with ALiBi biases instead of RoPE
@@ -416,6 +420,8 @@ def shapes_main(args):
 SHAPES_DISPATCH_ORDER = {
     "lazyattn::decode_mma16_kernel<4, 0>": ["llama8b_decode", "zipf_reuse_decode", "llama8b_decode_ragged",
                                             "decode_g4_equal_bytes"],
+    # the planned decode (shared documents read together), on the Zipf mix
+    "lazyattn::decode_planned_kernel<4>": ["zipf_reuse_decode_planned"],
     "lazyattn::decode_mma16_wide_kernel<2, 0>": ["decode_g32_equal_bytes"],
     "lazyattn::decode_mma16_wide_kernel<4, 0>": ["decode_g64_equal_bytes"],
     "lazyattn::decode_mma16_kernel<4, 2>": ["llama8b_decode_alibi"],
@@ -429,6 +435,7 @@ SHAPES_DISPATCH_ORDER = {
 }
 PROFILE_STEMS = {
     "llama8b_decode": "decode_llama8b", "zipf_reuse_decode": "decode_zipf",
+    "zipf_reuse_decode_planned": "decode_zipf_planned",
     "llama8b_decode_ragged": "decode_llama8b_ragged", "llama8b_decode_alibi": "decode_llama8b_alibi",
     "llama70b_decode": "decode_llama70b", "llama8b_decode_fp8": "decode_llama8b_fp8",
     "llama70b_decode_fp8": "decode_llama70b_fp8", "llama8b_prefill": "prefill_llama8b",
@@ -437,6 +444,30 @@ PROFILE_STEMS = {
     "decode_g4_equal_bytes": "decode_g4_equal_bytes",
     "decode_g32_equal_bytes": "decode_g32_equal_bytes", "decode_g64_equal_bytes": "decode_g64_equal_bytes",
 }
+
+
+def planned_decode_shape(case, d, out, timed):
+    """--shapes: the planned decode (lazyattn_decode_planned) on a decode
+    workload's inputs; the plan is built once on the host, outside the
+    timing."""
+    import position_agnostic_kv_amd as pak
+    import torch
+
+    t0 = time.perf_counter()
+    plan = pak.decode_plan(d.table, d.seq_lens, case.num_q_heads, case.num_kv_heads)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    wsb = pak.decode_planned_workspace_size(case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                                            plan.max_items_per_seq)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=d.q.device)
+    med, p10, p90 = timed(lambda: pak.lazyattn_decode_planned(d.q, d.q_pos, d.k_pool, d.v_pool, d.table,
+                                                              d.seq_lens, plan, scale=case.scale,
+                                                              rope_theta=case.rope_theta, out=out, workspace=ws))
+    kv, alg = decode_algorithmic_bytes(case)
+    return {"ms_p50": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
+            "gbps_logical": round(kv / (med * 1e-3) / 1e9, 1),
+            "pool_bytes_physical": int(d.k_pool.numel()) * 2 * 2,
+            "plan": {"items": plan.num_items, "max_items_per_seq": plan.max_items_per_seq,
+                     "host_build_ms": round(plan_ms, 2)}}
 
 
 def _profile_workload_bytes(name):
@@ -449,7 +480,7 @@ def _profile_workload_bytes(name):
         return (f"{name}: the {slots} visible (block, KV head) slots of llama8b_prefill over an E4M3 pool, "
                 f"widened once to bf16; algorithmic = 2 x 2 KiB of codes read + 2 x 4 KiB bf16 written per "
                 f"slot"), total
-    base = name.replace("_fp8", "").replace("_alibi", "")
+    base = name.replace("_fp8", "").replace("_alibi", "").replace("_planned", "")
     case = W.make(base)
     if case.kind == "decode":
         kv, total = decode_algorithmic_bytes(case)
@@ -759,7 +790,10 @@ def decode_workload_line(name, args, dev):
     lazyattn_decode) on another decode workload of the same metric, timed the
     same way (W warm-up passes, then K timed ones, HIP events on the launch
     stream): its own K+V rate, kernel-time percentiles, roofline and oracle
-    baseline.  Inputs are dropped afterwards."""
+    baseline.  On the Zipf mix the record is the planned decode's
+    (lazyattn_decode_planned: the readers of each shared document run
+    together), with the per-sequence decode's figures beside it.  Inputs are
+    dropped afterwards."""
     import torch
     import position_agnostic_kv_amd as pak
     import workloads as W
@@ -784,20 +818,53 @@ def decode_workload_line(name, args, dev):
         if ev is not None:
             ev[2].record()
 
-    for _ in range(args.warmup):
-        one()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        one(events[k])
-    torch.cuda.synchronize()
-    pass_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in events]))
-    kx = np.array([e[1].elapsed_time(e[2]) for e in events])
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            fn(events[k])
+        torch.cuda.synchronize()
+        return (float(np.mean([e[0].elapsed_time(e[2]) for e in events])),
+                np.array([e[1].elapsed_time(e[2]) for e in events]))
+
+    pass_ms, kx = timed(one)
     kernel_ms = float(np.mean(kx))
     kv, alg = decode_algorithmic_bytes(case)
     g = case.num_q_heads // case.num_kv_heads
     kname = f"lazyattn::decode_mma16_kernel<{min(g, 16)}, 0>"
     stem = {"llama70b_decode": "decode_llama70b", "zipf_reuse_decode": "decode_zipf"}[name]
+    per_seq = None
+    if name == "zipf_reuse_decode":
+        # shared documents: the planned decode (the host plan is built once,
+        # outside the timing, as a scheduler builds the block table)
+        per_seq = {"path": "lazyattn_decode", "decode_pass_ms": round(pass_ms, 4),
+                   "decode_kernel_ms": round(kernel_ms, 4),
+                   "value": round(kv / (pass_ms * 1e-3) / 1e9, 2),
+                   "traffic": measured_traffic(stem, DECODE_SOURCES)}
+        t0 = time.perf_counter()
+        plan = pak.decode_plan(d.table, d.seq_lens, case.num_q_heads, case.num_kv_heads)
+        plan_ms = (time.perf_counter() - t0) * 1e3
+        pws = torch.empty(max(pak.decode_planned_workspace_size(case.batch, case.num_q_heads, case.num_kv_heads,
+                                                                case.head_dim, plan.max_items_per_seq), 1),
+                          dtype=torch.uint8, device=dev)
+
+        def planned(ev=None):
+            if ev is not None:
+                ev[0].record()
+            pak.kvcache_append(d.k_pool, d.v_pool, d.k_new, d.v_new, d.slots)
+            if ev is not None:
+                ev[1].record()
+            pak.lazyattn_decode_planned(d.q, d.q_pos, d.k_pool, d.v_pool, d.table, d.seq_lens, plan,
+                                        scale=case.scale, rope_theta=case.rope_theta, out=out, workspace=pws)
+            if ev is not None:
+                ev[2].record()
+
+        pass_ms, kx = timed(planned)
+        kernel_ms = float(np.mean(kx))
+        stem = "decode_zipf_planned"
+        kname = f"lazyattn::decode_planned_kernel<{g}>"
     rec = {
         "value": round(kv / (pass_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
         "config": {"batch": case.batch, "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
@@ -814,11 +881,17 @@ def decode_workload_line(name, args, dev):
     }
     if name == "zipf_reuse_decode":
         phys = int(d.k_pool.numel()) * 2 * 2
-        rec["roofline"]["note"] = ("algorithmic bytes count every attended token once per sequence; documents "
-                                   "shared between sequences are read again and served by L2/MALL, so the "
-                                   "logical rate may exceed the HBM peak")
+        rec["path"] = "lazyattn_decode_planned"
+        rec["plan"] = {"items": plan.num_items, "max_items_per_seq": plan.max_items_per_seq,
+                       "host_build_ms": round(plan_ms, 2),
+                       "note": "built on the host from the block table and lengths, outside the timing; valid "
+                               "while sequences grow into blocks appended to their rows"}
+        rec["roofline"]["note"] = ("algorithmic bytes count every attended token once per sequence; the plan "
+                                   "runs the readers of each shared document together so the L2 serves the "
+                                   "repeats, so the logical rate exceeds the HBM peak")
         rec["pool_bytes_physical"] = phys
         rec["physical_pool_gbps"] = round(phys / (kernel_ms * 1e-3) / 1e9, 1)
+        rec["per_sequence_decode"] = per_seq
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_decode(case, d, args.cpu_seconds)
     del d, out, ws

@@ -141,45 +141,53 @@ int lazyattn_decode(void *out, const void *q, const int32_t *q_pos, const void *
                     int split_blocks, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Planned decode: lazyattn_decode with its work cut at document boundaries
- * and ordered so that sequences sharing a cached document read it together.
- * One physical copy of a document serves every request that places it, at
- * any position (LazyAttention summary, "Metodologia"; the Zipf-skewed reuse
- * of "Resultados Experimentais"); per-sequence decode reads that copy once
- * per sequence.  A plan makes each (sequence, document run, KV head) one
- * workgroup and puts the workgroups of one (document, KV head) on one XCD in
- * consecutive places, so that XCD's L2 serves all but the first reader.
+ * Planned decode: lazyattn_decode with its work cut at document boundaries,
+ * and the sequences that share a cached document reading it together.  One
+ * physical copy of a document serves every request that places it, at any
+ * position (LazyAttention summary, "Metodologia"; the Zipf-skewed reuse of
+ * "Resultados Experimentais"); per-sequence decode reads that copy once per
+ * sequence.  A plan cuts each sequence's table into runs; the runs of up to
+ * four sequences that hold the same blocks (and for 16 / G >= 2) become one
+ * work item, whose workgroup reads the blocks once for all of them (its 16
+ * matrix-core columns are (sequence, query head) pairs).  The items of one
+ * (document, KV head) go to one XCD in consecutive places, so that XCD's L2
+ * serves the document's further readers.
  *
  * lazyattn_decode_plan (host code, host memory, no GPU): builds the plan
  * from a host copy of block_table and seq_lens.  A run ends where the table
- * offset changes once it holds 4 blocks, or at max_item_blocks blocks
- * (0 = 128); a last run shorter than 4 blocks joins the one before.  Runs
- * are keyed by their first block id.  plan receives lazyattn_decode_plan_ints
- * ints at most: int32 [batch] slot counts, padded to a multiple of 4, then
- * *num_items items of 4 ints (sequence, KV head, slot | first block << 16,
- * end block).  *max_items_per_seq sizes the workspace.  Returns
- * LAZYATTN_ERR_WORKSPACE if plan_ints is too small.  The plan depends only on
- * the table, the lengths and the KV head count.  A sequence's last run ends
- * at max_blocks_per_seq and the kernel clips it to the sequence's length, so
- * the plan stays valid while sequences grow into blocks appended to their
- * rows; rebuild it when words already in a row change.
+ * offset changes once it holds 4 blocks, at max_item_blocks blocks (0 = 128),
+ * and at the sequence's end; runs are shared only if they are not their
+ * sequence's last and keep one offset throughout.  plan receives
+ * lazyattn_decode_plan_ints ints at most: int32 [batch] run counts (the
+ * partial slots per sequence), padded to a multiple of 4, then *num_items
+ * items of 12 ints: KV head | members << 16, first and end block (in the
+ * first member's row), 0, up to 4 members as sequence | slot << 16, and the
+ * run's first block in each member's row (a shared document may sit at a
+ * different place in each).  *max_items_per_seq sizes
+ * the workspace.  Returns LAZYATTN_ERR_WORKSPACE if plan_ints is too small.
+ * The plan depends only on the table, the lengths and the head counts.  A
+ * sequence's last run ends at max_blocks_per_seq and the kernel clips it to
+ * the sequence's length, so the plan stays valid while sequences grow into
+ * blocks appended to their rows; rebuild it when words already in a row
+ * change.
  *
  * lazyattn_decode_planned: as lazyattn_decode, with plan a device copy of
- * the plan's first (padded batch + 4 * num_items) ints, 16-byte aligned,
+ * the plan's first (padded batch + 12 * num_items) ints, 16-byte aligned,
  * read only.  bf16 pools, head_dim 128, group sizes 1..16 (LAZYATTN_ERR_SHAPE
  * otherwise); lazy RoPE only.  The workspace (16-byte aligned, no
  * initialisation) holds max_items_per_seq partials per (sequence, KV head);
  * lazyattn_decode_planned_workspace_size gives its size (0: none needed).
  * Results match lazyattn_decode up to the order in which partials are
  * summed.  A plan for other sizes never makes the kernels read outside the
- * table, pool or workspace (items outside the batch, heads or a sequence's
- * slot count are skipped, block ranges are clipped to the sequence), but its
- * output is then undefined.
+ * table, pool or workspace (items naming sequences, heads or slots outside
+ * the batch, the heads or a sequence's run count are skipped, block ranges
+ * are clipped to the first member's sequence), but its output is then
+ * undefined.
  */
 size_t lazyattn_decode_plan_ints(int batch, int max_blocks_per_seq, int num_kv_heads);
 int lazyattn_decode_plan(const uint32_t *block_table, const int32_t *seq_lens, int batch,
-                         int max_blocks_per_seq, int num_kv_heads, int max_item_blocks, int32_t *plan,
-                         size_t plan_ints, int *num_items, int *max_items_per_seq);
+                         int max_blocks_per_seq, int num_q_heads, int num_kv_heads, int max_item_blocks,
+                         int32_t *plan, size_t plan_ints, int *num_items, int *max_items_per_seq);
 size_t lazyattn_decode_planned_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                               int max_items_per_seq);
 int lazyattn_decode_planned(void *out, const void *q, const int32_t *q_pos, const void *k_pool,

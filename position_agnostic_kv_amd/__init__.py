@@ -65,7 +65,7 @@ _SIGNATURES["lazyattn_prefill_fp8"] = (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp
                                               _i32, _i32, _i32, _i32, _f32, _f32, _f32, _f32, _vp, _sz, _vp])
 _SIGNATURES["lazyattn_prefill_fp8_workspace_size"] = (_sz, [_i32, _i32, _i32, _i32])
 _SIGNATURES["lazyattn_decode_plan_ints"] = (_sz, [_i32, _i32, _i32])
-_SIGNATURES["lazyattn_decode_plan"] = (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _vp])
+_SIGNATURES["lazyattn_decode_plan"] = (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _vp])
 _SIGNATURES["lazyattn_decode_planned_workspace_size"] = (_sz, [_i32, _i32, _i32, _i32, _i32])
 _SIGNATURES["lazyattn_decode_planned"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                                  _i32, _i32, _f32, _f32, _vp, _i32, _i32, _vp, _sz, _vp])
@@ -291,18 +291,19 @@ class DecodePlan:
     library's planner wrote it, ``device`` its copy on the GPU, and the item
     count and largest per-sequence slot count the call needs."""
 
-    def __init__(self, ints, device, num_items, max_items_per_seq, batch, num_kv_heads):
+    def __init__(self, ints, device, num_items, max_items_per_seq, batch, num_q_heads, num_kv_heads):
         self.ints, self.device = ints, device
         self.num_items, self.max_items_per_seq = num_items, max_items_per_seq
-        self.batch, self.num_kv_heads = batch, num_kv_heads
+        self.batch, self.num_q_heads, self.num_kv_heads = batch, num_q_heads, num_kv_heads
 
 
-def decode_plan(block_table, seq_lens, num_kv_heads, *, max_item_blocks=0, device=None):
+def decode_plan(block_table, seq_lens, num_q_heads, num_kv_heads, *, max_item_blocks=0, device=None):
     """Build a plan for lazyattn_decode_planned with the library's host-side
     planner (lazyattn_decode_plan) from copies of block_table [B, max_blocks]
     and seq_lens [B] in host memory; the plan goes to ``device`` (default: the
-    table's device, if a GPU).  Rebuild it when the table, the lengths or the
-    KV head count change."""
+    table's device, if a GPU).  It stays valid while sequences grow into
+    blocks appended to their rows; rebuild it when the words already in the
+    table, or the head counts, change."""
     _int32(block_table, "block_table")
     _int32(seq_lens, "seq_lens")
     if block_table.dim() != 2 or seq_lens.numel() != block_table.shape[0]:
@@ -316,13 +317,14 @@ def decode_plan(block_table, seq_lens, num_kv_heads, *, max_item_blocks=0, devic
         raise LazyAttnError("decode_plan: empty batch or bad sizes")
     buf = torch.empty(cap, dtype=torch.int32)
     n, m = ctypes.c_int(0), ctypes.c_int(0)
-    _check(lib.lazyattn_decode_plan(_ptr(table), _ptr(lens), b, max_blocks, num_kv_heads, int(max_item_blocks),
-                                    _ptr(buf), cap, ctypes.byref(n), ctypes.byref(m)), "lazyattn_decode_plan")
-    ints = buf[:(b + 3) // 4 * 4 + 4 * n.value].clone()
+    _check(lib.lazyattn_decode_plan(_ptr(table), _ptr(lens), b, max_blocks, num_q_heads, num_kv_heads,
+                                    int(max_item_blocks), _ptr(buf), cap, ctypes.byref(n), ctypes.byref(m)),
+           "lazyattn_decode_plan")
+    ints = buf[:(b + 3) // 4 * 4 + 12 * n.value].clone()
     if device is None:
         device = block_table.device if block_table.device.type == "cuda" else None
     dev_ints = ints.to(device) if device is not None else None
-    return DecodePlan(ints, dev_ints, n.value, m.value, b, num_kv_heads)
+    return DecodePlan(ints, dev_ints, n.value, m.value, b, num_q_heads, num_kv_heads)
 
 
 def decode_planned_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_items_per_seq):
@@ -346,7 +348,8 @@ def lazyattn_decode_planned(q, q_pos, k_pool, v_pool, block_table, seq_lens, pla
         raise LazyAttnError("q and pools must share a dtype")
     if block_table.dim() != 2 or block_table.shape[0] != b or q_pos.numel() != b or seq_lens.numel() != b:
         raise LazyAttnError("block_table [B, max_blocks], q_pos [B], seq_lens [B]")
-    if not isinstance(plan, DecodePlan) or plan.device is None or plan.batch != b or plan.num_kv_heads != hkv:
+    if not isinstance(plan, DecodePlan) or plan.device is None or plan.batch != b or plan.num_kv_heads != hkv \
+            or plan.num_q_heads != hq:
         raise LazyAttnError("plan must be decode_plan() of this batch's table and KV heads, on the GPU")
     _dev(plan.device, q)
     if out is None:

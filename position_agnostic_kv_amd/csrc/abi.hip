@@ -165,6 +165,7 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
   a.plan_items = plan_items;
   a.plan_max_items = plan_max_items;
   if (pool8) return from_hip(launch_decode_fp8(a, (hipStream_t)stream));
+  if (plan) return from_hip(launch_decode_planned(a, (hipStream_t)stream));
   return from_hip(launch_decode(a, bf16, (hipStream_t)stream));
 }
 
@@ -229,7 +230,8 @@ int lazyattn_decode_planned(void *out, const void *q, const int32_t *q_pos, cons
   if (!valid_dtype(dtype)) return LAZYATTN_ERR_DTYPE;
   if (dtype != LAZYATTN_BF16) return LAZYATTN_ERR_DTYPE;
   if (head_dim != 128 || num_kv_heads < 1 || num_q_heads < 1 || num_q_heads % num_kv_heads ||
-      num_q_heads / num_kv_heads > 16 || num_items < 1 || max_items_per_seq < 1 || max_items_per_seq > 65535)
+      !pow2_group(num_q_heads / num_kv_heads) || num_q_heads / num_kv_heads > 16 || num_items < 1 ||
+      max_items_per_seq < 1 || max_items_per_seq > 65535)
     return LAZYATTN_ERR_SHAPE;
   if (batch > 0 && !plan) return LAZYATTN_ERR_NULL;
   if ((uintptr_t)plan & 15u) return LAZYATTN_ERR_SHAPE;

@@ -92,9 +92,8 @@ struct DecodeKernelArgs {
   int num_blocks, split_blocks, max_splits;
   float scale_log2, rope_theta;
   float out_scale;   // V scale of an 8-bit pool (1 otherwise)
-  // A work plan (nullptr: uniform splits of split_blocks blocks).  Item i,
-  // taken by workgroup i: (sequence, work head, slot | first block << 16,
-  // end block); plan_counts[b] = the slots (partials) of sequence b.
+  // A work plan (planned decode): per-sequence slot counts, and the items
+  // (kPlanInts ints each) that workgroup i takes; nullptr otherwise.
   const int4 *plan_items;
   const int32_t *plan_counts;
   int batch;
@@ -102,50 +101,32 @@ struct DecodeKernelArgs {
 
 // The share of the decode a workgroup takes: sequence b, work head g, split
 // `split` of `nsplit`, blocks [blk0, blk1) of the sequence's table (nblk of
-// them in all).  Returns false for a workgroup with nothing to do: past the
-// last unit, or a plan item outside the batch, the heads or the sequence's
-// slot count (a malformed plan is never read past).
+// them in all).  Returns false for a workgroup past the last unit.
 struct DecodeShare {
   int b, g, split, nsplit, blk0, blk1, nblk, seq_len;
   bool bad_len;
 };
 __device__ __forceinline__ bool decode_share(const DecodeKernelArgs &a, DecodeShare &w) {
+  // Work item -> (split, KV head, sequence).  A KV head whose query heads are
+  // split over 2^kv_shift workgroups gives them consecutive slots on one XCD
+  // (workgroups go round-robin over the XCDs), so they run side by side and
+  // the twin reads of each K/V block are served by that XCD's L2.
   const int hkv = a.num_kv_heads;
-  if (a.plan_items) {
-    if ((int)blockIdx.x >= a.num_units) return false;
-    const int4 it = a.plan_items[blockIdx.x];
-    if ((unsigned)it.x >= (unsigned)a.batch || (unsigned)it.y >= (unsigned)hkv) return false;
-    w.b = it.x;
-    w.g = it.y;
-    w.split = it.z & 0xffff;
-    w.nsplit = a.plan_counts[w.b];
-    if (w.nsplit < 1 || w.nsplit > a.max_splits || w.split >= w.nsplit) return false;
-    w.blk0 = (int)((unsigned)it.z >> 16);
-    w.blk1 = it.w;
-  } else {
-    // Work item -> (split, KV head, sequence).  A KV head whose query heads
-    // are split over 2^kv_shift workgroups gives them consecutive slots on
-    // one XCD (workgroups go round-robin over the XCDs), so they run side by
-    // side and the twin reads of each K/V block are served by that XCD's L2.
-    const int slot = blockIdx.x / kXcds;
-    const int hsub = slot & ((1 << a.kv_shift) - 1);
-    const int unit = (slot >> a.kv_shift) * kXcds + (int)(blockIdx.x % kXcds);
-    if (unit >= a.num_units) return false;
-    const int hkv_pool = hkv >> a.kv_shift;
-    w.split = unit % a.max_splits;
-    const int gp = (unit / a.max_splits) % hkv_pool;  // KV head in the pool
-    w.b = unit / a.max_splits / hkv_pool;
-    w.g = (gp << a.kv_shift) | hsub;                  // work head: query heads g*G .. g*G+G-1
-  }
+  const int slot = blockIdx.x / kXcds;
+  const int hsub = slot & ((1 << a.kv_shift) - 1);
+  const int unit = (slot >> a.kv_shift) * kXcds + (int)(blockIdx.x % kXcds);
+  if (unit >= a.num_units) return false;
+  const int hkv_pool = hkv >> a.kv_shift;
+  w.split = unit % a.max_splits;
+  const int gp = (unit / a.max_splits) % hkv_pool;  // KV head in the pool
+  w.b = unit / a.max_splits / hkv_pool;
+  w.g = (gp << a.kv_shift) | hsub;                  // work head: query heads g*G .. g*G+G-1
   w.seq_len = a.seq_lens[w.b];
   w.bad_len = w.seq_len < 0 || w.seq_len > a.max_blocks * kBlockTokens;
   w.nblk = w.bad_len ? 0 : (w.seq_len + kBlockTokens - 1) / kBlockTokens;
-  if (!a.plan_items) {
-    w.nsplit = (w.nblk + a.split_blocks - 1) / a.split_blocks;
-    w.blk0 = w.split * a.split_blocks;
-    w.blk1 = w.blk0 + a.split_blocks;
-  }
-  w.blk1 = min(w.blk1, w.nblk);
+  w.nsplit = (w.nblk + a.split_blocks - 1) / a.split_blocks;
+  w.blk0 = w.split * a.split_blocks;
+  w.blk1 = min(w.blk0 + a.split_blocks, w.nblk);
   w.blk0 = min(w.blk0, w.blk1);
   return true;
 }
@@ -838,9 +819,17 @@ decode_mma8_kernel(const DecodeKernelArgs a) {
 constexpr int kMmaSlots = 2;           // LDS ring slots per wave (K and V of one block each)
 constexpr int kMma16WorkgroupsPerCu = 2;
 
-template <int G, int MODE>
-__global__ void __launch_bounds__(kDecodeWaves * kWave, kMma16WorkgroupsPerCu)
-decode_mma16_kernel(const DecodeKernelArgs a) {
+// PLAN: the workgroup takes one item of a host-built plan (see
+// decode_plan.cpp): a run of blocks of one KV head and up to kPlanMembers
+// sequences that read the same blocks (one document they all hold).  Its 16
+// MFMA columns are then (member, query head) pairs: member t16 / G, head
+// t16 % G, each with its own query, position and offset; every member
+// writes its own partial.
+constexpr int kPlanMembers = 4;
+constexpr int kPlanInts = 12;  // ints per plan item
+
+template <int G, int MODE, bool PLAN>
+__device__ __forceinline__ void decode_mma16_body(const DecodeKernelArgs &a) {
   using E = Elem<bf16>;
   constexpr int D = 128;
   constexpr int CPR = D / 8;               // 16-byte chunks per row
@@ -852,43 +841,105 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
   constexpr bool EAGER = MODE == kRopeEager;
   constexpr bool ALIBI = MODE == kAlibi;
   static_assert(G >= 1 && G <= 16, "one workgroup takes up to 16 query heads");
-  static_assert(G * D * sizeof(float) <= kMmaSlots * 2 * BLKB, "a wave's partial output fits its ring");
+  static_assert(!PLAN || MODE == kRopeLazy, "plans: lazy RoPE");
+  constexpr int NC = PLAN ? 16 : G;  // MFMA columns in use at most
+  static_assert(NC * D * sizeof(float) <= kMmaSlots * 2 * BLKB, "a wave's partial output fits its ring");
 
   // per wave: kMmaSlots x (K tile, V tile); after the loop a wave's ring holds
-  // its partial output [G][D] for the merge
+  // its partial output [NC][D] for the merge
   __shared__ __attribute__((aligned(1024))) char s_ring[kDecodeWaves][kMmaSlots][2][BLKB];
-  __shared__ float s_m[kDecodeWaves][G];
-  __shared__ float s_l[kDecodeWaves][G];
+  __shared__ float s_m[kDecodeWaves][NC];
+  __shared__ float s_l[kDecodeWaves][NC];
   __shared__ int s_bad[kDecodeWaves];  // per wave: a table word pointed outside the pool
 
-  DecodeShare sh;
-  if (!decode_share(a, sh)) return;
   const int hkv = a.num_kv_heads;
   const int hkv_pool = hkv >> a.kv_shift;
-  const int b = sh.b, g = sh.g, gp = g >> a.kv_shift, split = sh.split, nsplit = sh.nsplit;
-  const int seq_len = sh.seq_len;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int hq = hkv * G;
+  const int t16 = lane & 15;  // K token row / query head column / V^T dim row
+  const int g4 = lane >> 4;   // lane group
+
+  int b, g, split, nsplit, nblk, seq_len, blk0, blk1;
+  bool bad_len;
+  int nmem = 1;                              // planned: members of the item
+  uint32_t mem[kPlanMembers] = {0u, 0u, 0u, 0u};  // (sequence | slot << 16)
+  int mstart[kPlanMembers] = {0, 0, 0, 0};        // the run's first block in each member's row
+  if constexpr (PLAN) {
+    // item: (KV head | members << 16, first block, end block (both in
+    // member 0's row), 0, members 0..3, the run's start in each member's
+    // row); an item naming a sequence, head, slot or row place outside the
+    // batch, the heads, a sequence's slot count or the table is skipped,
+    // block ranges are clipped to member 0's length
+    if ((int)blockIdx.x >= a.num_units) return;
+    const int4 r0 = a.plan_items[3 * blockIdx.x], r1 = a.plan_items[3 * blockIdx.x + 1];
+    const int4 r2 = a.plan_items[3 * blockIdx.x + 2];
+    g = r0.x & 0xffff;
+    nmem = (int)((uint32_t)r0.x >> 16);
+    blk0 = r0.y;
+    blk1 = r0.z;
+    mem[0] = (uint32_t)r1.x;
+    mem[1] = (uint32_t)r1.y;
+    mem[2] = (uint32_t)r1.z;
+    mem[3] = (uint32_t)r1.w;
+    mstart[0] = r2.x;
+    mstart[1] = r2.y;
+    mstart[2] = r2.z;
+    mstart[3] = r2.w;
+    if (g >= hkv || nmem < 1 || nmem > kPlanMembers || nmem * G > 16) return;
+    for (int k = 0; k < nmem; ++k) {
+      const int mb = (int)(mem[k] & 0xffffu), ms = (int)(mem[k] >> 16);
+      if (mb >= a.batch || mstart[k] < 0 || mstart[k] >= a.max_blocks) return;
+      const int cnt = a.plan_counts[mb];
+      if (cnt < 1 || cnt > a.max_splits || ms >= cnt) return;
+    }
+    b = (int)(mem[0] & 0xffffu);
+    split = (int)(mem[0] >> 16);
+    nsplit = a.plan_counts[b];
+    seq_len = a.seq_lens[b];
+    bad_len = seq_len < 0 || seq_len > a.max_blocks * kBlockTokens;
+    nblk = bad_len ? 0 : (seq_len + kBlockTokens - 1) / kBlockTokens;
+    blk1 = min(max(blk1, 0), nblk);
+    blk0 = min(max(blk0, 0), blk1);
+  } else {
+    DecodeShare sh;
+    if (!decode_share(a, sh)) return;
+    b = sh.b;
+    g = sh.g;
+    split = sh.split;
+    nsplit = sh.nsplit;
+    nblk = sh.nblk;
+    seq_len = sh.seq_len;
+    bad_len = sh.bad_len;
+    blk0 = sh.blk0;
+    blk1 = sh.blk1;
+  }
+  const int gp = g >> a.kv_shift;
 
   bf16 *out = (bf16 *)a.out + ((size_t)b * hq + (size_t)g * G) * D;
-  if (sh.nblk == 0) {  // empty sequence -> zeros; invalid length -> NaN
-    if (split == 0)
-      for (int i = tid; i < G * D; i += NT) E::store(out, i, sh.bad_len ? __builtin_nanf("") : 0.f);
+  if (nblk == 0) {  // empty sequence -> zeros; invalid length -> NaN
+    if (split == 0 && nmem == 1)
+      for (int i = tid; i < G * D; i += NT) E::store(out, i, bad_len ? __builtin_nanf("") : 0.f);
     return;
   }
   if (split >= nsplit) return;
 
   const int n_pos = a.q_pos[b];
-  const int t16 = lane & 15;  // K token row / query head column / V^T dim row
-  const int g4 = lane >> 4;   // lane group
-  const bool live = t16 < G;
+  // this lane's column: query head t16, or (planned) head t16 % G of member
+  // t16 / G, whose sequence is bcol
+  const int ncol = PLAN ? nmem * G : G;
+  const bool live = t16 < ncol;
+  const int mcol = PLAN ? t16 / G : 0;
+  const int hcol = PLAN ? t16 % G : t16;
+  const int bcol = !PLAN || !live ? b
+                   : (int)((mcol == 0 ? mem[0] : mcol == 1 ? mem[1] : mcol == 2 ? mem[2] : mem[3]) & 0xffffu);
 
-  // raw (bf16) query of head t16, dims 32c + 8 g4 .. + 8 (chunk 4c + g4)
+  // raw (bf16) query of the lane's column, dims 32c + 8 g4 .. + 8 (chunk 4c + g4)
   uint4 qraw[4];
   {
-    const uint4 *qh = (const uint4 *)((const bf16 *)a.q + ((size_t)b * hq + (size_t)g * G + (live ? t16 : 0)) * D);
+    const uint4 *qh =
+        (const uint4 *)((const bf16 *)a.q + ((size_t)bcol * hq + (size_t)g * G + (live ? hcol : 0)) * D);
 #pragma unroll
     for (int c = 0; c < 4; ++c) qraw[c] = live ? qh[4 * c + g4] : make_uint4(0u, 0u, 0u, 0u);
   }
@@ -916,6 +967,39 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
           const int e = 2 * k + e2;
           const int fi = 32 * c + 8 * g4 + e;
           const float cv = __shfl(cs, fi), sv = __shfl(sn, fi);
+          const uint32_t wx = dw4(qraw[c], k), wy = dw4(qraw[c + 2], k);
+          const float x = e2 ? bf16_hi(wx) : bf16_lo(wx);
+          const float y = e2 ? bf16_hi(wy) : bf16_lo(wy);
+          r[e2] = fmaf(x, cv, -(y * sv)) * a.scale_log2;
+          r[2 + e2] = fmaf(y, cv, x * sv) * a.scale_log2;
+        }
+        split_bf16x2(r[0], r[1], xh[k], xl[k]);
+        split_bf16x2(r[2], r[3], yh[k], yl[k]);
+      }
+      qh[c] = as_bf16x8(make_uint4(xh[0], xh[1], xh[2], xh[3]));
+      ql[c] = as_bf16x8(make_uint4(xl[0], xl[1], xl[2], xl[3]));
+      qh[c + 2] = as_bf16x8(make_uint4(yh[0], yh[1], yh[2], yh[3]));
+      ql[c + 2] = as_bf16x8(make_uint4(yl[0], yl[1], yl[2], yl[3]));
+    }
+  };
+  // the same rotation with a delta of the lane's own (planned items with
+  // several members: each column has its sequence's position and offset):
+  // the lane evaluates its 16 frequencies itself, from lane fi's inverse
+  // frequency, by the same expression, so a delta gives the same q' either way
+  auto rotate_own = [&](int delta) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t xh[4], xl[4], yh[4], yl[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float r[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const int e = 2 * k + e2;
+          const int fi = 32 * c + 8 * g4 + e;
+          const double tt = (double)delta * (__shfl(inv_freq, fi) * 0.15915494309189535);
+          const float f = (float)(tt - rint(tt));
+          const float cv = __builtin_amdgcn_cosf(f), sv = __builtin_amdgcn_sinf(f);
           const uint32_t wx = dw4(qraw[c], k), wy = dw4(qraw[c + 2], k);
           const float x = e2 ? bf16_hi(wx) : bf16_lo(wx);
           const float y = e2 ? bf16_hi(wy) : bf16_lo(wy);
@@ -959,7 +1043,6 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
   char *ring = &s_ring[wave][0][0][0];
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr_t)ring;
 
-  const int blk0 = sh.blk0, blk1 = sh.blk1;
   // table words and fill counts as scalar loads (see as_const_as)
   const auto trow = as_const_as(a.table + (size_t)b * a.max_blocks);
   const auto fill4 = a.fill4 ? as_const_as(a.fill4) : nullptr;
@@ -993,6 +1076,17 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
   for (int c = 0; c < 8; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = kMaxFloor, lsum = 0.f;
   int cur_off = -1;
+  // several members: every column rotated once, by its own sequence's
+  // position and offset (the plan takes such runs only where each member's
+  // offset stays the same over the run)
+  const bool multi = PLAN && nmem > 1;
+  if constexpr (PLAN) {
+    if (multi && blk0 < blk1) {
+      const int scol = mcol == 0 ? mstart[0] : mcol == 1 ? mstart[1] : mcol == 2 ? mstart[2] : mstart[3];
+      const int own_off = word_offset(a.table[(size_t)bcol * a.max_blocks + (live ? scol : blk0)]);
+      rotate_own(live ? a.q_pos[bcol] - own_off : 0);
+    }
+  }
 
   // this wave takes blocks blk0 + wave, + 4, ...; slots alternate
   int blk = blk0 + wave;
@@ -1027,7 +1121,7 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
 
     if constexpr (MODE == kRopeLazy) {
       const int off = word_offset(mcur);
-      if (off != cur_off) {
+      if (!multi && off != cur_off) {
         rotate(n_pos - off);
         cur_off = off;
       }
@@ -1097,11 +1191,9 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
   if (lane == 0) s_bad[wave] = bad;
   __syncthreads();
 
-  const bool single = nsplit == 1;
   const bool flagged = (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) != 0;
-  const size_t part = ((size_t)b * hkv + g) * a.max_splits + split;
-  for (int i = tid; i < G * D; i += NT) {
-    const int h = i / D;
+  for (int i = tid; i < ncol * D; i += NT) {
+    const int h = i / D;  // column
     float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
@@ -1116,11 +1208,23 @@ decode_mma16_kernel(const DecodeKernelArgs a) {
       o = __builtin_nanf("");
       ls = __builtin_nanf("");
     }
-    if (single) {
-      E::store(out, i, ls != 0.f ? o / ls : 0.f);
+    // the column's sequence, query head (within the group) and partial slot
+    int bs = b, hh = h, sp = split, ns = nsplit;
+    if constexpr (PLAN) {
+      const int k = h / G;
+      const uint32_t mk = k == 0 ? mem[0] : k == 1 ? mem[1] : k == 2 ? mem[2] : mem[3];
+      bs = (int)(mk & 0xffffu);
+      sp = (int)(mk >> 16);
+      hh = h % G;
+      ns = a.plan_counts[bs];
+    }
+    const int d = i % D;
+    if (ns == 1) {
+      E::store((bf16 *)a.out + ((size_t)bs * hq + (size_t)g * G + hh) * D, d, ls != 0.f ? o / ls : 0.f);
     } else {
-      a.ws_o[part * G * D + i] = o;
-      if (i % D == 0) a.ws_ml[part * G + h] = make_float2(mx, ls);
+      const size_t part = ((size_t)bs * hkv + g) * a.max_splits + sp;
+      a.ws_o[(part * G + hh) * D + d] = o;
+      if (d == 0) a.ws_ml[part * G + hh] = make_float2(mx, ls);
     }
   }
 }
@@ -1460,6 +1564,19 @@ decode_mma16_wide_kernel(const DecodeKernelArgs a) {
   }
 }
 
+template <int G, int MODE>
+__global__ void __launch_bounds__(kDecodeWaves * kWave, kMma16WorkgroupsPerCu)
+decode_mma16_kernel(const DecodeKernelArgs a) {
+  decode_mma16_body<G, MODE, false>(a);
+}
+
+// the planned decode: one plan item per workgroup
+template <int G>
+__global__ void __launch_bounds__(kDecodeWaves * kWave, kMma16WorkgroupsPerCu)
+decode_planned_kernel(const DecodeKernelArgs a) {
+  decode_mma16_body<G, kRopeLazy, true>(a);
+}
+
 // Merge the per-split partials of one (sequence, KV head): log-sum-exp weights.
 // One workgroup per (sequence, KV head, group of up to 8 query heads); each
 // thread merges 4 consecutive dims of one head with 16-byte loads, so that a
@@ -1602,8 +1719,7 @@ enum DecodeImplKernel { kValu = 0, kMma8 = 1, kMma16 = 2, kMma16Wide = 3 };
 
 template <typename T, int D, int G, int MODE, bool F8 = false, int IMPL = kValu>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
-  // a work plan is read by the bf16 matrix-core kernel for up to 16 heads only
-  if (a.plan && (IMPL != kMma16 || a.plan_items < 1 || a.plan_max_items < 1)) return hipErrorInvalidValue;
+  if (a.plan) return hipErrorInvalidValue;  // plans go to launch_decode_planned
   DecodeKernelArgs k;
   k.out = a.out;
   k.q = a.q;
@@ -1621,15 +1737,15 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   k.kv_shift = __builtin_ctz((unsigned)hsplit);  // hsplit is a power of two
   k.num_blocks = a.num_blocks;
   k.split_blocks = a.split_blocks;
-  k.max_splits = a.plan ? a.plan_max_items : (a.max_blocks + a.split_blocks - 1) / a.split_blocks;
+  k.max_splits = (a.max_blocks + a.split_blocks - 1) / a.split_blocks;
   k.batch = a.batch;
-  k.plan_counts = a.plan;
-  k.plan_items = a.plan ? (const int4 *)(a.plan + decode_plan_items_offset(a.batch)) : nullptr;
+  k.plan_counts = nullptr;
+  k.plan_items = nullptr;
   k.scale_log2 = a.scale * kLog2e * (F8 ? a.k_scale : 1.f);
   k.out_scale = F8 ? a.v_scale : 1.f;
   k.rope_theta = a.rope_theta;
-  const long long units = a.plan ? (long long)a.plan_items : (long long)k.max_splits * a.num_kv_heads * a.batch;
-  const long long grid = a.plan ? units : (units + kXcds - 1) / kXcds * kXcds * hsplit;
+  const long long units = (long long)k.max_splits * a.num_kv_heads * a.batch;
+  const long long grid = (units + kXcds - 1) / kXcds * kXcds * hsplit;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   k.num_units = (int)units;
   size_t off_o, total;
@@ -1655,6 +1771,61 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_combine_kernel<T, D, G>), dim3((unsigned)(work_heads * (G / kGh)), (unsigned)a.batch),
                      dim3(kGh * D / 4), 0, stream, k);
   return hipGetLastError();
+}
+
+// Planned decode (bf16 pools, head_dim 128, lazy RoPE): one workgroup per
+// plan item, then the combine over each sequence's slots.
+template <int G>
+static hipError_t launch_planned_t(const DecodeArgs &a, hipStream_t stream) {
+  DecodeKernelArgs k;
+  k.out = a.out;
+  k.q = a.q;
+  k.q_pos = a.q_pos;
+  k.k_pool = (const uint4 *)a.k_pool;
+  k.v_pool = (const uint4 *)a.v_pool;
+  k.table = a.table;
+  k.seq_lens = a.seq_lens;
+  k.slopes = nullptr;
+  k.fill4 = (const uint32_t *)a.block_fill;
+  k.max_blocks = a.max_blocks;
+  k.num_kv_heads = a.num_kv_heads;
+  k.kv_shift = 0;
+  k.num_units = a.plan_items;
+  k.num_blocks = a.num_blocks;
+  k.split_blocks = 0;  // unused: slots come from the plan
+  k.max_splits = a.plan_max_items;
+  k.scale_log2 = a.scale * kLog2e;
+  k.rope_theta = a.rope_theta;
+  k.out_scale = 1.f;
+  k.batch = a.batch;
+  k.plan_counts = a.plan;
+  k.plan_items = (const int4 *)(a.plan + decode_plan_items_offset(a.batch));
+  size_t off_o, total;
+  workspace_layout(a.batch, a.num_q_heads, a.num_kv_heads, a.head_dim, (size_t)k.max_splits, &off_o, &total);
+  char *ws = (char *)a.workspace;
+  k.ws_ml = ws ? (float2 *)ws : nullptr;
+  k.ws_o = ws ? (float *)(ws + off_o) : nullptr;
+  hipLaunchKernelGGL((decode_planned_kernel<G>), dim3((unsigned)a.plan_items),
+                     dim3(kDecodeWaves * kWave), 0, stream, k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || k.max_splits <= 1) return e;
+  constexpr int kGh = G < 8 ? G : 8;
+  hipLaunchKernelGGL((decode_combine_kernel<bf16, 128, G>), dim3((unsigned)(a.num_kv_heads * (G / kGh)),
+                     (unsigned)a.batch), dim3(kGh * 128 / 4), 0, stream, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_planned(const DecodeArgs &a, hipStream_t s) {
+  if (!a.plan || a.plan_items < 1 || a.plan_max_items < 1 || a.head_dim != 128 || a.mode != kRopeLazy)
+    return hipErrorInvalidValue;
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_planned_t<1>(a, s);
+    case 2: return launch_planned_t<2>(a, s);
+    case 4: return launch_planned_t<4>(a, s);
+    case 8: return launch_planned_t<8>(a, s);
+    case 16: return launch_planned_t<16>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int MODE>

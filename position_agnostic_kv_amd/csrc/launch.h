@@ -54,11 +54,12 @@ struct DecodeArgs {
   int mode;             // PosMode
   float k_scale = 1.f, v_scale = 1.f;  // 8-bit pools: value = code * scale
   // work plan (device): per-sequence slot counts [batch], then plan_items
-  // items of 4 ints from decode_plan_items_offset(batch); nullptr: splits
+  // items of 12 ints from decode_plan_items_offset(batch); nullptr: splits
   const int32_t *plan = nullptr;
   int plan_items = 0, plan_max_items = 0;
 };
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t stream);
+hipError_t launch_decode_planned(const DecodeArgs &a, hipStream_t stream);
 size_t decode_planned_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                      int max_items_per_seq);
 size_t decode_plan_items_offset(int batch);

@@ -107,6 +107,7 @@ def test_planned_decode_argument_errors(lib):
     assert planned(lib, d=64) == -3                # head_dim 128 only
     assert planned(lib, hq=64, hkv=2) == -3        # groups up to 16
     assert planned(lib, hq=6, hkv=4) == -3
+    assert planned(lib, hq=6, hkv=2) == -3         # group 3
     assert planned(lib, items=0) == -3
     assert planned(lib, max_items=0) == -3
     assert planned(lib, plan=NULL) == -1

@@ -48,7 +48,7 @@ def test_planned_shared_documents(hq, hkv):
     W.materialize_numpy(case)
     dc = DeviceCase(case)
     dc.append()
-    plan = pak.decode_plan(dc.table, dc.seq_lens, hkv)
+    plan = pak.decode_plan(dc.table, dc.seq_lens, hq, hkv)
     assert plan.max_items_per_seq > 1
     out = _planned(dc, case, plan)
     again = _planned(dc, case, plan)
@@ -58,15 +58,15 @@ def test_planned_shared_documents(hq, hkv):
 
 @pytest.mark.parametrize("limit", [8, 0])
 def test_planned_runs_equal_to_splits_are_bit_identical(limit):
-    """Zero offsets: runs are cut only at the size limit.  Lengths are chosen
-    so that no short last run is merged: the runs are the splits."""
+    """Zero offsets: runs are cut only at the size limit, so the runs are the
+    uniform splits and the kernel sees the same partials."""
     ctx = [16 * 44, 16 * 23, 16 * 21, 16 * 12]   # + the new token: 45, 24, 22, 13 blocks
     case = W.decode_case(47, len(ctx), 16, 4, 128, ctx, (2, 9), offsets="random")
     W.materialize_numpy(case)
     dc = DeviceCase(case)
     dc.append()
     table0 = (dc.table & 0xFFFF).contiguous()
-    plan = pak.decode_plan(table0, dc.seq_lens, 4, max_item_blocks=limit)
+    plan = pak.decode_plan(table0, dc.seq_lens, 16, 4, max_item_blocks=limit)
     split = limit if limit else 1024
     say(f"[planned] bit-identical runs of {split} blocks, {plan.num_items} items")
     want = pak.lazyattn_decode(dc.q, dc.q_pos, dc.k_pool, dc.v_pool, table0, dc.seq_lens, scale=case.scale,
@@ -85,7 +85,7 @@ def test_planned_ragged_empty_and_invalid():
     lens[2] = 0
     lens[5] = 16 * case.layout.table.shape[1] + 3
     dlens = torch.from_numpy(lens.astype(np.int32)).to(dc.q.device)
-    plan = pak.decode_plan(dc.table, dlens, 4, max_item_blocks=6)
+    plan = pak.decode_plan(dc.table, dlens, 16, 4, max_item_blocks=6)
     say(f"[planned] ragged, {plan.num_items} items, up to {plan.max_items_per_seq} slots")
     out = W.to_float(_planned(dc, case, plan, seq_lens=dlens), case.dtype)
     assert np.all(out[2] == 0)
@@ -104,7 +104,7 @@ def test_planned_plan_survives_growth():
     dc = DeviceCase(case)
     dc.append()
     short = torch.from_numpy(case.layout.cached_lens.astype(np.int32)).to(dc.q.device)  # before the new token
-    plan = pak.decode_plan(dc.table, short, 8)
+    plan = pak.decode_plan(dc.table, short, 32, 8)
     out = _planned(dc, case, plan)
     assert_parity(W.to_float(out, case.dtype), oracle_decode(case), case.dtype, "planned after growth")
 
@@ -120,7 +120,7 @@ def test_full_size_zipf_planned_sampled():
     seqs = sorted(rng.choice(case.batch, size=4, replace=False).tolist())
     kp, vp, tab, fill = _gather(dc, case, seqs)
     dc.append()
-    plan = pak.decode_plan(dc.table, dc.seq_lens, case.num_kv_heads)
+    plan = pak.decode_plan(dc.table, dc.seq_lens, case.num_q_heads, case.num_kv_heads)
     got_t = _planned(dc, case, plan)
     ref_t = dc.decode()
     torch.cuda.synchronize()
