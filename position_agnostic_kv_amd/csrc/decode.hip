@@ -843,7 +843,11 @@ __device__ __forceinline__ void decode_mma16_body(const DecodeKernelArgs &a) {
   static_assert(G >= 1 && G <= 16, "one workgroup takes up to 16 query heads");
   static_assert(!PLAN || MODE == kRopeLazy, "plans: lazy RoPE");
   constexpr int NC = PLAN ? 16 : G;  // MFMA columns in use at most
-  static_assert(NC * D * sizeof(float) <= kMmaSlots * 2 * BLKB, "a wave's partial output fits its ring");
+  // a column's partial output row in the ring at the merge: with all 16
+  // columns live, rows padded by 16 bytes keep the eight lanes of a
+  // ds_write_b128 cycle (eight columns, same dims) out of one bank slot
+  constexpr int OROW = PLAN ? D + 4 : D;
+  static_assert(NC * OROW * sizeof(float) <= kMmaSlots * 2 * BLKB, "a wave's partial output fits its ring");
 
   // per wave: kMmaSlots x (K tile, V tile); after the loop a wave's ring holds
   // its partial output [NC][D] for the merge
@@ -1184,7 +1188,7 @@ __device__ __forceinline__ void decode_mma16_body(const DecodeKernelArgs &a) {
     s_l[wave][t16] = lsum;
   }
   if (live) {
-    float *so = (float *)ring + t16 * D + 4 * g4;
+    float *so = (float *)ring + t16 * OROW + 4 * g4;
 #pragma unroll
     for (int c = 0; c < 8; ++c) *(f32x4_t *)(so + 16 * c) = O[c];
   }
@@ -1194,6 +1198,7 @@ __device__ __forceinline__ void decode_mma16_body(const DecodeKernelArgs &a) {
   const bool flagged = (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) != 0;
   for (int i = tid; i < ncol * D; i += NT) {
     const int h = i / D;  // column
+    const int d = i % D;
     float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
@@ -1201,7 +1206,7 @@ __device__ __forceinline__ void decode_mma16_body(const DecodeKernelArgs &a) {
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w) {
       const float f = s_m[w][h] == -INFINITY ? 0.f : fast_exp2(s_m[w][h] - mx);
-      o = fmaf(((const float *)&s_ring[w][0][0][0])[i], f, o);
+      o = fmaf(((const float *)&s_ring[w][0][0][0])[h * OROW + d], f, o);
       ls = fmaf(s_l[w][h], f, ls);
     }
     if (flagged) {
@@ -1218,7 +1223,6 @@ __device__ __forceinline__ void decode_mma16_body(const DecodeKernelArgs &a) {
       hh = h % G;
       ns = a.plan_counts[bs];
     }
-    const int d = i % D;
     if (ns == 1) {
       E::store((bf16 *)a.out + ((size_t)bs * hq + (size_t)g * G + hh) * D, d, ls != 0.f ? o / ls : 0.f);
     } else {

@@ -163,9 +163,10 @@ def test_staged_query_rows_are_padded():
 
 
 def test_wide_merge_stores_are_conflict_free():
-    """Multi-query decode: at the merge, lane (t, g) stores head t's four
-    dims 4 g + 16 c .. + 3 as one ds_write_b128 into rows of 132 floats
-    (unpadded rows of 128 put eight consecutive lanes in one slot)."""
+    """Multi-query decode, and the planned decode with all 16 columns live:
+    at the merge, lane (t, g) stores column t's four dims 4 g + 16 c .. + 3
+    as one ds_write_b128 into rows of 132 floats (unpadded rows of 128 put
+    eight consecutive lanes in one slot)."""
     for c in range(8):
         padded = [((lane & 15) * 132 + 4 * (lane >> 4) + 16 * c) * 4 for lane in range(64)]
         plain = [((lane & 15) * 128 + 4 * (lane >> 4) + 16 * c) * 4 for lane in range(64)]
