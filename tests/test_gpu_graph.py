@@ -1,6 +1,7 @@
 """The C-ABI calls are stream-ordered and allocate nothing, so a whole step
-(append + decode with split-K partials, append + prefill, and the 8-bit
-pool's append + decode) can be captured in a HIP graph and replayed.  Every
+(append + decode with split-K partials, append + prefill, the 8-bit pool's
+append + decode, and the planned decode with a plan built beforehand) can be
+captured in a HIP graph and replayed.  Every
 replay, with eager work on the same stream between replays, must give the
 eager results bit for bit (the kernels are deterministic).  Outputs and the
 decode workspace are allocated before capture; nothing inside the graph
@@ -36,6 +37,11 @@ def test_graph_replays_equal_eager():
     k8 = W.e4m3_codes_torch(shape, DEV, 11)
     v8 = W.e4m3_codes_torch(shape, DEV, 12)
     out8 = torch.empty_like(dd.q)
+    plan = pak.decode_plan(dd.table, dd.seq_lens, dcase.num_q_heads, dcase.num_kv_heads, max_item_blocks=8)
+    pws = torch.empty(max(pak.decode_planned_workspace_size(dcase.batch, dcase.num_q_heads, dcase.num_kv_heads,
+                                                            dcase.head_dim, plan.max_items_per_seq), 1),
+                      dtype=torch.uint8, device=DEV)
+    pl_out = torch.empty_like(dd.q)
 
     def step():
         pak.kvcache_append(dd.k_pool, dd.v_pool, dd.k_new, dd.v_new, dd.slots)
@@ -47,10 +53,13 @@ def test_graph_replays_equal_eager():
         pak.kvcache_append_fp8(k8, v8, dd.k_new, dd.v_new, dd.slots, 0.25, 0.125)
         pak.lazyattn_decode_fp8(dd.q, dd.q_pos, k8, v8, dd.table, dd.seq_lens, 0.25, 0.125, scale=dcase.scale,
                                 rope_theta=dcase.rope_theta, split_blocks=split, out=out8, workspace=ws)
+        pak.lazyattn_decode_planned(dd.q, dd.q_pos, dd.k_pool, dd.v_pool, dd.table, dd.seq_lens, plan,
+                                    scale=dcase.scale, rope_theta=dcase.rope_theta, out=pl_out, workspace=pws)
 
+    outs = (dout, pout, out8, pl_out)
     step()
     torch.cuda.synchronize()
-    want = [_bits(dout), _bits(pout), _bits(out8)]
+    want = [_bits(t) for t in outs]
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -63,16 +72,16 @@ def test_graph_replays_equal_eager():
         step()
     torch.cuda.synchronize()
     for r in range(4):
-        for t in (dout, pout, out8):
+        for t in outs:
             t.fill_(0)
         graph.replay()
         torch.cuda.synchronize()
-        got = [_bits(dout), _bits(pout), _bits(out8)]
+        got = [_bits(t) for t in outs]
         say(f"[graph] replay {r}")
-        for name, g, w in zip(("decode", "prefill", "decode fp8"), got, want):
+        for name, g, w in zip(("decode", "prefill", "decode fp8", "planned decode"), got, want):
             assert torch.equal(g, w), f"replay {r}: {name} differs from the eager step"
         # eager work between replays, on the same buffers
         step()
         torch.cuda.synchronize()
-        assert all(torch.equal(_bits(t), w) for t, w in zip((dout, pout, out8), want))
+        assert all(torch.equal(_bits(t), w) for t, w in zip(outs, want))
     assert np.isfinite(W.to_float(dout, W.BF16)).all()

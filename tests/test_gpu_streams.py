@@ -96,3 +96,29 @@ def test_side_stream_prefill_allocates_safely():
     for i, out in enumerate(outs):
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"side-stream call {i} differs"
     assert_parity(W.to_float(outs[-1], case.dtype), want, case.dtype, "side-stream prefill")
+
+
+def test_side_stream_planned_decode_allocates_safely():
+    case = _ragged("decode", 404)
+    say(f"[side stream planned decode] blocks={case.layout.num_blocks} slots={case.seq_lens.tolist()}")
+    dc = DeviceCase(case)
+    dc.append()
+    fill = _odd_fill(dc)
+    assert fill.numel() % 4 != 0
+    plan = pak.decode_plan(dc.table, dc.seq_lens, case.num_q_heads, case.num_kv_heads, max_item_blocks=5)
+    kw = dict(scale=case.scale, rope_theta=case.rope_theta, block_fill=fill)
+    args = (dc.q, dc.q_pos, dc.k_pool, dc.v_pool, dc.table, dc.seq_lens, plan)
+    ref = pak.lazyattn_decode_planned(*args, **kw)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=DEV)
+    outs = []
+    for _ in range(3):
+        outs.append(pak.lazyattn_decode_planned(*args, stream=side, **kw))
+        _churn()
+    torch.cuda.synchronize()
+    kp, vp = host_pools_after_append(case)
+    want = oracle.decode(W.to_float(case.q, case.dtype), case.q_pos, kp, vp, case.layout.table,
+                         case.seq_lens, case.scale, case.rope_theta, block_fill=case.block_fill)
+    for i, out in enumerate(outs):
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"side-stream call {i} differs"
+    assert_parity(W.to_float(outs[-1], case.dtype), want, case.dtype, "side-stream planned decode")
