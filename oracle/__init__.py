@@ -19,8 +19,8 @@ step by step, without blocking, fusion or reordering:
   "Lo que hace el decoding autorregresivo", "El remedio", "El precio".
 
 Modules: ``lazy_oracle`` (deferred-RoPE attention, append, cache bytes, the
-tile-by-tile softmax), ``alibi_oracle`` (the ALiBi variant), ``quant_oracle`` (a KV
-pool of 8-bit E4M3 floats with one scale per tensor) and ``cache_policy``
+tile-by-tile softmax), ``alibi_oracle`` (the ALiBi variant), ``quant_oracle`` (KV
+pools of 8-bit E4M3 floats or int8 integers, one scale per tensor) and ``cache_policy``
 (a plain model of the host pool manager's block and eviction policy).
 
 Every function is pinned by a ``-m "not gpu"`` test in ``tests/`` against
@@ -50,10 +50,17 @@ from .lazy_oracle import (  # noqa: F401
 from .alibi_oracle import alibi_slopes, decode_alibi, key_positions, prefill_alibi  # noqa: F401
 from .quant_oracle import (  # noqa: F401
     append_fp8,
+    append_int8,
     decode_fp8,
+    decode_int8,
     dequantize,
+    dequantize_int8,
     e4m3_decode,
     e4m3_quantize,
+    int8_decode,
+    int8_quantize,
     prefill_fp8,
+    prefill_int8,
     quantize_kv,
+    quantize_kv_int8,
 )

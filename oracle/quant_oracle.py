@@ -18,6 +18,13 @@ plainest one that the rest supports):
 
 Everything is float64 numpy apart from the one float32 division that decides
 the code (both sides take that decision in float32).
+
+The pages also count one byte per element for an int8 cache ([WHY] "El
+precio", s = 1) without a format.  Reading taken for it: symmetric signed
+8-bit integers with one scale per tensor; the code is the float32 quotient
+x / scale rounded to the nearest integer, ties to even, clamped to
+[-127, 127] (-128 is never written, so the range is symmetric; infinities
+clamp, NaN is stored as 0); the attended value is code * scale.
 """
 
 import numpy as np
@@ -95,3 +102,51 @@ def prefill_fp8(q, cu_q_lens, q_pos_start, k_codes, v_codes, block_table, kv_len
     """Deferred-RoPE prefill over the dequantised pools."""
     return _prefill(q, cu_q_lens, q_pos_start, dequantize(k_codes, k_scale), dequantize(v_codes, v_scale),
                     block_table, kv_lens, scale, theta, block_fill=block_fill)
+
+
+# ------------------------------------------------------------------ int8 pool
+INT8_MAX = 127
+
+
+def int8_quantize(x):
+    """Nearest integer of each value of x (float64 holding float32 values),
+    ties to even, clamped to [-127, 127]; NaN to 0.  Returns int8."""
+    x = np.asarray(x, dtype=np.float64)
+    r = np.rint(np.clip(np.where(np.isnan(x), 0.0, x), -INT8_MAX, INT8_MAX))
+    return r.astype(np.int8)
+
+
+def int8_decode(codes):
+    """Value of each int8 code as float64."""
+    return np.asarray(codes).view(np.int8).astype(np.float64)
+
+
+def quantize_kv_int8(x, scale):
+    """int8 codes of new K or V rows: the float32 quotient x / scale, quantised."""
+    q = np.asarray(x, dtype=np.float32) / np.float32(scale)
+    return int8_quantize(q.astype(np.float64))
+
+
+def dequantize_int8(codes, scale):
+    """Attended values of stored int8 codes: code * scale (float64)."""
+    return int8_decode(codes) * float(np.float32(scale))
+
+
+def append_int8(k_codes, v_codes, k_new, v_new, slot_mapping, k_scale, v_scale):
+    """Append on an int8 pool: quantise the new rows, then the plain append."""
+    return _append(k_codes, v_codes, quantize_kv_int8(k_new, k_scale), quantize_kv_int8(v_new, v_scale),
+                   slot_mapping)
+
+
+def decode_int8(q, q_pos, k_codes, v_codes, block_table, seq_lens, scale, theta, k_scale, v_scale,
+                block_fill=None):
+    """Deferred-RoPE decode over the dequantised int8 pools."""
+    return _decode(q, q_pos, dequantize_int8(k_codes, k_scale), dequantize_int8(v_codes, v_scale), block_table,
+                   seq_lens, scale, theta, block_fill=block_fill)
+
+
+def prefill_int8(q, cu_q_lens, q_pos_start, k_codes, v_codes, block_table, kv_lens, scale, theta, k_scale,
+                 v_scale, block_fill=None):
+    """Deferred-RoPE prefill over the dequantised int8 pools."""
+    return _prefill(q, cu_q_lens, q_pos_start, dequantize_int8(k_codes, k_scale),
+                    dequantize_int8(v_codes, v_scale), block_table, kv_lens, scale, theta, block_fill=block_fill)

@@ -827,6 +827,7 @@ constexpr int kMma16WorkgroupsPerCu = 2;
 // writes its own partial.
 constexpr int kPlanMembers = 4;
 constexpr int kPlanInts = 12;  // ints per plan item
+static_assert(kPlanInts == 12, "the kernel reads an item as three int4");
 
 template <int G, int MODE, bool PLAN>
 __device__ __forceinline__ void decode_mma16_body(const DecodeKernelArgs &a) {
@@ -877,8 +878,8 @@ __device__ __forceinline__ void decode_mma16_body(const DecodeKernelArgs &a) {
     // batch, the heads, a sequence's slot count or the table is skipped,
     // block ranges are clipped to member 0's length
     if ((int)blockIdx.x >= a.num_units) return;
-    const int4 r0 = a.plan_items[3 * blockIdx.x], r1 = a.plan_items[3 * blockIdx.x + 1];
-    const int4 r2 = a.plan_items[3 * blockIdx.x + 2];
+    const int4 *item = a.plan_items + (size_t)(kPlanInts / 4) * blockIdx.x;
+    const int4 r0 = item[0], r1 = item[1], r2 = item[2];
     g = r0.x & 0xffff;
     nmem = (int)((uint32_t)r0.x >> 16);
     blk0 = r0.y;
