@@ -243,20 +243,34 @@ def fp8_decode_algorithmic_bytes(case):
     return kv // 2, total - kv // 2
 
 
-def fp8_decode_shape(case, d, out, ws, timed):
-    """Time lazyattn_decode_fp8 on the case's layout with an 8-bit pool of
-    random E4M3 codes (k_scale 0.25, v_scale 0.125); the step's new rows are
-    quantised in by kvcache_append_fp8 first."""
-    import torch
+# 8-bit pools timed by --shapes: (code generator, k_scale, v_scale) per format
+POOL8_FORMATS = {"fp8": ("e4m3_codes_torch", 0.25, 0.125), "int8": ("int8_codes_torch", 0.01, 0.005)}
+
+
+def _pool8(case, d, fmt):
+    """Random 8-bit pools of the case's shape on the GPU, with the step's new
+    rows quantised in by the format's append; returns (k, v, k_scale, v_scale)."""
     import position_agnostic_kv_amd as pak
     import workloads as W
+    gen, ks, vs = POOL8_FORMATS[fmt]
     shape = tuple(d.k_pool.shape)
-    k8 = W.e4m3_codes_torch(shape, d.k_pool.device, case.seed + 5000)
-    v8 = W.e4m3_codes_torch(shape, d.k_pool.device, case.seed + 6000)
-    pak.kvcache_append_fp8(k8, v8, d.k_new, d.v_new, d.slots, 0.25, 0.125)
-    med, p10, p90 = timed(lambda: pak.lazyattn_decode_fp8(d.q, d.q_pos, k8, v8, d.table, d.seq_lens, 0.25, 0.125,
-                                                          scale=case.scale, rope_theta=case.rope_theta,
-                                                          out=out, workspace=ws))
+    k8 = getattr(W, gen)(shape, d.k_pool.device, case.seed + 5000)
+    v8 = getattr(W, gen)(shape, d.k_pool.device, case.seed + 6000)
+    getattr(pak, f"kvcache_append_{fmt}")(k8, v8, d.k_new, d.v_new, d.slots, ks, vs)
+    return k8, v8, ks, vs
+
+
+def fp8_decode_shape(case, d, out, ws, timed, fmt="fp8"):
+    """Time lazyattn_decode_fp8 (or _int8) on the case's layout with an 8-bit
+    pool of random codes (E4M3: k_scale 0.25, v_scale 0.125; int8: 0.01,
+    0.005); the step's new rows are quantised in by the format's append
+    first."""
+    import torch
+    import position_agnostic_kv_amd as pak
+    k8, v8, ks, vs = _pool8(case, d, fmt)
+    fn = getattr(pak, f"lazyattn_decode_{fmt}")
+    med, p10, p90 = timed(lambda: fn(d.q, d.q_pos, k8, v8, d.table, d.seq_lens, ks, vs, scale=case.scale,
+                                     rope_theta=case.rope_theta, out=out, workspace=ws))
     kv, alg = fp8_decode_algorithmic_bytes(case)
     del k8, v8
     torch.cuda.empty_cache()
@@ -266,22 +280,18 @@ def fp8_decode_shape(case, d, out, ws, timed):
             "tokens_per_s": round(float(case.layout.total_lens.sum()) / (med * 1e-3), 0)}
 
 
-def fp8_prefill_shape(case, d, out, timed):
-    """Time lazyattn_prefill_fp8 (widening pass and prefill) on the case's
-    layout with an 8-bit pool of random E4M3 codes (k_scale 0.25, v_scale
-    0.125); the prompts' rows are quantised in by kvcache_append_fp8 first."""
+def fp8_prefill_shape(case, d, out, timed, fmt="fp8"):
+    """Time lazyattn_prefill_fp8 (or _int8: widening pass and prefill) on the
+    case's layout with an 8-bit pool of random codes; the prompts' rows are
+    quantised in by the format's append first."""
     import torch
     import position_agnostic_kv_amd as pak
-    import workloads as W
-    shape = tuple(d.k_pool.shape)
-    k8 = W.e4m3_codes_torch(shape, d.k_pool.device, case.seed + 5000)
-    v8 = W.e4m3_codes_torch(shape, d.k_pool.device, case.seed + 6000)
-    pak.kvcache_append_fp8(k8, v8, d.k_new, d.v_new, d.slots, 0.25, 0.125)
+    k8, v8, ks, vs = _pool8(case, d, fmt)
     ws = torch.empty(pak.prefill_fp8_workspace_size(case.batch, d.table.shape[1], case.num_kv_heads),
                      dtype=torch.uint8, device=d.k_pool.device)
-    med, p10, p90 = timed(lambda: pak.lazyattn_prefill_fp8(d.q, d.cu, d.q_pos_start, k8, v8, d.table, d.seq_lens,
-                                                           case.max_q_len, 0.25, 0.125, scale=case.scale,
-                                                           rope_theta=case.rope_theta, out=out, workspace=ws))
+    fn = getattr(pak, f"lazyattn_prefill_{fmt}")
+    med, p10, p90 = timed(lambda: fn(d.q, d.cu, d.q_pos_start, k8, v8, d.table, d.seq_lens, case.max_q_len, ks,
+                                     vs, scale=case.scale, rope_theta=case.rope_theta, out=out, workspace=ws))
     del k8, v8, ws
     torch.cuda.empty_cache()
     fl = case.attention_flops()
@@ -357,6 +367,8 @@ def shapes_main(args):
             res[name + "_planned"] = planned_decode_shape(case, d, out, timed)
         if name in ("llama8b_decode", "llama70b_decode"):  # the same geometry over an 8-bit (E4M3) pool
             res[name + "_fp8"] = fp8_decode_shape(case, d, out, ws, timed)
+            if name == "llama8b_decode":  # and over an int8 pool
+                res[name + "_int8"] = fp8_decode_shape(case, d, out, ws, timed, "int8")
         if name == "llama8b_decode":  # the same inputs read with ALiBi biases instead of RoPE
             import oracle
             tab = torch.from_numpy(W.block_frame_table(case.layout).view(np.int32)).to(dev)
@@ -383,6 +395,7 @@ def shapes_main(args):
                               "attention_flops": fl, "tflops": round(fl / (med * 1e-3) / 1e12, 1),
                               "frac_of_bf16_peak": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
     res["llama8b_prefill_fp8"] = fp8_prefill_shape(case, d, out, timed)  # the same shape over an 8-bit pool
+    res["llama8b_prefill_int8"] = fp8_prefill_shape(case, d, out, timed, "int8")  # and over an int8 pool
     import oracle
     tab = torch.from_numpy(W.block_frame_table(case.layout).view(np.int32)).to(dev)
     sl = torch.from_numpy(oracle.alibi_slopes(case.num_q_heads).astype(np.float32)).to(dev)
@@ -427,10 +440,13 @@ SHAPES_DISPATCH_ORDER = {
     "lazyattn::decode_mma16_kernel<4, 2>": ["llama8b_decode_alibi"],
     "lazyattn::decode_mma16_kernel<8, 0>": ["llama70b_decode"],
     "lazyattn::decode_mma8_kernel<4, 0>": ["llama8b_decode_fp8"],
+    "lazyattn::decode_int8_kernel<4>": ["llama8b_decode_int8"],
     "lazyattn::decode_mma8_kernel<8, 0>": ["llama70b_decode_fp8"],
     # the 8-bit prefill: the widening pass, then the bf16 kernel on the widened copy
-    "lazyattn::prefill_kernel<128, 4, 0>": ["llama8b_prefill", "llama8b_prefill_fp8", "llama8b_prefill_ragged"],
+    "lazyattn::prefill_kernel<128, 4, 0>": ["llama8b_prefill", "llama8b_prefill_fp8", "llama8b_prefill_int8",
+                                            "llama8b_prefill_ragged"],
     "lazyattn::widen_fp8_kernel": ["llama8b_prefill_fp8_widen"],
+    "lazyattn::widen_int8_kernel": ["llama8b_prefill_int8_widen"],
     "lazyattn::prefill_kernel<128, 4, 2>": ["llama8b_prefill_alibi"],
 }
 PROFILE_STEMS = {
@@ -441,6 +457,8 @@ PROFILE_STEMS = {
     "llama70b_decode_fp8": "decode_llama70b_fp8", "llama8b_prefill": "prefill_llama8b",
     "llama8b_prefill_ragged": "prefill_llama8b_ragged", "llama8b_prefill_alibi": "prefill_llama8b_alibi",
     "llama8b_prefill_fp8": "prefill_llama8b_fp8", "llama8b_prefill_fp8_widen": "widen_llama8b_fp8",
+    "llama8b_decode_int8": "decode_llama8b_int8", "llama8b_prefill_int8": "prefill_llama8b_int8",
+    "llama8b_prefill_int8_widen": "widen_llama8b_int8",
     "decode_g4_equal_bytes": "decode_g4_equal_bytes",
     "decode_g32_equal_bytes": "decode_g32_equal_bytes", "decode_g64_equal_bytes": "decode_g64_equal_bytes",
 }
@@ -473,22 +491,23 @@ def planned_decode_shape(case, d, out, timed):
 def _profile_workload_bytes(name):
     """(description, algorithmic bytes of one launch) of a --shapes workload."""
     import workloads as W
-    if name == "llama8b_prefill_fp8_widen":
+    pool = "E4M3" if "_fp8" in name else "int8" if "_int8" in name else None
+    if name.endswith("_widen"):
         case = W.make("llama8b_prefill")
         slots = int(sum(-(-int(n) // W.BLOCK) for n in case.seq_lens)) * case.num_kv_heads
         total = slots * (2 * 2048 + 2 * 4096)
-        return (f"{name}: the {slots} visible (block, KV head) slots of llama8b_prefill over an E4M3 pool, "
+        return (f"{name}: the {slots} visible (block, KV head) slots of llama8b_prefill over an {pool} pool, "
                 f"widened once to bf16; algorithmic = 2 x 2 KiB of codes read + 2 x 4 KiB bf16 written per "
                 f"slot"), total
-    base = name.replace("_fp8", "").replace("_alibi", "").replace("_planned", "")
+    base = name.replace("_fp8", "").replace("_int8", "").replace("_alibi", "").replace("_planned", "")
     case = W.make(base)
     if case.kind == "decode":
         kv, total = decode_algorithmic_bytes(case)
-        if name.endswith("_fp8"):
+        if pool:
             kv, total = fp8_decode_algorithmic_bytes(case)
         desc = (f"{name}: {case.batch} seqs, {int(case.layout.total_lens.sum())} tokens attended, "
                 f"{case.num_q_heads} q / {case.num_kv_heads} KV heads, d_h {case.head_dim}, "
-                f"{'E4M3 pool, bf16 q' if name.endswith('_fp8') else 'bf16'}; algorithmic = K+V once + q, out, "
+                f"{pool + ' pool, bf16 q' if pool else 'bf16'}; algorithmic = K+V once + q, out, "
                 f"table words")
         return desc, total
     toks = int(case.layout.total_lens.sum())
@@ -496,7 +515,7 @@ def _profile_workload_bytes(name):
     total = toks * case.num_kv_heads * case.head_dim * 2 * 2 + 2 * rows * case.num_q_heads * case.head_dim * 2
     desc = (f"{name}: {case.batch} seqs, {toks} K/V tokens ({rows} prompt rows), {case.num_q_heads} q / "
             f"{case.num_kv_heads} KV heads, d_h {case.head_dim}, "
-            f"{'bf16 copy widened from an E4M3 pool' if name.endswith('_fp8') else 'bf16'}; "
+            f"{'bf16 copy widened from an ' + pool + ' pool' if pool else 'bf16'}; "
             f"algorithmic = K+V once + q + out")
     return desc, total
 
@@ -675,7 +694,7 @@ def activity_summary_main(args):
             alg = None
             if "prefill" in kernel:
                 import workloads as W
-                alg = W.make(name.replace("_alibi", "").replace("_fp8", "")).attention_flops()
+                alg = W.make(name.replace("_alibi", "").replace("_fp8", "").replace("_int8", "")).attention_flops()
             lds = mean("SQ_LDS_IDX_ACTIVE")
             lines.append(
                 f"{kernel.replace('lazyattn::', '')} | {name} | {t * 1e6:.1f} | {cyc / t / 1e9:.3f} | "

@@ -383,6 +383,41 @@ int lazyattn_prefill_fp8(void *out, const void *q, int total_q, const int32_t *c
                          int head_dim, int num_blocks, float scale, float rope_theta, float k_scale,
                          float v_scale, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * int8 KV pools: the same one-byte cache (lynx-cortex "00 — Por qué existe un
+ * KV Cache", "El precio": s = 1 for int8) with symmetric signed integer codes
+ * and one float scale per tensor: the value a code stands for is
+ * code * scale.  Same record layout and lane order as the 8-bit E4M3 pools
+ * above, head_dim 128.
+ *
+ * kvcache_append_int8 -- each element is stored as the integer nearest to the
+ * float32 quotient x / scale (correctly rounded division), ties to even,
+ * clamped to [-127, 127] (-128 is never written; infinities clamp), NaN as 0.
+ * Arguments and errors as kvcache_append_fp8.
+ *
+ * lazyattn_decode_int8, lazyattn_prefill_int8 -- lazyattn_decode_fp8 and
+ * lazyattn_prefill_fp8 over int8 pools: keys are code * k_scale, values
+ * code * v_scale (a code of -128, which the append never writes, reads as
+ * -128).  The widening for the prefill is exact; its workspace is
+ * lazyattn_prefill_fp8_workspace_size bytes.  Arguments, workspaces and errors
+ * as the E4M3 calls.
+ */
+int kvcache_append_int8(void *k_pool, void *v_pool, int dtype, int num_blocks, int num_kv_heads,
+                        int head_dim, const void *k_new, const void *v_new, const int32_t *slot_mapping,
+                        int num_tokens, float k_scale, float v_scale, void *stream);
+int lazyattn_decode_int8(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                         const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                         const uint8_t *block_fill, const int32_t *seq_lens, int batch, int num_q_heads,
+                         int num_kv_heads, int head_dim, int num_blocks, float scale, float rope_theta,
+                         float k_scale, float v_scale, int split_blocks, void *workspace,
+                         size_t workspace_bytes, void *stream);
+int lazyattn_prefill_int8(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                          const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                          const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
+                          const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads, int num_kv_heads,
+                          int head_dim, int num_blocks, float scale, float rope_theta, float k_scale,
+                          float v_scale, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,7 @@ __all__ = [
     "decode_workspace_size", "lazyattn_decode", "lazyattn_prefill", "lazyattn_decode_eager",
     "lazyattn_prefill_eager", "lazyattn_decode_alibi", "lazyattn_prefill_alibi", "kvcache_append_fp8",
     "lazyattn_decode_fp8", "lazyattn_prefill_fp8", "prefill_fp8_workspace_size", "lazyattn_decode_noalloc",
+    "kvcache_append_int8", "lazyattn_decode_int8", "lazyattn_prefill_int8",
     "DecodePlan", "decode_plan", "decode_planned_workspace_size", "lazyattn_decode_planned", "BLOCK_TOKENS",
 ]
 
@@ -64,6 +65,9 @@ _SIGNATURES["lazyattn_decode_fp8"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32,
 _SIGNATURES["lazyattn_prefill_fp8"] = (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
                                               _i32, _i32, _i32, _i32, _f32, _f32, _f32, _f32, _vp, _sz, _vp])
 _SIGNATURES["lazyattn_prefill_fp8_workspace_size"] = (_sz, [_i32, _i32, _i32, _i32])
+_SIGNATURES["kvcache_append_int8"] = _SIGNATURES["kvcache_append_fp8"]
+_SIGNATURES["lazyattn_decode_int8"] = _SIGNATURES["lazyattn_decode_fp8"]
+_SIGNATURES["lazyattn_prefill_int8"] = _SIGNATURES["lazyattn_prefill_fp8"]
 _SIGNATURES["lazyattn_decode_plan_ints"] = (_sz, [_i32, _i32, _i32])
 _SIGNATURES["lazyattn_decode_plan"] = (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _vp])
 _SIGNATURES["lazyattn_decode_planned_workspace_size"] = (_sz, [_i32, _i32, _i32, _i32, _i32])
@@ -175,29 +179,43 @@ def kvcache_append(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
                               _stream_ptr(stream, dev)), "kvcache_append")
 
 
-_POOL8 = (torch.uint8, torch.float8_e4m3fn)
+_POOL8 = (torch.uint8, torch.float8_e4m3fn)   # E4M3 code pools
+_POOL_INT8 = (torch.int8, torch.uint8)         # int8 code pools (uint8: the same bytes)
 
 
 def kvcache_append_fp8(k_pool, v_pool, k_new, v_new, slot_mapping, k_scale, v_scale, stream=None):
     """Quantise rows k_new/v_new [T, Hkv, D] (bf16 or f32) into an 8-bit pool
     (uint8 or float8_e4m3fn [NB, Hkv, 16, D] of E4M3 codes): code = nearest E4M3
     of the float32 x / scale, saturating at 448.  Slots < 0 are skipped."""
+    return _append8("kvcache_append_fp8", _POOL8, k_pool, v_pool, k_new, v_new, slot_mapping, k_scale, v_scale,
+                    stream)
+
+
+def kvcache_append_int8(k_pool, v_pool, k_new, v_new, slot_mapping, k_scale, v_scale, stream=None):
+    """Quantise rows k_new/v_new [T, Hkv, D] (bf16 or f32) into an int8 pool
+    (int8 or uint8 [NB, Hkv, 16, D]): code = the float32 x / scale rounded to
+    the nearest integer (ties to even), clamped to +-127, NaN as 0.  Slots < 0
+    are skipped."""
+    return _append8("kvcache_append_int8", _POOL_INT8, k_pool, v_pool, k_new, v_new, slot_mapping, k_scale,
+                    v_scale, stream)
+
+
+def _append8(fn, pool_types, k_pool, v_pool, k_new, v_new, slot_mapping, k_scale, v_scale, stream):
     dev = _dev(k_pool, v_pool, k_new, v_new, slot_mapping)
     _int32(slot_mapping, "slot_mapping")
     nb, hkv, bt, d = k_pool.shape
     if bt != BLOCK_TOKENS or v_pool.shape != k_pool.shape:
         raise LazyAttnError("pools must be [num_blocks, num_kv_heads, 16, head_dim]")
-    if k_pool.dtype not in _POOL8 or v_pool.dtype != k_pool.dtype:
-        raise LazyAttnError("8-bit pools must be uint8 or float8_e4m3fn")
+    if k_pool.dtype not in pool_types or v_pool.dtype != k_pool.dtype:
+        raise LazyAttnError(f"{fn}: pools must be one of {pool_types}")
     if k_new.shape != v_new.shape or k_new.shape[1:] != (hkv, d) or k_new.dtype != v_new.dtype:
         raise LazyAttnError("k_new/v_new must be [T, num_kv_heads, head_dim] of one dtype")
     if slot_mapping.numel() != k_new.shape[0]:
         raise LazyAttnError("slot_mapping must have one entry per new row")
     lib = load_library()
-    _check(lib.kvcache_append_fp8(_ptr(k_pool), _ptr(v_pool), _dtype_code(k_new), nb, hkv, d,
-                                  _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), k_new.shape[0],
-                                  float(k_scale), float(v_scale), _stream_ptr(stream, dev)),
-           "kvcache_append_fp8")
+    _check(getattr(lib, fn)(_ptr(k_pool), _ptr(v_pool), _dtype_code(k_new), nb, hkv, d,
+                            _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), k_new.shape[0],
+                            float(k_scale), float(v_scale), _stream_ptr(stream, dev)), fn)
 
 
 def lazyattn_decode_fp8(q, q_pos, k_pool, v_pool, block_table, seq_lens, k_scale, v_scale, *, scale=None,
@@ -208,7 +226,17 @@ def lazyattn_decode_fp8(q, q_pos, k_pool, v_pool, block_table, seq_lens, k_scale
     v_scale.  q and out are bf16; head_dim 128."""
     return _decode("lazyattn_decode_fp8", q, q_pos, k_pool, v_pool, block_table, seq_lens, scale,
                    rope_theta, split_blocks, out, workspace, stream, block_fill=block_fill,
-                   kv_scales=(float(k_scale), float(v_scale)))
+                   kv_scales=(float(k_scale), float(v_scale)), pool_types=_POOL8)
+
+
+def lazyattn_decode_int8(q, q_pos, k_pool, v_pool, block_table, seq_lens, k_scale, v_scale, *, scale=None,
+                         rope_theta=10000.0, split_blocks=0, out=None, workspace=None, stream=None,
+                         block_fill=None):
+    """lazyattn_decode over an int8 pool (int8 or uint8): keys are code *
+    k_scale, values code * v_scale.  q and out are bf16; head_dim 128."""
+    return _decode("lazyattn_decode_int8", q, q_pos, k_pool, v_pool, block_table, seq_lens, scale,
+                   rope_theta, split_blocks, out, workspace, stream, block_fill=block_fill,
+                   kv_scales=(float(k_scale), float(v_scale)), pool_types=_POOL_INT8)
 
 
 def decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
@@ -394,7 +422,7 @@ def _fill_arg(block_fill, num_blocks, dev):
 
 
 def _decode(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, rope_theta, split_blocks,
-            out, workspace, stream, slopes=None, block_fill=None, kv_scales=None):
+            out, workspace, stream, slopes=None, block_fill=None, kv_scales=None, pool_types=_POOL8):
     dev = _dev(q, q_pos, k_pool, v_pool, block_table, seq_lens)
     _int32(q_pos, "q_pos")
     _int32(block_table, "block_table")
@@ -404,8 +432,8 @@ def _decode(fn, q, q_pos, k_pool, v_pool, block_table, seq_lens, scale, rope_the
     if bt != BLOCK_TOKENS or dk != d or v_pool.shape != k_pool.shape:
         raise LazyAttnError("pools must be [num_blocks, num_kv_heads, 16, head_dim]")
     if kv_scales is not None:
-        if q.dtype != torch.bfloat16 or k_pool.dtype not in _POOL8 or v_pool.dtype != k_pool.dtype:
-            raise LazyAttnError("8-bit pools (uint8 or float8_e4m3fn) take bf16 queries")
+        if q.dtype != torch.bfloat16 or k_pool.dtype not in pool_types or v_pool.dtype != k_pool.dtype:
+            raise LazyAttnError(f"{fn}: pools must be one of {pool_types}, queries bf16")
     elif q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
         raise LazyAttnError("q and pools must share a dtype")
     if block_table.dim() != 2 or block_table.shape[0] != b or q_pos.numel() != b or seq_lens.numel() != b:
@@ -500,11 +528,23 @@ def lazyattn_prefill_fp8(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
     (prefill_fp8_workspace_size); allocated here when not given."""
     return _prefill("lazyattn_prefill_fp8", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
                     kv_lens, max_q_len, scale, rope_theta, out, stream, block_fill=block_fill,
-                    kv_scales=(float(k_scale), float(v_scale)), workspace=workspace)
+                    kv_scales=(float(k_scale), float(v_scale)), workspace=workspace, pool_types=_POOL8)
+
+
+def lazyattn_prefill_int8(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len,
+                          k_scale, v_scale, *, scale=None, rope_theta=10000.0, out=None, workspace=None,
+                          stream=None, block_fill=None):
+    """lazyattn_prefill over an int8 pool (int8 or uint8) written by
+    kvcache_append_int8: keys are code * k_scale, values code * v_scale.
+    workspace as lazyattn_prefill_fp8 (prefill_fp8_workspace_size bytes)."""
+    return _prefill("lazyattn_prefill_int8", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                    kv_lens, max_q_len, scale, rope_theta, out, stream, block_fill=block_fill,
+                    kv_scales=(float(k_scale), float(v_scale)), workspace=workspace, pool_types=_POOL_INT8)
 
 
 def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len, scale,
-             rope_theta, out, stream, slopes=None, block_fill=None, kv_scales=None, workspace=None):
+             rope_theta, out, stream, slopes=None, block_fill=None, kv_scales=None, workspace=None,
+             pool_types=_POOL8):
     dev = _dev(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens)
     for t, n in ((cu_q_lens, "cu_q_lens"), (q_pos_start, "q_pos_start"), (kv_lens, "kv_lens"),
                  (block_table, "block_table")):
@@ -515,8 +555,8 @@ def _prefill(fn, q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens
     if bt != BLOCK_TOKENS or dk != d or v_pool.shape != k_pool.shape:
         raise LazyAttnError("pools must be [num_blocks, num_kv_heads, 16, head_dim]")
     if kv_scales is not None:
-        if q.dtype != torch.bfloat16 or k_pool.dtype not in _POOL8 or v_pool.dtype != k_pool.dtype:
-            raise LazyAttnError("8-bit pools (uint8 or float8_e4m3fn) take bf16 queries")
+        if q.dtype != torch.bfloat16 or k_pool.dtype not in pool_types or v_pool.dtype != k_pool.dtype:
+            raise LazyAttnError(f"{fn}: pools must be one of {pool_types}, queries bf16")
     elif q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
         raise LazyAttnError("q and pools must share a dtype")
     if cu_q_lens.numel() != b + 1 or q_pos_start.numel() != b or block_table.dim() != 2 \

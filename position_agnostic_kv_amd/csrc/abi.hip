@@ -79,9 +79,9 @@ int kvcache_append(void *k_pool, void *v_pool, int dtype, int num_blocks, int nu
                                 (hipStream_t)stream));
 }
 
-int kvcache_append_fp8(void *k_pool, void *v_pool, int dtype, int num_blocks, int num_kv_heads,
-                       int head_dim, const void *k_new, const void *v_new, const int32_t *slot_mapping,
-                       int num_tokens, float k_scale, float v_scale, void *stream) {
+static int append8_common(void *k_pool, void *v_pool, int dtype, int num_blocks, int num_kv_heads,
+                          int head_dim, const void *k_new, const void *v_new, const int32_t *slot_mapping,
+                          int num_tokens, float k_scale, float v_scale, void *stream, bool int8) {
   if (!valid_dtype(dtype)) return LAZYATTN_ERR_DTYPE;
   if (num_tokens < 0 || num_blocks < 1 || num_blocks > LAZYATTN_MAX_BLOCKS || num_kv_heads < 1 ||
       num_kv_heads > 1024)
@@ -92,7 +92,21 @@ int kvcache_append_fp8(void *k_pool, void *v_pool, int dtype, int num_blocks, in
   if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return LAZYATTN_ERR_NULL;
   return from_hip(launch_append_fp8(k_pool, v_pool, dtype == LAZYATTN_BF16, num_blocks, num_kv_heads,
                                     head_dim, k_new, v_new, slot_mapping, num_tokens, k_scale, v_scale,
-                                    (hipStream_t)stream));
+                                    (hipStream_t)stream, int8));
+}
+
+int kvcache_append_fp8(void *k_pool, void *v_pool, int dtype, int num_blocks, int num_kv_heads,
+                       int head_dim, const void *k_new, const void *v_new, const int32_t *slot_mapping,
+                       int num_tokens, float k_scale, float v_scale, void *stream) {
+  return append8_common(k_pool, v_pool, dtype, num_blocks, num_kv_heads, head_dim, k_new, v_new, slot_mapping,
+                        num_tokens, k_scale, v_scale, stream, false);
+}
+
+int kvcache_append_int8(void *k_pool, void *v_pool, int dtype, int num_blocks, int num_kv_heads,
+                        int head_dim, const void *k_new, const void *v_new, const int32_t *slot_mapping,
+                        int num_tokens, float k_scale, float v_scale, void *stream) {
+  return append8_common(k_pool, v_pool, dtype, num_blocks, num_kv_heads, head_dim, k_new, v_new, slot_mapping,
+                        num_tokens, k_scale, v_scale, stream, true);
 }
 
 size_t lazyattn_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
@@ -111,7 +125,7 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
                          int split_blocks, void *workspace, size_t workspace_bytes, void *stream,
                          int mode, const float *slopes, bool pool8 = false, float k_scale = 1.f,
                          float v_scale = 1.f, const int32_t *plan = nullptr, int plan_items = 0,
-                         int plan_max_items = 0) {
+                         int plan_max_items = 0, bool int8 = false) {
   if (!valid_dtype(dtype)) return LAZYATTN_ERR_DTYPE;
   if (batch < 0 || batch > 65535 || num_kv_heads < 1 || num_kv_heads > 65535 || num_q_heads < 1 ||
       num_q_heads % num_kv_heads || !pow2_group(num_q_heads / num_kv_heads))
@@ -164,6 +178,7 @@ static int decode_common(void *out, const void *q, const int32_t *q_pos, const v
   a.plan = plan;
   a.plan_items = plan_items;
   a.plan_max_items = plan_max_items;
+  a.int8 = int8;
   if (pool8) return from_hip(launch_decode_fp8(a, (hipStream_t)stream));
   if (plan) return from_hip(launch_decode_planned(a, (hipStream_t)stream));
   return from_hip(launch_decode(a, bf16, (hipStream_t)stream));
@@ -201,6 +216,18 @@ int lazyattn_decode_fp8(void *out, const void *q, const int32_t *q_pos, const vo
                        batch, num_q_heads, num_kv_heads, head_dim, num_blocks, LAZYATTN_BF16, scale,
                        rope_theta, split_blocks, workspace, workspace_bytes, stream, kRopeLazy, nullptr,
                        true, k_scale, v_scale);
+}
+
+int lazyattn_decode_int8(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
+                         const void *v_pool, const uint32_t *block_table, int max_blocks_per_seq,
+                         const uint8_t *block_fill, const int32_t *seq_lens, int batch, int num_q_heads,
+                         int num_kv_heads, int head_dim, int num_blocks, float scale, float rope_theta,
+                         float k_scale, float v_scale, int split_blocks, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  return decode_common(out, q, q_pos, k_pool, v_pool, block_table, max_blocks_per_seq, block_fill, seq_lens,
+                       batch, num_q_heads, num_kv_heads, head_dim, num_blocks, LAZYATTN_BF16, scale,
+                       rope_theta, split_blocks, workspace, workspace_bytes, stream, kRopeLazy, nullptr,
+                       true, k_scale, v_scale, nullptr, 0, 0, true);
 }
 
 int lazyattn_decode(void *out, const void *q, const int32_t *q_pos, const void *k_pool,
@@ -269,7 +296,8 @@ static int prefill_common(void *out, const void *q, int total_q, const int32_t *
                           int batch, int max_q_len, int num_q_heads, int num_kv_heads, int head_dim,
                           int num_blocks, int dtype, float scale, float rope_theta, void *stream,
                           int mode, const float *slopes, bool pool8 = false, float k_scale = 1.f,
-                          float v_scale = 1.f, void *workspace = nullptr, size_t workspace_bytes = 0) {
+                          float v_scale = 1.f, void *workspace = nullptr, size_t workspace_bytes = 0,
+                          bool int8 = false) {
   if (dtype != LAZYATTN_BF16) return LAZYATTN_ERR_DTYPE;
   if (pool8 && (head_dim != 128 || !valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
     return LAZYATTN_ERR_SHAPE;
@@ -312,6 +340,7 @@ static int prefill_common(void *out, const void *q, int total_q, const int32_t *
   a.block_fill = block_fill;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.int8 = int8;
   if (pool8) return from_hip(launch_prefill_fp8(a, workspace, (hipStream_t)stream));
   return from_hip(launch_prefill(a, (hipStream_t)stream));
 }
@@ -358,6 +387,18 @@ int lazyattn_prefill_fp8(void *out, const void *q, int total_q, const int32_t *c
                         max_blocks_per_seq, block_fill, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
                         head_dim, num_blocks, LAZYATTN_BF16, scale, rope_theta, stream, kRopeLazy, nullptr,
                         true, k_scale, v_scale, workspace, workspace_bytes);
+}
+
+int lazyattn_prefill_int8(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                          const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                          const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
+                          const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads, int num_kv_heads,
+                          int head_dim, int num_blocks, float scale, float rope_theta, float k_scale,
+                          float v_scale, void *workspace, size_t workspace_bytes, void *stream) {
+  return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                        max_blocks_per_seq, block_fill, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
+                        head_dim, num_blocks, LAZYATTN_BF16, scale, rope_theta, stream, kRopeLazy, nullptr,
+                        true, k_scale, v_scale, workspace, workspace_bytes, true);
 }
 
 size_t lazyattn_prefill_fp8_workspace_size(int batch, int max_blocks_per_seq, int num_kv_heads, int head_dim) {

@@ -66,6 +66,21 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | code;
 }
 
+// An int8 pool (symmetric codes, one scale per tensor): the stored code is
+// the float32 quotient x / scale rounded to the nearest integer (ties to
+// even), clamped to [-127, 127], NaN stored as 0.
+__device__ __forceinline__ uint32_t f32_to_i8(float x) {
+  if (!(x == x)) return 0u;
+  const float r = __builtin_rintf(fminf(fmaxf(x, -127.f), 127.f));
+  return (uint32_t)(uint8_t)(int8_t)(int)r;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t f32_to_code8(float x) {
+  if constexpr (FMT == kCodeInt8) return f32_to_i8(x);
+  else return f32_to_e4m3(x);
+}
+
 __device__ __forceinline__ void load8(const uint16_t *p, float (&x)[8]) {
   const uint4 c = *(const uint4 *)p;
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
@@ -80,10 +95,11 @@ __device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
+template <int FMT>
 __device__ __forceinline__ uint2 quant8(const float (&x)[8], float scale) {
   uint32_t w[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) w[i >> 2] |= f32_to_e4m3(__fdiv_rn(x[i], scale)) << (8 * (i & 3));
+  for (int i = 0; i < 8; ++i) w[i >> 2] |= f32_to_code8<FMT>(__fdiv_rn(x[i], scale)) << (8 * (i & 3));
   return make_uint2(w[0], w[1]);
 }
 
@@ -93,11 +109,12 @@ __device__ __forceinline__ uint2 quant8(const float (&x)[8], float scale) {
 // x < 16) holds K[token t][dim 32 g + 16 i + x] and
 // V[token 4 g + x % 4][dim 16 (4 i + x / 4) + t].  The K codes of 8 dims are 8
 // adjacent bytes; the V codes of 8 dims go to 8 lanes' bytes.
-template <typename TI>
-__global__ void __launch_bounds__(256)
-append_fp8_kernel(uint8_t *__restrict__ k_pool, uint8_t *__restrict__ v_pool, const TI *__restrict__ k_new,
-                  const TI *__restrict__ v_new, const int32_t *__restrict__ slot_mapping, int num_tokens,
-                  int num_kv_heads, long long num_slots, float k_scale, float v_scale) {
+template <int FMT, typename TI>
+__device__ __forceinline__ void append8_body(uint8_t *__restrict__ k_pool, uint8_t *__restrict__ v_pool,
+                                             const TI *__restrict__ k_new, const TI *__restrict__ v_new,
+                                             const int32_t *__restrict__ slot_mapping, int num_tokens,
+                                             int num_kv_heads, long long num_slots, float k_scale,
+                                             float v_scale) {
   constexpr int kGroups = 16;  // 128 dims / 8
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)num_tokens * num_kv_heads * kGroups;
@@ -115,32 +132,61 @@ append_fp8_kernel(uint8_t *__restrict__ k_pool, uint8_t *__restrict__ v_pool, co
   const int d0 = grp * 8;
   float x[8];
   load8(k_new + idx * 8, x);
-  *(uint2 *)(kb + ((d0 >> 4) & 1) * 1024 + (16 * (d0 >> 5) + t) * 16 + (d0 & 15)) = quant8(x, k_scale);
+  *(uint2 *)(kb + ((d0 >> 4) & 1) * 1024 + (16 * (d0 >> 5) + t) * 16 + (d0 & 15)) = quant8<FMT>(x, k_scale);
   load8(v_new + idx * 8, x);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int d = d0 + e, c = d >> 4;
     vb[(c >> 2) * 1024 + (16 * (t >> 2) + (d & 15)) * 16 + (c & 3) * 4 + (t & 3)] =
-        (uint8_t)f32_to_e4m3(__fdiv_rn(x[e], v_scale));
+        (uint8_t)f32_to_code8<FMT>(__fdiv_rn(x[e], v_scale));
   }
+}
+
+template <typename TI>
+__global__ void __launch_bounds__(256)
+append_fp8_kernel(uint8_t *__restrict__ k_pool, uint8_t *__restrict__ v_pool, const TI *__restrict__ k_new,
+                  const TI *__restrict__ v_new, const int32_t *__restrict__ slot_mapping, int num_tokens,
+                  int num_kv_heads, long long num_slots, float k_scale, float v_scale) {
+  append8_body<kCodeE4M3>(k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens, num_kv_heads, num_slots,
+                          k_scale, v_scale);
+}
+
+// the same for an int8 pool (same lane-order layout)
+template <typename TI>
+__global__ void __launch_bounds__(256)
+append_int8_kernel(uint8_t *__restrict__ k_pool, uint8_t *__restrict__ v_pool, const TI *__restrict__ k_new,
+                   const TI *__restrict__ v_new, const int32_t *__restrict__ slot_mapping, int num_tokens,
+                   int num_kv_heads, long long num_slots, float k_scale, float v_scale) {
+  append8_body<kCodeInt8>(k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens, num_kv_heads, num_slots,
+                          k_scale, v_scale);
 }
 
 hipError_t launch_append_fp8(void *k_pool, void *v_pool, bool bf16_rows, int num_blocks,
                              int num_kv_heads, int head_dim, const void *k_new, const void *v_new,
                              const int32_t *slot_mapping, int num_tokens, float k_scale, float v_scale,
-                             hipStream_t stream) {
+                             hipStream_t stream, bool int8) {
   if (head_dim != 128) return hipErrorInvalidValue;  // the lane-order layout is defined for 128 dims
   const long long total = (long long)num_tokens * num_kv_heads * 16;
   const unsigned grid = (unsigned)((total + 255) / 256);
   const long long slots = (long long)num_blocks * kBlockTokens;
-  if (bf16_rows)
-    hipLaunchKernelGGL(append_fp8_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, (uint8_t *)k_pool,
-                       (uint8_t *)v_pool, (const uint16_t *)k_new, (const uint16_t *)v_new, slot_mapping,
-                       num_tokens, num_kv_heads, slots, k_scale, v_scale);
-  else
-    hipLaunchKernelGGL(append_fp8_kernel<float>, dim3(grid), dim3(256), 0, stream, (uint8_t *)k_pool,
-                       (uint8_t *)v_pool, (const float *)k_new, (const float *)v_new, slot_mapping,
-                       num_tokens, num_kv_heads, slots, k_scale, v_scale);
+  uint8_t *kp = (uint8_t *)k_pool, *vp = (uint8_t *)v_pool;
+  if (bf16_rows) {
+    const uint16_t *kn = (const uint16_t *)k_new, *vn = (const uint16_t *)v_new;
+    if (int8)
+      hipLaunchKernelGGL(append_int8_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, kp, vp, kn, vn,
+                         slot_mapping, num_tokens, num_kv_heads, slots, k_scale, v_scale);
+    else
+      hipLaunchKernelGGL(append_fp8_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream, kp, vp, kn, vn,
+                         slot_mapping, num_tokens, num_kv_heads, slots, k_scale, v_scale);
+  } else {
+    const float *kn = (const float *)k_new, *vn = (const float *)v_new;
+    if (int8)
+      hipLaunchKernelGGL(append_int8_kernel<float>, dim3(grid), dim3(256), 0, stream, kp, vp, kn, vn,
+                         slot_mapping, num_tokens, num_kv_heads, slots, k_scale, v_scale);
+    else
+      hipLaunchKernelGGL(append_fp8_kernel<float>, dim3(grid), dim3(256), 0, stream, kp, vp, kn, vn,
+                         slot_mapping, num_tokens, num_kv_heads, slots, k_scale, v_scale);
+  }
   return hipGetLastError();
 }
 

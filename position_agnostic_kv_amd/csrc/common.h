@@ -74,6 +74,23 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
+// Two signed 8-bit integer codes (bytes 0-1, or 2-3 with HI) of a word -> a
+// packed bf16 pair, byte 2 HI in the low half: exact (every integer of
+// magnitude <= 256 is a bf16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w) {
+  const int sh = HI ? 16 : 0;
+  return pack_bf16x2((float)(int)(int8_t)(w >> sh), (float)(int)(int8_t)(w >> (sh + 8)));
+}
+
+// 8-bit pool code formats
+enum Code8 { kCodeE4M3 = 0, kCodeInt8 = 1 };
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t code8x2_to_bf16x2(uint32_t w) {
+  if constexpr (FMT == kCodeInt8) return i8x2_to_bf16x2<HI>(w);
+  else return e4m3x2_to_bf16x2<HI>(w);
+}
+
 // Dword w (a compile-time constant after unrolling) of a 16-byte chunk.
 __device__ __forceinline__ uint32_t dw4(const uint4 &v, int w) {
   return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;

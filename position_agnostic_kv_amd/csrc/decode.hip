@@ -536,9 +536,8 @@ decode_split_kernel(const DecodeKernelArgs a) {
 //     swaps per block), since P.V sums their tokens in one accumulator.
 constexpr int kMma8WorkgroupsPerCu = 2;  // occupancy the register allocation is held to
 
-template <int G, int MODE>
-__global__ void __launch_bounds__(kDecodeWaves * kWave, kMma8WorkgroupsPerCu)
-decode_mma8_kernel(const DecodeKernelArgs a) {
+template <int G, int MODE, int FMT>
+__device__ __forceinline__ void decode_mma8_body(const DecodeKernelArgs &a) {
   using E = Elem<bf16>;
   constexpr int D = 128;
   constexpr int NT = kDecodeWaves * kWave;
@@ -684,8 +683,8 @@ decode_mma8_kernel(const DecodeKernelArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t w0 = dw4(kc[c >> 1], 2 * (c & 1)), w1 = dw4(kc[c >> 1], 2 * (c & 1) + 1);
-      const uint4 ka = make_uint4(e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
-                                  e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1));
+      const uint4 ka = make_uint4(code8x2_to_bf16x2<FMT, false>(w0), code8x2_to_bf16x2<FMT, true>(w0),
+                                  code8x2_to_bf16x2<FMT, false>(w1), code8x2_to_bf16x2<FMT, true>(w1));
       S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qh[c], S, 0, 0, 0);
       Sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), ql[c], Sl, 0, 0, 0);
     }
@@ -731,7 +730,7 @@ decode_mma8_kernel(const DecodeKernelArgs a) {
     for (int c = 0; c < 8; ++c) {
       const uint32_t vw = dw4(vc[c >> 2], c & 3);
       const s16x4_t vb =
-          __builtin_bit_cast(s16x4_t, make_uint2(e4m3x2_to_bf16x2<false>(vw), e4m3x2_to_bf16x2<true>(vw)));
+          __builtin_bit_cast(s16x4_t, make_uint2(code8x2_to_bf16x2<FMT, false>(vw), code8x2_to_bf16x2<FMT, true>(vw)));
       O[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[c], 0, 0, 0);
     }
     blk += kDecodeWaves;
@@ -789,6 +788,19 @@ decode_mma8_kernel(const DecodeKernelArgs a) {
       if (d == 0) a.ws_ml[part * G + h] = make_float2(mx, ls);
     }
   }
+}
+
+template <int G, int MODE>
+__global__ void __launch_bounds__(kDecodeWaves * kWave, kMma8WorkgroupsPerCu)
+decode_mma8_kernel(const DecodeKernelArgs a) {
+  decode_mma8_body<G, MODE, kCodeE4M3>(a);
+}
+
+// the same over an int8 pool (same lane-order layout; codes widened exactly)
+template <int G>
+__global__ void __launch_bounds__(kDecodeWaves * kWave, kMma8WorkgroupsPerCu)
+decode_int8_kernel(const DecodeKernelArgs a) {
+  decode_mma8_body<G, kRopeLazy, kCodeInt8>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -1720,7 +1732,7 @@ size_t decode_plan_items_offset(int batch) { return ((size_t)batch + 3) / 4 * 4;
 
 // IMPL: kValu (decode_split_kernel), kMma8 (8-bit pools), kMma16 (bf16 pools,
 // matrix cores, up to 16 heads), kMma16Wide (bf16 pools, 32 or 64 heads)
-enum DecodeImplKernel { kValu = 0, kMma8 = 1, kMma16 = 2, kMma16Wide = 3 };
+enum DecodeImplKernel { kValu = 0, kMma8 = 1, kMma16 = 2, kMma16Wide = 3, kMma8Int8 = 4 };
 
 template <typename T, int D, int G, int MODE, bool F8 = false, int IMPL = kValu>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
@@ -1761,6 +1773,8 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   if constexpr (IMPL == kMma8)
     hipLaunchKernelGGL((decode_mma8_kernel<G, MODE>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave), 0, stream,
                        k);
+  else if constexpr (IMPL == kMma8Int8)
+    hipLaunchKernelGGL((decode_int8_kernel<G>), dim3((unsigned)grid), dim3(kDecodeWaves * kWave), 0, stream, k);
   else if constexpr (IMPL == kMma16Wide)
     hipLaunchKernelGGL((decode_mma16_wide_kernel<G / 16, MODE>), dim3((unsigned)grid),
                        dim3(wide_waves(G / 16) * kWave), 0, stream, k);
@@ -1875,6 +1889,16 @@ static hipError_t dispatch_group(const DecodeArgs &a, hipStream_t s) {
 // matrix cores (the pool in the lane order decode_mma8_kernel reads).
 hipError_t launch_decode_fp8(const DecodeArgs &a, hipStream_t s) {
   if (a.head_dim != 128 || a.mode != kRopeLazy) return hipErrorInvalidValue;
+  if (a.int8) {
+    switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads, kDecodeMma8)) {
+      case 1: return launch_decode_t<bf16, 128, 1, kRopeLazy, true, kMma8Int8>(a, s);
+      case 2: return launch_decode_t<bf16, 128, 2, kRopeLazy, true, kMma8Int8>(a, s);
+      case 4: return launch_decode_t<bf16, 128, 4, kRopeLazy, true, kMma8Int8>(a, s);
+      case 8: return launch_decode_t<bf16, 128, 8, kRopeLazy, true, kMma8Int8>(a, s);
+      case 16: return launch_decode_t<bf16, 128, 16, kRopeLazy, true, kMma8Int8>(a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.num_q_heads / a.num_kv_heads / decode_head_split(a.num_q_heads, a.num_kv_heads, kDecodeMma8)) {
     case 1: return launch_decode_t<bf16, 128, 1, kRopeLazy, true, kMma8>(a, s);
     case 2: return launch_decode_t<bf16, 128, 2, kRopeLazy, true, kMma8>(a, s);

@@ -20,7 +20,7 @@ hipError_t launch_append(void *k_pool, void *v_pool, int elem_bytes, int num_blo
 hipError_t launch_append_fp8(void *k_pool, void *v_pool, bool bf16_rows, int num_blocks,
                              int num_kv_heads, int head_dim, const void *k_new, const void *v_new,
                              const int32_t *slot_mapping, int num_tokens, float k_scale, float v_scale,
-                             hipStream_t stream);
+                             hipStream_t stream, bool int8 = false);
 
 // Which decode kernel family a launch runs on.
 enum DecodeImpl : int {
@@ -53,6 +53,7 @@ struct DecodeArgs {
   const uint8_t *block_fill;  // per-block fill counts, or nullptr (all full)
   int mode;             // PosMode
   float k_scale = 1.f, v_scale = 1.f;  // 8-bit pools: value = code * scale
+  bool int8 = false;    // 8-bit pools: int8 codes instead of E4M3
   // work plan (device): per-sequence slot counts [batch], then plan_items
   // items of 12 ints from decode_plan_items_offset(batch); nullptr: splits
   const int32_t *plan = nullptr;
@@ -80,6 +81,7 @@ struct PrefillArgs {
   const uint8_t *block_fill;  // per-block fill counts, or nullptr (all full)
   int mode;             // PosMode
   float k_scale = 1.f, v_scale = 1.f;  // 8-bit pools: value = code * scale
+  bool int8 = false;    // 8-bit pools: int8 codes instead of E4M3
   int staged = 0;       // K/V pools are the widened copy of an 8-bit pool
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);

@@ -718,8 +718,9 @@ struct WidenArgs {
 // K[t][32 g + 16 i + x] and V[4 g + x % 4][16 (4 i + x / 4) + t].  K goes
 // straight to its row-major place (32 contiguous bytes per lane and chunk);
 // V is transposed through LDS so that every store is a contiguous 1 KiB.
-// Widening E4M3 to bf16 is exact.
-__global__ void __launch_bounds__(4 * kWave) widen_fp8_kernel(const WidenArgs a) {
+// Widening E4M3 or int8 codes to bf16 is exact.
+template <int FMT>
+__device__ __forceinline__ void widen8_body(const WidenArgs &a) {
   // V rows padded to 272 bytes: the transposing stores write 4 rows at once
   // (one per lane group), which unpadded start in the same LDS bank
   constexpr int VROW = 136;
@@ -753,8 +754,8 @@ __global__ void __launch_bounds__(4 * kWave) widen_fp8_kernel(const WidenArgs a)
     uint32_t w[8];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      w[2 * d] = e4m3x2_to_bf16x2<false>(dw4(kc[i], d));
-      w[2 * d + 1] = e4m3x2_to_bf16x2<true>(dw4(kc[i], d));
+      w[2 * d] = code8x2_to_bf16x2<FMT, false>(dw4(kc[i], d));
+      w[2 * d + 1] = code8x2_to_bf16x2<FMT, true>(dw4(kc[i], d));
     }
     uint4 *dst = (uint4 *)(ko + t * 128 + 32 * gq + 16 * i);
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -771,7 +772,7 @@ __global__ void __launch_bounds__(4 * kWave) widen_fp8_kernel(const WidenArgs a)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const uint32_t c = dw4(vc[i], jj);
-      const uint32_t lo = e4m3x2_to_bf16x2<false>(c), hi = e4m3x2_to_bf16x2<true>(c);  // rows (0,1), (2,3)
+      const uint32_t lo = code8x2_to_bf16x2<FMT, false>(c), hi = code8x2_to_bf16x2<FMT, true>(c);  // rows (0,1), (2,3)
       const uint32_t give = odd ? lo : hi;
       const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, kDppQuadXor1, 0xf, 0xf, false);
       const uint32_t mine = odd ? hi : lo;
@@ -796,13 +797,16 @@ __global__ void __launch_bounds__(4 * kWave) widen_fp8_kernel(const WidenArgs a)
   }
 }
 
+__global__ void __launch_bounds__(4 * kWave) widen_fp8_kernel(const WidenArgs a) { widen8_body<kCodeE4M3>(a); }
+__global__ void __launch_bounds__(4 * kWave) widen_int8_kernel(const WidenArgs a) { widen8_body<kCodeInt8>(a); }
+
 size_t prefill_fp8_workspace_size(int batch, int max_blocks, int num_kv_heads) {
   if (batch <= 0 || max_blocks <= 0 || num_kv_heads <= 0) return 0;
   return 2 * (size_t)batch * max_blocks * num_kv_heads * (kBlockTokens * 128 * sizeof(uint16_t));
 }
 
-// bf16 queries against 8-bit (E4M3) pools in the decode's lane order, lazy
-// RoPE, head_dim 128: widen, then the bf16 kernel on the widened copy.
+// bf16 queries against 8-bit (E4M3 or int8) pools in the decode's lane order,
+// lazy RoPE, head_dim 128: widen, then the bf16 kernel on the widened copy.
 hipError_t launch_prefill_fp8(const PrefillArgs &a, void *workspace, hipStream_t stream) {
   if (a.head_dim != 128 || a.mode != kRopeLazy || !workspace) return hipErrorInvalidValue;
   const size_t half = prefill_fp8_workspace_size(a.batch, a.max_blocks, a.num_kv_heads) / 2;
@@ -821,7 +825,8 @@ hipError_t launch_prefill_fp8(const PrefillArgs &a, void *workspace, hipStream_t
   const long long wgs = (items + 3) / 4;
   if (wgs <= 0) return hipSuccess;
   if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(widen_fp8_kernel, dim3((unsigned)wgs), dim3(4 * kWave), 0, stream, w);
+  if (a.int8) hipLaunchKernelGGL(widen_int8_kernel, dim3((unsigned)wgs), dim3(4 * kWave), 0, stream, w);
+  else hipLaunchKernelGGL(widen_fp8_kernel, dim3((unsigned)wgs), dim3(4 * kWave), 0, stream, w);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   PrefillArgs s = a;

@@ -174,8 +174,10 @@ def test_prefill_and_append_argument_errors(lib):
     assert a(NULL, NULL, 1, 16, 8, 128, NULL, NULL, NULL, 0, NULL) == 0
 
 
-def test_fp8_entry_points_check_arguments(lib):
-    a = lib.kvcache_append_fp8
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_fp8_entry_points_check_arguments(lib, fmt):
+    """The E4M3 and int8 pools' calls check their arguments alike."""
+    a = getattr(lib, f"kvcache_append_{fmt}")
     ok = [P, P, 1, 16, 8, 128, P, P, P, 4, 0.5, 0.5, NULL]
 
     def with_(args, **kw):
@@ -191,7 +193,7 @@ def test_fp8_entry_points_check_arguments(lib):
     assert a(*with_(ok, vs=float("inf"))) == -3
     assert a(*with_(ok, k_new=NULL)) == -1
     assert a(*with_(ok, tokens=0, k_new=NULL)) == 0
-    d = lib.lazyattn_decode_fp8
+    d = getattr(lib, f"lazyattn_decode_{fmt}")
     ok_d = [P, P, P, P, P, P, 4, NULL, P, 2, 8, 2, 128, 16, 0.088, 1e4, 0.5, 0.5, 0, P, 1 << 30, NULL]
 
     def dwith(**kw):
@@ -201,7 +203,7 @@ def test_fp8_entry_points_check_arguments(lib):
         for k, v in kw.items():
             out[idx[k]] = v
         return d(*out)
-    p = lib.lazyattn_prefill_fp8
+    p = getattr(lib, f"lazyattn_prefill_{fmt}")
     ok_p = [P, P, 8, P, P, P, P, P, 4, NULL, P, 1, 8, 8, 2, 128, 16, 0.088, 1e4, 0.5, 0.5, P, 1 << 30, NULL]
 
     def pwith(**kw):

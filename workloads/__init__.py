@@ -82,6 +82,22 @@ def e4m3_codes_torch(shape, device, seed, exp_lo=3, exp_hi=9):
     return sign | (exp << 3) | man
 
 
+def int8_codes(rng, shape, spread=40.0):
+    """Random contents of an int8 pool: rounded N(0, spread^2) integers,
+    clipped to [-127, 127], as int8 bytes.  Input data only."""
+    x = np.clip(np.rint(rng.standard_normal(size=shape) * spread), -127, 127)
+    return x.astype(np.int8)
+
+
+def int8_codes_torch(shape, device, seed, spread=40.0):
+    """int8_codes drawn on the GPU with torch's seeded generator (full-size pools)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    x = torch.randn(shape, device=device, generator=gen) * spread
+    return x.round().clamp(-127, 127).to(torch.int8)
+
+
 def _fp8_lane_order():
     """For byte b of an 8-bit pool's (block, KV head) record (2048 bytes, the
     lane order the library documents), the logical index token * 128 + dim of
@@ -707,6 +723,7 @@ __all__ = [
     "materialize_torch", "add_score_shift", "decode_case", "prefill_case", "tiny_decode",
     "llama8b_decode", "llama8b_prefill", "llama70b_decode", "zipf_decode", "ragged_case",
     "llama8b_decode_ragged", "llama8b_prefill_ragged", "group_decode_equal_bytes", "e4m3_codes", "e4m3_codes_torch",
+    "int8_codes", "int8_codes_torch",
     "fp8_pools_to_device_order", "fp8_pools_from_device_order", "make",
     "WORKLOADS",
 ]
