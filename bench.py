@@ -404,6 +404,15 @@ def shapes_main(args):
     res["llama8b_prefill_alibi"] = {"ms_p50": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
                                     "tflops": round(fl / (med * 1e-3) / 1e12, 1),
                                     "frac_of_bf16_peak": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    # the same inputs through the precise prefill (twice the Q.K^T products;
+    # the rate counts the algorithmic FLOPs only)
+    med, p10, p90 = timed(lambda: pak.lazyattn_prefill_precise(d.q, d.cu, d.q_pos_start, d.k_pool, d.v_pool,
+                                                               d.table, d.seq_lens, case.max_q_len,
+                                                               scale=case.scale, rope_theta=case.rope_theta,
+                                                               out=out))
+    res["llama8b_prefill_precise"] = {"ms_p50": round(med, 4), "ms_p10": round(p10, 4), "ms_p90": round(p90, 4),
+                                      "tflops": round(fl / (med * 1e-3) / 1e12, 1),
+                                      "frac_of_bf16_peak": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
     del d, out
     case.q = case.k_pool = case.v_pool = case.k_new = case.v_new = None
     torch.cuda.empty_cache()
@@ -443,11 +452,13 @@ SHAPES_DISPATCH_ORDER = {
     "lazyattn::decode_int8_kernel<4>": ["llama8b_decode_int8"],
     "lazyattn::decode_mma8_kernel<8, 0>": ["llama70b_decode_fp8"],
     # the 8-bit prefill: the widening pass, then the bf16 kernel on the widened copy
-    "lazyattn::prefill_kernel<128, 4, 0>": ["llama8b_prefill", "llama8b_prefill_fp8", "llama8b_prefill_int8",
+    "lazyattn::prefill_kernel<128, 4, 0, false>": ["llama8b_prefill", "llama8b_prefill_fp8", "llama8b_prefill_int8",
                                             "llama8b_prefill_ragged"],
     "lazyattn::widen_fp8_kernel": ["llama8b_prefill_fp8_widen"],
     "lazyattn::widen_int8_kernel": ["llama8b_prefill_int8_widen"],
-    "lazyattn::prefill_kernel<128, 4, 2>": ["llama8b_prefill_alibi"],
+    "lazyattn::prefill_kernel<128, 4, 2, false>": ["llama8b_prefill_alibi"],
+    # the precise prefill (query as bf16 hi + lo, tiles cut at document ends)
+    "lazyattn::prefill_kernel<128, 4, 0, true>": ["llama8b_prefill_precise"],
 }
 PROFILE_STEMS = {
     "llama8b_decode": "decode_llama8b", "zipf_reuse_decode": "decode_zipf",
@@ -458,7 +469,7 @@ PROFILE_STEMS = {
     "llama8b_prefill_ragged": "prefill_llama8b_ragged", "llama8b_prefill_alibi": "prefill_llama8b_alibi",
     "llama8b_prefill_fp8": "prefill_llama8b_fp8", "llama8b_prefill_fp8_widen": "widen_llama8b_fp8",
     "llama8b_decode_int8": "decode_llama8b_int8", "llama8b_prefill_int8": "prefill_llama8b_int8",
-    "llama8b_prefill_int8_widen": "widen_llama8b_int8",
+    "llama8b_prefill_int8_widen": "widen_llama8b_int8", "llama8b_prefill_precise": "prefill_llama8b_precise",
     "decode_g4_equal_bytes": "decode_g4_equal_bytes",
     "decode_g32_equal_bytes": "decode_g32_equal_bytes", "decode_g64_equal_bytes": "decode_g64_equal_bytes",
 }
@@ -499,7 +510,8 @@ def _profile_workload_bytes(name):
         return (f"{name}: the {slots} visible (block, KV head) slots of llama8b_prefill over an {pool} pool, "
                 f"widened once to bf16; algorithmic = 2 x 2 KiB of codes read + 2 x 4 KiB bf16 written per "
                 f"slot"), total
-    base = name.replace("_fp8", "").replace("_int8", "").replace("_alibi", "").replace("_planned", "")
+    base = (name.replace("_fp8", "").replace("_int8", "").replace("_alibi", "").replace("_planned", "")
+            .replace("_precise", ""))
     case = W.make(base)
     if case.kind == "decode":
         kv, total = decode_algorithmic_bytes(case)
@@ -721,7 +733,7 @@ def trace_summary_main(args):
     for key, start, end in rows:
         durs.setdefault(key, []).append((end - start) / 1000.0)
     # the timed steps: the last K prefill dispatches, each with the decode dispatch before it
-    pf_key, dec_key = "lazyattn::prefill_kernel<128, 4, 0>", "lazyattn::decode_mma16_kernel<4, 0>"
+    pf_key, dec_key = "lazyattn::prefill_kernel<128, 4, 0, false>", "lazyattn::decode_mma16_kernel<4, 0>"
     pf_idx = [i for i, r in enumerate(rows) if r[0] == pf_key][-args.steps:]
     timed_pf = [(rows[i][2] - rows[i][1]) / 1000.0 for i in pf_idx]
     timed_dec = []
@@ -1135,7 +1147,7 @@ def main():
             "algorithmic_bytes": dec_alg_bytes,
         },
         "roofline_prefill": {
-            "kernel": "lazyattn::prefill_kernel<128, 4, 0>",
+            "kernel": "lazyattn::prefill_kernel<128, 4, 0, false>",
             "bound": "mfma",
             "achieved": round(pf_tflops, 2),
             "peak": BF16_PEAK_TFLOPS,

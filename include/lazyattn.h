@@ -229,6 +229,27 @@ int lazyattn_prefill(void *out, const void *q, int total_q, const int32_t *cu_q_
                      int num_blocks, int dtype, float scale, float rope_theta, void *stream);
 
 /*
+ * lazyattn_prefill_precise -- lazyattn_prefill for score rows that spread
+ * widely across keys.  The pages trace every quality difference of the method
+ * to floating-point precision (LazyAttention summary, "Resultados
+ * Experimentais"); lazyattn_prefill rounds the rotated, pre-scaled query to
+ * bf16 once per row and document, so a score moves by up to ~|s| * 2^-9 and
+ * rows whose scores differ by more than a few units lose accuracy.  Here the
+ * query reaches the matrix cores as bf16 hi + lo (~2^-17), and K/V tiles end
+ * where the document offset changes, so stored keys are used as they are
+ * (never rotated and rounded).  The error then no longer grows with the score
+ * spread; the price is twice the Q.K^T products.
+ *
+ * Same arguments, layout, ownership and error codes as lazyattn_prefill.
+ */
+int lazyattn_prefill_precise(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                             const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                             const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
+                             const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads,
+                             int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
+                             float rope_theta, void *stream);
+
+/*
  * lazyattn_decode_noalloc -- lazyattn_decode for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, layout, results and

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "LazyAttnError", "lib_path", "load_library", "version", "kvcache_append",
     "decode_workspace_size", "lazyattn_decode", "lazyattn_prefill", "lazyattn_decode_eager",
-    "lazyattn_prefill_eager", "lazyattn_decode_alibi", "lazyattn_prefill_alibi", "kvcache_append_fp8",
+    "lazyattn_prefill_eager", "lazyattn_prefill_precise", "lazyattn_decode_alibi", "lazyattn_prefill_alibi", "kvcache_append_fp8",
     "lazyattn_decode_fp8", "lazyattn_prefill_fp8", "prefill_fp8_workspace_size", "lazyattn_decode_noalloc",
     "kvcache_append_int8", "lazyattn_decode_int8", "lazyattn_prefill_int8",
     "DecodePlan", "decode_plan", "decode_planned_workspace_size", "lazyattn_decode_planned", "BLOCK_TOKENS",
@@ -59,6 +59,7 @@ _SIGNATURES["lazyattn_decode_alibi"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i3
 _SIGNATURES["lazyattn_prefill_alibi"] = (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
                                                 _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp])
 _SIGNATURES["lazyattn_prefill_eager"] = _SIGNATURES["lazyattn_prefill"]
+_SIGNATURES["lazyattn_prefill_precise"] = _SIGNATURES["lazyattn_prefill"]
 _SIGNATURES["kvcache_append_fp8"] = (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _f32, _f32, _vp])
 _SIGNATURES["lazyattn_decode_fp8"] = (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                              _i32, _f32, _f32, _f32, _f32, _i32, _vp, _sz, _vp])
@@ -503,6 +504,14 @@ def lazyattn_prefill_eager(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_tabl
     """Non-lazy baseline of lazyattn_prefill: keys already rotated to their
     absolute positions, table offsets ignored, each query row rotated once."""
     return _prefill("lazyattn_prefill_eager", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                    kv_lens, max_q_len, scale, rope_theta, out, stream, block_fill=block_fill)
+
+
+def lazyattn_prefill_precise(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len,
+                             *, scale=None, rope_theta=10000.0, out=None, stream=None, block_fill=None):
+    """lazyattn_prefill with the rotated query carried as bf16 hi + lo (twice
+    the Q.K^T products): accurate however widely the scores spread."""
+    return _prefill("lazyattn_prefill_precise", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
                     kv_lens, max_q_len, scale, rope_theta, out, stream, block_fill=block_fill)
 
 

@@ -297,7 +297,7 @@ static int prefill_common(void *out, const void *q, int total_q, const int32_t *
                           int num_blocks, int dtype, float scale, float rope_theta, void *stream,
                           int mode, const float *slopes, bool pool8 = false, float k_scale = 1.f,
                           float v_scale = 1.f, void *workspace = nullptr, size_t workspace_bytes = 0,
-                          bool int8 = false) {
+                          bool int8 = false, bool precise = false) {
   if (dtype != LAZYATTN_BF16) return LAZYATTN_ERR_DTYPE;
   if (pool8 && (head_dim != 128 || !valid_kv_scale(k_scale) || !valid_kv_scale(v_scale)))
     return LAZYATTN_ERR_SHAPE;
@@ -341,6 +341,7 @@ static int prefill_common(void *out, const void *q, int total_q, const int32_t *
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.int8 = int8;
+  a.precise = precise;
   if (pool8) return from_hip(launch_prefill_fp8(a, workspace, (hipStream_t)stream));
   return from_hip(launch_prefill(a, (hipStream_t)stream));
 }
@@ -353,6 +354,18 @@ int lazyattn_prefill(void *out, const void *q, int total_q, const int32_t *cu_q_
   return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
                         max_blocks_per_seq, block_fill, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
                         head_dim, num_blocks, dtype, scale, rope_theta, stream, kRopeLazy, nullptr);
+}
+
+int lazyattn_prefill_precise(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                             const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                             const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
+                             const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads,
+                             int num_kv_heads, int head_dim, int num_blocks, int dtype, float scale,
+                             float rope_theta, void *stream) {
+  return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                        max_blocks_per_seq, block_fill, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
+                        head_dim, num_blocks, dtype, scale, rope_theta, stream, kRopeLazy, nullptr, false, 1.f,
+                        1.f, nullptr, 0, false, true);
 }
 
 int lazyattn_prefill_eager(void *out, const void *q, int total_q, const int32_t *cu_q_lens,

@@ -83,6 +83,7 @@ struct PrefillArgs {
   float k_scale = 1.f, v_scale = 1.f;  // 8-bit pools: value = code * scale
   bool int8 = false;    // 8-bit pools: int8 codes instead of E4M3
   int staged = 0;       // K/V pools are the widened copy of an 8-bit pool
+  bool precise = false; // rotated query as bf16 hi + lo, tiles cut at offset changes (lazy RoPE)
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // 8-bit pools: bytes of the bf16 copy of every block slot the batch can see

@@ -90,13 +90,22 @@ struct PrefillKernelArgs {
 // walked from the last visible block back to the first, so that each row meets
 // its largest biases first and the reference below rarely has to move.
 //
+// PRECISE (lazy RoPE only): the rotated, pre-scaled query is carried as two
+// bf16 parts, hi = bf16(q') and lo = bf16(q' - hi), and every K fragment meets
+// both (twice the QK products), so q' reaches the matrix cores to ~2^-17
+// instead of 2^-9.  A score's error then no longer grows with the spread of
+// the scores across keys.  Keys are never rotated either: a K/V tile ends
+// where the block offset changes, so each tile's keys all take the query's
+// rotation.  The raw query rows are reloaded (from L2) at each re-rotation to
+// make room for the low parts in registers.
+//
 // 8-bit pools: a bandwidth-bound pass (widen_fp8_kernel) first widens every
 // visible block of the batch once, exactly, into a bf16 copy laid out like a
 // bf16 pool; this kernel then reads that copy (staged).  Widening inside the
 // kernel would repeat it for every query tile that reads a block (64 times
 // per block for a 2048-token prompt).  The K scale is folded into the
 // rotated query, the V scale into the final normalisation.
-template <int D, int HP, int MODE>
+template <int D, int HP, int MODE, bool PRECISE>
 __global__ void __launch_bounds__(kPfWaves * kWave, 2)
 prefill_kernel(const PrefillKernelArgs a) {
   constexpr int KC = D / 32;          // 32-dim k-chunks of the QK product
@@ -113,6 +122,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   static_assert(HP == 1 || HP == 2 || HP == 4, "1, 2 or 4 heads per workgroup");
   constexpr bool ALIBI = MODE == kAlibi;
   constexpr bool LAZY = MODE == kRopeLazy;  // table offsets rotate queries and keys
+  static_assert(!PRECISE || LAZY, "the hi + lo query is built for lazy RoPE");
 
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILEB / 2];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILEB / 2];
@@ -212,7 +222,15 @@ prefill_kernel(const PrefillKernelArgs a) {
   // blocks' keys are rotated by the difference (rotate_keys)
   auto tile_of = [&](uint32_t wv, int jw, int &cnt, int &off) {
     cnt = min(kPfTileBlocks, nblk_vis - jw);
-    off = !LAZY ? 0 : word_offset((uint32_t)__builtin_amdgcn_readlane((int)wv, min(2, cnt - 1)));
+    if constexpr (PRECISE) {
+      // the tile ends before the first block whose offset differs from its
+      // first block's, so no key of it needs a rotation of its own
+      off = word_offset((uint32_t)__builtin_amdgcn_readlane((int)wv, 0));
+      const uint64_t diff = __ballot(lane < cnt && word_offset(wv) != off);
+      if (diff) cnt = (int)__builtin_ctzll(diff);
+    } else {
+      off = !LAZY ? 0 : word_offset((uint32_t)__builtin_amdgcn_readlane((int)wv, min(2, cnt - 1)));
+    }
   };
   // the tile [jw, jw + cnt): wave w < cnt streams block jw + w
   auto issue_tile = [&](uint32_t wv, int jw, int cnt, auto bufc) {
@@ -248,7 +266,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   auto rotate_keys = [&](int cnt, int qoff, uint32_t wv, auto bufc) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr int PPL = CPR / 8;  // chunk pairs per lane
-    if constexpr (LAZY) {
+    if constexpr (LAZY && !PRECISE) {
       if (wave >= cnt) return;
       const int delta = word_offset((uint32_t)__builtin_amdgcn_readlane((int)wv, wave)) - qoff;
       if (delta == 0) return;
@@ -330,6 +348,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   // per row against the lower bound until every row holds a sum -- so no
   // per-tile maximum is needed.
   bf16x8_t bq[2][KC];
+  bf16x8_t bql[2][KC];  // PRECISE: the low parts of the rotated query
   f32x4_t O[DT][2];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -377,10 +396,13 @@ prefill_kernel(const PrefillKernelArgs a) {
   // raw (bf16) query rows, loaded once and kept packed in registers for the
   // rotations at document changes
   uint4 qraw[2][KC];
+  auto load_rows = [&](uint4 (&r)[2][KC]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) qraw[nt][kc] = qok[nt] ? qsrc[nt][kc * 4 + lg] : make_uint4(0u, 0u, 0u, 0u);
+      for (int kc = 0; kc < KC; ++kc) r[nt][kc] = qok[nt] ? qsrc[nt][kc * 4 + lg] : make_uint4(0u, 0u, 0u, 0u);
+  };
+  if constexpr (!PRECISE) load_rows(qraw);
   if constexpr (ALIBI) {  // no rotation: q * scale * log2(e), once
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
@@ -398,13 +420,19 @@ prefill_kernel(const PrefillKernelArgs a) {
   // turn_i); the large part is reduced in double, the rest (< TOK turns)
   // evaluated with v_sin/v_cos.
   auto rotate_q = [&](int off) __attribute__((always_inline)) {
-    // opaque to the optimiser: otherwise it hoists the bf16 unpacking out of
-    // the tile loop and keeps twice the registers live
+    uint4 qre[2][KC];  // PRECISE: the raw rows, reloaded for this rotation
+    if constexpr (PRECISE) {
+      load_rows(qre);
+    } else {
+      // opaque to the optimiser: otherwise it hoists the bf16 unpacking out of
+      // the tile loop and keeps twice the registers live
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        asm volatile("" : "+v"(qraw[nt][kc].x), "+v"(qraw[nt][kc].y), "+v"(qraw[nt][kc].z), "+v"(qraw[nt][kc].w));
+        for (int kc = 0; kc < KC; ++kc)
+          asm volatile("" : "+v"(qraw[nt][kc].x), "+v"(qraw[nt][kc].y), "+v"(qraw[nt][kc].z), "+v"(qraw[nt][kc].w));
+    }
+    auto row = [&](int nt, int kc) -> const uint4 & { return PRECISE ? qre[nt][kc] : qraw[nt][kc]; };
     if (lane < HALF) {
       const double t = (double)(n0 - off) * turn_d;
       s_frac[wave][lane] = (float)(t - rint(t));
@@ -420,11 +448,17 @@ prefill_kernel(const PrefillKernelArgs a) {
           const int fi = kc * 32 + lg * 8 + e;
           const float turns = fmaf(rho, s_turn[fi], s_frac[wave][fi]);
           const float c = __builtin_amdgcn_cosf(turns), s = __builtin_amdgcn_sinf(turns);
-          const uint32_t wx = dw4(qraw[nt][kc], e >> 1), wy = dw4(qraw[nt][kc + KC / 2], e >> 1);
+          const uint32_t wx = dw4(row(nt, kc), e >> 1), wy = dw4(row(nt, kc + KC / 2), e >> 1);
           const float x = (e & 1) ? bf16_hi(wx) : bf16_lo(wx);
           const float y = (e & 1) ? bf16_hi(wy) : bf16_lo(wy);
-          bq[nt][kc][e] = (__bf16)(fmaf(x, c, -(y * s)) * a.scale_log2);
-          bq[nt][kc + KC / 2][e] = (__bf16)(fmaf(y, c, x * s) * a.scale_log2);
+          const float fx = fmaf(x, c, -(y * s)) * a.scale_log2;
+          const float fy = fmaf(y, c, x * s) * a.scale_log2;
+          bq[nt][kc][e] = (__bf16)fx;
+          bq[nt][kc + KC / 2][e] = (__bf16)fy;
+          if constexpr (PRECISE) {
+            bql[nt][kc][e] = (__bf16)(fx - (float)bq[nt][kc][e]);
+            bql[nt][kc + KC / 2][e] = (__bf16)(fy - (float)bq[nt][kc + KC / 2][e]);
+          }
         }
       }
     }
@@ -497,6 +531,10 @@ prefill_kernel(const PrefillKernelArgs a) {
           const bf16x8_t ka = as_bf16x8(*(const uint4 *)(kb + mt * 16 * ROWB + k_off[kc]));
           S[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bq[0][kc], S[mt][0], 0, 0, 0);
           S[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bq[1][kc], S[mt][1], 0, 0, 0);
+          if constexpr (PRECISE) {
+            S[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bql[0][kc], S[mt][0], 0, 0, 0);
+            S[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bql[1][kc], S[mt][1], 0, 0, 0);
+          }
         }
       }
     };
@@ -649,7 +687,7 @@ prefill_kernel(const PrefillKernelArgs a) {
   }
 }
 
-template <int D, int HP, int MODE>
+template <int D, int HP, int MODE, bool PRECISE = false>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   PrefillKernelArgs k;
   k.out = (uint16_t *)a.out;
@@ -679,21 +717,22 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
   const long long grid = (long long)(k.num_units + kXcds - 1) / kXcds * kXcds * k.tok_tiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D, HP, MODE>), dim3((unsigned)grid), dim3(kPfWaves * kWave), 0, stream,
-                     k);
+  hipLaunchKernelGGL((prefill_kernel<D, HP, MODE, PRECISE>), dim3((unsigned)grid), dim3(kPfWaves * kWave), 0,
+                     stream, k);
   return hipGetLastError();
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool PRECISE = false>
 static hipError_t launch_prefill_e(const PrefillArgs &a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
-  if (group % 4 == 0) return launch_prefill_t<D, 4, MODE>(a, stream);
-  if (group % 2 == 0) return launch_prefill_t<D, 2, MODE>(a, stream);
-  return launch_prefill_t<D, 1, MODE>(a, stream);
+  if (group % 4 == 0) return launch_prefill_t<D, 4, MODE, PRECISE>(a, stream);
+  if (group % 2 == 0) return launch_prefill_t<D, 2, MODE, PRECISE>(a, stream);
+  return launch_prefill_t<D, 1, MODE, PRECISE>(a, stream);
 }
 
 template <int D>
 static hipError_t launch_prefill_d(const PrefillArgs &a, hipStream_t stream) {
+  if (a.precise) return a.mode == kRopeLazy ? launch_prefill_e<D, kRopeLazy, true>(a, stream) : hipErrorInvalidValue;
   switch (a.mode) {
     case kRopeLazy: return launch_prefill_e<D, kRopeLazy>(a, stream);
     case kRopeEager: return launch_prefill_e<D, kRopeEager>(a, stream);

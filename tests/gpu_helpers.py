@@ -44,11 +44,11 @@ class DeviceCase(DeviceInputs):
                                    scale=c.scale, rope_theta=c.rope_theta,
                                    split_blocks=split_blocks, workspace=workspace, block_fill=self.fill)
 
-    def prefill(self):
+    def prefill(self, precise=False):
         c = self.case
-        return pak.lazyattn_prefill(self.q, self.cu, self.q_pos_start, self.k_pool, self.v_pool,
-                                    self.table, self.seq_lens, c.max_q_len, scale=c.scale,
-                                    rope_theta=c.rope_theta, block_fill=self.fill)
+        fn = pak.lazyattn_prefill_precise if precise else pak.lazyattn_prefill
+        return fn(self.q, self.cu, self.q_pos_start, self.k_pool, self.v_pool, self.table, self.seq_lens,
+                  c.max_q_len, scale=c.scale, rope_theta=c.rope_theta, block_fill=self.fill)
 
 
 def host_float(t_or_a, dtype):

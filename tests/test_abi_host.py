@@ -66,12 +66,16 @@ def test_eager_baseline_checks_arguments_alike(lib):
     for kw in ({"dtype": 7}, {"hq": 6, "hkv": 4}, {"d": 96}, {"split": 2}, {"q": NULL},
                {"batch": 0, "q": NULL}, {"ws": NULL, "max_blocks": 4000}):
         assert decode(lib, eager=True, **kw) == decode(lib, **kw)
-    f, g = lib.lazyattn_prefill, lib.lazyattn_prefill_eager
+    f, g, h = lib.lazyattn_prefill, lib.lazyattn_prefill_eager, lib.lazyattn_prefill_precise
     ok = [P, P, 4096, P, P, P, P, P, 8, NULL, P, 2, 128, 32, 8, 128, 64, 1, 0.088, 5e5, NULL]
-    for idx, val in ((17, 0), (15, 256), (2, -1), (1, NULL)):
+    for idx, val in ((17, 0), (15, 256), (2, -1), (1, NULL), (14, 3), (19, 1.0)):
         bad = list(ok)
         bad[idx] = val
-        assert g(*bad) == f(*bad) != 0
+        assert g(*bad) == f(*bad) == h(*bad) != 0
+    empty = list(ok)
+    empty[11] = 0
+    empty[1] = NULL
+    assert h(*empty) == 0
 
 
 def test_decode_argument_errors(lib):

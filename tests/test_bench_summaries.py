@@ -93,7 +93,7 @@ def test_activity_summary_formulas(tmp_path, monkeypatch):
                 "SQ_INSTS_VALU_MFMA_MOPS_BF16": 1e12 / 512, "SQ_ACTIVE_INST_VALU": 0.3 * cyc * 256,
                 "SQ_VALU_MFMA_COEXEC_CYCLES": 0.05 * cyc * 1024, "SQ_LDS_IDX_ACTIVE": 0.25 * cyc * 256,
                 "SQ_LDS_BANK_CONFLICT": 0.1 * 0.25 * cyc * 256, "SQ_BUSY_CU_CYCLES": 1.0}
-    kernel = "lazyattn::prefill_kernel<128, 4, 0>"
+    kernel = "lazyattn::prefill_kernel<128, 4, 0, false>"
     disp = []
     t = 0
     for _ in range(2 * (WARMUP + STEPS)):   # the 8B prefill, then the 8-bit one
@@ -106,7 +106,7 @@ def test_activity_summary_formulas(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(prof))
     bench.activity_summary_main(argparse.Namespace(activity_summary=d, steps=STEPS, warmup=WARMUP))
     md = (prof / "decode_prefill_shapes_activity.md").read_text()
-    row = next(line for line in md.splitlines() if line.startswith("prefill_kernel<128, 4, 0> | llama8b_prefill |"))
+    row = next(line for line in md.splitlines() if line.startswith("prefill_kernel<128, 4, 0, false> | llama8b_prefill |"))
     cells = [c.strip() for c in row.split("|")]
     assert cells[2] == "1000.0"          # us
     assert cells[3] == "2.000"           # GHz
@@ -121,7 +121,7 @@ def test_activity_summary_formulas(tmp_path, monkeypatch):
 def test_trace_summary(tmp_path, monkeypatch):
     disp = [(_full("lazyattn::decode_mma16_kernel<4, 0>"), {}, 0, 360_000),
             (_full("lazyattn::decode_mma16_kernel<4, 0>"), {}, 400_000, 762_000),
-            (_full("lazyattn::prefill_kernel<128, 4, 0>"), {}, 800_000, 1_800_000)]
+            (_full("lazyattn::prefill_kernel<128, 4, 0, false>"), {}, 800_000, 1_800_000)]
     d = str(tmp_path / "tr")
     _db(os.path.join(d, "run_results.db"), disp)
     prof = tmp_path / "profiles"
@@ -130,4 +130,4 @@ def test_trace_summary(tmp_path, monkeypatch):
     bench.trace_summary_main(argparse.Namespace(trace_summary=d, steps=2, warmup=0))
     md = (prof / "decode_prefill_llama8b_kernel_trace.md").read_text()
     assert "lazyattn::decode_mma16_kernel<4, 0> | 2 | 361.0 | 361.0 | 722.0 |" in md
-    assert "lazyattn::prefill_kernel<128, 4, 0> | 1 | 1000.0 |" in md
+    assert "lazyattn::prefill_kernel<128, 4, 0, false> | 1 | 1000.0 |" in md

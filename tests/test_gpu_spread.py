@@ -18,6 +18,9 @@ meeting the stated tolerance (bf16: 2e-2 max-abs, 5e-3 mean-abs).
   sigma = 2 and not beyond; the failing spreads are kept as skipped cases
   with the errors measured on MI355X.  A bf16 pipeline that rotates q and
   stores it as bf16 before attention rounds the same way.
+  lazyattn_prefill_precise carries q' as hi + lo as the decode does (twice
+  the Q.K^T products, ~20 % more time on the 8B prefill) and is green at the
+  same spreads up to sigma = 64 (tests/test_gpu_precise.py).
 * 8-bit pools: a K scale of 3 on codes up to 7.5 spreads scores the same
   way; a V scale of 2 makes |V| up to 15, where the bf16 rounding of the
   softmax weights and of the output itself (2^-9 relative) reaches the
@@ -67,7 +70,8 @@ def test_decode_wide_score_spread(sigma, hq, hkv, d, split):
     _decode(sigma, hq, hkv, d, split)
 
 
-_Q_ROUNDING = "prefill rounds the rotated query to bf16 (a product against its low part would add 50% matrix-core work)"
+_Q_ROUNDING = ("lazyattn_prefill rounds the rotated query to bf16; lazyattn_prefill_precise (hi + lo query) "
+               "is green at this spread")
 
 
 @pytest.mark.parametrize("sigma,hq,hkv,d", [
