@@ -706,7 +706,8 @@ def activity_summary_main(args):
             alg = None
             if "prefill" in kernel:
                 import workloads as W
-                alg = W.make(name.replace("_alibi", "").replace("_fp8", "").replace("_int8", "")).attention_flops()
+                alg = W.make(name.replace("_alibi", "").replace("_fp8", "").replace("_int8", "")
+                         .replace("_precise", "")).attention_flops()
             lds = mean("SQ_LDS_IDX_ACTIVE")
             lines.append(
                 f"{kernel.replace('lazyattn::', '')} | {name} | {t * 1e6:.1f} | {cyc / t / 1e9:.3f} | "
