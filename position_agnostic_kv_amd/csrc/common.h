@@ -125,23 +125,12 @@ constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7-i within 8
 constexpr int kDppRowMirror = 0x140;     // lane i <-> 15-i within 16
 
-// Sum over aligned groups of N consecutive lanes (N a power of two, <= 64).
-// Every lane of a group gets the bit-identical total (each step pairs lanes
-// symmetrically and float addition is commutative).
-template <int N>
-__device__ __forceinline__ float group_sum(float x) {
-  if constexpr (N >= 2) x += dpp_f32<kDppQuadXor1>(x);
-  if constexpr (N >= 4) x += dpp_f32<kDppQuadXor2>(x);
-  if constexpr (N >= 8) x += dpp_f32<kDppRowHalfMirror>(x);
-  if constexpr (N >= 16) x += dpp_f32<kDppRowMirror>(x);
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32);
-  return x;
-}
-
-// group_sum over the n values x[0..n): each DPP step is applied to all values
-// before the next step, so a value is never read by DPP right after the
-// instruction that wrote it (no wait states between dependent DPP adds).
+// Sums over aligned groups of N consecutive lanes (N a power of two, <= 64)
+// of the n values x[0..n).  Every lane of a group gets the bit-identical total
+// (each step pairs lanes symmetrically and float addition is commutative).
+// Each DPP step is applied to all values before the next step, so a value is
+// never read by DPP right after the instruction that wrote it (no wait states
+// between dependent DPP adds).
 template <int N, int n>
 __device__ __forceinline__ void group_sum_all(float *x) {
   if constexpr (N >= 2) {
