@@ -96,7 +96,7 @@ struct PrefillKernelArgs {
 // instead of 2^-9.  A score's error then no longer grows with the spread of
 // the scores across keys.  Keys are never rotated either: a K/V tile ends
 // where the block offset changes, so each tile's keys all take the query's
-// rotation.  The raw query rows are reloaded (from L2) at each re-rotation to
+// rotation.  The raw query rows are reloaded from memory at each re-rotation to
 // make room for the low parts in registers.
 //
 // 8-bit pools: a bandwidth-bound pass (widen_fp8_kernel) first widens every
