@@ -81,9 +81,33 @@ def host_threads():
         return os.cpu_count() or 1
 
 
-def cpu_baseline_decode(case, dc, seconds):
+class SampleParity:
+    """Element-wise error of the GPU output against the oracle on the rows the
+    CPU baseline computed (bf16 tolerances: 2e-2 max-abs, 5e-3 mean-abs)."""
+
+    def __init__(self):
+        self.max_abs, self.sum_abs, self.count = 0.0, 0.0, 0
+
+    def add(self, got, want):
+        err = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(want, dtype=np.float64))
+        self.max_abs = max(self.max_abs, float(err.max()))
+        self.sum_abs += float(err.sum())
+        self.count += err.size
+
+    def record(self, what):
+        mean = self.sum_abs / max(self.count, 1)
+        return {"max_abs": self.max_abs, "mean_abs": mean, "elements": self.count,
+                "tolerance": {"max_abs": 2e-2, "mean_abs": 5e-3},
+                "within_tolerance": bool(self.max_abs <= 2e-2 and mean <= 5e-3),
+                "sample": f"{what}: the GPU output of the timed steps against the float64 oracle on the "
+                          f"CPU baseline's sample"}
+
+
+def cpu_baseline_decode(case, dc, seconds, out=None):
     """The oracle, single-threaded, on whole (sequence, KV head) groups of the
-    same workload until `seconds` of CPU work; scaled to GB/s of K+V."""
+    same workload until `seconds` of CPU work; scaled to GB/s of K+V.  With
+    the GPU output `out` of the same inputs, also returns its error against
+    the oracle on those groups (else None)."""
     from threadpoolctl import threadpool_limits
     import oracle
     import workloads as W
@@ -92,6 +116,7 @@ def cpu_baseline_decode(case, dc, seconds):
     q = W.to_float(case.q, case.dtype)
     g = case.num_q_heads // case.num_kv_heads
     done_bytes, groups, t_used = 0, 0, 0.0
+    par = SampleParity()
     nthr = host_threads()
     with threadpool_limits(nthr):
         for b in range(case.batch):
@@ -107,23 +132,27 @@ def cpu_baseline_decode(case, dc, seconds):
                                                            case.rope_theta)
                 qr = oracle.rope(q[b, kvh * g:(kvh + 1) * g], int(case.q_pos[b]), case.rope_theta)
                 p = oracle.softmax(case.scale * (qr @ k_hat.T))
-                _ = p @ v_hat
+                o = p @ v_hat
                 t_used += time.perf_counter() - t0
+                if out is not None:
+                    par.add(W.to_float(out[b, kvh * g:(kvh + 1) * g], case.dtype), o)
                 done_bytes += int(case.seq_lens[b]) * case.head_dim * 2 * 2
                 groups += 1
                 if t_used >= seconds:
                     break
             if t_used >= seconds:
                 break
-    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": nthr, "kind": "oracle",
+    base = {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": nthr, "kind": "oracle",
             "sample": f"{groups} (sequence, KV head) groups of {case.name} "
                       f"({groups * g} query heads, {done_bytes // (case.head_dim * 4)} tokens x KV heads), "
                       f"{t_used:.1f} s, float64 numpy, {nthr} BLAS threads"}
+    return base, (par.record(f"{groups * g} query heads of {case.name}") if out is not None else None)
 
 
-def cpu_baseline_prefill(case, dc, seconds):
+def cpu_baseline_prefill(case, dc, seconds, out=None):
     """The oracle on the prompt rows of (sequence, head) pairs of the prefill
-    workload, head by head, until `seconds` of CPU work."""
+    workload, head by head, until `seconds` of CPU work; with the GPU output
+    `out`, also its error against the oracle on those rows (else None)."""
     from threadpoolctl import threadpool_limits
     import oracle
     import workloads as W
@@ -133,6 +162,7 @@ def cpu_baseline_prefill(case, dc, seconds):
     q = W.to_float(case.q, case.dtype)
     plen = case.max_q_len
     flops, t_used, rows_done, heads = 0, 0.0, 0, 0
+    par = SampleParity()
     nthr = host_threads()
     with threadpool_limits(nthr):
         for b in range(case.batch):
@@ -149,9 +179,12 @@ def cpu_baseline_prefill(case, dc, seconds):
                 for r0 in range(0, plen, 128):
                     rows = np.arange(r0, min(plen, r0 + 128))
                     t0 = time.perf_counter()
-                    oracle.prefill_rows(q[q0 + rows, h], rows, plen, int(lay.tail_pos[b]), kp, vp, row,
-                                        kv_len, h // g, case.scale, case.rope_theta)
+                    o = oracle.prefill_rows(q[q0 + rows, h], rows, plen, int(lay.tail_pos[b]), kp, vp, row,
+                                            kv_len, h // g, case.scale, case.rope_theta)
                     t_used += time.perf_counter() - t0
+                    if out is not None:
+                        idx = torch.from_numpy(q0 + rows).to(out.device)
+                        par.add(W.to_float(out[:, h].index_select(0, idx), case.dtype), o)
                     flops += 4 * case.head_dim * int(np.sum(cached + rows + 1))
                     rows_done += len(rows)
                 heads += 1
@@ -159,9 +192,10 @@ def cpu_baseline_prefill(case, dc, seconds):
                     break
             if t_used >= seconds:
                 break
-    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": nthr, "kind": "oracle",
+    base = {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": nthr, "kind": "oracle",
             "sample": f"{rows_done} prompt rows ({heads} (sequence, head) pairs) of llama8b_prefill, "
                       f"{t_used:.1f} s, float64 numpy, {nthr} BLAS threads"}
+    return base, (par.record(f"{rows_done} prompt rows of llama8b_prefill") if out is not None else None)
 
 
 def overhead_main(args):
@@ -925,7 +959,7 @@ def decode_workload_line(name, args, dev):
         rec["physical_pool_gbps"] = round(phys / (kernel_ms * 1e-3) / 1e9, 1)
         rec["per_sequence_decode"] = per_seq
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline_decode(case, d, args.cpu_seconds)
+        rec["cpu_baseline"], rec["parity_sample"] = cpu_baseline_decode(case, d, args.cpu_seconds, out)
     del d, out, ws
     case.q = case.k_pool = case.v_pool = case.k_new = case.v_new = None
     torch.cuda.empty_cache()
@@ -1159,8 +1193,9 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_decode(dcase, dd, args.cpu_seconds)
-        res["cpu_baseline_prefill"] = cpu_baseline_prefill(pcase, pd, args.cpu_seconds)
+        res["cpu_baseline"], res["parity_sample"] = cpu_baseline_decode(dcase, dd, args.cpu_seconds, dout)
+        res["cpu_baseline_prefill"], res["parity_sample_prefill"] = cpu_baseline_prefill(
+            pcase, pd, args.cpu_seconds, pout)
     # the metric's other decode workloads, each timed as its own pass after the steps above
     del dd, pd, ws, dout, pout
     dcase.q = dcase.k_pool = dcase.v_pool = dcase.k_new = dcase.v_new = None
