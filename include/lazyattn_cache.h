@@ -63,7 +63,9 @@ enum { LAZYATTN_CACHE_AGNOSTIC = 0, LAZYATTN_CACHE_AWARE = 1, LAZYATTN_CACHE_PRE
 
 enum {
   LAZYATTN_CACHE_OK = 0,
-  LAZYATTN_CACHE_ERR_ARG = -1,      /* NULL pointer, bad size or mode, unknown request */
+  LAZYATTN_CACHE_ERR_ARG = -1,      /* NULL pointer, bad size or mode, unknown request, or a
+                                       document named with another length than it is cached
+                                       (or named earlier in the same request) with */
   LAZYATTN_CACHE_ERR_NOSPACE = -2,  /* not enough free + evictable blocks, or the table row is too short */
   LAZYATTN_CACHE_ERR_POSITION = -3  /* a frame start would not fit the 16-bit offset field */
 };
@@ -86,7 +88,11 @@ void lazyattn_cache_destroy(lazyattn_cache *c);
  *                          (the caller must write their K/V, encoded in the
  *                          document's own frame), 0 where they were reused
  *   request_id             handle for lazyattn_cache_release
- * Returns the number of table words written (>= 0) or a negative status.
+ * Returns the number of table words written (>= 0) or a negative status;
+ * on a negative status nothing is placed and no output is written.  A
+ * document's length is part of its identity: naming a cached document (or
+ * one named earlier in the same request) with another length is
+ * LAZYATTN_CACHE_ERR_ARG.
  * The request holds a reference on each of its documents until released.
  */
 int lazyattn_cache_acquire(lazyattn_cache *c, const int32_t *doc_ids, const int32_t *doc_lens, int n_docs,

@@ -26,6 +26,9 @@ Readings (the pages give no allocator details nor an eviction policy):
   ones are allocated in request order (a document missing twice in one
   request is allocated once); then the prompt.  A request that cannot be
   placed changes nothing.
+* A document's length is part of its identity (it is stored once, by
+  content): naming a cached document, or one named earlier in the same
+  request, with another length is an argument error, and changes nothing.
 * Frame starts (the table word's high 16 bits) are the document's placement
   position (the running sum of the lengths before it) and, for the prompt,
   the first position after the documents; every position must be < 65536.
@@ -41,6 +44,10 @@ class NoSpace(Exception):
 
 
 class BadPosition(Exception):
+    pass
+
+
+class BadArgument(Exception):
     pass
 
 
@@ -98,6 +105,13 @@ class CachePolicyModel:
         prompt_nb = -(-prompt_len // BLOCK)
         if sum(L // BLOCK for L in lens) + prompt_nb > max_blocks:
             raise NoSpace()
+        named = {}
+        for k, L in zip(keys, lens):
+            nb = L // BLOCK
+            if k in self.docs and len(self.docs[k]["blocks"]) != nb:
+                raise BadArgument()
+            if named.setdefault(k, nb) != nb:
+                raise BadArgument()
         # will it fit?  blocks to allocate against free + evictable-but-not-hit
         hit = {k for k in keys if k in self.docs}
         new, need = set(), prompt_nb

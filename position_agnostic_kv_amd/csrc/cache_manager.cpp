@@ -139,15 +139,23 @@ int lazyattn_cache_acquire(lazyattn_cache *c, const int32_t *doc_ids, const int3
 
   // dry run: blocks to allocate (a key missing twice in one request is
   // allocated once) against free blocks plus those of unreferenced documents
-  // this request does not hit
-  std::set<Key> hit_keys, new_keys;
+  // this request does not hit.  A document must keep its length: a key
+  // cached (or named earlier in this request) with another block count is
+  // rejected, since the row would get the cached blocks, not doc_lens[i].
+  std::set<Key> hit_keys;
+  std::map<Key, int> new_keys;
   long long need = prompt_nb;
   for (int i = 0; i < n_docs; ++i) {
     const Key &k = keys[(size_t)i];
-    if (c->docs.count(k)) {
+    const int nb = doc_lens[i] / kBlockTokens;
+    auto it = c->docs.find(k);
+    if (it != c->docs.end()) {
+      if (it->second.blocks.size() != (size_t)nb) return LAZYATTN_CACHE_ERR_ARG;
       hit_keys.insert(k);
-    } else if (new_keys.insert(k).second) {
-      need += doc_lens[i] / kBlockTokens;
+    } else {
+      auto ins = new_keys.emplace(k, nb);
+      if (ins.second) need += nb;
+      else if (ins.first->second != nb) return LAZYATTN_CACHE_ERR_ARG;
     }
   }
   long long avail = (long long)c->free_list.size();

@@ -18,7 +18,7 @@
 import numpy as np
 import pytest
 
-from oracle.cache_policy import AGNOSTIC, AWARE, PREFIX, BadPosition, CachePolicyModel, NoSpace
+from oracle.cache_policy import AGNOSTIC, AWARE, PREFIX, BadArgument, BadPosition, CachePolicyModel, NoSpace
 
 C = pytest.importorskip("position_agnostic_kv_amd.cache")
 
@@ -68,6 +68,8 @@ class Model:
             return "nospace"
         except BadPosition:
             return "position"
+        except BadArgument:
+            return "arg"
 
     def release(self, rid):
         self.m.release(rid)
@@ -151,6 +153,25 @@ def test_repeat_within_one_request_shares_blocks(mk):
     assert row == [w(0, 0), w(1, 0), w(2, 32), w(0, 48), w(1, 48)]
 
 
+def test_document_length_is_part_of_its_identity(mk):
+    """Naming a cached document with another length, or one document twice in
+    a request with two lengths, is an argument error that changes nothing.
+    (The native manager once placed the cached blocks regardless and wrote
+    them past a row sized for the request's own lengths.)"""
+    for mode in ("agnostic", "aware"):
+        c = mk(16, mode)
+        _, _, r0 = c.acquire([4], [48], 0)                       # 3 blocks
+        before = c.stats()
+        assert c.acquire([4], [16], 0, max_blocks=1) == "arg"     # claims 1 block
+        assert c.acquire([4], [64], 0) == "arg"
+        if mode == "agnostic":   # position-aware: two positions are two documents
+            assert c.acquire([9, 9], [32, 48], 0) == "arg"        # not cached, two lengths
+        assert c.stats() == before
+        row, miss, _ = c.acquire([4, 9, 9], [48, 32, 32], 0)     # consistent: placed
+        assert miss == ([0, 1, 0] if mode == "agnostic" else [0, 1, 1]) and len(row) == 3 + 2 + 2
+        c.release(r0)
+
+
 def test_positions_beyond_the_offset_field(mk):
     c = mk(4096, "agnostic")
     assert c.acquire([1, 2], [32768, 32768], 1) == "position"   # prompt at 65536
@@ -210,6 +231,33 @@ def test_native_matches_model_on_random_traces(mode, seed):
         _check_partition(mod)
         for d in mod.m.docs.values():
             assert d["refs"] >= 0
+
+
+@pytest.mark.parametrize("mode", ["agnostic", "aware", "prefix"])
+def test_native_matches_model_with_inconsistent_lengths(mode):
+    """Random traces in which a tenth of the documents are named with a wrong
+    length: both reject the same requests and otherwise agree exactly."""
+    rng = np.random.default_rng(200)
+    nb = 48
+    nat, mod = Native(nb, mode), Model(nb, mode)
+    live, rejected = [], 0
+    for step in range(400):
+        if live and rng.random() < 0.45:
+            rid = live.pop(int(rng.integers(len(live))))
+            nat.release(rid)
+            mod.release(rid)
+            continue
+        ids = [int(x) for x in rng.integers(0, 10, size=int(rng.integers(1, 4)))]
+        lens = [16 * (1 + (i * 7919) % 4) + (16 if rng.random() < 0.1 else 0) for i in ids]
+        prompt = int(rng.integers(0, 40))
+        maxb = sum(L // 16 for L in lens) + -(-prompt // 16)
+        a, b = nat.acquire(ids, lens, prompt, maxb), mod.acquire(ids, lens, prompt, maxb)
+        assert a == b, f"step {step}: native {a} model {b}"
+        rejected += a == "arg"
+        if not isinstance(a, str):
+            live.append(a[2])
+        assert nat.stats() == mod.stats(), f"step {step}"
+    assert rejected > 0
 
 
 # --------------------------------------------------- hit rates under a budget
