@@ -439,6 +439,31 @@ int lazyattn_prefill_int8(void *out, const void *q, int total_q, const int32_t *
                           int head_dim, int num_blocks, float scale, float rope_theta, float k_scale,
                           float v_scale, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * lazyattn_prefill_fp8_precise, lazyattn_prefill_int8_precise -- the 8-bit
+ * prefills with the rotated query carried as bf16 hi + lo and K/V tiles cut
+ * where the document offset changes, as lazyattn_prefill_precise does for
+ * bf16 pools (LazyAttention summary, "Resultados Experimentais": quality
+ * differences come down to floating-point precision).  A large K scale
+ * spreads a row's scores the way large keys do; these calls stay within
+ * tolerance there.  Same arguments, workspace, layout and errors as
+ * lazyattn_prefill_fp8 / lazyattn_prefill_int8.
+ */
+int lazyattn_prefill_fp8_precise(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                                 const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                                 const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
+                                 const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads,
+                                 int num_kv_heads, int head_dim, int num_blocks, float scale, float rope_theta,
+                                 float k_scale, float v_scale, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+int lazyattn_prefill_int8_precise(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                                  const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                                  const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
+                                  const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int num_blocks, float scale, float rope_theta,
+                                  float k_scale, float v_scale, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ __all__ = [
     "decode_workspace_size", "lazyattn_decode", "lazyattn_prefill", "lazyattn_decode_eager",
     "lazyattn_prefill_eager", "lazyattn_prefill_precise", "lazyattn_decode_alibi", "lazyattn_prefill_alibi", "kvcache_append_fp8",
     "lazyattn_decode_fp8", "lazyattn_prefill_fp8", "prefill_fp8_workspace_size", "lazyattn_decode_noalloc",
-    "kvcache_append_int8", "lazyattn_decode_int8", "lazyattn_prefill_int8",
+    "kvcache_append_int8", "lazyattn_decode_int8", "lazyattn_prefill_int8", "lazyattn_prefill_fp8_precise",
+    "lazyattn_prefill_int8_precise",
     "DecodePlan", "decode_plan", "decode_planned_workspace_size", "lazyattn_decode_planned", "BLOCK_TOKENS",
 ]
 
@@ -69,6 +70,8 @@ _SIGNATURES["lazyattn_prefill_fp8_workspace_size"] = (_sz, [_i32, _i32, _i32, _i
 _SIGNATURES["kvcache_append_int8"] = _SIGNATURES["kvcache_append_fp8"]
 _SIGNATURES["lazyattn_decode_int8"] = _SIGNATURES["lazyattn_decode_fp8"]
 _SIGNATURES["lazyattn_prefill_int8"] = _SIGNATURES["lazyattn_prefill_fp8"]
+_SIGNATURES["lazyattn_prefill_fp8_precise"] = _SIGNATURES["lazyattn_prefill_fp8"]
+_SIGNATURES["lazyattn_prefill_int8_precise"] = _SIGNATURES["lazyattn_prefill_fp8"]
 _SIGNATURES["lazyattn_decode_plan_ints"] = (_sz, [_i32, _i32, _i32])
 _SIGNATURES["lazyattn_decode_plan"] = (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _vp])
 _SIGNATURES["lazyattn_decode_planned_workspace_size"] = (_sz, [_i32, _i32, _i32, _i32, _i32])
@@ -547,6 +550,26 @@ def lazyattn_prefill_int8(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table
     kvcache_append_int8: keys are code * k_scale, values code * v_scale.
     workspace as lazyattn_prefill_fp8 (prefill_fp8_workspace_size bytes)."""
     return _prefill("lazyattn_prefill_int8", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                    kv_lens, max_q_len, scale, rope_theta, out, stream, block_fill=block_fill,
+                    kv_scales=(float(k_scale), float(v_scale)), workspace=workspace, pool_types=_POOL_INT8)
+
+
+def lazyattn_prefill_fp8_precise(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len,
+                                 k_scale, v_scale, *, scale=None, rope_theta=10000.0, out=None, workspace=None,
+                                 stream=None, block_fill=None):
+    """lazyattn_prefill_fp8 with the rotated query as bf16 hi + lo (see
+    lazyattn_prefill_precise)."""
+    return _prefill("lazyattn_prefill_fp8_precise", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                    kv_lens, max_q_len, scale, rope_theta, out, stream, block_fill=block_fill,
+                    kv_scales=(float(k_scale), float(v_scale)), workspace=workspace, pool_types=_POOL8)
+
+
+def lazyattn_prefill_int8_precise(q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table, kv_lens, max_q_len,
+                                  k_scale, v_scale, *, scale=None, rope_theta=10000.0, out=None, workspace=None,
+                                  stream=None, block_fill=None):
+    """lazyattn_prefill_int8 with the rotated query as bf16 hi + lo (see
+    lazyattn_prefill_precise)."""
+    return _prefill("lazyattn_prefill_int8_precise", q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
                     kv_lens, max_q_len, scale, rope_theta, out, stream, block_fill=block_fill,
                     kv_scales=(float(k_scale), float(v_scale)), workspace=workspace, pool_types=_POOL_INT8)
 

@@ -414,6 +414,32 @@ int lazyattn_prefill_int8(void *out, const void *q, int total_q, const int32_t *
                         true, k_scale, v_scale, workspace, workspace_bytes, true);
 }
 
+int lazyattn_prefill_fp8_precise(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                                 const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                                 const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
+                                 const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads,
+                                 int num_kv_heads, int head_dim, int num_blocks, float scale, float rope_theta,
+                                 float k_scale, float v_scale, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+  return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                        max_blocks_per_seq, block_fill, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
+                        head_dim, num_blocks, LAZYATTN_BF16, scale, rope_theta, stream, kRopeLazy, nullptr,
+                        true, k_scale, v_scale, workspace, workspace_bytes, false, true);
+}
+
+int lazyattn_prefill_int8_precise(void *out, const void *q, int total_q, const int32_t *cu_q_lens,
+                                  const int32_t *q_pos_start, const void *k_pool, const void *v_pool,
+                                  const uint32_t *block_table, int max_blocks_per_seq, const uint8_t *block_fill,
+                                  const int32_t *kv_lens, int batch, int max_q_len, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int num_blocks, float scale, float rope_theta,
+                                  float k_scale, float v_scale, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  return prefill_common(out, q, total_q, cu_q_lens, q_pos_start, k_pool, v_pool, block_table,
+                        max_blocks_per_seq, block_fill, kv_lens, batch, max_q_len, num_q_heads, num_kv_heads,
+                        head_dim, num_blocks, LAZYATTN_BF16, scale, rope_theta, stream, kRopeLazy, nullptr,
+                        true, k_scale, v_scale, workspace, workspace_bytes, true, true);
+}
+
 size_t lazyattn_prefill_fp8_workspace_size(int batch, int max_blocks_per_seq, int num_kv_heads, int head_dim) {
   if (head_dim != 128) return 0;
   return prefill_fp8_workspace_size(batch, max_blocks_per_seq, num_kv_heads);

@@ -872,10 +872,8 @@ hipError_t launch_prefill_fp8(const PrefillArgs &a, void *workspace, hipStream_t
   s.k_pool = w.k_out;
   s.v_pool = w.v_out;
   s.staged = 1;
-  const int group = a.num_q_heads / a.num_kv_heads;
-  if (group % 4 == 0) return launch_prefill_t<128, 4, kRopeLazy>(s, stream);
-  if (group % 2 == 0) return launch_prefill_t<128, 2, kRopeLazy>(s, stream);
-  return launch_prefill_t<128, 1, kRopeLazy>(s, stream);
+  if (a.precise) return launch_prefill_e<128, kRopeLazy, true>(s, stream);
+  return launch_prefill_e<128, kRopeLazy>(s, stream);
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {

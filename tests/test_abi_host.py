@@ -223,6 +223,14 @@ def test_fp8_entry_points_check_arguments(lib, fmt):
     assert pwith(hq=6, hkv=4) == -3
     assert pwith(q=NULL) == -1
     assert pwith(batch=0, q=NULL) == 0
+    assert pwith(ws=NULL) == -4
+    pp = getattr(lib, f"lazyattn_prefill_{fmt}_precise")   # the precise variant checks alike
+    for kw in ({"d": 64}, {"ks": 0.0}, {"vs": float("inf")}, {"hq": 6, "hkv": 4}, {"q": NULL},
+               {"batch": 0, "q": NULL}, {"ws": NULL}):
+        args = list(ok_p)
+        for k, v in kw.items():
+            args[{"q": 1, "batch": 11, "hq": 13, "hkv": 14, "d": 15, "ks": 19, "vs": 20, "ws": 21}[k]] = v
+        assert pp(*args) == pwith(**kw)
     need = lib.lazyattn_prefill_fp8_workspace_size(1, 4, 2, 128)
     assert need == 2 * 1 * 4 * 2 * 16 * 128 * 2     # K and V, bf16, every block slot
     assert lib.lazyattn_prefill_fp8_workspace_size(1, 4, 2, 64) == 0

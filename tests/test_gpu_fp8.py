@@ -206,7 +206,7 @@ def test_full_size_decode_fp8_sampled(name):
 
 
 # ---------------------------------------------------------------- prefill
-def _run_prefill(case, seed, ks, vs):
+def _run_prefill(case, seed, ks, vs, precise=False):
     """Append the prompts' rows into an 8-bit pool of random codes, prefill,
     and return (got, want) with the oracle on the same codes (the append
     bytes checked exactly on the way)."""
@@ -215,8 +215,9 @@ def _run_prefill(case, seed, ks, vs):
     dc = DeviceCase(case)
     k8, v8 = (_u8(x) for x in W.fp8_pools_to_device_order(kc, vc))
     pak.kvcache_append_fp8(k8, v8, dc.k_new, dc.v_new, dc.slots, ks, vs)
-    out = pak.lazyattn_prefill_fp8(dc.q, dc.cu, dc.q_pos_start, k8, v8, dc.table, dc.seq_lens, case.max_q_len,
-                                   ks, vs, scale=case.scale, rope_theta=case.rope_theta, block_fill=dc.fill)
+    fn = pak.lazyattn_prefill_fp8_precise if precise else pak.lazyattn_prefill_fp8
+    out = fn(dc.q, dc.cu, dc.q_pos_start, k8, v8, dc.table, dc.seq_lens, case.max_q_len,
+             ks, vs, scale=case.scale, rope_theta=case.rope_theta, block_fill=dc.fill)
     torch.cuda.synchronize()
     kn, vn = W.to_float(case.k_new, case.dtype), W.to_float(case.v_new, case.dtype)
     kc2, vc2 = oracle.append_fp8(kc, vc, kn, vn, case.layout.slot_mapping, np.float32(ks), np.float32(vs))
@@ -382,3 +383,16 @@ def test_full_size_prefill_fp8_sampled():
                                              tab[i], int(case.seq_lens[b]), h // g, case.scale, case.rope_theta))
             gots.append(got[q0 + qrows, h])
     assert_parity(np.concatenate(gots), np.concatenate(wants), W.BF16, "llama8b_prefill fp8 sampled")
+
+
+@pytest.mark.parametrize("hq,hkv,cached,prompt,docs,offs,ks,vs", PREFILL[:3] + [
+    (32, 8, [512, 96], [256, 77], (2, 12), "random", 3.0, 0.25),   # a K scale that spreads the scores
+])
+def test_prefill_fp8_precise(hq, hkv, cached, prompt, docs, offs, ks, vs):
+    """lazyattn_prefill_fp8_precise (rotated query as bf16 hi + lo, tiles cut
+    at document ends) against the oracle, including a K scale of 3 on codes up
+    to 7.5, where lazyattn_prefill_fp8 misses the tolerance."""
+    case = W.prefill_case(233 + hq + int(ks * 10), len(prompt), hq, hkv, 128, cached, prompt, docs, offsets=offs)
+    say(f"[fp8 precise prefill] Hq{hq} Hkv{hkv} k_scale {ks} v_scale {vs} {offs}")
+    got, want = _run_prefill(case, 61, ks, vs, precise=True)
+    assert_parity(got, want, W.BF16, f"fp8 precise prefill k_scale {ks}")

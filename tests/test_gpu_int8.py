@@ -143,14 +143,15 @@ def test_single_token_reads_every_code_exactly():
         assert np.array_equal(got[h], want), f"head {h}"
 
 
-def _run_prefill(case, seed, ks, vs):
+def _run_prefill(case, seed, ks, vs, precise=False):
     W.materialize_numpy(case)
     kc, vc = _codes(case, seed)
     dc = DeviceCase(case)
     k8, v8 = (_dev8(x) for x in W.fp8_pools_to_device_order(kc, vc))
     pak.kvcache_append_int8(k8, v8, dc.k_new, dc.v_new, dc.slots, ks, vs)
-    out = pak.lazyattn_prefill_int8(dc.q, dc.cu, dc.q_pos_start, k8, v8, dc.table, dc.seq_lens, case.max_q_len,
-                                    ks, vs, scale=case.scale, rope_theta=case.rope_theta, block_fill=dc.fill)
+    fn = pak.lazyattn_prefill_int8_precise if precise else pak.lazyattn_prefill_int8
+    out = fn(dc.q, dc.cu, dc.q_pos_start, k8, v8, dc.table, dc.seq_lens, case.max_q_len,
+             ks, vs, scale=case.scale, rope_theta=case.rope_theta, block_fill=dc.fill)
     torch.cuda.synchronize()
     kn, vn = W.to_float(case.k_new, case.dtype), W.to_float(case.v_new, case.dtype)
     kc2, vc2 = oracle.append_int8(kc, vc, kn, vn, case.layout.slot_mapping, np.float32(ks), np.float32(vs))
@@ -271,3 +272,16 @@ def test_full_size_decode_int8_sampled():
                                                h // g, case.scale, case.rope_theta))
             rows_got.append(got[b, h])
     assert_parity(np.stack(rows_got), np.stack(rows_want), W.BF16, "llama8b_decode int8 sampled")
+
+
+@pytest.mark.parametrize("hq,hkv,cached,prompt,docs,offs,ks,vs", PREFILL + [
+    (32, 8, [512, 96], [256, 77], (2, 12), "random", 0.08, 0.005),   # a K scale that spreads the scores
+])
+def test_prefill_int8_precise(hq, hkv, cached, prompt, docs, offs, ks, vs):
+    """lazyattn_prefill_int8_precise against the oracle, including a K scale
+    that spreads each row's scores several units wide."""
+    case = W.prefill_case(331 + hq + int(ks * 1000), len(prompt), hq, hkv, 128, cached, prompt, docs,
+                          offsets=offs)
+    say(f"[int8 precise prefill] Hq{hq} Hkv{hkv} k_scale {ks} v_scale {vs} {offs}")
+    got, want = _run_prefill(case, 67, ks, vs, precise=True)
+    assert_parity(got, want, W.BF16, f"int8 precise prefill k_scale {ks}")

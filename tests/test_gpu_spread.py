@@ -72,8 +72,9 @@ def test_decode_wide_score_spread(sigma, hq, hkv, d, split):
 
 _Q_ROUNDING = ("lazyattn_prefill rounds the rotated query to bf16; lazyattn_prefill_precise (hi + lo query) "
                "is green at this spread")
-_Q_ROUNDING_8BIT = ("the 8-bit prefill rounds the rotated, K-scaled query to bf16 (the hi + lo query of "
-                    "lazyattn_prefill_precise is offered for bf16 pools only)")
+_Q_ROUNDING_8BIT = ("lazyattn_prefill_fp8 rounds the rotated, K-scaled query to bf16; "
+                    "lazyattn_prefill_fp8_precise (hi + lo query) is green at k_scale 3 "
+                    "(tests/test_gpu_fp8.py)")
 
 
 @pytest.mark.parametrize("sigma,hq,hkv,d", [
