@@ -38,7 +38,7 @@ def driver(tmp_path_factory):
 
 @pytest.mark.parametrize("seed", [12345, 777])
 def test_host_code_is_clean_under_sanitizers(driver, seed):
-    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:verify_asan_link_order=0",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
     res = subprocess.run([driver, "300", str(seed)], stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
                          text=True, env=env, timeout=300)
