@@ -1,6 +1,7 @@
 """The C-ABI calls are stream-ordered and allocate nothing, so a whole step
 (append + decode with split-K partials, append + prefill, the 8-bit pool's
-append + decode, and the planned decode with a plan built beforehand) can be
+append + decode, the planned decode with a plan built beforehand, the
+precise prefill, and the 8-bit prefill's widening pass and prefill) can be
 captured in a HIP graph and replayed.  Every
 replay, with eager work on the same stream between replays, must give the
 eager results bit for bit (the kernels are deterministic).  Outputs and the
@@ -42,6 +43,12 @@ def test_graph_replays_equal_eager():
                                                             dcase.head_dim, plan.max_items_per_seq), 1),
                       dtype=torch.uint8, device=DEV)
     pl_out = torch.empty_like(dd.q)
+    pre_out = torch.empty_like(pd.q)
+    pshape = tuple(pd.k_pool.shape)
+    pk8, pv8 = W.e4m3_codes_torch(pshape, DEV, 13), W.e4m3_codes_torch(pshape, DEV, 14)
+    pws8 = torch.empty(max(pak.prefill_fp8_workspace_size(pcase.batch, pd.table.shape[1], pcase.num_kv_heads), 1),
+                       dtype=torch.uint8, device=DEV)
+    pout8 = torch.empty_like(pd.q)
 
     def step():
         pak.kvcache_append(dd.k_pool, dd.v_pool, dd.k_new, dd.v_new, dd.slots)
@@ -55,8 +62,14 @@ def test_graph_replays_equal_eager():
                                 rope_theta=dcase.rope_theta, split_blocks=split, out=out8, workspace=ws)
         pak.lazyattn_decode_planned(dd.q, dd.q_pos, dd.k_pool, dd.v_pool, dd.table, dd.seq_lens, plan,
                                     scale=dcase.scale, rope_theta=dcase.rope_theta, out=pl_out, workspace=pws)
+        pak.lazyattn_prefill_precise(pd.q, pd.cu, pd.q_pos_start, pd.k_pool, pd.v_pool, pd.table, pd.seq_lens,
+                                     pcase.max_q_len, scale=pcase.scale, rope_theta=pcase.rope_theta, out=pre_out)
+        pak.kvcache_append_fp8(pk8, pv8, pd.k_new, pd.v_new, pd.slots, 0.25, 0.125)
+        pak.lazyattn_prefill_fp8(pd.q, pd.cu, pd.q_pos_start, pk8, pv8, pd.table, pd.seq_lens, pcase.max_q_len,
+                                 0.25, 0.125, scale=pcase.scale, rope_theta=pcase.rope_theta, out=pout8,
+                                 workspace=pws8)
 
-    outs = (dout, pout, out8, pl_out)
+    outs = (dout, pout, out8, pl_out, pre_out, pout8)
     step()
     torch.cuda.synchronize()
     want = [_bits(t) for t in outs]
@@ -78,7 +91,8 @@ def test_graph_replays_equal_eager():
         torch.cuda.synchronize()
         got = [_bits(t) for t in outs]
         say(f"[graph] replay {r}")
-        for name, g, w in zip(("decode", "prefill", "decode fp8", "planned decode"), got, want):
+        for name, g, w in zip(("decode", "prefill", "decode fp8", "planned decode", "precise prefill",
+                               "prefill fp8 (widening pass + prefill)"), got, want):
             assert torch.equal(g, w), f"replay {r}: {name} differs from the eager step"
         # eager work between replays, on the same buffers
         step()
